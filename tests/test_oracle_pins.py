@@ -1,0 +1,402 @@
+"""Pins of oracle/ref.py to things other than itself: torch float64 modules
+(an independent implementation of the dense special cases), brute force on
+tiny inputs, closed forms and invariants the pages state."""
+import functools
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import ref
+from contextual_sparsity_decoding_amd import synth
+from contextual_sparsity_decoding_amd.configs import LayerDims
+
+T64 = torch.float64
+
+
+def t64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+# ------------------------------------------------------------- LayerNorm ----
+
+def test_layernorm_matches_torch():
+    x = synth.normal((3, 200), 1, 0, "x")
+    g = synth.normal((200,), 2, 0, "x") + 1
+    b = synth.normal((200,), 3, 0, "x")
+    want = F.layer_norm(t64(x), (200,), t64(g), t64(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(ref.layernorm(x, g, b, 1e-5), want, rtol=0, atol=1e-12)
+
+
+def test_layernorm_shift_invariant():
+    x = synth.normal((2, 64), 4, 0, "x").astype(np.float64)
+    g, b = np.ones(64), np.zeros(64)
+    np.testing.assert_allclose(ref.layernorm(x + 3.5, g, b), ref.layernorm(x, g, b), atol=1e-12)
+
+
+# ------------------------------------------------------------- predictor ----
+
+@pytest.mark.parametrize("act", ["relu", "none"])
+def test_predictor_matches_torch_two_layer_net(act):
+    d, r, n = 96, 16, 200
+    p1_t = synth.normal((r, d), 5, 0, "pm1_t", 0.1)
+    p2_t = synth.normal((n, r), 5, 0, "pm2_t", 0.1)
+    y = synth.normal((2, d), 5, 0, "x")
+    fc1 = torch.nn.Linear(d, r, bias=False).double()
+    fc2 = torch.nn.Linear(r, n, bias=False).double()
+    with torch.no_grad():
+        fc1.weight.copy_(t64(p1_t))
+        fc2.weight.copy_(t64(p2_t))
+        hid = fc1(t64(y))
+        want = fc2(torch.relu(hid) if act == "relu" else hid).numpy()
+    np.testing.assert_allclose(ref.predictor(y, p1_t, p2_t, act), want, atol=1e-12)
+
+
+def test_predictor_linear_is_low_rank_product():
+    d, r, n = 64, 8, 50
+    p1_t = synth.normal((r, d), 6, 0, "pm1_t")
+    p2_t = synth.normal((n, r), 6, 0, "pm2_t")
+    y = synth.normal((1, d), 6, 0, "x")
+    P = p1_t.T.astype(np.float64) @ p2_t.T.astype(np.float64)   # d x n
+    np.testing.assert_allclose(ref.predictor(y, p1_t, p2_t, "none"), y @ P, atol=1e-10)
+
+
+# ------------------------------------------------------------- top-k --------
+
+def _brute_order(s):
+    """Comparison sort straight from the definition: i before j iff s_i > s_j,
+    or s_i == s_j and i < j; NaN after every number (NaNs tie with each other)."""
+    def before(i, j):
+        a, b = s[i], s[j]
+        if math.isnan(a) or math.isnan(b):
+            if math.isnan(a) and math.isnan(b):
+                return -1 if i < j else 1
+            return 1 if math.isnan(a) else -1
+        if a > b:
+            return -1
+        if a < b:
+            return 1
+        return -1 if i < j else 1
+    return sorted(range(len(s)), key=functools.cmp_to_key(before))
+
+
+VALUES = [-1.0, -0.0, 0.0, 1.0, float("nan"), float("inf"), float("-inf")]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_topk_exhaustive_ties(n):
+    for combo in itertools.product(VALUES, repeat=n):
+        s = np.array(combo, dtype=np.float32)
+        order = _brute_order(list(combo))
+        for k in range(n + 1):
+            got = ref.topk_select(s, k)
+            assert list(got) == sorted(order[:k]), (combo, k)
+
+
+def test_topk_random_against_brute_force():
+    g = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(g.integers(1, 40))
+        s = g.integers(-3, 4, size=n).astype(np.float32)
+        s[g.random(n) < 0.1] = np.nan
+        k = int(g.integers(0, n + 1))
+        assert list(ref.topk_select(s, k)) == sorted(_brute_order(list(s))[:k])
+
+
+def test_topk_properties():
+    s = synth.tied_scores(1, 500, 3, levels=7)[0]
+    assert list(ref.topk_select(s, 500)) == list(range(500))
+    prev = set()
+    for k in range(0, 501, 25):
+        cur = set(ref.topk_select(s, k).tolist())
+        assert prev <= cur and len(cur) == k
+        prev = cur
+    with pytest.raises(ValueError):
+        ref.topk_select(s, 501)
+
+
+def test_union_matches_numpy():
+    g = np.random.default_rng(8)
+    sets = [np.sort(g.choice(1000, 60, replace=False)) for _ in range(5)]
+    want = functools.reduce(np.union1d, sets)
+    assert list(ref.union_sorted(sets)) == list(want)
+    assert list(ref.union_sorted(sets[:1])) == list(sets[0])
+
+
+# ------------------------------------------------------------- MLP ----------
+
+def _torch_mlp(y, w1_t, b1, w2_t, b2, residual=None, keep=None):
+    """Dense OPT MLP from torch modules; ``keep`` zeroes the other neurons'
+    fc1 weights and biases (so their ReLU output is exactly 0)."""
+    N, d = w1_t.shape
+    fc1 = torch.nn.Linear(d, N).double()
+    fc2 = torch.nn.Linear(N, d).double()
+    with torch.no_grad():
+        w1 = t64(w1_t).clone()
+        bb1 = t64(b1).clone()
+        if keep is not None:
+            mask = torch.zeros(N, dtype=torch.bool)
+            mask[torch.as_tensor(keep)] = True
+            w1[~mask] = 0
+            bb1[~mask] = 0
+        fc1.weight.copy_(w1)
+        fc1.bias.copy_(bb1)
+        fc2.weight.copy_(t64(w2_t).T)      # W2 is d x N; its column j is w2_t[j]
+        fc2.bias.copy_(t64(b2))
+        out = fc2(torch.relu(fc1(t64(y))))
+        if residual is not None:
+            out = out + t64(residual)
+    return out.numpy()
+
+
+@pytest.fixture(scope="module")
+def mlp_block():
+    dims = LayerDims(d=256, N=1024, h=0, r_mlp=64, wdt="f32")
+    w = synth.mlp_weights(dims, seed=0)
+    x = synth.layer_inputs(256, 1, 2, seed=0)[0]
+    return w, x
+
+
+def test_sparse_mlp_full_set_equals_dense(mlp_block):
+    w, x = mlp_block
+    out, _ = ref.sparse_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"], np.arange(1024))
+    want = _torch_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"])
+    np.testing.assert_allclose(out, want, atol=1e-12)
+
+
+def test_sparse_mlp_equals_masked_dense(mlp_block):
+    w, x = mlp_block
+    idx = np.sort(np.random.default_rng(1).choice(1024, 256, replace=False))
+    res = synth.normal((2, 256), 9, 0, "x")
+    out, a = ref.sparse_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx, residual=res)
+    want = _torch_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"], residual=res, keep=idx)
+    np.testing.assert_allclose(out, want, atol=1e-12)
+    assert a.shape == (2, 256) and np.all(a >= 0)
+
+
+def test_skip_nonpositive_is_exact(mlp_block):
+    w, x = mlp_block
+    idx = np.arange(1024)
+    full, a = ref.sparse_mlp(x[:1], w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx)
+    assert 0 < (a > 0).sum() < 1024      # the test drops something real
+    skip, _ = ref.sparse_mlp(x[:1], w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx, skip_nonpos=True)
+    assert np.array_equal(full, skip)
+    # and dropping them from S altogether gives the same output
+    live = idx[a[0] > 0]
+    only, _ = ref.sparse_mlp(x[:1], w["w1_t"], w["b1"], w["w2_t"], w["b2"], live)
+    assert np.array_equal(full, only)
+
+
+def test_sparse_mlp_order_of_set_does_not_matter(mlp_block):
+    w, x = mlp_block
+    idx = np.arange(0, 1024, 3)
+    a, _ = ref.sparse_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx)
+    b, _ = ref.sparse_mlp(x, w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx[::-1].copy())
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# ------------------------------------------------------------- attention ----
+
+def small_dims():
+    return LayerDims(d=64, N=256, h=4, d_h=16, r_attn=8, r_mlp=8, wdt="f16")
+
+
+def test_attend_matches_torch_sdpa():
+    g = np.random.default_rng(2)
+    for n in (1, 7, 100):
+        q = g.standard_normal(16)
+        K = g.standard_normal((n, 16)).astype(np.float16)
+        V = g.standard_normal((n, 16)).astype(np.float16)
+        want = F.scaled_dot_product_attention(t64(q)[None, None, None], t64(K)[None, None],
+                                              t64(V)[None, None], scale=0.25)[0, 0, 0].numpy()
+        np.testing.assert_allclose(ref.attend(q, K, V, 0.25), want, atol=1e-12)
+
+
+def test_attend_special_cases():
+    g = np.random.default_rng(3)
+    V = g.standard_normal((5, 8))
+    np.testing.assert_allclose(ref.attend(g.standard_normal(8), V[:1] * 0 + 1, V[:1], 1.0), V[0])
+    K = np.tile(g.standard_normal(8), (5, 1))        # equal keys -> mean of V
+    np.testing.assert_allclose(ref.attend(g.standard_normal(8), K, V, 1.0), V.mean(0), atol=1e-12)
+
+
+@pytest.mark.parametrize("bounds", [[0, 50], [0, 10, 50], [0, 0, 17, 17, 50], [0, 1, 2, 3, 50],
+                                    list(range(0, 51))])
+def test_splitk_combine_equals_softmax(bounds):
+    g = np.random.default_rng(4)
+    q, K, V = g.standard_normal(16), g.standard_normal((50, 16)) * 3, g.standard_normal((50, 16))
+    parts = ref.splitk_partials(q, K, V, 0.3, bounds)
+    np.testing.assert_allclose(ref.splitk_combine(parts), ref.attend(q, K, V, 0.3), atol=1e-12)
+
+
+def _mha_module(W, dims):
+    """torch.nn.MultiheadAttention with DejaVu §2.3's per-head blocks."""
+    d, h, dh = dims.d, dims.h, dims.d_h
+    m = torch.nn.MultiheadAttention(d, h, bias=True, batch_first=True).double()
+    with torch.no_grad():
+        # in_proj rows: Q then K then V, head-major with d_h rows per head
+        m.in_proj_weight.copy_(t64(W["w_qkv_t"]).reshape(3 * h * dh, d))
+        m.in_proj_bias.copy_(t64(W["b_qkv"]).reshape(-1))
+        m.out_proj.weight.copy_(t64(W["w_o_t"]).T)      # W^O is (h d_h) x d
+        m.out_proj.bias.copy_(t64(W["b_o"]))
+    return m
+
+
+def test_dense_attention_block_matches_torch_mha():
+    """All heads every step: cache filled by qkv_step, attention, out_proj vs
+    torch MultiheadAttention over the same inputs (K/V rounding to fp16 in the
+    cache bounds the difference)."""
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=11)
+    T = 9
+    X = synth.layer_inputs(dims.d, T, 1, seed=11)[:, 0, :].astype(np.float64)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 0, 16, seed=11)
+    kv = ref.KVState(K, V, np.zeros((1, 16, dims.d)), np.full((1, dims.h), -1))
+    heads = np.arange(dims.h)
+    for t in range(T):
+        q = ref.qkv_step(X[t:t + 1], W["w_qkv_t"], W["b_qkv"], heads, kv, t)
+    o = ref.attention(q, kv, heads, T, 1 / math.sqrt(dims.d_h))
+    got = ref.out_proj(o, W["w_o_t"], W["b_o"], heads)
+    m = _mha_module(W, dims)
+    with torch.no_grad():
+        want = m(t64(X[-1:])[None], t64(X)[None], t64(X)[None], need_weights=False)[0][0].numpy()
+    err = np.abs(got - want).max() / np.abs(want).max()
+    assert err < 3e-3, err
+
+
+def test_hole_fill_reproduces_on_time_cache():
+    """DejaVu §4.2: K/V recomputed from stored inputs equal those computed on time."""
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=12)
+    T, L = 12, 16
+    X = synth.layer_inputs(dims.d, T, 1, seed=12)[:, 0, :].astype(np.float64)
+    g = np.random.default_rng(12)
+    K0, V0 = synth.kv_cache(dims.h, dims.d_h, 0, L, seed=12)
+    lazy = ref.KVState(K0.copy(), V0.copy(), np.zeros((1, L, dims.d)), np.full((1, dims.h), -1))
+    eager = ref.KVState(K0.copy(), V0.copy(), np.zeros((1, L, dims.d)), np.full((1, dims.h), -1))
+    for t in range(T):
+        sel = np.sort(g.choice(dims.h, 2, replace=False))
+        ref.qkv_step(X[t:t + 1], W["w_qkv_t"], W["b_qkv"], sel, lazy, t)
+        ref.qkv_step(X[t:t + 1], W["w_qkv_t"], W["b_qkv"], np.arange(dims.h), eager, t)
+    ref.qkv_step(X[-1:], W["w_qkv_t"], W["b_qkv"], np.arange(dims.h), lazy, T - 1)
+    assert np.array_equal(lazy.K[:, :, :T], eager.K[:, :, :T])
+    assert np.array_equal(lazy.V[:, :, :T], eager.V[:, :, :T])
+    # without hole fill the skipped slots stay empty
+    nofill = ref.KVState(K0.copy(), V0.copy(), None, None)
+    ref.qkv_step(X[:1], W["w_qkv_t"], W["b_qkv"], np.array([0]), nofill, 0)
+    assert np.all(nofill.K[0, 1:, 0] == 0) and np.any(nofill.K[0, 0, 0] != 0)
+
+
+def test_kv_selected_attention_with_full_budget_is_dense():
+    dims = small_dims()
+    g = np.random.default_rng(13)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 40, 48, seed=13)
+    kv = ref.KVState(K, V)
+    q = g.standard_normal((1, dims.h, dims.d_h))
+    heads = np.arange(dims.h)
+    sel = np.tile(np.arange(40), (1, dims.h, 1))
+    lens = np.full((1, dims.h), 40)
+    a = ref.attention(q, kv, heads, 44, 0.2, sel, lens, 40)
+    b = ref.attention(q, kv, heads, 44, 0.2)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# ------------------------------------------------------- KV-position scores --
+
+def test_kv_scores_match_masked_softmax():
+    g = np.random.default_rng(14)
+    n, n_obs, dh = 50, 8, 16
+    K = g.standard_normal((n, dh)).astype(np.float16)
+    Q = g.standard_normal((n_obs, dh)).astype(np.float16)
+    pos = torch.arange(n - n_obs, n)[:, None]
+    mask = torch.arange(n)[None, :] <= pos                      # causal
+    s = 0.3 * t64(Q) @ t64(K).T
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+    want = p.sum(0).numpy()
+    got = ref.kv_position_scores(Q, K, n, 0.3)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+    assert math.isclose(got.sum(), n_obs, rel_tol=1e-12)     # each query's mass is 1
+
+
+def test_moving_average_matches_convolution():
+    s = np.random.default_rng(15).standard_normal(40)
+    np.testing.assert_allclose(ref.moving_average(s, 7), np.convolve(s, np.ones(7) / 7, mode="same"),
+                               atol=1e-12)
+
+
+def test_kv_select_properties():
+    g = np.random.default_rng(16)
+    n, dh = 200, 16
+    K = g.standard_normal((n, dh)).astype(np.float16)
+    Q = g.standard_normal((64, dh)).astype(np.float16)
+    full, _ = ref.kv_select(Q, K, n, 0.25, n)
+    assert list(full) == list(range(n))
+    prev = set()
+    for b in (68, 80, 120, 200):
+        S, _ = ref.kv_select(Q, K, n, 0.25, b)
+        S = set(S.tolist())
+        assert len(S) == b
+        assert set(range(4)) | set(range(n - 64, n)) <= S     # sinks and window forced
+        assert prev <= S
+        prev = S
+
+
+# ------------------------------------------------------------- the layer ----
+
+def _torch_dense_layer(x, W, K, V, pos, scale, eps):
+    """A pre-LN OPT-style decoder layer from torch float64 ops over a given
+    fp16 cache, the new token's k/v written at ``pos`` (rounded to fp16)."""
+    d = x.shape[1]
+    h, dh = W["w_qkv_t"].shape[1], W["w_qkv_t"].shape[2]
+    xt = t64(x)
+    y = F.layer_norm(xt, (d,), t64(W["ln1_g"]), t64(W["ln1_b"]), eps)
+    qkv = F.linear(y, t64(W["w_qkv_t"]).reshape(3 * h * dh, d), t64(W["b_qkv"]).reshape(-1))
+    q, k, v = qkv.reshape(3, h, dh)
+    Kc, Vc = t64(K[0]).clone(), t64(V[0]).clone()
+    Kc[:, pos] = k.to(torch.float16).double()
+    Vc[:, pos] = v.to(torch.float16).double()
+    o = F.scaled_dot_product_attention(q[:, None, :], Kc[:, :pos + 1], Vc[:, :pos + 1], scale=scale)
+    hres = xt + F.linear(o.reshape(1, h * dh), t64(W["w_o_t"]).T, t64(W["b_o"]))
+    y2 = F.layer_norm(hres, (d,), t64(W["ln2_g"]), t64(W["ln2_b"]), eps)
+    a = torch.relu(F.linear(y2, t64(W["w1_t"]), t64(W["b1"])))
+    return (hres + F.linear(a, t64(W["w2_t"]).T, t64(W["b2"]))).numpy()
+
+
+def test_decode_layer_full_keep_equals_dense_torch_layer():
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=17)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 20, 24, seed=17)
+    x = synth.layer_inputs(dims.d, 1, 1, seed=17)[0]
+    want = _torch_dense_layer(x, W, K, V, 20, 0.25, 1e-5)
+    for dense in (True, False):
+        kv = ref.KVState(K.copy(), V.copy(), np.zeros((1, 24, dims.d)), np.full((1, dims.h), 19))
+        got, rec = ref.decode_layer(x, W, kv, 20, k_heads=dims.h, k_neurons=dims.N, scale=0.25,
+                                    dense_attn=dense, dense_mlp=dense)
+        np.testing.assert_allclose(got, want, atol=1e-9, rtol=0)
+        assert len(rec["head_idx"]) == dims.h and len(rec["neuron_idx"]) == dims.N
+
+
+def test_decode_layer_batch_uses_union():
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=18)
+    B = 3
+    K, V = synth.kv_cache(dims.h, dims.d_h, 10, 16, seed=18, batch=B)
+    x = synth.layer_inputs(dims.d, 1, B, seed=18)[0]
+    kv = ref.KVState(K.copy(), V.copy(), np.zeros((B, 16, dims.d)), np.full((B, dims.h), 9))
+    out, rec = ref.decode_layer(x, W, kv, 10, k_heads=1, k_neurons=20, scale=0.25)
+    per = [ref.topk_select(rec["neuron_scores"][b], 20) for b in range(B)]
+    assert list(rec["neuron_idx"]) == sorted(set(np.concatenate(per).tolist()))
+    # each row equals running that row alone over the union sets
+    for b in range(B):
+        kv1 = ref.KVState(K[b:b + 1].copy(), V[b:b + 1].copy(), np.zeros((1, 16, dims.d)),
+                          np.full((1, dims.h), 9))
+        q = ref.qkv_step(ref.layernorm(x[b:b + 1], W["ln1_g"], W["ln1_b"]), W["w_qkv_t"], W["b_qkv"],
+                         rec["head_idx"], kv1, 10)
+        o = ref.attention(q, kv1, rec["head_idx"], 11, 0.25)
+        hres = ref.out_proj(o, W["w_o_t"], W["b_o"], rec["head_idx"], residual=x[b:b + 1])
+        y2 = ref.layernorm(hres, W["ln2_g"], W["ln2_b"])
+        row, _ = ref.sparse_mlp(y2, W["w1_t"], W["b1"], W["w2_t"], W["b2"], rec["neuron_idx"], hres)
+        np.testing.assert_allclose(out[b:b + 1], row, atol=1e-12)
