@@ -1,0 +1,467 @@
+// C-ABI entry points of libdv: argument validation (host only, before any
+// launch), workspace sizing and the order of kernel launches.
+//
+// Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
+// Inference Time" (arXiv 2310.17157); ByteCross = "Where Activation Sparsity
+// and KV-Cache Sparsity Cross in LLM Decoding" (arXiv 2609.33889v1).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dv_internal.h"
+
+namespace dvh {
+
+static thread_local char g_err[512];
+
+dv_status fail(dv_status code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int elt_bytes(int wdt) { return wdt == DV_F16 ? 2 : 4; }
+
+static bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool wdt_ok(int wdt) { return wdt == DV_F16 || wdt == DV_F32; }
+static bool dh_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128 || d_h == 256; }
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return a && b && x < y + nb && y < x + na;
+}
+
+#define REQ(cond, code, ...)                 \
+    do {                                     \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+#define TRY(expr)                            \
+    do {                                     \
+        dv_status st_ = (expr);              \
+        if (st_ != DV_OK) return st_;        \
+    } while (0)
+
+// ---- workspace layouts ------------------------------------------------------
+
+static size_t predict_ws(int B, int d, int r, int wdt) { return align_up(pred_partials(B, d, r, wdt) * 4, 256); }
+
+struct MlpWs {
+    float* a;
+    float* partial;
+    unsigned* counters;
+    size_t bytes;
+};
+static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a) {
+    Carve cv(ws);
+    MlpWs w;
+    w.a = need_a ? cv.take<float>((size_t)B * (n_idx_max > 0 ? n_idx_max : 1)) : nullptr;
+    const AxpyPlan p = axpy_plan(d, n_idx_max, wdt);
+    w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
+    w.counters = cv.take<unsigned>(p.n_slices);
+    w.bytes = align_up(cv.off, 256);
+    return w;
+}
+
+struct ProjWs {
+    float* partial;
+    unsigned* counters;
+    size_t bytes;
+};
+static ProjWs proj_ws(void* ws, int mode, int B, int d, int n_sel, int d_h, int wdt) {
+    Carve cv(ws);
+    ProjWs w{nullptr, nullptr, 0};
+    if (mode == DV_PROJ_OUT) {
+        const AxpyPlan p = axpy_plan(d, n_sel * d_h, wdt);
+        w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
+        w.counters = cv.take<unsigned>(p.n_slices);
+    } else {
+        w.counters = cv.take<unsigned>(1);
+    }
+    w.bytes = align_up(cv.off, 256);
+    return w;
+}
+
+static size_t splitk_ws(int B, int n_sel, int d_h, int max_positions, int num_splits) {
+    if (num_splits <= 0) num_splits = splitk_auto(max_positions, B * n_sel);
+    return align_up((size_t)B * n_sel * num_splits * (d_h + 2) * 4, 256);
+}
+
+}  // namespace dvh
+
+using namespace dvh;
+
+extern "C" {
+
+int dv_api_version(void) { return DV_API_VERSION; }
+
+const char* dv_status_str(int s) {
+    switch (s) {
+        case DV_OK: return "DV_OK";
+        case DV_ERR_NULL: return "DV_ERR_NULL";
+        case DV_ERR_SHAPE: return "DV_ERR_SHAPE";
+        case DV_ERR_DTYPE: return "DV_ERR_DTYPE";
+        case DV_ERR_ALIGN: return "DV_ERR_ALIGN";
+        case DV_ERR_RANGE: return "DV_ERR_RANGE";
+        case DV_ERR_WORKSPACE: return "DV_ERR_WORKSPACE";
+        case DV_ERR_UNSUPPORTED: return "DV_ERR_UNSUPPORTED";
+        case DV_ERR_HIP: return "DV_ERR_HIP";
+        default: return "DV_ERR_UNKNOWN";
+    }
+}
+
+const char* dv_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------- LayerNorm --
+dv_status dv_layernorm(const float* x, int B, int d, const float* gamma, const float* beta, float eps,
+                       float* y, void* stream) {
+    clear_error();
+    REQ(x && gamma && beta && y, DV_ERR_NULL, "dv_layernorm: NULL pointer");
+    REQ(B >= 1 && d >= 1, DV_ERR_SHAPE, "dv_layernorm: B=%d d=%d", B, d);
+    REQ(eps >= 0.f && isfinite(eps), DV_ERR_RANGE, "dv_layernorm: eps");
+    return launch_layernorm(x, B, d, gamma, beta, eps, y, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- predictor --
+size_t dv_predict_workspace_bytes(int B, int d, int r, int wdt) {
+    if (B < 1 || d < 1 || r < 1 || !wdt_ok(wdt)) return 0;
+    return predict_ws(B, d, r, wdt);
+}
+
+static dv_status check_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t,
+                               int n_out, int wdt, int act, const float* scores) {
+    REQ(y && p1_t && p2_t && scores, DV_ERR_NULL, "dv_predict: NULL pointer");
+    REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_predict: wdt %d", wdt);
+    REQ(act == DV_ACT_NONE || act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_predict: act %d", act);
+    REQ(B >= 1 && B <= 16 && d >= 1 && r >= 1 && r <= 512 && n_out >= 1, DV_ERR_SHAPE,
+        "dv_predict: B=%d d=%d r=%d n_out=%d", B, d, r, n_out);
+    const int eb = elt_bytes(wdt);
+    REQ((size_t)d * eb % 16 == 0 && (size_t)r * eb % 16 == 0, DV_ERR_ALIGN,
+        "dv_predict: rows of d=%d and r=%d elements must be multiples of 16 bytes", d, r);
+    REQ(a16(p1_t) && a16(p2_t) && a16(y), DV_ERR_ALIGN, "dv_predict: pointers must be 16-byte aligned");
+    return DV_OK;
+}
+
+dv_status dv_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t, int n_out, int wdt,
+                     int act, float* scores, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    TRY(check_predict(y, B, d, p1_t, r, p2_t, n_out, wdt, act, scores));
+    REQ(ws && ws_bytes >= predict_ws(B, d, r, wdt), DV_ERR_WORKSPACE, "dv_predict: workspace");
+    return launch_predict(y, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, (float*)ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- top-k -----
+size_t dv_topk_workspace_bytes(int B, int n, int k) {
+    (void)B; (void)n; (void)k;
+    return 0;
+}
+
+dv_status dv_topk_select(const float* scores, int B, int n, int k, int32_t* idx, int32_t* union_idx,
+                         int32_t* union_count, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    (void)ws; (void)ws_bytes;
+    REQ(B >= 1 && B <= 64 && n >= 0 && n <= 65536, DV_ERR_SHAPE, "dv_topk_select: B=%d n=%d", B, n);
+    REQ(k >= 0 && k <= n, DV_ERR_RANGE, "dv_topk_select: k=%d outside [0, n=%d]", k, n);
+    REQ(k == 0 || (scores && idx), DV_ERR_NULL, "dv_topk_select: NULL pointer");
+    REQ((union_idx == nullptr) == (union_count == nullptr), DV_ERR_NULL,
+        "dv_topk_select: union_idx and union_count go together");
+    hipStream_t s = (hipStream_t)stream;
+    TRY(launch_topk(scores, B, n, k, idx, s));
+    if (union_idx) TRY(launch_union(idx, B, k, n, union_idx, union_count, s));
+    return DV_OK;
+}
+
+// ---------------------------------------------------------------- MLP -------
+size_t dv_sparse_mlp_workspace_bytes(int B, int d, int n_idx_max, int wdt) {
+    if (B < 1 || d < 1 || n_idx_max < 0 || !wdt_ok(wdt)) return 0;
+    return mlp_ws(nullptr, B, d, n_idx_max, wdt, true).bytes;
+}
+
+dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, const void* b1, const void* w2_t,
+                        const void* b2, int wdt, const int32_t* idx, int n_idx_max, const int32_t* n_idx_dev,
+                        const float* residual, float* out, float* act_out, int32_t* fc2_rows, unsigned flags,
+                        void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    REQ(y && w1_t && b1 && w2_t && b2 && out, DV_ERR_NULL, "dv_sparse_mlp: NULL pointer");
+    REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_sparse_mlp: wdt %d", wdt);
+    REQ(B >= 1 && B <= 16 && d >= 1 && N >= 1, DV_ERR_SHAPE, "dv_sparse_mlp: B=%d d=%d N=%d", B, d, N);
+    REQ(n_idx_max >= 0 && n_idx_max <= N, DV_ERR_RANGE, "dv_sparse_mlp: n_idx_max=%d N=%d", n_idx_max, N);
+    REQ(idx || n_idx_max == N, DV_ERR_SHAPE, "dv_sparse_mlp: idx NULL needs n_idx_max == N");
+    REQ((flags & ~(unsigned)DV_SKIP_NONPOS_FC2) == 0, DV_ERR_DTYPE, "dv_sparse_mlp: flags 0x%x", flags);
+    REQ((size_t)d * elt_bytes(wdt) % 16 == 0, DV_ERR_ALIGN, "dv_sparse_mlp: d=%d rows not 16-byte multiples", d);
+    REQ(a16(w1_t) && a16(w2_t) && a16(y), DV_ERR_ALIGN, "dv_sparse_mlp: pointers must be 16-byte aligned");
+    const size_t act_bytes = (size_t)B * d * 4;
+    REQ(!overlap(out, act_bytes, y, act_bytes) && !overlap(out, act_bytes, residual, act_bytes), DV_ERR_RANGE,
+        "dv_sparse_mlp: out overlaps y or residual");
+    const MlpWs w = mlp_ws(ws, B, d, n_idx_max, wdt, act_out == nullptr);
+    REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "dv_sparse_mlp: workspace %zu < %zu", ws_bytes, w.bytes);
+    hipStream_t s = (hipStream_t)stream;
+    float* a = act_out ? act_out : w.a;
+    TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
+    return launch_axpy(w2_t, wdt, d, N, n_idx_max, n_idx_dev, idx, 1, a, n_idx_max, (flags & DV_SKIP_NONPOS_FC2) != 0,
+                       B, b2, residual, out, fc2_rows, w.partial, w.counters, s);
+}
+
+// ---------------------------------------------------------------- projections --
+size_t dv_attn_proj_workspace_bytes(int mode, int B, int d, int h, int d_h, int n_sel, int wdt) {
+    (void)h;
+    if ((mode != DV_PROJ_QKV && mode != DV_PROJ_OUT) || B < 1 || d < 1 || d_h < 1 || n_sel < 0 || !wdt_ok(wdt))
+        return 0;
+    return proj_ws(nullptr, mode, B, d, n_sel, d_h, wdt).bytes;
+}
+
+dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
+                              const void* w_t, const void* bias, int wdt, const float* in, const float* residual,
+                              float* out, const dv_kv_state* kv, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    REQ(mode == DV_PROJ_QKV || mode == DV_PROJ_OUT, DV_ERR_DTYPE, "dv_sparse_attn_proj: mode %d", mode);
+    REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_sparse_attn_proj: wdt %d", wdt);
+    REQ(w_t && in && out, DV_ERR_NULL, "dv_sparse_attn_proj: NULL pointer");
+    REQ(B >= 1 && B <= 16 && d >= 1 && h >= 1 && dh_ok(d_h), DV_ERR_SHAPE,
+        "dv_sparse_attn_proj: B=%d d=%d h=%d d_h=%d", B, d, h, d_h);
+    REQ(n_sel >= 0 && n_sel <= h, DV_ERR_RANGE, "dv_sparse_attn_proj: n_sel=%d h=%d", n_sel, h);
+    REQ((size_t)d * elt_bytes(wdt) % 16 == 0, DV_ERR_ALIGN, "dv_sparse_attn_proj: d=%d rows", d);
+    REQ(a16(w_t) && a16(in), DV_ERR_ALIGN, "dv_sparse_attn_proj: pointers must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const ProjWs w = proj_ws(ws, mode, B, d, n_sel, d_h, wdt);
+    if (mode == DV_PROJ_QKV) {
+        REQ(kv && kv->k_cache && kv->v_cache && bias, DV_ERR_NULL, "dv_sparse_attn_proj: QKV needs kv and bias");
+        REQ(kv->max_len >= 1 && kv->pos >= 0 && kv->pos < kv->max_len, DV_ERR_RANGE,
+            "dv_sparse_attn_proj: pos=%d max_len=%d", kv->pos, kv->max_len);
+        REQ(!overlap(out, (size_t)B * n_sel * d_h * 4, in, (size_t)B * d * 4), DV_ERR_RANGE,
+            "dv_sparse_attn_proj: q overlaps y");
+        const bool fill = kv->y_buf && kv->valid_upto;
+        REQ(!fill || (ws && ws_bytes >= w.bytes), DV_ERR_WORKSPACE, "dv_sparse_attn_proj: workspace");
+        return launch_qkv(in, B, d, h, d_h, head_idx, n_sel, w_t, bias, wdt, out, kv, fill ? w.counters : nullptr, s);
+    }
+    REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "dv_sparse_attn_proj: workspace %zu < %zu", ws_bytes, w.bytes);
+    REQ(!overlap(out, (size_t)B * d * 4, in, (size_t)B * n_sel * d_h * 4) &&
+            !overlap(out, (size_t)B * d * 4, residual, (size_t)B * d * 4),
+        DV_ERR_RANGE, "dv_sparse_attn_proj: out overlaps o or residual");
+    return launch_axpy(w_t, wdt, d, h * d_h, n_sel * d_h, nullptr, head_idx, d_h, in, n_sel * d_h, false, B, bias, residual,
+                       out, nullptr, w.partial, w.counters, s);
+}
+
+// ---------------------------------------------------------------- attention --
+size_t dv_splitk_workspace_bytes(int B, int n_sel, int d_h, int max_positions, int num_splits) {
+    if (B < 1 || n_sel < 0 || d_h < 1 || max_positions < 0 || num_splits < 0) return 0;
+    return splitk_ws(B, n_sel, d_h, max_positions, num_splits);
+}
+
+static dv_status check_view(const dv_kv_view* kv, const char* who) {
+    REQ(kv && kv->k_cache && kv->v_cache, DV_ERR_NULL, "%s: kv view NULL", who);
+    REQ(kv->h >= 1 && kv->max_len >= 1, DV_ERR_SHAPE, "%s: h=%d max_len=%d", who, kv->h, kv->max_len);
+    REQ(kv->n_ctx >= 1 && kv->n_ctx <= kv->max_len, DV_ERR_RANGE, "%s: n_ctx=%d max_len=%d", who, kv->n_ctx,
+        kv->max_len);
+    if (kv->sel_idx) {
+        REQ(kv->sel_len, DV_ERR_NULL, "%s: sel_len NULL", who);
+        REQ(kv->sel_end >= 0 && kv->sel_end <= kv->n_ctx && kv->sel_cap >= 0 && kv->sel_cap <= kv->sel_end,
+            DV_ERR_RANGE, "%s: sel_cap=%d sel_end=%d n_ctx=%d", who, kv->sel_cap, kv->sel_end, kv->n_ctx);
+    }
+    return DV_OK;
+}
+
+dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel, const dv_kv_view* kv,
+                         float scale, int num_splits, float* o, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    REQ(q && o, DV_ERR_NULL, "dv_splitk_attn: NULL pointer");
+    TRY(check_view(kv, "dv_splitk_attn"));
+    REQ(B >= 1 && dh_ok(d_h), DV_ERR_SHAPE, "dv_splitk_attn: B=%d d_h=%d", B, d_h);
+    REQ(n_sel >= 0 && n_sel <= kv->h, DV_ERR_RANGE, "dv_splitk_attn: n_sel=%d h=%d", n_sel, kv->h);
+    REQ(isfinite(scale), DV_ERR_RANGE, "dv_splitk_attn: scale");
+    REQ(num_splits >= 0 && num_splits <= 65536, DV_ERR_RANGE, "dv_splitk_attn: num_splits=%d", num_splits);
+    REQ((long)B * n_sel * (num_splits > 0 ? num_splits : 1) <= (1L << 26), DV_ERR_RANGE, "dv_splitk_attn: too many splits");
+    const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
+    const size_t need = splitk_ws(B, n_sel, d_h, maxpos, num_splits);
+    REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_splitk_attn: workspace %zu < %zu", ws_bytes, need);
+    return launch_splitk(q, B, d_h, head_idx, n_sel, kv, scale, num_splits, o, (float*)ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- KV scoring --
+size_t dv_kv_score_workspace_bytes(int B, int h, int n, int n_obs) {
+    if (B < 1 || h < 1 || n < 1 || n_obs < 1) return 0;
+    return align_up(kv_score_stats_floats(B, h, n, n_obs) * 4, 256);
+}
+
+dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv, float scale,
+                      int n_sink, int n_window, int width, float* scores, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    REQ(q_obs && scores, DV_ERR_NULL, "dv_kv_score: NULL pointer");
+    TRY(check_view(kv, "dv_kv_score"));
+    REQ(kv->sel_idx == nullptr, DV_ERR_UNSUPPORTED, "dv_kv_score: scores a dense view");
+    REQ(B >= 1 && h == kv->h && dh_ok(d_h), DV_ERR_SHAPE, "dv_kv_score: B=%d h=%d d_h=%d", B, h, d_h);
+    REQ(n_obs >= 1 && (size_t)n_obs * (d_h + 2) * 4 <= 65536 && n_obs <= kv->n_ctx, DV_ERR_RANGE, "dv_kv_score: n_obs=%d n=%d",
+        n_obs, kv->n_ctx);
+    REQ(width >= 1 && width <= 63 && (width & 1), DV_ERR_RANGE, "dv_kv_score: width=%d", width);
+    REQ(n_sink >= 0 && n_window >= 0, DV_ERR_RANGE, "dv_kv_score: n_sink=%d n_window=%d", n_sink, n_window);
+    REQ(isfinite(scale), DV_ERR_RANGE, "dv_kv_score: scale");
+    REQ(a16(q_obs), DV_ERR_ALIGN, "dv_kv_score: q_obs alignment");
+    const size_t need = dv_kv_score_workspace_bytes(B, h, kv->n_ctx, n_obs);
+    REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_kv_score: workspace %zu < %zu", ws_bytes, need);
+    return launch_kv_score(q_obs, B, h, d_h, n_obs, kv, scale, n_sink, n_window, width, scores, (float*)ws,
+                           (float*)ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- the layer --
+struct LayerWs {
+    float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
+    int32_t *head_idx, *nidx, *uidx, *ucnt;
+    unsigned *qkv_cnt, *axpy_cnt;
+    size_t bytes;
+};
+
+static int layer_nmax(const dv_decode_cfg* c) {
+    if (c->flags & DV_DENSE_MLP) return c->N;
+    const long m = (long)c->B * c->k_neurons;
+    return (int)(m < c->N ? m : c->N);
+}
+
+static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
+    Carve cv(ws);
+    LayerWs w;
+    const int B = c->B, d = c->d, h = c->h, dh = c->d_h;
+    const int nsel = (c->flags & DV_DENSE_ATTN) ? h : c->k_heads;
+    const int nmax = layer_nmax(c);
+    w.y = cv.take<float>((size_t)B * d);
+    w.hres = cv.take<float>((size_t)B * d);
+    w.y2 = cv.take<float>((size_t)B * d);
+    const size_t hp = pred_partials(B, d, c->r_attn > c->r_mlp ? c->r_attn : c->r_mlp, c->wdt);
+    w.hpart = cv.take<float>(hp > 0 ? hp : 1);
+    w.sA = cv.take<float>((size_t)B * h);
+    w.sM = cv.take<float>((size_t)B * c->N);
+    w.head_idx = cv.take<int32_t>(h);
+    w.nidx = cv.take<int32_t>((size_t)B * (c->k_neurons > 0 ? c->k_neurons : 1));
+    w.uidx = cv.take<int32_t>(c->N);
+    w.ucnt = cv.take<int32_t>(1);
+    w.q = cv.take<float>((size_t)B * h * dh);
+    w.o = cv.take<float>((size_t)B * h * dh);
+    const int splits = splitk_auto(max_len, B * nsel);
+    w.apart = cv.take<float>((size_t)B * (nsel > 0 ? nsel : 1) * splits * (dh + 2));
+    w.a = cv.take<float>((size_t)B * (nmax > 0 ? nmax : 1));
+    const AxpyPlan po = axpy_plan(d, nsel * dh, c->wdt), pm = axpy_plan(d, nmax, c->wdt);
+    const size_t xp = axpy_ws_floats(po, B, d) > axpy_ws_floats(pm, B, d) ? axpy_ws_floats(po, B, d)
+                                                                           : axpy_ws_floats(pm, B, d);
+    w.xpart = cv.take<float>(xp);
+    w.qkv_cnt = cv.take<unsigned>(1);
+    w.axpy_cnt = cv.take<unsigned>(po.n_slices > pm.n_slices ? po.n_slices : pm.n_slices);
+    w.bytes = align_up(cv.off, 256);
+    return w;
+}
+
+static dv_status check_cfg(const dv_decode_cfg* c) {
+    REQ(c, DV_ERR_NULL, "dv_decode_layer: cfg NULL");
+    REQ(wdt_ok(c->wdt), DV_ERR_DTYPE, "dv_decode_layer: wdt %d", c->wdt);
+    REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
+    const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT;
+    REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
+    REQ(c->B >= 1 && c->B <= 16 && c->d >= 1 && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
+        "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
+    const int eb = elt_bytes(c->wdt);
+    REQ((size_t)c->d * eb % 16 == 0, DV_ERR_ALIGN, "dv_decode_layer: d=%d rows", c->d);
+    if (!(c->flags & DV_DENSE_ATTN)) {
+        REQ(c->r_attn >= 1 && c->r_attn <= 512 && (size_t)c->r_attn * eb % 16 == 0, DV_ERR_SHAPE,
+            "dv_decode_layer: r_attn=%d", c->r_attn);
+        REQ(c->k_heads >= 0 && c->k_heads <= c->h, DV_ERR_RANGE, "dv_decode_layer: k_heads=%d", c->k_heads);
+        REQ(c->B == 1, DV_ERR_UNSUPPORTED, "dv_decode_layer: head sparsity with B=%d", c->B);
+    }
+    if (!(c->flags & DV_DENSE_MLP)) {
+        REQ(c->r_mlp >= 1 && c->r_mlp <= 512 && (size_t)c->r_mlp * eb % 16 == 0, DV_ERR_SHAPE,
+            "dv_decode_layer: r_mlp=%d", c->r_mlp);
+        REQ(c->k_neurons >= 0 && c->k_neurons <= c->N && c->N <= 65536, DV_ERR_RANGE, "dv_decode_layer: k_neurons=%d",
+            c->k_neurons);
+    }
+    REQ(isfinite(c->scale) && c->eps >= 0.f && isfinite(c->eps), DV_ERR_RANGE, "dv_decode_layer: scale/eps");
+    return DV_OK;
+}
+
+size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len) {
+    if (check_cfg(cfg) != DV_OK || max_len < 1) return 0;
+    return layer_ws(nullptr, cfg, max_len).bytes;
+}
+
+dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                          const float* x_in, float* x_out, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    TRY(check_cfg(c));
+    REQ(w && st && x_in && x_out, DV_ERR_NULL, "dv_decode_layer: NULL pointer");
+    REQ(w->ln1_g && w->ln1_b && w->ln2_g && w->ln2_b && w->w_qkv_t && w->b_qkv && w->w_o_t && w->b_o && w->w1_t &&
+            w->b1 && w->w2_t && w->b2,
+        DV_ERR_NULL, "dv_decode_layer: weight pointer NULL");
+    REQ((c->flags & DV_DENSE_ATTN) || (w->pa1_t && w->pa2_t), DV_ERR_NULL, "dv_decode_layer: head predictor NULL");
+    REQ((c->flags & DV_DENSE_MLP) || (w->pm1_t && w->pm2_t), DV_ERR_NULL, "dv_decode_layer: neuron predictor NULL");
+    const dv_kv_state& kv = st->kv;
+    REQ(kv.k_cache && kv.v_cache, DV_ERR_NULL, "dv_decode_layer: KV cache NULL");
+    REQ(kv.max_len >= 1 && kv.pos >= 0 && kv.pos < kv.max_len, DV_ERR_RANGE, "dv_decode_layer: pos=%d max_len=%d",
+        kv.pos, kv.max_len);
+    REQ(!(c->flags & DV_HOLE_FILL) || (kv.y_buf && kv.valid_upto), DV_ERR_NULL, "dv_decode_layer: hole fill state");
+    REQ(a16(w->w_qkv_t) && a16(w->w_o_t) && a16(w->w1_t) && a16(w->w2_t) && a16(x_in), DV_ERR_ALIGN,
+        "dv_decode_layer: weight alignment");
+    REQ(!overlap(x_out, (size_t)c->B * c->d * 4, x_in, (size_t)c->B * c->d * 4), DV_ERR_RANGE,
+        "dv_decode_layer: x_out overlaps x_in");
+    dv_kv_view view;
+    view.k_cache = kv.k_cache; view.v_cache = kv.v_cache; view.h = c->h; view.max_len = kv.max_len;
+    view.n_ctx = kv.pos + 1;
+    view.sel_idx = nullptr; view.sel_len = nullptr; view.sel_cap = 0; view.sel_end = 0;
+    if (c->flags & DV_KV_SELECT) {
+        view.sel_idx = st->sel_idx; view.sel_len = st->sel_len; view.sel_cap = st->sel_cap; view.sel_end = st->sel_end;
+        REQ(view.sel_idx, DV_ERR_NULL, "dv_decode_layer: DV_KV_SELECT without sel_idx");
+        TRY(check_view(&view, "dv_decode_layer"));
+    }
+    const LayerWs L = layer_ws(ws, c, kv.max_len);
+    REQ(ws && ws_bytes >= L.bytes, DV_ERR_WORKSPACE, "dv_decode_layer: workspace %zu < %zu", ws_bytes, L.bytes);
+
+    hipStream_t s = (hipStream_t)stream;
+    const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N;
+    // attention block
+    TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+    const int32_t* head_idx = nullptr;
+    int n_sel = h;
+    if (!(c->flags & DV_DENSE_ATTN)) {
+        int32_t* hi = st->head_idx_out ? st->head_idx_out : L.head_idx;
+        TRY(launch_predict(L.y, B, d, w->pa1_t, c->r_attn, w->pa2_t, h, c->wdt, c->pred_act, L.sA, L.hpart, s));
+        TRY(launch_topk(L.sA, B, h, c->k_heads, hi, s));
+        head_idx = hi;
+        n_sel = c->k_heads;
+    }
+    dv_kv_state kvs = kv;
+    if (!(c->flags & DV_HOLE_FILL)) {
+        kvs.y_buf = nullptr;
+        kvs.valid_upto = nullptr;
+    }
+    TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, L.qkv_cnt, s));
+    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, c->scale, 0, L.o, L.apart, s));
+    TRY(launch_axpy(w->w_o_t, c->wdt, d, h * dh, n_sel * dh, nullptr, head_idx, dh, L.o, n_sel * dh, false, B, w->b_o, x_in,
+                    L.hres, nullptr, L.xpart, L.axpy_cnt, s));
+    // MLP block
+    TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
+    const int32_t* idx = nullptr;
+    const int32_t* n_dev = nullptr;
+    int n_max = N;
+    if (!(c->flags & DV_DENSE_MLP)) {
+        TRY(launch_predict(L.y2, B, d, w->pm1_t, c->r_mlp, w->pm2_t, N, c->wdt, c->pred_act, L.sM, L.hpart, s));
+        if (B == 1) {
+            int32_t* ni = st->neuron_idx_out ? st->neuron_idx_out : L.nidx;
+            TRY(launch_topk(L.sM, 1, N, c->k_neurons, ni, s));
+            if (st->neuron_count_out) TRY(launch_set_i32(st->neuron_count_out, c->k_neurons, s));
+            idx = ni;
+            n_max = c->k_neurons;
+        } else {
+            int32_t* ui = st->neuron_idx_out ? st->neuron_idx_out : L.uidx;
+            int32_t* uc = st->neuron_count_out ? st->neuron_count_out : L.ucnt;
+            TRY(launch_topk(L.sM, B, N, c->k_neurons, L.nidx, s));
+            TRY(launch_union(L.nidx, B, c->k_neurons, N, ui, uc, s));
+            idx = ui;
+            n_dev = uc;
+            n_max = layer_nmax(c);
+        }
+    }
+    TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
+    return launch_axpy(w->w2_t, c->wdt, d, N, n_max, n_dev, idx, 1, L.a, n_max, (c->flags & DV_SKIP_NONPOS_FC2) != 0, B,
+                       w->b2, L.hres, x_out, st->fc2_rows_out, L.xpart, L.axpy_cnt, s);
+}
+
+}  // extern "C"

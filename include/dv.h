@@ -1,0 +1,290 @@
+/*
+ * dv.h -- C ABI of libdv, the decode step of contextual sparsity on AMD
+ * MI355X (gfx950).
+ *
+ * Pages cited:
+ *   DejaVu    "Deja Vu: Contextual Sparsity for Efficient LLMs at Inference
+ *             Time" (arXiv 2310.17157).
+ *   ByteCross "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
+ *             Decoding" (arXiv 2609.33889v1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device memory must be HIP device allocations on the
+ *   current device; scalars (sizes, counts, positions) are host values.
+ * - Every call validates its arguments on the host first.  On error nothing
+ *   is enqueued, a DV_ERR_* code is returned and dv_last_error() holds a
+ *   message for the calling thread.  A failed launch returns DV_ERR_HIP.
+ *   Faults inside a kernel surface at the caller's next synchronisation.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *   null stream) and returns without synchronising.  The library never
+ *   allocates, frees or synchronises.
+ * - Scratch memory is the caller's `ws` of at least the size the matching
+ *   *_workspace_bytes() query returns, 256-byte aligned.  It must be zero
+ *   filled before its first use; every call leaves its counters at zero
+ *   again, so one workspace serves any number of calls issued in order on
+ *   one stream.  Calls that overlap in time must use separate workspaces.
+ * - Weight pointers must be 16-byte aligned and a weight row (d elements)
+ *   must be a multiple of 16 bytes (d % 8 == 0 for fp16, d % 4 == 0 for
+ *   fp32), else DV_ERR_ALIGN.
+ * - Index sets are int32 and ascending, as dv_topk_select writes them.
+ * - Layouts are row-major.  Weights are stored so that each selected unit is
+ *   one contiguous run (DejaVu §4.4 "Memory coalescing": W1, W2 and W^O are
+ *   kept transposed):
+ *     w1_t, w2_t  [N][d]        row j = neuron j's fc1 / fc2 weights
+ *     w_qkv_t     [3][h][d_h][d] Q, K, V block of head i = [which][i]
+ *     w_o_t       [h*d_h][d]    rows i*d_h..i*d_h+d_h-1 = W_i^O
+ *     p1_t [r][d], p2_t [n_out][r]   predictor layers, transposed
+ *     K, V cache  fp16 [B][h][max_len][d_h]
+ *   Activations (x, y, q, o, scores) are fp32.
+ */
+#ifndef DV_H
+#define DV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DV_API_VERSION 1
+
+typedef enum {
+    DV_OK = 0,
+    DV_ERR_NULL = 1,        /* a required pointer is NULL */
+    DV_ERR_SHAPE = 2,       /* a size is out of its valid range or sizes disagree */
+    DV_ERR_DTYPE = 3,       /* unknown dtype, activation or mode value */
+    DV_ERR_ALIGN = 4,       /* pointer or row not 16-byte aligned */
+    DV_ERR_RANGE = 5,       /* k > n, pos >= max_len, count > capacity ... */
+    DV_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than its query */
+    DV_ERR_UNSUPPORTED = 7, /* a valid combination this build does not implement */
+    DV_ERR_HIP = 8          /* a HIP launch failed */
+} dv_status;
+
+typedef enum { DV_F32 = 0, DV_F16 = 1 } dv_dtype;
+typedef enum { DV_ACT_NONE = 0, DV_ACT_RELU = 1 } dv_act;
+typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
+
+/* dv_sparse_mlp / dv_decode_layer flags */
+#define DV_SKIP_NONPOS_FC2 0x1u  /* do not read fc2 rows of neurons whose ReLU output is 0 */
+#define DV_DENSE_ATTN      0x2u  /* every head, no head predictor */
+#define DV_DENSE_MLP       0x4u  /* every neuron, no neuron predictor */
+#define DV_HOLE_FILL       0x8u  /* recompute skipped heads' K/V (DejaVu §4.2) */
+#define DV_KV_SELECT       0x10u /* attend to retained KV positions only (ByteCross §4.1) */
+
+int dv_api_version(void);
+const char* dv_status_str(int status);
+/* Message of the last error returned on the calling thread ("" if none). */
+const char* dv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * LayerNorm: y[b] = (x[b] - mean) / sqrt(var + eps) * gamma + beta, the
+ * normalisation before each block (DejaVu App. B), population variance.
+ * x, y: device fp32 [B][d]; gamma, beta: device fp32 [d].  y may alias x.
+ */
+dv_status dv_layernorm(const float* x, int B, int d, const float* gamma, const float* beta,
+                       float eps, float* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparsity predictor, DejaVu §4.1 (MLP) and §4.2 (heads, same
+ * architecture): scores[b] = act(y[b] P1) P2, a two-layer fully connected
+ * network without biases, one score per neuron or head.
+ *   y       device fp32 [B][d]
+ *   p1_t    device [r][d]      (P1 transposed), dtype wdt
+ *   p2_t    device [n_out][r]  (P2 transposed), dtype wdt
+ *   act     dv_act applied to the r hidden units
+ *   scores  device fp32 [B][n_out]
+ * Accumulation is fp32.  1 <= B <= 16.
+ */
+size_t dv_predict_workspace_bytes(int B, int d, int r, int wdt);
+dv_status dv_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t,
+                     int n_out, int wdt, int act, float* scores, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k selection of the set S (DejaVu §2.3: S_M subset of [4d], S_A
+ * subset of [h], under a budget on its size).  Row b of `scores` yields the
+ * k indices that come first in the order: score descending, ties to the
+ * lower index, NaN after every number (+0 and -0 tie).  Written ascending.
+ *   scores      device fp32 [B][n]
+ *   idx         device int32 [B][k]
+ *   union_idx   device int32 [n] or NULL: ascending union of the B sets
+ *               (DejaVu §5.2 / App. C.1, the batch union), when B > 1
+ *   union_count device int32 [1] or NULL: size of that union
+ * 0 <= k <= n <= 65536; k > n gives DV_ERR_RANGE.  1 <= B <= 64.
+ */
+size_t dv_topk_workspace_bytes(int B, int n, int k);
+dv_status dv_topk_select(const float* scores, int B, int n, int k, int32_t* idx,
+                         int32_t* union_idx, int32_t* union_count, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse MLP, DejaVu §2.3 Eq. (1) with OPT's biases:
+ *   a[b][u]  = max(0, w1_t[idx[u]] . y[b] + b1[idx[u]])
+ *   out[b]   = residual[b] + b2 + sum_u a[b][u] * w2_t[idx[u]]
+ * Every row b uses the same set idx (a batch passes the union).  With
+ * DV_SKIP_NONPOS_FC2 the fc2 rows of neurons with a[b][u] == 0 for every b
+ * are not read (the second layer is sparsified by the ReLU, DejaVu §2.3).
+ *   y        device fp32 [B][d]
+ *   w1_t, w2_t device [N][d]; b1 device [N]; b2 device [d]; dtype wdt
+ *   idx      device int32 [n_idx_max] ascending, or NULL = every neuron
+ *            (then n_idx_max must equal N)
+ *   n_idx_dev device int32 [1] or NULL: the count actually used, <= n_idx_max
+ *   residual device fp32 [B][d] or NULL
+ *   out      device fp32 [B][d] (must not alias y or residual)
+ *   act_out  device fp32 [B][n_idx_max] or NULL: the activations a
+ *   fc2_rows device int32 [1] or NULL: incremented by the number of fc2
+ *            rows read (the caller zeroes it)
+ * 1 <= B <= 16.
+ */
+size_t dv_sparse_mlp_workspace_bytes(int B, int d, int n_idx_max, int wdt);
+dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, const void* b1,
+                        const void* w2_t, const void* b2, int wdt, const int32_t* idx,
+                        int n_idx_max, const int32_t* n_idx_dev, const float* residual,
+                        float* out, float* act_out, int32_t* fc2_rows, unsigned flags, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * KV state of one layer, updated by dv_sparse_attn_proj(DV_PROJ_QKV).
+ *   k_cache, v_cache  device fp16 [B][h][max_len][d_h]
+ *   pos               slot written by this step, 0 <= pos < max_len
+ *   y_buf             device fp32 [B][max_len][d]: every step's layer input,
+ *                     kept for heads that were not selected (DejaVu §4.2);
+ *                     NULL disables hole fill
+ *   valid_upto        device int32 [B][h]: last position whose K/V head i
+ *                     holds; NULL disables hole fill
+ * With hole fill, a selected head whose valid_upto < pos - 1 first gets its
+ * K/V at positions valid_upto+1 .. pos-1 recomputed from y_buf, then
+ * valid_upto = pos.  Without it, skipped slots keep their old contents.
+ */
+typedef struct {
+    void* k_cache;
+    void* v_cache;
+    int max_len;
+    int pos;
+    float* y_buf;
+    int32_t* valid_upto;
+} dv_kv_state;
+
+/* ------------------------------------------------------------------------
+ * Sparse attention projections, DejaVu §2.3 Eq. (2) / §4.2 / App. E.
+ * DV_PROJ_QKV: for each selected head i = head_idx[s]:
+ *     q[b][s] = W_i^Q y[b] + b^Q_i;  k, v likewise, rounded to fp16 (RNE)
+ *     and written to slot pos of head i; y[b] saved to y_buf[b][pos].
+ *   w_t  [3][h][d_h][d]; bias [3][h][d_h]; in = y [B][d]; out = q [B][n_sel][d_h];
+ *   residual unused; kv required.
+ * DV_PROJ_OUT: out[b] = residual[b] + bias + sum_s o[b][s] . W^O_{head_idx[s]}
+ *   w_t  [h*d_h][d]; bias [d]; in = o [B][n_sel][d_h]; out [B][d]; kv unused.
+ * head_idx device int32 [n_sel] ascending, or NULL = heads 0..n_sel-1 (dense).
+ * The head set is shared by the batch.  d_h in {32, 64, 128, 256}.
+ */
+size_t dv_attn_proj_workspace_bytes(int mode, int B, int d, int h, int d_h, int n_sel, int wdt);
+dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int32_t* head_idx,
+                              int n_sel, const void* w_t, const void* bias, int wdt,
+                              const float* in, const float* residual, float* out,
+                              const dv_kv_state* kv, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Which cached positions attention reads.
+ *   n_ctx    positions 0..n_ctx-1 exist (the current token included)
+ *   sel_idx  device int32 [B][h][sel_cap] or NULL (dense): per head, the
+ *            retained positions (ascending, each < sel_end) of the KV
+ *            branch (ByteCross §4.1: top positions per KV head kept)
+ *   sel_len  device int32 [B][h]: entries of sel_idx in use (<= sel_cap)
+ *   sel_end  positions sel_end..n_ctx-1 are always read (the cache keeps
+ *            receiving entries, ByteCross §3.2)
+ */
+typedef struct {
+    const void* k_cache;
+    const void* v_cache;
+    int h;
+    int max_len;
+    int n_ctx;
+    const int32_t* sel_idx;
+    const int32_t* sel_len;
+    int sel_cap;
+    int sel_end;
+} dv_kv_view;
+
+/* ------------------------------------------------------------------------
+ * Split-K decode attention over the selected heads, DejaVu §2.3 Eq. (2):
+ *   o[b][s] = softmax(scale * q[b][s] . K_i^T) V_i,  i = head_idx[s],
+ * over the positions of `kv`.  The positions are split into num_splits
+ * ranges read in parallel; each yields (max, sum of exp, weighted V) and a
+ * combine step merges them (the split-K kernel ByteCross §4.1 times every
+ * mode with).  Empty ranges contribute nothing; a head with no position
+ * gets o = 0.
+ *   q  device fp32 [B][n_sel][d_h];  o device fp32 [B][n_sel][d_h]
+ *   head_idx as in dv_sparse_attn_proj;  num_splits 0 = chosen by the library
+ */
+size_t dv_splitk_workspace_bytes(int B, int n_sel, int d_h, int max_positions, int num_splits);
+dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
+                         const dv_kv_view* kv, float scale, int num_splits, float* o, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention-scored KV selection scores, ByteCross §4.1 / App. A: the
+ * attention each cached position receives from the last n_obs prompt
+ * queries (query w at position n - n_obs + w attends causally), summed over
+ * those queries, then a centred width-`width` moving average (zero outside
+ * [0, n), divided by width); positions < n_sink and >= n - n_window are
+ * set to +inf so that a following dv_topk_select(k = budget) keeps them.
+ *   q_obs   device fp16 [B][h][n_obs][d_h]
+ *   scores  device fp32 [B][h][n]
+ * width odd, 1 <= width <= 63.
+ */
+size_t dv_kv_score_workspace_bytes(int B, int h, int n, int n_obs);
+dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv,
+                      float scale, int n_sink, int n_window, int width, float* scores, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * One decode step of one pre-LN OPT-style layer, DejaVu §4.3 sequential
+ * form: y = LN1(x); S_A = top-k_heads(SP_A(y)); h = x + MHA_{S_A}(y);
+ * y2 = LN2(h); S_M = top-k_neurons(SP_M(y2)); x_out = h + MLP_{S_M}(y2).
+ * A batch uses the union of its rows' neuron sets (DejaVu App. C.1); head
+ * sparsity needs B == 1 in this build (DV_ERR_UNSUPPORTED otherwise).
+ */
+typedef struct {
+    int B, d, h, d_h, N;
+    int r_attn, r_mlp;        /* predictor ranks */
+    int k_heads, k_neurons;   /* budgets (ignored with DV_DENSE_ATTN / DV_DENSE_MLP) */
+    int wdt;                  /* dv_dtype of every weight */
+    int pred_act;             /* dv_act of the predictors' hidden layer */
+    float eps;                /* LayerNorm epsilon */
+    float scale;              /* attention score scale */
+    unsigned flags;           /* DV_* flags above */
+} dv_decode_cfg;
+
+typedef struct {
+    const float *ln1_g, *ln1_b, *ln2_g, *ln2_b;   /* fp32 [d] */
+    const void *w_qkv_t, *b_qkv;                   /* [3][h][d_h][d], [3][h][d_h] */
+    const void *w_o_t, *b_o;                       /* [h*d_h][d], [d] */
+    const void *w1_t, *b1, *w2_t, *b2;             /* [N][d], [N], [N][d], [d] */
+    const void *pa1_t, *pa2_t;                     /* [r_attn][d], [h][r_attn] */
+    const void *pm1_t, *pm2_t;                     /* [r_mlp][d], [N][r_mlp] */
+} dv_layer_weights;
+
+typedef struct {
+    dv_kv_state kv;             /* the cache and hole-fill state */
+    const int32_t* sel_idx;     /* DV_KV_SELECT: as in dv_kv_view */
+    const int32_t* sel_len;
+    int sel_cap;
+    int sel_end;
+    /* optional device outputs (NULL to skip) */
+    int32_t* head_idx_out;      /* [k_heads] selected heads */
+    int32_t* neuron_idx_out;    /* [min(N, B*k_neurons)] selected (union) neurons */
+    int32_t* neuron_count_out;  /* [1] number of entries in neuron_idx_out */
+    int32_t* fc2_rows_out;      /* [1] incremented by the fc2 rows read */
+} dv_layer_state;
+
+size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len);
+dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* cfg,
+                          const dv_layer_state* st, const float* x_in, float* x_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DV_H */

@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every entry point include/dv.h declares,
+and rejects bad arguments on the host before any launch (no GPU needed: every
+call here fails validation, so nothing reaches the device)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dv.h")
+LIB = os.path.join(ROOT, "contextual_sparsity_decoding_amd", "libdv.so")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def dv():
+    if not os.path.exists(LIB):
+        pytest.fail("libdv.so is not built (python -m contextual_sparsity_decoding_amd.build)")
+    from contextual_sparsity_decoding_amd import dv as mod
+    return mod
+
+
+def test_every_declared_symbol_is_exported(dv):
+    names = declared()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(dv.lib, n), n
+    assert set(dv.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings(dv):
+    assert dv.lib.dv_api_version() == 1
+    for i, s in enumerate(dv.STATUS):
+        assert dv.lib.dv_status_str(i).decode() == s
+
+
+# fake device addresses: validation rejects these calls before touching them
+P = 1 << 20          # 16-byte aligned, never dereferenced
+Q = (1 << 20) + 8    # misaligned
+
+
+def err(dv):
+    return dv.lib.dv_last_error().decode()
+
+
+def test_predict_validation(dv):
+    L = dv.lib
+    s = L.dv_predict(0, 1, 64, P, 16, P, 10, dv.DV_F16, dv.DV_ACT_RELU, P, P, 1 << 20, 0)
+    assert s == 1 and "NULL" in err(dv)
+    assert L.dv_predict(P, 1, 64, P, 16, P, 10, 7, 1, P, P, 1 << 20, 0) == 3
+    assert L.dv_predict(P, 1, 64, P, 16, P, 10, dv.DV_F16, 9, P, P, 1 << 20, 0) == 3
+    assert L.dv_predict(P, 0, 64, P, 16, P, 10, dv.DV_F16, 1, P, P, 1 << 20, 0) == 2
+    assert L.dv_predict(P, 17, 64, P, 16, P, 10, dv.DV_F16, 1, P, P, 1 << 20, 0) == 2
+    assert L.dv_predict(P, 1, 60, P, 16, P, 10, dv.DV_F16, 1, P, P, 1 << 20, 0) == 4   # 120-byte rows
+    assert L.dv_predict(P, 1, 64, Q, 16, P, 10, dv.DV_F16, 1, P, P, 1 << 20, 0) == 4
+    assert L.dv_predict(P, 1, 64, P, 16, P, 10, dv.DV_F16, 1, P, P, 0, 0) == 6
+    assert L.dv_predict_workspace_bytes(1, 5120, 128, dv.DV_F16) > 0
+
+
+def test_topk_validation(dv):
+    L = dv.lib
+    assert L.dv_topk_select(P, 1, 10, 11, P, 0, 0, 0, 0, 0) == 5
+    assert L.dv_topk_select(P, 1, 10, -1, P, 0, 0, 0, 0, 0) == 5
+    assert L.dv_topk_select(0, 1, 10, 3, P, 0, 0, 0, 0, 0) == 1
+    assert L.dv_topk_select(P, 1, 70000, 3, P, 0, 0, 0, 0, 0) == 2
+    assert L.dv_topk_select(P, 65, 10, 3, P, 0, 0, 0, 0, 0) == 2
+    assert L.dv_topk_select(P, 2, 10, 3, P, P, 0, 0, 0, 0) == 1     # union needs both outputs
+    assert L.dv_topk_select(0, 1, 10, 0, 0, 0, 0, 0, 0, 0) == 0     # k = 0 is empty, nothing to launch
+
+
+def test_sparse_mlp_validation(dv):
+    L = dv.lib
+    args = dict(y=P, B=1, d=64, N=256, w1=P, b1=P, w2=P, b2=P, wdt=dv.DV_F16, idx=P, nmax=32, ndev=0, res=0,
+                out=P + 4096, act=0, rows=0, flags=0, ws=P, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dv_sparse_mlp(a["y"], a["B"], a["d"], a["N"], a["w1"], a["b1"], a["w2"], a["b2"], a["wdt"],
+                               a["idx"], a["nmax"], a["ndev"], a["res"], a["out"], a["act"], a["rows"], a["flags"],
+                               a["ws"], a["wsb"], 0)
+    assert call(y=0) == 1
+    assert call(wdt=5) == 3
+    assert call(B=0) == 2
+    assert call(nmax=257) == 5
+    assert call(idx=0) == 2                 # NULL idx means every neuron: n_idx_max must be N
+    assert call(flags=0x40) == 3
+    assert call(d=60) == 4
+    assert call(w2=Q) == 4
+    assert call(out=P) == 5                 # out aliases y
+    assert call(wsb=16) == 6
+    assert L.dv_sparse_mlp_workspace_bytes(1, 5120, 2048, dv.DV_F16) > 0
+
+
+def test_attn_proj_validation(dv):
+    L = dv.lib
+    kv = dv.KVState(P, P, 100, 100, 0, 0)          # pos == max_len
+    assert L.dv_sparse_attn_proj(0, 1, 64, 4, 16, P, 2, P, P, 1, P, 0, P + 4096, C.byref(kv), P, 1 << 20, 0) == 2
+    assert L.dv_sparse_attn_proj(0, 1, 64, 4, 64, P, 2, P, P, 1, P, 0, P + 4096, C.byref(kv), P, 1 << 20, 0) == 5
+    assert L.dv_sparse_attn_proj(0, 1, 64, 4, 64, P, 5, P, P, 1, P, 0, P + 4096, None, P, 1 << 20, 0) == 5
+    assert L.dv_sparse_attn_proj(0, 1, 64, 4, 64, P, 2, P, P, 1, P, 0, P + 4096, None, P, 1 << 20, 0) == 1
+    assert L.dv_sparse_attn_proj(3, 1, 64, 4, 64, P, 2, P, P, 1, P, 0, P + 4096, None, P, 1 << 20, 0) == 3
+    assert L.dv_sparse_attn_proj(1, 1, 64, 4, 64, P, 2, P, P, 1, P, 0, P + 4096, None, P, 0, 0) == 6
+
+
+def test_splitk_and_score_validation(dv):
+    L = dv.lib
+    v = dv.KVView(P, P, 4, 100, 101, 0, 0, 0, 0)    # n_ctx > max_len
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 5
+    v = dv.KVView(P, P, 4, 100, 50, P, P, 40, 30)    # sel_cap > sel_end
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 5
+    v = dv.KVView(P, P, 4, 100, 50, 0, 0, 0, 0)
+    assert L.dv_splitk_attn(P, 1, 48, P, 2, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 2
+    assert L.dv_splitk_attn(P, 1, 64, P, 5, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 5
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 0, 0) == 6
+    assert L.dv_kv_score(P, 1, 4, 64, 8, C.byref(v), 0.1, 4, 8, 6, P, P, 1 << 20, 0) == 5   # even width
+    assert L.dv_kv_score(P, 1, 4, 64, 51, C.byref(v), 0.1, 4, 8, 7, P, P, 1 << 20, 0) == 5  # n_obs > n
+
+
+def test_decode_layer_validation(dv):
+    L = dv.lib
+    cfg = dv.DecodeCfg(B=2, d=64, h=4, d_h=16, N=256, r_attn=16, r_mlp=16, k_heads=2, k_neurons=32,
+                       wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.25, flags=0)
+    assert L.dv_decode_workspace_bytes(C.byref(cfg), 32) == 0          # d_h = 16 unsupported
+    cfg.d_h = 64
+    w = dv.LayerWeights(*([P] * 16))
+    st = dv.LayerState()
+    st.kv = dv.KVState(P, P, 32, 5, 0, 0)
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 7  # heads, B=2
+    cfg.B = 1
+    assert L.dv_decode_workspace_bytes(C.byref(cfg), 32) > 0
+    cfg.flags = 0x8
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 1  # hole state
+    cfg.flags = 0x100
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 3
+    cfg.flags = 0
+    cfg.k_neurons = 300
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
