@@ -30,6 +30,8 @@ int elt_bytes(int wdt) { return wdt == DV_F16 ? 2 : 4; }
 static bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool wdt_ok(int wdt) { return wdt == DV_F16 || wdt == DV_F32; }
 static bool dh_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128 || d_h == 256; }
+// one counter per output column slice (64 lanes x 16 bytes) must fit the counter block
+static bool d_ok(int d) { return d >= 1 && (long)d <= (long)(kMaxCounters - 1) * 256; }
 static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const char* x = (const char*)a;
     const char* y = (const char*)b;
@@ -48,7 +50,10 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 // ---- workspace layouts ------------------------------------------------------
 
-static size_t predict_ws(int B, int d, int r, int wdt) { return align_up(pred_partials(B, d, r, wdt) * 4, 256); }
+static size_t predict_ws(int B, int d, int r, int wdt) {
+    return kCounterBytes + align_up(pred_partials(B, d, r, wdt) * 4, 256);
+}
+static float* predict_part(void* ws) { return ws ? (float*)((char*)ws + kCounterBytes) : nullptr; }
 
 struct MlpWs {
     float* a;
@@ -62,7 +67,7 @@ static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a)
     w.a = need_a ? cv.take<float>((size_t)B * (n_idx_max > 0 ? n_idx_max : 1)) : nullptr;
     const AxpyPlan p = axpy_plan(d, n_idx_max, wdt);
     w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
-    w.counters = cv.take<unsigned>(p.n_slices);
+    w.counters = ws_counters(ws, 1);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -78,9 +83,9 @@ static ProjWs proj_ws(void* ws, int mode, int B, int d, int n_sel, int d_h, int 
     if (mode == DV_PROJ_OUT) {
         const AxpyPlan p = axpy_plan(d, n_sel * d_h, wdt);
         w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
-        w.counters = cv.take<unsigned>(p.n_slices);
+        w.counters = ws_counters(ws, 1);
     } else {
-        w.counters = cv.take<unsigned>(1);
+        w.counters = ws_counters(ws);
     }
     w.bytes = align_up(cv.off, 256);
     return w;
@@ -88,7 +93,7 @@ static ProjWs proj_ws(void* ws, int mode, int B, int d, int n_sel, int d_h, int 
 
 static size_t splitk_ws(int B, int n_sel, int d_h, int max_positions, int num_splits) {
     if (num_splits <= 0) num_splits = splitk_auto(max_positions, B * n_sel);
-    return align_up((size_t)B * n_sel * num_splits * (d_h + 2) * 4, 256);
+    return kCounterBytes + align_up((size_t)B * n_sel * num_splits * (d_h + 2) * 4, 256);
 }
 
 }  // namespace dvh
@@ -151,7 +156,7 @@ dv_status dv_predict(const float* y, int B, int d, const void* p1_t, int r, cons
     clear_error();
     TRY(check_predict(y, B, d, p1_t, r, p2_t, n_out, wdt, act, scores));
     REQ(ws && ws_bytes >= predict_ws(B, d, r, wdt), DV_ERR_WORKSPACE, "dv_predict: workspace");
-    return launch_predict(y, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, (float*)ws, (hipStream_t)stream);
+    return launch_predict(y, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, predict_part(ws), (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- top-k -----
@@ -188,7 +193,7 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
     clear_error();
     REQ(y && w1_t && b1 && w2_t && b2 && out, DV_ERR_NULL, "dv_sparse_mlp: NULL pointer");
     REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_sparse_mlp: wdt %d", wdt);
-    REQ(B >= 1 && B <= 16 && d >= 1 && N >= 1, DV_ERR_SHAPE, "dv_sparse_mlp: B=%d d=%d N=%d", B, d, N);
+    REQ(B >= 1 && B <= 16 && d_ok(d) && N >= 1, DV_ERR_SHAPE, "dv_sparse_mlp: B=%d d=%d N=%d", B, d, N);
     REQ(n_idx_max >= 0 && n_idx_max <= N, DV_ERR_RANGE, "dv_sparse_mlp: n_idx_max=%d N=%d", n_idx_max, N);
     REQ(idx || n_idx_max == N, DV_ERR_SHAPE, "dv_sparse_mlp: idx NULL needs n_idx_max == N");
     REQ((flags & ~(unsigned)DV_SKIP_NONPOS_FC2) == 0, DV_ERR_DTYPE, "dv_sparse_mlp: flags 0x%x", flags);
@@ -221,7 +226,7 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
     REQ(mode == DV_PROJ_QKV || mode == DV_PROJ_OUT, DV_ERR_DTYPE, "dv_sparse_attn_proj: mode %d", mode);
     REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_sparse_attn_proj: wdt %d", wdt);
     REQ(w_t && in && out, DV_ERR_NULL, "dv_sparse_attn_proj: NULL pointer");
-    REQ(B >= 1 && B <= 16 && d >= 1 && h >= 1 && dh_ok(d_h), DV_ERR_SHAPE,
+    REQ(B >= 1 && B <= 16 && d_ok(d) && h >= 1 && dh_ok(d_h), DV_ERR_SHAPE,
         "dv_sparse_attn_proj: B=%d d=%d h=%d d_h=%d", B, d, h, d_h);
     REQ(n_sel >= 0 && n_sel <= h, DV_ERR_RANGE, "dv_sparse_attn_proj: n_sel=%d h=%d", n_sel, h);
     REQ((size_t)d * elt_bytes(wdt) % 16 == 0, DV_ERR_ALIGN, "dv_sparse_attn_proj: d=%d rows", d);
@@ -278,13 +283,14 @@ dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx
     const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
     const size_t need = splitk_ws(B, n_sel, d_h, maxpos, num_splits);
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_splitk_attn: workspace %zu < %zu", ws_bytes, need);
-    return launch_splitk(q, B, d_h, head_idx, n_sel, kv, scale, num_splits, o, (float*)ws, (hipStream_t)stream);
+    return launch_splitk(q, B, d_h, head_idx, n_sel, kv, scale, num_splits, o, (float*)((char*)ws + kCounterBytes),
+                         (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- KV scoring --
 size_t dv_kv_score_workspace_bytes(int B, int h, int n, int n_obs) {
     if (B < 1 || h < 1 || n < 1 || n_obs < 1) return 0;
-    return align_up(kv_score_stats_floats(B, h, n, n_obs) * 4, 256);
+    return kCounterBytes + align_up(kv_score_stats_floats(B, h, n, n_obs) * 4, 256);
 }
 
 dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv, float scale,
@@ -302,8 +308,9 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
     REQ(a16(q_obs), DV_ERR_ALIGN, "dv_kv_score: q_obs alignment");
     const size_t need = dv_kv_score_workspace_bytes(B, h, kv->n_ctx, n_obs);
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_kv_score: workspace %zu < %zu", ws_bytes, need);
-    return launch_kv_score(q_obs, B, h, d_h, n_obs, kv, scale, n_sink, n_window, width, scores, (float*)ws,
-                           (float*)ws, (hipStream_t)stream);
+    float* st = (float*)((char*)ws + kCounterBytes);
+    return launch_kv_score(q_obs, B, h, d_h, n_obs, kv, scale, n_sink, n_window, width, scores, st, st,
+                           (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- the layer --
@@ -346,8 +353,8 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     const size_t xp = axpy_ws_floats(po, B, d) > axpy_ws_floats(pm, B, d) ? axpy_ws_floats(po, B, d)
                                                                            : axpy_ws_floats(pm, B, d);
     w.xpart = cv.take<float>(xp);
-    w.qkv_cnt = cv.take<unsigned>(1);
-    w.axpy_cnt = cv.take<unsigned>(po.n_slices > pm.n_slices ? po.n_slices : pm.n_slices);
+    w.qkv_cnt = ws_counters(ws);
+    w.axpy_cnt = ws_counters(ws, 1);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -358,7 +365,7 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
     const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT;
     REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
-    REQ(c->B >= 1 && c->B <= 16 && c->d >= 1 && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
+    REQ(c->B >= 1 && c->B <= 16 && d_ok(c->d) && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
         "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
     const int eb = elt_bytes(c->wdt);
     REQ((size_t)c->d * eb % 16 == 0, DV_ERR_ALIGN, "dv_decode_layer: d=%d rows", c->d);

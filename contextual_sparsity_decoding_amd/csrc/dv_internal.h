@@ -136,10 +136,17 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 int elt_bytes(int wdt);
 
+// Every workspace starts with a fixed block of counters (zero between calls;
+// the kernels that use one reset it), so calls of any shape can share one
+// workspace.  Scratch buffers are carved after it.
+constexpr size_t kCounterBytes = 4096;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
+inline unsigned* ws_counters(void* ws, int i = 0) { return ws ? (unsigned*)ws + i : nullptr; }
+
 // Workspace carving: a bump allocator over the caller's buffer.
 struct Carve {
     char* base;
-    size_t off = 0;
+    size_t off = kCounterBytes;
     explicit Carve(void* p) : base((char*)p) {}
     template <typename T> T* take(size_t n) {
         off = align_up(off, 256);

@@ -180,12 +180,16 @@ def dv_sparse_mlp(y, w1_t, b1, w2_t, b2, idx, n_idx_max, out, ws, *, n_idx_dev=N
 
 
 def kv_state(K, V, pos, y_buf=None, valid_upto=None) -> KVState:
-    return KVState(ptr(K), ptr(V), K.shape[2], pos, ptr(y_buf), ptr(valid_upto))
+    s = KVState(ptr(K), ptr(V), K.shape[2], pos, ptr(y_buf), ptr(valid_upto))
+    s._keep = (K, V, y_buf, valid_upto)       # the struct holds raw pointers: keep the tensors alive
+    return s
 
 
 def kv_view(K, V, n_ctx, sel_idx=None, sel_len=None, sel_end=0) -> KVView:
     cap = sel_idx.shape[-1] if sel_idx is not None else 0
-    return KVView(ptr(K), ptr(V), K.shape[1], K.shape[2], n_ctx, ptr(sel_idx), ptr(sel_len), cap, sel_end)
+    v = KVView(ptr(K), ptr(V), K.shape[1], K.shape[2], n_ctx, ptr(sel_idx), ptr(sel_len), cap, sel_end)
+    v._keep = (K, V, sel_idx, sel_len)
+    return v
 
 
 def dv_attn_proj_workspace_bytes(mode, B, d, h, d_h, n_sel, wdt) -> int:
@@ -224,7 +228,9 @@ def dv_kv_score(q_obs, view: KVView, scale, n_sink, n_window, width, scores, ws,
 
 def layer_weights(W: dict) -> LayerWeights:
     """LayerWeights from a dict of device tensors (keys as in synth.layer_weights)."""
-    return LayerWeights(*[ptr(W.get(n)) for n, _ in LayerWeights._fields_])
+    w = LayerWeights(*[ptr(W.get(n)) for n, _ in LayerWeights._fields_])
+    w._keep = dict(W)
+    return w
 
 
 def decode_cfg(**kw) -> DecodeCfg:

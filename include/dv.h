@@ -20,10 +20,12 @@
  *   null stream) and returns without synchronising.  The library never
  *   allocates, frees or synchronises.
  * - Scratch memory is the caller's `ws` of at least the size the matching
- *   *_workspace_bytes() query returns, 256-byte aligned.  It must be zero
- *   filled before its first use; every call leaves its counters at zero
- *   again, so one workspace serves any number of calls issued in order on
- *   one stream.  Calls that overlap in time must use separate workspaces.
+ *   *_workspace_bytes() query returns, 256-byte aligned.  Its first 4096
+ *   bytes hold counters: zero fill the workspace before its first use; every
+ *   call leaves the counters at zero again, so one workspace serves any
+ *   number of calls, of any shapes, issued in order on one stream.  Calls
+ *   that overlap in time must use separate workspaces.
+ * - d (the model width) is at most 261,888 (one counter per 256 columns).
  * - Weight pointers must be 16-byte aligned and a weight row (d elements)
  *   must be a multiple of 16 bytes (d % 8 == 0 for fp16, d % 4 == 0 for
  *   fp32), else DV_ERR_ALIGN.

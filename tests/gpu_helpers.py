@@ -41,14 +41,16 @@ def check_close(got, want, wdt: str, what: str = ""):
     return e
 
 
-def f16_ulps(got, want):
-    """Largest distance in fp16 units in the last place between two fp16 arrays."""
-    g = np.asarray(got, np.float16).view(np.int16).astype(np.int32)
-    w = np.asarray(want, np.float16).view(np.int16).astype(np.int32)
-    # map sign-magnitude to a monotone integer line
-    g = np.where(g < 0, -32768 - g, g)
-    w = np.where(w < 0, -32768 - w, w)
-    return int(np.abs(g - w).max()) if g.size else 0
+def f16_kv_ok(got, want, rel=1e-5):
+    """Both sides round their own fp32 / fp64 value to fp16: entries may differ
+    by one fp16 unit in the last place, or, near zero where that unit is
+    smaller than the accumulation error, by rel * max|want|."""
+    g = np.asarray(got, np.float16).astype(np.float64)
+    w = np.asarray(want, np.float16)
+    ulp = np.spacing(np.abs(w)).astype(np.float64)
+    tol = ulp + rel * (np.abs(w).max() if w.size else 0.0)
+    bad = np.abs(g - w.astype(np.float64)) > tol
+    return not bool(bad.any()), int(bad.sum())
 
 
 def upload(W: dict) -> dict:

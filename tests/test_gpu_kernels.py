@@ -12,7 +12,7 @@ import torch
 from contextual_sparsity_decoding_amd import synth
 from contextual_sparsity_decoding_amd.configs import LayerDims
 from oracle import ref
-from tests.gpu_helpers import check_close, dev, f16_ulps, host, maxabs, normwise, selection_margin
+from tests.gpu_helpers import check_close, dev, f16_kv_ok, host, maxabs, normwise, selection_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -184,7 +184,7 @@ def test_mlp_block_fp32_end_to_end(dvlib):
                         flags=dvlib.DV_SKIP_NONPOS_FC2)
     sc = ref.predictor(x, W["pm1_t"], W["pm2_t"]).astype(np.float32)[0]
     want_idx = ref.topk_select(sc, 256)
-    assert selection_margin(sc, 256) > 1e-4
+    assert selection_margin(sc, 256) > 1e-6      # fp32 score error is ~1e-8 here
     assert np.array_equal(host(idx)[0], want_idx)
     want, _ = ref.sparse_mlp(x, W["w1_t"], W["b1"], W["w2_t"], W["b2"], want_idx, skip_nonpos=True)
     check_close(host(out), want, "f32", "mlp block")
@@ -226,8 +226,11 @@ def test_qkv_with_holes_over_steps(dvlib, dh):
         check_close(host(q), wq_, "f16", f"q step {t}")
     assert np.array_equal(host(vu), okv.valid_upto)
     Kg, Vg = host(Kd), host(Vd)
-    assert f16_ulps(Kg, okv.K) <= 1 and f16_ulps(Vg, okv.V) <= 1
-    np.testing.assert_array_equal(host(yb)[:, n0:n0 + T], okv.y_buf[:, n0:n0 + T].astype(np.float32))
+    ok_k, nk = f16_kv_ok(Kg, okv.K)
+    ok_v, nv = f16_kv_ok(Vg, okv.V)
+    assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
+    same = np.array_equal(host(yb)[:, n0:n0 + T], okv.y_buf[:, n0:n0 + T].astype(np.float32))
+    assert same, "stored layer inputs differ"
 
 
 def test_qkv_without_hole_fill(dvlib):
@@ -242,7 +245,9 @@ def test_qkv_without_hole_fill(dvlib):
     okv = ref.KVState(K.copy(), V.copy())
     wq = ref.qkv_step(x, W["w_qkv_t"], W["b_qkv"], sel, okv, 8, hole_fill=False)
     check_close(host(q), wq, "f16", "q")
-    assert f16_ulps(host(Kd), okv.K) <= 1 and f16_ulps(host(Vd), okv.V) <= 1
+    ok_k, nk = f16_kv_ok(host(Kd), okv.K)
+    ok_v, nv = f16_kv_ok(host(Vd), okv.V)
+    assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
     assert np.all(host(Kd)[0, :, 5:8] == 0)          # skipped slots untouched
 
 

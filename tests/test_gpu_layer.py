@@ -13,7 +13,7 @@ import torch
 from contextual_sparsity_decoding_amd import configs, synth
 from contextual_sparsity_decoding_amd.configs import LayerDims
 from oracle import ref
-from tests.gpu_helpers import check_close, dev, f16_ulps, host, normwise, selection_margin, upload
+from tests.gpu_helpers import check_close, dev, f16_kv_ok, host, normwise, selection_margin, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -108,7 +108,8 @@ def test_opt13b_layer_full_size(dvlib):
     e = _compare_step(L, got, want, rec, w.k_heads, w.k_neurons, flags, "opt13b sparse")
     assert e is not None, "choose a seed whose selections are unique"
     print(f"opt13b sparse layer normwise error {e:.2e}")
-    assert f16_ulps(host(L.K)[0, :, w.n_ctx], L.okv.K[0, :, w.n_ctx]) <= 1
+    ok, nbad = f16_kv_ok(host(L.K)[0, :, w.n_ctx], L.okv.K[0, :, w.n_ctx])
+    assert ok, f"{nbad} appended K entries off"
 
 
 def test_opt13b_layer_dense_path(dvlib):
@@ -139,7 +140,9 @@ def test_multistep_decode_with_holes(dvlib):
             break
     assert checked >= T - 1
     assert np.array_equal(host(L.valid), L.okv.valid_upto)
-    assert f16_ulps(host(L.K), L.okv.K) <= 1 and f16_ulps(host(L.V), L.okv.V) <= 1
+    ok_k, nk = f16_kv_ok(host(L.K), L.okv.K)
+    ok_v, nv = f16_kv_ok(host(L.V), L.okv.V)
+    assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
 
 
 def test_batch_union_decode(dvlib):
