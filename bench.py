@@ -1,0 +1,270 @@
+"""Benchmark: sparse decode of one OPT-13B-shaped layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one decode token through one layer (d=5120, 40 heads x 128,
+d_ffn=20480 ReLU, fp16 weights, fp32 accumulate, 2048 cached tokens), with
+10% of neurons and 50% of heads selected by rank-128 predictors, hole fill
+on and fc2 rows of non-positive neurons skipped: LN -> head predictor ->
+top-k -> Q/K/V + KV append -> split-K attention -> W^O -> LN -> neuron
+predictor -> top-k -> fc1 -> fc2.  Four independent layer copies are used
+in turn so that the 256 MB Infinity Cache cannot serve repeated reads; each
+copy's position advances by one per step it takes.
+
+Prints one JSON line: decode tokens/s, effective HBM bandwidth on the bytes
+the step must read, the dominant kernel's roofline, the same library's dense
+path, and the CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+SEED = 1234
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--copies", type=int, default=4)
+    p.add_argument("--kernel-launches", type=int, default=64)
+    p.add_argument("--dense-steps", type=int, default=16)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "contextual_sparsity_decoding_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, digest: str):
+    """HBM traffic per launch from a committed PMC summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources") != digest:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Copy:
+    """One layer copy's weights and decode state on the device."""
+
+    def __init__(self, dv, torch, dims, n0, max_len, seed):
+        from contextual_sparsity_decoding_amd import synth
+        self.W = synth.layer_weights(dims, seed, layer=0)
+        K, V = synth.kv_cache(dims.h, dims.d_h, n0, max_len, seed)
+        self.host_K, self.host_V = K, V
+        self.Wd = {k: torch.from_numpy(v).cuda() for k, v in self.W.items()}
+        self.K, self.V = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+        self.y_buf = torch.zeros(1, max_len, dims.d, device="cuda")
+        self.valid = torch.full((1, dims.h), n0 - 1, dtype=torch.int32, device="cuda")
+        self.pos = n0
+        self.wts = dv.layer_weights(self.Wd)
+        self.st = dv.LayerState()
+        self.head_idx = torch.zeros(dims.h, dtype=torch.int32, device="cuda")
+        self.st.head_idx_out = self.head_idx.data_ptr()
+
+    def set_pos(self, dv, pos):
+        self.st.kv = dv.kv_state(self.K, self.V, pos, self.y_buf, self.valid)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from contextual_sparsity_decoding_amd import account, configs, dv
+
+    w = configs.OPT13B_LAYER
+    dims = w.dims
+    R = args.copies
+    total_steps = args.warmup + args.steps + args.dense_steps + 2
+    max_len = w.n_ctx + math.ceil(total_steps / R) + 8
+    torch.cuda.set_device(0)
+    copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
+    X = torch.from_numpy(np.ascontiguousarray(
+        __import__("contextual_sparsity_decoding_amd.synth", fromlist=["x"]).layer_inputs(
+            dims.d, total_steps, 1, SEED))).cuda()
+    out = torch.empty(1, dims.d, device="cuda")
+    flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2
+
+    def cfg(flags_):
+        dense_a = bool(flags_ & dv.DV_DENSE_ATTN)
+        dense_m = bool(flags_ & dv.DV_DENSE_MLP)
+        return dv.decode_cfg(B=1, d=dims.d, h=dims.h, d_h=dims.d_h, N=dims.N, r_attn=dims.r_attn,
+                             r_mlp=dims.r_mlp, k_heads=dims.h if dense_a else w.k_heads,
+                             k_neurons=dims.N if dense_m else w.k_neurons, wdt=dv.DV_F16,
+                             pred_act=dv.DV_ACT_RELU, eps=1e-5, scale=1 / math.sqrt(dims.d_h), flags=flags_)
+
+    sparse_cfg = cfg(flags)
+    dense_cfg = cfg(flags | dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP)
+    ws = dv.workspace(max(dv.dv_decode_workspace_bytes(sparse_cfg, max_len),
+                          dv.dv_decode_workspace_bytes(dense_cfg, max_len)))
+    fc2_rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = dv.stream_handle()
+    step_no = [0]
+
+    def run_step(c_cfg, count_rows=False):
+        s = step_no[0]
+        cp = copies[s % R]
+        cp.set_pos(dv, cp.pos)
+        cp.st.fc2_rows_out = fc2_rows.data_ptr() if count_rows else 0
+        dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(c_cfg), dv.C.byref(cp.st), X[s].data_ptr(),
+                               out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        cp.pos += 1
+        step_no[0] += 1
+
+    # warmup
+    for _ in range(args.warmup):
+        run_step(sparse_cfg)
+    torch.cuda.synchronize()
+    # timed sparse steps
+    fc2_rows.zero_()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run_step(sparse_cfg, count_rows=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    rows_per_step = int(fc2_rows.item()) / args.steps
+
+    # dense path through the same kernels
+    dense_ms = None
+    if args.dense_steps > 0:
+        run_step(dense_cfg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_steps):
+            run_step(dense_cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_steps
+
+    # dominant kernel: sparse Q/K/V projection, launch by launch on the same stream
+    qws = dv.workspace(dv.dv_attn_proj_workspace_bytes(0, 1, dims.d, dims.h, dims.d_h, w.k_heads, dv.DV_F16))
+    q = torch.empty(1, w.k_heads, dims.d_h, device="cuda")
+    yq = torch.from_numpy(np.ascontiguousarray(
+        __import__("contextual_sparsity_decoding_amd.synth", fromlist=["x"]).normal((1, dims.d), SEED, 9, "x"))).cuda()
+    durs = []
+    for i in range(args.kernel_launches + 4):
+        cp = copies[i % R]
+        kv = dv.kv_state(cp.K, cp.V, cp.pos - 1, cp.y_buf, cp.valid)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dv.dv_sparse_attn_proj(dv.DV_PROJ_QKV, dims.h, dims.d_h, cp.head_idx, w.k_heads, cp.Wd["w_qkv_t"],
+                               cp.Wd["b_qkv"], yq, q, qws, kv=kv)
+        b.record()
+        if i >= 4:
+            durs.append((a, b))
+    torch.cuda.synchronize()
+    qkv_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
+
+    # byte account
+    sb = account.step_bytes(dims, w.k_heads, w.k_neurons, n_att=w.n_ctx + 1, fc2_rows=rows_per_step)
+    db = account.step_bytes(dims, dims.h, dims.N, n_att=w.n_ctx + 1, fc2_rows=dims.N, head_pred=False,
+                            neuron_pred=False)
+    qkv_bytes = account.step_bytes(dims, w.k_heads, 0, 0, 0).qkv
+    achieved = qkv_bytes / (qkv_ms * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    traffic = read_traffic("traffic_qkv_opt13b_layer.txt", digest)
+
+    result = {
+        "metric": "decode tokens/s + effective HBM GB/s (% of peak) vs keep ratio, 1 GPU",
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 weights, f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) inputs and KV cache)",
+        "config": {
+            "workload": "opt13b-layer decode: d=5120, 40 heads x 128, d_ffn=20480 ReLU, fp16, batch 1, "
+                        "2048 cached tokens, keep 10% neurons (2048) and 50% heads (20), rank-128 predictors, "
+                        "4 rotating layer copies",
+            "global_batch": 1, "seq_len": w.n_ctx, "keep_neurons": 0.10, "keep_heads": 0.50,
+        },
+        "effective_hbm_GBps": round(sb.total / (ms_step * 1e-3) / 1e9, 1),
+        "pct_of_peak_hbm": round(100 * sb.total / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1),
+        "bytes_per_step": int(sb.total),
+        "fc2_rows_per_step": round(rows_per_step, 1),
+        "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 5),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "byte_bound_speedup": round(db.total / sb.total, 3),
+        "host_wall_ms_per_step": round(1000 * wall / args.steps, 4),
+        "roofline": {
+            "kernel": "k_qkv (sparse Q/K/V gather-GEMV + KV append)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+            "bytes_per_launch": int(qkv_bytes), "avg_launch_ms": round(qkv_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(copies[0], dims, w, X, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline(cp, dims, w, X, budget_s):
+    """The oracle, as it stands, on a sample of the same workload: decode
+    steps of layer copy 0 from its seeded state, until ~budget_s of CPU time."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    Xh = X.cpu().numpy()
+    L = cp.host_K.shape[2]
+    kv = ref.KVState(cp.host_K.copy(), cp.host_V.copy(), np.zeros((1, L, dims.d)), np.full((1, dims.h), w.n_ctx - 1))
+    steps, t0 = 0, time.perf_counter()
+    while steps == 0 or (time.perf_counter() - t0 < budget_s and steps < 16):
+        ref.decode_layer(Xh[steps], cp.W, kv, w.n_ctx + steps, k_heads=w.k_heads, k_neurons=w.k_neurons,
+                         scale=1 / math.sqrt(dims.d_h), skip_nonpos=True, hole_fill=True)
+        steps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(steps / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} decode steps of one OPT-13B-shaped layer (float64 NumPy oracle), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
