@@ -38,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=64)
-    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--kernel-launches", type=int, default=64)
     p.add_argument("--dense-steps", type=int, default=16)
@@ -77,7 +77,8 @@ def read_traffic(name: str, digest: str):
 
 
 class Copy:
-    """One layer copy's weights and decode state on the device."""
+    """One layer copy's weights and decode state on the device.  The decode
+    position lives on the device (pos_dev) so captured steps can be replayed."""
 
     def __init__(self, dv, torch, dims, n0, max_len, seed):
         from contextual_sparsity_decoding_amd import synth
@@ -88,14 +89,40 @@ class Copy:
         self.K, self.V = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
         self.y_buf = torch.zeros(1, max_len, dims.d, device="cuda")
         self.valid = torch.full((1, dims.h), n0 - 1, dtype=torch.int32, device="cuda")
-        self.pos = n0
+        self.pos_dev = torch.full((1,), n0, dtype=torch.int32, device="cuda")
         self.wts = dv.layer_weights(self.Wd)
         self.st = dv.LayerState()
+        # pos (the host field) is only the bound of the device position
+        self.st.kv = dv.kv_state(self.K, self.V, max_len - 1, self.y_buf, self.valid, self.pos_dev)
         self.head_idx = torch.zeros(dims.h, dtype=torch.int32, device="cuda")
         self.st.head_idx_out = self.head_idx.data_ptr()
 
-    def set_pos(self, dv, pos):
-        self.st.kv = dv.kv_state(self.K, self.V, pos, self.y_buf, self.valid)
+
+def capture_steps(dv, torch, copies, cfg, X, first, count, out, ws, fc2_rows):
+    """A HIP graph of `count` decode steps (step s uses copy s % R and input X[first + s])."""
+    g = torch.cuda.CUDAGraph()
+    R = len(copies)
+    with torch.cuda.graph(g):
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(count):
+            cp = copies[i % R]
+            cp.st.fc2_rows_out = fc2_rows.data_ptr() if fc2_rows is not None else 0
+            st = dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(cfg), dv.C.byref(cp.st),
+                                        X[first + i].data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+            if st != 0:
+                raise dv.DVError("dv_decode_layer", st)
+    return g
+
+
+def time_graph(torch, g):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - t0
 
 
 def main():
@@ -105,20 +132,21 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from contextual_sparsity_decoding_amd import account, configs, dv
+    from contextual_sparsity_decoding_amd import account, configs, dv, synth
 
     w = configs.OPT13B_LAYER
     dims = w.dims
     R = args.copies
-    total_steps = args.warmup + args.steps + args.dense_steps + 2
+    K = args.steps
+    warm_reps = max(1, math.ceil(args.warmup / K))
+    Kd = args.dense_steps
+    total_steps = (warm_reps + 1) * K + (2 * Kd if Kd > 0 else 0)
     max_len = w.n_ctx + math.ceil(total_steps / R) + 8
     torch.cuda.set_device(0)
     copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
-    X = torch.from_numpy(np.ascontiguousarray(
-        __import__("contextual_sparsity_decoding_amd.synth", fromlist=["x"]).layer_inputs(
-            dims.d, total_steps, 1, SEED))).cuda()
+    X = torch.from_numpy(np.ascontiguousarray(synth.layer_inputs(dims.d, K + max(Kd, 1), 1, SEED))).cuda()
     out = torch.empty(1, dims.d, device="cuda")
-    flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2
+    flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
 
     def cfg(flags_):
         dense_a = bool(flags_ & dv.DV_DENSE_ATTN)
@@ -133,59 +161,34 @@ def main():
     ws = dv.workspace(max(dv.dv_decode_workspace_bytes(sparse_cfg, max_len),
                           dv.dv_decode_workspace_bytes(dense_cfg, max_len)))
     fc2_rows = torch.zeros(1, dtype=torch.int32, device="cuda")
-    stream = dv.stream_handle()
-    step_no = [0]
 
-    def run_step(c_cfg, count_rows=False):
-        s = step_no[0]
-        cp = copies[s % R]
-        cp.set_pos(dv, cp.pos)
-        cp.st.fc2_rows_out = fc2_rows.data_ptr() if count_rows else 0
-        dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(c_cfg), dv.C.byref(cp.st), X[s].data_ptr(),
-                               out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
-        cp.pos += 1
-        step_no[0] += 1
-
-    # warmup
-    for _ in range(args.warmup):
-        run_step(sparse_cfg)
+    # K sparse steps captured once; warm-up replays, then one timed replay
+    g_sparse = capture_steps(dv, torch, copies, sparse_cfg, X, 0, K, out, ws, fc2_rows)
+    for _ in range(warm_reps):
+        g_sparse.replay()
     torch.cuda.synchronize()
-    # timed sparse steps
     fc2_rows.zero_()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        run_step(sparse_cfg, count_rows=True)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    rows_per_step = int(fc2_rows.item()) / args.steps
+    ms_total, wall = time_graph(torch, g_sparse)
+    ms_step = ms_total / K
+    rows_per_step = int(fc2_rows.item()) / K
 
     # dense path through the same kernels
     dense_ms = None
-    if args.dense_steps > 0:
-        run_step(dense_cfg)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.dense_steps):
-            run_step(dense_cfg)
-        e1.record()
-        torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1) / args.dense_steps
+    if Kd > 0:
+        g_dense = capture_steps(dv, torch, copies, dense_cfg, X, 0, Kd, out, ws, None)
+        g_dense.replay()
+        dense_ms = time_graph(torch, g_dense)[0] / Kd
 
     # dominant kernel: sparse Q/K/V projection, launch by launch on the same stream
     qws = dv.workspace(dv.dv_attn_proj_workspace_bytes(0, 1, dims.d, dims.h, dims.d_h, w.k_heads, dv.DV_F16))
     q = torch.empty(1, w.k_heads, dims.d_h, device="cuda")
-    yq = torch.from_numpy(np.ascontiguousarray(
-        __import__("contextual_sparsity_decoding_amd.synth", fromlist=["x"]).normal((1, dims.d), SEED, 9, "x"))).cuda()
+    yq = torch.from_numpy(np.ascontiguousarray(synth.normal((1, dims.d), SEED, 9, "x"))).cuda()
+    last = [int(cp.pos_dev.item()) - 1 for cp in copies]
     durs = []
     for i in range(args.kernel_launches + 4):
-        cp = copies[i % R]
-        kv = dv.kv_state(cp.K, cp.V, cp.pos - 1, cp.y_buf, cp.valid)
+        c = i % R
+        cp = copies[c]
+        kv = dv.kv_state(cp.K, cp.V, last[c], cp.y_buf, cp.valid)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         dv.dv_sparse_attn_proj(dv.DV_PROJ_QKV, dims.h, dims.d_h, cp.head_idx, w.k_heads, cp.Wd["w_qkv_t"],
@@ -210,8 +213,8 @@ def main():
         "value": round(1000.0 / ms_step, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": warm_reps * K,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -221,7 +224,7 @@ def main():
         "config": {
             "workload": "opt13b-layer decode: d=5120, 40 heads x 128, d_ffn=20480 ReLU, fp16, batch 1, "
                         "2048 cached tokens, keep 10% neurons (2048) and 50% heads (20), rank-128 predictors, "
-                        "4 rotating layer copies",
+                        "4 rotating layer copies, one HIP graph of the timed steps",
             "global_batch": 1, "seq_len": w.n_ctx, "keep_neurons": 0.10, "keep_heads": 0.50,
         },
         "effective_hbm_GBps": round(sb.total / (ms_step * 1e-3) / 1e9, 1),
@@ -231,7 +234,7 @@ def main():
         "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 5),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "byte_bound_speedup": round(db.total / sb.total, 3),
-        "host_wall_ms_per_step": round(1000 * wall / args.steps, 4),
+        "host_wall_ms_per_step": round(1000 * wall / K, 4),
         "roofline": {
             "kernel": "k_qkv (sparse Q/K/V gather-GEMV + KV append)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

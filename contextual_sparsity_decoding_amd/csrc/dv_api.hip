@@ -58,7 +58,6 @@ static float* predict_part(void* ws) { return ws ? (float*)((char*)ws + kCounter
 struct MlpWs {
     float* a;
     float* partial;
-    unsigned* counters;
     size_t bytes;
 };
 static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a) {
@@ -67,25 +66,20 @@ static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a)
     w.a = need_a ? cv.take<float>((size_t)B * (n_idx_max > 0 ? n_idx_max : 1)) : nullptr;
     const AxpyPlan p = axpy_plan(d, n_idx_max, wdt);
     w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
-    w.counters = ws_counters(ws, 1);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
 
 struct ProjWs {
     float* partial;
-    unsigned* counters;
     size_t bytes;
 };
 static ProjWs proj_ws(void* ws, int mode, int B, int d, int n_sel, int d_h, int wdt) {
     Carve cv(ws);
-    ProjWs w{nullptr, nullptr, 0};
+    ProjWs w{nullptr, 0};
     if (mode == DV_PROJ_OUT) {
         const AxpyPlan p = axpy_plan(d, n_sel * d_h, wdt);
         w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
-        w.counters = ws_counters(ws, 1);
-    } else {
-        w.counters = ws_counters(ws);
     }
     w.bytes = align_up(cv.off, 256);
     return w;
@@ -208,7 +202,7 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
     float* a = act_out ? act_out : w.a;
     TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
     return launch_axpy(w2_t, wdt, d, N, n_idx_max, n_idx_dev, idx, 1, a, n_idx_max, (flags & DV_SKIP_NONPOS_FC2) != 0,
-                       B, b2, residual, out, fc2_rows, w.partial, w.counters, s);
+                       B, b2, residual, out, fc2_rows, w.partial, nullptr, s);
 }
 
 // ---------------------------------------------------------------- projections --
@@ -239,16 +233,15 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
             "dv_sparse_attn_proj: pos=%d max_len=%d", kv->pos, kv->max_len);
         REQ(!overlap(out, (size_t)B * n_sel * d_h * 4, in, (size_t)B * d * 4), DV_ERR_RANGE,
             "dv_sparse_attn_proj: q overlaps y");
-        const bool fill = kv->y_buf && kv->valid_upto;
-        REQ(!fill || (ws && ws_bytes >= w.bytes), DV_ERR_WORKSPACE, "dv_sparse_attn_proj: workspace");
-        return launch_qkv(in, B, d, h, d_h, head_idx, n_sel, w_t, bias, wdt, out, kv, fill ? w.counters : nullptr, s);
+        REQ(qkv_supported(B, d, wdt), DV_ERR_UNSUPPORTED, "dv_sparse_attn_proj: d=%d rows too long", d);
+        return launch_qkv(in, B, d, h, d_h, head_idx, n_sel, w_t, bias, wdt, out, kv, true, s);
     }
     REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "dv_sparse_attn_proj: workspace %zu < %zu", ws_bytes, w.bytes);
     REQ(!overlap(out, (size_t)B * d * 4, in, (size_t)B * n_sel * d_h * 4) &&
             !overlap(out, (size_t)B * d * 4, residual, (size_t)B * d * 4),
         DV_ERR_RANGE, "dv_sparse_attn_proj: out overlaps o or residual");
     return launch_axpy(w_t, wdt, d, h * d_h, n_sel * d_h, nullptr, head_idx, d_h, in, n_sel * d_h, false, B, bias, residual,
-                       out, nullptr, w.partial, w.counters, s);
+                       out, nullptr, w.partial, nullptr, s);
 }
 
 // ---------------------------------------------------------------- attention --
@@ -283,8 +276,8 @@ dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx
     const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
     const size_t need = splitk_ws(B, n_sel, d_h, maxpos, num_splits);
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_splitk_attn: workspace %zu < %zu", ws_bytes, need);
-    return launch_splitk(q, B, d_h, head_idx, n_sel, kv, scale, num_splits, o, (float*)((char*)ws + kCounterBytes),
-                         (hipStream_t)stream);
+    return launch_splitk(q, B, d_h, head_idx, n_sel, kv, kv->n_ctx_dev, 0, scale, num_splits, o,
+                         (float*)((char*)ws + kCounterBytes), nullptr, 0, nullptr, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- KV scoring --
@@ -317,7 +310,6 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
 struct LayerWs {
     float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
     int32_t *head_idx, *nidx, *uidx, *ucnt;
-    unsigned *qkv_cnt, *axpy_cnt;
     size_t bytes;
 };
 
@@ -353,8 +345,6 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     const size_t xp = axpy_ws_floats(po, B, d) > axpy_ws_floats(pm, B, d) ? axpy_ws_floats(po, B, d)
                                                                            : axpy_ws_floats(pm, B, d);
     w.xpart = cv.take<float>(xp);
-    w.qkv_cnt = ws_counters(ws);
-    w.axpy_cnt = ws_counters(ws, 1);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -363,7 +353,7 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(c, DV_ERR_NULL, "dv_decode_layer: cfg NULL");
     REQ(wdt_ok(c->wdt), DV_ERR_DTYPE, "dv_decode_layer: wdt %d", c->wdt);
     REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
-    const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT;
+    const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT | DV_ADVANCE_POS;
     REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
     REQ(c->B >= 1 && c->B <= 16 && d_ok(c->d) && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
         "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
@@ -405,6 +395,8 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     REQ(kv.max_len >= 1 && kv.pos >= 0 && kv.pos < kv.max_len, DV_ERR_RANGE, "dv_decode_layer: pos=%d max_len=%d",
         kv.pos, kv.max_len);
     REQ(!(c->flags & DV_HOLE_FILL) || (kv.y_buf && kv.valid_upto), DV_ERR_NULL, "dv_decode_layer: hole fill state");
+    REQ(!(c->flags & DV_ADVANCE_POS) || kv.pos_dev, DV_ERR_NULL, "dv_decode_layer: DV_ADVANCE_POS needs kv.pos_dev");
+    REQ(qkv_supported(c->B, c->d, c->wdt), DV_ERR_UNSUPPORTED, "dv_decode_layer: d=%d rows too long", c->d);
     REQ(a16(w->w_qkv_t) && a16(w->w_o_t) && a16(w->w1_t) && a16(w->w2_t) && a16(x_in), DV_ERR_ALIGN,
         "dv_decode_layer: weight alignment");
     REQ(!overlap(x_out, (size_t)c->B * c->d * 4, x_in, (size_t)c->B * c->d * 4), DV_ERR_RANGE,
@@ -412,7 +404,7 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     dv_kv_view view;
     view.k_cache = kv.k_cache; view.v_cache = kv.v_cache; view.h = c->h; view.max_len = kv.max_len;
     view.n_ctx = kv.pos + 1;
-    view.sel_idx = nullptr; view.sel_len = nullptr; view.sel_cap = 0; view.sel_end = 0;
+    view.sel_idx = nullptr; view.sel_len = nullptr; view.sel_cap = 0; view.sel_end = 0; view.n_ctx_dev = nullptr;
     if (c->flags & DV_KV_SELECT) {
         view.sel_idx = st->sel_idx; view.sel_len = st->sel_len; view.sel_cap = st->sel_cap; view.sel_end = st->sel_end;
         REQ(view.sel_idx, DV_ERR_NULL, "dv_decode_layer: DV_KV_SELECT without sel_idx");
@@ -423,33 +415,37 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
 
     hipStream_t s = (hipStream_t)stream;
     const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N;
-    // attention block
-    TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+    // attention block: LN1 folded into the head predictor when heads are selected
     const int32_t* head_idx = nullptr;
     int n_sel = h;
     if (!(c->flags & DV_DENSE_ATTN)) {
         int32_t* hi = st->head_idx_out ? st->head_idx_out : L.head_idx;
-        TRY(launch_predict(L.y, B, d, w->pa1_t, c->r_attn, w->pa2_t, h, c->wdt, c->pred_act, L.sA, L.hpart, s));
+        TRY(launch_predict_ln(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, w->pa1_t, c->r_attn, w->pa2_t, h, c->wdt,
+                              c->pred_act, L.sA, L.hpart, s));
         TRY(launch_topk(L.sA, B, h, c->k_heads, hi, s));
         head_idx = hi;
         n_sel = c->k_heads;
+    } else {
+        TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
     }
     dv_kv_state kvs = kv;
     if (!(c->flags & DV_HOLE_FILL)) {
         kvs.y_buf = nullptr;
         kvs.valid_upto = nullptr;
     }
-    TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, L.qkv_cnt, s));
-    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, c->scale, 0, L.o, L.apart, s));
+    const bool fill = kvs.y_buf && kvs.valid_upto;
+    TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
+    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, L.o, L.apart,
+                      fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s));
     TRY(launch_axpy(w->w_o_t, c->wdt, d, h * dh, n_sel * dh, nullptr, head_idx, dh, L.o, n_sel * dh, false, B, w->b_o, x_in,
-                    L.hres, nullptr, L.xpart, L.axpy_cnt, s));
-    // MLP block
-    TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
+                    L.hres, nullptr, L.xpart, nullptr, s));
+    // MLP block: LN2 folded into the neuron predictor
     const int32_t* idx = nullptr;
     const int32_t* n_dev = nullptr;
     int n_max = N;
     if (!(c->flags & DV_DENSE_MLP)) {
-        TRY(launch_predict(L.y2, B, d, w->pm1_t, c->r_mlp, w->pm2_t, N, c->wdt, c->pred_act, L.sM, L.hpart, s));
+        TRY(launch_predict_ln(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, w->pm1_t, c->r_mlp, w->pm2_t, N, c->wdt,
+                              c->pred_act, L.sM, L.hpart, s));
         if (B == 1) {
             int32_t* ni = st->neuron_idx_out ? st->neuron_idx_out : L.nidx;
             TRY(launch_topk(L.sM, 1, N, c->k_neurons, ni, s));
@@ -465,10 +461,13 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
             n_dev = uc;
             n_max = layer_nmax(c);
         }
+    } else {
+        TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
     }
     TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
     return launch_axpy(w->w2_t, c->wdt, d, N, n_max, n_dev, idx, 1, L.a, n_max, (c->flags & DV_SKIP_NONPOS_FC2) != 0, B,
-                       w->b2, L.hres, x_out, st->fc2_rows_out, L.xpart, L.axpy_cnt, s);
+                       w->b2, L.hres, x_out, st->fc2_rows_out, L.xpart,
+                       (c->flags & DV_ADVANCE_POS) ? kv.pos_dev : nullptr, s);
 }
 
 }  // extern "C"

@@ -120,6 +120,39 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block (<= 1024 threads); *total gets the sum.
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tot /* >= 17 */, unsigned* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const unsigned incl = wave_incl_scan(v);
+    __syncthreads();
+    if (lane == 63) tot[w] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const unsigned t = tot[i];
+            tot[i] = run;
+            run += t;
+        }
+        tot[16] = run;
+    }
+    __syncthreads();
+    const unsigned r = tot[w] + incl - v;
+    *total = tot[16];
+    __syncthreads();
+    return r;
+}
+
 // Load a small vector from global memory into LDS with the whole block.
 __device__ __forceinline__ void block_copy_f32(float* __restrict__ dst, const float* __restrict__ src, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
@@ -173,10 +206,15 @@ size_t axpy_ws_floats(const AxpyPlan& p, int B, int d);
 dv_status launch_axpy(const void* w, int wdt, int d, int w_rows, int rows, const int32_t* n_rows_dev,
                       const int32_t* idx, int blk, const float* coef, int coef_stride, bool skip_zero,
                       int B, const void* bias, const float* residual, float* out, int32_t* rows_read,
-                      float* partial, unsigned* counters, hipStream_t s);
+                      float* partial, int32_t* advance, hipStream_t s);
+bool qkv_supported(int B, int d, int wdt);
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
-                     const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv,
-                     unsigned* counter, hipStream_t s);
+                     const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
+                     hipStream_t s);
+bool ln_fusable(int B, int d);
+dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
+                            const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
+                            float* hid, hipStream_t s);
 int topk_block_threads(int n);
 dv_status launch_set_i32(int32_t* p, int v, hipStream_t s);
 dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hipStream_t s);
@@ -184,8 +222,8 @@ dv_status launch_union(const int32_t* idx, int B, int k, int n, int32_t* union_i
                        int32_t* union_count, hipStream_t s);
 int splitk_auto(int max_positions, int rows);
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
-                        const dv_kv_view* kv, float scale, int num_splits, float* o, float* part,
-                        hipStream_t s);
+                        const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
+                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s);
 dv_status launch_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv,
                           float scale, int n_sink, int n_window, int width, float* scores,
                           float* raw, float* stats, hipStream_t s);

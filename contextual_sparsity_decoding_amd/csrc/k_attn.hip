@@ -26,13 +26,18 @@ struct AttnArgs {
     const int32_t* head_idx;
     const half_t* K;
     const half_t* V;
-    int max_len, n_ctx;
+    int max_len, n_ctx;       // n_ctx: the count, or its bound when n_dev is set
+    const int32_t* n_dev;     // count read at run time (+ n_add), or NULL
+    int n_add;
     const int32_t* sel_idx;
     const int32_t* sel_len;
     int sel_cap, sel_end;
     float scale_log2;
     int num_splits, chunk;
     float* part;            // [B][n_sel][num_splits][DH + 2]
+    int32_t* mark_valid;    // [B][h]: set the selected heads to mark_pos (decode layer), or NULL
+    int mark_pos;
+    const int32_t* mark_pos_dev;
 };
 
 template <int DH>
@@ -40,6 +45,14 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
     constexpr int LPR = DH / 8;            // lanes per row
     constexpr int RPW = kWave / LPR;       // rows per wave load
     constexpr int U = 4;                   // wave loads in flight (K and V each)
+    if (a.mark_valid && blockIdx.x == 0) {  // Q/K/V has finished: the selected heads hold K/V up to pos
+        const int p = a.mark_pos_dev ? *a.mark_pos_dev : a.mark_pos;
+        if (p >= 0 && p < a.max_len)
+            for (int i = threadIdx.x; i < a.B * a.n_sel; i += kBlock) {
+                const int hh = a.head_idx ? a.head_idx[i % a.n_sel] : i % a.n_sel;
+                if ((unsigned)hh < (unsigned)a.h) a.mark_valid[(i / a.n_sel) * a.h + hh] = p;
+            }
+    }
     const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (task >= a.B * a.n_sel * a.num_splits) return;
     const int c = task % a.num_splits;
@@ -57,14 +70,15 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = qp[e] * a.scale_log2;
     }
+    const int n_ctx = a.n_dev ? min(max(*a.n_dev + a.n_add, 0), a.n_ctx) : a.n_ctx;
     int cnt, sl = 0;
     const int32_t* sidx = nullptr;
     if (a.sel_idx) {
         sl = min(max(a.sel_len[b * a.h + head], 0), a.sel_cap);
         sidx = a.sel_idx + ((size_t)b * a.h + head) * a.sel_cap;
-        cnt = sl + max(0, a.n_ctx - a.sel_end);
+        cnt = sl + max(0, n_ctx - a.sel_end);
     } else {
-        cnt = a.n_ctx;
+        cnt = n_ctx;
     }
     if (!head_ok) cnt = 0;
     const int j0 = c * a.chunk;
@@ -87,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
             kw[u] = vw[u] = u32x4{0u, 0u, 0u, 0u};
             if (valid[u]) {
                 const int p = sidx ? (j < sl ? sidx[j] : a.sel_end + (j - sl)) : j;
-                valid[u] = (unsigned)p < (unsigned)a.n_ctx;       // a retained index past the cache reads nothing
+                valid[u] = (unsigned)p < (unsigned)n_ctx;         // a retained index past the cache reads nothing
                 if (valid[u]) {
                     kw[u] = ld16(Kh + (size_t)p * DH);
                     vw[u] = ld16(Vh + (size_t)p * DH);
@@ -153,40 +167,78 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
 }
 
 // o = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c over splits with l_c > 0.
+// One workgroup per row: the block finds M, then each wave adds a contiguous
+// quarter of the splits (up to 16 splits' loads in flight at once) and the
+// quarters are added in order.
 template <int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(const float* __restrict__ part, int rows,
                                                          int num_splits, float* __restrict__ o) {
     constexpr int PER = DH >= 64 ? DH / 64 : 1;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int lane = threadIdx.x & 63;
+    constexpr int MAXQ = 16;
+    __shared__ float red_m[4];
+    __shared__ float red_n[3][DH + 1];
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const float* P = part + (size_t)row * num_splits * (DH + 2);
     float M = -INFINITY;
-    for (int c = 0; c < num_splits; ++c) {
+    for (int c = threadIdx.x; c < num_splits; c += kBlock) {
         const float* pc = P + (size_t)c * (DH + 2);
         if (pc[DH + 1] > 0.f) M = fmaxf(M, pc[DH]);
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    if (lane == 0) red_m[wv] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    const int per = (num_splits + 3) / 4;
+    const int c0 = wv * per, c1 = min(num_splits, c0 + per);
     float num[PER], den = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) num[i] = 0.f;
     if (M != -INFINITY) {
-        for (int c = 0; c < num_splits; ++c) {
-            const float* pc = P + (size_t)c * (DH + 2);
-            const float lc = pc[DH + 1];
-            if (!(lc > 0.f)) continue;
-            const float w = exp2f(pc[DH] - M);
-            den = fmaf(w, lc, den);
+        for (int cb = c0; cb < c1; cb += MAXQ) {
+            float ml[MAXQ][2], av[MAXQ][PER];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int e = lane * PER + i;
-                if (e < DH) num[i] = fmaf(w, pc[e], num[i]);
+            for (int t = 0; t < MAXQ; ++t) {
+                const bool ok = cb + t < c1;
+                const float* pc = P + (size_t)(ok ? cb + t : c0) * (DH + 2);
+                ml[t][0] = pc[DH];
+                ml[t][1] = ok ? pc[DH + 1] : 0.f;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = lane * PER + i;
+                    av[t][i] = e < DH ? pc[e] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < MAXQ; ++t) {
+                if (!(ml[t][1] > 0.f)) continue;
+                const float wgt = exp2f(ml[t][0] - M);
+                den = fmaf(wgt, ml[t][1], den);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) num[i] = fmaf(wgt, av[t][i], num[i]);
             }
         }
     }
+    if (wv > 0) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane * PER + i;
-        if (e < DH) o[(size_t)row * DH + e] = den > 0.f ? num[i] / den : 0.f;
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            if (e < DH) red_n[wv - 1][e] = num[i];
+        }
+        if (lane == 0) red_n[wv - 1][DH] = den;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const float dt = den + red_n[0][DH] + red_n[1][DH] + red_n[2][DH];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            if (e < DH) {
+                const float nt = num[i] + red_n[0][e] + red_n[1][e] + red_n[2][e];
+                o[(size_t)row * DH + e] = dt > 0.f ? nt / dt : 0.f;
+            }
+        }
     }
 }
 
@@ -207,26 +259,27 @@ int splitk_auto(int max_positions, int rows) {
 }
 
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
-                        const dv_kv_view* kv, float scale, int num_splits, float* o, float* part,
-                        hipStream_t s) {
+                        const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
+                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s) {
     if (n_sel == 0) return DV_OK;
     const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
     if (num_splits <= 0) num_splits = splitk_auto(maxpos, B * n_sel);
     AttnArgs a;
     a.q = q; a.B = B; a.n_sel = n_sel; a.h = kv->h; a.head_idx = head_idx;
     a.K = (const half_t*)kv->k_cache; a.V = (const half_t*)kv->v_cache;
-    a.max_len = kv->max_len; a.n_ctx = kv->n_ctx;
+    a.max_len = kv->max_len; a.n_ctx = kv->n_ctx; a.n_dev = n_dev; a.n_add = n_add;
     a.sel_idx = kv->sel_idx; a.sel_len = kv->sel_len; a.sel_cap = kv->sel_cap; a.sel_end = kv->sel_end;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.num_splits = num_splits;
     a.chunk = cdiv(maxpos < 1 ? 1 : maxpos, num_splits);
     a.part = part;
+    a.mark_valid = mark_valid; a.mark_pos = mark_pos; a.mark_pos_dev = mark_pos_dev;
     const int tasks = B * n_sel * num_splits;
     const int rows = B * n_sel;
 #define DV_ATT(DH)                                                                                   \
     case DH:                                                                                         \
         hipLaunchKernelGGL((k_attn_split<DH>), dim3(cdiv(tasks, 4)), dim3(kBlock), 0, s, a);        \
-        hipLaunchKernelGGL((k_attn_combine<DH>), dim3(cdiv(rows, 4)), dim3(kBlock), 0, s, part, rows, \
+        hipLaunchKernelGGL((k_attn_combine<DH>), dim3(rows), dim3(kBlock), 0, s, part, rows,        \
                            num_splits, o);                                                           \
         break;
     switch (d_h) {

@@ -7,31 +7,31 @@
 // selected neuron or head is a contiguous run of rows.
 //
 // Work split: the d output columns are cut into slices of one wave-load
-// (64 lanes x 16 bytes); the selected rows into groups.  A workgroup
-// (4 waves) streams one slice of its group's rows, reduces across its waves
-// in LDS and writes one partial per group.  The last workgroup of a slice
-// to finish (atomic counter) adds the partials in group order, plus bias and
-// residual, so the result does not depend on scheduling.
+// (64 lanes x 16 bytes); the selected rows into groups of up to 64.  A
+// workgroup (4 waves) first stages its group's row indices and coefficients
+// in LDS (one batch of loads, an ordered compaction that drops rows whose
+// coefficients are all zero when asked), then every wave issues its weight
+// loads back to back, reduces across the 4 waves in LDS and writes one
+// partial sum per group.  k_axpy_finalize adds the partials in a fixed
+// order, plus bias and residual.  Results do not depend on scheduling.
 #include "dv_internal.h"
 
 namespace dv {
 
+constexpr int kRowsPerGroup = 64;
+
 struct AxpyArgs {
     const void* w;
-    int d, w_rows, rows;      // w has w_rows rows of d; rows = selected rows (u)
+    int d, w_rows, rows;      // W has w_rows rows of d; rows = selected rows (u)
     const int32_t* n_rows_dev;
-    const int32_t* idx;      // row(u) = idx[u / blk] * blk + u % blk, or u when NULL
+    const int32_t* idx;       // row(u) = idx[u / blk] * blk + u % blk, or u when NULL
     int blk;
-    const float* coef;       // coef[b * coef_stride + u]
+    const float* coef;        // coef[b * coef_stride + u]
     int coef_stride;
     int skip_zero;
-    int B, n_groups, rows_per_group;
-    const void* bias;
-    const float* residual;
-    float* out;
+    int B, n_groups;
+    float* partial;           // [n_groups][B][d]
     int32_t* rows_read;
-    float* partial;          // [n_groups][B][d]
-    unsigned* counters;      // [n_slices]
 };
 
 template <typename T, int NB, int U>
@@ -39,63 +39,75 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     constexpr int E = Vec<T>::E;
     constexpr int SW = kWave * E;                  // columns per slice
     constexpr int NBC = NB < 4 ? NB : 4;           // batch rows per LDS reduction round
+    __shared__ int s_row[kRowsPerGroup];
+    __shared__ float s_cf[kRowsPerGroup * NB];
     __shared__ float red[3][NBC][SW];
-    __shared__ int last;
+    __shared__ unsigned tot[17];
     const T* W = (const T*)a.w;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, g = blockIdx.y;
     const int col = slice * SW + lane * E;
     const bool colok = col < a.d;
     const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
-    const int r0 = g * a.rows_per_group;
-    const int r1 = min(rows, r0 + a.rows_per_group);
+    const int r0 = g * kRowsPerGroup;
 
+    // ---- prologue: this group's rows and coefficients, compacted in order
+    bool live = false;
+    int row = 0;
+    float cf[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cf[b] = 0.f;
+    if (threadIdx.x < kRowsPerGroup && r0 + (int)threadIdx.x < rows) {
+        const int u = r0 + threadIdx.x;
+        row = a.idx ? a.idx[u / a.blk] * a.blk + u % a.blk : u;
+        bool any = false;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            cf[b] = b < a.B ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
+            any |= cf[b] != 0.f;
+        }
+        live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
+    }
+    unsigned nlive;
+    const unsigned slot = block_excl_scan(live ? 1u : 0u, tot, &nlive);
+    if (live) {
+        s_row[slot] = row;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s_cf[slot * NB + b] = cf[b];
+    }
+    __syncthreads();
+    if (a.rows_read && slice == 0 && threadIdx.x == 0 && nlive > 0) atomicAdd(a.rows_read, (int)nlive);
+
+    // ---- stream the live rows: wave wv takes rows wv, wv+4, ...
     float acc[NB][E];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[b][e] = 0.f;
-    int nread = 0;
-
-    for (int u0 = r0 + wv; u0 < r1; u0 += 4 * U) {
+    for (int k0 = wv; k0 < (int)nlive; k0 += 4 * U) {
         u32x4 w[U];
-        float cf[U][NB];
-        bool live[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int u = u0 + 4 * i;
-            live[i] = u < r1;
-            bool any = false;
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float c = (live[i] && b < a.B) ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
-                cf[i][b] = c;
-                any |= c != 0.f;
-            }
-            if (a.skip_zero) live[i] = live[i] && any;
-            w[i] = u32x4{0u, 0u, 0u, 0u};
-            int row = 0;
-            if (live[i]) {
-                row = a.idx ? a.idx[u / a.blk] * a.blk + u % a.blk : u;
-                live[i] = (unsigned)row < (unsigned)a.w_rows;   // an index outside W selects nothing
-            }
-            if (live[i] && colok) w[i] = ld16_stream(W + (size_t)row * a.d + col);
+        for (int t = 0; t < U; ++t) {
+            const int k = k0 + 4 * t;
+            w[t] = (k < (int)nlive && colok) ? ld16_stream(W + (size_t)s_row[k] * a.d + col) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            if (!live[i]) continue;
-            ++nread;
-            float f[E];
-            unpack(w[i], f, T());
+        for (int t = 0; t < U; ++t) {
+            const int k = k0 + 4 * t;
+            if (k < (int)nlive) {
+                float f[E];
+                unpack(w[t], f, T());
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b) {
+                    const float c = s_cf[k * NB + b];
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[b][e] = fmaf(cf[i][b], f[e], acc[b][e]);
+                    for (int e = 0; e < E; ++e) acc[b][e] = fmaf(c, f[e], acc[b][e]);
+                }
+            }
         }
     }
-    if (a.rows_read && slice == 0 && lane == 0 && nread > 0) atomicAdd(a.rows_read, nread);
 
-    // reduce the 4 waves into wave 0, NBC batch rows at a time
+    // ---- reduce the 4 waves into wave 0, NBC batch rows at a time
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += NBC) {
         if (wv > 0) {
@@ -109,34 +121,64 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 #pragma unroll
             for (int bb = 0; bb < NBC; ++bb) {
                 const int b = b0 + bb;
+                if (b < a.B && colok) {
+                    float o[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float v = acc[b][e] + red[0][bb][lane * E + e] + red[1][bb][lane * E + e] +
-                                    red[2][bb][lane * E + e];
-                    if (b < a.B && colok) a.partial[((size_t)g * a.B + b) * a.d + col + e] = v;
+                    for (int e = 0; e < E; ++e)
+                        o[e] = acc[b][e] + red[0][bb][lane * E + e] + red[1][bb][lane * E + e] + red[2][bb][lane * E + e];
+                    float* dst = a.partial + ((size_t)g * a.B + b) * a.d + col;
+#pragma unroll
+                    for (int q = 0; q < E / 4; ++q)
+                        reinterpret_cast<f32x4*>(dst)[q] = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
                 }
             }
         }
         __syncthreads();
     }
+}
 
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(&a.counters[slice], 1u) == gridDim.y - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const T* bias = (const T*)a.bias;
-    for (int i = threadIdx.x; i < a.B * SW; i += kBlock) {
-        const int b = i / SW, c = slice * SW + i % SW;
-        if (c >= a.d) continue;
-        float s = 0.f;
-        for (int gg = 0; gg < a.n_groups; ++gg) s += a.partial[((size_t)gg * a.B + b) * a.d + c];
-        if (bias) s += to_f32(bias[c]);
-        if (a.residual) s += a.residual[(size_t)b * a.d + c];
-        a.out[(size_t)b * a.d + c] = s;
+// out[b][c] = residual[b][c] + bias[c] + sum_g partial[g][b][c].  A block
+// covers 64 float4 columns of one batch row; its 4 waves each add a
+// contiguous quarter of the groups (all loads of a quarter in flight
+// together), then the quarters are added in order.  One thread also
+// advances a decode position when asked (nothing here reads it).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restrict__ partial, int n_groups, int B, int d,
+                                                          const void* bias, const float* __restrict__ residual,
+                                                          float* __restrict__ out, int32_t* advance) {
+    constexpr int MAXQ = 16;                      // groups per quarter held in flight
+    __shared__ f32x4 red[3][64];
+    const int b = blockIdx.y;
+    const int c4 = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int q = threadIdx.x >> 6;
+    const int n4 = d / 4;
+    const int per = (n_groups + 3) / 4;
+    const int g0 = q * per, g1 = min(n_groups, g0 + per);
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c4 < n4) {
+        for (int gb = g0; gb < g1; gb += MAXQ) {
+            f32x4 v[MAXQ];
+#pragma unroll
+            for (int i = 0; i < MAXQ; ++i)
+                v[i] = gb + i < g1 ? reinterpret_cast<const f32x4*>(partial + ((size_t)(gb + i) * B + b) * d)[c4]
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < MAXQ; ++i) s += v[i];
+        }
     }
-    if (threadIdx.x == 0) a.counters[slice] = 0u;
+    if (q > 0) red[q - 1][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (q == 0 && c4 < n4) {
+        s = s + red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x];
+        if (bias) {
+            const T* bb = (const T*)bias + (size_t)c4 * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] += to_f32(bb[e]);
+        }
+        if (residual) s += reinterpret_cast<const f32x4*>(residual + (size_t)b * d)[c4];
+        reinterpret_cast<f32x4*>(out + (size_t)b * d)[c4] = s;
+    }
+    if (advance && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *advance += 1;
 }
 
 }  // namespace dv
@@ -148,12 +190,8 @@ AxpyPlan axpy_plan(int d, int rows, int wdt) {
     AxpyPlan p;
     const int E = 16 / elt_bytes(wdt);
     p.n_slices = cdiv(d, kWave * E);
-    // about 32 rows (8 per wave) per group; at most 128 groups
-    int groups = cdiv(rows < 1 ? 1 : rows, 32);
-    if (groups > 128) groups = 128;
-    if (groups < 1) groups = 1;
-    p.rows_per_group = cdiv(rows < 1 ? 1 : rows, groups);
-    p.n_groups = cdiv(rows < 1 ? 1 : rows, p.rows_per_group);
+    p.rows_per_group = kRowsPerGroup;
+    p.n_groups = cdiv(rows < 1 ? 1 : rows, kRowsPerGroup);
     return p;
 }
 
@@ -161,20 +199,18 @@ size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_grou
 
 template <typename T, int NB>
 static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
-    hipLaunchKernelGGL((k_axpy<T, NB, 8>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_axpy<T, NB, 16>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
 }
 
 dv_status launch_axpy(const void* w, int wdt, int d, int w_rows, int rows, const int32_t* n_rows_dev,
                       const int32_t* idx, int blk, const float* coef, int coef_stride, bool skip_zero,
                       int B, const void* bias, const float* residual, float* out, int32_t* rows_read,
-                      float* partial, unsigned* counters, hipStream_t s) {
+                      float* partial, int32_t* advance, hipStream_t s) {
     const AxpyPlan p = axpy_plan(d, rows, wdt);
     AxpyArgs a;
     a.w = w; a.d = d; a.w_rows = w_rows; a.rows = rows; a.n_rows_dev = n_rows_dev; a.idx = idx; a.blk = blk;
     a.coef = coef; a.coef_stride = coef_stride; a.skip_zero = skip_zero ? 1 : 0;
-    a.B = B; a.n_groups = p.n_groups; a.rows_per_group = p.rows_per_group;
-    a.bias = bias; a.residual = residual; a.out = out; a.rows_read = rows_read;
-    a.partial = partial; a.counters = counters;
+    a.B = B; a.n_groups = p.n_groups; a.partial = partial; a.rows_read = rows_read;
     const int nb = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16;
 #define DV_AXPY(NB)                                                            \
     case NB:                                                                   \
@@ -185,6 +221,13 @@ dv_status launch_axpy(const void* w, int wdt, int d, int w_rows, int rows, const
         DV_AXPY(1) DV_AXPY(2) DV_AXPY(4) DV_AXPY(8) DV_AXPY(16)
     }
 #undef DV_AXPY
+    const dim3 fg(cdiv(d / 4, 64), B);
+    if (wdt == DV_F16)
+        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, partial, p.n_groups, B, d, bias, residual,
+                           out, advance);
+    else
+        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, partial, p.n_groups, B, d, bias, residual,
+                           out, advance);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DV_OK;

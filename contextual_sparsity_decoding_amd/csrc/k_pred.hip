@@ -1,0 +1,274 @@
+// LayerNorm, the predictor's second layer, the predictor's first layer with
+// LayerNorm folded in, and the valid-position update of hole fill.
+//
+// Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
+// Inference Time" (arXiv 2310.17157).
+#include "rowdot.h"
+
+namespace dv {
+
+__global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restrict__ x, int d,
+                                                          const float* __restrict__ g,
+                                                          const float* __restrict__ b, float eps,
+                                                          float* y) {
+    __shared__ float red[16];
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)blockIdx.x * d);
+    const int n4 = d / 4;
+    f32x4 v[kLnVec];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        v[i] = c < n4 ? xr[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    const float mean = block_sum1024(s, red) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        if (c < n4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float t = v[i][e] - mean;
+                q = fmaf(t, t, q);
+            }
+    }
+    const float var = block_sum1024(q, red) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(b);
+    f32x4* yr = reinterpret_cast<f32x4*>(y + (size_t)blockIdx.x * d);
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        if (c < n4) {
+            const f32x4 gg = g4[c], bb = b4[c];
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mean) * rstd * gg[e] + bb[e];
+            yr[c] = o;
+        }
+    }
+}
+
+// The predictor's first layer with the block's LayerNorm folded in (batch
+// row 0 only): every workgroup normalises x in LDS itself (the statistics of
+// a 5120-float row cost far less than a launch), workgroup 0 also writes y
+// for the kernels that follow.
+struct LnArgs {
+    const float* x;
+    const float* g;
+    const float* b;
+    float eps;
+    float* y_out;
+};
+
+__device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < d; i += kBlock) s += ys[i];
+    const float mean = block_sum256(s, red) / (float)d;
+    float q = 0.f;
+    for (int i = threadIdx.x; i < d; i += kBlock) {
+        const float t = ys[i] - mean;
+        q = fmaf(t, t, q);
+    }
+    const float rstd = 1.0f / sqrtf(block_sum256(q, red) / (float)d + ln.eps);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
+    f32x4* y4 = reinterpret_cast<f32x4*>(ys);
+#pragma unroll 8
+    for (int c = threadIdx.x; c < d / 4; c += kBlock) {
+        const f32x4 gg = g4[c], bb = b4[c];
+        f32x4 v = y4[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd * gg[e] + bb[e];
+        y4[c] = v;
+        if (write) reinterpret_cast<f32x4*>(ln.y_out)[c] = v;
+    }
+    __syncthreads();
+}
+
+template <typename T, int CH>
+__global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
+    constexpr int E = Vec<T>::E;
+    extern __shared__ float ys[];
+    const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nchunk = a.d / E;
+    const bool live = u < a.n_max;
+    u32x4 w[CH];
+    if (live) load_row<T, CH, true>((const T*)a.w + (size_t)u * a.d, nchunk, w);
+    stage_rows<1, 8>(ys, ln.x, 1, a.d);
+    __syncthreads();
+    layernorm_lds(ys, a.d, ln, blockIdx.x == 0);
+    if (!live) return;
+    float acc[1] = {0.f};
+    dot_row<T, CH, 1>(w, nchunk, ys, a.d, 1, acc);
+    const float v = wave_sum(acc[0]);
+    if ((threadIdx.x & 63) == 0) a.out[u] = v;
+}
+
+// ---------------------------------------------------------------- predictor --
+// DejaVu §4.1/§4.2: SP(y) = act(y P1) P2.  Layer 1 is k_rowdot (r rows);
+// layer 2 applies act to the r hidden values and scores every output row,
+// lpr lanes per row of r elements.
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict__ hid_in, int B, int r, int act,
+                                                        const T* __restrict__ p2, int n_out, int lpr,
+                                                        int rows_per_block, float* __restrict__ scores) {
+    constexpr int E = Vec<T>::E;
+    extern __shared__ float hid[];                       // [NB][r_pad]
+    const int r_pad = (r + 3) & ~3;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int grp = lane / lpr, t = lane % lpr;
+    const int rpw = kWave / lpr;                         // rows per wave pass
+    const int rchunk = r / E;                            // r*wb is a multiple of 16
+    const int j0 = blockIdx.x * rows_per_block;
+    const int j1 = min(n_out, j0 + rows_per_block);
+    // this wave's first row, loaded before the hidden vector is staged
+    const int jfirst = j0 + wv * rpw + grp;
+    u32x4 w0 = u32x4{0u, 0u, 0u, 0u};
+    if (jfirst < j1 && t < rchunk) w0 = ld16(p2 + (size_t)jfirst * r + (size_t)t * E);
+    for (int i = threadIdx.x; i < NB * r_pad; i += kBlock) {
+        const int b = i / r_pad, k = i % r_pad;
+        float v = (b < B && k < r) ? hid_in[(size_t)b * r + k] : 0.f;
+        if (act == DV_ACT_RELU) v = fmaxf(v, 0.f);
+        hid[i] = v;
+    }
+    __syncthreads();
+    bool first = true;
+    for (int jb = j0 + wv * rpw; jb < j1; jb += 4 * rpw) {
+        const int j = jb + grp;
+        float acc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+        if (j < j1) {
+            const T* row = p2 + (size_t)j * r;
+            for (int c = t; c < rchunk; c += lpr) {
+                float f[E];
+                unpack((first && c == t) ? w0 : ld16(row + (size_t)c * E), f, T());
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[b] = fmaf(f[e], hid[b * r_pad + c * E + e], acc[b]);
+            }
+        }
+        first = false;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float v = group_sum_dyn(acc[b], lpr);
+            if (t == 0 && j < j1 && b < B) scores[(size_t)b * n_out + j] = v;
+        }
+    }
+}
+
+}  // namespace dv
+
+namespace dvh {
+using namespace dv;
+
+#define DV_LAUNCH_CHECK()                                                          \
+    do {                                                                           \
+        hipError_t e_ = hipGetLastError();                                         \
+        if (e_ != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e_)); \
+    } while (0)
+
+dv_status launch_layernorm(const float* x, int B, int d, const float* g, const float* b, float eps,
+                           float* y, hipStream_t s) {
+    hipLaunchKernelGGL(k_layernorm, dim3(B), dim3(kLnThreads), 0, s, x, d, g, b, eps, y);
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
+
+dv_status rowdot_plain(const RowArgs& a, int wdt, hipStream_t s);
+
+size_t pred_partials(int B, int d, int r, int wdt) {
+    (void)d; (void)wdt;
+    return (size_t)B * r;
+}
+
+template <typename T, int NB>
+static void scores_go(const float* hid, int B, int r, int act, const void* p2, int n_out, float* scores,
+                      hipStream_t s) {
+    constexpr int E = Vec<T>::E;
+    const int rchunk = r / E;
+    int lpr = 1;
+    while (lpr < rchunk && lpr < kWave) lpr *= 2;
+    const int rows_per_block = (kWave / lpr) * 4 * 4;
+    const int r_pad = (r + 3) & ~3;
+    hipLaunchKernelGGL((k_pred_scores<T, NB>), dim3(cdiv(n_out, rows_per_block)), dim3(kBlock),
+                       (size_t)NB * r_pad * sizeof(float), s, hid, B, r, act, (const T*)p2, n_out, lpr,
+                       rows_per_block, scores);
+}
+
+dv_status launch_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t,
+                         int n_out, int wdt, int act, float* scores, float* hid, hipStream_t s) {
+    RowArgs a{};
+    a.y = y; a.B = B; a.d = d; a.w = p1_t; a.bias = nullptr; a.idx = nullptr;
+    a.n_max = r; a.n_dev = nullptr; a.w_rows = r; a.out = hid;
+    dv_status st = rowdot_plain(a, wdt, s);
+    if (st != DV_OK) return st;
+#define DV_SC(NB)                                                                              \
+    case NB:                                                                                   \
+        if (wdt == DV_F16) scores_go<half_t, NB>(hid, B, r, act, p2_t, n_out, scores, s);      \
+        else scores_go<float, NB>(hid, B, r, act, p2_t, n_out, scores, s);                     \
+        break;
+    switch (nb_bucket(B)) {
+        DV_SC(1) DV_SC(2) DV_SC(4) DV_SC(8) DV_SC(16)
+    }
+#undef DV_SC
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
+
+bool ln_fusable(int B, int d) { return B == 1 && (size_t)d * sizeof(float) <= kYLdsMax && d % 4 == 0; }
+
+template <typename T>
+static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStream_t s) {
+    const int grid = cdiv(a.n_max, 4);
+    const size_t lds = (size_t)a.d * sizeof(float);
+    switch (ch) {
+        case 4: hipLaunchKernelGGL((k_rowdot_ln<T, 4>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 8: hipLaunchKernelGGL((k_rowdot_ln<T, 8>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 10: hipLaunchKernelGGL((k_rowdot_ln<T, 10>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 12: hipLaunchKernelGGL((k_rowdot_ln<T, 12>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 16: hipLaunchKernelGGL((k_rowdot_ln<T, 16>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 18: hipLaunchKernelGGL((k_rowdot_ln<T, 18>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 24: hipLaunchKernelGGL((k_rowdot_ln<T, 24>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        default: return fail(DV_ERR_UNSUPPORTED, "fused LayerNorm: d=%d", a.d);
+    }
+    return DV_OK;
+}
+
+dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
+                            const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
+                            float* hid, hipStream_t s) {
+    if (!ln_fusable(B, d) || ch_tier(d, wdt) == 0) {
+        dv_status st = launch_layernorm(x, B, d, g, b, eps, y_out, s);
+        if (st != DV_OK) return st;
+        return launch_predict(y_out, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, hid, s);
+    }
+    RowArgs a{};
+    a.y = nullptr; a.B = 1; a.d = d; a.w = p1_t; a.n_max = r; a.w_rows = r; a.out = hid;
+    LnArgs ln{x, g, b, eps, y_out};
+    dv_status st = wdt == DV_F16 ? predict_ln_t<half_t>(a, ln, ch_tier(d, wdt), s)
+                                 : predict_ln_t<float>(a, ln, ch_tier(d, wdt), s);
+    if (st != DV_OK) return st;
+    DV_LAUNCH_CHECK();
+#define DV_SC(NB)                                                                              \
+    case NB:                                                                                   \
+        if (wdt == DV_F16) scores_go<half_t, NB>(hid, B, r, act, p2_t, n_out, scores, s);      \
+        else scores_go<float, NB>(hid, B, r, act, p2_t, n_out, scores, s);                     \
+        break;
+    switch (nb_bucket(B)) {
+        DV_SC(1)
+    }
+#undef DV_SC
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
+
+
+}  // namespace dvh

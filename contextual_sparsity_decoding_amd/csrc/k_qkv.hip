@@ -1,0 +1,57 @@
+// Sparse Q/K/V projections with KV append and hole fill (DejaVu §4.2):
+// entry point and the fp16 instantiation.
+//
+// Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
+// Inference Time" (arXiv 2310.17157).
+#include "qkv.h"
+
+namespace dv {
+
+// Selected heads now hold K/V up to pos (run after k_qkv has finished).
+__global__ void k_mark_valid_qkv(const int32_t* __restrict__ head_idx, int n_sel, int B, int h, int pos,
+                                 const int32_t* __restrict__ pos_dev, int max_len, int32_t* __restrict__ valid_upto) {
+    const int p = pos_dev ? *pos_dev : pos;
+    if (p < 0 || p >= max_len) return;
+    for (int i = threadIdx.x; i < B * n_sel; i += blockDim.x) {
+        const int b = i / n_sel, s = i % n_sel;
+        const int head = head_idx ? head_idx[s] : s;
+        if ((unsigned)head < (unsigned)h) valid_upto[b * h + head] = p;
+    }
+}
+
+}  // namespace dv
+
+namespace dvh {
+using namespace dv;
+
+template dv_status qkv_launch_t<half_t>(const QkvArgs&, int, hipStream_t);
+extern template dv_status qkv_launch_t<float>(const QkvArgs&, int, hipStream_t);
+
+bool qkv_supported(int B, int d, int wdt) {
+    (void)B;
+    return ch_tier(d, wdt) > 0;
+}
+
+dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
+                     const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
+                     hipStream_t s) {
+    if (n_sel == 0) return DV_OK;
+    QkvArgs a;
+    a.y = y; a.B = B; a.d = d; a.h = h; a.dh = d_h; a.n_sel = n_sel;
+    a.head_idx = head_idx; a.w = w; a.bias = bias; a.q = q;
+    a.K = (half_t*)kv->k_cache; a.V = (half_t*)kv->v_cache;
+    a.max_len = kv->max_len; a.pos = kv->pos; a.pos_dev = kv->pos_dev;
+    a.y_buf = kv->y_buf; a.valid_upto = kv->valid_upto;
+    const int ch = ch_tier(d, wdt);
+    const dv_status st = wdt == DV_F16 ? qkv_launch_t<half_t>(a, ch, s) : qkv_launch_t<float>(a, ch, s);
+    if (st != DV_OK) return st;
+    DV_LAUNCH_CHECK();
+    if (mark_valid && a.y_buf && a.valid_upto) {
+        hipLaunchKernelGGL(k_mark_valid_qkv, dim3(1), dim3(256), 0, s, head_idx, n_sel, B, h, kv->pos, kv->pos_dev,
+                           kv->max_len, kv->valid_upto);
+        DV_LAUNCH_CHECK();
+    }
+    return DV_OK;
+}
+
+}  // namespace dvh

@@ -1,0 +1,160 @@
+// Device helpers shared by the row-dot kernels (LayerNorm, predictor, fc1,
+// Q/K/V): staging inputs in LDS, whole weight rows in registers, dot
+// products of a register-resident row, and the chunk tiers.
+#pragma once
+
+#include "dv_internal.h"
+
+#include <math.h>
+
+namespace dv {
+
+// ---------------------------------------------------------------- LayerNorm --
+// DejaVu App. B: a normalisation precedes each block of the residual stream.
+// One 1024-thread workgroup per row; the row stays in registers (float4
+// loads, all issued together), two block reductions, one store.
+constexpr int kLnThreads = 1024;
+constexpr int kLnVec = 4;                 // float4 per thread: d <= 16384
+
+__device__ __forceinline__ float block_sum1024(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += red[i];
+    return s;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------- staging ---
+// Copy NB rows of length d (d % 4 == 0, 16-byte aligned) from global memory
+// into LDS; rows b >= B are zero.  Each thread issues its first MAXV float4
+// loads before the first LDS store.
+template <int NB, int MAXV>
+__device__ __forceinline__ void stage_rows(float* __restrict__ lds, const float* __restrict__ src, int B, int d) {
+    const int n4 = NB * d / 4;
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+    f32x4 v[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c = threadIdx.x + i * kBlock;
+        v[i] = (c < n4 && (c * 4) / d < B) ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4* l4 = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c = threadIdx.x + i * kBlock;
+        if (c < n4) l4[c] = v[i];
+    }
+    for (int c = threadIdx.x + MAXV * kBlock; c < n4; c += kBlock)   // inputs longer than MAXV*1024 floats
+        l4[c] = (c * 4) / d < B ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// One wave's whole weight row in registers: chunks lane, lane+64, ... of
+// nchunk (at most CH per lane).
+template <typename T, int CH, bool STREAM>
+__device__ __forceinline__ void load_row(const T* __restrict__ row, int nchunk, u32x4 (&w)[CH]) {
+    constexpr int E = Vec<T>::E;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk)
+            w[i] = STREAM ? ld16_stream(row + (size_t)c * E) : ld16(row + (size_t)c * E);
+        else
+            w[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Lane-partial dots of a register-resident row with NB vectors (LDS or
+// global, vector b at ys + b * ystride).
+template <typename T, int CH, int NB>
+__device__ __forceinline__ void dot_row(const u32x4 (&w)[CH], int nchunk, const float* __restrict__ ys, int ystride,
+                                        int nvalid, float (&acc)[NB]) {
+    constexpr int E = Vec<T>::E;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk) {
+            float f[E];
+            unpack(w[i], f, T());
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int bb = b < nvalid ? b : 0;     // vectors past the batch are discarded
+                const f32x4* yv = reinterpret_cast<const f32x4*>(ys + (size_t)bb * ystride + (size_t)c * E);
+#pragma unroll
+                for (int q = 0; q < E / 4; ++q) {
+                    const f32x4 y4 = yv[q];
+                    acc[b] = fmaf(f[4 * q + 0], y4[0], acc[b]);
+                    acc[b] = fmaf(f[4 * q + 1], y4[1], acc[b]);
+                    acc[b] = fmaf(f[4 * q + 2], y4[2], acc[b]);
+                    acc[b] = fmaf(f[4 * q + 3], y4[3], acc[b]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- row-dot ---
+// out[b][u] = epilogue(W[row(u)] . y[b]) for u in [0, n): the predictor's
+// first layer (its activation is applied by the next kernel) and sparse fc1
+// (bias + ReLU).
+enum RowOp { ROW_PLAIN = 0, ROW_FC1 = 1 };
+
+struct RowArgs {
+    const float* y;
+    int B, d;
+    const void* w;
+    const void* bias;       // per row (FC1)
+    const int32_t* idx;     // row(u) = idx[u], or u
+    int n_max;
+    const int32_t* n_dev;   // count used, <= n_max, or NULL
+    int w_rows;             // rows of W (bounds of idx)
+    float* out;             // [B][n_max]
+};
+
+
+// The layer input normalised in LDS (used by the predictor with LN folded in).
+}  // namespace dv
+
+namespace dvh {
+using namespace dv;
+
+inline int nb_bucket(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
+
+// Chunks per lane held in registers: the smallest tier covering a row.
+inline int ch_tier(int d, int wdt) {
+    const int E = 16 / elt_bytes(wdt);
+    const int per_lane = cdiv(d / E, kWave);
+    if (per_lane <= 4) return 4;
+    if (per_lane <= 8) return 8;
+    if (per_lane <= 10) return 10;            // d = 5120 in fp16
+    if (per_lane <= 12) return 12;
+    if (per_lane <= 16) return 16;
+    if (per_lane <= 18) return 18;            // d = 9216 in fp16
+    if (per_lane <= 24) return 24;
+    return 0;                                 // too long: generic path
+}
+
+// Rows per workgroup for the streaming kernels: a multiple of 4, about
+// two workgroups per CU (256 CUs) when there are enough rows, at most 32.
+inline int rows_per_group(long rows) {
+    long r = (rows + 2047) / 2048;              // 512 workgroups of 4 * r rows
+    r = r < 1 ? 1 : r > 8 ? 8 : r;
+    return (int)(4 * r);
+}
+
+
+}  // namespace dvh

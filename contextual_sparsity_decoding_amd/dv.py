@@ -30,6 +30,7 @@ DV_DENSE_ATTN = 0x2
 DV_DENSE_MLP = 0x4
 DV_HOLE_FILL = 0x8
 DV_KV_SELECT = 0x10
+DV_ADVANCE_POS = 0x20
 STATUS = ["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN", "DV_ERR_RANGE",
           "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]
 
@@ -38,12 +39,12 @@ vp, ci, cf, cu, sz = C.c_void_p, C.c_int, C.c_float, C.c_uint, C.c_size_t
 
 class KVState(C.Structure):
     _fields_ = [("k_cache", vp), ("v_cache", vp), ("max_len", ci), ("pos", ci),
-                ("y_buf", vp), ("valid_upto", vp)]
+                ("y_buf", vp), ("valid_upto", vp), ("pos_dev", vp)]
 
 
 class KVView(C.Structure):
     _fields_ = [("k_cache", vp), ("v_cache", vp), ("h", ci), ("max_len", ci), ("n_ctx", ci),
-                ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci), ("sel_end", ci)]
+                ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci), ("sel_end", ci), ("n_ctx_dev", vp)]
 
 
 class DecodeCfg(C.Structure):
@@ -179,16 +180,17 @@ def dv_sparse_mlp(y, w1_t, b1, w2_t, b2, idx, n_idx_max, out, ws, *, n_idx_dev=N
         ptr(residual), ptr(out), ptr(act_out), ptr(fc2_rows), flags, ptr(ws), ws.numel(), stream_handle(stream)))
 
 
-def kv_state(K, V, pos, y_buf=None, valid_upto=None) -> KVState:
-    s = KVState(ptr(K), ptr(V), K.shape[2], pos, ptr(y_buf), ptr(valid_upto))
-    s._keep = (K, V, y_buf, valid_upto)       # the struct holds raw pointers: keep the tensors alive
+def kv_state(K, V, pos, y_buf=None, valid_upto=None, pos_dev=None) -> KVState:
+    s = KVState(ptr(K), ptr(V), K.shape[2], pos, ptr(y_buf), ptr(valid_upto), ptr(pos_dev))
+    s._keep = (K, V, y_buf, valid_upto, pos_dev)   # the struct holds raw pointers: keep the tensors alive
     return s
 
 
-def kv_view(K, V, n_ctx, sel_idx=None, sel_len=None, sel_end=0) -> KVView:
+def kv_view(K, V, n_ctx, sel_idx=None, sel_len=None, sel_end=0, n_ctx_dev=None) -> KVView:
     cap = sel_idx.shape[-1] if sel_idx is not None else 0
-    v = KVView(ptr(K), ptr(V), K.shape[1], K.shape[2], n_ctx, ptr(sel_idx), ptr(sel_len), cap, sel_end)
-    v._keep = (K, V, sel_idx, sel_len)
+    v = KVView(ptr(K), ptr(V), K.shape[1], K.shape[2], n_ctx, ptr(sel_idx), ptr(sel_len), cap, sel_end,
+               ptr(n_ctx_dev))
+    v._keep = (K, V, sel_idx, sel_len, n_ctx_dev)
     return v
 
 

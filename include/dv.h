@@ -21,10 +21,10 @@
  *   allocates, frees or synchronises.
  * - Scratch memory is the caller's `ws` of at least the size the matching
  *   *_workspace_bytes() query returns, 256-byte aligned.  Its first 4096
- *   bytes hold counters: zero fill the workspace before its first use; every
- *   call leaves the counters at zero again, so one workspace serves any
- *   number of calls, of any shapes, issued in order on one stream.  Calls
- *   that overlap in time must use separate workspaces.
+ *   bytes are reserved for counters; zero fill the workspace before its
+ *   first use.  One workspace serves any number of calls, of any shapes,
+ *   issued in order on one stream; calls that overlap in time must use
+ *   separate workspaces.
  * - d (the model width) is at most 261,888 (one counter per 256 columns).
  * - Weight pointers must be 16-byte aligned and a weight row (d elements)
  *   must be a multiple of 16 bytes (d % 8 == 0 for fp16, d % 4 == 0 for
@@ -74,6 +74,7 @@ typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
 #define DV_DENSE_MLP       0x4u  /* every neuron, no neuron predictor */
 #define DV_HOLE_FILL       0x8u  /* recompute skipped heads' K/V (DejaVu §4.2) */
 #define DV_KV_SELECT       0x10u /* attend to retained KV positions only (ByteCross §4.1) */
+#define DV_ADVANCE_POS     0x20u /* dv_decode_layer: add 1 to *kv.pos_dev when the step is done */
 
 int dv_api_version(void);
 const char* dv_status_str(int status);
@@ -156,6 +157,11 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
  *                     NULL disables hole fill
  *   valid_upto        device int32 [B][h]: last position whose K/V head i
  *                     holds; NULL disables hole fill
+ *   pos_dev           device int32 [1] or NULL: when set, the slot is read
+ *                     from here when the kernels run (so a captured HIP
+ *                     graph can be replayed step after step) and `pos` is
+ *                     only its upper bound, used to size launches; a run-time
+ *                     value outside [0, max_len) makes the step write nothing
  * With hole fill, a selected head whose valid_upto < pos - 1 first gets its
  * K/V at positions valid_upto+1 .. pos-1 recomputed from y_buf, then
  * valid_upto = pos.  Without it, skipped slots keep their old contents.
@@ -167,6 +173,7 @@ typedef struct {
     int pos;
     float* y_buf;
     int32_t* valid_upto;
+    int32_t* pos_dev;
 } dv_kv_state;
 
 /* ------------------------------------------------------------------------
@@ -196,6 +203,8 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
  *   sel_len  device int32 [B][h]: entries of sel_idx in use (<= sel_cap)
  *   sel_end  positions sel_end..n_ctx-1 are always read (the cache keeps
  *            receiving entries, ByteCross §3.2)
+ *   n_ctx_dev device int32 [1] or NULL: when set, the count is read from
+ *            here at run time (clamped to [0, n_ctx]) and n_ctx is its bound
  */
 typedef struct {
     const void* k_cache;
@@ -207,6 +216,7 @@ typedef struct {
     const int32_t* sel_len;
     int sel_cap;
     int sel_end;
+    const int32_t* n_ctx_dev;
 } dv_kv_view;
 
 /* ------------------------------------------------------------------------
@@ -247,6 +257,9 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
  * y2 = LN2(h); S_M = top-k_neurons(SP_M(y2)); x_out = h + MLP_{S_M}(y2).
  * A batch uses the union of its rows' neuron sets (DejaVu App. C.1); head
  * sparsity needs B == 1 in this build (DV_ERR_UNSUPPORTED otherwise).
+ * With st->kv.pos_dev set the step position is read on the device (and
+ * n_ctx = position + 1), so the whole call can be captured in a HIP graph
+ * once and replayed; DV_ADVANCE_POS then moves the position on by one.
  */
 typedef struct {
     int B, d, h, d_h, N;

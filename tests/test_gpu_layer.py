@@ -187,3 +187,41 @@ def test_decode_is_deterministic(dvlib):
         x = synth.layer_inputs(dims.d, 1, 1, seed=6)[0]
         outs.append(L.step(x, 64, 4, 400, dvlib.DV_HOLE_FILL | dvlib.DV_SKIP_NONPOS_FC2)[0])
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_graph_replay_with_device_position(dvlib):
+    """One decode step captured in a HIP graph with the position on the
+    device (DV_ADVANCE_POS) and replayed step after step, with eager input
+    copies and synchronisations in between, matches eager steps driven by
+    host positions, replay by replay."""
+    dims = LayerDims(d=512, N=2048, h=8, d_h=64, r_attn=16, r_mlp=32, wdt="f16")
+    n0, T, L = 20, 6, 40
+    eager = Layer(dvlib, dims, n0, L, seed=7)
+    graph = Layer(dvlib, dims, n0, L, seed=7)
+    X = synth.layer_inputs(dims.d, T, 1, seed=7)
+    flags = dvlib.DV_HOLE_FILL | dvlib.DV_SKIP_NONPOS_FC2
+    pos_dev = torch.full((1,), n0, dtype=torch.int32, device="cuda")
+    cfg = graph.cfg(3, 200, flags | dvlib.DV_ADVANCE_POS)
+    st = dvlib.LayerState()
+    st.kv = dvlib.kv_state(graph.K, graph.V, L - 1, graph.y_buf, graph.valid, pos_dev)
+    ws = dvlib.workspace(dvlib.dv_decode_workspace_bytes(cfg, L))
+    wts = dvlib.layer_weights(graph.Wd)
+    x_in = torch.zeros(1, dims.d, device="cuda")
+    out = torch.zeros(1, dims.d, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dvlib.dv_decode_layer(wts, cfg, st, x_in, out, ws)
+    for t in range(T):
+        want = eager.step(X[t], n0 + t, 3, 200, flags)[0]
+        x_in.copy_(dev(X[t]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        e = normwise(got, want)
+        assert e < 1e-5, f"replay {t}: normwise {e:.2e}"
+    assert int(host(pos_dev)[0]) == n0 + T
+    assert np.array_equal(host(graph.valid), host(eager.valid))
+    ok_k, nk = f16_kv_ok(host(graph.K), host(eager.K))
+    ok_v, nv = f16_kv_ok(host(graph.V), host(eager.V))
+    assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
