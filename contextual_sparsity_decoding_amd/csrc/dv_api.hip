@@ -163,11 +163,12 @@ dv_status dv_topk_select(const float* scores, int B, int n, int k, int32_t* idx,
                          int32_t* union_count, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     (void)ws; (void)ws_bytes;
-    REQ(B >= 1 && B <= 64 && n >= 0 && n <= 65536, DV_ERR_SHAPE, "dv_topk_select: B=%d n=%d", B, n);
+    REQ(B >= 1 && B <= 64 && n >= 0 && n <= dv::kTopkMaxN, DV_ERR_SHAPE, "dv_topk_select: B=%d n=%d", B, n);
     REQ(k >= 0 && k <= n, DV_ERR_RANGE, "dv_topk_select: k=%d outside [0, n=%d]", k, n);
     REQ(k == 0 || (scores && idx), DV_ERR_NULL, "dv_topk_select: NULL pointer");
     REQ((union_idx == nullptr) == (union_count == nullptr), DV_ERR_NULL,
         "dv_topk_select: union_idx and union_count go together");
+    REQ(union_idx == nullptr || n <= dv::kUnionMaxN, DV_ERR_SHAPE, "dv_topk_select: union over n=%d > %d", n, dv::kUnionMaxN);
     hipStream_t s = (hipStream_t)stream;
     TRY(launch_topk(scores, B, n, k, idx, s));
     if (union_idx) TRY(launch_union(idx, B, k, n, union_idx, union_count, s));
@@ -201,8 +202,11 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
     hipStream_t s = (hipStream_t)stream;
     float* a = act_out ? act_out : w.a;
     TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
-    return launch_axpy(w2_t, wdt, d, N, n_idx_max, n_idx_dev, idx, 1, a, n_idx_max, (flags & DV_SKIP_NONPOS_FC2) != 0,
-                       B, b2, residual, out, fc2_rows, w.partial, nullptr, s);
+    AxpyCall c{};
+    c.w = w2_t; c.wdt = wdt; c.d = d; c.w_rows = N; c.rows = n_idx_max; c.n_rows_dev = n_idx_dev; c.idx = idx; c.blk = 1;
+    c.coef = a; c.coef_stride = n_idx_max; c.skip_zero = (flags & DV_SKIP_NONPOS_FC2) != 0;
+    c.B = B; c.bias = b2; c.residual = residual; c.out = out; c.rows_read = fc2_rows; c.partial = w.partial;
+    return launch_axpy(c, s);
 }
 
 // ---------------------------------------------------------------- projections --
@@ -240,8 +244,11 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
     REQ(!overlap(out, (size_t)B * d * 4, in, (size_t)B * n_sel * d_h * 4) &&
             !overlap(out, (size_t)B * d * 4, residual, (size_t)B * d * 4),
         DV_ERR_RANGE, "dv_sparse_attn_proj: out overlaps o or residual");
-    return launch_axpy(w_t, wdt, d, h * d_h, n_sel * d_h, nullptr, head_idx, d_h, in, n_sel * d_h, false, B, bias, residual,
-                       out, nullptr, w.partial, nullptr, s);
+    AxpyCall c{};
+    c.w = w_t; c.wdt = wdt; c.d = d; c.w_rows = h * d_h; c.rows = n_sel * d_h; c.idx = head_idx; c.blk = d_h;
+    c.coef = in; c.coef_stride = n_sel * d_h; c.B = B; c.bias = bias; c.residual = residual; c.out = out;
+    c.partial = w.partial;
+    return launch_axpy(c, s);
 }
 
 // ---------------------------------------------------------------- attention --
@@ -420,9 +427,17 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     int n_sel = h;
     if (!(c->flags & DV_DENSE_ATTN)) {
         int32_t* hi = st->head_idx_out ? st->head_idx_out : L.head_idx;
-        TRY(launch_predict_ln(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, w->pa1_t, c->r_attn, w->pa2_t, h, c->wdt,
-                              c->pred_act, L.sA, L.hpart, s));
-        TRY(launch_topk(L.sA, B, h, c->k_heads, hi, s));
+        if (pred_topk_fusable(B, h, c->r_attn)) {
+            if (c->k_heads > 0)
+                TRY(launch_predict_ln_topk(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.y, w->pa1_t, c->r_attn, w->pa2_t, h,
+                                           c->wdt, c->pred_act, L.sA, L.hpart, c->k_heads, hi, s));
+            else
+                TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+        } else {
+            TRY(launch_predict_ln(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, w->pa1_t, c->r_attn, w->pa2_t, h,
+                                  c->wdt, c->pred_act, L.sA, L.hpart, s));
+            TRY(launch_topk(L.sA, B, h, c->k_heads, hi, s));
+        }
         head_idx = hi;
         n_sel = c->k_heads;
     } else {
@@ -435,10 +450,17 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     }
     const bool fill = kvs.y_buf && kvs.valid_upto;
     TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
-    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, L.o, L.apart,
-                      fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s));
-    TRY(launch_axpy(w->w_o_t, c->wdt, d, h * dh, n_sel * dh, nullptr, head_idx, dh, L.o, n_sel * dh, false, B, w->b_o, x_in,
-                    L.hres, nullptr, L.xpart, nullptr, s));
+    // split-K partials go straight into the output projection, which merges them per row
+    int splits = 0;
+    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
+                      fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s, &splits));
+    {
+        AxpyCall ac{};
+        ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;
+        ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = B; ac.bias = w->b_o; ac.residual = x_in;
+        ac.out = L.hres; ac.partial = L.xpart;
+        TRY(launch_axpy(ac, s));
+    }
     // MLP block: LN2 folded into the neuron predictor
     const int32_t* idx = nullptr;
     const int32_t* n_dev = nullptr;
@@ -465,9 +487,12 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
         TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
     }
     TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
-    return launch_axpy(w->w2_t, c->wdt, d, N, n_max, n_dev, idx, 1, L.a, n_max, (c->flags & DV_SKIP_NONPOS_FC2) != 0, B,
-                       w->b2, L.hres, x_out, st->fc2_rows_out, L.xpart,
-                       (c->flags & DV_ADVANCE_POS) ? kv.pos_dev : nullptr, s);
+    AxpyCall mc{};
+    mc.w = w->w2_t; mc.wdt = c->wdt; mc.d = d; mc.w_rows = N; mc.rows = n_max; mc.n_rows_dev = n_dev; mc.idx = idx;
+    mc.blk = 1; mc.coef = L.a; mc.coef_stride = n_max; mc.skip_zero = (c->flags & DV_SKIP_NONPOS_FC2) != 0; mc.B = B;
+    mc.bias = w->b2; mc.residual = L.hres; mc.out = x_out; mc.rows_read = st->fc2_rows_out; mc.partial = L.xpart;
+    mc.advance = (c->flags & DV_ADVANCE_POS) ? kv.pos_dev : nullptr;
+    return launch_axpy(mc, s);
 }
 
 }  // extern "C"

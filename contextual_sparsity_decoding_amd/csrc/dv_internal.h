@@ -22,6 +22,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kBlock = 256;          // 4 waves per workgroup
 constexpr size_t kYLdsMax = 64 * 1024;
+constexpr int kTopkMaxN = 1 << 22;          // longest row dv_topk_select takes
+constexpr int kUnionMaxN = 1 << 18;         // union bitmap in LDS: n / 8 bytes
+constexpr int kTopkStage = 8192;            // selected sets up to this size leave through LDS
 
 // ---- element traits: E elements of T per 16-byte chunk --------------------
 template <typename T> struct Vec;
@@ -49,21 +52,51 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[4], float) {
 template <typename T>
 __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 
-// ---- reductions (fixed butterfly order, so results are deterministic) ------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+// ---- cross-lane moves and reductions --------------------------------------
+// DPP (data-parallel primitives) move values between lanes inside the VALU
+// instruction itself, with no trip through the LDS crossbar.  gfx9 control
+// words: quad_perm 0x00-0xff, row_shr:n 0x110+n, row_ror:n 0x120+n,
+// row_mirror 0x140, row_half_mirror 0x141, row_bcast:15 0x142,
+// row_bcast:31 0x143.  A row is 16 lanes.  Lanes that a control word or a
+// row mask leaves without a source keep `old`, here 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of G lanes (G divides 16, or 64), every lane of a
+// group gets its group's sum.  The order of additions is fixed, so results
+// are deterministic.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "power of two lanes");
+    if constexpr (G >= 2) v += dpp_f32<0xb1>(v);          // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (G >= 4) v += dpp_f32<0x4e>(v);          // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (G >= 8) v += dpp_f32<0x141>(v);         // half-row mirror: the other quad
+    if constexpr (G >= 16) v += dpp_f32<0x140>(v);        // row mirror: the other half-row
+    if constexpr (G == 32) v += __shfl_xor(v, 16, kWave);  // the neighbouring row
+    if constexpr (G == 64)
+        v = (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float group_sum_dyn(float v, int G) {
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    switch (G) {
+        case 1: return v;
+        case 2: return group_sum<2>(v);
+        case 4: return group_sum<4>(v);
+        case 8: return group_sum<8>(v);
+        case 16: return group_sum<16>(v);
+        case 32: return group_sum<32>(v);
+        default: return group_sum<64>(v);
+    }
 }
 
 // Dot products of one weight row (nchunk 16-byte chunks of T) with NB fp32
@@ -120,37 +153,33 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the wave: shifts of 1, 2, 4, 8 inside each row,
+// then row totals carried forward by the row broadcasts.
 __device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
+    v += dpp_u32<0x111>(v);
+    v += dpp_u32<0x112>(v);
+    v += dpp_u32<0x114>(v);
+    v += dpp_u32<0x118>(v);
+    v += dpp_u32<0x142, 0xa>(v);                          // lane 15 of rows 0, 2 into rows 1, 3
+    v += dpp_u32<0x143, 0xc>(v);                          // lane 31 into rows 2, 3
     return v;
 }
 
 // Exclusive prefix sum over the block (<= 1024 threads); *total gets the sum.
-__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tot /* >= 17 */, unsigned* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+// Every wave combines the wave totals itself, so no lane waits on a serial
+// pass.  `tot` holds >= 16 words and may be reused by the next call.
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tot, unsigned* total) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nw = (int)(blockDim.x >> 6);
     const unsigned incl = wave_incl_scan(v);
-    __syncthreads();
+    __syncthreads();                                      // a previous call may still read tot
     if (lane == 63) tot[w] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const unsigned t = tot[i];
-            tot[i] = run;
-            run += t;
-        }
-        tot[16] = run;
-    }
-    __syncthreads();
-    const unsigned r = tot[w] + incl - v;
-    *total = tot[16];
-    __syncthreads();
-    return r;
+    const unsigned ts = wave_incl_scan(lane < nw ? tot[lane] : 0u);
+    const unsigned before = w > 0 ? (unsigned)__builtin_amdgcn_readlane((int)ts, w - 1) : 0u;
+    *total = (unsigned)__builtin_amdgcn_readlane((int)ts, 63);
+    return before + incl - v;
 }
 
 // Load a small vector from global memory into LDS with the whole block.
@@ -203,10 +232,26 @@ struct AxpyPlan {
 };
 AxpyPlan axpy_plan(int d, int rows, int wdt);
 size_t axpy_ws_floats(const AxpyPlan& p, int B, int d);
-dv_status launch_axpy(const void* w, int wdt, int d, int w_rows, int rows, const int32_t* n_rows_dev,
-                      const int32_t* idx, int blk, const float* coef, int coef_stride, bool skip_zero,
-                      int B, const void* bias, const float* residual, float* out, int32_t* rows_read,
-                      float* partial, int32_t* advance, hipStream_t s);
+struct AxpyCall {
+    const void* w;            // W [w_rows][d]
+    int wdt, d, w_rows, rows;
+    const int32_t* n_rows_dev;
+    const int32_t* idx;       // row(u) = idx[u / blk] * blk + u % blk, or u when NULL
+    int blk;
+    const float* coef;        // [B][coef_stride], or NULL with apart
+    int coef_stride;
+    bool skip_zero;
+    const float* apart;       // split-K attention partials giving the coefficients, or NULL
+    int num_splits;
+    int B;
+    const void* bias;
+    const float* residual;
+    float* out;
+    int32_t* rows_read;
+    float* partial;
+    int32_t* advance;
+};
+dv_status launch_axpy(const AxpyCall& c, hipStream_t s);
 bool qkv_supported(int B, int d, int wdt);
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
                      const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
@@ -215,6 +260,10 @@ bool ln_fusable(int B, int d);
 dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
                             const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
                             float* hid, hipStream_t s);
+bool pred_topk_fusable(int B, int n_out, int r);
+dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
+                                 const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act,
+                                 float* scores, float* hid, int k, int32_t* idx, hipStream_t s);
 int topk_block_threads(int n);
 dv_status launch_set_i32(int32_t* p, int v, hipStream_t s);
 dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hipStream_t s);
@@ -223,7 +272,8 @@ dv_status launch_union(const int32_t* idx, int B, int k, int n, int32_t* union_i
 int splitk_auto(int max_positions, int rows);
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
-                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s);
+                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,
+                        int* splits_used = nullptr);
 dv_status launch_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv,
                           float scale, int n_sink, int n_window, int width, float* scores,
                           float* raw, float* stats, hipStream_t s);

@@ -260,10 +260,12 @@ int splitk_auto(int max_positions, int rows) {
 
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
-                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s) {
-    if (n_sel == 0) return DV_OK;
+                        float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,
+                        int* splits_used) {
     const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
     if (num_splits <= 0) num_splits = splitk_auto(maxpos, B * n_sel);
+    if (splits_used) *splits_used = num_splits;
+    if (n_sel == 0) return DV_OK;
     AttnArgs a;
     a.q = q; a.B = B; a.n_sel = n_sel; a.h = kv->h; a.head_idx = head_idx;
     a.K = (const half_t*)kv->k_cache; a.V = (const half_t*)kv->v_cache;
@@ -279,8 +281,9 @@ dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx,
 #define DV_ATT(DH)                                                                                   \
     case DH:                                                                                         \
         hipLaunchKernelGGL((k_attn_split<DH>), dim3(cdiv(tasks, 4)), dim3(kBlock), 0, s, a);        \
-        hipLaunchKernelGGL((k_attn_combine<DH>), dim3(rows), dim3(kBlock), 0, s, part, rows,        \
-                           num_splits, o);                                                           \
+        if (o)                                                                                       \
+            hipLaunchKernelGGL((k_attn_combine<DH>), dim3(rows), dim3(kBlock), 0, s, part, rows,    \
+                               num_splits, o);                                                       \
         break;
     switch (d_h) {
         DV_ATT(32) DV_ATT(64) DV_ATT(128) DV_ATT(256)

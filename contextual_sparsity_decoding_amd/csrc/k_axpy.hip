@@ -7,18 +7,27 @@
 // selected neuron or head is a contiguous run of rows.
 //
 // Work split: the d output columns are cut into slices of one wave-load
-// (64 lanes x 16 bytes); the selected rows into groups of up to 64.  A
-// workgroup (4 waves) first stages its group's row indices and coefficients
-// in LDS (one batch of loads, an ordered compaction that drops rows whose
-// coefficients are all zero when asked), then every wave issues its weight
-// loads back to back, reduces across the 4 waves in LDS and writes one
-// partial sum per group.  k_axpy_finalize adds the partials in a fixed
-// order, plus bias and residual.  Results do not depend on scheduling.
+// (64 lanes x 16 bytes); the selected rows into groups of 64.  A workgroup
+// (4 waves) takes one (slice, group): it resolves its rows, issues all 64
+// row loads at once (16 per wave), obtains the coefficients meanwhile, then
+// accumulates, reduces its 4 waves in LDS and writes one partial sum.
+//
+// Coefficients come either from memory (compacted in order, dropping rows
+// whose coefficients are all zero when asked) or, for the output projection
+// of a decode layer, straight from the split-K attention partials: the
+// workgroup merges a head's splits (running max, rescaled sums) for its own
+// rows, so no separate combine pass runs.
+//
+// k_axpy_finalize then adds the partials in a fixed order, plus bias and
+// residual.  Results do not depend on scheduling.
 #include "dv_internal.h"
+
+#include <math.h>
 
 namespace dv {
 
 constexpr int kRowsPerGroup = 64;
+constexpr int kAxpyU = kRowsPerGroup / 4;    // row loads per wave
 
 struct AxpyArgs {
     const void* w;
@@ -29,20 +38,93 @@ struct AxpyArgs {
     const float* coef;        // coef[b * coef_stride + u]
     int coef_stride;
     int skip_zero;
+    const float* apart;       // attention partials [B][rows / blk][num_splits][blk + 2], or NULL
+    int num_splits;
     int B, n_groups;
     float* partial;           // [n_groups][B][d]
     int32_t* rows_read;
 };
 
-template <typename T, int NB, int U>
+// Coefficient of row u = s * dh + e for batch row b: the attention output
+// o[b][s][e] = sum_c 2^(m_c - M) acc_c[e] / sum_c 2^(m_c - M) l_c over the
+// splits c with l_c > 0 (log2-domain partials).  Wave q merges its quarter
+// of the splits with a running maximum; the quarters are merged in order.
+template <int NB>
+__device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, float* s_cf,
+                                          float (*s_q)[kRowsPerGroup][NB][3]) {
+    constexpr int CB = 8;                          // splits in flight
+    const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int dh = a.blk, ns = a.num_splits;
+    const int n_sel = a.rows / dh;
+    const bool ok = t < nlive;
+    const int u = r0 + (ok ? t : 0);
+    const int s = u / dh, e = u % dh;
+    const int per = (ns + 3) / 4;
+    const int c0 = q * per, c1 = min(ns, c0 + per);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float m = -INFINITY, l = 0.f, num = 0.f;
+        if (b < a.B && ok) {
+            const float* P = a.apart + ((size_t)(b * n_sel + s) * ns) * (dh + 2);
+            for (int cb = c0; cb < c1; cb += CB) {
+                float mc[CB], lc[CB], ac[CB];
+#pragma unroll
+                for (int i = 0; i < CB; ++i) {
+                    const bool in = cb + i < c1;
+                    const float* pc = P + (size_t)(in ? cb + i : c0) * (dh + 2);
+                    mc[i] = pc[dh];
+                    lc[i] = in ? pc[dh + 1] : 0.f;
+                    ac[i] = pc[e];
+                }
+#pragma unroll
+                for (int i = 0; i < CB; ++i) {
+                    if (!(lc[i] > 0.f)) continue;
+                    const float M = fmaxf(m, mc[i]);
+                    const float sa = exp2f(m - M), sb = exp2f(mc[i] - M);
+                    num = num * sa + ac[i] * sb;
+                    l = l * sa + lc[i] * sb;
+                    m = M;
+                }
+            }
+        }
+        s_q[q][t][b][0] = m;
+        s_q[q][t][b][1] = l;
+        s_q[q][t][b][2] = num;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRowsPerGroup) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float m = -INFINITY, l = 0.f, num = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const float mq = s_q[qq][t][b][0], lq = s_q[qq][t][b][1], nq = s_q[qq][t][b][2];
+                if (!(lq > 0.f)) continue;
+                const float M = fmaxf(m, mq);
+                const float sa = exp2f(m - M), sb = exp2f(mq - M);
+                num = num * sa + nq * sb;
+                l = l * sa + lq * sb;
+                m = M;
+            }
+            s_cf[t * NB + b] = l > 0.f ? num / l : 0.f;
+        }
+    }
+}
+
+template <typename T, int NB, bool ATTN>
 __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     constexpr int E = Vec<T>::E;
     constexpr int SW = kWave * E;                  // columns per slice
     constexpr int NBC = NB < 4 ? NB : 4;           // batch rows per LDS reduction round
+    constexpr int NQ = ATTN ? NB : 1;
+    constexpr int RED = 3 * NBC * SW, QF = ATTN ? 4 * kRowsPerGroup * NQ * 3 : 0;
     __shared__ int s_row[kRowsPerGroup];
     __shared__ float s_cf[kRowsPerGroup * NB];
-    __shared__ float red[3][NBC][SW];
+    __shared__ float shbuf[RED > QF ? RED : QF];   // split merging, then the wave reduction
     __shared__ unsigned tot[17];
+    auto red = reinterpret_cast<float (*)[NBC][SW]>(shbuf);
+    auto s_q = reinterpret_cast<float (*)[kRowsPerGroup][NQ][3]>(shbuf);
+    __shared__ int s_last;
     const T* W = (const T*)a.w;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, g = blockIdx.y;
@@ -51,63 +133,84 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
     const int r0 = g * kRowsPerGroup;
 
-    // ---- prologue: this group's rows and coefficients, compacted in order
-    bool live = false;
-    int row = 0;
-    float cf[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) cf[b] = 0.f;
-    if (threadIdx.x < kRowsPerGroup && r0 + (int)threadIdx.x < rows) {
-        const int u = r0 + threadIdx.x;
-        row = a.idx ? a.idx[u / a.blk] * a.blk + u % a.blk : u;
-        bool any = false;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            cf[b] = b < a.B ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
-            any |= cf[b] != 0.f;
+    // ---- this group's rows (and coefficients read from memory), in order
+    int nlive;
+    if (ATTN) {
+        // every selected row is used; an index outside W reads nothing
+        nlive = max(0, min(kRowsPerGroup, rows - r0));
+        if (threadIdx.x < kRowsPerGroup) {
+            const int u = r0 + threadIdx.x;
+            int row = -1;
+            if ((int)threadIdx.x < nlive) {
+                const int hb = a.idx ? a.idx[u / a.blk] : u / a.blk;
+                if ((unsigned)hb < (unsigned)(a.w_rows / a.blk)) row = hb * a.blk + u % a.blk;
+            }
+            s_row[threadIdx.x] = row;
         }
-        live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
-    }
-    unsigned nlive;
-    const unsigned slot = block_excl_scan(live ? 1u : 0u, tot, &nlive);
-    if (live) {
-        s_row[slot] = row;
+    } else {
+        bool live = false;
+        int row = 0;
+        float cf[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) s_cf[slot * NB + b] = cf[b];
+        for (int b = 0; b < NB; ++b) cf[b] = 0.f;
+        if (threadIdx.x < kRowsPerGroup && r0 + (int)threadIdx.x < rows) {
+            const int u = r0 + threadIdx.x;
+            row = a.idx ? a.idx[u / a.blk] * a.blk + u % a.blk : u;
+            bool any = false;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                cf[b] = b < a.B ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
+                any |= cf[b] != 0.f;
+            }
+            live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
+        }
+        unsigned nl;
+        const unsigned slot = block_excl_scan(live ? 1u : 0u, tot, &nl);
+        nlive = (int)min(nl, (unsigned)kRowsPerGroup);
+        if (live && slot < (unsigned)kRowsPerGroup) {
+            s_row[slot] = row;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) s_cf[slot * NB + b] = cf[b];
+        }
+        if (a.rows_read && slice == 0 && threadIdx.x == 0 && nl > 0) atomicAdd(a.rows_read, (int)nl);
     }
     __syncthreads();
-    if (a.rows_read && slice == 0 && threadIdx.x == 0 && nlive > 0) atomicAdd(a.rows_read, (int)nlive);
 
-    // ---- stream the live rows: wave wv takes rows wv, wv+4, ...
+    // ---- all of this wave's row loads in flight: rows wv, wv + 4, ...
+    u32x4 w[kAxpyU];
+#pragma unroll
+    for (int t = 0; t < kAxpyU; ++t) {
+        const int k = wv + 4 * t;
+        const int rr = k < nlive ? s_row[k] : -1;
+        w[t] = (rr >= 0 && colok) ? ld16_stream(W + (size_t)rr * a.d + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (ATTN) {
+        attn_coef<NQ>(a, r0, nlive, s_cf, s_q);
+        __syncthreads();
+    }
+
     float acc[NB][E];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[b][e] = 0.f;
-    for (int k0 = wv; k0 < (int)nlive; k0 += 4 * U) {
-        u32x4 w[U];
 #pragma unroll
-        for (int t = 0; t < U; ++t) {
-            const int k = k0 + 4 * t;
-            w[t] = (k < (int)nlive && colok) ? ld16_stream(W + (size_t)s_row[k] * a.d + col) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int t = 0; t < kAxpyU; ++t) {
+        const int k = wv + 4 * t;
+        if (k < nlive) {
+            float f[E];
+            unpack(w[t], f, T());
 #pragma unroll
-        for (int t = 0; t < U; ++t) {
-            const int k = k0 + 4 * t;
-            if (k < (int)nlive) {
-                float f[E];
-                unpack(w[t], f, T());
+            for (int b = 0; b < NB; ++b) {
+                const float c = s_cf[k * NB + b];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const float c = s_cf[k * NB + b];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[b][e] = fmaf(c, f[e], acc[b][e]);
-                }
+                for (int e = 0; e < E; ++e) acc[b][e] = fmaf(c, f[e], acc[b][e]);
             }
         }
     }
 
-    // ---- reduce the 4 waves into wave 0, NBC batch rows at a time
+    // ---- reduce the 4 waves into wave 0, NBC batch rows at a time; wave 0
+    // writes the group's partial
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += NBC) {
         if (wv > 0) {
@@ -135,6 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
         }
         __syncthreads();
     }
+
 }
 
 // out[b][c] = residual[b][c] + bias[c] + sum_g partial[g][b][c].  A block
@@ -199,35 +303,36 @@ size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_grou
 
 template <typename T, int NB>
 static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
-    hipLaunchKernelGGL((k_axpy<T, NB, 16>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
+    if (a.apart)
+        hipLaunchKernelGGL((k_axpy<T, NB, true>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_axpy<T, NB, false>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
 }
 
-dv_status launch_axpy(const void* w, int wdt, int d, int w_rows, int rows, const int32_t* n_rows_dev,
-                      const int32_t* idx, int blk, const float* coef, int coef_stride, bool skip_zero,
-                      int B, const void* bias, const float* residual, float* out, int32_t* rows_read,
-                      float* partial, int32_t* advance, hipStream_t s) {
-    const AxpyPlan p = axpy_plan(d, rows, wdt);
+dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
+    const AxpyPlan p = axpy_plan(c.d, c.rows, c.wdt);
     AxpyArgs a;
-    a.w = w; a.d = d; a.w_rows = w_rows; a.rows = rows; a.n_rows_dev = n_rows_dev; a.idx = idx; a.blk = blk;
-    a.coef = coef; a.coef_stride = coef_stride; a.skip_zero = skip_zero ? 1 : 0;
-    a.B = B; a.n_groups = p.n_groups; a.partial = partial; a.rows_read = rows_read;
-    const int nb = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16;
+    a.w = c.w; a.d = c.d; a.w_rows = c.w_rows; a.rows = c.rows; a.n_rows_dev = c.n_rows_dev; a.idx = c.idx;
+    a.blk = c.blk; a.coef = c.coef; a.coef_stride = c.coef_stride; a.skip_zero = c.skip_zero ? 1 : 0;
+    a.apart = c.apart; a.num_splits = c.num_splits;
+    a.B = c.B; a.n_groups = p.n_groups; a.partial = c.partial; a.rows_read = c.rows_read;
+    const int nb = c.B <= 1 ? 1 : c.B <= 2 ? 2 : c.B <= 4 ? 4 : c.B <= 8 ? 8 : 16;
 #define DV_AXPY(NB)                                                            \
     case NB:                                                                   \
-        if (wdt == DV_F16) axpy_go<half_t, NB>(a, p.n_slices, s);              \
+        if (c.wdt == DV_F16) axpy_go<half_t, NB>(a, p.n_slices, s);            \
         else axpy_go<float, NB>(a, p.n_slices, s);                             \
         break;
     switch (nb) {
         DV_AXPY(1) DV_AXPY(2) DV_AXPY(4) DV_AXPY(8) DV_AXPY(16)
     }
 #undef DV_AXPY
-    const dim3 fg(cdiv(d / 4, 64), B);
-    if (wdt == DV_F16)
-        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, partial, p.n_groups, B, d, bias, residual,
-                           out, advance);
+    const dim3 fg(cdiv(c.d / 4, 64), c.B);
+    if (c.wdt == DV_F16)
+        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
+                           c.residual, c.out, c.advance);
     else
-        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, partial, p.n_groups, B, d, bias, residual,
-                           out, advance);
+        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
+                           c.residual, c.out, c.advance);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DV_OK;

@@ -164,6 +164,62 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict_
     }
 }
 
+// The predictor's second layer fused with the selection for a short score
+// row (n_out <= 256, e.g. heads; batch row 0): thread j scores row j of P2
+// (all its r-element loads in flight at once), then ranks its key against
+// the others in LDS; rank < k selects it, and a block scan writes the set
+// ascending.  Same order as k_topk: score descending, ties to the lower
+// index, NaN last.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_pred_topk_small(const float* __restrict__ hid_in, int r, int act,
+                                                            const T* __restrict__ p2, int n_out,
+                                                            float* __restrict__ scores, int k,
+                                                            int32_t* __restrict__ idx) {
+    constexpr int E = Vec<T>::E;
+    constexpr int CB = 16;                               // chunk loads in flight per batch
+    __shared__ float hid[512];
+    __shared__ uint32_t keys[kBlock];
+    __shared__ unsigned tot[17];
+    const int j = threadIdx.x;
+    const int rchunk = r / E;
+    for (int i = threadIdx.x; i < r; i += kBlock) {
+        const float v = hid_in[i];
+        hid[i] = act == DV_ACT_RELU ? fmaxf(v, 0.f) : v;
+    }
+    const T* row = p2 + (size_t)(j < n_out ? j : 0) * r;
+    float acc = 0.f;
+    for (int c0 = 0; c0 < rchunk; c0 += CB) {
+        u32x4 w[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            w[c] = (j < n_out && c0 + c < rchunk) ? ld16(row + (size_t)(c0 + c) * E) : u32x4{0u, 0u, 0u, 0u};
+        if (c0 == 0) __syncthreads();                    // hid staged
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            if (c0 + c < rchunk) {
+                float f[E];
+                unpack(w[c], f, T());
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc = fmaf(f[e], hid[(c0 + c) * E + e], acc);
+            }
+        }
+    }
+    if (rchunk == 0) __syncthreads();
+    const uint32_t kj = j < n_out ? order_key(acc) : 0u;
+    if (j < n_out) scores[j] = acc;
+    keys[j] = kj;
+    __syncthreads();
+    unsigned rank = 0;
+    for (int i = 0; i < n_out; ++i) {
+        const uint32_t ki = keys[i];
+        rank += (ki > kj) || (ki == kj && i < j);
+    }
+    const bool sel = j < n_out && rank < (unsigned)k;
+    unsigned total;
+    const unsigned pos = block_excl_scan(sel ? 1u : 0u, tot, &total);
+    if (sel && pos < (unsigned)k) idx[pos] = j;
+}
+
 }  // namespace dv
 
 namespace dvh {
@@ -270,5 +326,36 @@ dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const 
     return DV_OK;
 }
 
+bool pred_topk_fusable(int B, int n_out, int r) { return B == 1 && n_out <= kBlock && r <= 512; }
+
+dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
+                                 const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act,
+                                 float* scores, float* hid, int k, int32_t* idx, hipStream_t s) {
+    if (ln_fusable(1, d) && ch_tier(d, wdt) != 0) {
+        RowArgs a{};
+        a.y = nullptr; a.B = 1; a.d = d; a.w = p1_t; a.n_max = r; a.w_rows = r; a.out = hid;
+        LnArgs ln{x, g, b, eps, y_out};
+        dv_status st = wdt == DV_F16 ? predict_ln_t<half_t>(a, ln, ch_tier(d, wdt), s)
+                                     : predict_ln_t<float>(a, ln, ch_tier(d, wdt), s);
+        if (st != DV_OK) return st;
+    } else {
+        dv_status st = launch_layernorm(x, 1, d, g, b, eps, y_out, s);
+        if (st != DV_OK) return st;
+        RowArgs a{};
+        a.y = y_out; a.B = 1; a.d = d; a.w = p1_t; a.bias = nullptr; a.idx = nullptr;
+        a.n_max = r; a.n_dev = nullptr; a.w_rows = r; a.out = hid;
+        st = rowdot_plain(a, wdt, s);
+        if (st != DV_OK) return st;
+    }
+    DV_LAUNCH_CHECK();
+    if (wdt == DV_F16)
+        hipLaunchKernelGGL(k_pred_topk_small<half_t>, dim3(1), dim3(kBlock), 0, s, hid, r, act, (const half_t*)p2_t,
+                           n_out, scores, k, idx);
+    else
+        hipLaunchKernelGGL(k_pred_topk_small<float>, dim3(1), dim3(kBlock), 0, s, hid, r, act, (const float*)p2_t,
+                           n_out, scores, k, idx);
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
 
 }  // namespace dvh

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot(RowArgs a, int rpg) {
         const int j = a.idx ? a.idx[u] : u;
         my_j = (unsigned)j < (unsigned)a.w_rows ? j : -1;   // an index outside W selects nothing
     }
-    auto row_of = [&](int k) -> int { return __shfl(my_j, k, kWave); };
+    auto row_of = [&](int k) -> int { return __builtin_amdgcn_readlane(my_j, k); };   // k is wave-uniform
     u32x4 wa[CH], wb[CH];
     int ja = nk > 0 ? row_of(0) : -1, jb = -1;
     if (ja >= 0) load_row<T, CH, true>((const T*)a.w + (size_t)ja * a.d, nchunk, wa);

@@ -6,212 +6,312 @@
 // The pages do not describe the selection kernel; this one is exact:
 //
 //   order:  score descending, ties to the lower index, NaN after numbers.
-//   method: radix select on order-preserving uint32 keys, 8 bits per pass,
-//           finds the k-th key T and how many keys equal to T to take; then
-//           one ordered compaction (block prefix sums over contiguous index
-//           ranges per thread) writes the set in ascending index order.
+//   method: radix select on order-preserving uint32 keys, 12, 12 and 8 bits
+//           per pass (stopping once a bin is taken whole), finds the k-th
+//           key T and how many keys equal to T to take; then one ordered
+//           compaction (block prefix sums over contiguous index ranges per
+//           thread) writes the set in ascending index order.
 #include "dv_internal.h"
 
 namespace dv {
 
-__device__ __forceinline__ float key_value(uint32_t k) {
-    const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-    return __builtin_bit_cast(float, u);
-}
-
-// Value-linear bin of a finite key: monotone in the score (the fp32
-// subtraction, the product with a positive scale and the floor are all
-// monotone), so equal scores share a bin and a larger score never falls in
-// a lower bin.
-__device__ __forceinline__ int value_bin(uint32_t k, float vmin, float scale) {
-    const float t = (key_value(k) - vmin) * scale;
-    const int b = (int)t;
-    return b < 0 ? 0 : b > 4095 ? 4095 : b;
-}
-
-// Exact top-k of one row by a 4096-bin histogram pass over value-linear
-// bins between the row's min and max, then radix passes of 12, 12 and 8 bits
-// over the keys of the boundary bin only.  After any pass, when every
-// candidate left in the chosen bin is needed, the selection is complete.
-// Rows with NaN or infinite scores skip the value pass (plain key radix).
-template <int EMAX>
-__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores, int n, int k,
-                                               int32_t* __restrict__ idx) {
-    constexpr int NBIN = 4096;
-    __shared__ unsigned hist[NBIN];
-    __shared__ unsigned tot[17];
-    __shared__ uint32_t red_min[16], red_max[16];
-    __shared__ unsigned red_nan[16];
-    __shared__ unsigned sh_digit, sh_above, sh_bin;
-    const float* s = scores + (size_t)blockIdx.x * n;
-    int32_t* out = idx + (size_t)blockIdx.x * k;
-    const int nt = blockDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int E = (n + nt - 1) / nt;
-    const int i0 = tid * E;
-    uint32_t key[EMAX];
-    if ((E & 3) == 0 && (n & 3) == 0 && ((uintptr_t)s & 15u) == 0) {   // contiguous float4 runs per thread
+// Digit search over a filled histogram of nb bins: the digit whose bin
+// holds the krem-th largest candidate (bins scanned from the top, 4 per
+// thread).  *above = candidates in higher bins, *inbin = in the chosen bin.
+// Each thread zeroes the bins it read, ready for the next pass (the
+// barriers inside order that before any later histogram update).
+__device__ __forceinline__ unsigned find_digit(unsigned* hist, int nb, unsigned krem, unsigned* tot,
+                                               unsigned* sh, unsigned* above, unsigned* inbin) {
+    unsigned c[4], local = 0u;
 #pragma unroll
-        for (int e = 0; e < EMAX; e += 4) {
-            if (e < E && i0 + e < n) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(s + i0 + e);
-                key[e] = order_key(v[0]); key[e + 1] = order_key(v[1]);
-                key[e + 2] = order_key(v[2]); key[e + 3] = order_key(v[3]);
-            } else {
-                key[e] = key[e + 1] = key[e + 2] = key[e + 3] = 0u;
-            }
+    for (int i = 0; i < 4; ++i) {
+        const int p = 4 * (int)threadIdx.x + i;
+        c[i] = p < nb ? hist[nb - 1 - p] : 0u;
+        if (p < nb) hist[nb - 1 - p] = 0u;
+        local += c[i];
+    }
+    unsigned total;
+    unsigned run = block_excl_scan(local, tot, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = 4 * (int)threadIdx.x + i;
+        if (p < nb && run < krem && run + c[i] >= krem) {
+            sh[0] = (unsigned)(nb - 1 - p);
+            sh[1] = run;
+            sh[2] = c[i];
+        }
+        run += c[i];
+    }
+    __syncthreads();
+    const unsigned d = sh[0];
+    *above = sh[1];
+    *inbin = sh[2];
+    __syncthreads();
+    return d;
+}
+
+// Add the valid keys (slot < lim) whose masked high bits equal `prefix` to
+// the histogram of digit (key >> shift) & dmask.  After the first pass few
+// keys are candidates, and a wave with none skips the update.
+template <int E>
+__device__ __forceinline__ void hist_keys(const uint32_t (&key)[E], int lim, uint32_t prefix, uint32_t pmask,
+                                          int shift, uint32_t dmask, unsigned* hist) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (((key[e] & pmask) == prefix) && e < lim) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+}
+
+// Exact top-k of one row (row = blockIdx.x) by 1024 threads.  Thread t
+// holds the E consecutive elements [i0, i0 + E) of each tile of 1024*E
+// elements; keys stay in registers when the row is one tile, else every
+// pass re-reads its tiles (the row is L2-resident).  Radix passes of 12,
+// 12 and 8 bits over order keys find the k-th key; a pass stops the search
+// early when every candidate left in its bin is needed.  The selected
+// indices are written ascending by an ordered prefix sum over threads.
+template <int E>
+__device__ __forceinline__ void load_keys(const float* __restrict__ s, int n, int i0, bool vec, uint32_t (&key)[E]) {
+    if (vec && i0 + E <= n) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(s + i0 + e);
+            key[e] = order_key(v[0]); key[e + 1] = order_key(v[1]);
+            key[e + 2] = order_key(v[2]); key[e + 3] = order_key(v[3]);
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e) key[e] = (e < E && i0 + e < n) ? order_key(s[i0 + e]) : 0u;
+        for (int e = 0; e < E; ++e) key[e] = i0 + e < n ? order_key(s[i0 + e]) : 0u;
     }
-    auto valid = [&](int e) { return e < E && i0 + e < n; };
+}
 
-    // ---- row statistics: NaN count (key 0), min and max key of the rest
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    unsigned nnan = 0;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-        if (valid(e)) {
-            if (key[e] == 0u) {
-                ++nnan;
-            } else {
-                kmin = min(kmin, key[e]);
-                kmax = max(kmax, key[e]);
-            }
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
-        nnan += (unsigned)__shfl_xor((int)nnan, o, kWave);
-    }
-    if (lane == 0) {
-        red_min[wv] = kmin;
-        red_max[wv] = kmax;
-        red_nan[wv] = nnan;
-    }
-    __syncthreads();
-    kmin = 0xffffffffu; kmax = 0u; nnan = 0;
-    for (int i = 0; i < (nt >> 6); ++i) {
-        kmin = min(kmin, red_min[i]);
-        kmax = max(kmax, red_max[i]);
-        nnan += red_nan[i];
-    }
-    const float vmin = key_value(kmin), vmax = key_value(kmax);
-    const bool binned = nnan == 0 && kmin <= kmax && isfinite(vmin) && isfinite(vmax) && isfinite(vmax - vmin);
-    const float scale = (binned && vmax > vmin) ? (float)(NBIN - 1) / (vmax - vmin) : 0.f;
+template <int E>
+__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores, int n, int k,
+                                               int32_t* __restrict__ idx) {
+    __shared__ unsigned hist[4096];
+    __shared__ int32_t stage[kTopkStage];
+    __shared__ unsigned tot[17];
+    __shared__ unsigned sh[3];
+    static_assert(E % 4 == 0, "E is a multiple of 4");
+    const float* s = scores + (size_t)blockIdx.x * n;
+    int32_t* out = idx + (size_t)blockIdx.x * k;
+    const int tile = 1024 * E;
+    const int ntile = (n + tile - 1) / tile;
+    const bool vec = (n & 3) == 0 && ((uintptr_t)s & 15u) == 0;
+    uint32_t key[E];
+    if (ntile == 1) load_keys<E>(s, n, (int)threadIdx.x * E, vec, key);
+    for (int i = threadIdx.x; i < 4096; i += blockDim.x) hist[i] = 0u;   // while the loads fly
 
     unsigned krem = (unsigned)k;
-    int bin_d = -1;                        // the boundary value bin (binned rows)
-    bool early = false;
-    if (binned) {
-        for (int i = tid; i < NBIN; i += nt) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < EMAX; ++e)
-            if (valid(e)) atomicAdd(&hist[value_bin(key[e], vmin, scale)], 1u);
-        __syncthreads();
-        unsigned c[4], local = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = 4 * tid + i;
-            c[i] = p < NBIN ? hist[NBIN - 1 - p] : 0u;
-            local += c[i];
-        }
-        unsigned total;
-        unsigned run = block_excl_scan(local, tot, &total);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = 4 * tid + i;
-            if (p < NBIN && run < krem && run + c[i] >= krem) {
-                sh_digit = (unsigned)(NBIN - 1 - p);
-                sh_above = run;
-                sh_bin = c[i];
-            }
-            run += c[i];
-        }
-        __syncthreads();
-        bin_d = (int)sh_digit;
-        krem -= sh_above;
-        early = sh_bin == krem;
-        __syncthreads();
-    }
-    auto cand = [&](int e) { return !binned || value_bin(key[e], vmin, scale) == bin_d; };
-    auto above_bin = [&](int e) { return binned && value_bin(key[e], vmin, scale) > bin_d; };
-
-    // ---- exact radix passes over the candidates
     uint32_t prefix = 0u, pmask = 0u;
-    for (int ps = 0; ps < 3 && !early; ++ps) {
+    bool done = false;
+    for (int ps = 0; ps < 3 && !done; ++ps) {
         const int shift = ps == 0 ? 20 : ps == 1 ? 8 : 0;
         const int nb = ps < 2 ? 4096 : 256;
         const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int i = tid; i < nb; i += nt) hist[i] = 0u;
+        if (ps == 0) __syncthreads();       // the initial clear
+        if (ntile == 1) {
+            hist_keys<E>(key, min(E, n - (int)threadIdx.x * E), prefix, pmask, shift, dmask, hist);
+        } else {
+            for (int t = 0; t < ntile; ++t) {
+                const int i0 = t * tile + (int)threadIdx.x * E;
+                uint32_t kt[E];
+                load_keys<E>(s, n, i0, vec, kt);
+                hist_keys<E>(kt, min(E, n - i0), prefix, pmask, shift, dmask, hist);
+            }
+        }
         __syncthreads();
+        unsigned above, inbin;
+        const unsigned d = find_digit(hist, nb, krem, tot, sh, &above, &inbin);
+        prefix |= d << shift;
+        pmask |= dmask << shift;
+        krem -= above;
+        done = inbin == krem;               // every candidate left in the bin is taken
+    }
+
+    // ---- selection: keys above the threshold prefix (the whole last bin
+    // after an early stop), then the first krem keys equal to the full
+    // threshold in index order.  Tiles are written in order, through LDS
+    // when the set fits so that the global writes are contiguous.
+    const bool staged = k <= kTopkStage;
+    unsigned base = 0u, eq_seen = 0u;
+    for (int t = 0; t < ntile; ++t) {
+        const int i0 = t * tile + (int)threadIdx.x * E;
+        uint32_t kt[E];
+        if (ntile == 1) {
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e)
-            if (valid(e) && (key[e] & pmask) == prefix && cand(e)) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+            for (int e = 0; e < E; ++e) kt[e] = key[e];
+        } else {
+            load_keys<E>(s, n, i0, vec, kt);
+        }
+        const int lim = min(E, n - i0);
+        unsigned gt = 0u, eq = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t mk = kt[e] & pmask;
+            const unsigned v = e < lim;
+            gt += v & (mk > prefix || (done && mk == prefix));
+            eq += v & (!done && kt[e] == prefix);
+        }
+        unsigned tsum;
+        unsigned take_eq = 0u;
+        if (!done) {
+            unsigned eq_tot;
+            const unsigned eq_before = eq_seen + block_excl_scan(eq, tot, &eq_tot);
+            take_eq = krem > eq_before ? min(eq, krem - eq_before) : 0u;
+            eq_seen += eq_tot;
+        }
+        unsigned pos = base + block_excl_scan(gt + take_eq, tot, &tsum);
+        base += tsum;
+        unsigned taken = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t mk = kt[e] & pmask;
+            bool sel = e < lim && (mk > prefix || (done && mk == prefix));
+            if (!done && e < lim && kt[e] == prefix) sel = taken++ < take_eq;
+            if (sel) {
+                if (pos < (unsigned)k) {
+                    if (staged) stage[pos] = i0 + e;
+                    else out[pos] = i0 + e;
+                }
+                ++pos;
+            }
+        }
+    }
+    if (staged) {
         __syncthreads();
+        for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = stage[i];
+    }
+}
+
+// The same selection for a row of one tile (n <= 1024 * E, E <= 32), with
+// fewer instructions per element: per-thread bit masks (bit e = element
+// i0 + e) for candidates and for the selection, so each pass costs a
+// compare or two per element.  The first pass, where every key counts,
+// spreads each bin over 4 copies (lane & 3) so that equal digits within a
+// wave instruction rarely update the same LDS word.
+template <int E>
+__global__ __launch_bounds__(1024) void k_topk_tile(const float* __restrict__ scores, int n, int k,
+                                                    int32_t* __restrict__ idx) {
+    static_assert(E % 4 == 0 && E <= 32, "E in 4..32");
+    __shared__ unsigned hist[4096 * 4];
+    __shared__ int32_t stage[kTopkStage];
+    __shared__ unsigned tot[17];
+    __shared__ unsigned sh[3];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const float* s = scores + (size_t)blockIdx.x * n;
+    int32_t* out = idx + (size_t)blockIdx.x * k;
+    const int i0 = tid * E;
+    const int lim = max(0, min(E, n - i0));
+    const unsigned vmask = lim >= 32 ? 0xffffffffu : (1u << lim) - 1u;
+    const bool vec = (n & 3) == 0 && ((uintptr_t)s & 15u) == 0;
+    uint32_t key[E];
+    load_keys<E>(s, n, i0, vec, key);
+    for (int i = tid; i < 4096; i += 1024) reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    // ---- pass 0: top 12 bits of every valid key, 4 copies per bin
+    if (lim == E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) atomicAdd(&hist[(key[e] >> 20) * 4 + (lane & 3)], 1u);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (e < lim) atomicAdd(&hist[(key[e] >> 20) * 4 + (lane & 3)], 1u);
+    }
+    __syncthreads();
+    unsigned krem = (unsigned)k;
+    uint32_t prefix, pmask = 0xfff00000u;
+    bool done;
+    {
+        // digit search over the summed copies (bins read and cleared 4 per thread)
         unsigned c[4], local = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int p = 4 * tid + i;
-            c[i] = p < nb ? hist[nb - 1 - p] : 0u;
+            const int bin = 4095 - (4 * tid + i);
+            u32x4 v = reinterpret_cast<u32x4*>(hist)[bin];
+            reinterpret_cast<u32x4*>(hist)[bin] = u32x4{0u, 0u, 0u, 0u};
+            c[i] = v[0] + v[1] + v[2] + v[3];
             local += c[i];
         }
         unsigned total;
         unsigned run = block_excl_scan(local, tot, &total);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int p = 4 * tid + i;
-            if (p < nb && run < krem && run + c[i] >= krem) {
-                sh_digit = (unsigned)(nb - 1 - p);
-                sh_above = run;
-                sh_bin = c[i];
+            if (run < krem && run + c[i] >= krem) {
+                sh[0] = (unsigned)(4095 - (4 * tid + i));
+                sh[1] = run;
+                sh[2] = c[i];
             }
             run += c[i];
         }
         __syncthreads();
-        prefix |= sh_digit << shift;
-        pmask |= dmask << shift;
-        krem -= sh_above;
-        early = sh_bin == krem;             // every candidate left in the bin is taken
+        prefix = sh[0] << 20;
+        krem -= sh[1];
+        done = sh[2] == krem;
         __syncthreads();
     }
-    // ---- selection: elements above the boundary bin, then candidates above
-    // the key threshold, then the first krem candidates equal to it in index
-    // order (after an early stop every candidate in the last bin is taken).
-    unsigned gt = 0, eq = 0;
+    // ---- passes 1 and 2 over the candidates left in the chosen bin
+    for (int ps = 1; ps < 3 && !done; ++ps) {
+        const int shift = ps == 1 ? 8 : 0;
+        const int nb = ps == 1 ? 4096 : 256;
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        unsigned cm = 0u;
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-        if (valid(e)) {
-            if (above_bin(e)) {
-                ++gt;
-            } else if (cand(e) && (key[e] & pmask) >= prefix) {
-                if (early) ++gt;                                  // the whole chosen bin
-                else if (key[e] > prefix) ++gt;
-                else if (key[e] == prefix) ++eq;
-            }
+        for (int e = 0; e < E; ++e) cm |= (unsigned)((key[e] & pmask) == prefix) << e;
+        cm &= vmask;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (cm & (1u << e)) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        unsigned above, inbin;
+        const unsigned d = find_digit(hist, nb, krem, tot, sh, &above, &inbin);
+        prefix |= d << shift;
+        pmask |= dmask << shift;
+        krem -= above;
+        done = inbin == krem;
+    }
+
+    // ---- selection mask: keys above the threshold prefix (the whole last
+    // bin after an early stop), then the first krem keys equal to the full
+    // threshold in index order
+    unsigned sel = 0u, eqm = 0u;
+    if (done) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) sel |= (unsigned)((key[e] & pmask) >= prefix) << e;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            sel |= (unsigned)(key[e] > prefix) << e;
+            eqm |= (unsigned)(key[e] == prefix) << e;
         }
     }
-    unsigned total;
-    const unsigned eq_before = block_excl_scan(eq, tot, &total);
-    const unsigned take_eq = krem > eq_before ? min(eq, krem - eq_before) : 0u;
-    unsigned pos = block_excl_scan(gt + (early ? 0u : take_eq), tot, &total);
-    unsigned taken = 0;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-        if (valid(e)) {
-            bool sel = false;
-            if (above_bin(e)) {
-                sel = true;
-            } else if (cand(e) && (key[e] & pmask) >= prefix) {
-                if (early) sel = true;
-                else if (key[e] > prefix) sel = true;
-                else if (key[e] == prefix) sel = taken++ < take_eq;
-            }
-            if (sel && pos < (unsigned)k) out[pos++] = i0 + e;
+    sel &= vmask;
+    eqm &= vmask;
+    if (!done) {                                   // ties at the threshold: lowest indices first
+        unsigned eq_tot;
+        const unsigned eq_before = block_excl_scan(__popc(eqm), tot, &eq_tot);
+        unsigned take = krem > eq_before ? min((unsigned)__popc(eqm), krem - eq_before) : 0u;
+        for (unsigned m = eqm; take > 0; --take) {
+            const unsigned low = m & (0u - m);
+            sel |= low;
+            m ^= low;
         }
+    }
+    const bool staged = k <= kTopkStage;
+    unsigned tsum;
+    unsigned pos = block_excl_scan(__popc(sel), tot, &tsum);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (sel & (1u << e)) {
+            if (pos < (unsigned)k) {
+                if (staged) stage[pos] = i0 + e;
+                else out[pos] = i0 + e;
+            }
+            ++pos;
+        }
+    }
+    if (staged) {
+        __syncthreads();
+        for (int i = tid; i < k; i += 1024) out[i] = stage[i];
     }
 }
 
@@ -234,7 +334,7 @@ __global__ __launch_bounds__(256) void k_topk_small(const float* __restrict__ sc
     const bool sel = i < n && rank < (unsigned)k;
     unsigned total;
     const unsigned pos = block_excl_scan(sel ? 1u : 0u, tot, &total);
-    if (sel) idx[(size_t)blockIdx.x * k + pos] = i;
+    if (sel && pos < (unsigned)k) idx[(size_t)blockIdx.x * k + pos] = i;
 }
 
 // U = union of the B index sets (each ascending, values < n), written
@@ -261,11 +361,12 @@ __global__ __launch_bounds__(1024) void k_union(const int32_t* __restrict__ idx,
         unsigned m = bits[w];
         while (m) {
             const int b = __ffs(m) - 1;
-            uidx[pos++] = w * 32 + b;
+            if (pos < (unsigned)n) uidx[pos] = w * 32 + b;
+            ++pos;
             m &= m - 1;
         }
     }
-    if (threadIdx.x == 0 && ucount) *ucount = (int32_t)total;
+    if (threadIdx.x == 0 && ucount) *ucount = (int32_t)min(total, (unsigned)n);
 }
 
 __global__ void k_set_i32(int32_t* p, int v) { *p = v; }
@@ -288,16 +389,17 @@ dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hi
         if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
         return DV_OK;
     }
-    const int nt = topk_block_threads(n);
-    const int E = cdiv(n, nt);
-    if (E <= 16)
-        hipLaunchKernelGGL((k_topk<16>), dim3(B), dim3(nt), 0, s, scores, n, k, idx);
-    else if (E <= 32)
-        hipLaunchKernelGGL((k_topk<32>), dim3(B), dim3(nt), 0, s, scores, n, k, idx);
-    else if (E <= 48)
-        hipLaunchKernelGGL((k_topk<48>), dim3(B), dim3(nt), 0, s, scores, n, k, idx);
-    else
-        hipLaunchKernelGGL((k_topk<64>), dim3(B), dim3(nt), 0, s, scores, n, k, idx);
+    const int E = cdiv(n, 1024);     // elements per thread when the row is one tile
+#define DV_TK(EE) hipLaunchKernelGGL((k_topk_tile<EE>), dim3(B), dim3(1024), 0, s, scores, n, k, idx)
+    if (E <= 4) DV_TK(4);
+    else if (E <= 8) DV_TK(8);
+    else if (E <= 12) DV_TK(12);
+    else if (E <= 16) DV_TK(16);
+    else if (E <= 20) DV_TK(20);
+    else if (E <= 24) DV_TK(24);
+    else if (E <= 32) DV_TK(32);
+    else hipLaunchKernelGGL((k_topk<16>), dim3(B), dim3(1024), 0, s, scores, n, k, idx);   // tiles of 16384
+#undef DV_TK
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DV_OK;

@@ -115,7 +115,8 @@ dv_status dv_predict(const float* y, int B, int d, const void* p1_t, int r, cons
  *   union_idx   device int32 [n] or NULL: ascending union of the B sets
  *               (DejaVu §5.2 / App. C.1, the batch union), when B > 1
  *   union_count device int32 [1] or NULL: size of that union
- * 0 <= k <= n <= 65536; k > n gives DV_ERR_RANGE.  1 <= B <= 64.
+ * 0 <= k <= n <= 4194304 (2^22); k > n gives DV_ERR_RANGE.  1 <= B <= 64.
+ * The union needs n <= 262144 (2^18).
  */
 size_t dv_topk_workspace_bytes(int B, int n, int k);
 dv_status dv_topk_select(const float* scores, int B, int n, int k, int32_t* idx,

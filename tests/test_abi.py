@@ -68,7 +68,8 @@ def test_topk_validation(dv):
     assert L.dv_topk_select(P, 1, 10, 11, P, 0, 0, 0, 0, 0) == 5
     assert L.dv_topk_select(P, 1, 10, -1, P, 0, 0, 0, 0, 0) == 5
     assert L.dv_topk_select(0, 1, 10, 3, P, 0, 0, 0, 0, 0) == 1
-    assert L.dv_topk_select(P, 1, 70000, 3, P, 0, 0, 0, 0, 0) == 2
+    assert L.dv_topk_select(P, 1, (1 << 22) + 1, 3, P, 0, 0, 0, 0, 0) == 2
+    assert L.dv_topk_select(P, 2, (1 << 18) + 1, 3, P, P, P, 0, 0, 0) == 2   # union bitmap limit
     assert L.dv_topk_select(P, 65, 10, 3, P, 0, 0, 0, 0, 0) == 2
     assert L.dv_topk_select(P, 2, 10, 3, P, P, 0, 0, 0, 0) == 1     # union needs both outputs
     assert L.dv_topk_select(0, 1, 10, 0, 0, 0, 0, 0, 0, 0) == 0     # k = 0 is empty, nothing to launch
