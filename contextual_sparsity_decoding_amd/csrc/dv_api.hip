@@ -238,6 +238,7 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
         REQ(!overlap(out, (size_t)B * n_sel * d_h * 4, in, (size_t)B * d * 4), DV_ERR_RANGE,
             "dv_sparse_attn_proj: q overlaps y");
         REQ(qkv_supported(B, d, wdt), DV_ERR_UNSUPPORTED, "dv_sparse_attn_proj: d=%d rows too long", d);
+        REQ(!kv->y_buf || a16(kv->y_buf), DV_ERR_ALIGN, "dv_sparse_attn_proj: y_buf must be 16-byte aligned");
         return launch_qkv(in, B, d, h, d_h, head_idx, n_sel, w_t, bias, wdt, out, kv, true, s);
     }
     REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "dv_sparse_attn_proj: workspace %zu < %zu", ws_bytes, w.bytes);
@@ -402,6 +403,7 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     REQ(kv.max_len >= 1 && kv.pos >= 0 && kv.pos < kv.max_len, DV_ERR_RANGE, "dv_decode_layer: pos=%d max_len=%d",
         kv.pos, kv.max_len);
     REQ(!(c->flags & DV_HOLE_FILL) || (kv.y_buf && kv.valid_upto), DV_ERR_NULL, "dv_decode_layer: hole fill state");
+    REQ(!kv.y_buf || a16(kv.y_buf), DV_ERR_ALIGN, "dv_decode_layer: y_buf must be 16-byte aligned");
     REQ(!(c->flags & DV_ADVANCE_POS) || kv.pos_dev, DV_ERR_NULL, "dv_decode_layer: DV_ADVANCE_POS needs kv.pos_dev");
     REQ(qkv_supported(c->B, c->d, c->wdt), DV_ERR_UNSUPPORTED, "dv_decode_layer: d=%d rows too long", c->d);
     REQ(a16(w->w_qkv_t) && a16(w->w_o_t) && a16(w->w1_t) && a16(w->w2_t) && a16(x_in), DV_ERR_ALIGN,

@@ -124,7 +124,6 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     __shared__ unsigned tot[17];
     auto red = reinterpret_cast<float (*)[NBC][SW]>(shbuf);
     auto s_q = reinterpret_cast<float (*)[kRowsPerGroup][NQ][3]>(shbuf);
-    __shared__ int s_last;
     const T* W = (const T*)a.w;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, g = blockIdx.y;

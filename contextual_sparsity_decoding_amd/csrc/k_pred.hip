@@ -98,10 +98,10 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
     const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nchunk = a.d / E;
     const bool live = u < a.n_max;
+    stage_dma(ys, ln.x, a.d);                        // x straight into LDS, ahead of the row
     u32x4 w[CH];
     if (live) load_row<T, CH, true>((const T*)a.w + (size_t)u * a.d, nchunk, w);
-    stage_rows<1, 8>(ys, ln.x, 1, a.d);
-    __syncthreads();
+    wait_dma_and_sync();
     layernorm_lds(ys, a.d, ln, blockIdx.x == 0);
     if (!live) return;
     float acc[1] = {0.f};

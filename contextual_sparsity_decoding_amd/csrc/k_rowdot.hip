@@ -9,7 +9,9 @@ namespace dv {
 
 // A workgroup owns rows [blockIdx.x * rpg, +rpg); wave wv takes rows
 // wv, wv+4, ... of them, double-buffered: the next row's loads are in
-// flight while the current row is reduced.
+// flight while the current row is reduced.  y reaches LDS by DMA, issued
+// before the first row's loads (batch rows past B are never read: their
+// sums are discarded).
 template <typename T, int NB, int CH, int OP>
 __global__ __launch_bounds__(kBlock) void k_rowdot(RowArgs a, int rpg) {
     constexpr int E = Vec<T>::E;
@@ -29,11 +31,11 @@ __global__ __launch_bounds__(kBlock) void k_rowdot(RowArgs a, int rpg) {
         my_j = (unsigned)j < (unsigned)a.w_rows ? j : -1;   // an index outside W selects nothing
     }
     auto row_of = [&](int k) -> int { return __builtin_amdgcn_readlane(my_j, k); };   // k is wave-uniform
+    stage_dma(ys, a.y, a.B * a.d);                        // y straight into LDS, ahead of the rows
     u32x4 wa[CH], wb[CH];
     int ja = nk > 0 ? row_of(0) : -1, jb = -1;
     if (ja >= 0) load_row<T, CH, true>((const T*)a.w + (size_t)ja * a.d, nchunk, wa);
-    stage_rows<NB, 8>(ys, a.y, a.B, a.d);
-    __syncthreads();
+    wait_dma_and_sync();
     auto emit = [&](int k, int j, const u32x4 (&w)[CH]) {
         const int u = u0 + wv + 4 * k;
         float acc[NB];

@@ -7,14 +7,15 @@
 
 #include "rowdot.h"
 
+#include <type_traits>
+
 namespace dv {
 
 // ---------------------------------------------------------------- Q/K/V -----
 // DejaVu §4.2: for the selected heads compute q, k, v; store k, v in the
 // cache; keep y for the heads not selected; recompute a selected head's
-// missing K/V from the stored inputs, reusing the weight row already held
-// in registers.  Rows are ordered [which][s][e]; a workgroup's 4 rows lie
-// in one head block.
+// missing K/V from the stored inputs, reusing the weight rows already held
+// in registers.  Rows are ordered [which][s][e].
 struct QkvArgs {
     const float* y;
     int B, d, h, dh, n_sel;
@@ -30,100 +31,174 @@ struct QkvArgs {
     int32_t* valid_upto;
 };
 
-// A workgroup owns rpg consecutive rows of one (which, head) block; wave wv
-// takes rows wv, wv+4, ..., double-buffered.  The head's stored inputs for
-// its first HB missing positions are staged in LDS next to y.
-template <typename T, int NB, int CH, bool YLDS, int HB>
-__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a, int rpg) {
+// A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
+// holds rows wv*R .. wv*R+R-1 in registers (lane l: chunks l, l+64, ...), so
+// every input chunk read from LDS serves R rows.  The inputs are y (NB
+// batch rows) and, for K and V of batch row 0, the stored inputs of the
+// head's missing positions, staged HB at a time by the whole workgroup.
+// Inputs reach LDS by DMA (no registers), issued before the weight loads.
+// Recomputed entries take the same instructions on the same input values as
+// the entries computed on time, so they are bit-identical to them.  When y
+// does not fit in LDS (YL false: wide batches) it is read from global memory.
+template <typename T, int NB, int CH, int R, int HB, bool YL>
+__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     constexpr int E = Vec<T>::E;
     constexpr int HV = HB > 0 ? HB : 1;
-    extern __shared__ float ys[];                      // y [NB][d], then HB stored inputs [HB][d]
+    extern __shared__ float ys[];                      // y [NB][d], then [HB][d] stored inputs
     const int d = a.d, dh = a.dh;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int r0 = blockIdx.x * rpg;                   // rpg divides dh: one head block per workgroup
+    const int r0 = blockIdx.x * 4 * R;                 // 4*R divides dh: one head block per workgroup
     const int which = r0 / (a.n_sel * dh);
     const int s = (r0 / dh) % a.n_sel;
-    const int e0 = r0 % dh;
+    const int e0 = r0 % dh + wv * R;                   // this wave's first row in the block
     const int nchunk = d / E;
     const int head = a.head_idx ? a.head_idx[s] : s;
     const bool live = (unsigned)head < (unsigned)a.h;
-    const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh) * d;
-    const int nk = rpg > wv ? (rpg - wv + 3) / 4 : 0;
-    u32x4 wa[CH], wb[CH];
-    if (live && nk > 0) load_row<T, CH, true>(Wb + (size_t)(e0 + wv) * d, nchunk, wa);
-    if (YLDS) stage_rows<NB, 8>(ys, a.y, a.B, d);
     const int pos = a.pos_dev ? *a.pos_dev : a.pos;
     const bool pos_ok = pos >= 0 && pos < a.max_len;   // else the call writes nothing
     const bool fill = pos_ok && live && a.y_buf != nullptr && a.valid_upto != nullptr && which > 0;
-    const int lo0 = fill ? max(a.valid_upto[head] + 1, 0) : pos;
-    const int staged = (HB > 0 && fill) ? min(HB, max(pos - lo0, 0)) : 0;
-    if (HB > 0 && staged > 0) stage_rows<HV, 4>(ys + NB * d, a.y_buf + (size_t)lo0 * d, staged, d);
-    if (blockIdx.x == 0 && a.y_buf && pos_ok) {
-        for (int i = threadIdx.x; i < a.B * d; i += kBlock) {
-            const int b = i / d, c = i % d;
-            a.y_buf[((size_t)b * a.max_len + pos) * d + c] = a.y[i];
+    const int lo0 = fill ? min(max(a.valid_upto[head] + 1, 0), pos) : pos;
+    float* hin = ys + (YL ? NB : 0) * d;               // stored inputs of missing positions
+    // inputs straight into LDS first (y, then the first round of stored
+    // inputs), then the weight rows, all in flight together
+    if (YL) stage_dma(ys, a.y, a.B * d);
+    if (HB > 0 && fill && pos > lo0) stage_dma(hin, a.y_buf + (size_t)lo0 * d, min(HB, pos - lo0) * d);
+    const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh + e0) * d;
+    // chunk-major, the order the dot products consume them in
+    u32x4 w[R][CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int c = lane + i * kWave;
+            w[j][i] = (live && c < nchunk) ? ld16_stream(Wb + (size_t)j * d + (size_t)c * E) : u32x4{0u, 0u, 0u, 0u};
+        }
+    float bv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e0 + j]) : 0.f;
+    wait_dma_and_sync();
+    // this step's input joins the stored inputs: float4 c of [B][d] goes
+    // with thread c of the grid (a handful of workgroups), from LDS when staged
+    if (a.y_buf && pos_ok) {
+        for (int c = blockIdx.x * kBlock + threadIdx.x; c < a.B * d / 4; c += gridDim.x * kBlock) {
+            const int b = (c * 4) / d, col = (c * 4) % d;
+            const f32x4 v = YL ? reinterpret_cast<const f32x4*>(ys)[c] : reinterpret_cast<const f32x4*>(a.y)[c];
+            *reinterpret_cast<f32x4*>(a.y_buf + ((size_t)b * a.max_len + pos) * d + col) = v;
         }
     }
-    __syncthreads();
-    if (!live || !pos_ok) return;
-    half_t* cache = which == 1 ? a.K : a.V;
-    auto emit = [&](int k, const u32x4 (&w)[CH]) {
-        const int e = e0 + wv + 4 * k;
-        const float bv = to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e]);
-        float acc[NB];
+
+    // lane-partial dots of the R rows with NV inputs at `in` (stride d)
+    auto dots = [&](const float* in, auto nv_tag, float (&acc)[R][decltype(nv_tag)::value]) {
+        constexpr int NV = decltype(nv_tag)::value;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-        if (YLDS) dot_row<T, CH, NB>(w, nchunk, ys, d, NB, acc);
-        else dot_row<T, CH, NB>(w, nchunk, a.y, d, a.B, acc);
+        for (int j = 0; j < R; ++j)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = wave_sum(acc[b]) + bv;
-        if (which == 0) {
-            if (lane == 0)
+            for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    if (b < a.B) a.q[((size_t)b * a.n_sel + s) * dh + e] = acc[b];
-            return;
-        }
-        if (lane == 0)
+        for (int i = 0; i < CH; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                if (b < a.B) cache[(((size_t)b * a.h + head) * a.max_len + pos) * dh + e] = (half_t)acc[b];
-        if (!fill) return;
-        if (HB > 0 && staged > 0) {                    // missing positions whose inputs are in LDS
-            float hacc[HV];
+                for (int v = 0; v < NV; ++v) {
+                    float yv[E];
+                    const f32x4* y4 = reinterpret_cast<const f32x4*>(in + (size_t)v * d + (size_t)c * E);
 #pragma unroll
-            for (int v = 0; v < HV; ++v) hacc[v] = 0.f;
-            dot_row<T, CH, HV>(w, nchunk, ys + NB * d, d, staged, hacc);
+                    for (int q = 0; q < E / 4; ++q) {
+                        const f32x4 t = y4[q];
+                        yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
+                    }
 #pragma unroll
-            for (int v = 0; v < HV; ++v) {
-                const float hv = wave_sum(hacc[v]) + bv;
-                if (lane == 0 && v < staged) cache[((size_t)head * a.max_len + lo0 + v) * dh + e] = (half_t)hv;
-            }
-        }
-        for (int b = 0; b < a.B; ++b) {
-            const int lo = (b == 0) ? lo0 + staged : max(a.valid_upto[b * a.h + head] + 1, 0);
-            for (int p = lo; p < pos; p += 2) {
-                const int cnt = min(2, pos - p);
-                const float* base = a.y_buf + ((size_t)b * a.max_len + p) * d;
-                float hacc[2] = {0.f, 0.f};
-                // two stored inputs per pass, straight from global memory (L2)
-                dot_row<T, CH, 2>(w, nchunk, base, d, cnt, hacc);
+                    for (int j = 0; j < R; ++j) {
+                        float f[E];
+                        unpack(w[j][i], f, T());
 #pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    const float hv = wave_sum(hacc[v]) + bv;
-                    if (lane == 0 && v < cnt)
-                        cache[(((size_t)b * a.h + head) * a.max_len + p + v) * dh + e] = (half_t)hv;
+                        for (int e = 0; e < E; ++e) acc[j][v] = fmaf(f[e], yv[e], acc[j][v]);
+                    }
                 }
             }
         }
     };
-    for (int k = 0; k < nk; k += 2) {
-        if (k + 1 < nk) load_row<T, CH, true>(Wb + (size_t)(e0 + wv + 4 * (k + 1)) * d, nchunk, wb);
-        emit(k, wa);
-        if (k + 1 < nk) {
-            if (k + 2 < nk) load_row<T, CH, true>(Wb + (size_t)(e0 + wv + 4 * (k + 2)) * d, nchunk, wa);
-            emit(k + 1, wb);
+
+    // The weight registers are marked as rewritten after each use, so the
+    // compiler converts fp16 to fp32 again for every input instead of
+    // keeping all converted rows live (which would cost occupancy).
+    auto fence_w = [&]() {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int i = 0; i < CH; ++i) asm volatile("" : "+v"(w[j][i]));
+    };
+
+    // ---- on-time q, k, v
+    {
+        float acc[R][NB];
+        if (YL) dots(ys, std::integral_constant<int, NB>(), acc);
+        else dots(a.y, std::integral_constant<int, NB>(), acc);
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[j][b] = wave_sum(acc[j][b]) + bv[j];
+        if (live && pos_ok && lane == 0) {
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b >= a.B) continue;
+                    if (which == 0) a.q[((size_t)b * a.n_sel + s) * dh + e0 + j] = acc[j][b];
+                    else (which == 1 ? a.K : a.V)[(((size_t)b * a.h + head) * a.max_len + pos) * dh + e0 + j] =
+                        (half_t)acc[j][b];
+                }
+        }
+    }
+    if (which == 0 || !fill) return;                   // uniform over the workgroup
+    fence_w();
+
+    // ---- missing positions of batch row 0, HB stored inputs per round
+    half_t* cache = which == 1 ? a.K : a.V;
+    if constexpr (HB > 0) {
+        for (int p0 = lo0; p0 < pos; p0 += HB) {
+            const int cnt = min(HB, pos - p0);
+            if (p0 != lo0) {                           // the first round was staged up front
+                __syncthreads();                       // the previous round's inputs are consumed
+                stage_dma(hin, a.y_buf + (size_t)p0 * d, cnt * d);
+                wait_dma_and_sync();
+            }
+            float hacc[R][HV];
+            dots(hin, std::integral_constant<int, HV>(), hacc);
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int v = 0; v < HV; ++v) {
+                    const float hv = wave_sum(hacc[j][v]) + bv[j];
+                    if (lane == 0 && v < cnt) cache[((size_t)head * a.max_len + p0 + v) * dh + e0 + j] = (half_t)hv;
+                }
+            fence_w();
+        }
+    } else {
+        for (int p = lo0; p < pos; ++p) {              // inputs too long for LDS: read from global memory
+            float hacc[R][1];
+            dots(a.y_buf + (size_t)p * d, std::integral_constant<int, 1>(), hacc);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float hv = wave_sum(hacc[j][0]) + bv[j];
+                if (lane == 0) cache[((size_t)head * a.max_len + p) * dh + e0 + j] = (half_t)hv;
+            }
+            fence_w();
+        }
+    }
+    // batch rows past the first keep their own valid positions (read from global memory)
+    for (int b = 1; b < a.B; ++b) {
+        const int lo = min(max(a.valid_upto[b * a.h + head] + 1, 0), pos);
+        for (int p = lo; p < pos; ++p) {
+            float hacc[R][1];
+            dots(a.y_buf + ((size_t)b * a.max_len + p) * d, std::integral_constant<int, 1>(), hacc);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float hv = wave_sum(hacc[j][0]) + bv[j];
+                if (lane == 0) cache[(((size_t)b * a.h + head) * a.max_len + p) * dh + e0 + j] = (half_t)hv;
+            }
+            fence_w();
         }
     }
 }
@@ -139,42 +214,41 @@ using namespace dv;
         if (e_ != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e_)); \
     } while (0)
 
-template <typename T, int NB, bool YLDS, int HB>
-static void qkv_go2(const QkvArgs& a, int ch, size_t lds, hipStream_t s) {
+// Rows per wave held in registers: as many as fit in 40 chunk registers.
+inline int qkv_rows_per_wave(int ch) { return ch <= 10 ? 4 : ch <= 20 ? 2 : 1; }
+
+template <typename T, int NB, int CH, int R>
+static dv_status qkv_go3(const QkvArgs& a, hipStream_t s) {
     const int rows = 3 * a.n_sel * a.dh;
-    int rpg = rows_per_group(rows);
-    while (a.dh % rpg) rpg -= 4;                       // a workgroup stays inside one head block
-    const int grid = rows / rpg;
-    switch (ch) {
-        case 4: hipLaunchKernelGGL((k_qkv<T, NB, 4, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 8: hipLaunchKernelGGL((k_qkv<T, NB, 8, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 10: hipLaunchKernelGGL((k_qkv<T, NB, 10, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 12: hipLaunchKernelGGL((k_qkv<T, NB, 12, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 16: hipLaunchKernelGGL((k_qkv<T, NB, 16, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 18: hipLaunchKernelGGL((k_qkv<T, NB, 18, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        default: hipLaunchKernelGGL((k_qkv<T, NB, 24, YLDS, HB>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-    }
+    const size_t row = (size_t)a.d * sizeof(float);
+    const bool holes = a.y_buf && a.valid_upto;
+    if (a.dh % (4 * R)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
+    const int grid = rows / (4 * R);
+    const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
+#define DV_QKV(HB, LDS)                                                                                  \
+    do {                                                                                                 \
+        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true>), dim3(grid), dim3(kBlock), LDS, s, a); \
+        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
+    } while (0)
+    if (holes && yl + 2 * row <= kQkvLdsMax) DV_QKV(2, yl + 2 * row);
+    else if (holes && yl + row <= kQkvLdsMax) DV_QKV(1, yl + row);
+    else DV_QKV(0, yl);
+#undef DV_QKV
+    return DV_OK;
 }
 
 template <typename T, int NB>
 static dv_status qkv_go(const QkvArgs& a, int ch, hipStream_t s) {
-    if (ch == 0) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: rows of d=%d are too long", a.d);
-    const size_t row = (size_t)a.d * sizeof(float);
-    const size_t lds = NB * row;
-    const bool holes = a.y_buf && a.valid_upto;
-    if constexpr (NB == 1) {
-        if (holes && lds + 2 * row <= kYLdsMax) {
-            qkv_go2<T, NB, true, 2>(a, ch, lds + 2 * row, s);
-            return DV_OK;
-        }
-        if (holes && lds + row <= kYLdsMax) {
-            qkv_go2<T, NB, true, 1>(a, ch, lds + row, s);
-            return DV_OK;
-        }
+    switch (ch) {
+        case 4: return qkv_go3<T, NB, 4, 4>(a, s);
+        case 8: return qkv_go3<T, NB, 8, 4>(a, s);
+        case 10: return qkv_go3<T, NB, 10, 4>(a, s);
+        case 12: return qkv_go3<T, NB, 12, 2>(a, s);
+        case 16: return qkv_go3<T, NB, 16, 2>(a, s);
+        case 18: return qkv_go3<T, NB, 18, 2>(a, s);
+        case 24: return qkv_go3<T, NB, 24, 1>(a, s);
+        default: return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: rows of d=%d are too long", a.d);
     }
-    if (lds <= kYLdsMax) qkv_go2<T, NB, true, 0>(a, ch, lds, s);
-    else qkv_go2<T, NB, false, 0>(a, ch, 0, s);
-    return DV_OK;
 }
 
 template <typename T>

@@ -61,6 +61,26 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ lds, const float*
         l4[c] = (c * 4) / d < B ? s4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Copy n floats (n % 4 == 0, 16-byte aligned source) from global memory
+// straight into LDS (gfx950 LDS DMA: lane l of a wave fills bytes
+// [16 l, 16 l + 16) of the wave's 1 KB block), with no registers in
+// between.  The data is there once the issuing wave's vmcnt has drained;
+// callers wait for vmcnt(0) and then synchronise the workgroup.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void stage_dma(float* lds, const float* __restrict__ src, int n) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nkb = (n + 255) / 256;
+    for (int c = wv; c < nkb; c += kBlock / kWave) {
+        const int i = c * 256 + lane * 4;
+        if (i < n) __builtin_amdgcn_global_load_lds(src + i, (lds_void_t*)(lds + c * 256), 16, 0, 0);
+    }
+}
+__device__ __forceinline__ void wait_dma_and_sync() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
 // One wave's whole weight row in registers: chunks lane, lane+64, ... of
 // nchunk (at most CH per lane).
 template <typename T, int CH, bool STREAM>

@@ -155,7 +155,8 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
  *   pos               slot written by this step, 0 <= pos < max_len
  *   y_buf             device fp32 [B][max_len][d]: every step's layer input,
  *                     kept for heads that were not selected (DejaVu §4.2);
- *                     NULL disables hole fill
+ *                     16-byte aligned (else DV_ERR_ALIGN); NULL disables
+ *                     hole fill
  *   valid_upto        device int32 [B][h]: last position whose K/V head i
  *                     holds; NULL disables hole fill
  *   pos_dev           device int32 [1] or NULL: when set, the slot is read
