@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--kernel-launches", type=int, default=64)
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sweep-steps", type=int, default=32,
+                   help="steps per point of the neuron keep-ratio sweep (0 skips the sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="before the Q/K/V launches, copy this many MiB device to device three times "
@@ -143,7 +145,8 @@ def main():
     K = args.steps
     warm_reps = max(1, math.ceil(args.warmup / K))
     Kd = args.dense_steps
-    total_steps = (warm_reps + 1) * K + (2 * Kd if Kd > 0 else 0)
+    sweep_keep = (0.05, 0.10, 0.25, 0.50, 1.00)
+    total_steps = (warm_reps + 1) * K + (2 * Kd if Kd > 0 else 0) + 2 * args.sweep_steps * len(sweep_keep)
     max_len = w.n_ctx + math.ceil(total_steps / R) + 8
     torch.cuda.set_device(0)
     copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
@@ -151,18 +154,20 @@ def main():
     out = torch.empty(1, dims.d, device="cuda")
     flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
 
-    def cfg(flags_):
+    def cfg(flags_, k_neurons=w.k_neurons):
         dense_a = bool(flags_ & dv.DV_DENSE_ATTN)
         dense_m = bool(flags_ & dv.DV_DENSE_MLP)
         return dv.decode_cfg(B=1, d=dims.d, h=dims.h, d_h=dims.d_h, N=dims.N, r_attn=dims.r_attn,
                              r_mlp=dims.r_mlp, k_heads=dims.h if dense_a else w.k_heads,
-                             k_neurons=dims.N if dense_m else w.k_neurons, wdt=dv.DV_F16,
+                             k_neurons=dims.N if dense_m else k_neurons, wdt=dv.DV_F16,
                              pred_act=dv.DV_ACT_RELU, eps=1e-5, scale=1 / math.sqrt(dims.d_h), flags=flags_)
 
     sparse_cfg = cfg(flags)
     dense_cfg = cfg(flags | dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP)
-    ws = dv.workspace(max(dv.dv_decode_workspace_bytes(sparse_cfg, max_len),
-                          dv.dv_decode_workspace_bytes(dense_cfg, max_len)))
+    ws = dv.workspace(max([dv.dv_decode_workspace_bytes(sparse_cfg, max_len),
+                           dv.dv_decode_workspace_bytes(dense_cfg, max_len)] +
+                          [dv.dv_decode_workspace_bytes(cfg(flags, int(math.floor(k * dims.N))), max_len)
+                           for k in sweep_keep]))
     fc2_rows = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     # K sparse steps captured once; warm-up replays, then one timed replay
@@ -181,6 +186,29 @@ def main():
         g_dense = capture_steps(dv, torch, copies, dense_cfg, X, 0, Kd, out, ws, None)
         g_dense.replay()
         dense_ms = time_graph(torch, g_dense)[0] / Kd
+
+    # neuron keep-ratio sweep at 50% heads: same kernels, same copies, one graph per point
+    sweep = []
+    if args.sweep_steps > 0:
+        Ks = args.sweep_steps
+        for keep in sweep_keep:
+            kn = int(math.floor(keep * dims.N))
+            fc2_rows.zero_()
+            g = capture_steps(dv, torch, copies, cfg(flags, kn), X, 0, Ks, out, ws, fc2_rows)
+            g.replay()
+            torch.cuda.synchronize()
+            fc2_rows.zero_()
+            ms = time_graph(torch, g)[0] / Ks
+            rows = int(fc2_rows.item()) / Ks
+            b = account.step_bytes(dims, w.k_heads, kn, n_att=w.n_ctx + 1, fc2_rows=rows)
+            db_ = account.step_bytes(dims, dims.h, dims.N, n_att=w.n_ctx + 1, fc2_rows=dims.N, head_pred=False,
+                                     neuron_pred=False)
+            sweep.append({"keep_neurons": keep, "k_neurons": kn, "ms_per_step": round(ms, 5),
+                          "tokens_per_s": round(1000.0 / ms, 1),
+                          "effective_hbm_GBps": round(b.total / (ms * 1e-3) / 1e9, 1),
+                          "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms, 3),
+                          "byte_bound_speedup": round(db_.total / b.total, 3)})
+            del g
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -245,6 +273,7 @@ def main():
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "byte_bound_speedup": round(db.total / sb.total, 3),
         "host_wall_ms_per_step": round(1000 * wall / K, 4),
+        "keep_sweep": sweep,
         "roofline": {
             "kernel": "k_qkv (sparse Q/K/V gather-GEMV + KV append)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -129,16 +129,16 @@ def sparse_mlp(y, w1_t, b1, w2_t, b2, idx, residual=None, skip_nonpos: bool = Fa
     """
     y = _f64(np.atleast_2d(y))
     idx = np.asarray(idx, dtype=np.int64)
-    W1_S = _f64(w1_t)[idx].T                # d x |S|, columns W1_j
+    W1_S = _f64(w1_t[idx]).T                # d x |S|, columns W1_j
     a = relu(y @ W1_S + _f64(b1)[idx])       # B x |S|
     out = np.zeros((y.shape[0], y.shape[1]), F64) + _f64(b2)
     if residual is not None:
         out = out + _f64(np.atleast_2d(residual))
-    W2 = _f64(w2_t)
-    for jj, j in enumerate(idx):
+    W2_S = _f64(w2_t[idx])                   # |S| x d, rows W2_j
+    for jj in range(len(idx)):
         if skip_nonpos and not np.any(a[:, jj] > 0):
             continue
-        out = out + a[:, jj:jj + 1] * W2[j][None, :]
+        out = out + a[:, jj:jj + 1] * W2_S[jj][None, :]
     return out, a
 
 
@@ -188,11 +188,11 @@ def qkv_step(y, w_qkv_t, b_qkv, head_idx, kv: KVState, pos: int, hole_fill: bool
     fill = hole_fill and kv.y_buf is not None and kv.valid_upto is not None
     if kv.y_buf is not None:
         kv.y_buf[:, pos] = y
-    for b in range(B):
-        for s, i in enumerate(head_idx):
-            WQ, bQ = head_rows(w_qkv_t, b_qkv, 0, i)
-            WK, bK = head_rows(w_qkv_t, b_qkv, 1, i)
-            WV, bV = head_rows(w_qkv_t, b_qkv, 2, i)
+    for s, i in enumerate(head_idx):
+        WQ, bQ = head_rows(w_qkv_t, b_qkv, 0, i)
+        WK, bK = head_rows(w_qkv_t, b_qkv, 1, i)
+        WV, bV = head_rows(w_qkv_t, b_qkv, 2, i)
+        for b in range(B):
             q[b, s] = y[b] @ WQ + bQ
             first = int(kv.valid_upto[b, i]) + 1 if fill else pos
             for p in range(min(first, pos), pos + 1):
