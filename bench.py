@@ -5,15 +5,19 @@
 A step is one decode token through one layer (d=5120, 40 heads x 128,
 d_ffn=20480 ReLU, fp16 weights, fp32 accumulate, 2048 cached tokens), with
 10% of neurons and 50% of heads selected by rank-128 predictors, hole fill
-on and fc2 rows of non-positive neurons skipped: LN -> head predictor ->
-top-k -> Q/K/V + KV append -> split-K attention -> W^O -> LN -> neuron
-predictor -> top-k -> fc1 -> fc2.  Four independent layer copies are used
-in turn so that the 256 MB Infinity Cache cannot serve repeated reads; each
-copy's position advances by one per step it takes.
+on and fc2 rows of non-positive neurons skipped.  The timed schedule is
+DejaVu §4.3's parallel form: the step runs Q/K/V + KV append (LN folded in)
+-> split-K attention -> W^O -> fc1 (LN folded in) -> fc2 on the sets
+predicted during the previous step, while the next step's head and neuron
+predictors and top-k run on a second stream.  Four independent layer copies
+are used in turn so that the 256 MB Infinity Cache cannot serve repeated
+reads; each copy's position advances by one per step it takes, and step s
+predicts for copy (s + 1) mod 4 with that copy's predictors.
 
 Prints one JSON line: decode tokens/s, effective HBM bandwidth on the bytes
-the step must read, the dominant kernel's roofline, the same library's dense
-path, and the CPU oracle timed on a sample of the same workload.
+the step must read, the dominant kernel's roofline, the sequential schedule
+and the dense path of the same library, a neuron keep-ratio sweep, and the
+CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
 
@@ -103,19 +107,57 @@ class Copy:
         self.st.head_idx_out = self.head_idx.data_ptr()
 
 
-def capture_steps(dv, torch, copies, cfg, X, first, count, out, ws, fc2_rows):
-    """A HIP graph of `count` decode steps (step s uses copy s % R and input X[first + s])."""
+class Ahead:
+    """What the look-ahead schedule (DejaVu §4.3, parallel form) carries from
+    step to step: two ping-pong pairs of index buffers (step s reads pair s % 2
+    and writes the next step's sets into the other), the second stream and the
+    fork/join events."""
+
+    def __init__(self, torch, dims):
+        self.aux = torch.cuda.Stream()
+        self.evs = [torch.cuda.Event(), torch.cuda.Event()]
+        for e in self.evs:
+            e.record()
+        torch.cuda.synchronize()
+        self.hb = [torch.zeros(dims.h, dtype=torch.int32, device="cuda") for _ in range(2)]
+        self.nb = [torch.zeros(dims.N, dtype=torch.int32, device="cuda") for _ in range(2)]
+        self.dims = dims
+
+    def seed_sets(self, torch, k_heads, k_neurons, seed):
+        """Sets for the very first step (every later step uses predicted ones)."""
+        g = np.random.default_rng(seed)
+        self.hb[0][:k_heads] = torch.from_numpy(np.sort(g.choice(self.dims.h, k_heads, replace=False)).astype(np.int32))
+        self.nb[0][:k_neurons] = torch.from_numpy(np.sort(g.choice(self.dims.N, k_neurons, replace=False)).astype(np.int32))
+
+
+def capture_steps(dv, torch, copies, cfg, X, first, count, out, ws, fc2_rows, ahead=None):
+    """A HIP graph of `count` decode steps (step s uses copy s % R and input
+    X[first + s]).  With `ahead`, step s runs copy s % R on the sets predicted
+    by step s - 1 and predicts copy (s + 1) % R's sets with that copy's
+    predictors on the second stream."""
     g = torch.cuda.CUDAGraph()
     R = len(copies)
     with torch.cuda.graph(g):
         stream = torch.cuda.current_stream().cuda_stream
         for i in range(count):
             cp = copies[i % R]
-            cp.st.fc2_rows_out = fc2_rows.data_ptr() if fc2_rows is not None else 0
-            st = dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(cfg), dv.C.byref(cp.st),
+            st = cp.st
+            if ahead is not None:
+                nxt = copies[(i + 1) % R]
+                st = dv.LayerState()
+                st.kv = cp.st.kv
+                p, q = i % 2, (i + 1) % 2
+                st.head_idx_in, st.neuron_idx_in = ahead.hb[p].data_ptr(), ahead.nb[p].data_ptr()
+                st.next_head_idx, st.next_neuron_idx = ahead.hb[q].data_ptr(), ahead.nb[q].data_ptr()
+                st.next_pa1_t, st.next_pa2_t = nxt.Wd["pa1_t"].data_ptr(), nxt.Wd["pa2_t"].data_ptr()
+                st.next_pm1_t, st.next_pm2_t = nxt.Wd["pm1_t"].data_ptr(), nxt.Wd["pm2_t"].data_ptr()
+                st.aux_stream = ahead.aux.cuda_stream
+                st.ev_fork, st.ev_join = ahead.evs[0].cuda_event, ahead.evs[1].cuda_event
+            st.fc2_rows_out = fc2_rows.data_ptr() if fc2_rows is not None else 0
+            rc = dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(cfg), dv.C.byref(st),
                                         X[first + i].data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
-            if st != 0:
-                raise dv.DVError("dv_decode_layer", st)
+            if rc != 0:
+                raise dv.DVError("dv_decode_layer", rc)
     return g
 
 
@@ -146,7 +188,7 @@ def main():
     warm_reps = max(1, math.ceil(args.warmup / K))
     Kd = args.dense_steps
     sweep_keep = (0.05, 0.10, 0.25, 0.50, 1.00)
-    total_steps = (warm_reps + 1) * K + (2 * Kd if Kd > 0 else 0) + 2 * args.sweep_steps * len(sweep_keep)
+    total_steps = (warm_reps + 1) * K + 2 * K + (2 * Kd if Kd > 0 else 0) + 2 * args.sweep_steps * len(sweep_keep)
     max_len = w.n_ctx + math.ceil(total_steps / R) + 8
     torch.cuda.set_device(0)
     copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
@@ -162,16 +204,19 @@ def main():
                              k_neurons=dims.N if dense_m else k_neurons, wdt=dv.DV_F16,
                              pred_act=dv.DV_ACT_RELU, eps=1e-5, scale=1 / math.sqrt(dims.d_h), flags=flags_)
 
-    sparse_cfg = cfg(flags)
+    ahead_flags = flags | dv.DV_LOOKAHEAD
+    sparse_cfg = cfg(ahead_flags)
+    seq_cfg = cfg(flags)
     dense_cfg = cfg(flags | dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP)
-    ws = dv.workspace(max([dv.dv_decode_workspace_bytes(sparse_cfg, max_len),
-                           dv.dv_decode_workspace_bytes(dense_cfg, max_len)] +
-                          [dv.dv_decode_workspace_bytes(cfg(flags, int(math.floor(k * dims.N))), max_len)
+    ws = dv.workspace(max([dv.dv_decode_workspace_bytes(c, max_len) for c in (sparse_cfg, seq_cfg, dense_cfg)] +
+                          [dv.dv_decode_workspace_bytes(cfg(ahead_flags, int(math.floor(k * dims.N))), max_len)
                            for k in sweep_keep]))
     fc2_rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ahead = Ahead(torch, dims)
+    ahead.seed_sets(torch, w.k_heads, w.k_neurons, SEED)
 
-    # K sparse steps captured once; warm-up replays, then one timed replay
-    g_sparse = capture_steps(dv, torch, copies, sparse_cfg, X, 0, K, out, ws, fc2_rows)
+    # K sparse steps (look-ahead schedule) captured once; warm-up replays, then one timed replay
+    g_sparse = capture_steps(dv, torch, copies, sparse_cfg, X, 0, K, out, ws, fc2_rows, ahead)
     for _ in range(warm_reps):
         g_sparse.replay()
     torch.cuda.synchronize()
@@ -179,6 +224,13 @@ def main():
     ms_total, wall = time_graph(torch, g_sparse)
     ms_step = ms_total / K
     rows_per_step = int(fc2_rows.item()) / K
+    del g_sparse
+
+    # the sequential schedule (each block's predictor before the block) through the same kernels
+    g_seq = capture_steps(dv, torch, copies, seq_cfg, X, 0, K, out, ws, None)
+    g_seq.replay()
+    seq_ms = time_graph(torch, g_seq)[0] / K
+    del g_seq
 
     # dense path through the same kernels
     dense_ms = None
@@ -193,8 +245,9 @@ def main():
         Ks = args.sweep_steps
         for keep in sweep_keep:
             kn = int(math.floor(keep * dims.N))
+            ahead.seed_sets(torch, w.k_heads, kn, SEED + 1)
             fc2_rows.zero_()
-            g = capture_steps(dv, torch, copies, cfg(flags, kn), X, 0, Ks, out, ws, fc2_rows)
+            g = capture_steps(dv, torch, copies, cfg(ahead_flags, kn), X, 0, Ks, out, ws, fc2_rows, ahead)
             g.replay()
             torch.cuda.synchronize()
             fc2_rows.zero_()
@@ -261,8 +314,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) inputs and KV cache)",
         "config": {
             "workload": "opt13b-layer decode: d=5120, 40 heads x 128, d_ffn=20480 ReLU, fp16, batch 1, "
-                        "2048 cached tokens, keep 10% neurons (2048) and 50% heads (20), rank-128 predictors, "
-                        "4 rotating layer copies, one HIP graph of the timed steps",
+                        "2048 cached tokens, keep 10% neurons (2048) and 50% heads (20), rank-128 predictors run "
+                        "one layer ahead on a second stream, 4 rotating layer copies, one HIP graph of the timed steps",
             "global_batch": 1, "seq_len": w.n_ctx, "keep_neurons": 0.10, "keep_heads": 0.50,
         },
         "effective_hbm_GBps": round(sb.total / (ms_step * 1e-3) / 1e9, 1),
@@ -273,6 +326,7 @@ def main():
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "byte_bound_speedup": round(db.total / sb.total, 3),
         "host_wall_ms_per_step": round(1000 * wall / K, 4),
+        "sequential_ms_per_step": round(seq_ms, 5),
         "keep_sweep": sweep,
         "roofline": {
             "kernel": "k_qkv (sparse Q/K/V gather-GEMV + KV append)",

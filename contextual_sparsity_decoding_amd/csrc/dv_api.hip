@@ -47,6 +47,11 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
         dv_status st_ = (expr);              \
         if (st_ != DV_OK) return st_;        \
     } while (0)
+#define HIP_TRY(expr)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess) return fail(DV_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
 
 // ---- workspace layouts ------------------------------------------------------
 
@@ -317,6 +322,7 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
 // ---------------------------------------------------------------- the layer --
 struct LayerWs {
     float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
+    float *ya, *hpartA, *hpartM, *sA2, *sM2;      // the look-ahead predictions' own scratch
     int32_t *head_idx, *nidx, *uidx, *ucnt;
     size_t bytes;
 };
@@ -353,6 +359,11 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     const size_t xp = axpy_ws_floats(po, B, d) > axpy_ws_floats(pm, B, d) ? axpy_ws_floats(po, B, d)
                                                                            : axpy_ws_floats(pm, B, d);
     w.xpart = cv.take<float>(xp);
+    w.ya = cv.take<float>((size_t)d);
+    w.hpartA = cv.take<float>(pred_partials(1, d, c->r_attn > 0 ? c->r_attn : 1, c->wdt));
+    w.hpartM = cv.take<float>(pred_partials(1, d, c->r_mlp > 0 ? c->r_mlp : 1, c->wdt));
+    w.sA2 = cv.take<float>((size_t)h);
+    w.sM2 = cv.take<float>((size_t)c->N);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -361,7 +372,8 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(c, DV_ERR_NULL, "dv_decode_layer: cfg NULL");
     REQ(wdt_ok(c->wdt), DV_ERR_DTYPE, "dv_decode_layer: wdt %d", c->wdt);
     REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
-    const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT | DV_ADVANCE_POS;
+    const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT | DV_ADVANCE_POS |
+                           DV_LOOKAHEAD;
     REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
     REQ(c->B >= 1 && c->B <= 16 && d_ok(c->d) && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
         "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
@@ -380,6 +392,104 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
             c->k_neurons);
     }
     REQ(isfinite(c->scale) && c->eps >= 0.f && isfinite(c->eps), DV_ERR_RANGE, "dv_decode_layer: scale/eps");
+    if (c->flags & DV_LOOKAHEAD) {
+        REQ(c->B == 1, DV_ERR_UNSUPPORTED, "dv_decode_layer: DV_LOOKAHEAD with B=%d", c->B);
+        REQ(c->r_attn >= 1 && c->r_attn <= 512 && (size_t)c->r_attn * eb % 16 == 0 && c->r_mlp >= 1 &&
+                c->r_mlp <= 512 && (size_t)c->r_mlp * eb % 16 == 0,
+            DV_ERR_SHAPE, "dv_decode_layer: look-ahead ranks r_attn=%d r_mlp=%d", c->r_attn, c->r_mlp);
+        REQ(c->k_heads >= 0 && c->k_heads <= c->h && c->k_neurons >= 0 && c->k_neurons <= c->N &&
+                c->N <= dv::kTopkMaxN,
+            DV_ERR_RANGE, "dv_decode_layer: look-ahead budgets k_heads=%d k_neurons=%d", c->k_heads, c->k_neurons);
+    }
+    return DV_OK;
+}
+
+// DejaVu §4.3, the parallel form (batch of one): the next layer's sets are
+// predicted from this layer's y = LN1(x) on the auxiliary stream while this
+// layer runs on the main one with its given sets.  LN1 is folded into the
+// Q/K/V kernel and LN2 into fc1, so the main stream runs seven kernels.
+static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                                  const dv_kv_view& view, const LayerWs& L, const float* x_in, float* x_out, void* ws,
+                                  hipStream_t s) {
+    const int d = c->d, h = c->h, dh = c->d_h, N = c->N;
+    const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
+    REQ(dense_a || st->head_idx_in, DV_ERR_NULL, "dv_decode_layer: DV_LOOKAHEAD needs head_idx_in");
+    REQ(dense_m || st->neuron_idx_in, DV_ERR_NULL, "dv_decode_layer: DV_LOOKAHEAD needs neuron_idx_in");
+    REQ((st->next_pa1_t == nullptr) == (st->next_pa2_t == nullptr) &&
+            (st->next_pm1_t == nullptr) == (st->next_pm2_t == nullptr),
+        DV_ERR_NULL, "dv_decode_layer: next predictor layers go in pairs");
+    REQ(!st->next_pa1_t || st->next_head_idx, DV_ERR_NULL, "dv_decode_layer: next_head_idx NULL");
+    REQ(!st->next_pm1_t || st->next_neuron_idx, DV_ERR_NULL, "dv_decode_layer: next_neuron_idx NULL");
+    REQ(!st->next_pa1_t || (a16(st->next_pa1_t) && a16(st->next_pa2_t)), DV_ERR_ALIGN, "dv_decode_layer: next_pa alignment");
+    REQ(!st->next_pm1_t || (a16(st->next_pm1_t) && a16(st->next_pm2_t)), DV_ERR_ALIGN, "dv_decode_layer: next_pm alignment");
+    REQ(!st->aux_stream || (st->ev_fork && st->ev_join), DV_ERR_NULL, "dv_decode_layer: aux_stream needs ev_fork and ev_join");
+    const bool predict = st->next_pa1_t || st->next_pm1_t;
+    hipStream_t ps = st->aux_stream ? (hipStream_t)st->aux_stream : s;
+    if (predict && st->aux_stream) {
+        HIP_TRY(hipEventRecord((hipEvent_t)st->ev_fork, s));
+        HIP_TRY(hipStreamWaitEvent(ps, (hipEvent_t)st->ev_fork, 0));
+    }
+    // ---- the next layer's sets from this layer's y (predictor layers fold LN1 in)
+    if (st->next_pa1_t && c->k_heads > 0) {
+        if (pred_topk_fusable(1, h, c->r_attn)) {
+            TRY(launch_predict_ln_topk(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn,
+                                       st->next_pa2_t, h, c->wdt, c->pred_act, L.sA2, L.hpartA, c->k_heads,
+                                       st->next_head_idx, ps));
+        } else {
+            TRY(launch_predict_ln(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn,
+                                  st->next_pa2_t, h, c->wdt, c->pred_act, L.sA2, L.hpartA, ps));
+            TRY(launch_topk(L.sA2, 1, h, c->k_heads, st->next_head_idx, ps));
+        }
+    }
+    if (st->next_pm1_t && c->k_neurons > 0) {
+        TRY(launch_predict_ln(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pm1_t, c->r_mlp, st->next_pm2_t,
+                              N, c->wdt, c->pred_act, L.sM2, L.hpartM, ps));
+        TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, ps));
+    }
+    if (predict && st->aux_stream) HIP_TRY(hipEventRecord((hipEvent_t)st->ev_join, ps));
+
+    // ---- this layer with its given sets
+    const int32_t* head_idx = dense_a ? nullptr : st->head_idx_in;
+    const int n_sel = dense_a ? h : c->k_heads;
+    dv_kv_state kvs = st->kv;
+    if (!(c->flags & DV_HOLE_FILL)) {
+        kvs.y_buf = nullptr;
+        kvs.valid_upto = nullptr;
+    }
+    const bool fill = kvs.y_buf && kvs.valid_upto;
+    if (ln_fusable(1, d)) {
+        TRY(launch_qkv(x_in, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s, w->ln1_g,
+                       w->ln1_b, c->eps));
+    } else {
+        TRY(launch_layernorm(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+        TRY(launch_qkv(L.y, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
+    }
+    int splits = 0;
+    TRY(launch_splitk(L.q, 1, dh, head_idx, n_sel, &view, st->kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
+                      fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits));
+    {
+        AxpyCall ac{};
+        ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;
+        ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = 1; ac.bias = w->b_o; ac.residual = x_in;
+        ac.out = L.hres; ac.partial = L.xpart;
+        TRY(launch_axpy(ac, s));
+    }
+    const int32_t* idx = dense_m ? nullptr : st->neuron_idx_in;
+    const int n_max = dense_m ? N : c->k_neurons;
+    if (row_ln_supported(d, c->wdt)) {
+        TRY(launch_fc1_ln(L.hres, d, w->ln2_g, w->ln2_b, c->eps, w->w1_t, w->b1, c->wdt, idx, n_max, nullptr, N, L.a, s));
+    } else {
+        TRY(launch_layernorm(L.hres, 1, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
+        TRY(launch_fc1(L.y2, 1, d, w->w1_t, w->b1, c->wdt, idx, n_max, nullptr, N, L.a, s));
+    }
+    AxpyCall mc{};
+    mc.w = w->w2_t; mc.wdt = c->wdt; mc.d = d; mc.w_rows = N; mc.rows = n_max; mc.idx = idx; mc.blk = 1; mc.coef = L.a;
+    mc.coef_stride = n_max; mc.skip_zero = (c->flags & DV_SKIP_NONPOS_FC2) != 0; mc.B = 1; mc.bias = w->b2;
+    mc.residual = L.hres; mc.out = x_out; mc.rows_read = st->fc2_rows_out; mc.partial = L.xpart;
+    mc.advance = (c->flags & DV_ADVANCE_POS) ? st->kv.pos_dev : nullptr;
+    TRY(launch_axpy(mc, s));
+    if (predict && st->aux_stream) HIP_TRY(hipStreamWaitEvent(s, (hipEvent_t)st->ev_join, 0));
+    (void)ws;
     return DV_OK;
 }
 
@@ -396,8 +506,10 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     REQ(w->ln1_g && w->ln1_b && w->ln2_g && w->ln2_b && w->w_qkv_t && w->b_qkv && w->w_o_t && w->b_o && w->w1_t &&
             w->b1 && w->w2_t && w->b2,
         DV_ERR_NULL, "dv_decode_layer: weight pointer NULL");
-    REQ((c->flags & DV_DENSE_ATTN) || (w->pa1_t && w->pa2_t), DV_ERR_NULL, "dv_decode_layer: head predictor NULL");
-    REQ((c->flags & DV_DENSE_MLP) || (w->pm1_t && w->pm2_t), DV_ERR_NULL, "dv_decode_layer: neuron predictor NULL");
+    const bool ahead = (c->flags & DV_LOOKAHEAD) != 0;   // this layer's sets are given: its predictors are not read
+    REQ(ahead || (c->flags & DV_DENSE_ATTN) || (w->pa1_t && w->pa2_t), DV_ERR_NULL, "dv_decode_layer: head predictor NULL");
+    REQ(ahead || (c->flags & DV_DENSE_MLP) || (w->pm1_t && w->pm2_t), DV_ERR_NULL,
+        "dv_decode_layer: neuron predictor NULL");
     const dv_kv_state& kv = st->kv;
     REQ(kv.k_cache && kv.v_cache, DV_ERR_NULL, "dv_decode_layer: KV cache NULL");
     REQ(kv.max_len >= 1 && kv.pos >= 0 && kv.pos < kv.max_len, DV_ERR_RANGE, "dv_decode_layer: pos=%d max_len=%d",
@@ -423,6 +535,7 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     REQ(ws && ws_bytes >= L.bytes, DV_ERR_WORKSPACE, "dv_decode_layer: workspace %zu < %zu", ws_bytes, L.bytes);
 
     hipStream_t s = (hipStream_t)stream;
+    if (ahead) return decode_lookahead(w, c, st, view, L, x_in, x_out, ws, s);
     const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N;
     // attention block: LN1 folded into the head predictor when heads are selected
     const int32_t* head_idx = nullptr;

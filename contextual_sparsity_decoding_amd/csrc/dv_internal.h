@@ -256,12 +256,16 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s);
 bool qkv_supported(int B, int d, int wdt);
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
                      const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
-                     hipStream_t s);
+                     hipStream_t s, const float* ln_g = nullptr, const float* ln_b = nullptr, float eps = 0.f);
+dv_status launch_fc1_ln(const float* x, int d, const float* g, const float* b, float eps, const void* w1_t,
+                        const void* b1, int wdt, const int32_t* idx, int n_max, const int32_t* n_dev, int N, float* a_out,
+                        hipStream_t s);
 bool ln_fusable(int B, int d);
 dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
                             const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
                             float* hid, hipStream_t s);
 bool pred_topk_fusable(int B, int n_out, int r);
+bool row_ln_supported(int d, int wdt);
 dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
                                  const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act,
                                  float* scores, float* hid, int k, int32_t* idx, hipStream_t s);

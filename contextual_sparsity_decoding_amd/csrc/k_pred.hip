@@ -53,60 +53,40 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restric
     }
 }
 
-// The predictor's first layer with the block's LayerNorm folded in (batch
-// row 0 only): every workgroup normalises x in LDS itself (the statistics of
-// a 5120-float row cost far less than a launch), workgroup 0 also writes y
-// for the kernels that follow.
-struct LnArgs {
-    const float* x;
-    const float* g;
-    const float* b;
-    float eps;
-    float* y_out;
-};
-
-__device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
-    __shared__ float red[4];
-    float s = 0.f;
-    for (int i = threadIdx.x; i < d; i += kBlock) s += ys[i];
-    const float mean = block_sum256(s, red) / (float)d;
-    float q = 0.f;
-    for (int i = threadIdx.x; i < d; i += kBlock) {
-        const float t = ys[i] - mean;
-        q = fmaf(t, t, q);
-    }
-    const float rstd = 1.0f / sqrtf(block_sum256(q, red) / (float)d + ln.eps);
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
-    const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
-    f32x4* y4 = reinterpret_cast<f32x4*>(ys);
-#pragma unroll 8
-    for (int c = threadIdx.x; c < d / 4; c += kBlock) {
-        const f32x4 gg = g4[c], bb = b4[c];
-        f32x4 v = y4[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd * gg[e] + bb[e];
-        y4[c] = v;
-        if (write) reinterpret_cast<f32x4*>(ln.y_out)[c] = v;
-    }
-    __syncthreads();
-}
-
-template <typename T, int CH>
+// A row-dot with the block's LayerNorm folded in (batch row 0): the
+// predictor's first layer (OP = ROW_PLAIN, rows 0..n_max-1) or fc1 over the
+// selected rows (OP = ROW_FC1: bias, ReLU).  One row per wave.  Every
+// workgroup normalises x in LDS itself while its rows are still in flight
+// (the statistics of a 5120-float row cost far less than a launch);
+// workgroup 0 also writes y when ln.y_out is set.
+template <typename T, int CH, int OP>
 __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
     constexpr int E = Vec<T>::E;
     extern __shared__ float ys[];
-    const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
+    const int u = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nchunk = a.d / E;
-    const bool live = u < a.n_max;
+    int j = -1;
+    if (u < n) {
+        const int jj = a.idx ? a.idx[u] : u;
+        j = (unsigned)jj < (unsigned)a.w_rows ? jj : -1;   // an index outside W selects nothing
+    }
+    j = __builtin_amdgcn_readfirstlane(j);
     stage_dma(ys, ln.x, a.d);                        // x straight into LDS, ahead of the row
+    issue_order_fence();
     u32x4 w[CH];
-    if (live) load_row<T, CH, true>((const T*)a.w + (size_t)u * a.d, nchunk, w);
-    wait_dma_and_sync();
-    layernorm_lds(ys, a.d, ln, blockIdx.x == 0);
-    if (!live) return;
+    if (j >= 0) {
+        load_row_all<T, CH>((const T*)a.w + (size_t)j * a.d, nchunk, w);
+        sync_after_dma<CH>();                        // x has landed; the row may still be in flight
+    } else {
+        sync_after_dma<0>();
+    }
+    layernorm_lds(ys, a.d, ln, blockIdx.x == 0 && ln.y_out != nullptr);
+    if (u >= a.n_max) return;
     float acc[1] = {0.f};
-    dot_row<T, CH, 1>(w, nchunk, ys, a.d, 1, acc);
-    const float v = wave_sum(acc[0]);
+    if (j >= 0) dot_row<T, CH, 1>(w, nchunk, ys, a.d, 1, acc);
+    float v = wave_sum(acc[0]);
+    if (OP == ROW_FC1) v = j >= 0 ? fmaxf(v + to_f32(((const T*)a.bias)[j]), 0.f) : 0.f;
     if ((threadIdx.x & 63) == 0) a.out[u] = v;
 }
 
@@ -281,18 +261,18 @@ dv_status launch_predict(const float* y, int B, int d, const void* p1_t, int r, 
 
 bool ln_fusable(int B, int d) { return B == 1 && (size_t)d * sizeof(float) <= kYLdsMax && d % 4 == 0; }
 
-template <typename T>
+template <typename T, int OP>
 static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStream_t s) {
     const int grid = cdiv(a.n_max, 4);
     const size_t lds = (size_t)a.d * sizeof(float);
     switch (ch) {
-        case 4: hipLaunchKernelGGL((k_rowdot_ln<T, 4>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 8: hipLaunchKernelGGL((k_rowdot_ln<T, 8>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 10: hipLaunchKernelGGL((k_rowdot_ln<T, 10>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 12: hipLaunchKernelGGL((k_rowdot_ln<T, 12>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 16: hipLaunchKernelGGL((k_rowdot_ln<T, 16>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 18: hipLaunchKernelGGL((k_rowdot_ln<T, 18>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 24: hipLaunchKernelGGL((k_rowdot_ln<T, 24>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 4: hipLaunchKernelGGL((k_rowdot_ln<T, 4, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 8: hipLaunchKernelGGL((k_rowdot_ln<T, 8, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 10: hipLaunchKernelGGL((k_rowdot_ln<T, 10, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 12: hipLaunchKernelGGL((k_rowdot_ln<T, 12, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 16: hipLaunchKernelGGL((k_rowdot_ln<T, 16, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 18: hipLaunchKernelGGL((k_rowdot_ln<T, 18, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        case 24: hipLaunchKernelGGL((k_rowdot_ln<T, 24, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
         default: return fail(DV_ERR_UNSUPPORTED, "fused LayerNorm: d=%d", a.d);
     }
     return DV_OK;
@@ -309,8 +289,8 @@ dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const 
     RowArgs a{};
     a.y = nullptr; a.B = 1; a.d = d; a.w = p1_t; a.n_max = r; a.w_rows = r; a.out = hid;
     LnArgs ln{x, g, b, eps, y_out};
-    dv_status st = wdt == DV_F16 ? predict_ln_t<half_t>(a, ln, ch_tier(d, wdt), s)
-                                 : predict_ln_t<float>(a, ln, ch_tier(d, wdt), s);
+    dv_status st = wdt == DV_F16 ? predict_ln_t<half_t, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s)
+                                 : predict_ln_t<float, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s);
     if (st != DV_OK) return st;
     DV_LAUNCH_CHECK();
 #define DV_SC(NB)                                                                              \
@@ -326,6 +306,24 @@ dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const 
     return DV_OK;
 }
 
+dv_status launch_fc1_ln(const float* x, int d, const float* g, const float* b, float eps, const void* w1_t,
+                        const void* b1, int wdt, const int32_t* idx, int n_max, const int32_t* n_dev, int N, float* a_out,
+                        hipStream_t s) {
+    if (n_max == 0) return DV_OK;
+    if (!ln_fusable(1, d) || ch_tier(d, wdt) == 0) return fail(DV_ERR_UNSUPPORTED, "fc1 with LayerNorm: d=%d", d);
+    RowArgs a{};
+    a.y = nullptr; a.B = 1; a.d = d; a.w = w1_t; a.bias = b1; a.idx = idx; a.n_max = n_max; a.n_dev = n_dev;
+    a.w_rows = N; a.out = a_out;
+    LnArgs ln{x, g, b, eps, nullptr};
+    dv_status st = wdt == DV_F16 ? predict_ln_t<half_t, ROW_FC1>(a, ln, ch_tier(d, wdt), s)
+                                 : predict_ln_t<float, ROW_FC1>(a, ln, ch_tier(d, wdt), s);
+    if (st != DV_OK) return st;
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
+
+bool row_ln_supported(int d, int wdt) { return ln_fusable(1, d) && ch_tier(d, wdt) != 0; }
+
 bool pred_topk_fusable(int B, int n_out, int r) { return B == 1 && n_out <= kBlock && r <= 512; }
 
 dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
@@ -335,8 +333,8 @@ dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const fl
         RowArgs a{};
         a.y = nullptr; a.B = 1; a.d = d; a.w = p1_t; a.n_max = r; a.w_rows = r; a.out = hid;
         LnArgs ln{x, g, b, eps, y_out};
-        dv_status st = wdt == DV_F16 ? predict_ln_t<half_t>(a, ln, ch_tier(d, wdt), s)
-                                     : predict_ln_t<float>(a, ln, ch_tier(d, wdt), s);
+        dv_status st = wdt == DV_F16 ? predict_ln_t<half_t, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s)
+                                     : predict_ln_t<float, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s);
         if (st != DV_OK) return st;
     } else {
         dv_status st = launch_layernorm(x, 1, d, g, b, eps, y_out, s);

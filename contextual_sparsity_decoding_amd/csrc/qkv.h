@@ -29,6 +29,9 @@ struct QkvArgs {
     const int32_t* pos_dev;   // slot read at run time, or NULL for pos
     float* y_buf;
     int32_t* valid_upto;
+    const float* ln_g;        // LNF: y = LayerNorm(input) computed in the kernel
+    const float* ln_b;
+    float eps;
 };
 
 // A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
@@ -40,7 +43,10 @@ struct QkvArgs {
 // Recomputed entries take the same instructions on the same input values as
 // the entries computed on time, so they are bit-identical to them.  When y
 // does not fit in LDS (YL false: wide batches) it is read from global memory.
-template <typename T, int NB, int CH, int R, int HB, bool YL>
+// With LNF (batch of one) the input is the residual stream x and every
+// workgroup applies the block's LayerNorm in LDS while its weight rows are
+// still in flight.
+template <typename T, int NB, int CH, int R, int HB, bool YL, bool LNF>
 __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     constexpr int E = Vec<T>::E;
     constexpr int HV = HB > 0 ? HB : 1;
@@ -65,25 +71,42 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     if (YL) stage_dma(ys, a.y, a.B * d);
     if (HB > 0 && fill && pos > lo0) stage_dma(hin, a.y_buf + (size_t)lo0 * d, min(HB, pos - lo0) * d);
     const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh + e0) * d;
-    // chunk-major, the order the dot products consume them in
+    issue_order_fence();
+    // chunk-major, the order the dot products consume them in; a live
+    // workgroup issues all R * CH loads (chunks past the row re-read chunk 0
+    // and are never used: the dot products stop at the row's end)
     u32x4 w[R][CH];
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+        for (int i = 0; i < CH; ++i)
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const int c = lane + i * kWave;
-            w[j][i] = (live && c < nchunk) ? ld16_stream(Wb + (size_t)j * d + (size_t)c * E) : u32x4{0u, 0u, 0u, 0u};
-        }
+            for (int j = 0; j < R; ++j) {
+                const int c = lane + i * kWave;
+                w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+            for (int j = 0; j < R; ++j) w[j][i] = u32x4{0u, 0u, 0u, 0u};
+    }
     float bv[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e0 + j]) : 0.f;
-    wait_dma_and_sync();
+    if constexpr (LNF) {
+        if (live) sync_after_dma<R * CH>();          // the inputs have landed; the rows may still be in flight
+        else sync_after_dma<0>();
+        const LnArgs ln{a.y, a.ln_g, a.ln_b, a.eps, nullptr};
+        layernorm_lds(ys, d, ln, false);
+    } else {
+        wait_dma_and_sync();
+    }
     // this step's input joins the stored inputs: float4 c of [B][d] goes
     // with thread c of the grid (a handful of workgroups), from LDS when staged
     if (a.y_buf && pos_ok) {
         for (int c = blockIdx.x * kBlock + threadIdx.x; c < a.B * d / 4; c += gridDim.x * kBlock) {
             const int b = (c * 4) / d, col = (c * 4) % d;
-            const f32x4 v = YL ? reinterpret_cast<const f32x4*>(ys)[c] : reinterpret_cast<const f32x4*>(a.y)[c];
+            const f32x4 v = (YL || LNF) ? reinterpret_cast<const f32x4*>(ys)[c] : reinterpret_cast<const f32x4*>(a.y)[c];
             *reinterpret_cast<f32x4*>(a.y_buf + ((size_t)b * a.max_len + pos) * d + col) = v;
         }
     }
@@ -225,10 +248,18 @@ static dv_status qkv_go3(const QkvArgs& a, hipStream_t s) {
     if (a.dh % (4 * R)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
     const int grid = rows / (4 * R);
     const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
-#define DV_QKV(HB, LDS)                                                                                  \
-    do {                                                                                                 \
-        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true>), dim3(grid), dim3(kBlock), LDS, s, a); \
-        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
+    const bool lnf = a.ln_g != nullptr;
+    if (lnf && (NB != 1 || !yl)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V with LayerNorm: B=%d d=%d", a.B, a.d);
+#define DV_QKV(HB, LDS)                                                                                          \
+    do {                                                                                                         \
+        if constexpr (NB == 1) {                                                                                 \
+            if (lnf) {                                                                                           \
+                hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, true>), dim3(grid), dim3(kBlock), LDS, s, a);  \
+                break;                                                                                           \
+            }                                                                                                    \
+        }                                                                                                        \
+        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, false>), dim3(grid), dim3(kBlock), LDS, s, a); \
+        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false, false>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
     } while (0)
     if (holes && yl + 2 * row <= kQkvLdsMax) DV_QKV(2, yl + 2 * row);
     else if (holes && yl + row <= kQkvLdsMax) DV_QKV(1, yl + row);

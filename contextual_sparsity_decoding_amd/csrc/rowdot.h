@@ -16,6 +16,16 @@ namespace dv {
 constexpr int kLnThreads = 1024;
 constexpr int kLnVec = 4;                 // float4 per thread: d <= 16384
 
+// A workgroup barrier for LDS traffic only: this wave's LDS operations have
+// completed, then s_barrier.  Unlike __syncthreads it does not wait for
+// outstanding global loads, so weight rows stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float block_sum1024(float v, float* red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
@@ -31,10 +41,70 @@ __device__ __forceinline__ float block_sum1024(float v, float* red) {
 __device__ __forceinline__ float block_sum256(float v, float* red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
+    lds_barrier();
     return red[0] + red[1] + red[2] + red[3];
+}
+
+// LayerNorm of one row held in LDS, in place: population variance, then
+// gamma and beta (DejaVu App. B: a norm precedes each block).  Every thread
+// of the workgroup takes part; ends with a barrier.  With `write`, the
+// normalised row is also stored to ln.y_out.
+struct LnArgs {
+    const float* x;
+    const float* g;
+    const float* b;
+    float eps;
+    float* y_out;
+};
+
+__device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < d; i += kBlock) s += ys[i];
+    const float mean = block_sum256(s, red) / (float)d;
+    float q = 0.f;
+    for (int i = threadIdx.x; i < d; i += kBlock) {
+        const float t = ys[i] - mean;
+        q = fmaf(t, t, q);
+    }
+    const float rstd = 1.0f / sqrtf(block_sum256(q, red) / (float)d + ln.eps);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
+    f32x4* y4 = reinterpret_cast<f32x4*>(ys);
+#pragma unroll 8
+    for (int c = threadIdx.x; c < d / 4; c += kBlock) {
+        const f32x4 gg = g4[c], bb = b4[c];
+        f32x4 v = y4[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd * gg[e] + bb[e];
+        y4[c] = v;
+        if (write) reinterpret_cast<f32x4*>(ln.y_out)[c] = v;
+    }
+    lds_barrier();
+}
+
+// Wait until at most N vector-memory operations of this wave are still
+// outstanding (loads retire in issue order, so everything issued before the
+// last N has completed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Keeps the compiler from moving memory operations across this point (the
+// input DMA must be issued before the weight loads that a partial vmcnt
+// wait leaves in flight).
+__device__ __forceinline__ void issue_order_fence() { asm volatile("" ::: "memory"); }
+
+// After an input DMA followed by N weight loads per wave: the DMA has landed
+// in every wave's share of LDS, the weights may still be in flight.
+template <int N>
+__device__ __forceinline__ void sync_after_dma() {
+    wait_vmcnt<N>();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------- staging ---
@@ -94,6 +164,20 @@ __device__ __forceinline__ void load_row(const T* __restrict__ row, int nchunk, 
             w[i] = STREAM ? ld16_stream(row + (size_t)c * E) : ld16(row + (size_t)c * E);
         else
             w[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// As load_row, but every one of the CH loads is issued (chunks past the row
+// re-read chunk 0; dot_row never uses them), so a wave has exactly CH loads
+// in flight.
+template <typename T, int CH>
+__device__ __forceinline__ void load_row_all(const T* __restrict__ row, int nchunk, u32x4 (&w)[CH]) {
+    constexpr int E = Vec<T>::E;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        w[i] = ld16_stream(row + (size_t)(c < nchunk ? c : 0) * E);
     }
 }
 

@@ -31,6 +31,7 @@ DV_DENSE_MLP = 0x4
 DV_HOLE_FILL = 0x8
 DV_KV_SELECT = 0x10
 DV_ADVANCE_POS = 0x20
+DV_LOOKAHEAD = 0x40
 STATUS = ["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN", "DV_ERR_RANGE",
           "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]
 
@@ -61,7 +62,12 @@ class LayerWeights(C.Structure):
 class LayerState(C.Structure):
     _fields_ = [("kv", KVState), ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci), ("sel_end", ci),
                 ("head_idx_out", vp), ("neuron_idx_out", vp), ("neuron_count_out", vp),
-                ("fc2_rows_out", vp)]
+                ("fc2_rows_out", vp),
+                # DV_LOOKAHEAD
+                ("head_idx_in", vp), ("neuron_idx_in", vp),
+                ("next_pa1_t", vp), ("next_pa2_t", vp), ("next_pm1_t", vp), ("next_pm2_t", vp),
+                ("next_head_idx", vp), ("next_neuron_idx", vp),
+                ("aux_stream", vp), ("ev_fork", vp), ("ev_join", vp)]
 
 
 def _sig(name, restype, *argtypes):

@@ -75,6 +75,7 @@ typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
 #define DV_HOLE_FILL       0x8u  /* recompute skipped heads' K/V (DejaVu §4.2) */
 #define DV_KV_SELECT       0x10u /* attend to retained KV positions only (ByteCross §4.1) */
 #define DV_ADVANCE_POS     0x20u /* dv_decode_layer: add 1 to *kv.pos_dev when the step is done */
+#define DV_LOOKAHEAD       0x40u /* dv_decode_layer: DejaVu §4.3 parallel form (see dv_layer_state) */
 
 int dv_api_version(void);
 const char* dv_status_str(int status);
@@ -294,6 +295,27 @@ typedef struct {
     int32_t* neuron_idx_out;    /* [min(N, B*k_neurons)] selected (union) neurons */
     int32_t* neuron_count_out;  /* [1] number of entries in neuron_idx_out */
     int32_t* fc2_rows_out;      /* [1] incremented by the fc2 rows read */
+    /* DV_LOOKAHEAD (DejaVu §4.3, the parallel form; B == 1).  This layer's
+     * sets were predicted one layer ahead and are given; the layer computes
+     * h = x + MHA_{S_A}(LN1(x)) and x_out = h + MLP_{S_M}(LN2(h)).  Alongside,
+     * the next layer's predictors read this layer's y = LN1(x):
+     * next_head_idx = top-k_heads(SP_A'(y)), next_neuron_idx =
+     * top-k_neurons(SP_M'(y)), with this call's ranks, budgets and act.  With
+     * aux_stream set, those predictions run on it: the call records ev_fork
+     * on `stream`, makes aux_stream wait for it, records ev_join on
+     * aux_stream after the predictions and makes `stream` wait for ev_join
+     * before returning (a captured graph gets two branches).  Without
+     * aux_stream they run first on `stream`.  The events and the stream are
+     * the caller's (created once, reused by every call). */
+    const int32_t* head_idx_in;     /* [k_heads] ascending; ignored with DV_DENSE_ATTN */
+    const int32_t* neuron_idx_in;   /* [k_neurons] ascending; ignored with DV_DENSE_MLP */
+    const void *next_pa1_t, *next_pa2_t;   /* next layer's head predictor, or NULL for none */
+    const void *next_pm1_t, *next_pm2_t;   /* next layer's neuron predictor, or NULL for none */
+    int32_t* next_head_idx;         /* [k_heads] out, ascending */
+    int32_t* next_neuron_idx;       /* [k_neurons] out, ascending */
+    void* aux_stream;               /* hipStream_t, or NULL */
+    void* ev_fork;                  /* hipEvent_t, required with aux_stream */
+    void* ev_join;                  /* hipEvent_t, required with aux_stream */
 } dv_layer_state;
 
 size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len);

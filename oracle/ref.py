@@ -401,3 +401,44 @@ def decode_layer(x, W: dict, kv: KVState, pos: int, *, k_heads: int, k_neurons: 
                         residual=hres, skip_nonpos=skip_nonpos)
     rec.update(y=y, q=q, o=o, h=hres, y2=y2, a=a)
     return out, rec
+
+
+def decode_layer_lookahead(x, W: dict, W_next: Optional[dict], kv: KVState, pos: int, *,
+                           head_idx, neuron_idx, k_heads: int, k_neurons: int, scale: float,
+                           eps: float = 1e-5, pred_act: str = "relu", skip_nonpos: bool = True,
+                           hole_fill: bool = True, sel_idx=None, sel_len=None, sel_end: Optional[int] = None):
+    """One decode step in DejaVu §4.3's parallel form (batch of one).
+
+    This layer's sets S_A^l = ``head_idx`` and S_M^l = ``neuron_idx`` were
+    predicted one layer ahead and are given; the layer computes
+    y~ = MHA_{S_A^l}(y) and y^ = MLP_{S_M^l}(y~) with the same pre-LN residual
+    structure as ``decode_layer``.  Alongside, the next layer's predictors
+    (``W_next``'s pa1/pa2 and pm1/pm2) read this layer's normalised input
+    y = LN1(x): S_A^{l+1} = top-k_heads(SP_A^{l+1}(y)), S_M^{l+1} =
+    top-k_neurons(SP_M^{l+1}(y)) (DejaVu §4.3: both sets for layer l+1 come
+    from layer l's input, computed in parallel with layer l; Explainer §4.3).
+    ``head_idx`` / ``neuron_idx`` of None mean every head / neuron.
+
+    x [1][d].  Returns (x_out [1][d], record dict with next_head_idx,
+    next_neuron_idx and their fp32 scores).  Mutates ``kv``.
+    """
+    x = _f64(np.atleast_2d(x))
+    assert x.shape[0] == 1, "the parallel form is defined here for one sequence"
+    h = W["w_qkv_t"].shape[1]
+    N = W["w1_t"].shape[0]
+    rec = {}
+    y = layernorm(x, W["ln1_g"], W["ln1_b"], eps)
+    heads = np.arange(h) if head_idx is None else np.asarray(head_idx, dtype=np.int64)
+    q = qkv_step(y, W["w_qkv_t"], W["b_qkv"], heads, kv, pos, hole_fill)
+    o = attention(q, kv, heads, pos + 1, scale, sel_idx, sel_len, sel_end)
+    hres = out_proj(o, W["w_o_t"], W["b_o"], heads, residual=x)
+    y2 = layernorm(hres, W["ln2_g"], W["ln2_b"], eps)
+    idx = np.arange(N) if neuron_idx is None else np.asarray(neuron_idx, dtype=np.int64)
+    out, a = sparse_mlp(y2, W["w1_t"], W["b1"], W["w2_t"], W["b2"], idx, residual=hres, skip_nonpos=skip_nonpos)
+    if W_next is not None:
+        sA = predictor(y, W_next["pa1_t"], W_next["pa2_t"], pred_act).astype(np.float32)
+        sM = predictor(y, W_next["pm1_t"], W_next["pm2_t"], pred_act).astype(np.float32)
+        rec.update(next_head_scores=sA, next_neuron_scores=sM,
+                   next_head_idx=topk_select(sA[0], k_heads), next_neuron_idx=topk_select(sM[0], k_neurons))
+    rec.update(y=y, q=q, o=o, h=hres, y2=y2, a=a, head_idx=heads, neuron_idx=idx)
+    return out, rec

@@ -400,3 +400,53 @@ def test_decode_layer_batch_uses_union():
         y2 = ref.layernorm(hres, W["ln2_g"], W["ln2_b"])
         row, _ = ref.sparse_mlp(y2, W["w1_t"], W["b1"], W["w2_t"], W["b2"], rec["neuron_idx"], hres)
         np.testing.assert_allclose(out[b:b + 1], row, atol=1e-12)
+
+
+# ------------------------------------------------------------- look-ahead ----
+
+def test_lookahead_with_every_head_and_neuron_equals_dense_torch_layer():
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=19)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 20, 24, seed=19)
+    x = synth.layer_inputs(dims.d, 1, 1, seed=19)[0]
+    want = _torch_dense_layer(x, W, K, V, 20, 0.25, 1e-5)
+    kv = ref.KVState(K.copy(), V.copy(), np.zeros((1, 24, dims.d)), np.full((1, dims.h), 19))
+    got, _ = ref.decode_layer_lookahead(x, W, None, kv, 20, head_idx=None, neuron_idx=None, k_heads=dims.h,
+                                        k_neurons=dims.N, scale=0.25)
+    np.testing.assert_allclose(got, want, atol=1e-9, rtol=0)
+
+
+def test_lookahead_next_sets_are_brute_force_top_k_of_this_layers_input():
+    """The next layer's sets come from its predictors applied to this layer's
+    normalised input (torch float64 predictor, scores rounded to fp32, then
+    brute-force order: score descending, lower index first)."""
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=20)
+    Wn = synth.layer_weights(dims, seed=21)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 12, 16, seed=20)
+    x = synth.layer_inputs(dims.d, 1, 1, seed=20)[0]
+    kv = ref.KVState(K.copy(), V.copy(), np.zeros((1, 16, dims.d)), np.full((1, dims.h), 11))
+    k_h, k_m = 2, 17
+    _, rec = ref.decode_layer_lookahead(x, W, Wn, kv, 12, head_idx=[0, 3], neuron_idx=np.arange(0, 40, 3),
+                                        k_heads=k_h, k_neurons=k_m, scale=0.25)
+    y = F.layer_norm(t64(x), (dims.d,), t64(W["ln1_g"]), t64(W["ln1_b"]), 1e-5)
+    for p1, p2, k, key in (("pa1_t", "pa2_t", k_h, "next_head_idx"), ("pm1_t", "pm2_t", k_m, "next_neuron_idx")):
+        s = (torch.relu(y @ t64(Wn[p1]).T) @ t64(Wn[p2]).T).numpy().astype(np.float32)[0]
+        brute = sorted(sorted(range(len(s)), key=lambda i: (-float(s[i]), i))[:k])
+        assert list(rec[key]) == brute, key
+
+
+def test_lookahead_given_the_sequential_sets_reproduces_the_sequential_layer():
+    dims = small_dims()
+    W = synth.layer_weights(dims, seed=22)
+    K, V = synth.kv_cache(dims.h, dims.d_h, 10, 14, seed=22)
+    x = synth.layer_inputs(dims.d, 1, 1, seed=22)[0]
+    kv1 = ref.KVState(K.copy(), V.copy(), np.zeros((1, 14, dims.d)), np.full((1, dims.h), 9))
+    kv2 = ref.KVState(K.copy(), V.copy(), np.zeros((1, 14, dims.d)), np.full((1, dims.h), 9))
+    seq, rec = ref.decode_layer(x, W, kv1, 10, k_heads=2, k_neurons=30, scale=0.25)
+    par, rec2 = ref.decode_layer_lookahead(x, W, W, kv2, 10, head_idx=rec["head_idx"], neuron_idx=rec["neuron_idx"],
+                                           k_heads=2, k_neurons=30, scale=0.25)
+    assert np.array_equal(seq, par)
+    assert np.array_equal(kv1.K, kv2.K) and np.array_equal(kv1.V, kv2.V)
+    # the same predictor on the same input picks the same heads one layer ahead
+    assert np.array_equal(rec2["next_head_idx"], rec["head_idx"])
