@@ -192,7 +192,8 @@ def main():
     max_len = w.n_ctx + math.ceil(total_steps / R) + 8
     torch.cuda.set_device(0)
     copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
-    X = torch.from_numpy(np.ascontiguousarray(synth.layer_inputs(dims.d, K + max(Kd, 1), 1, SEED))).cuda()
+    X = torch.from_numpy(np.ascontiguousarray(synth.layer_inputs(dims.d, max(K, Kd, args.sweep_steps, 16), 1,
+                                                                 SEED))).cuda()
     out = torch.empty(1, dims.d, device="cuda")
     flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
 

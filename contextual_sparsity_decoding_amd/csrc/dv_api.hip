@@ -360,7 +360,7 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
                                                                            : axpy_ws_floats(pm, B, d);
     w.xpart = cv.take<float>(xp);
     w.ya = cv.take<float>((size_t)d);
-    w.hpartA = cv.take<float>(pred_partials(1, d, c->r_attn > 0 ? c->r_attn : 1, c->wdt));
+    w.hpartA = cv.take<float>((size_t)(c->r_attn > 0 ? c->r_attn : 1) + (c->r_mlp > 0 ? c->r_mlp : 1));   // [rA + rM]
     w.hpartM = cv.take<float>(pred_partials(1, d, c->r_mlp > 0 ? c->r_mlp : 1, c->wdt));
     w.sA2 = cv.take<float>((size_t)h);
     w.sM2 = cv.take<float>((size_t)c->N);
@@ -430,7 +430,15 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         HIP_TRY(hipStreamWaitEvent(ps, (hipEvent_t)st->ev_fork, 0));
     }
     // ---- the next layer's sets from this layer's y (predictor layers fold LN1 in)
-    if (st->next_pa1_t && c->k_heads > 0) {
+    const bool pair = st->next_pa1_t && st->next_pm1_t && c->k_heads > 0 && c->k_neurons > 0 &&
+                      row_ln_supported(d, c->wdt) && pred_topk_fusable(1, h, c->r_attn);
+    if (pair) {
+        TRY(launch_predict_pair_ln(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn, st->next_pa2_t,
+                                   h, c->k_heads, st->next_head_idx, st->next_pm1_t, c->r_mlp, st->next_pm2_t, N, L.sA2,
+                                   L.sM2, L.hpartA, c->wdt, c->pred_act, ps));
+        TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, ps));
+    }
+    if (!pair && st->next_pa1_t && c->k_heads > 0) {
         if (pred_topk_fusable(1, h, c->r_attn)) {
             TRY(launch_predict_ln_topk(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn,
                                        st->next_pa2_t, h, c->wdt, c->pred_act, L.sA2, L.hpartA, c->k_heads,
@@ -441,7 +449,7 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
             TRY(launch_topk(L.sA2, 1, h, c->k_heads, st->next_head_idx, ps));
         }
     }
-    if (st->next_pm1_t && c->k_neurons > 0) {
+    if (!pair && st->next_pm1_t && c->k_neurons > 0) {
         TRY(launch_predict_ln(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pm1_t, c->r_mlp, st->next_pm2_t,
                               N, c->wdt, c->pred_act, L.sM2, L.hpartM, ps));
         TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, ps));

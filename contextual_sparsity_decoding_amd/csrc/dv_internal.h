@@ -266,6 +266,10 @@ dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const 
                             float* hid, hipStream_t s);
 bool pred_topk_fusable(int B, int n_out, int r);
 bool row_ln_supported(int d, int wdt);
+dv_status launch_predict_pair_ln(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
+                                 const void* pa1_t, int rA, const void* pa2_t, int h, int kA, int32_t* idxA,
+                                 const void* pm1_t, int rM, const void* pm2_t, int N, float* sA, float* sM, float* hid,
+                                 int wdt, int act, hipStream_t s);
 dv_status launch_predict_ln_topk(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
                                  const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act,
                                  float* scores, float* hid, int k, int32_t* idx, hipStream_t s);

@@ -54,8 +54,9 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restric
 }
 
 // A row-dot with the block's LayerNorm folded in (batch row 0): the
-// predictor's first layer (OP = ROW_PLAIN, rows 0..n_max-1) or fc1 over the
-// selected rows (OP = ROW_FC1: bias, ReLU).  One row per wave.  Every
+// predictor's first layer (OP = ROW_PLAIN, rows 0..n_max-1, optionally the
+// rows of two predictors, the second's from a.w2) or fc1 over the selected
+// rows (OP = ROW_FC1: bias, ReLU).  One row per wave.  Every
 // workgroup normalises x in LDS itself while its rows are still in flight
 // (the statistics of a 5120-float row cost far less than a launch);
 // workgroup 0 also writes y when ln.y_out is set.
@@ -76,7 +77,9 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
     issue_order_fence();
     u32x4 w[CH];
     if (j >= 0) {
-        load_row_all<T, CH>((const T*)a.w + (size_t)j * a.d, nchunk, w);
+        const T* row = (a.w2 && j >= a.split) ? (const T*)a.w2 + (size_t)(j - a.split) * a.d
+                                              : (const T*)a.w + (size_t)j * a.d;
+        load_row_all<T, CH>(row, nchunk, w);
         sync_after_dma<CH>();                        // x has landed; the row may still be in flight
     } else {
         sync_after_dma<0>();
@@ -95,17 +98,17 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
 // layer 2 applies act to the r hidden values and scores every output row,
 // lpr lanes per row of r elements.
 template <typename T, int NB>
-__global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict__ hid_in, int B, int r, int act,
-                                                        const T* __restrict__ p2, int n_out, int lpr,
-                                                        int rows_per_block, float* __restrict__ scores) {
+__device__ __forceinline__ void pred_scores_block(int blk, float* hid /* LDS [NB][r_pad] */,
+                                                  const float* __restrict__ hid_in, int B, int r, int act,
+                                                  const T* __restrict__ p2, int n_out, int lpr, int rows_per_block,
+                                                  float* __restrict__ scores) {
     constexpr int E = Vec<T>::E;
-    extern __shared__ float hid[];                       // [NB][r_pad]
     const int r_pad = (r + 3) & ~3;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int grp = lane / lpr, t = lane % lpr;
     const int rpw = kWave / lpr;                         // rows per wave pass
     const int rchunk = r / E;                            // r*wb is a multiple of 16
-    const int j0 = blockIdx.x * rows_per_block;
+    const int j0 = blk * rows_per_block;
     const int j1 = min(n_out, j0 + rows_per_block);
     // this wave's first row, loaded before the hidden vector is staged
     const int jfirst = j0 + wv * rpw + grp;
@@ -144,6 +147,14 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict_
     }
 }
 
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict__ hid_in, int B, int r, int act,
+                                                        const T* __restrict__ p2, int n_out, int lpr,
+                                                        int rows_per_block, float* __restrict__ scores) {
+    extern __shared__ float hid[];
+    pred_scores_block<T, NB>(blockIdx.x, hid, hid_in, B, r, act, p2, n_out, lpr, rows_per_block, scores);
+}
+
 // The predictor's second layer fused with the selection for a short score
 // row (n_out <= 256, e.g. heads; batch row 0): thread j scores row j of P2
 // (all its r-element loads in flight at once), then ranks its key against
@@ -151,10 +162,9 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict_
 // ascending.  Same order as k_topk: score descending, ties to the lower
 // index, NaN last.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_pred_topk_small(const float* __restrict__ hid_in, int r, int act,
-                                                            const T* __restrict__ p2, int n_out,
-                                                            float* __restrict__ scores, int k,
-                                                            int32_t* __restrict__ idx) {
+__device__ __forceinline__ void pred_topk_small_block(const float* __restrict__ hid_in, int r, int act,
+                                                      const T* __restrict__ p2, int n_out, float* __restrict__ scores,
+                                                      int k, int32_t* __restrict__ idx) {
     constexpr int E = Vec<T>::E;
     constexpr int CB = 16;                               // chunk loads in flight per batch
     __shared__ float hid[512];
@@ -198,6 +208,28 @@ __global__ __launch_bounds__(kBlock) void k_pred_topk_small(const float* __restr
     unsigned total;
     const unsigned pos = block_excl_scan(sel ? 1u : 0u, tot, &total);
     if (sel && pos < (unsigned)k) idx[pos] = j;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_pred_topk_small(const float* __restrict__ hid_in, int r, int act,
+                                                            const T* __restrict__ p2, int n_out,
+                                                            float* __restrict__ scores, int k,
+                                                            int32_t* __restrict__ idx) {
+    pred_topk_small_block<T>(hid_in, r, act, p2, n_out, scores, k, idx);
+}
+
+// Both predictors' second layers in one launch: workgroup 0 scores the heads
+// and selects k_h of them, the others score the neurons (their selection is
+// the next launch).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_pred2_pair(const float* __restrict__ hidA, int rA, const T* __restrict__ p2A,
+                                                       int nA, float* __restrict__ sA, int kA, int32_t* __restrict__ idxA,
+                                                       const float* __restrict__ hidM, int rM, const T* __restrict__ p2M,
+                                                       int nM, int lpr, int rows_per_block, float* __restrict__ sM,
+                                                       int act) {
+    extern __shared__ float hid[];
+    if (blockIdx.x == 0) pred_topk_small_block<T>(hidA, rA, act, p2A, nA, sA, kA, idxA);
+    else pred_scores_block<T, 1>(blockIdx.x - 1, hid, hidM, 1, rM, act, p2M, nM, lpr, rows_per_block, sM);
 }
 
 }  // namespace dv
@@ -318,6 +350,40 @@ dv_status launch_fc1_ln(const float* x, int d, const float* g, const float* b, f
     dv_status st = wdt == DV_F16 ? predict_ln_t<half_t, ROW_FC1>(a, ln, ch_tier(d, wdt), s)
                                  : predict_ln_t<float, ROW_FC1>(a, ln, ch_tier(d, wdt), s);
     if (st != DV_OK) return st;
+    DV_LAUNCH_CHECK();
+    return DV_OK;
+}
+
+// Both predictors of a layer from one normalised input: one layer-one launch
+// over the head and neuron predictors' rows, one launch for both second
+// layers (the heads also selected).  hid holds rA + rM floats.
+dv_status launch_predict_pair_ln(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
+                                 const void* pa1_t, int rA, const void* pa2_t, int h, int kA, int32_t* idxA,
+                                 const void* pm1_t, int rM, const void* pm2_t, int N, float* sA, float* sM, float* hid,
+                                 int wdt, int act, hipStream_t s) {
+    if (!row_ln_supported(d, wdt) || !pred_topk_fusable(1, h, rA))
+        return fail(DV_ERR_UNSUPPORTED, "paired predictors: d=%d h=%d r=%d", d, h, rA);
+    RowArgs a{};
+    a.y = nullptr; a.B = 1; a.d = d; a.w = pa1_t; a.w2 = pm1_t; a.split = rA; a.n_max = rA + rM; a.w_rows = rA + rM;
+    a.out = hid;
+    LnArgs ln{x, g, b, eps, y_out};
+    dv_status st = wdt == DV_F16 ? predict_ln_t<half_t, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s)
+                                 : predict_ln_t<float, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s);
+    if (st != DV_OK) return st;
+    DV_LAUNCH_CHECK();
+    const int E = 16 / elt_bytes(wdt);
+    const int rchunk = rM / E;
+    int lpr = 1;
+    while (lpr < rchunk && lpr < kWave) lpr *= 2;
+    const int rows_per_block = (kWave / lpr) * 4 * 4;
+    const int grid = 1 + cdiv(N, rows_per_block);
+    const size_t lds = (size_t)((rM + 3) & ~3) * sizeof(float);
+    if (wdt == DV_F16)
+        hipLaunchKernelGGL(k_pred2_pair<half_t>, dim3(grid), dim3(kBlock), lds, s, hid, rA, (const half_t*)pa2_t, h, sA,
+                           kA, idxA, hid + rA, rM, (const half_t*)pm2_t, N, lpr, rows_per_block, sM, act);
+    else
+        hipLaunchKernelGGL(k_pred2_pair<float>, dim3(grid), dim3(kBlock), lds, s, hid, rA, (const float*)pa2_t, h, sA,
+                           kA, idxA, hid + rA, rM, (const float*)pm2_t, N, lpr, rows_per_block, sM, act);
     DV_LAUNCH_CHECK();
     return DV_OK;
 }

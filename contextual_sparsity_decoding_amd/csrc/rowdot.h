@@ -227,6 +227,8 @@ struct RowArgs {
     const int32_t* n_dev;   // count used, <= n_max, or NULL
     int w_rows;             // rows of W (bounds of idx)
     float* out;             // [B][n_max]
+    const void* w2;         // rows j >= split come from w2 (row j - split), or NULL
+    int split;
 };
 
 
