@@ -9,14 +9,19 @@ on and fc2 rows of non-positive neurons skipped.  The timed schedule is
 DejaVu §4.3's parallel form: the step runs Q/K/V + KV append (LN folded in)
 -> split-K attention -> W^O -> fc1 (LN folded in) -> fc2 on the sets
 predicted during the previous step, while the next step's head and neuron
-predictors and top-k run on a second stream.  Four independent layer copies
+predictors and selections ride in those launches as extra workgroups (the
+predictors' first layers beside Q/K/V, their second layers beside
+attention, the neuron top-k split over W^O, its finalize and fc2).  The same
+schedule with the predictions on a second stream is timed too.  Four
+independent layer copies
 are used in turn so that the 256 MB Infinity Cache cannot serve repeated
 reads; each copy's position advances by one per step it takes, and step s
 predicts for copy (s + 1) mod 4 with that copy's predictors.
 
 Prints one JSON line: decode tokens/s, effective HBM bandwidth on the bytes
-the step must read, the dominant kernel's roofline, the sequential schedule
-and the dense path of the same library, a neuron keep-ratio sweep, and the
+the step must read, the dominant kernel's roofline, the two-stream and
+sequential schedules and the dense path of the same library, a neuron
+keep-ratio sweep, and the
 CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
@@ -110,10 +115,12 @@ class Copy:
 class Ahead:
     """What the look-ahead schedule (DejaVu §4.3, parallel form) carries from
     step to step: two ping-pong pairs of index buffers (step s reads pair s % 2
-    and writes the next step's sets into the other), the second stream and the
-    fork/join events."""
+    and writes the next step's sets into the other), and for the two-stream
+    form the second stream and the fork/join events (without them the
+    predictions ride in the layer's own launches)."""
 
-    def __init__(self, torch, dims):
+    def __init__(self, torch, dims, two_stream=False):
+        self.two_stream = two_stream
         self.aux = torch.cuda.Stream()
         self.evs = [torch.cuda.Event(), torch.cuda.Event()]
         for e in self.evs:
@@ -134,7 +141,7 @@ def capture_steps(dv, torch, copies, cfg, X, first, count, out, ws, fc2_rows, ah
     """A HIP graph of `count` decode steps (step s uses copy s % R and input
     X[first + s]).  With `ahead`, step s runs copy s % R on the sets predicted
     by step s - 1 and predicts copy (s + 1) % R's sets with that copy's
-    predictors on the second stream."""
+    predictors (on the second stream when ahead.two_stream)."""
     g = torch.cuda.CUDAGraph()
     R = len(copies)
     with torch.cuda.graph(g):
@@ -151,8 +158,9 @@ def capture_steps(dv, torch, copies, cfg, X, first, count, out, ws, fc2_rows, ah
                 st.next_head_idx, st.next_neuron_idx = ahead.hb[q].data_ptr(), ahead.nb[q].data_ptr()
                 st.next_pa1_t, st.next_pa2_t = nxt.Wd["pa1_t"].data_ptr(), nxt.Wd["pa2_t"].data_ptr()
                 st.next_pm1_t, st.next_pm2_t = nxt.Wd["pm1_t"].data_ptr(), nxt.Wd["pm2_t"].data_ptr()
-                st.aux_stream = ahead.aux.cuda_stream
-                st.ev_fork, st.ev_join = ahead.evs[0].cuda_event, ahead.evs[1].cuda_event
+                if ahead.two_stream:
+                    st.aux_stream = ahead.aux.cuda_stream
+                    st.ev_fork, st.ev_join = ahead.evs[0].cuda_event, ahead.evs[1].cuda_event
             st.fc2_rows_out = fc2_rows.data_ptr() if fc2_rows is not None else 0
             rc = dv.lib.dv_decode_layer(dv.C.byref(cp.wts), dv.C.byref(cfg), dv.C.byref(st),
                                         X[first + i].data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
@@ -188,7 +196,7 @@ def main():
     warm_reps = max(1, math.ceil(args.warmup / K))
     Kd = args.dense_steps
     sweep_keep = (0.05, 0.10, 0.25, 0.50, 1.00)
-    total_steps = (warm_reps + 1) * K + 2 * K + (2 * Kd if Kd > 0 else 0) + 2 * args.sweep_steps * len(sweep_keep)
+    total_steps = (warm_reps + 1) * K + 4 * K + (2 * Kd if Kd > 0 else 0) + 2 * args.sweep_steps * len(sweep_keep)
     max_len = w.n_ctx + math.ceil(total_steps / R) + 8
     torch.cuda.set_device(0)
     copies = [Copy(dv, torch, dims, w.n_ctx, max_len, SEED + c) for c in range(R)]
@@ -226,6 +234,14 @@ def main():
     ms_step = ms_total / K
     rows_per_step = int(fc2_rows.item()) / K
     del g_sparse
+
+    # the same schedule with the predictions on a second stream (a fork and a join per step)
+    ahead2 = Ahead(torch, dims, two_stream=True)
+    ahead2.seed_sets(torch, w.k_heads, w.k_neurons, SEED)
+    g_two = capture_steps(dv, torch, copies, sparse_cfg, X, 0, K, out, ws, None, ahead2)
+    g_two.replay()
+    two_ms = time_graph(torch, g_two)[0] / K
+    del g_two
 
     # the sequential schedule (each block's predictor before the block) through the same kernels
     g_seq = capture_steps(dv, torch, copies, seq_cfg, X, 0, K, out, ws, None)
@@ -316,7 +332,8 @@ def main():
         "config": {
             "workload": "opt13b-layer decode: d=5120, 40 heads x 128, d_ffn=20480 ReLU, fp16, batch 1, "
                         "2048 cached tokens, keep 10% neurons (2048) and 50% heads (20), rank-128 predictors run "
-                        "one layer ahead on a second stream, 4 rotating layer copies, one HIP graph of the timed steps",
+                        "one layer ahead inside the layer's own launches, 4 rotating layer copies, one HIP graph of "
+                        "the timed steps",
             "global_batch": 1, "seq_len": w.n_ctx, "keep_neurons": 0.10, "keep_heads": 0.50,
         },
         "effective_hbm_GBps": round(sb.total / (ms_step * 1e-3) / 1e9, 1),
@@ -328,6 +345,7 @@ def main():
         "byte_bound_speedup": round(db.total / sb.total, 3),
         "host_wall_ms_per_step": round(1000 * wall / K, 4),
         "sequential_ms_per_step": round(seq_ms, 5),
+        "two_stream_ms_per_step": round(two_ms, 5),
         "keep_sweep": sweep,
         "roofline": {
             "kernel": "k_qkv (sparse Q/K/V gather-GEMV + KV append)",

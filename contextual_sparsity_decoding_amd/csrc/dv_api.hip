@@ -9,7 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "dv_internal.h"
+#include "pred.h"
+#include "topk_split.h"
 
 namespace dvh {
 
@@ -323,6 +324,8 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
 struct LayerWs {
     float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
     float *ya, *hpartA, *hpartM, *sA2, *sM2;      // the look-ahead predictions' own scratch
+    unsigned* khist;                              // [4096] top-12-bit histogram of the next layer's neuron scores
+    void* kthr;                                   // their selection threshold and slice offsets
     int32_t *head_idx, *nidx, *uidx, *ucnt;
     size_t bytes;
 };
@@ -364,6 +367,8 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     w.hpartM = cv.take<float>(pred_partials(1, d, c->r_mlp > 0 ? c->r_mlp : 1, c->wdt));
     w.sA2 = cv.take<float>((size_t)h);
     w.sM2 = cv.take<float>((size_t)c->N);
+    w.khist = cv.take<unsigned>(4096);
+    w.kthr = cv.take<unsigned>(4 + 64);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -425,14 +430,22 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     REQ(!st->aux_stream || (st->ev_fork && st->ev_join), DV_ERR_NULL, "dv_decode_layer: aux_stream needs ev_fork and ev_join");
     const bool predict = st->next_pa1_t || st->next_pm1_t;
     hipStream_t ps = st->aux_stream ? (hipStream_t)st->aux_stream : s;
+    const bool pair = st->next_pa1_t && st->next_pm1_t && c->k_heads > 0 && c->k_neurons > 0 &&
+                      row_ln_supported(d, c->wdt) && pred_topk_fusable(1, h, c->r_attn);
+    // Without a second stream the predictions ride in this layer's launches
+    // as extra workgroups: both first layers in the Q/K/V launch (same
+    // LN1(x)), both second layers in the attention launch, and the neuron
+    // selection split over later launches: a histogram of the scores beside
+    // the output projection, the threshold beside its finalize and the
+    // ordered emission beside fc2 (else a launch of its own after attention).
+    const bool ride = pair && !st->aux_stream && ln_fusable(1, d);
+    const bool ride_topk = ride && topk_split_supported(N, c->k_neurons);
     if (predict && st->aux_stream) {
         HIP_TRY(hipEventRecord((hipEvent_t)st->ev_fork, s));
         HIP_TRY(hipStreamWaitEvent(ps, (hipEvent_t)st->ev_fork, 0));
     }
     // ---- the next layer's sets from this layer's y (predictor layers fold LN1 in)
-    const bool pair = st->next_pa1_t && st->next_pm1_t && c->k_heads > 0 && c->k_neurons > 0 &&
-                      row_ln_supported(d, c->wdt) && pred_topk_fusable(1, h, c->r_attn);
-    if (pair) {
+    if (pair && !ride) {
         TRY(launch_predict_pair_ln(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn, st->next_pa2_t,
                                    h, c->k_heads, st->next_head_idx, st->next_pm1_t, c->r_mlp, st->next_pm2_t, N, L.sA2,
                                    L.sM2, L.hpartA, c->wdt, c->pred_act, ps));
@@ -465,21 +478,32 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         kvs.valid_upto = nullptr;
     }
     const bool fill = kvs.y_buf && kvs.valid_upto;
+    RowArgs p1{};
+    if (ride) {
+        p1.B = 1; p1.d = d; p1.w = st->next_pa1_t; p1.w2 = st->next_pm1_t; p1.split = c->r_attn;
+        p1.n_max = c->r_attn + c->r_mlp; p1.w_rows = p1.n_max; p1.out = L.hpartA;
+    }
     if (ln_fusable(1, d)) {
         TRY(launch_qkv(x_in, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s, w->ln1_g,
-                       w->ln1_b, c->eps));
+                       w->ln1_b, c->eps, ride ? &p1 : nullptr));
     } else {
         TRY(launch_layernorm(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
         TRY(launch_qkv(L.y, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
     }
     int splits = 0;
+    Pred2Args p2 = pred2_args(L.hpartA, c->r_attn, st->next_pa2_t, h, L.sA2, c->k_heads, st->next_head_idx,
+                              L.hpartA + c->r_attn, c->r_mlp, st->next_pm2_t, N, L.sM2, c->pred_act, c->wdt);
+    p2.zero = ride_topk ? L.khist : nullptr;
     TRY(launch_splitk(L.q, 1, dh, head_idx, n_sel, &view, st->kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
-                      fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits));
+                      fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits, ride ? &p2 : nullptr));
+    if (ride && !ride_topk) TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, s));
+    const TopkSel tk{L.sM2, N, c->k_neurons, L.khist, L.kthr, st->next_neuron_idx};
     {
         AxpyCall ac{};
         ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;
         ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = 1; ac.bias = w->b_o; ac.residual = x_in;
         ac.out = L.hres; ac.partial = L.xpart;
+        ac.sel = ride_topk ? &tk : nullptr;
         TRY(launch_axpy(ac, s));
     }
     const int32_t* idx = dense_m ? nullptr : st->neuron_idx_in;
@@ -495,6 +519,7 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     mc.coef_stride = n_max; mc.skip_zero = (c->flags & DV_SKIP_NONPOS_FC2) != 0; mc.B = 1; mc.bias = w->b2;
     mc.residual = L.hres; mc.out = x_out; mc.rows_read = st->fc2_rows_out; mc.partial = L.xpart;
     mc.advance = (c->flags & DV_ADVANCE_POS) ? st->kv.pos_dev : nullptr;
+    mc.sel = ride_topk ? &tk : nullptr;
     TRY(launch_axpy(mc, s));
     if (predict && st->aux_stream) HIP_TRY(hipStreamWaitEvent(s, (hipEvent_t)st->ev_join, 0));
     (void)ws;

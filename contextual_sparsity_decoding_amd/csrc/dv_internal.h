@@ -188,6 +188,9 @@ __device__ __forceinline__ void block_copy_f32(float* __restrict__ dst, const fl
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
 }
 
+struct RowArgs;    // rowdot.h
+struct Pred2Args;  // pred.h
+
 }  // namespace dv
 
 // ---- host side --------------------------------------------------------------
@@ -233,6 +236,17 @@ struct AxpyPlan {
 };
 AxpyPlan axpy_plan(int d, int rows, int wdt);
 size_t axpy_ws_floats(const AxpyPlan& p, int B, int d);
+// A top-k over n scores split into roles that ride in other launches
+// (topk_split.h): histogram slices, the threshold, ordered emission.
+struct TopkSel {
+    const float* s;           // scores [n], 16-byte aligned
+    int n, k;                 // 0 < k <= n <= 20480, n % 4 == 0
+    unsigned* hist;           // [4096], cleared before the histogram role
+    void* thr;                // the threshold (16 bytes), then per-slice offsets [n / 1024]
+    int32_t* idx;             // [k] selected, ascending
+};
+bool topk_split_supported(int n, int k);
+
 struct AxpyCall {
     const void* w;            // W [w_rows][d]
     int wdt, d, w_rows, rows;
@@ -251,12 +265,15 @@ struct AxpyCall {
     int32_t* rows_read;
     float* partial;
     int32_t* advance;
+    const TopkSel* sel;       // B == 1: also run a role of this selection in one more column of
+                              // workgroups (the first, with attention coefficients; else the last), or NULL
 };
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s);
 bool qkv_supported(int B, int d, int wdt);
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
                      const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
-                     hipStream_t s, const float* ln_g = nullptr, const float* ln_b = nullptr, float eps = 0.f);
+                     hipStream_t s, const float* ln_g = nullptr, const float* ln_b = nullptr, float eps = 0.f,
+                     const dv::RowArgs* pred = nullptr);
 dv_status launch_fc1_ln(const float* x, int d, const float* g, const float* b, float eps, const void* w1_t,
                         const void* b1, int wdt, const int32_t* idx, int n_max, const int32_t* n_dev, int N, float* a_out,
                         hipStream_t s);
@@ -282,7 +299,9 @@ int splitk_auto(int max_positions, int rows);
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
                         float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,
-                        int* splits_used = nullptr);
+                        int* splits_used = nullptr, const dv::Pred2Args* pred = nullptr);
+dv::Pred2Args pred2_args(const float* hid_a, int r_a, const void* p2_a, int n_a, float* s_a, int k_a, int32_t* idx_a,
+                         const float* hid_m, int r_m, const void* p2_m, int n_m, float* s_m, int act, int wdt);
 dv_status launch_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const dv_kv_view* kv,
                           float scale, int n_sink, int n_window, int width, float* scores,
                           float* raw, float* stats, hipStream_t s);

@@ -14,7 +14,11 @@
 // exp is the native exp2.  Each wave keeps a running (max, sum, weighted V),
 // merges its row groups with shuffles and writes one partial; the combine
 // kernel merges the partials of a head in split order.
-#include "dv_internal.h"
+//
+// In the look-ahead schedule the launch also carries the next layer's
+// predictor second layers (DejaVu §4.3): workgroups past the attention grid
+// take that role, so the predictions need no launch or stream of their own.
+#include "pred.h"
 
 #include <math.h>
 
@@ -38,13 +42,20 @@ struct AttnArgs {
     int32_t* mark_valid;    // [B][h]: set the selected heads to mark_pos (decode layer), or NULL
     int mark_pos;
     const int32_t* mark_pos_dev;
+    int attn_blocks;        // workgroups of attention; later ones run `pred` (weights of type T)
+    Pred2Args pred;
 };
 
-template <int DH>
+template <int DH, typename T>
 __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
     constexpr int LPR = DH / 8;            // lanes per row
     constexpr int RPW = kWave / LPR;       // rows per wave load
     constexpr int U = 4;                   // wave loads in flight (K and V each)
+    if ((int)blockIdx.x >= a.attn_blocks) {
+        extern __shared__ float hid[];
+        pred2_pair_block<T>(blockIdx.x - a.attn_blocks, hid, a.pred);
+        return;
+    }
     if (a.mark_valid && blockIdx.x == 0) {  // Q/K/V has finished: the selected heads hold K/V up to pos
         const int p = a.mark_pos_dev ? *a.mark_pos_dev : a.mark_pos;
         if (p >= 0 && p < a.max_len)
@@ -261,11 +272,11 @@ int splitk_auto(int max_positions, int rows) {
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
                         float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,
-                        int* splits_used) {
+                        int* splits_used, const Pred2Args* pred) {
     const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
     if (num_splits <= 0) num_splits = splitk_auto(maxpos, B * n_sel);
     if (splits_used) *splits_used = num_splits;
-    if (n_sel == 0) return DV_OK;
+    if (n_sel == 0 && !pred) return DV_OK;
     AttnArgs a;
     a.q = q; a.B = B; a.n_sel = n_sel; a.h = kv->h; a.head_idx = head_idx;
     a.K = (const half_t*)kv->k_cache; a.V = (const half_t*)kv->v_cache;
@@ -278,10 +289,16 @@ dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx,
     a.mark_valid = mark_valid; a.mark_pos = mark_pos; a.mark_pos_dev = mark_pos_dev;
     const int tasks = B * n_sel * num_splits;
     const int rows = B * n_sel;
+    a.attn_blocks = cdiv(tasks, 4);
+    a.pred = pred ? *pred : Pred2Args{};
+    const int grid = a.attn_blocks + (pred ? pred2_blocks(*pred) : 0);
+    const size_t lds = pred ? (size_t)((pred->r_m + 3) & ~3) * sizeof(float) : 0;
+    const bool pf32 = pred && pred->wdt == DV_F32;
 #define DV_ATT(DH)                                                                                   \
     case DH:                                                                                         \
-        hipLaunchKernelGGL((k_attn_split<DH>), dim3(cdiv(tasks, 4)), dim3(kBlock), 0, s, a);        \
-        if (o)                                                                                       \
+        if (pf32) hipLaunchKernelGGL((k_attn_split<DH, float>), dim3(grid), dim3(kBlock), lds, s, a); \
+        else hipLaunchKernelGGL((k_attn_split<DH, half_t>), dim3(grid), dim3(kBlock), lds, s, a);    \
+        if (o && rows)                                                                               \
             hipLaunchKernelGGL((k_attn_combine<DH>), dim3(rows), dim3(kBlock), 0, s, part, rows,    \
                                num_splits, o);                                                       \
         break;

@@ -20,7 +20,14 @@
 //
 // k_axpy_finalize then adds the partials in a fixed order, plus bias and
 // residual.  Results do not depend on scheduling.
-#include "dv_internal.h"
+//
+// In a look-ahead decode layer (DejaVu §4.3) these launches also carry the
+// next layer's neuron selection (topk_split.h): one more column of
+// workgroups, each taking 1024 scores, histograms their top key bits in the
+// output projection; one more workgroup of its finalize finds the
+// threshold; one more column emits the selected indices in the second MLP
+// layer, while the other workgroups stream rows.
+#include "topk_split.h"
 
 #include <math.h>
 
@@ -43,6 +50,14 @@ struct AxpyArgs {
     int B, n_groups;
     float* partial;           // [n_groups][B][d]
     int32_t* rows_read;
+    // NB == 1, tk_s set: the last column of workgroups runs a selection
+    // role over scores tk_s[0, tk_n), 1024 per workgroup: ATTN histograms
+    // them into tk_hist, otherwise emits the indices above tk_thr into tk_idx
+    const float* tk_s;
+    int tk_n, tk_k;
+    unsigned* tk_hist;
+    const TopkThreshold* tk_thr;
+    int32_t* tk_idx;
 };
 
 // Coefficient of row u = s * dh + e for batch row b: the attention output
@@ -127,6 +142,21 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     const T* W = (const T*)a.w;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, g = blockIdx.y;
+    if constexpr (NB == 1) {
+        static_assert(kBlock == 256, "a selection slice takes one 256-thread workgroup");
+        if (a.tk_s && slice == (int)gridDim.x - 1) {   // the extra column
+            if (g * kTopkSlice < a.tk_n) {
+                if constexpr (ATTN) {
+                    __shared__ unsigned tk_lds[4096];
+                    topk_hist_slice(a.tk_s, a.tk_n, g, tk_lds, a.tk_hist);
+                } else {
+                    topk_emit_slice(a.tk_s, a.tk_n, a.tk_k, g, a.tk_thr, (const unsigned*)a.tk_thr + 4, tot, a.tk_idx);
+                }
+            }
+            return;
+        }
+    }
+    if (g >= a.n_groups) return;                   // the extra column may be taller than the groups
     const int col = slice * SW + lane * E;
     const bool colok = col < a.d;
     const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
@@ -241,21 +271,22 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 }
 
 // out[b][c] = residual[b][c] + bias[c] + sum_g partial[g][b][c].  A block
-// covers 64 float4 columns of one batch row; its 4 waves each add a
-// contiguous quarter of the groups (all loads of a quarter in flight
-// together), then the quarters are added in order.  One thread also
-// advances a decode position when asked (nothing here reads it).
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restrict__ partial, int n_groups, int B, int d,
-                                                          const void* bias, const float* __restrict__ residual,
-                                                          float* __restrict__ out, int32_t* advance) {
-    constexpr int MAXQ = 16;                      // groups per quarter held in flight
-    __shared__ f32x4 red[3][64];
+// covers 64 float4 columns of one batch row; its NT/64 waves each add a
+// contiguous share of the groups (all loads of a share in flight together),
+// then the shares are added in order.  One thread also advances a decode
+// position when asked (nothing here reads it).
+template <typename T, int NT = kBlock>
+__device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ partial, int n_groups, int B, int d,
+                                                    const void* bias, const float* __restrict__ residual,
+                                                    float* __restrict__ out, int32_t* advance) {
+    constexpr int NW = NT / kWave;
+    constexpr int MAXQ = 16;                      // groups per share held in flight
+    __shared__ f32x4 red[NW - 1][64];
     const int b = blockIdx.y;
     const int c4 = blockIdx.x * 64 + (threadIdx.x & 63);
     const int q = threadIdx.x >> 6;
     const int n4 = d / 4;
-    const int per = (n_groups + 3) / 4;
+    const int per = (n_groups + NW - 1) / NW;
     const int g0 = q * per, g1 = min(n_groups, g0 + per);
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c4 < n4) {
@@ -272,7 +303,8 @@ __global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restric
     if (q > 0) red[q - 1][threadIdx.x & 63] = s;
     __syncthreads();
     if (q == 0 && c4 < n4) {
-        s = s + red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x];
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) s = s + red[w][threadIdx.x];
         if (bias) {
             const T* bb = (const T*)bias + (size_t)c4 * 4;
 #pragma unroll
@@ -284,10 +316,47 @@ __global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restric
     if (advance && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *advance += 1;
 }
 
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restrict__ partial, int n_groups, int B, int d,
+                                                          const void* bias, const float* __restrict__ residual,
+                                                          float* __restrict__ out, int32_t* advance) {
+    axpy_finalize_block<T>(partial, n_groups, B, d, bias, residual, out, advance);
+}
+
+// The finalize by 1024-thread workgroups, with one more workgroup (the last
+// of row 0) that finds the selection threshold from the histogram the
+// output projection built.
+constexpr int kFinThrThreads = 1024;
+struct FinThr {
+    const float* s;
+    int n, k;
+    const unsigned* hist;
+    TopkThreshold* thr;
+    unsigned* offs;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kFinThrThreads) void k_axpy_finalize_thr(const float* __restrict__ partial, int n_groups, int B,
+                                                              int d, const void* bias, const float* __restrict__ residual,
+                                                              float* __restrict__ out, int32_t* advance, FinThr f) {
+    if (blockIdx.x == gridDim.x - 1) {
+        if (blockIdx.y == 0) {
+            __shared__ unsigned lds[4096];
+            __shared__ unsigned tot[17];
+            __shared__ unsigned sh[3];
+            topk_threshold<kFinThrThreads>(f.s, f.n, f.k, f.hist, lds, tot, sh, f.thr, f.offs);
+        }
+        return;
+    }
+    axpy_finalize_block<T, kFinThrThreads>(partial, n_groups, B, d, bias, residual, out, advance);
+}
+
 }  // namespace dv
 
 namespace dvh {
 using namespace dv;
+
+bool topk_split_supported(int n, int k) { return k > 0 && k <= n && n % 4 == 0 && n <= kTopkRegN; }
 
 AxpyPlan axpy_plan(int d, int rows, int wdt) {
     AxpyPlan p;
@@ -302,10 +371,12 @@ size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_grou
 
 template <typename T, int NB>
 static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
+    const int hs = a.tk_s ? cdiv(a.tk_n, kTopkSlice) : 0;
+    const dim3 grid(n_slices + (hs ? 1 : 0), max(a.n_groups, hs));
     if (a.apart)
-        hipLaunchKernelGGL((k_axpy<T, NB, true>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((k_axpy<T, NB, true>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_axpy<T, NB, false>), dim3(n_slices, a.n_groups), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((k_axpy<T, NB, false>), grid, dim3(kBlock), 0, s, a);
 }
 
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
@@ -315,6 +386,15 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     a.blk = c.blk; a.coef = c.coef; a.coef_stride = c.coef_stride; a.skip_zero = c.skip_zero ? 1 : 0;
     a.apart = c.apart; a.num_splits = c.num_splits;
     a.B = c.B; a.n_groups = p.n_groups; a.partial = c.partial; a.rows_read = c.rows_read;
+    a.tk_s = nullptr; a.tk_n = a.tk_k = 0; a.tk_hist = nullptr; a.tk_thr = nullptr; a.tk_idx = nullptr;
+    if (c.sel) {
+        const TopkSel& t = *c.sel;
+        if (c.B != 1 || !topk_split_supported(t.n, t.k) || ((uintptr_t)t.s & 15u) ||
+            !t.hist || !t.thr || !t.idx || ((uintptr_t)t.hist & 15u))
+            return fail(DV_ERR_UNSUPPORTED, "selection slices beside a gather-AXPY: n=%d k=%d", t.n, t.k);
+        a.tk_s = t.s; a.tk_n = t.n; a.tk_k = t.k; a.tk_hist = t.hist; a.tk_thr = (const TopkThreshold*)t.thr;
+        a.tk_idx = t.idx;
+    }
     const int nb = c.B <= 1 ? 1 : c.B <= 2 ? 2 : c.B <= 4 ? 4 : c.B <= 8 ? 8 : 16;
 #define DV_AXPY(NB)                                                            \
     case NB:                                                                   \
@@ -326,7 +406,17 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     }
 #undef DV_AXPY
     const dim3 fg(cdiv(c.d / 4, 64), c.B);
-    if (c.wdt == DV_F16)
+    if (c.sel && c.apart) {                        // the selection threshold rides in the finalize
+        const FinThr f{c.sel->s, c.sel->n, c.sel->k, c.sel->hist, (TopkThreshold*)c.sel->thr,
+                       (unsigned*)c.sel->thr + 4};
+        const dim3 fg2(fg.x + 1, fg.y);
+        if (c.wdt == DV_F16)
+            hipLaunchKernelGGL(k_axpy_finalize_thr<half_t>, fg2, dim3(kFinThrThreads), 0, s, c.partial, p.n_groups, c.B,
+                               c.d, c.bias, c.residual, c.out, c.advance, f);
+        else
+            hipLaunchKernelGGL(k_axpy_finalize_thr<float>, fg2, dim3(kFinThrThreads), 0, s, c.partial, p.n_groups, c.B,
+                               c.d, c.bias, c.residual, c.out, c.advance, f);
+    } else if (c.wdt == DV_F16)
         hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
                            c.residual, c.out, c.advance);
     else

@@ -3,7 +3,7 @@
 //
 // Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
 // Inference Time" (arXiv 2310.17157).
-#include "rowdot.h"
+#include "pred.h"
 
 namespace dv {
 
@@ -53,98 +53,11 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restric
     }
 }
 
-// A row-dot with the block's LayerNorm folded in (batch row 0): the
-// predictor's first layer (OP = ROW_PLAIN, rows 0..n_max-1, optionally the
-// rows of two predictors, the second's from a.w2) or fc1 over the selected
-// rows (OP = ROW_FC1: bias, ReLU).  One row per wave.  Every
-// workgroup normalises x in LDS itself while its rows are still in flight
-// (the statistics of a 5120-float row cost far less than a launch);
-// workgroup 0 also writes y when ln.y_out is set.
+// The row-dot with LayerNorm folded in, one workgroup per block of 4 rows.
 template <typename T, int CH, int OP>
 __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
-    constexpr int E = Vec<T>::E;
     extern __shared__ float ys[];
-    const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
-    const int u = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int nchunk = a.d / E;
-    int j = -1;
-    if (u < n) {
-        const int jj = a.idx ? a.idx[u] : u;
-        j = (unsigned)jj < (unsigned)a.w_rows ? jj : -1;   // an index outside W selects nothing
-    }
-    j = __builtin_amdgcn_readfirstlane(j);
-    stage_dma(ys, ln.x, a.d);                        // x straight into LDS, ahead of the row
-    issue_order_fence();
-    u32x4 w[CH];
-    if (j >= 0) {
-        const T* row = (a.w2 && j >= a.split) ? (const T*)a.w2 + (size_t)(j - a.split) * a.d
-                                              : (const T*)a.w + (size_t)j * a.d;
-        load_row_all<T, CH>(row, nchunk, w);
-        sync_after_dma<CH>();                        // x has landed; the row may still be in flight
-    } else {
-        sync_after_dma<0>();
-    }
-    layernorm_lds(ys, a.d, ln, blockIdx.x == 0 && ln.y_out != nullptr);
-    if (u >= a.n_max) return;
-    float acc[1] = {0.f};
-    if (j >= 0) dot_row<T, CH, 1>(w, nchunk, ys, a.d, 1, acc);
-    float v = wave_sum(acc[0]);
-    if (OP == ROW_FC1) v = j >= 0 ? fmaxf(v + to_f32(((const T*)a.bias)[j]), 0.f) : 0.f;
-    if ((threadIdx.x & 63) == 0) a.out[u] = v;
-}
-
-// ---------------------------------------------------------------- predictor --
-// DejaVu §4.1/§4.2: SP(y) = act(y P1) P2.  Layer 1 is k_rowdot (r rows);
-// layer 2 applies act to the r hidden values and scores every output row,
-// lpr lanes per row of r elements.
-template <typename T, int NB>
-__device__ __forceinline__ void pred_scores_block(int blk, float* hid /* LDS [NB][r_pad] */,
-                                                  const float* __restrict__ hid_in, int B, int r, int act,
-                                                  const T* __restrict__ p2, int n_out, int lpr, int rows_per_block,
-                                                  float* __restrict__ scores) {
-    constexpr int E = Vec<T>::E;
-    const int r_pad = (r + 3) & ~3;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int grp = lane / lpr, t = lane % lpr;
-    const int rpw = kWave / lpr;                         // rows per wave pass
-    const int rchunk = r / E;                            // r*wb is a multiple of 16
-    const int j0 = blk * rows_per_block;
-    const int j1 = min(n_out, j0 + rows_per_block);
-    // this wave's first row, loaded before the hidden vector is staged
-    const int jfirst = j0 + wv * rpw + grp;
-    u32x4 w0 = u32x4{0u, 0u, 0u, 0u};
-    if (jfirst < j1 && t < rchunk) w0 = ld16(p2 + (size_t)jfirst * r + (size_t)t * E);
-    for (int i = threadIdx.x; i < NB * r_pad; i += kBlock) {
-        const int b = i / r_pad, k = i % r_pad;
-        float v = (b < B && k < r) ? hid_in[(size_t)b * r + k] : 0.f;
-        if (act == DV_ACT_RELU) v = fmaxf(v, 0.f);
-        hid[i] = v;
-    }
-    __syncthreads();
-    bool first = true;
-    for (int jb = j0 + wv * rpw; jb < j1; jb += 4 * rpw) {
-        const int j = jb + grp;
-        float acc[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-        if (j < j1) {
-            const T* row = p2 + (size_t)j * r;
-            for (int c = t; c < rchunk; c += lpr) {
-                float f[E];
-                unpack((first && c == t) ? w0 : ld16(row + (size_t)c * E), f, T());
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[b] = fmaf(f[e], hid[b * r_pad + c * E + e], acc[b]);
-            }
-        }
-        first = false;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const float v = group_sum_dyn(acc[b], lpr);
-            if (t == 0 && j < j1 && b < B) scores[(size_t)b * n_out + j] = v;
-        }
-    }
+    rowdot_ln_block<T, CH, OP>(blockIdx.x, ys, a, ln);
 }
 
 template <typename T, int NB>
@@ -153,61 +66,6 @@ __global__ __launch_bounds__(kBlock) void k_pred_scores(const float* __restrict_
                                                         int rows_per_block, float* __restrict__ scores) {
     extern __shared__ float hid[];
     pred_scores_block<T, NB>(blockIdx.x, hid, hid_in, B, r, act, p2, n_out, lpr, rows_per_block, scores);
-}
-
-// The predictor's second layer fused with the selection for a short score
-// row (n_out <= 256, e.g. heads; batch row 0): thread j scores row j of P2
-// (all its r-element loads in flight at once), then ranks its key against
-// the others in LDS; rank < k selects it, and a block scan writes the set
-// ascending.  Same order as k_topk: score descending, ties to the lower
-// index, NaN last.
-template <typename T>
-__device__ __forceinline__ void pred_topk_small_block(const float* __restrict__ hid_in, int r, int act,
-                                                      const T* __restrict__ p2, int n_out, float* __restrict__ scores,
-                                                      int k, int32_t* __restrict__ idx) {
-    constexpr int E = Vec<T>::E;
-    constexpr int CB = 16;                               // chunk loads in flight per batch
-    __shared__ float hid[512];
-    __shared__ uint32_t keys[kBlock];
-    __shared__ unsigned tot[17];
-    const int j = threadIdx.x;
-    const int rchunk = r / E;
-    for (int i = threadIdx.x; i < r; i += kBlock) {
-        const float v = hid_in[i];
-        hid[i] = act == DV_ACT_RELU ? fmaxf(v, 0.f) : v;
-    }
-    const T* row = p2 + (size_t)(j < n_out ? j : 0) * r;
-    float acc = 0.f;
-    for (int c0 = 0; c0 < rchunk; c0 += CB) {
-        u32x4 w[CB];
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-            w[c] = (j < n_out && c0 + c < rchunk) ? ld16(row + (size_t)(c0 + c) * E) : u32x4{0u, 0u, 0u, 0u};
-        if (c0 == 0) __syncthreads();                    // hid staged
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            if (c0 + c < rchunk) {
-                float f[E];
-                unpack(w[c], f, T());
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc = fmaf(f[e], hid[(c0 + c) * E + e], acc);
-            }
-        }
-    }
-    if (rchunk == 0) __syncthreads();
-    const uint32_t kj = j < n_out ? order_key(acc) : 0u;
-    if (j < n_out) scores[j] = acc;
-    keys[j] = kj;
-    __syncthreads();
-    unsigned rank = 0;
-    for (int i = 0; i < n_out; ++i) {
-        const uint32_t ki = keys[i];
-        rank += (ki > kj) || (ki == kj && i < j);
-    }
-    const bool sel = j < n_out && rank < (unsigned)k;
-    unsigned total;
-    const unsigned pos = block_excl_scan(sel ? 1u : 0u, tot, &total);
-    if (sel && pos < (unsigned)k) idx[pos] = j;
 }
 
 template <typename T>
@@ -222,14 +80,9 @@ __global__ __launch_bounds__(kBlock) void k_pred_topk_small(const float* __restr
 // and selects k_h of them, the others score the neurons (their selection is
 // the next launch).
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_pred2_pair(const float* __restrict__ hidA, int rA, const T* __restrict__ p2A,
-                                                       int nA, float* __restrict__ sA, int kA, int32_t* __restrict__ idxA,
-                                                       const float* __restrict__ hidM, int rM, const T* __restrict__ p2M,
-                                                       int nM, int lpr, int rows_per_block, float* __restrict__ sM,
-                                                       int act) {
+__global__ __launch_bounds__(kBlock) void k_pred2_pair(Pred2Args a) {
     extern __shared__ float hid[];
-    if (blockIdx.x == 0) pred_topk_small_block<T>(hidA, rA, act, p2A, nA, sA, kA, idxA);
-    else pred_scores_block<T, 1>(blockIdx.x - 1, hid, hidM, 1, rM, act, p2M, nM, lpr, rows_per_block, sM);
+    pred2_pair_block<T>(blockIdx.x, hid, a);
 }
 
 }  // namespace dv
@@ -371,21 +224,24 @@ dv_status launch_predict_pair_ln(const float* x, int d, const float* g, const fl
                                  : predict_ln_t<float, ROW_PLAIN>(a, ln, ch_tier(d, wdt), s);
     if (st != DV_OK) return st;
     DV_LAUNCH_CHECK();
-    const int E = 16 / elt_bytes(wdt);
-    const int rchunk = rM / E;
-    int lpr = 1;
-    while (lpr < rchunk && lpr < kWave) lpr *= 2;
-    const int rows_per_block = (kWave / lpr) * 4 * 4;
-    const int grid = 1 + cdiv(N, rows_per_block);
+    const Pred2Args p2 = pred2_args(hid, rA, pa2_t, h, sA, kA, idxA, hid + rA, rM, pm2_t, N, sM, act, wdt);
     const size_t lds = (size_t)((rM + 3) & ~3) * sizeof(float);
-    if (wdt == DV_F16)
-        hipLaunchKernelGGL(k_pred2_pair<half_t>, dim3(grid), dim3(kBlock), lds, s, hid, rA, (const half_t*)pa2_t, h, sA,
-                           kA, idxA, hid + rA, rM, (const half_t*)pm2_t, N, lpr, rows_per_block, sM, act);
-    else
-        hipLaunchKernelGGL(k_pred2_pair<float>, dim3(grid), dim3(kBlock), lds, s, hid, rA, (const float*)pa2_t, h, sA,
-                           kA, idxA, hid + rA, rM, (const float*)pm2_t, N, lpr, rows_per_block, sM, act);
+    if (wdt == DV_F16) hipLaunchKernelGGL(k_pred2_pair<half_t>, dim3(pred2_blocks(p2)), dim3(kBlock), lds, s, p2);
+    else hipLaunchKernelGGL(k_pred2_pair<float>, dim3(pred2_blocks(p2)), dim3(kBlock), lds, s, p2);
     DV_LAUNCH_CHECK();
     return DV_OK;
+}
+
+Pred2Args pred2_args(const float* hid_a, int r_a, const void* p2_a, int n_a, float* s_a, int k_a, int32_t* idx_a,
+                     const float* hid_m, int r_m, const void* p2_m, int n_m, float* s_m, int act, int wdt) {
+    Pred2Args p{};
+    p.hid_a = hid_a; p.r_a = r_a; p.p2_a = p2_a; p.n_a = n_a; p.s_a = s_a; p.k_a = k_a; p.idx_a = idx_a;
+    p.hid_m = hid_m; p.r_m = r_m; p.p2_m = p2_m; p.n_m = n_m; p.s_m = s_m; p.act = act; p.wdt = wdt;
+    const int rchunk = r_m / (16 / elt_bytes(wdt));
+    p.lpr = 1;
+    while (p.lpr < rchunk && p.lpr < kWave) p.lpr *= 2;
+    p.rows_per_block = (kWave / p.lpr) * 4 * 4;
+    return p;
 }
 
 bool row_ln_supported(int d, int wdt) { return ln_fusable(1, d) && ch_tier(d, wdt) != 0; }

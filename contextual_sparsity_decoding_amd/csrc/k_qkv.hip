@@ -34,10 +34,11 @@ bool qkv_supported(int B, int d, int wdt) {
 
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
                      const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,
-                     hipStream_t s, const float* ln_g, const float* ln_b, float eps) {
-    if (n_sel == 0) return DV_OK;
+                     hipStream_t s, const float* ln_g, const float* ln_b, float eps, const RowArgs* pred) {
+    if (n_sel == 0 && !pred) return DV_OK;
     QkvArgs a;
     a.ln_g = ln_g; a.ln_b = ln_b; a.eps = eps;
+    a.pred = pred ? *pred : RowArgs{};
     a.y = y; a.B = B; a.d = d; a.h = h; a.dh = d_h; a.n_sel = n_sel;
     a.head_idx = head_idx; a.w = w; a.bias = bias; a.q = q;
     a.K = (half_t*)kv->k_cache; a.V = (half_t*)kv->v_cache;

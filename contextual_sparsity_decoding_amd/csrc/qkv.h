@@ -5,7 +5,7 @@
 // Inference Time" (arXiv 2310.17157), §4.2.
 #pragma once
 
-#include "rowdot.h"
+#include "pred.h"
 
 #include <type_traits>
 
@@ -32,6 +32,9 @@ struct QkvArgs {
     const float* ln_g;        // LNF: y = LayerNorm(input) computed in the kernel
     const float* ln_b;
     float eps;
+    int qkv_blocks;           // the projection's workgroups
+    int pred_blocks;          // LNF: workgroups placed first that compute `pred` rows (4*R per workgroup)
+    RowArgs pred;             // the next layer's predictor layer one (look-ahead) on LN(input), or w == NULL
 };
 
 // A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
@@ -51,10 +54,19 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     constexpr int E = Vec<T>::E;
     constexpr int HV = HB > 0 ? HB : 1;
     extern __shared__ float ys[];                      // y [NB][d], then [HB][d] stored inputs
+    int qb = blockIdx.x;                               // this workgroup among the projection's
+    if constexpr (LNF) {
+        if (qb < a.pred_blocks) {                      // look-ahead: the next layer's predictor rows, same LN1(x)
+            const LnArgs ln{a.y, a.ln_g, a.ln_b, a.eps, nullptr};
+            rowdot_ln_block<T, CH, ROW_PLAIN, R>(qb, ys, a.pred, ln);
+            return;
+        }
+        qb -= a.pred_blocks;
+    }
     const int d = a.d, dh = a.dh;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int r0 = blockIdx.x * 4 * R;                 // 4*R divides dh: one head block per workgroup
+    const int r0 = qb * 4 * R;                         // 4*R divides dh: one head block per workgroup
     const int which = r0 / (a.n_sel * dh);
     const int s = (r0 / dh) % a.n_sel;
     const int e0 = r0 % dh + wv * R;                   // this wave's first row in the block
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     // this step's input joins the stored inputs: float4 c of [B][d] goes
     // with thread c of the grid (a handful of workgroups), from LDS when staged
     if (a.y_buf && pos_ok) {
-        for (int c = blockIdx.x * kBlock + threadIdx.x; c < a.B * d / 4; c += gridDim.x * kBlock) {
+        for (int c = qb * kBlock + threadIdx.x; c < a.B * d / 4; c += a.qkv_blocks * kBlock) {
             const int b = (c * 4) / d, col = (c * 4) % d;
             const f32x4 v = (YL || LNF) ? reinterpret_cast<const f32x4*>(ys)[c] : reinterpret_cast<const f32x4*>(a.y)[c];
             *reinterpret_cast<f32x4*>(a.y_buf + ((size_t)b * a.max_len + pos) * d + col) = v;
@@ -241,15 +253,19 @@ using namespace dv;
 inline int qkv_rows_per_wave(int ch) { return ch <= 10 ? 4 : ch <= 20 ? 2 : 1; }
 
 template <typename T, int NB, int CH, int R>
-static dv_status qkv_go3(const QkvArgs& a, hipStream_t s) {
+static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
+    QkvArgs a = a_in;
     const int rows = 3 * a.n_sel * a.dh;
     const size_t row = (size_t)a.d * sizeof(float);
     const bool holes = a.y_buf && a.valid_upto;
     if (a.dh % (4 * R)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
-    const int grid = rows / (4 * R);
+    a.qkv_blocks = rows / (4 * R);
+    a.pred_blocks = a.pred.w ? cdiv(a.pred.n_max, 4 * R) : 0;
+    const int grid = a.pred_blocks + a.qkv_blocks;
     const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
     const bool lnf = a.ln_g != nullptr;
     if (lnf && (NB != 1 || !yl)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V with LayerNorm: B=%d d=%d", a.B, a.d);
+    if (a.pred.w && (!lnf || a.pred.d != a.d)) return fail(DV_ERR_UNSUPPORTED, "predictor rows need the LayerNorm-folded Q/K/V");
 #define DV_QKV(HB, LDS)                                                                                          \
     do {                                                                                                         \
         if constexpr (NB == 1) {                                                                                 \

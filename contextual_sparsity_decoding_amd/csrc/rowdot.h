@@ -38,19 +38,26 @@ __device__ __forceinline__ float block_sum1024(float v, float* red) {
     return s;
 }
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+// Sum over a workgroup of NW waves (red: NW floats of LDS).
+template <int NW>
+__device__ __forceinline__ float block_sum_waves(float v, float* red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
     lds_barrier();
     if ((threadIdx.x & 63) == 0) red[w] = v;
     lds_barrier();
-    return red[0] + red[1] + red[2] + red[3];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) s += red[i];
+    return s;
 }
+
+__device__ __forceinline__ float block_sum256(float v, float* red) { return block_sum_waves<4>(v, red); }
 
 // LayerNorm of one row held in LDS, in place: population variance, then
 // gamma and beta (DejaVu App. B: a norm precedes each block).  Every thread
-// of the workgroup takes part; ends with a barrier.  With `write`, the
-// normalised row is also stored to ln.y_out.
+// of the NT-thread workgroup takes part; ends with a barrier.  With `write`,
+// the normalised row is also stored to ln.y_out.
 struct LnArgs {
     const float* x;
     const float* g;
@@ -59,22 +66,23 @@ struct LnArgs {
     float* y_out;
 };
 
+template <int NT = kBlock>
 __device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
-    __shared__ float red[4];
+    __shared__ float red[NT / kWave];
     float s = 0.f;
-    for (int i = threadIdx.x; i < d; i += kBlock) s += ys[i];
-    const float mean = block_sum256(s, red) / (float)d;
+    for (int i = threadIdx.x; i < d; i += NT) s += ys[i];
+    const float mean = block_sum_waves<NT / kWave>(s, red) / (float)d;
     float q = 0.f;
-    for (int i = threadIdx.x; i < d; i += kBlock) {
+    for (int i = threadIdx.x; i < d; i += NT) {
         const float t = ys[i] - mean;
         q = fmaf(t, t, q);
     }
-    const float rstd = 1.0f / sqrtf(block_sum256(q, red) / (float)d + ln.eps);
+    const float rstd = 1.0f / sqrtf(block_sum_waves<NT / kWave>(q, red) / (float)d + ln.eps);
     const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
     const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
     f32x4* y4 = reinterpret_cast<f32x4*>(ys);
 #pragma unroll 8
-    for (int c = threadIdx.x; c < d / 4; c += kBlock) {
+    for (int c = threadIdx.x; c < d / 4; c += NT) {
         const f32x4 gg = g4[c], bb = b4[c];
         f32x4 v = y4[c];
 #pragma unroll
@@ -137,11 +145,12 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ lds, const float*
 // between.  The data is there once the issuing wave's vmcnt has drained;
 // callers wait for vmcnt(0) and then synchronise the workgroup.
 typedef __attribute__((address_space(3))) void lds_void_t;
+template <int NT = kBlock>
 __device__ __forceinline__ void stage_dma(float* lds, const float* __restrict__ src, int n) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nkb = (n + 255) / 256;
-    for (int c = wv; c < nkb; c += kBlock / kWave) {
+    for (int c = wv; c < nkb; c += NT / kWave) {
         const int i = c * 256 + lane * 4;
         if (i < n) __builtin_amdgcn_global_load_lds(src + i, (lds_void_t*)(lds + c * 256), 16, 0, 0);
     }

@@ -1,7 +1,8 @@
 """Parity of dv_decode_layer with DV_LOOKAHEAD (DejaVu §4.3, the parallel
 form) against the oracle's decode_layer_lookahead (GPU): the layer runs with
-given sets while the next layer's predictors read its normalised input on a
-second stream; also inside a captured two-branch HIP graph."""
+given sets while the next layer's predictors read its normalised input,
+either on a second stream or as extra workgroups of the layer's own
+launches; also inside captured HIP graphs."""
 import math
 
 import numpy as np
@@ -116,20 +117,36 @@ def test_lookahead_steps_match_oracle(dvlib, aux):
     assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
 
 
-def test_lookahead_opt13b_layer_full_size(dvlib):
+@pytest.mark.parametrize("N,k_m", [(24576, 2400), (1000, 100), (4100, 4100)])
+def test_lookahead_selection_shapes(dvlib, N, k_m):
+    """The neuron selection of the single-stream schedule at budgets its
+    split form does not take (more than 20480 scores; a count that is not a
+    multiple of 4) and at k = n (every neuron kept): the same sets as the
+    oracle either way."""
+    dims = LayerDims(d=512, N=N, h=8, d_h=64, r_attn=16, r_mlp=32, wdt="f16")
+    n0, T = 12, 2
+    A = Ahead(dvlib, dims, n0, n0 + T + 2, seed=47, k_heads=3, k_neurons=k_m)
+    X = synth.layer_inputs(dims.d, T, 1, seed=47)
+    assert _run_steps(dvlib, A, n0, X, None) == T
+
+
+@pytest.mark.parametrize("aux", [True, False])
+def test_lookahead_opt13b_layer_full_size(dvlib, aux):
     """The OPT-13B-shaped layer in the parallel form: 20 given heads, 2048
     given neurons, the next layer's 20 heads and 2048 neurons predicted
-    alongside, on a second stream."""
+    alongside (on a second stream, or inside the layer's launches)."""
     w = configs.OPT13B_LAYER
     A = Ahead(dvlib, w.dims, w.n_ctx, w.n_ctx + 4, seed=43, k_heads=w.k_heads, k_neurons=w.k_neurons)
     X = synth.layer_inputs(w.dims.d, 2, 1, seed=43)
-    assert _run_steps(dvlib, A, w.n_ctx, X, _sync_objects()) == 2
+    assert _run_steps(dvlib, A, w.n_ctx, X, _sync_objects() if aux else None) == 2
 
 
-def test_lookahead_graph_two_branches(dvlib):
+@pytest.mark.parametrize("aux", [True, False])
+def test_lookahead_graph(dvlib, aux):
     """T steps captured in one HIP graph, the predictions on a second stream
-    (a fork and a join per step), the position on the device: replayed with
-    eager work in between, every replay equals the eager steps."""
+    (a fork and a join per step) or inside the layer's launches, the position
+    on the device: replayed with eager work in between, every replay equals
+    the eager steps."""
     dims = LayerDims(d=512, N=2048, h=8, d_h=64, r_attn=16, r_mlp=32, wdt="f16")
     n0, T, L = 20, 5, 40
     k_h, k_m = 3, 200
@@ -152,7 +169,7 @@ def test_lookahead_graph_two_branches(dvlib):
         dvlib.dv_decode_layer(eager.wts, cfg, st, dev(X[t]), out, ws_e)
         want.append(host(out))
     # graph: one step captured, ping-pong buffers swapped between two captured steps
-    sync = _sync_objects()
+    sync = _sync_objects() if aux else None
     pos_dev = torch.full((1,), n0, dtype=torch.int32, device="cuda")
     cfg_g = graph.cfg(flags | dvlib.DV_ADVANCE_POS)
     ws_g = dvlib.workspace(dvlib.dv_decode_workspace_bytes(cfg_g, L))
