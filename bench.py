@@ -372,7 +372,8 @@ def cpu_baseline(cp, dims, w, X, budget_s):
     L = cp.host_K.shape[2]
     kv = ref.KVState(cp.host_K.copy(), cp.host_V.copy(), np.zeros((1, L, dims.d)), np.full((1, dims.h), w.n_ctx - 1))
     steps, t0 = 0, time.perf_counter()
-    while steps == 0 or (time.perf_counter() - t0 < budget_s and steps < 16):
+    cap = min(len(Xh), L - w.n_ctx)
+    while steps == 0 or (time.perf_counter() - t0 < budget_s and steps < cap):
         ref.decode_layer(Xh[steps], cp.W, kv, w.n_ctx + steps, k_heads=w.k_heads, k_neurons=w.k_neurons,
                          scale=1 / math.sqrt(dims.d_h), skip_nonpos=True, hole_fill=True)
         steps += 1

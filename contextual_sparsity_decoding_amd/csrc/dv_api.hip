@@ -410,9 +410,10 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
 }
 
 // DejaVu §4.3, the parallel form (batch of one): the next layer's sets are
-// predicted from this layer's y = LN1(x) on the auxiliary stream while this
-// layer runs on the main one with its given sets.  LN1 is folded into the
-// Q/K/V kernel and LN2 into fc1, so the main stream runs seven kernels.
+// predicted from this layer's y = LN1(x) while this layer runs with its
+// given sets, either on the auxiliary stream or riding as extra workgroups
+// in this layer's launches.  LN1 is folded into the Q/K/V kernel and LN2 into
+// fc1, so the layer itself runs seven kernels.
 static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
                                   const dv_kv_view& view, const LayerWs& L, const float* x_in, float* x_out, void* ws,
                                   hipStream_t s) {

@@ -22,7 +22,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kBlock = 256;          // 4 waves per workgroup
 constexpr size_t kYLdsMax = 64 * 1024;
-constexpr size_t kQkvLdsMax = 64 * 1024;     // Q/K/V inputs staged in LDS (the default dynamic limit)
+constexpr size_t kQkvLdsMax = 64 * 1024;     // Q/K/V inputs staged in LDS (two workgroups per CU, with room)
 constexpr int kTopkMaxN = 1 << 22;          // longest row dv_topk_select takes
 constexpr int kUnionMaxN = 1 << 18;         // union bitmap in LDS: n / 8 bytes
 constexpr int kTopkStage = 8192;            // selected sets up to this size leave through LDS

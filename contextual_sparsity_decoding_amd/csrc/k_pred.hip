@@ -54,10 +54,10 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restric
 }
 
 // The row-dot with LayerNorm folded in, one workgroup per block of 4 rows.
-template <typename T, int CH, int OP>
+template <typename T, int CH, int OP, int RR>
 __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
     extern __shared__ float ys[];
-    rowdot_ln_block<T, CH, OP>(blockIdx.x, ys, a, ln);
+    rowdot_ln_block<T, CH, OP, RR>(blockIdx.x, ys, a, ln);
 }
 
 template <typename T, int NB>
@@ -150,16 +150,13 @@ template <typename T, int OP>
 static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStream_t s) {
     const int grid = cdiv(a.n_max, 4);
     const size_t lds = (size_t)a.d * sizeof(float);
+#define DV_RL(CH) \
+    case CH: hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
     switch (ch) {
-        case 4: hipLaunchKernelGGL((k_rowdot_ln<T, 4, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 8: hipLaunchKernelGGL((k_rowdot_ln<T, 8, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 10: hipLaunchKernelGGL((k_rowdot_ln<T, 10, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 12: hipLaunchKernelGGL((k_rowdot_ln<T, 12, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 16: hipLaunchKernelGGL((k_rowdot_ln<T, 16, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 18: hipLaunchKernelGGL((k_rowdot_ln<T, 18, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
-        case 24: hipLaunchKernelGGL((k_rowdot_ln<T, 24, OP>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+        DV_RL(4) DV_RL(8) DV_RL(10) DV_RL(12) DV_RL(16) DV_RL(18) DV_RL(24)
         default: return fail(DV_ERR_UNSUPPORTED, "fused LayerNorm: d=%d", a.d);
     }
+#undef DV_RL
     return DV_OK;
 }
 

@@ -189,26 +189,31 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     if (which == 0 || !fill) return;                   // uniform over the workgroup
     fence_w();
 
-    // ---- missing positions of batch row 0, HB stored inputs per round
+    // ---- missing positions of batch row 0: the first HB were staged up
+    // front beside y; later rounds take HB2 at a time, y's slots included
     half_t* cache = which == 1 ? a.K : a.V;
     if constexpr (HB > 0) {
-        for (int p0 = lo0; p0 < pos; p0 += HB) {
-            const int cnt = min(HB, pos - p0);
-            if (p0 != lo0) {                           // the first round was staged up front
-                __syncthreads();                       // the previous round's inputs are consumed
-                stage_dma(hin, a.y_buf + (size_t)p0 * d, cnt * d);
-                wait_dma_and_sync();
-            }
-            float hacc[R][HV];
-            dots(hin, std::integral_constant<int, HV>(), hacc);
+        constexpr int HB2 = HB + (YL ? NB : 0);
+        auto round = [&](const float* in, int p0, int cnt, auto nv_tag) {
+            constexpr int NV = decltype(nv_tag)::value;
+            float hacc[R][NV];
+            dots(in, nv_tag, hacc);
 #pragma unroll
             for (int j = 0; j < R; ++j)
 #pragma unroll
-                for (int v = 0; v < HV; ++v) {
+                for (int v = 0; v < NV; ++v) {
                     const float hv = wave_sum(hacc[j][v]) + bv[j];
                     if (lane == 0 && v < cnt) cache[((size_t)head * a.max_len + p0 + v) * dh + e0 + j] = (half_t)hv;
                 }
             fence_w();
+        };
+        if (pos > lo0) round(hin, lo0, min(HB, pos - lo0), std::integral_constant<int, HV>());
+        for (int p0 = lo0 + HB; p0 < pos; p0 += HB2) {
+            const int cnt = min(HB2, pos - p0);
+            __syncthreads();                           // the previous round's inputs (and y) are consumed
+            stage_dma(ys, a.y_buf + (size_t)p0 * d, cnt * d);
+            wait_dma_and_sync();
+            round(ys, p0, cnt, std::integral_constant<int, HB2>());
         }
     } else {
         for (int p = lo0; p < pos; ++p) {              // inputs too long for LDS: read from global memory

@@ -305,8 +305,15 @@ typedef struct {
      * on `stream`, makes aux_stream wait for it, records ev_join on
      * aux_stream after the predictions and makes `stream` wait for ev_join
      * before returning (a captured graph gets two branches).  Without
-     * aux_stream they run first on `stream`.  The events and the stream are
-     * the caller's (created once, reused by every call). */
+     * aux_stream they run on `stream` as extra workgroups of this layer's
+     * own launches (both predictors' first layers beside Q/K/V, the second
+     * layers and head selection beside attention, the neuron selection
+     * split over the output projection, its finalize and fc2; when both
+     * predictors are given and the neuron count is a multiple of 4 and at
+     * most 20480, else in launches of their own).  The results are the
+     * same either way.  The events and the stream are the caller's (created
+     * once, reused by every call).  The workspace of a look-ahead call must
+     * not be shared with a call running concurrently. */
     const int32_t* head_idx_in;     /* [k_heads] ascending; ignored with DV_DENSE_ATTN */
     const int32_t* neuron_idx_in;   /* [k_neurons] ascending; ignored with DV_DENSE_MLP */
     const void *next_pa1_t, *next_pa2_t;   /* next layer's head predictor, or NULL for none */
