@@ -67,7 +67,7 @@ struct AxpyArgs {
 template <int NB>
 __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, float* s_cf,
                                           float (*s_q)[kRowsPerGroup][NB][3]) {
-    constexpr int CB = 8;                          // splits in flight
+    constexpr int CB = 20;                         // splits in flight: up to 80 splits in one round of loads
     const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
     const int dh = a.blk, ns = a.num_splits;
     const int n_sel = a.rows / dh;

@@ -84,18 +84,25 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     if (HB > 0 && fill && pos > lo0) stage_dma(hin, a.y_buf + (size_t)lo0 * d, min(HB, pos - lo0) * d);
     const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh + e0) * d;
     issue_order_fence();
-    // chunk-major, the order the dot products consume them in; a live
-    // workgroup issues all R * CH loads (chunks past the row re-read chunk 0
-    // and are never used: the dot products stop at the row's end)
+    // Chunk-major, the order the dot products consume them in.  Only the
+    // first PF chunks are issued here; the on-time dot products issue chunk
+    // i + PF after consuming chunk i.  A wave cannot issue loads faster than
+    // HBM drains them, so issuing all of them first would leave every dot
+    // product for after the last byte arrives.  A live workgroup issues all
+    // R * CH loads (chunks past the row re-read chunk 0 and are never used:
+    // the dot products stop at the row's end).
+    constexpr int PF = (8 / R) < CH ? 8 / R : CH;      // about 8 KB of rows in flight per wave
     u32x4 w[R][CH];
+    auto load_chunk = [&](int i) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int c = lane + i * kWave;
+            w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
+        }
+    };
     if (live) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int c = lane + i * kWave;
-                w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
-            }
+        for (int i = 0; i < PF; ++i) load_chunk(i);
     } else {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
@@ -105,13 +112,11 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     float bv[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e0 + j]) : 0.f;
+    if (live) sync_after_dma<R * PF>();              // the inputs have landed; the rows may still be in flight
+    else sync_after_dma<0>();
     if constexpr (LNF) {
-        if (live) sync_after_dma<R * CH>();          // the inputs have landed; the rows may still be in flight
-        else sync_after_dma<0>();
         const LnArgs ln{a.y, a.ln_g, a.ln_b, a.eps, nullptr};
         layernorm_lds(ys, d, ln, false);
-    } else {
-        wait_dma_and_sync();
     }
     // this step's input joins the stored inputs: float4 c of [B][d] goes
     // with thread c of the grid (a handful of workgroups), from LDS when staged
@@ -165,11 +170,43 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             for (int i = 0; i < CH; ++i) asm volatile("" : "+v"(w[j][i]));
     };
 
-    // ---- on-time q, k, v
+    // ---- on-time q, k, v (same instructions per input as `dots`, so the
+    // recomputed entries below stay bit-identical)
     {
         float acc[R][NB];
-        if (YL) dots(ys, std::integral_constant<int, NB>(), acc);
-        else dots(a.y, std::integral_constant<int, NB>(), acc);
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+        const float* yin = YL ? ys : a.y;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float yv[E];
+                    const f32x4* y4 = reinterpret_cast<const f32x4*>(yin + (size_t)b * d + (size_t)c * E);
+#pragma unroll
+                    for (int q = 0; q < E / 4; ++q) {
+                        const f32x4 t = y4[q];
+                        yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
+                    }
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+                        float f[E];
+                        unpack(w[j][i], f, T());
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[j][b] = fmaf(f[e], yv[e], acc[j][b]);
+                    }
+                }
+            }
+            if (i + PF < CH) {
+                issue_order_fence();                     // the next loads go out after this chunk's work
+                if (live) load_chunk(i + PF);
+                issue_order_fence();
+            }
+        }
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
