@@ -205,18 +205,29 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     }
     __syncthreads();
 
-    // ---- all of this wave's row loads in flight: rows wv, wv + 4, ...
-    u32x4 w[kAxpyU];
-#pragma unroll
-    for (int t = 0; t < kAxpyU; ++t) {
-        const int k = wv + 4 * t;
-        const int rr = k < nlive ? s_row[k] : -1;
-        w[t] = (rr >= 0 && colok) ? ld16_stream(W + (size_t)rr * a.d + col) : u32x4{0u, 0u, 0u, 0u};
-    }
+    // ---- the coefficients of the output projection first: the split-K
+    // partials are L2-resident, and their loads would otherwise queue
+    // behind the row stream
     if (ATTN) {
         attn_coef<NQ>(a, r0, nlive, s_cf, s_q);
         __syncthreads();
     }
+
+    // ---- this wave's rows wv, wv + 4, ...: for the output projection the
+    // first PF now, each later one issued after the FMAs of the row PF
+    // before it (a wave's loads go out only as fast as HBM drains them;
+    // issuing them all first would leave the FMAs as a tail).  fc2, with
+    // its coefficients already in LDS, measured faster with every row
+    // issued first.
+    constexpr int kAxpyPF = ATTN ? 8 : kAxpyU;
+    u32x4 w[kAxpyU];
+    auto load_row = [&](int t) {
+        const int k = wv + 4 * t;
+        const int rr = k < nlive ? s_row[k] : -1;
+        w[t] = (rr >= 0 && colok) ? ld16_stream(W + (size_t)rr * a.d + col) : u32x4{0u, 0u, 0u, 0u};
+    };
+#pragma unroll
+    for (int t = 0; t < kAxpyPF; ++t) load_row(t);
 
     float acc[NB][E];
 #pragma unroll
@@ -235,6 +246,11 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[b][e] = fmaf(c, f[e], acc[b][e]);
             }
+        }
+        if (t + kAxpyPF < kAxpyU) {
+            asm volatile("" ::: "memory");
+            load_row(t + kAxpyPF);
+            asm volatile("" ::: "memory");
         }
     }
 

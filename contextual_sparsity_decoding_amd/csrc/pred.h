@@ -39,27 +39,67 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
     }
     stage_dma<NT>(ys, ln.x, a.d);                    // x straight into LDS, ahead of the rows
     issue_order_fence();
+    // With several rows per wave, the first PF chunks of every row now and
+    // the rest one chunk ahead of the dot products (a wave's loads go out
+    // only as fast as HBM drains them; issuing them all first would leave
+    // the arithmetic as a tail).  With one row per wave (10 KB at d = 5120)
+    // every load goes out first: deferring any of them past the LayerNorm
+    // measured slower.
+    constexpr int PF = RR >= 2 && (8 / RR) < CH ? 8 / RR : CH;
+    const int lane = threadIdx.x & 63;
+    const T* rowp[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+        const int jl = j[r] >= 0 ? j[r] : (jany >= 0 ? jany : 0);
+        rowp[r] = (a.w2 && jl >= a.split) ? (const T*)a.w2 + (size_t)(jl - a.split) * a.d : (const T*)a.w + (size_t)jl * a.d;
+    }
     u32x4 w[RR][CH];
+    auto load_chunk = [&](int i) {
+        const int c = lane + i * kWave;
+#pragma unroll
+        for (int r = 0; r < RR; ++r) w[r][i] = ld16_stream(rowp[r] + (size_t)(c < nchunk ? c : 0) * E);
+    };
     if (jany >= 0) {
 #pragma unroll
-        for (int r = 0; r < RR; ++r) {
-            const int jl = j[r] >= 0 ? j[r] : jany;
-            const T* row = (a.w2 && jl >= a.split) ? (const T*)a.w2 + (size_t)(jl - a.split) * a.d
-                                                   : (const T*)a.w + (size_t)jl * a.d;
-            load_row_all<T, CH>(row, nchunk, w[r]);
-        }
-        sync_after_dma<RR * CH>();                   // x has landed; the rows may still be in flight
+        for (int i = 0; i < PF; ++i) load_chunk(i);
+        sync_after_dma<RR * PF>();                   // x has landed; the rows may still be in flight
     } else {
         sync_after_dma<0>();
     }
     layernorm_lds<NT>(ys, a.d, ln, blk == 0 && ln.y_out != nullptr);
+    float acc[RR];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk) {
+            float yv[E];
+            const f32x4* y4 = reinterpret_cast<const f32x4*>(ys + (size_t)c * E);
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+                const f32x4 t = y4[q];
+                yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
+            }
+#pragma unroll
+            for (int r = 0; r < RR; ++r) {
+                float f[E];
+                unpack(w[r][i], f, T());
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], yv[e], acc[r]);
+            }
+        }
+        if (i + PF < CH) {
+            issue_order_fence();
+            if (jany >= 0) load_chunk(i + PF);
+            issue_order_fence();
+        }
+    }
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
         const int u = u0 + r;
         if (u >= a.n_max) break;
-        float acc[1] = {0.f};
-        if (j[r] >= 0) dot_row<T, CH, 1>(w[r], nchunk, ys, a.d, 1, acc);
-        float v = wave_sum(acc[0]);
+        float v = wave_sum(j[r] >= 0 ? acc[r] : 0.f);
         if (OP == ROW_FC1) v = j[r] >= 0 ? fmaxf(v + to_f32(((const T*)a.bias)[j[r]]), 0.f) : 0.f;
         if ((threadIdx.x & 63) == 0) a.out[u] = v;
     }
