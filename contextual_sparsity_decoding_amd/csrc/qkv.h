@@ -171,7 +171,15 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     };
 
     // ---- on-time q, k, v (same instructions per input as `dots`, so the
-    // recomputed entries below stay bit-identical)
+    // recomputed entries below stay bit-identical).  The first round of
+    // missing positions rides along: its stored inputs were staged with y,
+    // and the VALU would otherwise wait on the rows.
+    const bool hole1 = HB > 0 && fill && pos > lo0;    // uniform over the workgroup
+    float hacc1[R][HV];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int v = 0; v < HV; ++v) hacc1[j][v] = 0.f;
     {
         float acc[R][NB];
 #pragma unroll
@@ -198,6 +206,27 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
                         unpack(w[j][i], f, T());
 #pragma unroll
                         for (int e = 0; e < E; ++e) acc[j][b] = fmaf(f[e], yv[e], acc[j][b]);
+                    }
+                }
+                if constexpr (HB > 0) {
+                    if (hole1) {
+#pragma unroll
+                        for (int v = 0; v < HV; ++v) {
+                            float yv[E];
+                            const f32x4* y4 = reinterpret_cast<const f32x4*>(hin + (size_t)v * d + (size_t)c * E);
+#pragma unroll
+                            for (int q = 0; q < E / 4; ++q) {
+                                const f32x4 t = y4[q];
+                                yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
+                            }
+#pragma unroll
+                            for (int j = 0; j < R; ++j) {
+                                float f[E];
+                                unpack(w[j][i], f, T());
+#pragma unroll
+                                for (int e = 0; e < E; ++e) hacc1[j][v] = fmaf(f[e], yv[e], hacc1[j][v]);
+                            }
+                        }
                     }
                 }
             }
@@ -244,7 +273,16 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
                 }
             fence_w();
         };
-        if (pos > lo0) round(hin, lo0, min(HB, pos - lo0), std::integral_constant<int, HV>());
+        {   // the first round, computed beside the on-time dot products
+            const int cnt = min(HB, pos - lo0);
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int v = 0; v < HV; ++v) {
+                    const float hv = wave_sum(hacc1[j][v]) + bv[j];
+                    if (lane == 0 && v < cnt) cache[((size_t)head * a.max_len + lo0 + v) * dh + e0 + j] = (half_t)hv;
+                }
+        }
         for (int p0 = lo0 + HB; p0 < pos; p0 += HB2) {
             const int cnt = min(HB2, pos - p0);
             __syncthreads();                           // the previous round's inputs (and y) are consumed
