@@ -122,10 +122,16 @@ __device__ __forceinline__ void pred_scores_block(int blk, float* hid /* LDS [NB
     const int rchunk = r / E;                            // r*wb is a multiple of 16
     const int j0 = blk * rows_per_block;
     const int j1 = min(n_out, j0 + rows_per_block);
-    // this wave's first row, loaded before the hidden vector is staged
-    const int jfirst = j0 + wv * rpw + grp;
-    u32x4 w0 = u32x4{0u, 0u, 0u, 0u};
-    if (jfirst < j1 && t < rchunk) w0 = ld16(p2 + (size_t)jfirst * r + (size_t)t * E);
+    // the first chunk of this wave's rows in its first MAXP passes, all
+    // loaded before the hidden vector is staged (one round trip, not one per
+    // pass)
+    constexpr int MAXP = 4;
+    u32x4 pre[MAXP];
+#pragma unroll
+    for (int pi = 0; pi < MAXP; ++pi) {
+        const int jp = j0 + wv * rpw + pi * 4 * rpw + grp;
+        pre[pi] = (jp < j1 && t < rchunk) ? ld16(p2 + (size_t)jp * r + (size_t)t * E) : u32x4{0u, 0u, 0u, 0u};
+    }
     for (int i = threadIdx.x; i < NB * r_pad; i += kBlock) {
         const int b = i / r_pad, k = i % r_pad;
         float v = (b < B && k < r) ? hid_in[(size_t)b * r + k] : 0.f;
@@ -133,24 +139,27 @@ __device__ __forceinline__ void pred_scores_block(int blk, float* hid /* LDS [NB
         hid[i] = v;
     }
     __syncthreads();
-    bool first = true;
-    for (int jb = j0 + wv * rpw; jb < j1; jb += 4 * rpw) {
+    int pi = 0;
+    for (int jb = j0 + wv * rpw; jb < j1; jb += 4 * rpw, ++pi) {
         const int j = jb + grp;
         float acc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+        u32x4 w0 = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+            if (q == pi) w0 = pre[q];
         if (j < j1) {
             const T* row = p2 + (size_t)j * r;
             for (int c = t; c < rchunk; c += lpr) {
                 float f[E];
-                unpack((first && c == t) ? w0 : ld16(row + (size_t)c * E), f, T());
+                unpack((pi < MAXP && c == t) ? w0 : ld16(row + (size_t)c * E), f, T());
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[b] = fmaf(f[e], hid[b * r_pad + c * E + e], acc[b]);
             }
         }
-        first = false;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const float v = group_sum_dyn(acc[b], lpr);
