@@ -54,10 +54,10 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float* __restric
 }
 
 // The row-dot with LayerNorm folded in, one workgroup per block of 4 rows.
-template <typename T, int CH, int OP, int RR>
+template <typename T, int CH, int OP, int RR, bool GB>
 __global__ __launch_bounds__(kBlock) void k_rowdot_ln(RowArgs a, LnArgs ln) {
     extern __shared__ float ys[];
-    rowdot_ln_block<T, CH, OP, RR>(blockIdx.x, ys, a, ln);
+    rowdot_ln_block<T, CH, OP, RR, kBlock, GB>(blockIdx.x, ys, a, ln);
 }
 
 template <typename T, int NB>
@@ -149,9 +149,14 @@ bool ln_fusable(int B, int d) { return B == 1 && (size_t)d * sizeof(float) <= kY
 template <typename T, int OP>
 static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStream_t s) {
     const int grid = cdiv(a.n_max, 4);
-    const size_t lds = (size_t)a.d * sizeof(float);
-#define DV_RL(CH) \
-    case CH: hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1>), dim3(grid), dim3(kBlock), lds, s, a, ln); break;
+    // gamma and beta staged in LDS beside x when the three fit
+    const bool gb = 3 * (size_t)a.d * sizeof(float) <= kYLdsMax;
+    const size_t lds = (gb ? 3 : 1) * (size_t)a.d * sizeof(float);
+#define DV_RL(CH)                                                                                              \
+    case CH:                                                                                                   \
+        if (gb) hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1, true>), dim3(grid), dim3(kBlock), lds, s, a, ln); \
+        else hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1, false>), dim3(grid), dim3(kBlock), lds, s, a, ln); \
+        break;
     switch (ch) {
         DV_RL(4) DV_RL(8) DV_RL(10) DV_RL(12) DV_RL(16) DV_RL(18) DV_RL(24)
         default: return fail(DV_ERR_UNSUPPORTED, "fused LayerNorm: d=%d", a.d);

@@ -18,7 +18,7 @@ namespace dv {
 // Every workgroup normalises x in LDS itself while its rows are still in
 // flight (the statistics of a 5120-float row cost far less than a launch);
 // workgroup 0 also writes y when ln.y_out is set.
-template <typename T, int CH, int OP, int RR = 1, int NT = kBlock>
+template <typename T, int CH, int OP, int RR = 1, int NT = kBlock, bool GB = false>
 __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArgs& a, const LnArgs& ln) {
     constexpr int E = Vec<T>::E;
     const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
@@ -38,6 +38,12 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         if (j[r] >= 0) jany = j[r];
     }
     stage_dma<NT>(ys, ln.x, a.d);                    // x straight into LDS, ahead of the rows
+    if constexpr (GB) {
+        // gamma and beta too: loads retire in issue order, so fetching them
+        // after the rows would hold the LayerNorm until the rows arrive
+        stage_dma<NT>(ys + a.d, ln.g, a.d);
+        stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
+    }
     issue_order_fence();
     // With several rows per wave, the first PF chunks of every row now and
     // the rest one chunk ahead of the dot products (a wave's loads go out
@@ -66,7 +72,7 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
     } else {
         sync_after_dma<0>();
     }
-    layernorm_lds<NT>(ys, a.d, ln, blk == 0 && ln.y_out != nullptr);
+    layernorm_lds<NT, GB>(ys, a.d, ln, blk == 0 && ln.y_out != nullptr);
     float acc[RR];
 #pragma unroll
     for (int r = 0; r < RR; ++r) acc[r] = 0.f;

@@ -66,20 +66,26 @@ struct LnArgs {
     float* y_out;
 };
 
-template <int NT = kBlock>
+template <int NT = kBlock, bool GB = false>
 __device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
     __shared__ float red[NT / kWave];
-    float s = 0.f;
-    for (int i = threadIdx.x; i < d; i += NT) s += ys[i];
-    const float mean = block_sum_waves<NT / kWave>(s, red) / (float)d;
-    float q = 0.f;
-    for (int i = threadIdx.x; i < d; i += NT) {
-        const float t = ys[i] - mean;
-        q = fmaf(t, t, q);
+    // float4 LDS reads, four independent partial sums per thread
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(ys);
+    f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = threadIdx.x; c < d / 4; c += NT) s4 += x4[c];
+    const float mean = block_sum_waves<NT / kWave>((s4[0] + s4[1]) + (s4[2] + s4[3]), red) / (float)d;
+    f32x4 q4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = threadIdx.x; c < d / 4; c += NT) {
+        const f32x4 t = x4[c] - mean;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q4[e] = fmaf(t[e], t[e], q4[e]);
     }
-    const float rstd = 1.0f / sqrtf(block_sum_waves<NT / kWave>(q, red) / (float)d + ln.eps);
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
-    const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
+    const float rstd = 1.0f / sqrtf(block_sum_waves<NT / kWave>((q4[0] + q4[1]) + (q4[2] + q4[3]), red) / (float)d + ln.eps);
+    // gamma and beta: staged in LDS after the row (GB), else from memory
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(GB ? ys + d : ln.g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(GB ? ys + 2 * d : ln.b);
     f32x4* y4 = reinterpret_cast<f32x4*>(ys);
 #pragma unroll 8
     for (int c = threadIdx.x; c < d / 4; c += NT) {
