@@ -357,10 +357,8 @@ __global__ __launch_bounds__(kFinThrThreads) void k_axpy_finalize_thr(const floa
                                                               float* __restrict__ out, int32_t* advance, FinThr f) {
     if (blockIdx.x == gridDim.x - 1) {
         if (blockIdx.y == 0) {
-            __shared__ unsigned lds[4096];
-            __shared__ unsigned tot[17];
-            __shared__ unsigned sh[3];
-            topk_threshold<kFinThrThreads>(f.s, f.n, f.k, f.hist, lds, tot, sh, f.thr, f.offs);
+            __shared__ unsigned lds[kTopkThrWords];
+            topk_threshold<kFinThrThreads>(f.s, f.n, f.k, f.hist, lds, f.thr, f.offs);
         }
         return;
     }

@@ -49,32 +49,38 @@ __device__ __forceinline__ void topk_hist_slice(const float* __restrict__ s, int
     }
 }
 
-// The digit whose bin holds the krem-th largest candidate; thread t holds
-// the counts of bins nb-1-(P*t+i), i < P (scanning from the top).
-template <int P>
-__device__ __forceinline__ unsigned topk_pick(const unsigned (&c)[P], int nb, unsigned krem, unsigned* tot,
-                                              unsigned* sh, unsigned* above, unsigned* inbin) {
+// The digit whose bin holds the krem-th largest candidate (0 < krem <= the
+// candidates counted); thread t holds the counts of bins nb-1-(P*t+i),
+// i < P (scanning from the top).  Two barriers.  buf holds 19 words that
+// the previous call's readers may still hold: calls alternate two buffers.
+template <int P, int NT>
+__device__ __forceinline__ unsigned topk_pick(const unsigned (&c)[P], int nb, unsigned krem, unsigned* buf,
+                                              unsigned* above, unsigned* inbin) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     unsigned local = 0u;
 #pragma unroll
     for (int i = 0; i < P; ++i) local += c[i];
-    unsigned total;
-    unsigned run = block_excl_scan(local, tot, &total);
+    const unsigned incl = wave_incl_scan(local);
+    if (lane == 63) buf[w] = incl;
+    __syncthreads();
+    const unsigned ts = wave_incl_scan(lane < NW ? buf[lane] : 0u);
+    unsigned run = (w > 0 ? (unsigned)__builtin_amdgcn_readlane((int)ts, w - 1) : 0u) + incl - local;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         const int p = P * (int)threadIdx.x + i;
         if (p < nb && run < krem && run + c[i] >= krem) {
-            sh[0] = (unsigned)(nb - 1 - p);
-            sh[1] = run;
-            sh[2] = c[i];
+            buf[16] = (unsigned)(nb - 1 - p);
+            buf[17] = run;
+            buf[18] = c[i];
         }
         run += c[i];
     }
     __syncthreads();
-    const unsigned d = sh[0];
-    *above = sh[1];
-    *inbin = sh[2];
-    __syncthreads();
-    return d;
+    *above = buf[17];
+    *inbin = buf[18];
+    return buf[16];
 }
 
 // Selected (gt) and equal-to-threshold (eq) bits of 4 keys.
@@ -94,18 +100,24 @@ __device__ __forceinline__ void topk_classify(const uint32_t (&key)[4], int vali
 
 // One workgroup of NT threads: the threshold, and per slice the counts of
 // selected and equal keys in the slices before it (offs[j] = gt | eq << 16).
-// Every load is issued at the start, so the role costs one memory round
-// trip.  lds: 4096 unsigned; tot: NT/64 + 1.  0 < k <= n <= kTopkRegN,
-// n % 4 == 0, s 16-byte aligned.
+// Every load is issued at the start and the keys stay in registers, so the
+// role costs one memory round trip; the per-slice counts come from wave
+// ballots.  lds: kTopkThrWords.  0 < k <= n <= kTopkRegN, n % 4 == 0, s
+// 16-byte aligned.
 constexpr int kTopkRegN = 20480;
+constexpr int kTopkThrWords = 4096 + 256 + kTopkRegN / 256 + 2 * 20;
 template <int NT>
 __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int n, int k,
-                                               const unsigned* __restrict__ ghist, unsigned* lds, unsigned* tot,
-                                               unsigned* sh, TopkThreshold* out, unsigned* __restrict__ offs) {
+                                               const unsigned* __restrict__ ghist, unsigned* lds,
+                                               TopkThreshold* out, unsigned* __restrict__ offs) {
     constexpr int Q = kTopkRegN / (4 * NT);              // float4 of scores per thread
     constexpr int P = 4096 / NT;                         // histogram bins per thread
     constexpr int NW = NT / kWave;
-    static_assert(Q * 4 * NT == kTopkRegN && P % 4 == 0, "NT in 256, 512, 1024");
+    static_assert(Q * 4 * NT == kTopkRegN && P % 4 == 0 && NW <= 16, "NT in 256, 512, 1024");
+    unsigned* bins12 = lds;                              // second digit (bits 8..19)
+    unsigned* bins8 = lds + 4096;                        // third digit (bits 0..7)
+    unsigned* red = lds + 4096 + 256;                    // per (register, wave) counts
+    unsigned* pbuf = red + Q * NW;                       // two pick buffers of 20 words
     const int tid = threadIdx.x;
     const int n4 = n >> 2;
     const f32x4* s4 = reinterpret_cast<const f32x4*>(s);
@@ -119,58 +131,80 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
         const int c = tid + NT * q;
         v[q] = s4[c < n4 ? c : 0];
     }
+    // both later histograms cleared while the loads are in flight (the
+    // first pick's barriers order this before their use)
+    for (int b = tid; b < 4096 + 256; b += NT) lds[b] = 0u;
     unsigned c[P];
 #pragma unroll
     for (int q = 0; q < P / 4; ++q) {
         c[P - 1 - 4 * q] = hv[q].x; c[P - 2 - 4 * q] = hv[q].y; c[P - 3 - 4 * q] = hv[q].z; c[P - 4 - 4 * q] = hv[q].w;
     }
+    uint32_t key[Q][4];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[q][e] = order_key(v[q][e]);
     unsigned krem = (unsigned)k;
     unsigned above, inbin;
-    uint32_t prefix = topk_pick<P>(c, 4096, krem, tot, sh, &above, &inbin) << 20;
+    uint32_t prefix = topk_pick<P, NT>(c, 4096, krem, pbuf, &above, &inbin) << 20;
     uint32_t pmask = 0xFFF00000u;
     krem -= above;
     bool done = inbin == krem;
-    for (int ps = 0; ps < 2 && !done; ++ps) {
-        const int shift = ps == 0 ? 8 : 0;
-        const int nb = ps == 0 ? 4096 : 256;
-        const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int b = tid; b < nb; b += NT) lds[b] = 0u;
-        __syncthreads();
+    if (!done) {                                         // bits 8..19 of the keys in the chosen bin
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             if (tid + NT * q >= n4) continue;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t key = order_key(v[q][e]);
-                if ((key & pmask) == prefix) atomicAdd(&lds[(key >> shift) & dmask], 1u);
-            }
+            for (int e = 0; e < 4; ++e)
+                if ((key[q][e] & pmask) == prefix) atomicAdd(&bins12[(key[q][e] >> 8) & 0xFFFu], 1u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < P; ++i) c[i] = bins12[4095 - (P * tid + i)];
+        const unsigned d = topk_pick<P, NT>(c, 4096, krem, pbuf + 20, &above, &inbin);
+        prefix |= d << 8;
+        pmask = 0xFFFFFF00u;
+        krem -= above;
+        done = inbin == krem;
+    }
+    if (!done) {                                         // bits 0..7
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if (tid + NT * q >= n4) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((key[q][e] & pmask) == prefix) atomicAdd(&bins8[key[q][e] & 0xFFu], 1u);
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int p = P * tid + i;
-            c[i] = p < nb ? lds[nb - 1 - p] : 0u;
+            c[i] = p < 256 ? bins8[255 - p] : 0u;
         }
-        const unsigned d = topk_pick<P>(c, nb, krem, tot, sh, &above, &inbin);
-        prefix |= d << shift;
-        pmask |= dmask << shift;
+        const unsigned d = topk_pick<P, NT>(c, 256, krem, pbuf, &above, &inbin);
+        prefix |= d;
+        pmask = 0xFFFFFFFFu;
         krem -= above;
         done = inbin == krem;
     }
-    // per-slice counts: a wave sum of gt + eq * 4096 per register (at most
-    // 256 + 256 * 4096, exact in fp32), kept in LDS by (register, wave); a
-    // wave of 64 float4 lies in one slice of 256 float4
-    float* red = reinterpret_cast<float*>(lds);          // [Q][NW]
+    // per-slice counts: per register q, this wave's selected and equal keys
+    // (ballots; a wave of 64 float4 lies in one slice of 256 float4)
     const int wv = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        unsigned gm = 0u, em = 0u;
-        if (tid + NT * q < n4) {
-            const uint32_t key[4] = {order_key(v[q][0]), order_key(v[q][1]), order_key(v[q][2]), order_key(v[q][3])};
-            topk_classify(key, 4, prefix, pmask, done, &gm, &em);
+        const bool ok = tid + NT * q < n4;
+        unsigned g = 0u, eq = 0u;
+        if (done) {                                      // uniform: every key at or above the prefix
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g += (unsigned)__popcll(__ballot(ok && (key[q][e] & pmask) >= prefix));
+        } else {                                         // pmask is all ones
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                g += (unsigned)__popcll(__ballot(ok && key[q][e] > prefix));
+                eq += (unsigned)__popcll(__ballot(ok && key[q][e] == prefix));
+            }
         }
-        const float w = wave_sum((float)(__builtin_popcount(gm) + ((unsigned)__builtin_popcount(em) << 12)));
-        if (lane == 0) red[q * NW + wv] = w;
+        if (lane == 0) red[q * NW + wv] = g | eq << 16;
     }
     __syncthreads();
     if (wv == 0) {
@@ -181,10 +215,7 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
         if (lane < nsl) {
             const int q = (256 * lane) / NT, w0 = ((256 * lane) % NT) / kWave;
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                const unsigned p = (unsigned)red[q * NW + w0 + w4];
-                cnt += (p & 0xFFFu) + ((p >> 12) << 16);
-            }
+            for (int w4 = 0; w4 < 4; ++w4) cnt += red[q * NW + w0 + w4];
         }
         const unsigned incl = wave_incl_scan(cnt);
         if (lane < nsl) offs[lane] = incl - cnt;
