@@ -325,7 +325,8 @@ struct LayerWs {
     float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
     float *ya, *hpartA, *hpartM, *sA2, *sM2;      // the look-ahead predictions' own scratch
     unsigned* khist;                              // [4096] top-12-bit histogram of the next layer's neuron scores
-    void* kthr;                                   // their selection threshold and slice offsets
+    uint32_t* kkeys;                              // [N] their order keys
+    void* kthr;                                   // their selection threshold
     int32_t *head_idx, *nidx, *uidx, *ucnt;
     size_t bytes;
 };
@@ -368,7 +369,8 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     w.sA2 = cv.take<float>((size_t)h);
     w.sM2 = cv.take<float>((size_t)c->N);
     w.khist = cv.take<unsigned>(4096);
-    w.kthr = cv.take<unsigned>(4 + 64);
+    w.kkeys = cv.take<uint32_t>((size_t)c->N);
+    w.kthr = cv.take<unsigned>(4);
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -498,7 +500,7 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     TRY(launch_splitk(L.q, 1, dh, head_idx, n_sel, &view, st->kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
                       fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits, ride ? &p2 : nullptr));
     if (ride && !ride_topk) TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, s));
-    const TopkSel tk{L.sM2, N, c->k_neurons, L.khist, L.kthr, st->next_neuron_idx};
+    const TopkSel tk{L.sM2, N, c->k_neurons, L.khist, L.kkeys, L.kthr, st->next_neuron_idx};
     {
         AxpyCall ac{};
         ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;

@@ -242,7 +242,8 @@ struct TopkSel {
     const float* s;           // scores [n], 16-byte aligned
     int n, k;                 // 0 < k <= n <= 20480, n % 4 == 0
     unsigned* hist;           // [4096], cleared before the histogram role
-    void* thr;                // the threshold (16 bytes), then per-slice offsets [n / 1024]
+    uint32_t* keys;           // [n] order keys, written by the histogram role; 16-byte aligned
+    void* thr;                // the threshold (16 bytes)
     int32_t* idx;             // [k] selected, ascending
 };
 bool topk_split_supported(int n, int k);

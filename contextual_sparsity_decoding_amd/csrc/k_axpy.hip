@@ -51,9 +51,11 @@ struct AxpyArgs {
     float* partial;           // [n_groups][B][d]
     int32_t* rows_read;
     // NB == 1, tk_s set: the last column of workgroups runs a selection
-    // role over scores tk_s[0, tk_n), 1024 per workgroup: ATTN histograms
-    // them into tk_hist, otherwise emits the indices above tk_thr into tk_idx
+    // role over scores tk_s[0, tk_n), 1024 per workgroup: ATTN stores their
+    // order keys in tk_keys and histograms them into tk_hist, otherwise
+    // emits the indices of the keys above tk_thr into tk_idx
     const float* tk_s;
+    uint32_t* tk_keys;
     int tk_n, tk_k;
     unsigned* tk_hist;
     const TopkThreshold* tk_thr;
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     __shared__ int s_row[kRowsPerGroup];
     __shared__ float s_cf[kRowsPerGroup * NB];
     __shared__ float shbuf[RED > QF ? RED : QF];   // split merging, then the wave reduction
-    __shared__ unsigned tot[17];
+    __shared__ unsigned tot[20];
     auto red = reinterpret_cast<float (*)[NBC][SW]>(shbuf);
     auto s_q = reinterpret_cast<float (*)[kRowsPerGroup][NQ][3]>(shbuf);
     const T* W = (const T*)a.w;
@@ -148,9 +150,9 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
             if (g * kTopkSlice < a.tk_n) {
                 if constexpr (ATTN) {
                     __shared__ unsigned tk_lds[4096];
-                    topk_hist_slice(a.tk_s, a.tk_n, g, tk_lds, a.tk_hist);
+                    topk_hist_slice(a.tk_s, a.tk_n, g, tk_lds, a.tk_hist, a.tk_keys);
                 } else {
-                    topk_emit_slice(a.tk_s, a.tk_n, a.tk_k, g, a.tk_thr, (const unsigned*)a.tk_thr + 4, tot, a.tk_idx);
+                    topk_emit_slice(a.tk_keys, a.tk_n, a.tk_k, g, a.tk_thr, tot, a.tk_idx);
                 }
             }
             return;
@@ -344,11 +346,10 @@ __global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restric
 // output projection built.
 constexpr int kFinThrThreads = 1024;
 struct FinThr {
-    const float* s;
+    const uint32_t* keys;
     int n, k;
     const unsigned* hist;
     TopkThreshold* thr;
-    unsigned* offs;
 };
 
 template <typename T>
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kFinThrThreads) void k_axpy_finalize_thr(const floa
     if (blockIdx.x == gridDim.x - 1) {
         if (blockIdx.y == 0) {
             __shared__ unsigned lds[kTopkThrWords];
-            topk_threshold<kFinThrThreads>(f.s, f.n, f.k, f.hist, lds, f.thr, f.offs);
+            topk_threshold<kFinThrThreads>(f.keys, f.n, f.k, f.hist, lds, f.thr);
         }
         return;
     }
@@ -400,13 +401,13 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     a.blk = c.blk; a.coef = c.coef; a.coef_stride = c.coef_stride; a.skip_zero = c.skip_zero ? 1 : 0;
     a.apart = c.apart; a.num_splits = c.num_splits;
     a.B = c.B; a.n_groups = p.n_groups; a.partial = c.partial; a.rows_read = c.rows_read;
-    a.tk_s = nullptr; a.tk_n = a.tk_k = 0; a.tk_hist = nullptr; a.tk_thr = nullptr; a.tk_idx = nullptr;
+    a.tk_s = nullptr; a.tk_keys = nullptr; a.tk_n = a.tk_k = 0; a.tk_hist = nullptr; a.tk_thr = nullptr; a.tk_idx = nullptr;
     if (c.sel) {
         const TopkSel& t = *c.sel;
         if (c.B != 1 || !topk_split_supported(t.n, t.k) || ((uintptr_t)t.s & 15u) ||
-            !t.hist || !t.thr || !t.idx || ((uintptr_t)t.hist & 15u))
+            !t.hist || !t.thr || !t.idx || !t.keys || ((uintptr_t)t.hist & 15u) || ((uintptr_t)t.keys & 15u))
             return fail(DV_ERR_UNSUPPORTED, "selection slices beside a gather-AXPY: n=%d k=%d", t.n, t.k);
-        a.tk_s = t.s; a.tk_n = t.n; a.tk_k = t.k; a.tk_hist = t.hist; a.tk_thr = (const TopkThreshold*)t.thr;
+        a.tk_s = t.s; a.tk_keys = t.keys; a.tk_n = t.n; a.tk_k = t.k; a.tk_hist = t.hist; a.tk_thr = (const TopkThreshold*)t.thr;
         a.tk_idx = t.idx;
     }
     const int nb = c.B <= 1 ? 1 : c.B <= 2 ? 2 : c.B <= 4 ? 4 : c.B <= 8 ? 8 : 16;
@@ -421,8 +422,7 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
 #undef DV_AXPY
     const dim3 fg(cdiv(c.d / 4, 64), c.B);
     if (c.sel && c.apart) {                        // the selection threshold rides in the finalize
-        const FinThr f{c.sel->s, c.sel->n, c.sel->k, c.sel->hist, (TopkThreshold*)c.sel->thr,
-                       (unsigned*)c.sel->thr + 4};
+        const FinThr f{c.sel->keys, c.sel->n, c.sel->k, c.sel->hist, (TopkThreshold*)c.sel->thr};
         const dim3 fg2(fg.x + 1, fg.y);
         if (c.wdt == DV_F16)
             hipLaunchKernelGGL(k_axpy_finalize_thr<half_t>, fg2, dim3(kFinThrThreads), 0, s, c.partial, p.n_groups, c.B,

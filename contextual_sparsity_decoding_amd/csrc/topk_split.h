@@ -7,14 +7,15 @@
 // Inference Time" (arXiv 2310.17157), §2.3 (the sets S_M under a budget)
 // and §4.3 (the next layer's selection overlaps this layer's work).
 //
-//   1. topk_hist_slice, one workgroup per 1024 scores: the histogram of the
-//      keys' top 12 bits, added into a global histogram (cleared earlier).
+//   1. topk_hist_slice, one workgroup per 1024 scores: stores the scores'
+//      order keys and adds the histogram of their top 12 bits into a global
+//      histogram (cleared earlier).
 //   2. topk_threshold, one workgroup: the k-th key by radix select, the
 //      first digit read off that histogram, the next 12 and 8 bits
 //      histogrammed in LDS over the keys still in the running (stopping once
 //      a bin is taken whole); it writes the threshold.
-//   3. topk_emit_slice, one workgroup per 1024 scores: counts the selected
-//      keys before its slice itself (the row is L2-resident), then writes
+//   3. topk_emit_slice, one workgroup per 1024 keys: counts the selected
+//      keys in the slices before its own (they are L2-resident), then writes
 //      its slice's selected indices in order.
 #pragma once
 
@@ -32,15 +33,19 @@ struct TopkThreshold {
 };
 
 __device__ __forceinline__ void topk_hist_slice(const float* __restrict__ s, int n, int slice, unsigned* lds,
-                                                unsigned* __restrict__ ghist) {
+                                                unsigned* __restrict__ ghist, uint32_t* __restrict__ keys) {
     const int tid = threadIdx.x;
     const int i = slice * kTopkSlice + 4 * tid;
     const f32x4 v = i < n ? *reinterpret_cast<const f32x4*>(s + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int b = tid; b < 4096; b += 256) lds[b] = 0u;
     __syncthreads();
     if (i < n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(&lds[order_key(v[e]) >> 20], 1u);
+        const uint4 kk{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
+        *reinterpret_cast<uint4*>(keys + i) = kk;
+        atomicAdd(&lds[kk.x >> 20], 1u);
+        atomicAdd(&lds[kk.y >> 20], 1u);
+        atomicAdd(&lds[kk.z >> 20], 1u);
+        atomicAdd(&lds[kk.w >> 20], 1u);
     }
     __syncthreads();
     for (int b = tid; b < 4096; b += 256) {     // at most one global add per bin and slice
@@ -98,38 +103,34 @@ __device__ __forceinline__ void topk_classify(const uint32_t (&key)[4], int vali
     *eqm = q;
 }
 
-// One workgroup of NT threads: the threshold, and per slice the counts of
-// selected and equal keys in the slices before it (offs[j] = gt | eq << 16).
-// Every load is issued at the start and the keys stay in registers, so the
-// role costs one memory round trip; the per-slice counts come from wave
-// ballots.  lds: kTopkThrWords.  0 < k <= n <= kTopkRegN, n % 4 == 0, s
-// 16-byte aligned.
+// One workgroup of NT threads: the threshold of the k largest of n order
+// keys.  Every load is issued at the start and the keys stay in registers,
+// so the role costs one memory round trip.  lds: kTopkThrWords.
+// 0 < k <= n <= kTopkRegN, n % 4 == 0, keys 16-byte aligned.
 constexpr int kTopkRegN = 20480;
-constexpr int kTopkThrWords = 4096 + 256 + kTopkRegN / 256 + 2 * 20;
+constexpr int kTopkThrWords = 4096 + 256 + 2 * 20;
 template <int NT>
-__device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int n, int k,
+__device__ __forceinline__ void topk_threshold(const uint32_t* __restrict__ keys, int n, int k,
                                                const unsigned* __restrict__ ghist, unsigned* lds,
-                                               TopkThreshold* out, unsigned* __restrict__ offs) {
-    constexpr int Q = kTopkRegN / (4 * NT);              // float4 of scores per thread
+                                               TopkThreshold* out) {
+    constexpr int Q = kTopkRegN / (4 * NT);              // uint4 of keys per thread
     constexpr int P = 4096 / NT;                         // histogram bins per thread
-    constexpr int NW = NT / kWave;
-    static_assert(Q * 4 * NT == kTopkRegN && P % 4 == 0 && NW <= 16, "NT in 256, 512, 1024");
+    static_assert(Q * 4 * NT == kTopkRegN && P % 4 == 0 && NT / kWave <= 16, "NT in 256, 512, 1024");
     unsigned* bins12 = lds;                              // second digit (bits 8..19)
     unsigned* bins8 = lds + 4096;                        // third digit (bits 0..7)
-    unsigned* red = lds + 4096 + 256;                    // per (register, wave) counts
-    unsigned* pbuf = red + Q * NW;                       // two pick buffers of 20 words
+    unsigned* pbuf = lds + 4096 + 256;                   // two pick buffers of 20 words
     const int tid = threadIdx.x;
     const int n4 = n >> 2;
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(s);
+    const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     const uint4* h4 = reinterpret_cast<const uint4*>(ghist + 4096 - P * (tid + 1));
     uint4 hv[P / 4];
 #pragma unroll
     for (int q = 0; q < P / 4; ++q) hv[q] = h4[q];
-    f32x4 v[Q];                                          // float4 tid + NT q
+    uint4 kv[Q];                                         // uint4 tid + NT q
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int c = tid + NT * q;
-        v[q] = s4[c < n4 ? c : 0];
+        kv[q] = k4[c < n4 ? c : 0];
     }
     // both later histograms cleared while the loads are in flight (the
     // first pick's barriers order this before their use)
@@ -139,11 +140,6 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
     for (int q = 0; q < P / 4; ++q) {
         c[P - 1 - 4 * q] = hv[q].x; c[P - 2 - 4 * q] = hv[q].y; c[P - 3 - 4 * q] = hv[q].z; c[P - 4 - 4 * q] = hv[q].w;
     }
-    uint32_t key[Q][4];
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) key[q][e] = order_key(v[q][e]);
     unsigned krem = (unsigned)k;
     unsigned above, inbin;
     uint32_t prefix = topk_pick<P, NT>(c, 4096, krem, pbuf, &above, &inbin) << 20;
@@ -154,9 +150,10 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             if (tid + NT * q >= n4) continue;
+            const uint32_t kq[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if ((key[q][e] & pmask) == prefix) atomicAdd(&bins12[(key[q][e] >> 8) & 0xFFFu], 1u);
+                if ((kq[e] & pmask) == prefix) atomicAdd(&bins12[(kq[e] >> 8) & 0xFFFu], 1u);
         }
         __syncthreads();
 #pragma unroll
@@ -171,9 +168,10 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             if (tid + NT * q >= n4) continue;
+            const uint32_t kq[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if ((key[q][e] & pmask) == prefix) atomicAdd(&bins8[key[q][e] & 0xFFu], 1u);
+                if ((kq[e] & pmask) == prefix) atomicAdd(&bins8[kq[e] & 0xFFu], 1u);
         }
         __syncthreads();
 #pragma unroll
@@ -187,61 +185,50 @@ __device__ __forceinline__ void topk_threshold(const float* __restrict__ s, int 
         krem -= above;
         done = inbin == krem;
     }
-    // per-slice counts: per register q, this wave's selected and equal keys
-    // (ballots; a wave of 64 float4 lies in one slice of 256 float4)
-    const int wv = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const bool ok = tid + NT * q < n4;
-        unsigned g = 0u, eq = 0u;
-        if (done) {                                      // uniform: every key at or above the prefix
-#pragma unroll
-            for (int e = 0; e < 4; ++e) g += (unsigned)__popcll(__ballot(ok && (key[q][e] & pmask) >= prefix));
-        } else {                                         // pmask is all ones
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                g += (unsigned)__popcll(__ballot(ok && key[q][e] > prefix));
-                eq += (unsigned)__popcll(__ballot(ok && key[q][e] == prefix));
-            }
-        }
-        if (lane == 0) red[q * NW + wv] = g | eq << 16;
-    }
-    __syncthreads();
-    if (wv == 0) {
-        // slice j = float4 [256 j, 256 j + 256) = register q = 256 j / NT, waves
-        // (256 j % NT) / 64 .. + 3
-        const int nsl = (n4 + 255) / 256;
-        unsigned cnt = 0u;                                // gt | eq << 16 of slice `lane`
-        if (lane < nsl) {
-            const int q = (256 * lane) / NT, w0 = ((256 * lane) % NT) / kWave;
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) cnt += red[q * NW + w0 + w4];
-        }
-        const unsigned incl = wave_incl_scan(cnt);
-        if (lane < nsl) offs[lane] = incl - cnt;
-        if (lane == 0) *out = TopkThreshold{prefix, pmask, krem, done ? 1u : 0u};
-    }
+    if (tid == 0) *out = TopkThreshold{prefix, pmask, krem, done ? 1u : 0u};
 }
 
-// One workgroup per slice of 1024 scores: the slice's selected indices at
-// their place in the ascending set, from the threshold and the counts of
-// the slices before it.
-__device__ __forceinline__ void topk_emit_slice(const float* __restrict__ s, int n, int k, int slice,
-                                                const TopkThreshold* __restrict__ thr,
-                                                const unsigned* __restrict__ offs, unsigned* tot,
+// One workgroup per slice of 1024 keys: the slice's selected indices at
+// their place in the ascending set.  The selected and equal keys of the
+// slices before it are counted here too, every one of their loads issued
+// at once (each workgroup reads at most kTopkRegN - 1024 keys).  tot: 20
+// words.
+__device__ __forceinline__ void topk_emit_slice(const uint32_t* __restrict__ keys, int n, int k, int slice,
+                                                const TopkThreshold* __restrict__ thr, unsigned* tot,
                                                 int32_t* __restrict__ idx) {
-    const int tid = threadIdx.x;
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(s);
+    constexpr int MAXB = kTopkRegN / kTopkSlice - 1;    // slices before the last
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     const int n4 = n >> 2;
     const int own = slice * (kTopkSlice / 4) + tid;
-    const f32x4 mine = s4[own < n4 ? own : 0];
+    const uint4 mine = k4[own < n4 ? own : 0];
+    uint4 pre[MAXB];                                     // uint4 tid + 256 j of slice j < slice
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) pre[j] = j < slice ? k4[tid + (kTopkSlice / 4) * j] : uint4{0u, 0u, 0u, 0u};
     const TopkThreshold t = *thr;
-    const unsigned off = offs[slice];
-    const uint32_t key[4] = {order_key(mine[0]), order_key(mine[1]), order_key(mine[2]), order_key(mine[3])};
+    const bool done = t.done != 0u;
+    unsigned pc = 0u;                                    // gt | eq << 16 over this thread's earlier keys
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) {
+        if (j < slice) {
+            const uint32_t kq[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t mk = kq[e] & t.pmask;
+                pc += (mk > t.prefix || (done && mk == t.prefix)) ? 1u
+                      : (!done && kq[e] == t.prefix)             ? 0x10000u
+                                                                 : 0u;
+            }
+        }
+    }
+    const unsigned pw = (unsigned)__builtin_amdgcn_readlane((int)wave_incl_scan(pc), 63);
+    if (lane == 0) tot[16 + wv] = pw;
+    const uint32_t key[4] = {mine.x, mine.y, mine.z, mine.w};
     unsigned gm, em;
-    topk_classify(key, own < n4 ? 4 : 0, t.prefix, t.pmask, t.done != 0u, &gm, &em);
+    topk_classify(key, own < n4 ? 4 : 0, t.prefix, t.pmask, done, &gm, &em);
     unsigned tsum;
     const unsigned ex = block_excl_scan(__builtin_popcount(gm) + ((unsigned)__builtin_popcount(em) << 16), tot, &tsum);
+    const unsigned off = (tot[16] + tot[17]) + (tot[18] + tot[19]);   // written before the scan's barriers
     unsigned eq_rank = (off >> 16) + (ex >> 16);        // equal keys before this thread's
     unsigned pos = (off & 0xFFFFu) + (ex & 0xFFFFu) + min(eq_rank, t.krem);
 #pragma unroll

@@ -130,6 +130,40 @@ def test_lookahead_selection_shapes(dvlib, N, k_m):
     assert _run_steps(dvlib, A, n0, X, None) == T
 
 
+@pytest.mark.parametrize("protos", [1, 5])
+def test_lookahead_selection_ties(dvlib, protos):
+    """Exact ties among the next layer's neuron scores: the rows of its second
+    predictor layer repeat `protos` distinct rows, so equal scores are equal on
+    both sides.  The selection split over the layer's launches must take the
+    lower indices among equal scores at the threshold, as the oracle does,
+    also across its 1024-score slices."""
+    dims = LayerDims(d=512, N=4096, h=8, d_h=64, r_attn=16, r_mlp=32, wdt="f16")
+    n0, k_h, k_m = 12, 3, 1000
+    A = Ahead(dvlib, dims, n0, n0 + 3, seed=49, k_heads=k_h, k_neurons=k_m)
+    A.Wn["pm2_t"] = A.Wn["pm2_t"][:protos].copy()[np.arange(dims.N) % protos]
+    A.Wnd = upload(A.Wn)
+    X = synth.layer_inputs(dims.d, 1, 1, seed=49)
+    cfg = A.cfg(dvlib.DV_LOOKAHEAD | dvlib.DV_HOLE_FILL | dvlib.DV_SKIP_NONPOS_FC2)
+    ws = dvlib.workspace(dvlib.dv_decode_workspace_bytes(cfg, A.max_len))
+    g = np.random.default_rng(7)
+    hi = np.sort(g.choice(dims.h, k_h, replace=False)).astype(np.int32)
+    ni = np.sort(g.choice(dims.N, k_m, replace=False)).astype(np.int32)
+    hn = torch.full((k_h,), -1, dtype=torch.int32, device="cuda")
+    nn = torch.full((k_m,), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty(1, dims.d, device="cuda")
+    hi_d, ni_d, x_d = dev(hi), dev(ni), dev(X[0])     # alive until the launches have run
+    st = A.state(n0, hi_d, ni_d, hn, nn)
+    dvlib.dv_decode_layer(A.wts, cfg, st, x_d, out, ws)
+    torch.cuda.synchronize()
+    want, rec = A.oracle(X[0], n0, hi, ni)
+    check_close(host(out), want, "f16", "tied selection step")
+    vals = np.unique(rec["next_neuron_scores"][0])
+    assert vals.size == protos
+    if protos > 1:
+        assert np.min(np.diff(vals)) > MARGIN
+    assert np.array_equal(host(nn), rec["next_neuron_idx"])
+
+
 @pytest.mark.parametrize("aux", [True, False])
 def test_lookahead_opt13b_layer_full_size(dvlib, aux):
     """The OPT-13B-shaped layer in the parallel form: 20 given heads, 2048
