@@ -33,9 +33,121 @@ struct QkvArgs {
     const float* ln_b;
     float eps;
     int qkv_blocks;           // the projection's workgroups
+    int hole_blocks;          // NB == 1, HB > 0: hole helpers after them (qkv_hole_items), or 0
     int pred_blocks;          // LNF: workgroups placed first that compute `pred` rows (4*R per workgroup)
     RowArgs pred;             // the next layer's predictor layer one (look-ahead) on LN(input), or w == NULL
 };
+
+// Lane-partial dots of a wave's R register-resident rows with NV inputs at
+// `in` (LDS, stride d): per accumulator the same sequence of fmaf over the
+// chunks and their elements as the on-time dot products.
+template <typename T, int CH, int R, int NV>
+__device__ __forceinline__ void qkv_dots(const u32x4 (&w)[R][CH], const float* in, int d, int nchunk,
+                                         float (&acc)[R][NV]) {
+    constexpr int E = Vec<T>::E;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float yv[E];
+                const f32x4* y4 = reinterpret_cast<const f32x4*>(in + (size_t)v * d + (size_t)c * E);
+#pragma unroll
+                for (int q = 0; q < E / 4; ++q) {
+                    const f32x4 t = y4[q];
+                    yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float f[E];
+                    unpack(w[j][i], f, T());
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[j][v] = fmaf(f[e], yv[e], acc[j][v]);
+                }
+            }
+        }
+    }
+}
+
+// Hole helpers (batch of one, n_sel <= 64): the missing positions of each
+// selected head past the first HB (which its owner workgroups compute beside
+// their on-time dot products) are cut into items of one K or V block of 4*R
+// rows and up to NV positions.  Helper `hid` takes items hid, hid + nhelp,
+// ...: it loads the item's weight rows again (read moments before by their
+// owner) and its stored inputs, and runs the owner's instructions on the
+// same values, so the entries are bit-identical to on-time ones.  The
+// helpers come after every owner in the grid, so they take the CUs the
+// owners leave, and the rounds run side by side instead of one after
+// another in the owner.
+template <typename T, int CH, int R, int HB, int NV>
+__device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float* ys) {
+    constexpr int E = Vec<T>::E;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int pos = a.pos_dev ? *a.pos_dev : a.pos;
+    if (pos < 0 || pos >= a.max_len || !a.y_buf || !a.valid_upto) return;
+    const int d = a.d, dh = a.dh, nchunk = d / E;
+    const int nrb = dh / (4 * R);                      // row blocks per K or V block
+    // lane s: selected head s, its first missing position, its rounds of NV
+    int head = 0, lo0 = pos, nr = 0;
+    if (lane < a.n_sel) {
+        head = a.head_idx ? a.head_idx[lane] : lane;
+        if ((unsigned)head < (unsigned)a.h) {
+            lo0 = min(max(a.valid_upto[head] + 1, 0), pos);
+            const int m = pos - lo0 - HB;
+            nr = m > 0 ? (m + NV - 1) / NV : 0;
+        }
+    }
+    const unsigned cnt = 2u * (unsigned)(nrb * nr);    // items of head s
+    const unsigned incl = wave_incl_scan(cnt);
+    const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+    for (unsigned it = (unsigned)hid; it < total; it += (unsigned)a.hole_blocks) {
+        const int s = (int)__builtin_ctzll(__ballot(incl > it));    // the first head whose items reach past it
+        const unsigned l = it - ((unsigned)__builtin_amdgcn_readlane((int)incl, s) -
+                                 (unsigned)__builtin_amdgcn_readlane((int)cnt, s));
+        const int hd = __builtin_amdgcn_readlane(head, s);
+        const int lo = __builtin_amdgcn_readlane(lo0, s);
+        const int nrs = __builtin_amdgcn_readlane(nr, s);
+        const int per = nrb * nrs;                     // items of one of K, V
+        const int which = 1 + (int)l / per;
+        const int rb = ((int)l % per) / nrs, rnd = ((int)l % per) % nrs;
+        const int p0 = lo + HB + rnd * NV;
+        const int np = min(NV, pos - p0);
+        const int e0 = rb * 4 * R + wv * R;
+        const T* Wb = (const T*)a.w + ((size_t)(which * a.h + hd) * dh + e0) * d;
+        __syncthreads();                               // the previous item's inputs are consumed
+        stage_dma(ys, a.y_buf + (size_t)p0 * d, np * d);
+        issue_order_fence();
+        u32x4 w[R][CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int c = lane + i * kWave;
+                w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
+            }
+        float bv[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) bv[j] = to_f32(((const T*)a.bias)[(size_t)(which * a.h + hd) * dh + e0 + j]);
+        wait_dma_and_sync();
+        float acc[R][NV];
+        qkv_dots<T, CH, R, NV>(w, ys, d, nchunk, acc);
+        half_t* cache = which == 1 ? a.K : a.V;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float hv = wave_sum(acc[j][v]) + bv[j];
+                if (lane == 0 && v < np) cache[((size_t)hd * a.max_len + p0 + v) * dh + e0 + j] = (half_t)hv;
+            }
+    }
+}
 
 // A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
 // holds rows wv*R .. wv*R+R-1 in registers (lane l: chunks l, l+64, ...), so
@@ -62,6 +174,12 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             return;
         }
         qb -= a.pred_blocks;
+    }
+    if constexpr (NB == 1 && HB > 0 && YL) {
+        if (qb >= a.qkv_blocks) {                      // a hole helper
+            qkv_hole_items<T, CH, R, HB, HB + 1>(a, qb - a.qkv_blocks, ys);
+            return;
+        }
     }
     const int d = a.d, dh = a.dh;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -130,34 +248,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
 
     // lane-partial dots of the R rows with NV inputs at `in` (stride d)
     auto dots = [&](const float* in, auto nv_tag, float (&acc)[R][decltype(nv_tag)::value]) {
-        constexpr int NV = decltype(nv_tag)::value;
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-#pragma unroll
-            for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    float yv[E];
-                    const f32x4* y4 = reinterpret_cast<const f32x4*>(in + (size_t)v * d + (size_t)c * E);
-#pragma unroll
-                    for (int q = 0; q < E / 4; ++q) {
-                        const f32x4 t = y4[q];
-                        yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
-                    }
-#pragma unroll
-                    for (int j = 0; j < R; ++j) {
-                        float f[E];
-                        unpack(w[j][i], f, T());
-#pragma unroll
-                        for (int e = 0; e < E; ++e) acc[j][v] = fmaf(f[e], yv[e], acc[j][v]);
-                    }
-                }
-            }
-        }
+        qkv_dots<T, CH, R, decltype(nv_tag)::value>(w, in, d, nchunk, acc);
     };
 
     // The weight registers are marked as rewritten after each use, so the
@@ -283,8 +374,9 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
                     if (lane == 0 && v < cnt) cache[((size_t)head * a.max_len + lo0 + v) * dh + e0 + j] = (half_t)hv;
                 }
         }
-        for (int p0 = lo0 + HB; p0 < pos; p0 += HB2) {
-            const int cnt = min(HB2, pos - p0);
+        const int p_end = a.hole_blocks > 0 ? lo0 + HB : pos;   // else the hole helpers take the rest
+        for (int p0 = lo0 + HB; p0 < p_end; p0 += HB2) {
+            const int cnt = min(HB2, p_end - p0);
             __syncthreads();                           // the previous round's inputs (and y) are consumed
             stage_dma(ys, a.y_buf + (size_t)p0 * d, cnt * d);
             wait_dma_and_sync();
@@ -341,8 +433,12 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     if (a.dh % (4 * R)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
     a.qkv_blocks = rows / (4 * R);
     a.pred_blocks = a.pred.w ? cdiv(a.pred.n_max, 4 * R) : 0;
-    const int grid = a.pred_blocks + a.qkv_blocks;
     const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
+    // batch of one with inputs in LDS: one hole helper per K/V row block
+    // (more items are taken in turn)
+    const int hb = holes && yl + 2 * row <= kQkvLdsMax ? 2 : holes && yl + row <= kQkvLdsMax ? 1 : 0;
+    a.hole_blocks = NB == 1 && a.B == 1 && yl && hb > 0 && a.n_sel <= kWave ? 2 * a.n_sel * (a.dh / (4 * R)) : 0;
+    const int grid = a.pred_blocks + a.qkv_blocks + a.hole_blocks;
     const bool lnf = a.ln_g != nullptr;
     if (lnf && (NB != 1 || !yl)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V with LayerNorm: B=%d d=%d", a.B, a.d);
     if (a.pred.w && (!lnf || a.pred.d != a.d)) return fail(DV_ERR_UNSUPPORTED, "predictor rows need the LayerNorm-folded Q/K/V");
@@ -357,8 +453,8 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
         if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, false>), dim3(grid), dim3(kBlock), LDS, s, a); \
         else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false, false>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
     } while (0)
-    if (holes && yl + 2 * row <= kQkvLdsMax) DV_QKV(2, yl + 2 * row);
-    else if (holes && yl + row <= kQkvLdsMax) DV_QKV(1, yl + row);
+    if (hb == 2) DV_QKV(2, yl + 2 * row);
+    else if (hb == 1) DV_QKV(1, yl + row);
     else DV_QKV(0, yl);
 #undef DV_QKV
     return DV_OK;
