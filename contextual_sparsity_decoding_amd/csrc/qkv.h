@@ -40,7 +40,10 @@ struct QkvArgs {
 
 // Lane-partial dots of a wave's R register-resident rows with NV inputs at
 // `in` (LDS, stride d): per accumulator the same sequence of fmaf over the
-// chunks and their elements as the on-time dot products.
+// chunks and their elements as the on-time dot products.  Within a chunk the
+// R * NV accumulators advance together, element by element, so a lone wave
+// has independent FMAs to issue instead of one dependent chain per
+// accumulator.
 template <typename T, int CH, int R, int NV>
 __device__ __forceinline__ void qkv_dots(const u32x4 (&w)[R][CH], const float* in, int d, int nchunk,
                                          float (&acc)[R][NV]) {
@@ -54,31 +57,34 @@ __device__ __forceinline__ void qkv_dots(const u32x4 (&w)[R][CH], const float* i
     for (int i = 0; i < CH; ++i) {
         const int c = lane + i * kWave;
         if (c < nchunk) {
+            float yv[NV][E];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                float yv[E];
                 const f32x4* y4 = reinterpret_cast<const f32x4*>(in + (size_t)v * d + (size_t)c * E);
 #pragma unroll
                 for (int q = 0; q < E / 4; ++q) {
                     const f32x4 t = y4[q];
-                    yv[4 * q] = t[0]; yv[4 * q + 1] = t[1]; yv[4 * q + 2] = t[2]; yv[4 * q + 3] = t[3];
-                }
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    float f[E];
-                    unpack(w[j][i], f, T());
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[j][v] = fmaf(f[e], yv[e], acc[j][v]);
+                    yv[v][4 * q] = t[0]; yv[v][4 * q + 1] = t[1]; yv[v][4 * q + 2] = t[2]; yv[v][4 * q + 3] = t[3];
                 }
             }
+            float f[R][E];
+#pragma unroll
+            for (int j = 0; j < R; ++j) unpack(w[j][i], f[j], T());
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) acc[j][v] = fmaf(f[j][e], yv[v][e], acc[j][v]);
         }
     }
 }
 
 // Hole helpers (batch of one, n_sel <= 64): the missing positions of each
 // selected head past the first HB (which its owner workgroups compute beside
-// their on-time dot products) are cut into items of one K or V block of 4*R
-// rows and up to NV positions.  Helper `hid` takes items hid, hid + nhelp,
+// their on-time dot products) are cut into items of 4*R rows of one K or V
+// block (R rows per wave; a row's sums do not depend on how many rows a wave
+// holds) and up to NV positions.  Helper `hid` takes items hid, hid + nhelp,
 // ...: it loads the item's weight rows again (read moments before by their
 // owner) and its stored inputs, and runs the owner's instructions on the
 // same values, so the entries are bit-identical to on-time ones.  The
@@ -94,15 +100,18 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
     if (pos < 0 || pos >= a.max_len || !a.y_buf || !a.valid_upto) return;
     const int d = a.d, dh = a.dh, nchunk = d / E;
     const int nrb = dh / (4 * R);                      // row blocks per K or V block
-    // lane s: selected head s, its first missing position, its rounds of NV
+    // lane s: selected head s, its first missing position, its rounds of NV.
+    // With at most 64 heads every head's valid position is loaded beside the
+    // head list and picked by lane (one memory round trip, not two).
     int head = 0, lo0 = pos, nr = 0;
-    if (lane < a.n_sel) {
-        head = a.head_idx ? a.head_idx[lane] : lane;
-        if ((unsigned)head < (unsigned)a.h) {
-            lo0 = min(max(a.valid_upto[head] + 1, 0), pos);
-            const int m = pos - lo0 - HB;
-            nr = m > 0 ? (m + NV - 1) / NV : 0;
-        }
+    const int vu_all = a.h <= kWave && lane < a.h ? a.valid_upto[lane] : 0;
+    if (lane < a.n_sel) head = a.head_idx ? a.head_idx[lane] : lane;
+    const bool hv = lane < a.n_sel && (unsigned)head < (unsigned)a.h;
+    const int vu = a.h <= kWave ? __shfl(vu_all, hv ? head : 0, kWave) : (hv ? a.valid_upto[head] : 0);
+    if (hv) {
+        lo0 = min(max(vu + 1, 0), pos);
+        const int m = pos - lo0 - HB;
+        nr = m > 0 ? (m + NV - 1) / NV : 0;
     }
     const unsigned cnt = 2u * (unsigned)(nrb * nr);    // items of head s
     const unsigned incl = wave_incl_scan(cnt);
@@ -149,6 +158,10 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
     }
 }
 
+// Rows per wave of a hole helper's item: half the owner's, so an item
+// reloads and computes half as much and twice as many run side by side.
+constexpr int qkv_hole_rows(int r) { return r >= 2 ? r / 2 : 1; }
+
 // A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
 // holds rows wv*R .. wv*R+R-1 in registers (lane l: chunks l, l+64, ...), so
 // every input chunk read from LDS serves R rows.  The inputs are y (NB
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     }
     if constexpr (NB == 1 && HB > 0 && YL) {
         if (qb >= a.qkv_blocks) {                      // a hole helper
-            qkv_hole_items<T, CH, R, HB, HB + 1>(a, qb - a.qkv_blocks, ys);
+            qkv_hole_items<T, CH, qkv_hole_rows(R), HB, HB + 1>(a, qb - a.qkv_blocks, ys);
             return;
         }
     }
@@ -434,10 +447,10 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     a.qkv_blocks = rows / (4 * R);
     a.pred_blocks = a.pred.w ? cdiv(a.pred.n_max, 4 * R) : 0;
     const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
-    // batch of one with inputs in LDS: one hole helper per K/V row block
-    // (more items are taken in turn)
+    // batch of one with inputs in LDS: one hole helper per K/V block of
+    // 4 * qkv_hole_rows(R) rows (more items are taken in turn)
     const int hb = holes && yl + 2 * row <= kQkvLdsMax ? 2 : holes && yl + row <= kQkvLdsMax ? 1 : 0;
-    a.hole_blocks = NB == 1 && a.B == 1 && yl && hb > 0 && a.n_sel <= kWave ? 2 * a.n_sel * (a.dh / (4 * R)) : 0;
+    a.hole_blocks = NB == 1 && a.B == 1 && yl && hb > 0 && a.n_sel <= kWave ? 2 * a.n_sel * (a.dh / (4 * qkv_hole_rows(R))) : 0;
     const int grid = a.pred_blocks + a.qkv_blocks + a.hole_blocks;
     const bool lnf = a.ln_g != nullptr;
     if (lnf && (NB != 1 || !yl)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V with LayerNorm: B=%d d=%d", a.B, a.d);
