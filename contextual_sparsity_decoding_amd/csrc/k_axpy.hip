@@ -66,9 +66,12 @@ struct AxpyArgs {
 // o[b][s][e] = sum_c 2^(m_c - M) acc_c[e] / sum_c 2^(m_c - M) l_c over the
 // splits c with l_c > 0 (log2-domain partials).  Wave q merges its quarter
 // of the splits with a running maximum; the quarters are merged in order.
-template <int NB>
+// after_loads() runs once per wave, right after the first round of partial
+// loads is issued (every lane loads; lanes past the live rows or batch rows
+// read row 0 and discard it), so loads issued there queue behind these.
+template <int NB, typename AfterLoads>
 __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, float* s_cf,
-                                          float (*s_q)[kRowsPerGroup][NB][3]) {
+                                          float (*s_q)[kRowsPerGroup][NB][3], AfterLoads&& after_loads) {
     constexpr int CB = 20;                         // splits in flight: up to 80 splits in one round of loads
     const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
     const int dh = a.blk, ns = a.num_splits;
@@ -78,12 +81,14 @@ __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, 
     const int s = u / dh, e = u % dh;
     const int per = (ns + 3) / 4;
     const int c0 = q * per, c1 = min(ns, c0 + per);
+    bool issued = false;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float m = -INFINITY, l = 0.f, num = 0.f;
-        if (b < a.B && ok) {
-            const float* P = a.apart + ((size_t)(b * n_sel + s) * ns) * (dh + 2);
-            for (int cb = c0; cb < c1; cb += CB) {
+        const bool act = b < a.B && ok;
+        {
+            const float* P = a.apart + ((size_t)((b < a.B ? b : 0) * n_sel + s) * ns) * (dh + 2);
+            for (int cb = c0; cb < c1; cb += CB) {     // uniform over the wave
                 float mc[CB], lc[CB], ac[CB];
 #pragma unroll
                 for (int i = 0; i < CB; ++i) {
@@ -93,6 +98,13 @@ __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, 
                     lc[i] = in ? pc[dh + 1] : 0.f;
                     ac[i] = pc[e];
                 }
+                if (!issued) {
+                    issued = true;
+                    asm volatile("" ::: "memory");
+                    after_loads();
+                    asm volatile("" ::: "memory");
+                }
+                if (!act) continue;
 #pragma unroll
                 for (int i = 0; i < CB; ++i) {
                     if (!(lc[i] > 0.f)) continue;
@@ -103,6 +115,10 @@ __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, 
                     m = M;
                 }
             }
+        }
+        if (!issued) {                                 // a wave without splits
+            issued = true;
+            after_loads();
         }
         s_q[q][t][b][0] = m;
         s_q[q][t][b][1] = l;
@@ -207,19 +223,12 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     }
     __syncthreads();
 
-    // ---- the coefficients of the output projection first: the split-K
-    // partials are L2-resident, and their loads would otherwise queue
-    // behind the row stream
-    if (ATTN) {
-        attn_coef<NQ>(a, r0, nlive, s_cf, s_q);
-        __syncthreads();
-    }
-
     // ---- this wave's rows wv, wv + 4, ...: for the output projection the
-    // first PF now, each later one issued after the FMAs of the row PF
-    // before it (a wave's loads go out only as fast as HBM drains them;
-    // issuing them all first would leave the FMAs as a tail).  fc2, with
-    // its coefficients already in LDS, measured faster with every row
+    // first PF go out right behind the split-K partials' loads (which are
+    // L2-resident and return first), each later one after the FMAs of the
+    // row PF before it (a wave's loads go out only as fast as HBM drains
+    // them; issuing them all first would leave the FMAs as a tail).  fc2,
+    // with its coefficients already in LDS, measured faster with every row
     // issued first.
     constexpr int kAxpyPF = ATTN ? 8 : kAxpyU;
     u32x4 w[kAxpyU];
@@ -228,8 +237,16 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
         const int rr = k < nlive ? s_row[k] : -1;
         w[t] = (rr >= 0 && colok) ? ld16_stream(W + (size_t)rr * a.d + col) : u32x4{0u, 0u, 0u, 0u};
     };
+    auto first_rows = [&]() {
 #pragma unroll
-    for (int t = 0; t < kAxpyPF; ++t) load_row(t);
+        for (int t = 0; t < kAxpyPF; ++t) load_row(t);
+    };
+    if (ATTN) {
+        attn_coef<NQ>(a, r0, nlive, s_cf, s_q, first_rows);
+        __syncthreads();
+    } else {
+        first_rows();
+    }
 
     float acc[NB][E];
 #pragma unroll
