@@ -201,12 +201,17 @@ def _attn_setup(d, h, dh, max_len, n_filled, seed, wdt="f16", B=1):
     return W, K, V
 
 
-@pytest.mark.parametrize("dh", [64, 128])
-def test_qkv_with_holes_over_steps(dvlib, dh):
-    d, h, L, n0, T, B = 512, 8, 48, 10, 9, 2
-    W, K, V = _attn_setup(d, h, dh, L, n0, seed=dh, B=B)
-    X = synth.layer_inputs(d, T, B, seed=dh)
-    g = np.random.default_rng(dh)
+@pytest.mark.parametrize("B,h,dh", [(2, 8, 64), (2, 8, 128), (1, 8, 64), (1, 8, 128), (1, 80, 64)])
+def test_qkv_with_holes_over_steps(dvlib, B, h, dh):
+    """Missing K/V positions recomputed from the stored inputs (DejaVu §4.2):
+    batch rows of two (each row its own holes), and a batch of one, where
+    helper workgroups take the rounds past the first (more items than
+    helpers when every head has a long gap; with 80 heads, 40 selected
+    and then all 80, past the helpers' 64-head limit)."""
+    d, L, n0, T = 512, 48, 10, 9
+    W, K, V = _attn_setup(d, h, dh, L, n0, seed=dh + h + B, B=B)
+    X = synth.layer_inputs(d, T, B, seed=dh + B)
+    g = np.random.default_rng(dh + h)
     # oracle state
     okv = ref.KVState(K.copy(), V.copy(), np.zeros((B, L, d)), np.full((B, h), n0 - 1))
     # device state
@@ -219,11 +224,14 @@ def test_qkv_with_holes_over_steps(dvlib, dh):
         pos = n0 + t
         if t == T - 1:
             sel = np.arange(h, dtype=np.int32)             # every head: holes of up to 8 steps
+        elif t == T - 2 and h > 64:
+            sel = np.sort(g.choice(h, 40, replace=False)).astype(np.int32)
         else:
             sel = np.sort(g.choice(h, 3, replace=False)).astype(np.int32)
+        sel_d, x_d = dev(sel), dev(X[t])
         q = torch.empty(B, len(sel), dh, device="cuda")
         kv = dvlib.kv_state(Kd, Vd, pos, yb, vu)
-        dvlib.dv_sparse_attn_proj(dvlib.DV_PROJ_QKV, h, dh, dev(sel), len(sel), wq, bq, dev(X[t]), q, ws, kv=kv)
+        dvlib.dv_sparse_attn_proj(dvlib.DV_PROJ_QKV, h, dh, sel_d, len(sel), wq, bq, x_d, q, ws, kv=kv)
         wq_ = ref.qkv_step(X[t], W["w_qkv_t"], W["b_qkv"], sel, okv, pos)
         check_close(host(q), wq_, "f16", f"q step {t}")
     assert np.array_equal(host(vu), okv.valid_upto)
