@@ -323,6 +323,17 @@ __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ pa
     const int n4 = d / 4;
     const int per = (n_groups + NW - 1) / NW;
     const int g0 = q * per, g1 = min(n_groups, g0 + per);
+    // wave 0's bias and residual go out first, beside the partials, rather
+    // than one more round trip after the reduction
+    f32x4 bv = f32x4{0.f, 0.f, 0.f, 0.f}, rv = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (q == 0 && c4 < n4) {
+        if (bias) {
+            const T* bb = (const T*)bias + (size_t)c4 * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = to_f32(bb[e]);
+        }
+        if (residual) rv = reinterpret_cast<const f32x4*>(residual + (size_t)b * d)[c4];
+    }
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c4 < n4) {
         for (int gb = g0; gb < g1; gb += MAXQ) {
@@ -340,12 +351,8 @@ __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ pa
     if (q == 0 && c4 < n4) {
 #pragma unroll
         for (int w = 0; w < NW - 1; ++w) s = s + red[w][threadIdx.x];
-        if (bias) {
-            const T* bb = (const T*)bias + (size_t)c4 * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] += to_f32(bb[e]);
-        }
-        if (residual) s += reinterpret_cast<const f32x4*>(residual + (size_t)b * d)[c4];
+        if (bias) s += bv;
+        if (residual) s += rv;
         reinterpret_cast<f32x4*>(out + (size_t)b * d)[c4] = s;
     }
     if (advance && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *advance += 1;
