@@ -44,6 +44,9 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         stage_dma<NT>(ys + a.d, ln.g, a.d);
         stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
     }
+    float bias[RR];                                  // fc1's bias now, ahead of the rows, not one more trip at the end
+#pragma unroll
+    for (int r = 0; r < RR; ++r) bias[r] = OP == ROW_FC1 && j[r] >= 0 ? to_f32(((const T*)a.bias)[j[r]]) : 0.f;
     issue_order_fence();
     // With several rows per wave, the first PF chunks of every row now and
     // the rest one chunk ahead of the dot products (a wave's loads go out
@@ -106,7 +109,7 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         const int u = u0 + r;
         if (u >= a.n_max) break;
         float v = wave_sum(j[r] >= 0 ? acc[r] : 0.f);
-        if (OP == ROW_FC1) v = j[r] >= 0 ? fmaxf(v + to_f32(((const T*)a.bias)[j[r]]), 0.f) : 0.f;
+        if (OP == ROW_FC1) v = j[r] >= 0 ? fmaxf(v + bias[r], 0.f) : 0.f;
         if ((threadIdx.x & 63) == 0) a.out[u] = v;
     }
 }
