@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     }
     if constexpr (NB == 1 && HB > 0 && YL) {
         if (qb >= a.qkv_blocks) {                      // a hole helper
-            qkv_hole_items<T, CH, qkv_hole_rows(R), HB, HB + 1>(a, qb - a.qkv_blocks, ys);
+            qkv_hole_items<T, CH, qkv_hole_rows(R), HB, HB>(a, qb - a.qkv_blocks, ys);   // HB positions per item: measured best of 1, 2, 3
             return;
         }
     }
