@@ -24,6 +24,15 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
     const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
     const int u0 = (blk * (NT / kWave) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) * RR;
     const int nchunk = a.d / E;
+    // x straight into LDS first (it depends on nothing), ahead of the row
+    // indices and the rows
+    stage_dma<NT>(ys, ln.x, a.d);
+    if constexpr (GB) {
+        // gamma and beta too: loads retire in issue order, so fetching them
+        // after the rows would hold the LayerNorm until the rows arrive
+        stage_dma<NT>(ys + a.d, ln.g, a.d);
+        stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
+    }
     int j[RR];
     int jany = -1;                                   // a valid row of this wave, re-read in place of invalid ones
 #pragma unroll
@@ -36,13 +45,6 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         }
         j[r] = __builtin_amdgcn_readfirstlane(jj);
         if (j[r] >= 0) jany = j[r];
-    }
-    stage_dma<NT>(ys, ln.x, a.d);                    // x straight into LDS, ahead of the rows
-    if constexpr (GB) {
-        // gamma and beta too: loads retire in issue order, so fetching them
-        // after the rows would hold the LayerNorm until the rows arrive
-        stage_dma<NT>(ys + a.d, ln.g, a.d);
-        stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
     }
     float bias[RR];                                  // fc1's bias now, ahead of the rows, not one more trip at the end
 #pragma unroll
