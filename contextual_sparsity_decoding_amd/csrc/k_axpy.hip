@@ -211,17 +211,27 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
             }
             live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
         }
-        unsigned nl;
-        const unsigned slot = block_excl_scan(live ? 1u : 0u, tot, &nl);
-        nlive = (int)min(nl, (unsigned)kRowsPerGroup);
-        if (live && slot < (unsigned)kRowsPerGroup) {
-            s_row[slot] = row;
+        // the group's rows are wave 0's lanes: a wave scan compacts them, and
+        // the count reaches the other waves through LDS across the barrier
+        static_assert(kRowsPerGroup == kWave, "one row per lane of wave 0");
+        if (threadIdx.x < kWave) {
+            const unsigned lv = live ? 1u : 0u;
+            const unsigned incl = wave_incl_scan(lv);
+            const unsigned nl = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+            if (live) {
+                const unsigned slot = incl - lv;
+                s_row[slot] = row;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) s_cf[slot * NB + b] = cf[b];
+                for (int b = 0; b < NB; ++b) s_cf[slot * NB + b] = cf[b];
+            }
+            if (threadIdx.x == 0) {
+                tot[0] = nl;
+                if (a.rows_read && slice == 0 && nl > 0) atomicAdd(a.rows_read, (int)nl);
+            }
         }
-        if (a.rows_read && slice == 0 && threadIdx.x == 0 && nl > 0) atomicAdd(a.rows_read, (int)nl);
     }
     __syncthreads();
+    if (!ATTN) nlive = (int)tot[0];
 
     // ---- this wave's rows wv, wv + 4, ...: for the output projection the
     // first PF go out right behind the split-K partials' loads (which are
