@@ -1,6 +1,6 @@
-// Top-k of one score row split into three roles, each a few 256-thread
-// workgroups that ride in a launch doing other work; the launches between
-// them order the roles.  Same selection as the top-k kernels (score
+// Top-k of one score row split into three roles that ride as extra
+// workgroups in launches doing other work; the launches between them order
+// the roles.  Same selection as the top-k kernels (score
 // descending, ties to the lower index, NaN after numbers; the set ascending).
 //
 // Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
@@ -10,7 +10,8 @@
 //   1. topk_hist_slice, one workgroup per 1024 scores: stores the scores'
 //      order keys and adds the histogram of their top 12 bits into a global
 //      histogram (cleared earlier).
-//   2. topk_threshold, one workgroup: the k-th key by radix select, the
+//   2. topk_threshold, one workgroup (1024 threads in the finalize that
+//      hosts it): the k-th key by radix select, the
 //      first digit read off that histogram, the next 12 and 8 bits
 //      histogrammed in LDS over the keys still in the running (stopping once
 //      a bin is taken whole); it writes the threshold.
