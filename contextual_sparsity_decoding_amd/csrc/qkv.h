@@ -81,17 +81,17 @@ __device__ __forceinline__ void qkv_dots(const u32x4 (&w)[R][CH], const float* i
 }
 
 // Hole helpers (batch of one, n_sel <= 64): the missing positions of each
-// selected head past the first HB (which its owner workgroups compute beside
-// their on-time dot products) are cut into items of 4*R rows of one K or V
+// selected head past the first FIRST (which its owner workgroups compute
+// beside their on-time dot products) are cut into items of 4*R rows of one K or V
 // block (R rows per wave; a row's sums do not depend on how many rows a wave
-// holds) and up to NV positions.  Helper `hid` takes items hid, hid + nhelp,
+// holds) and up to NV positions.  Helper `hid` takes items hid, hid + hole_blocks,
 // ...: it loads the item's weight rows again (read moments before by their
 // owner) and its stored inputs, and runs the owner's instructions on the
 // same values, so the entries are bit-identical to on-time ones.  The
 // helpers come after every owner in the grid, so they take the CUs the
 // owners leave, and the rounds run side by side instead of one after
 // another in the owner.
-template <typename T, int CH, int R, int HB, int NV>
+template <typename T, int CH, int R, int FIRST, int NV>
 __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float* ys) {
     constexpr int E = Vec<T>::E;
     const int lane = threadIdx.x & 63;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
     const int vu = a.h <= kWave ? __shfl(vu_all, hv ? head : 0, kWave) : (hv ? a.valid_upto[head] : 0);
     if (hv) {
         lo0 = min(max(vu + 1, 0), pos);
-        const int m = pos - lo0 - HB;
+        const int m = pos - lo0 - FIRST;
         nr = m > 0 ? (m + NV - 1) / NV : 0;
     }
     const unsigned cnt = 2u * (unsigned)(nrb * nr);    // items of head s
@@ -126,7 +126,7 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
         const int per = nrb * nrs;                     // items of one of K, V
         const int which = 1 + (int)l / per;
         const int rb = ((int)l % per) / nrs, rnd = ((int)l % per) % nrs;
-        const int p0 = lo + HB + rnd * NV;
+        const int p0 = lo + FIRST + rnd * NV;
         const int np = min(NV, pos - p0);
         const int e0 = rb * 4 * R + wv * R;
         const T* Wb = (const T*)a.w + ((size_t)(which * a.h + hd) * dh + e0) * d;
@@ -190,7 +190,9 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     }
     if constexpr (NB == 1 && HB > 0 && YL) {
         if (qb >= a.qkv_blocks) {                      // a hole helper
-            qkv_hole_items<T, CH, qkv_hole_rows(R), HB, HB>(a, qb - a.qkv_blocks, ys);   // HB positions per item: measured best of 1, 2, 3
+            // the owner computes the first HB missing positions; items of HB
+            // positions measured best of 1, 2 and 3
+            qkv_hole_items<T, CH, qkv_hole_rows(R), HB, HB>(a, qb - a.qkv_blocks, ys);
             return;
         }
     }
