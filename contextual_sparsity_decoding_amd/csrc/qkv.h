@@ -144,7 +144,7 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
         float bv[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) bv[j] = to_f32(((const T*)a.bias)[(size_t)(which * a.h + hd) * dh + e0 + j]);
-        wait_dma_and_sync();
+        sync_after_dma<R * CH>();                      // the inputs have landed; the rows may still be in flight
         float acc[R][NV];
         qkv_dots<T, CH, R, NV>(w, ys, d, nchunk, acc);
         half_t* cache = which == 1 ? a.K : a.V;
