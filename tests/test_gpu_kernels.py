@@ -201,14 +201,18 @@ def _attn_setup(d, h, dh, max_len, n_filled, seed, wdt="f16", B=1):
     return W, K, V
 
 
-@pytest.mark.parametrize("B,h,dh", [(2, 8, 64), (2, 8, 128), (1, 8, 64), (1, 8, 128), (1, 80, 64)])
-def test_qkv_with_holes_over_steps(dvlib, B, h, dh):
+@pytest.mark.parametrize("B,h,dh,full", [(2, 8, 64, False), (2, 8, 128, False), (1, 8, 64, False),
+                                         (1, 8, 128, False), (1, 80, 64, False), (1, 8, 128, True)])
+def test_qkv_with_holes_over_steps(dvlib, B, h, dh, full):
     """Missing K/V positions recomputed from the stored inputs (DejaVu §4.2):
     batch rows of two (each row its own holes), and a batch of one, where
     helper workgroups take the rounds past the first (more items than
     helpers when every head has a long gap; with 80 heads, 40 selected
-    and then all 80, past the helpers' 64-head limit)."""
-    d, L, n0, T = 512, 48, 10, 9
+    and then all 80, past the helpers' 64-head limit).  With `full` the
+    cache holds exactly the positions the steps write (the last step writes
+    slot max_len - 1)."""
+    d, n0, T = 512, 10, 9
+    L = n0 + T if full else 48
     W, K, V = _attn_setup(d, h, dh, L, n0, seed=dh + h + B, B=B)
     X = synth.layer_inputs(d, T, B, seed=dh + B)
     g = np.random.default_rng(dh + h)

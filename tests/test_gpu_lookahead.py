@@ -117,12 +117,12 @@ def test_lookahead_steps_match_oracle(dvlib, aux):
     assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
 
 
-@pytest.mark.parametrize("N,k_m", [(24576, 2400), (1000, 100), (4100, 4100)])
+@pytest.mark.parametrize("N,k_m", [(24576, 2400), (1000, 100), (4100, 4100), (2048, 1)])
 def test_lookahead_selection_shapes(dvlib, N, k_m):
     """The neuron selection of the single-stream schedule at budgets its
     split form does not take (more than 20480 scores; a count that is not a
-    multiple of 4) and at k = n (every neuron kept): the same sets as the
-    oracle either way."""
+    multiple of 4), at k = n (every neuron kept) and at k = 1: the same sets
+    as the oracle either way."""
     dims = LayerDims(d=512, N=N, h=8, d_h=64, r_attn=16, r_mlp=32, wdt="f16")
     n0, T = 12, 2
     A = Ahead(dvlib, dims, n0, n0 + T + 2, seed=47, k_heads=3, k_neurons=k_m)
