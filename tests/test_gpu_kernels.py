@@ -201,17 +201,19 @@ def _attn_setup(d, h, dh, max_len, n_filled, seed, wdt="f16", B=1):
     return W, K, V
 
 
-@pytest.mark.parametrize("B,h,dh,full", [(2, 8, 64, False), (2, 8, 128, False), (1, 8, 64, False),
-                                         (1, 8, 128, False), (1, 80, 64, False), (1, 8, 128, True)])
-def test_qkv_with_holes_over_steps(dvlib, B, h, dh, full):
+@pytest.mark.parametrize("B,h,dh,full,d", [(2, 8, 64, False, 512), (2, 8, 128, False, 512), (1, 8, 64, False, 512),
+                                           (1, 8, 128, False, 512), (1, 80, 64, False, 512), (1, 8, 128, True, 512),
+                                           (1, 8, 128, False, 6144)])
+def test_qkv_with_holes_over_steps(dvlib, B, h, dh, full, d):
     """Missing K/V positions recomputed from the stored inputs (DejaVu §4.2):
     batch rows of two (each row its own holes), and a batch of one, where
     helper workgroups take the rounds past the first (more items than
     helpers when every head has a long gap; with 80 heads, 40 selected
     and then all 80, past the helpers' 64-head limit).  With `full` the
     cache holds exactly the positions the steps write (the last step writes
-    slot max_len - 1)."""
-    d, n0, T = 512, 10, 9
+    slot max_len - 1).  At d = 6144 one stored input fits beside y in LDS:
+    the owner computes one missing position and helpers take one at a time."""
+    n0, T = 10, 9
     L = n0 + T if full else 48
     W, K, V = _attn_setup(d, h, dh, L, n0, seed=dh + h + B, B=B)
     X = synth.layer_inputs(d, T, B, seed=dh + B)
