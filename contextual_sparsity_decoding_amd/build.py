@@ -1,9 +1,11 @@
 """Build libdv.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m contextual_sparsity_decoding_amd.build
+    python -m contextual_sparsity_decoding_amd.build [--changed]
 
 Objects go to _build/ at the repository root; the library lands next to this
-file, where the binding loads it.
+file, where the binding loads it.  build() compiles every source each time;
+--changed recompiles only sources whose object is older than the source or
+one of the headers it includes (from hipcc's dependency files).
 """
 from __future__ import annotations
 
@@ -38,9 +40,29 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _obj(src: str) -> str:
+    return os.path.join(OBJDIR, os.path.basename(src) + ".o")
+
+
+def _stale(src: str) -> bool:
+    """True when the object is missing or older than anything it was built from."""
+    obj, dep = _obj(src), _obj(src) + ".d"
+    if not (os.path.exists(obj) and os.path.exists(dep)):
+        return True
+    t = os.path.getmtime(obj)
+    with open(dep) as f:
+        names = f.read().replace("\\\n", " ").split()
+    for n in names[1:]:
+        if n.endswith(":"):
+            continue
+        if not os.path.exists(n) or os.path.getmtime(n) > t:
+            return True
+    return False
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    obj = _obj(src)
+    cmd = [hipcc(), *FLAGS, "-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -50,11 +72,16 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, changed_only: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    todo = [s for s in srcs if _stale(s)] if changed_only else srcs
+    # the slowest sources first, so the pool's last jobs are short ones
+    todo.sort(key=lambda s: -os.path.getsize(s) - (1 << 20) * ("qkv" in s))
+    if todo:
+        with ThreadPoolExecutor(min(8, len(todo))) as ex:
+            list(ex.map(_compile, todo))
+    objs = [_obj(s) for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,4 +94,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(changed_only="--changed" in sys.argv[1:])

@@ -1,5 +1,5 @@
 // Sparse Q/K/V projections with KV append and hole fill (DejaVu §4.2):
-// entry point and the fp16 instantiation.
+// entry point (the kernel instantiations are in k_qkv_*.hip).
 //
 // Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
 // Inference Time" (arXiv 2310.17157).
@@ -24,8 +24,16 @@ __global__ void k_mark_valid_qkv(const int32_t* __restrict__ head_idx, int n_sel
 namespace dvh {
 using namespace dv;
 
-template dv_status qkv_launch_t<half_t>(const QkvArgs&, int, hipStream_t);
-extern template dv_status qkv_launch_t<float>(const QkvArgs&, int, hipStream_t);
+template <typename T>
+static dv_status qkv_launch_t(const QkvArgs& a, int ch, hipStream_t s) {
+    switch (nb_bucket(a.B)) {
+        case 1: return qkv_go<T, 1>(a, ch, s);
+        case 2: return qkv_go<T, 2>(a, ch, s);
+        case 4: return qkv_go<T, 4>(a, ch, s);
+        case 8: return qkv_go<T, 8>(a, ch, s);
+        default: return qkv_go<T, 16>(a, ch, s);
+    }
+}
 
 bool qkv_supported(int B, int d, int wdt) {
     (void)B;

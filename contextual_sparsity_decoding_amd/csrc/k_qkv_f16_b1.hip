@@ -1,0 +1,6 @@
+// Sparse Q/K/V projection kernels: fp16 weights, batch of one.
+#include "qkv.h"
+
+namespace dvh {
+template dv_status qkv_go<half_t, 1>(const QkvArgs&, int, hipStream_t);
+}  // namespace dvh

@@ -1,5 +1,5 @@
 // Sparse Q/K/V projection kernel and its launch templates (instantiated per
-// weight type in k_qkv.hip and k_qkv_f32.hip).
+// weight type and batch bucket in k_qkv_*.hip).
 //
 // Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
 // Inference Time" (arXiv 2310.17157), §4.2.
@@ -475,8 +475,10 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     return DV_OK;
 }
 
+// One (weight type, batch bucket) per translation unit: the instantiations
+// are spread over several sources so that they compile in parallel.
 template <typename T, int NB>
-static dv_status qkv_go(const QkvArgs& a, int ch, hipStream_t s) {
+dv_status qkv_go(const QkvArgs& a, int ch, hipStream_t s) {
     switch (ch) {
         case 4: return qkv_go3<T, NB, 4, 4>(a, s);
         case 8: return qkv_go3<T, NB, 8, 4>(a, s);
@@ -489,15 +491,10 @@ static dv_status qkv_go(const QkvArgs& a, int ch, hipStream_t s) {
     }
 }
 
-template <typename T>
-dv_status qkv_launch_t(const QkvArgs& a, int ch, hipStream_t s) {
-    switch (nb_bucket(a.B)) {
-        case 1: return qkv_go<T, 1>(a, ch, s);
-        case 2: return qkv_go<T, 2>(a, ch, s);
-        case 4: return qkv_go<T, 4>(a, ch, s);
-        case 8: return qkv_go<T, 8>(a, ch, s);
-        default: return qkv_go<T, 16>(a, ch, s);
-    }
-}
+#define DV_QKV_EXTERN(T, NB) extern template dv_status qkv_go<T, NB>(const QkvArgs&, int, hipStream_t);
+DV_QKV_EXTERN(half_t, 1) DV_QKV_EXTERN(half_t, 2) DV_QKV_EXTERN(half_t, 4) DV_QKV_EXTERN(half_t, 8)
+DV_QKV_EXTERN(half_t, 16) DV_QKV_EXTERN(float, 1) DV_QKV_EXTERN(float, 2) DV_QKV_EXTERN(float, 4)
+DV_QKV_EXTERN(float, 8) DV_QKV_EXTERN(float, 16)
+#undef DV_QKV_EXTERN
 
 }  // namespace dvh
