@@ -22,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdv.so")
+SYNTH_SRC = os.path.join(PKG, "synth_philox.c")
+SYNTH_LIB = os.path.join(PKG, "libsynth.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -72,7 +74,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_synth(verbose: bool = True) -> str:
+    """The host side of the seeded input generator (plain C, gcc, OpenMP)."""
+    tmp = SYNTH_LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-Wall", SYNTH_SRC, "-o", tmp, "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {SYNTH_SRC}:\n{r.stderr}")
+    os.replace(tmp, SYNTH_LIB)
+    if verbose:
+        print(f"built {SYNTH_LIB}")
+    return SYNTH_LIB
+
+
 def build(verbose: bool = True, changed_only: bool = False) -> str:
+    if not changed_only or not os.path.exists(SYNTH_LIB) or os.path.getmtime(SYNTH_LIB) < os.path.getmtime(SYNTH_SRC):
+        build_synth(verbose)
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     todo = [s for s in srcs if _stale(s)] if changed_only else srcs

@@ -26,6 +26,25 @@ dv_status fail(dv_status code, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
+// dv_time_launches state (per host thread)
+struct LaunchTiming {
+    int kind = 0;
+    hipEvent_t* ev = nullptr;
+    int n = 0, used = 0;
+};
+static thread_local LaunchTiming g_timing;
+
+void timed_begin(int kind, hipStream_t s) {
+    if (kind != 0 && kind == g_timing.kind && g_timing.used + 2 <= g_timing.n)
+        (void)hipEventRecord(g_timing.ev[g_timing.used], s);
+}
+void timed_end(int kind, hipStream_t s) {
+    if (kind != 0 && kind == g_timing.kind && g_timing.used + 2 <= g_timing.n) {
+        (void)hipEventRecord(g_timing.ev[g_timing.used + 1], s);
+        g_timing.used += 2;
+    }
+}
+
 int elt_bytes(int wdt) { return wdt == DV_F16 ? 2 : 4; }
 
 static bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -416,10 +435,8 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
 // given sets, either on the auxiliary stream or riding as extra workgroups
 // in this layer's launches.  LN1 is folded into the Q/K/V kernel and LN2 into
 // fc1, so the layer itself runs seven kernels.
-static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
-                                  const dv_kv_view& view, const LayerWs& L, const float* x_in, float* x_out, void* ws,
-                                  hipStream_t s) {
-    const int d = c->d, h = c->h, dh = c->d_h, N = c->N;
+// Arguments of the look-ahead form (checked before anything is enqueued).
+static dv_status check_lookahead(const dv_decode_cfg* c, const dv_layer_state* st) {
     const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
     REQ(dense_a || st->head_idx_in, DV_ERR_NULL, "dv_decode_layer: DV_LOOKAHEAD needs head_idx_in");
     REQ(dense_m || st->neuron_idx_in, DV_ERR_NULL, "dv_decode_layer: DV_LOOKAHEAD needs neuron_idx_in");
@@ -431,6 +448,65 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     REQ(!st->next_pa1_t || (a16(st->next_pa1_t) && a16(st->next_pa2_t)), DV_ERR_ALIGN, "dv_decode_layer: next_pa alignment");
     REQ(!st->next_pm1_t || (a16(st->next_pm1_t) && a16(st->next_pm2_t)), DV_ERR_ALIGN, "dv_decode_layer: next_pm alignment");
     REQ(!st->aux_stream || (st->ev_fork && st->ev_join), DV_ERR_NULL, "dv_decode_layer: aux_stream needs ev_fork and ev_join");
+    // the next sets are written while this layer's launches still read the
+    // given ones: they must be separate buffers
+    {
+        const size_t hb = (size_t)(c->k_heads > 0 ? c->k_heads : 1) * 4, nb = (size_t)(c->k_neurons > 0 ? c->k_neurons : 1) * 4;
+        const void* hin = dense_a ? nullptr : st->head_idx_in;
+        const void* nin = dense_m ? nullptr : st->neuron_idx_in;
+        const void* hout = st->next_pa1_t ? st->next_head_idx : nullptr;
+        const void* nout = st->next_pm1_t ? st->next_neuron_idx : nullptr;
+        REQ(!overlap(hout, hb, hin, hb) && !overlap(hout, hb, nin, nb) && !overlap(nout, nb, hin, hb) &&
+                !overlap(nout, nb, nin, nb) && !overlap(hout, hb, nout, nb),
+            DV_ERR_RANGE, "dv_decode_layer: next_head_idx / next_neuron_idx overlap the given sets or each other");
+    }
+    return DV_OK;
+}
+
+// The sets of one layer predicted from LN1(x) by the given predictors, in
+// launches of their own (the look-ahead form's predictions when they do not
+// ride in a layer's launches, and the first layer of a stack).
+static dv_status predict_sets(const dv_decode_cfg* c, const float* x, const float* g, const float* b,
+                              const void* pa1, const void* pa2, int32_t* head_idx, const void* pm1, const void* pm2,
+                              int32_t* neuron_idx, const LayerWs& L, hipStream_t s) {
+    const int d = c->d, h = c->h, N = c->N;
+    const bool pair = pa1 && pm1 && c->k_heads > 0 && c->k_neurons > 0 && row_ln_supported(d, c->wdt) &&
+                      pred_topk_fusable(1, h, c->r_attn);
+    if (pair) {
+        TRY(launch_predict_pair_ln(x, d, g, b, c->eps, L.ya, pa1, c->r_attn, pa2, h, c->k_heads, head_idx, pm1, c->r_mlp,
+                                   pm2, N, L.sA2, L.sM2, L.hpartA, c->wdt, c->pred_act, s));
+        return launch_topk(L.sM2, 1, N, c->k_neurons, neuron_idx, s);
+    }
+    if (pa1 && c->k_heads > 0) {
+        if (pred_topk_fusable(1, h, c->r_attn)) {
+            TRY(launch_predict_ln_topk(x, d, g, b, c->eps, L.ya, pa1, c->r_attn, pa2, h, c->wdt, c->pred_act, L.sA2,
+                                       L.hpartA, c->k_heads, head_idx, s));
+        } else {
+            TRY(launch_predict_ln(x, 1, d, g, b, c->eps, L.ya, pa1, c->r_attn, pa2, h, c->wdt, c->pred_act, L.sA2,
+                                  L.hpartA, s));
+            TRY(launch_topk(L.sA2, 1, h, c->k_heads, head_idx, s));
+        }
+    }
+    if (pm1 && c->k_neurons > 0) {
+        TRY(launch_predict_ln(x, 1, d, g, b, c->eps, L.ya, pm1, c->r_mlp, pm2, N, c->wdt, c->pred_act, L.sM2, L.hpartM, s));
+        TRY(launch_topk(L.sM2, 1, N, c->k_neurons, neuron_idx, s));
+    }
+    return DV_OK;
+}
+
+// Whether a look-ahead layer of a stack lacks a predictor its next layer needs.
+static bool next_layer_predictors_missing(const dv_layer_state& st, const dv_decode_cfg* c, bool has_next) {
+    if (!has_next) return false;
+    const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
+    return (!dense_a && c->k_heads > 0 && !(st.next_pa1_t && st.next_pa2_t)) ||
+           (!dense_m && c->k_neurons > 0 && !(st.next_pm1_t && st.next_pm2_t));
+}
+
+static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                                  const dv_kv_view& view, const LayerWs& L, const float* x_in, float* x_out, void* ws,
+                                  hipStream_t s) {
+    const int d = c->d, h = c->h, dh = c->d_h, N = c->N;
+    const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
     const bool predict = st->next_pa1_t || st->next_pm1_t;
     hipStream_t ps = st->aux_stream ? (hipStream_t)st->aux_stream : s;
     const bool pair = st->next_pa1_t && st->next_pm1_t && c->k_heads > 0 && c->k_neurons > 0 &&
@@ -448,28 +524,9 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         HIP_TRY(hipStreamWaitEvent(ps, (hipEvent_t)st->ev_fork, 0));
     }
     // ---- the next layer's sets from this layer's y (predictor layers fold LN1 in)
-    if (pair && !ride) {
-        TRY(launch_predict_pair_ln(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn, st->next_pa2_t,
-                                   h, c->k_heads, st->next_head_idx, st->next_pm1_t, c->r_mlp, st->next_pm2_t, N, L.sA2,
-                                   L.sM2, L.hpartA, c->wdt, c->pred_act, ps));
-        TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, ps));
-    }
-    if (!pair && st->next_pa1_t && c->k_heads > 0) {
-        if (pred_topk_fusable(1, h, c->r_attn)) {
-            TRY(launch_predict_ln_topk(x_in, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn,
-                                       st->next_pa2_t, h, c->wdt, c->pred_act, L.sA2, L.hpartA, c->k_heads,
-                                       st->next_head_idx, ps));
-        } else {
-            TRY(launch_predict_ln(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pa1_t, c->r_attn,
-                                  st->next_pa2_t, h, c->wdt, c->pred_act, L.sA2, L.hpartA, ps));
-            TRY(launch_topk(L.sA2, 1, h, c->k_heads, st->next_head_idx, ps));
-        }
-    }
-    if (!pair && st->next_pm1_t && c->k_neurons > 0) {
-        TRY(launch_predict_ln(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.ya, st->next_pm1_t, c->r_mlp, st->next_pm2_t,
-                              N, c->wdt, c->pred_act, L.sM2, L.hpartM, ps));
-        TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, ps));
-    }
+    if (!ride && predict)
+        TRY(predict_sets(c, x_in, w->ln1_g, w->ln1_b, st->next_pa1_t, st->next_pa2_t, st->next_head_idx, st->next_pm1_t,
+                         st->next_pm2_t, st->next_neuron_idx, L, ps));
     if (predict && st->aux_stream) HIP_TRY(hipEventRecord((hipEvent_t)st->ev_join, ps));
 
     // ---- this layer with its given sets
@@ -487,18 +544,24 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         p1.n_max = c->r_attn + c->r_mlp; p1.w_rows = p1.n_max; p1.out = L.hpartA;
     }
     if (ln_fusable(1, d)) {
+        timed_begin(DV_KERNEL_QKV, s);
         TRY(launch_qkv(x_in, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s, w->ln1_g,
                        w->ln1_b, c->eps, ride ? &p1 : nullptr));
+        timed_end(DV_KERNEL_QKV, s);
     } else {
         TRY(launch_layernorm(x_in, 1, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+        timed_begin(DV_KERNEL_QKV, s);
         TRY(launch_qkv(L.y, 1, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
+        timed_end(DV_KERNEL_QKV, s);
     }
     int splits = 0;
     Pred2Args p2 = pred2_args(L.hpartA, c->r_attn, st->next_pa2_t, h, L.sA2, c->k_heads, st->next_head_idx,
                               L.hpartA + c->r_attn, c->r_mlp, st->next_pm2_t, N, L.sM2, c->pred_act, c->wdt);
     p2.zero = ride_topk ? L.khist : nullptr;
+    timed_begin(DV_KERNEL_ATTN, s);
     TRY(launch_splitk(L.q, 1, dh, head_idx, n_sel, &view, st->kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
                       fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits, ride ? &p2 : nullptr));
+    timed_end(DV_KERNEL_ATTN, s);
     if (ride && !ride_topk) TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, s));
     const TopkSel tk{L.sM2, N, c->k_neurons, L.khist, L.kkeys, L.kthr, st->next_neuron_idx};
     {
@@ -507,15 +570,20 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = 1; ac.bias = w->b_o; ac.residual = x_in;
         ac.out = L.hres; ac.partial = L.xpart;
         ac.sel = ride_topk ? &tk : nullptr;
+        ac.timed = DV_KERNEL_OUT;
         TRY(launch_axpy(ac, s));
     }
     const int32_t* idx = dense_m ? nullptr : st->neuron_idx_in;
     const int n_max = dense_m ? N : c->k_neurons;
     if (row_ln_supported(d, c->wdt)) {
+        timed_begin(DV_KERNEL_FC1, s);
         TRY(launch_fc1_ln(L.hres, d, w->ln2_g, w->ln2_b, c->eps, w->w1_t, w->b1, c->wdt, idx, n_max, nullptr, N, L.a, s));
+        timed_end(DV_KERNEL_FC1, s);
     } else {
         TRY(launch_layernorm(L.hres, 1, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
+        timed_begin(DV_KERNEL_FC1, s);
         TRY(launch_fc1(L.y2, 1, d, w->w1_t, w->b1, c->wdt, idx, n_max, nullptr, N, L.a, s));
+        timed_end(DV_KERNEL_FC1, s);
     }
     AxpyCall mc{};
     mc.w = w->w2_t; mc.wdt = c->wdt; mc.d = d; mc.w_rows = N; mc.rows = n_max; mc.idx = idx; mc.blk = 1; mc.coef = L.a;
@@ -523,6 +591,7 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     mc.residual = L.hres; mc.out = x_out; mc.rows_read = st->fc2_rows_out; mc.partial = L.xpart;
     mc.advance = (c->flags & DV_ADVANCE_POS) ? st->kv.pos_dev : nullptr;
     mc.sel = ride_topk ? &tk : nullptr;
+    mc.timed = DV_KERNEL_FC2;
     TRY(launch_axpy(mc, s));
     if (predict && st->aux_stream) HIP_TRY(hipStreamWaitEvent(s, (hipEvent_t)st->ev_join, 0));
     (void)ws;
@@ -534,10 +603,20 @@ size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len) {
     return layer_ws(nullptr, cfg, max_len).bytes;
 }
 
+static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                            const float* x_in, float* x_out, void* ws, size_t ws_bytes, hipStream_t s, bool run = true);
+
 dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
                           const float* x_in, float* x_out, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     TRY(check_cfg(c));
+    return decode_one(w, c, st, x_in, x_out, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// One layer step: every argument is checked first; with run false nothing
+// is launched (a stack checks all its layers before enqueueing any).
+static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                            const float* x_in, float* x_out, void* ws, size_t ws_bytes, hipStream_t s, bool run) {
     REQ(w && st && x_in && x_out, DV_ERR_NULL, "dv_decode_layer: NULL pointer");
     REQ(w->ln1_g && w->ln1_b && w->ln2_g && w->ln2_b && w->w_qkv_t && w->b_qkv && w->w_o_t && w->b_o && w->w1_t &&
             w->b1 && w->w2_t && w->b2,
@@ -569,8 +648,9 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     }
     const LayerWs L = layer_ws(ws, c, kv.max_len);
     REQ(ws && ws_bytes >= L.bytes, DV_ERR_WORKSPACE, "dv_decode_layer: workspace %zu < %zu", ws_bytes, L.bytes);
+    if (ahead) TRY(check_lookahead(c, st));
+    if (!run) return DV_OK;
 
-    hipStream_t s = (hipStream_t)stream;
     if (ahead) return decode_lookahead(w, c, st, view, L, x_in, x_out, ws, s);
     const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N;
     // attention block: LN1 folded into the head predictor when heads are selected
@@ -600,16 +680,20 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
         kvs.valid_upto = nullptr;
     }
     const bool fill = kvs.y_buf && kvs.valid_upto;
+    timed_begin(DV_KERNEL_QKV, s);
     TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
+    timed_end(DV_KERNEL_QKV, s);
     // split-K partials go straight into the output projection, which merges them per row
     int splits = 0;
+    timed_begin(DV_KERNEL_ATTN, s);
     TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
                       fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s, &splits));
+    timed_end(DV_KERNEL_ATTN, s);
     {
         AxpyCall ac{};
         ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;
         ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = B; ac.bias = w->b_o; ac.residual = x_in;
-        ac.out = L.hres; ac.partial = L.xpart;
+        ac.out = L.hres; ac.partial = L.xpart; ac.timed = DV_KERNEL_OUT;
         TRY(launch_axpy(ac, s));
     }
     // MLP block: LN2 folded into the neuron predictor
@@ -637,13 +721,171 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* c, con
     } else {
         TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
     }
+    timed_begin(DV_KERNEL_FC1, s);
     TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
+    timed_end(DV_KERNEL_FC1, s);
     AxpyCall mc{};
     mc.w = w->w2_t; mc.wdt = c->wdt; mc.d = d; mc.w_rows = N; mc.rows = n_max; mc.n_rows_dev = n_dev; mc.idx = idx;
     mc.blk = 1; mc.coef = L.a; mc.coef_stride = n_max; mc.skip_zero = (c->flags & DV_SKIP_NONPOS_FC2) != 0; mc.B = B;
     mc.bias = w->b2; mc.residual = L.hres; mc.out = x_out; mc.rows_read = st->fc2_rows_out; mc.partial = L.xpart;
     mc.advance = (c->flags & DV_ADVANCE_POS) ? kv.pos_dev : nullptr;
+    mc.timed = DV_KERNEL_FC2;
     return launch_axpy(mc, s);
+}
+
+// ---------------------------------------------------------------- the stack --
+size_t dv_stack_workspace_bytes(const dv_decode_cfg* cfg, int max_len) {
+    if (check_cfg(cfg) != DV_OK || max_len < 1) return 0;
+    return layer_ws(nullptr, cfg, max_len).bytes + align_up((size_t)2 * cfg->B * cfg->d * sizeof(float), 256);
+}
+
+dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_decode_cfg* c, int32_t* head_sets,
+                          int32_t* neuron_sets, int32_t* neuron_counts, int32_t* fc2_rows, const float* x_in,
+                          float* x_out, float* x_trace, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    TRY(check_cfg(c));
+    REQ(layers && x_in && x_out, DV_ERR_NULL, "dv_decode_stack: NULL pointer");
+    REQ(n_layers >= 1 && n_layers <= 65536, DV_ERR_SHAPE, "dv_decode_stack: n_layers=%d", n_layers);
+    const bool ahead = (c->flags & DV_LOOKAHEAD) != 0;
+    const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
+    REQ(!ahead || dense_a || head_sets, DV_ERR_NULL, "dv_decode_stack: DV_LOOKAHEAD needs head_sets");
+    REQ(!ahead || dense_m || neuron_sets, DV_ERR_NULL, "dv_decode_stack: DV_LOOKAHEAD needs neuron_sets");
+    const size_t act = (size_t)c->B * c->d * sizeof(float);
+    REQ(!overlap(x_out, act, x_in, act), DV_ERR_RANGE, "dv_decode_stack: x_out overlaps x_in");
+    REQ(!overlap(x_trace, act * (n_layers - 1), x_in, act) && !overlap(x_trace, act * (n_layers - 1), x_out, act),
+        DV_ERR_RANGE, "dv_decode_stack: x_trace overlaps x_in or x_out");
+    int max_len = 1;
+    for (int l = 0; l < n_layers; ++l) max_len = layers[l].kv.max_len > max_len ? layers[l].kv.max_len : max_len;
+    const size_t lw = layer_ws(nullptr, c, max_len).bytes;
+    const size_t need = lw + align_up(2 * act, 256);
+    REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_decode_stack: workspace %zu < %zu", ws_bytes, need);
+    float* xb[2] = {(float*)((char*)ws + lw), (float*)((char*)ws + lw) + (size_t)c->B * c->d};
+    // the output of layer l (l < n_layers - 1): x_trace row l, else a ping-pong buffer
+    auto out_of = [&](int l) -> float* {
+        if (l == n_layers - 1) return x_out;
+        return x_trace ? x_trace + (size_t)l * c->B * c->d : xb[l & 1];
+    };
+    const int kA = c->k_heads, nmax = layer_nmax(c);
+    hipStream_t s = (hipStream_t)stream;
+
+    // every layer's state, checked before anything is enqueued
+    auto state = [&](int l, dv_layer_state& st, dv_decode_cfg& cl) {
+        const dv_stack_layer& ly = layers[l];
+        st = dv_layer_state{};
+        st.kv = ly.kv;
+        st.sel_idx = ly.sel_idx; st.sel_len = ly.sel_len; st.sel_cap = ly.sel_cap; st.sel_end = ly.sel_end;
+        st.fc2_rows_out = fc2_rows;
+        cl = *c;
+        // a decode position shared by several layers moves on in the last of them
+        for (int m = l + 1; m < n_layers; ++m)
+            if (layers[m].kv.pos_dev == ly.kv.pos_dev) cl.flags &= ~(unsigned)DV_ADVANCE_POS;
+        if (ahead) {
+            if (!dense_a) st.head_idx_in = head_sets + (size_t)l * kA;
+            if (!dense_m) st.neuron_idx_in = neuron_sets + (size_t)l * nmax;
+            if (l + 1 < n_layers) {
+                const dv_layer_weights& wn = layers[l + 1].w;
+                if (!dense_a && kA > 0) {
+                    st.next_pa1_t = wn.pa1_t; st.next_pa2_t = wn.pa2_t;
+                    st.next_head_idx = head_sets + (size_t)(l + 1) * kA;
+                }
+                if (!dense_m && c->k_neurons > 0) {
+                    st.next_pm1_t = wn.pm1_t; st.next_pm2_t = wn.pm2_t;
+                    st.next_neuron_idx = neuron_sets + (size_t)(l + 1) * nmax;
+                }
+            }
+        } else {
+            if (!dense_a && head_sets) st.head_idx_out = head_sets + (size_t)l * kA;
+            if (!dense_m && neuron_sets) st.neuron_idx_out = neuron_sets + (size_t)l * nmax;
+            if (!dense_m && neuron_counts) st.neuron_count_out = neuron_counts + l;
+        }
+    };
+    for (int l = 0; l < n_layers; ++l) {
+        dv_layer_state st;
+        dv_decode_cfg cl;
+        state(l, st, cl);
+        const float* xi = l == 0 ? x_in : out_of(l - 1);
+        float* xo = out_of(l);
+        const dv_status r = decode_one(&layers[l].w, &cl, &st, xi, xo, ws, lw, s, false);
+        if (r != DV_OK) {
+            char msg[512];
+            snprintf(msg, sizeof msg, "%s", dv_last_error());
+            return fail(r, "dv_decode_stack: layer %d: %s", l, msg);
+        }
+        if (ahead && next_layer_predictors_missing(st, c, l + 1 < n_layers))
+            return fail(DV_ERR_NULL, "dv_decode_stack: layer %d: predictor of the next layer NULL", l + 1);
+    }
+    if (ahead) {   // the first layer's sets from its own predictors on LN1(x)
+        const dv_layer_weights& w0 = layers[0].w;
+        REQ(dense_a || kA == 0 || (w0.pa1_t && w0.pa2_t), DV_ERR_NULL, "dv_decode_stack: layer 0 head predictor NULL");
+        REQ(dense_m || c->k_neurons == 0 || (w0.pm1_t && w0.pm2_t), DV_ERR_NULL, "dv_decode_stack: layer 0 neuron predictor NULL");
+        const LayerWs L0 = layer_ws(ws, c, max_len);
+        TRY(predict_sets(c, x_in, w0.ln1_g, w0.ln1_b, dense_a ? nullptr : w0.pa1_t, w0.pa2_t, head_sets,
+                         dense_m ? nullptr : w0.pm1_t, w0.pm2_t, neuron_sets, L0, s));
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        dv_layer_state st;
+        dv_decode_cfg cl;
+        state(l, st, cl);
+        const float* xi = l == 0 ? x_in : out_of(l - 1);
+        float* xo = out_of(l);
+        TRY(decode_one(&layers[l].w, &cl, &st, xi, xo, ws, lw, s, true));
+    }
+    return DV_OK;
+}
+
+// ---------------------------------------------------------------- launch timing --
+dv_status dv_time_launches(int kernel, void** events, int n_events) {
+    clear_error();
+    REQ(kernel >= 0 && kernel <= DV_KERNEL_FC2, DV_ERR_DTYPE, "dv_time_launches: kernel %d", kernel);
+    REQ(kernel == 0 || (events && n_events >= 2), DV_ERR_NULL, "dv_time_launches: events");
+    g_timing.kind = kernel;
+    g_timing.ev = kernel ? (hipEvent_t*)events : nullptr;
+    g_timing.n = kernel ? n_events : 0;
+    g_timing.used = 0;
+    return DV_OK;
+}
+
+int dv_launch_events_used(void) { return g_timing.used; }
+
+// ---------------------------------------------------------------- generator --
+dv_status dv_fill_normal(void* out, uint64_t n, int dtype, uint64_t seed, uint64_t stream, uint64_t offset, float mean,
+                         float stdv, void* hip_stream) {
+    clear_error();
+    REQ(n == 0 || out, DV_ERR_NULL, "dv_fill_normal: NULL pointer");
+    REQ(dtype == DV_F32 || dtype == DV_F16 || dtype == DV_U32, DV_ERR_DTYPE, "dv_fill_normal: dtype %d", dtype);
+    REQ(isfinite(mean) && isfinite(stdv), DV_ERR_RANGE, "dv_fill_normal: mean/std");
+    REQ(offset <= UINT64_MAX - n - 4, DV_ERR_RANGE, "dv_fill_normal: offset + n overflows");
+    REQ(((uintptr_t)out & 15u) == 0, DV_ERR_ALIGN, "dv_fill_normal: out must be 16-byte aligned");
+    return launch_fill_normal(out, n, dtype, seed, stream, offset, mean, stdv, (hipStream_t)hip_stream);
+}
+
+// ---------------------------------------------------------------- byte account --
+dv_status dv_bytes_read(const dv_decode_cfg* c, double n_att, double fc2_rows, double holes, dv_bytes* out) {
+    clear_error();
+    TRY(check_cfg(c));
+    REQ(out, DV_ERR_NULL, "dv_bytes_read: out NULL");
+    REQ(n_att >= 0 && fc2_rows >= 0 && holes >= 0, DV_ERR_RANGE, "dv_bytes_read: negative count");
+    const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
+    const double B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N, wb = elt_bytes(c->wdt);
+    const double kA = dense_a ? h : c->k_heads, kM = dense_m ? N : c->k_neurons;
+    const double a = 4.0 * d * B;                     // one fp32 activation vector per batch row
+    dv_bytes r{};
+    r.head_pred = dense_a ? 0.0 : (c->r_attn * d + h * c->r_attn) * wb;
+    r.neuron_pred = dense_m ? 0.0 : (c->r_mlp * d + N * c->r_mlp) * wb;
+    r.qkv = (3.0 * kA * dh * d + 3.0 * kA * dh) * wb;
+    r.out_proj = (kA * dh * d + d) * wb;
+    r.fc1 = (kM * d + kM) * wb;
+    r.fc2 = (fc2_rows * d + d) * wb;
+    r.weights = r.head_pred + r.neuron_pred + r.qkv + r.out_proj + r.fc1 + r.fc2;
+    r.kv_read = 2.0 * 2.0 * kA * n_att * dh * B;
+    r.kv_write = 2.0 * 2.0 * kA * dh * B + holes * 2.0 * 2.0 * dh;
+    // layer input and LayerNorm vectors, the predictors' inputs, the
+    // residual stream in and out of each block, the stored inputs re-read
+    // for recomputed K/V
+    r.act = 2.0 * a + 4.0 * 4.0 * d + (dense_a ? 0.0 : a) + (dense_m ? 0.0 : a) + 4.0 * a + holes * 4.0 * d;
+    r.total = r.weights + r.kv_read + r.kv_write + r.act;
+    *out = r;
+    return DV_OK;
 }
 
 }  // extern "C"

@@ -198,6 +198,10 @@ namespace dvh {
 
 dv_status fail(dv_status code, const char* fmt, ...);
 void clear_error();
+// dv_time_launches: an event before and after each launch of the kernel
+// role being timed (no-ops otherwise).
+void timed_begin(int kind, hipStream_t s);
+void timed_end(int kind, hipStream_t s);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 int elt_bytes(int wdt);
@@ -267,7 +271,8 @@ struct AxpyCall {
     float* partial;
     int32_t* advance;
     const TopkSel* sel;       // B == 1: also run a role of this selection in one more column of
-                              // workgroups (the first, with attention coefficients; else the last), or NULL
+                              // workgroups (the last), or NULL
+    int timed;                // DV_KERNEL_* role of the main launch for dv_time_launches, or 0
 };
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s);
 bool qkv_supported(int B, int d, int wdt);
@@ -307,5 +312,7 @@ dv_status launch_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, c
                           float scale, int n_sink, int n_window, int width, float* scores,
                           float* raw, float* stats, hipStream_t s);
 size_t kv_score_stats_floats(int B, int h, int n, int n_obs);
+dv_status launch_fill_normal(void* out, uint64_t n, int dtype, uint64_t seed, uint64_t stream, uint64_t offset,
+                             float mean, float stdv, hipStream_t s);
 
 }  // namespace dvh

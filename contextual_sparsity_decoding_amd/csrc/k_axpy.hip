@@ -450,10 +450,12 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
         if (c.wdt == DV_F16) axpy_go<half_t, NB>(a, p.n_slices, s);            \
         else axpy_go<float, NB>(a, p.n_slices, s);                             \
         break;
+    timed_begin(c.timed, s);
     switch (nb) {
         DV_AXPY(1) DV_AXPY(2) DV_AXPY(4) DV_AXPY(8) DV_AXPY(16)
     }
 #undef DV_AXPY
+    timed_end(c.timed, s);
     const dim3 fg(cdiv(c.d / 4, 64), c.B);
     if (c.sel && c.apart) {                        // the selection threshold rides in the finalize
         const FinThr f{c.sel->keys, c.sel->n, c.sel->k, c.sel->hist, (TopkThreshold*)c.sel->thr};

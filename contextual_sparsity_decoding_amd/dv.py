@@ -22,7 +22,7 @@ if not os.path.exists(_LIB_PATH):
                       "`python -m contextual_sparsity_decoding_amd.build` (hipcc, gfx950)")
 lib = C.CDLL(_LIB_PATH)
 
-DV_F32, DV_F16 = 0, 1
+DV_F32, DV_F16, DV_U32 = 0, 1, 2
 DV_ACT_NONE, DV_ACT_RELU = 0, 1
 DV_PROJ_QKV, DV_PROJ_OUT = 0, 1
 DV_SKIP_NONPOS_FC2 = 0x1
@@ -32,6 +32,7 @@ DV_HOLE_FILL = 0x8
 DV_KV_SELECT = 0x10
 DV_ADVANCE_POS = 0x20
 DV_LOOKAHEAD = 0x40
+DV_KERNEL_QKV, DV_KERNEL_ATTN, DV_KERNEL_OUT, DV_KERNEL_FC1, DV_KERNEL_FC2 = 1, 2, 3, 4, 5
 STATUS = ["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN", "DV_ERR_RANGE",
           "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]
 
@@ -70,6 +71,16 @@ class LayerState(C.Structure):
                 ("aux_stream", vp), ("ev_fork", vp), ("ev_join", vp)]
 
 
+class StackLayer(C.Structure):
+    _fields_ = [("w", LayerWeights), ("kv", KVState), ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci),
+                ("sel_end", ci)]
+
+
+class Bytes(C.Structure):
+    _fields_ = [(n, C.c_double) for n in ("head_pred", "neuron_pred", "qkv", "out_proj", "fc1", "fc2", "weights",
+                                          "kv_read", "kv_write", "act", "total")]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(lib, name)
     f.restype = restype
@@ -95,12 +106,19 @@ _sig("dv_kv_score_workspace_bytes", sz, ci, ci, ci, ci)
 _sig("dv_kv_score", ci, vp, ci, ci, ci, ci, C.POINTER(KVView), cf, ci, ci, ci, vp, vp, sz, vp)
 _sig("dv_decode_workspace_bytes", sz, C.POINTER(DecodeCfg), ci)
 _sig("dv_decode_layer", ci, C.POINTER(LayerWeights), C.POINTER(DecodeCfg), C.POINTER(LayerState), vp, vp, vp, sz, vp)
+_sig("dv_stack_workspace_bytes", sz, C.POINTER(DecodeCfg), ci)
+_sig("dv_decode_stack", ci, C.POINTER(StackLayer), ci, C.POINTER(DecodeCfg), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp)
+_sig("dv_fill_normal", ci, vp, C.c_uint64, ci, C.c_uint64, C.c_uint64, C.c_uint64, cf, cf, vp)
+_sig("dv_bytes_read", ci, C.POINTER(DecodeCfg), C.c_double, C.c_double, C.c_double, C.POINTER(Bytes))
+_sig("dv_time_launches", ci, ci, C.POINTER(vp), ci)
+_sig("dv_launch_events_used", ci)
 
 EXPORTS = ("dv_api_version", "dv_status_str", "dv_last_error", "dv_layernorm", "dv_predict_workspace_bytes",
            "dv_predict", "dv_topk_workspace_bytes", "dv_topk_select", "dv_sparse_mlp_workspace_bytes",
            "dv_sparse_mlp", "dv_attn_proj_workspace_bytes", "dv_sparse_attn_proj", "dv_splitk_workspace_bytes",
            "dv_splitk_attn", "dv_kv_score_workspace_bytes", "dv_kv_score", "dv_decode_workspace_bytes",
-           "dv_decode_layer")
+           "dv_decode_layer", "dv_stack_workspace_bytes", "dv_decode_stack", "dv_fill_normal", "dv_bytes_read",
+           "dv_time_launches", "dv_launch_events_used")
 
 
 class DVError(RuntimeError):
@@ -252,3 +270,70 @@ def dv_decode_workspace_bytes(cfg: DecodeCfg, max_len: int) -> int:
 def dv_decode_layer(wts: LayerWeights, cfg: DecodeCfg, st: LayerState, x_in, x_out, ws, stream=None):
     _check("dv_decode_layer", lib.dv_decode_layer(C.byref(wts), C.byref(cfg), C.byref(st), ptr(x_in), ptr(x_out),
                                                   ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def dv_stack_workspace_bytes(cfg: DecodeCfg, max_len: int) -> int:
+    return lib.dv_stack_workspace_bytes(C.byref(cfg), max_len)
+
+
+def stack_layers(layers) -> "C.Array":
+    """A C array of StackLayer from a sequence of them (kept alive by the array)."""
+    arr = (StackLayer * len(layers))(*layers)
+    arr._keep = list(layers)
+    return arr
+
+
+def dv_decode_stack(layers, cfg: DecodeCfg, x_in, x_out, ws, *, head_sets=None, neuron_sets=None,
+                    neuron_counts=None, fc2_rows=None, x_trace=None, stream=None):
+    _check("dv_decode_stack", lib.dv_decode_stack(
+        layers, len(layers), C.byref(cfg), ptr(head_sets), ptr(neuron_sets), ptr(neuron_counts), ptr(fc2_rows),
+        ptr(x_in), ptr(x_out), ptr(x_trace), ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def dv_fill_normal(out, seed: int, stream_id: int, offset: int = 0, mean: float = 0.0, std: float = 1.0,
+                   raw: bool = False, stream=None):
+    """Fill ``out`` (fp16 or fp32; int32 with ``raw``) with the seeded normal stream (seed, stream_id)."""
+    if raw:
+        dt = DV_U32
+        if out.dtype != torch.int32:
+            raise ValueError("raw words go to an int32 tensor")
+    else:
+        dt = wdt_of(out)
+    _check("dv_fill_normal", lib.dv_fill_normal(ptr(out), out.numel(), dt, seed, stream_id, offset, mean, std,
+                                                stream_handle(stream)))
+
+
+def dv_bytes_read(cfg: DecodeCfg, n_att: float, fc2_rows: float, holes: float = 0.0) -> Bytes:
+    b = Bytes()
+    _check("dv_bytes_read", lib.dv_bytes_read(C.byref(cfg), n_att, fc2_rows, holes, C.byref(b)))
+    return b
+
+
+class LaunchTimer:
+    """Events around each launch of one kernel role (dv_time_launches) on this thread.
+
+    Use as a context manager around calls of dv_decode_layer / dv_decode_stack;
+    ``durations_ms()`` afterwards (once the work has run) gives one duration
+    per timed launch."""
+
+    def __init__(self, kernel: int, max_launches: int):
+        self.kernel = kernel
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+        for e in self.events:          # materialise the HIP events
+            e.record()
+        torch.cuda.synchronize()
+        self._arr = (vp * len(self.events))(*[e.cuda_event for e in self.events])
+        self.used = 0
+
+    def __enter__(self):
+        _check("dv_time_launches", lib.dv_time_launches(self.kernel, self._arr, len(self.events)))
+        return self
+
+    def __exit__(self, *exc):
+        self.used = lib.dv_launch_events_used()
+        lib.dv_time_launches(0, None, 0)
+        return False
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(self.used // 2)]

@@ -1,0 +1,101 @@
+"""A decoder stack generated on the device and run one token at a time.
+
+Weights, biases, predictors and the seeded K/V caches of every layer are
+written by the library's own generator (dv_fill_normal), so stacks of
+100+ GB never pass through host memory; ``synth.stack_layer_weights`` and
+``synth.philox_tensor`` regenerate any of them on the host.  Streams: tensor
+``name`` of layer ``l`` is ``synth.stream_id(l, name)`` under the stack's
+seed.  Weights and biases ~ N(0, 0.02^2), caches ~ N(0, 1) (every slot,
+the filled ones being positions < n_ctx), LayerNorm gain 1 and bias 0.
+
+This module allocates device memory and marshals arguments; every step of
+the decode runs in libdv (dv_decode_stack).
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import dv, synth
+from .configs import LayerDims
+
+
+class Stack:
+    """``layers`` decoder layers of shape ``dims`` on the current device.
+
+    One decode position (``pos_dev``) is shared by every layer; it starts at
+    ``n_ctx`` and moves on by one per token (DV_ADVANCE_POS).  ``hole_fill``
+    allocates each layer's stored inputs and valid positions (DejaVu §4.2).
+    """
+
+    def __init__(self, dims: LayerDims, layers: int, n_ctx: int, max_len: int, seed: int, batch: int = 1,
+                 hole_fill: bool = True):
+        self.dims, self.L, self.n_ctx, self.max_len, self.seed, self.B = dims, layers, n_ctx, max_len, seed, batch
+        wdt = torch.float16 if dims.wdt == "f16" else torch.float32
+        shapes = synth.stack_tensor_shapes(dims)
+        self.W: List[dict] = []
+        self.K: List[torch.Tensor] = []
+        self.V: List[torch.Tensor] = []
+        self.y_buf: List[Optional[torch.Tensor]] = []
+        self.valid: List[Optional[torch.Tensor]] = []
+        one = torch.ones(dims.d, device="cuda")
+        zero = torch.zeros(dims.d, device="cuda")
+        for l in range(layers):
+            w = {}
+            for name, shp in shapes.items():
+                t = torch.empty(shp, dtype=wdt, device="cuda")
+                dv.dv_fill_normal(t, seed, synth.stream_id(l, name), std=synth.WEIGHT_STD)
+                w[name] = t
+            w.update(ln1_g=one, ln1_b=zero, ln2_g=one, ln2_b=zero)
+            self.W.append(w)
+            for name, lst in (("K", self.K), ("V", self.V)):
+                t = torch.empty(batch, dims.h, max_len, dims.d_h, dtype=torch.float16, device="cuda")
+                dv.dv_fill_normal(t, seed, synth.stream_id(l, name))
+                lst.append(t)
+            self.y_buf.append(torch.zeros(batch, max_len, dims.d, device="cuda") if hole_fill else None)
+            self.valid.append(torch.full((batch, dims.h), n_ctx - 1, dtype=torch.int32, device="cuda")
+                              if hole_fill else None)
+        self.pos_dev = torch.full((1,), n_ctx, dtype=torch.int32, device="cuda")
+        self.wts = [dv.layer_weights(w) for w in self.W]
+        self.sel = [None] * layers          # DV_KV_SELECT: (sel_idx, sel_len, sel_end) per layer
+        self._arr = None
+
+    def reset(self) -> None:
+        """Back to the seeded state: position n_ctx, every head valid up to n_ctx - 1
+        (slots past n_ctx - 1 are rewritten before they are read)."""
+        self.pos_dev.fill_(self.n_ctx)
+        for v in self.valid:
+            if v is not None:
+                v.fill_(self.n_ctx - 1)
+
+    def set_kv_selection(self, layer: int, sel_idx: torch.Tensor, sel_len: torch.Tensor, sel_end: int) -> None:
+        self.sel[layer] = (sel_idx, sel_len, sel_end)
+        self._arr = None
+
+    def layers_array(self):
+        """The C array of dv_stack_layer (built once, reused by every call)."""
+        if self._arr is None:
+            items = []
+            for l in range(self.L):
+                sl = dv.StackLayer()
+                sl.w = self.wts[l]
+                # kv.pos is only the bound of the device position
+                sl.kv = dv.kv_state(self.K[l], self.V[l], self.max_len - 1, self.y_buf[l], self.valid[l], self.pos_dev)
+                if self.sel[l] is not None:
+                    si, sn, se = self.sel[l]
+                    sl.sel_idx, sl.sel_len, sl.sel_cap, sl.sel_end = si.data_ptr(), sn.data_ptr(), si.shape[-1], se
+                    sl._keep_sel = (si, sn)
+                items.append(sl)
+            self._arr = dv.stack_layers(items)
+        return self._arr
+
+    def cfg(self, k_heads: int, k_neurons: int, flags: int, scale: float, eps: float = 1e-5,
+            pred_act: int = dv.DV_ACT_RELU) -> dv.DecodeCfg:
+        d = self.dims
+        dense_a = bool(flags & dv.DV_DENSE_ATTN)
+        dense_m = bool(flags & dv.DV_DENSE_MLP)
+        return dv.decode_cfg(B=self.B, d=d.d, h=d.h, d_h=d.d_h, N=d.N, r_attn=d.r_attn, r_mlp=d.r_mlp,
+                             k_heads=d.h if dense_a else k_heads, k_neurons=d.N if dense_m else k_neurons,
+                             wdt=dv.DV_F16 if d.wdt == "f16" else dv.DV_F32, pred_act=pred_act, eps=eps,
+                             scale=scale, flags=flags)

@@ -29,6 +29,7 @@ prescribes (the transposed fc2 and output projection):
 """
 from __future__ import annotations
 
+import ctypes
 import os
 from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Sequence
@@ -165,3 +166,95 @@ def tied_scores(rows: int, n: int, seed: int, levels: int = 0) -> np.ndarray:
     if levels > 0:
         return (g.integers(0, levels, size=(rows, n)).astype(np.float32) - levels / 2) * np.float32(0.25)
     return g.standard_normal((rows, n), dtype=np.float32)
+
+
+# ---- counter-based stream (the large workloads) ------------------------------
+# Stacks of 100+ GB are generated on the device by the HIP library's
+# dv_fill_normal; libsynth.so (synth_philox.c, built with gcc) is the host
+# side of the same generator, written separately from the same definition
+# (Philox-4x32-10 with Box-Muller; see synth_philox.c), so that any tensor,
+# or any range of one, can be regenerated on the host for the oracle.
+
+_SYNTH_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth.so")
+_synth = None
+
+
+def _lib():
+    global _synth
+    if _synth is None:
+        if not os.path.exists(_SYNTH_LIB):
+            raise ImportError(f"{_SYNTH_LIB} is missing: build it with "
+                              "`python -m contextual_sparsity_decoding_amd.build`")
+        lib = ctypes.CDLL(_SYNTH_LIB)
+        u64, u32p = ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32)
+        lib.synth_philox_block.argtypes = [u32p, u32p, u32p]
+        lib.synth_philox_words.argtypes = [u32p, u64, u64, u64, u64, ctypes.c_int]
+        lib.synth_philox_normal.argtypes = [ctypes.POINTER(ctypes.c_float), u64, u64, u64, u64, ctypes.c_float,
+                                            ctypes.c_float, ctypes.c_int]
+        _synth = lib
+    return _synth
+
+
+def philox_block(counter, key) -> np.ndarray:
+    """Philox-4x32-10 of one counter (4 words) under one key (2 words)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    p = ctypes.POINTER(ctypes.c_uint32)
+    _lib().synth_philox_block(c.ctypes.data_as(p), k.ctypes.data_as(p), out.ctypes.data_as(p))
+    return out
+
+
+def stream_id(layer: int, tensor: str | int) -> int:
+    """Stream of one tensor of one layer under a workload seed."""
+    tid = _TENSOR_IDS[tensor] if isinstance(tensor, str) else int(tensor)
+    return (int(layer) << 16) | tid
+
+
+def philox_words(n: int, seed: int, stream: int, offset: int = 0) -> np.ndarray:
+    out = np.empty(int(n), np.uint32)
+    _lib().synth_philox_words(out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), int(n), int(offset), int(seed),
+                              int(stream), _threads())
+    return out
+
+
+def philox_normal(n: int, seed: int, stream: int, offset: int = 0, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    """Elements [offset, offset + n) of the normal stream, fp32."""
+    out = np.empty(int(n), np.float32)
+    _lib().synth_philox_normal(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(n), int(offset), int(seed),
+                               int(stream), float(mean), float(std), _threads())
+    return out
+
+
+def philox_tensor(shape: Sequence[int], seed: int, layer: int, tensor: str, std: float = 1.0,
+                  dtype=np.float32) -> np.ndarray:
+    """The host copy of what dv_fill_normal writes for (seed, layer, tensor)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    a = philox_normal(n, seed, stream_id(layer, tensor), 0, 0.0, std).reshape(shape)
+    return _to_f16(a) if dtype == np.float16 else a
+
+
+# Shapes of one decoder layer's generated tensors (storage layouts above);
+# LayerNorm gain and bias are the constants 1 and 0.
+def stack_tensor_shapes(dims: LayerDims) -> Dict[str, tuple]:
+    d, h, dh, N = dims.d, dims.h, dims.d_h, dims.N
+    return {
+        "w_qkv_t": (3, h, dh, d), "b_qkv": (3, h, dh), "w_o_t": (h * dh, d), "b_o": (d,),
+        "w1_t": (N, d), "b1": (N,), "w2_t": (N, d), "b2": (d,),
+        "pa1_t": (dims.r_attn, d), "pa2_t": (h, dims.r_attn), "pm1_t": (dims.r_mlp, d), "pm2_t": (N, dims.r_mlp),
+    }
+
+
+def stack_layer_weights(dims: LayerDims, seed: int, layer: int, names: Sequence[str] | None = None) -> Dict[str, np.ndarray]:
+    """Host copy of one generated stack layer's weights (all, or ``names``)."""
+    wd = _wdt(dims)
+    shapes = stack_tensor_shapes(dims)
+    out = {}
+    for k in (names if names is not None else list(shapes) + ["ln1_g", "ln1_b", "ln2_g", "ln2_b"]):
+        if k in shapes:
+            out[k] = philox_tensor(shapes[k], seed, layer, k, WEIGHT_STD, wd)
+        elif k.endswith("_g"):
+            out[k] = np.ones(dims.d, np.float32)
+        else:
+            out[k] = np.zeros(dims.d, np.float32)
+    return out

@@ -64,7 +64,7 @@ typedef enum {
     DV_ERR_HIP = 8          /* a HIP launch failed */
 } dv_status;
 
-typedef enum { DV_F32 = 0, DV_F16 = 1 } dv_dtype;
+typedef enum { DV_F32 = 0, DV_F16 = 1, DV_U32 = 2 /* dv_fill_normal only */ } dv_dtype;
 typedef enum { DV_ACT_NONE = 0, DV_ACT_RELU = 1 } dv_act;
 typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
 
@@ -313,7 +313,10 @@ typedef struct {
      * most 20480, else in launches of their own).  The results are the
      * same either way.  The events and the stream are the caller's (created
      * once, reused by every call).  The workspace of a look-ahead call must
-     * not be shared with a call running concurrently. */
+     * not be shared with a call running concurrently.  next_head_idx and
+     * next_neuron_idx are written while the call's launches still read
+     * head_idx_in and neuron_idx_in: the four buffers must not overlap
+     * (else DV_ERR_RANGE). */
     const int32_t* head_idx_in;     /* [k_heads] ascending; ignored with DV_DENSE_ATTN */
     const int32_t* neuron_idx_in;   /* [k_neurons] ascending; ignored with DV_DENSE_MLP */
     const void *next_pa1_t, *next_pa2_t;   /* next layer's head predictor, or NULL for none */
@@ -329,6 +332,109 @@ size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len);
 dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* cfg,
                           const dv_layer_state* st, const float* x_in, float* x_out, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A stack of n_layers decoder layers for one token (DejaVu §3: the token
+ * passes every layer; §4.3: layer l's input predicts layer l+1's sets;
+ * ByteCross §3.1: one step reads every layer's projections and KV).  The
+ * output of layer l is the input of layer l+1; x_in feeds layer 0 and the
+ * last layer writes x_out.  Every layer uses `cfg` (with per-layer weights
+ * and state from layers[l]).
+ *
+ * With DV_LOOKAHEAD (batch of one), layer 0's sets come from its own
+ * predictors on LN1(x_in) (there is no layer before it), and layer l runs on
+ * the sets layer l-1 predicted from its LN1 input, with layer l's
+ * predictors, while computing its own block; the sets live in
+ *   head_sets    device int32 [n_layers][k_heads]   (required unless DV_DENSE_ATTN)
+ *   neuron_sets  device int32 [n_layers][k_neurons] (required unless DV_DENSE_MLP)
+ * and hold, after the call, the sets each layer ran on.  Without it each
+ * layer predicts its own blocks' sets in the sequential form, and the
+ * optional head_sets / neuron_sets (NULL to skip) receive them; with a
+ * batch, row l of neuron_sets ([n_layers][min(N, B*k_neurons)]) holds the
+ * union and neuron_counts (device int32 [n_layers] or NULL) its size.
+ * fc2_rows (device int32 [1] or NULL) is incremented by the fc2 rows read.
+ * x_trace (device fp32 [n_layers - 1][B][d] or NULL) receives the output of
+ * every layer but the last (the input of the next), in place of scratch.
+ * With DV_ADVANCE_POS a decode position shared by several layers (the same
+ * kv.pos_dev) moves on once, in the last layer that uses it.
+ * Every layer is checked before anything is enqueued; the message names
+ * the failing layer.  The workspace is dv_stack_workspace_bytes(cfg,
+ * largest max_len) bytes; layers run in order on `stream`.
+ */
+typedef struct {
+    dv_layer_weights w;
+    dv_kv_state kv;
+    const int32_t* sel_idx;     /* DV_KV_SELECT: as in dv_kv_view */
+    const int32_t* sel_len;
+    int sel_cap;
+    int sel_end;
+} dv_stack_layer;
+
+size_t dv_stack_workspace_bytes(const dv_decode_cfg* cfg, int max_len);
+dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_decode_cfg* cfg, int32_t* head_sets,
+                          int32_t* neuron_sets, int32_t* neuron_counts, int32_t* fc2_rows, const float* x_in,
+                          float* x_out, float* x_trace, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Seeded normal samples written into device memory (synthetic weights,
+ * caches and inputs of stacks too large to pass through the host).  The
+ * generator is Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC 2011) with the Box-Muller
+ * transform:
+ *   element i of stream (seed, stream) lies in Philox block b = i / 4, whose
+ *   counter is (b mod 2^32, b / 2^32, stream mod 2^32, stream / 2^32) and
+ *   key (seed mod 2^32, seed / 2^32); its words x0..x3 form the pairs
+ *   (x0, x1) and (x2, x3); for a pair (xa, xb), u = (xa + 1) / 2^32,
+ *   v = xb / 2^32, r = sqrt(-2 ln u), za = r cos(2 pi v), zb = r sin(2 pi v)
+ *   in double; element 4b + j takes z_j, and its value is
+ *   mean + std * z_j in double, rounded to float (then to half, RNE).
+ *   out     device, 16-byte aligned: n elements of dtype DV_F32, DV_F16, or
+ *           DV_U32 (the raw words x_j)
+ *   offset  index of out[0] within the stream (a range can be regenerated)
+ */
+dv_status dv_fill_normal(void* out, uint64_t n, int dtype, uint64_t seed, uint64_t stream, uint64_t offset,
+                         float mean, float std, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Byte account of one decode step of one layer (ByteCross §3.1: a step
+ * reads the projection weights it keeps and the KV entries it attends to;
+ * DejaVu §2.3 Eqs. 1-2 and §4.1-4.2 name what is read): the algorithmic
+ * bytes, i.e. what the step must move at least once, by kernel and by kind.
+ *   n_att     positions each selected head attends to
+ *   fc2_rows  fc2 rows read (the device count of dv_layer_state.fc2_rows_out
+ *             per step; k_neurons when every selected row is read)
+ *   holes     recomputed K/V positions summed over heads
+ * Host only: nothing is enqueued.
+ */
+typedef struct {
+    double head_pred, neuron_pred, qkv, out_proj, fc1, fc2;  /* weight and bias bytes by kernel */
+    double weights;     /* their sum */
+    double kv_read;     /* K and V entries attended to */
+    double kv_write;    /* K/V appended and recomputed */
+    double act;         /* fp32 activations, LayerNorm vectors, stored inputs re-read */
+    double total;
+} dv_bytes;
+dv_status dv_bytes_read(const dv_decode_cfg* cfg, double n_att, double fc2_rows, double holes, dv_bytes* out);
+
+/* ------------------------------------------------------------------------
+ * Launch timing, for measuring one kernel role inside the real decode step
+ * (effective bandwidth of that kernel on the bytes it must read, ByteCross
+ * §4.4 reports bandwidth as a share of peak per path).  While set on the
+ * calling thread, each launch of role `kernel` made by dv_decode_layer or
+ * dv_decode_stack is bracketed by hipEventRecord(events[2i]) before and
+ * events[2i + 1] after it, on the launch's stream (also inside a stream
+ * capture), for the first n_events / 2 launches.  `events` is a host array
+ * of hipEvent_t the caller created (with timing) and keeps alive until the
+ * recorded work has run.  kernel 0 turns timing off.
+ * dv_launch_events_used() gives the number of events recorded since.
+ */
+#define DV_KERNEL_QKV  1   /* sparse Q/K/V projection with KV append and hole fill */
+#define DV_KERNEL_ATTN 2   /* split-K attention */
+#define DV_KERNEL_OUT  3   /* output projection gather-AXPY (its reduction launch excluded) */
+#define DV_KERNEL_FC1  4   /* sparse fc1 */
+#define DV_KERNEL_FC2  5   /* sparse fc2 gather-AXPY (its reduction launch excluded) */
+dv_status dv_time_launches(int kernel, void** events, int n_events);
+int dv_launch_events_used(void);
 
 #ifdef __cplusplus
 }

@@ -442,3 +442,50 @@ def decode_layer_lookahead(x, W: dict, W_next: Optional[dict], kv: KVState, pos:
                    next_head_idx=topk_select(sA[0], k_heads), next_neuron_idx=topk_select(sM[0], k_neurons))
     rec.update(y=y, q=q, o=o, h=hres, y2=y2, a=a, head_idx=heads, neuron_idx=idx)
     return out, rec
+
+
+# ---------------------------------------------------------------- the stack --
+
+def predict_sets(x, W: dict, k_heads: int, k_neurons: int, eps: float = 1e-5, pred_act: str = "relu"):
+    """Sets of one layer from its own predictors on its normalised input
+    y = LN1(x): S_A = top-k_heads(SP_A(y)), S_M = top-k_neurons(SP_M(y)).
+
+    DejaVu §4.3's parallel form predicts layer l+1 from layer l's input; the
+    first layer of a stack has no layer before it, so its sets come from its
+    own input (the plainest reading consistent with that form).  Scores are
+    rounded to fp32 before selection.  x [1][d].
+    Returns (head_idx, neuron_idx, head scores, neuron scores).
+    """
+    y = layernorm(np.atleast_2d(x), W["ln1_g"], W["ln1_b"], eps)
+    sA = predictor(y, W["pa1_t"], W["pa2_t"], pred_act).astype(np.float32)
+    sM = predictor(y, W["pm1_t"], W["pm2_t"], pred_act).astype(np.float32)
+    return topk_select(sA[0], k_heads), topk_select(sM[0], k_neurons), sA, sM
+
+
+def decode_stack_lookahead(x, Ws: Sequence[dict], kvs: Sequence[KVState], pos: int, *, k_heads: int,
+                           k_neurons: int, scale: float, eps: float = 1e-5, pred_act: str = "relu",
+                           skip_nonpos: bool = True, hole_fill: bool = True):
+    """One token through a stack of layers in DejaVu §4.3's parallel form.
+
+    The output of layer l is the input of layer l+1 (§3, the residual
+    stream).  Layer 0 runs on the sets its own predictors give for LN1(x)
+    (``predict_sets``); layer l > 0 runs on the sets layer l-1's
+    ``decode_layer_lookahead`` predicted from its normalised input with
+    layer l's predictors.  Every layer's token sits at ``pos``.
+
+    x [1][d].  Returns (x_out [1][d], list of per-layer records, each with
+    the layer's input ``x`` and the sets it ran on).  Mutates ``kvs``.
+    """
+    heads, neurons, _, _ = predict_sets(x, Ws[0], k_heads, k_neurons, eps, pred_act)
+    recs = []
+    for l, W in enumerate(Ws):
+        W_next = Ws[l + 1] if l + 1 < len(Ws) else None
+        x_in = _f64(np.atleast_2d(x))
+        x, rec = decode_layer_lookahead(x, W, W_next, kvs[l], pos, head_idx=heads, neuron_idx=neurons,
+                                        k_heads=k_heads, k_neurons=k_neurons, scale=scale, eps=eps,
+                                        pred_act=pred_act, skip_nonpos=skip_nonpos, hole_fill=hole_fill)
+        rec["x"] = x_in
+        recs.append(rec)
+        if W_next is not None:
+            heads, neurons = rec["next_head_idx"], rec["next_neuron_idx"]
+    return x, recs

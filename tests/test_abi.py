@@ -142,3 +142,99 @@ def test_decode_layer_validation(dv):
     cfg.flags = 0
     cfg.k_neurons = 300
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+
+
+def test_lookahead_sets_must_not_alias(dv):
+    L = dv.lib
+    cfg = dv.DecodeCfg(B=1, d=64, h=4, d_h=64, N=256, r_attn=16, r_mlp=16, k_heads=2, k_neurons=32,
+                       wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.125, flags=dv.DV_LOOKAHEAD)
+    w = dv.LayerWeights(*([P] * 16))
+    st = dv.LayerState()
+    st.kv = dv.KVState(P, P, 32, 5, 0, 0)
+    st.head_idx_in, st.neuron_idx_in = P + 4096, P + 8192
+    st.next_pa1_t = st.next_pa2_t = st.next_pm1_t = st.next_pm2_t = P
+    st.next_head_idx, st.next_neuron_idx = P + 12288, P + 16384
+    ok = L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P + 20480, P + 24576, 0, 0, 0)
+    assert ok == 6                                   # separate buffers: only the workspace is missing
+    st.next_neuron_idx = P + 8192 + 64               # inside neuron_idx_in
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P + 20480, P + 24576, P, 1 << 30, 0) == 5
+    assert "overlap" in err(dv)
+    st.next_neuron_idx = P + 16384
+    st.next_head_idx = P + 4096                      # the same buffer as head_idx_in
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P + 20480, P + 24576, P, 1 << 30, 0) == 5
+
+
+def _stack_cfg(dv, flags):
+    return dv.DecodeCfg(B=1, d=64, h=4, d_h=64, N=256, r_attn=16, r_mlp=16, k_heads=2, k_neurons=32,
+                        wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.125, flags=flags)
+
+
+def test_decode_stack_validation(dv):
+    L = dv.lib
+    cfg = _stack_cfg(dv, dv.DV_LOOKAHEAD | dv.DV_ADVANCE_POS)
+    lay = dv.StackLayer()
+    lay.w = dv.LayerWeights(*([P] * 16))
+    lay.kv = dv.KVState(P, P, 32, 5, 0, 0, P)
+    arr = (dv.StackLayer * 3)(lay, lay, lay)
+    big = 1 << 30
+    assert L.dv_decode_stack(arr, 3, C.byref(cfg), 0, P, 0, 0, P, P + 4096, 0, P, big, 0) == 1     # head_sets
+    assert L.dv_decode_stack(arr, 0, C.byref(cfg), P, P, 0, 0, P, P + 4096, 0, P, big, 0) == 2
+    assert L.dv_decode_stack(arr, 3, C.byref(cfg), P, P, 0, 0, P, P, 0, P, big, 0) == 5           # x_out = x_in
+    assert L.dv_decode_stack(arr, 3, C.byref(cfg), P, P, 0, 0, P, P + 4096, 0, P, 64, 0) == 6
+    assert L.dv_stack_workspace_bytes(C.byref(cfg), 32) > L.dv_decode_workspace_bytes(C.byref(cfg), 32)
+    assert L.dv_decode_stack(arr, 3, C.byref(cfg), P, P, 0, 0, P, P + 4096, P + 256, P, big, 0) == 5  # x_trace on x_in
+    # a bad layer is named, and nothing is enqueued before the check
+    bad = dv.StackLayer()
+    bad.w = dv.LayerWeights(*([P] * 16))
+    bad.kv = dv.KVState(P, P, 32, 40, 0, 0, P)        # pos past max_len
+    arr2 = (dv.StackLayer * 3)(lay, lay, bad)
+    assert L.dv_decode_stack(arr2, 3, C.byref(cfg), P, P + 65536, 0, 0, P, P + 4096, 0, P + (1 << 20), big, 0) == 5
+    assert "layer 2" in err(dv)
+    # the next layer's predictor must be there in the look-ahead form
+    nopred = dv.StackLayer()
+    nopred.w = dv.LayerWeights(*([P] * 12 + [0] * 4))
+    nopred.kv = lay.kv
+    arr3 = (dv.StackLayer * 2)(lay, nopred)
+    assert L.dv_decode_stack(arr3, 2, C.byref(cfg), P, P + 65536, 0, 0, P, P + 4096, 0, P + (1 << 20), big, 0) == 1
+    assert "layer 1" in err(dv)
+
+
+def test_fill_normal_validation(dv):
+    L = dv.lib
+    assert L.dv_fill_normal(0, 10, dv.DV_F16, 1, 2, 0, 0.0, 1.0, 0) == 1
+    assert L.dv_fill_normal(P, 10, 7, 1, 2, 0, 0.0, 1.0, 0) == 3
+    assert L.dv_fill_normal(Q, 10, dv.DV_F32, 1, 2, 0, 0.0, 1.0, 0) == 4
+    assert L.dv_fill_normal(P, 10, dv.DV_F32, 1, 2, 0, float("nan"), 1.0, 0) == 5
+    assert L.dv_fill_normal(P, 10, dv.DV_F32, 1, 2, (1 << 64) - 8, 0.0, 1.0, 0) == 5
+    assert L.dv_fill_normal(0, 0, dv.DV_F32, 1, 2, 0, 0.0, 1.0, 0) == 0      # nothing to write
+
+
+def test_time_launches_validation(dv):
+    L = dv.lib
+    assert L.dv_time_launches(9, None, 0) == 3
+    assert L.dv_time_launches(dv.DV_KERNEL_QKV, None, 4) == 1
+    assert L.dv_time_launches(0, None, 0) == 0
+    assert L.dv_launch_events_used() == 0
+
+
+def test_bytes_read_matches_the_oracle_account(dv):
+    """The library's byte account of a step (weights and KV read) against
+    the oracle's (oracle/bytes.py, pinned to the pages' printed values)."""
+    from oracle import bytes as ob
+    for (d, h, N, kA, kM, n_att, rows, flags) in (
+            (5120, 40, 20480, 20, 2048, 2049, 1023.5, 0),
+            (9216, 72, 36864, 36, 3686, 1100, 3686, 0),
+            (9216, 72, 36864, 72, 36864, 1100, 36864, dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP),
+            (12288, 96, 49152, 96, 4915, 513, 2000, dv.DV_DENSE_ATTN)):
+        cfg = dv.DecodeCfg(B=1, d=d, h=h, d_h=128, N=N, r_attn=128, r_mlp=128, k_heads=kA, k_neurons=kM,
+                           wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.088, flags=flags)
+        b = dv.dv_bytes_read(cfg, n_att, rows, 0.0)
+        ra = 0 if flags & dv.DV_DENSE_ATTN else 128
+        rm = 0 if flags & dv.DV_DENSE_MLP else 128
+        want = ob.decode_layer_bytes(d, h, 128, N, n_att, kA, kM, 2, r_attn=ra, r_mlp=rm, fc2_rows=rows)
+        assert b.weights + b.kv_read == pytest.approx(want, rel=1e-12)
+        assert b.total > b.weights + b.kv_read
+    bad = dv.DecodeCfg(B=1, d=64, h=4, d_h=64, N=256, r_attn=16, r_mlp=16, k_heads=9, k_neurons=32,
+                       wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.125, flags=0)
+    with pytest.raises(dv.DVError):
+        dv.dv_bytes_read(bad, 10, 10)

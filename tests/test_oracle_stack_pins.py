@@ -1,0 +1,101 @@
+"""Pins of the oracle's stack in DejaVu §4.3's parallel form
+(ref.predict_sets, ref.decode_stack_lookahead) against code that shares
+nothing with it: a pre-LN decoder stack written with torch's float64 ops
+(layer_norm, linear, softmax), and the look-ahead rule recomputed from the
+layer inputs with torch."""
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from contextual_sparsity_decoding_amd import synth
+from contextual_sparsity_decoding_amd.configs import LayerDims
+from oracle import ref
+
+DIMS = LayerDims(d=64, N=256, h=4, d_h=16, r_attn=8, r_mlp=8, wdt="f16")
+L, N0, MAXLEN = 3, 6, 10
+
+
+def _setup(seed):
+    Ws = [synth.layer_weights(DIMS, seed, layer=l) for l in range(L)]
+    caches = [synth.kv_cache(DIMS.h, DIMS.d_h, N0, MAXLEN, seed, layer=l) for l in range(L)]
+    x = synth.layer_inputs(DIMS.d, 1, 1, seed)[0]
+    return Ws, caches, x
+
+
+def _t(a):
+    return torch.tensor(np.asarray(a, np.float64))
+
+
+def torch_layer(x, W, K, V, pos, scale):
+    """One dense pre-LN layer on a [1][d] input: the token's k and v go into
+    slot pos in fp16, then every head attends to positions 0..pos."""
+    d, h, dh = DIMS.d, DIMS.h, DIMS.d_h
+    x = _t(x)
+    y = F.layer_norm(x, (d,), _t(W["ln1_g"]), _t(W["ln1_b"]), 1e-5)
+    wqkv, bqkv = _t(W["w_qkv_t"]), _t(W["b_qkv"])
+    qkv = torch.stack([torch.stack([F.linear(y[0], wqkv[j, i], bqkv[j, i]) for i in range(h)]) for j in range(3)])
+    K[0, :, pos] = qkv[1].numpy().astype(np.float16)
+    V[0, :, pos] = qkv[2].numpy().astype(np.float16)
+    Kc, Vc = _t(K[0, :, :pos + 1]), _t(V[0, :, :pos + 1])
+    o = torch.stack([torch.softmax(scale * (Kc[i] @ qkv[0, i]), 0) @ Vc[i] for i in range(h)])
+    hres = x + o.reshape(1, h * dh) @ _t(W["w_o_t"]) + _t(W["b_o"])
+    y2 = F.layer_norm(hres, (d,), _t(W["ln2_g"]), _t(W["ln2_b"]), 1e-5)
+    a = torch.relu(F.linear(y2, _t(W["w1_t"]), _t(W["b1"])))
+    return (hres + a @ _t(W["w2_t"]) + _t(W["b2"])).numpy()
+
+
+def test_dense_stack_is_a_plain_decoder_stack():
+    Ws, caches, x = _setup(3)
+    scale = 1 / math.sqrt(DIMS.d_h)
+    kvs = [ref.KVState(K.copy(), V.copy()) for K, V in caches]
+    got, recs = ref.decode_stack_lookahead(x, Ws, kvs, N0, k_heads=DIMS.h, k_neurons=DIMS.N, scale=scale,
+                                           skip_nonpos=False, hole_fill=False)
+    want = np.atleast_2d(x).astype(np.float64)
+    for l in range(L):
+        K, V = caches[l][0].copy(), caches[l][1].copy()
+        want = torch_layer(want, Ws[l], K, V, N0, scale)
+        assert np.array_equal(kvs[l].K, K) and np.array_equal(kvs[l].V, V)
+    assert np.max(np.abs(got - want)) <= 1e-10 * np.max(np.abs(want))
+    assert all(np.array_equal(r["head_idx"], np.arange(DIMS.h)) for r in recs)
+
+
+def test_sets_come_from_the_layer_before():
+    """Layer 0 runs on its own predictors' choice for LN1(x); layer l on the
+    top-k of layer l's predictors applied to LN1 of layer l-1's input; the
+    input of layer l is the output of layer l-1."""
+    Ws, caches, x = _setup(5)
+    kA, kM = 2, 40
+    kvs = [ref.KVState(K.copy(), V.copy(), np.zeros((1, MAXLEN, DIMS.d)), np.full((1, DIMS.h), N0 - 1))
+           for K, V in caches]
+    out, recs = ref.decode_stack_lookahead(x, Ws, kvs, N0, k_heads=kA, k_neurons=kM, scale=0.25)
+    assert np.array_equal(recs[0]["x"], np.atleast_2d(x).astype(np.float64))
+    for l in range(L):
+        src = 0 if l == 0 else l - 1                 # the layer whose input and LN1 feed the predictor
+        y = F.layer_norm(_t(recs[src]["x"]), (DIMS.d,), _t(Ws[src]["ln1_g"]), _t(Ws[src]["ln1_b"]), 1e-5)
+        for p1, p2, k, key in (("pa1_t", "pa2_t", kA, "head_idx"), ("pm1_t", "pm2_t", kM, "neuron_idx")):
+            s = (torch.relu(y @ _t(Ws[l][p1]).T) @ _t(Ws[l][p2]).T)[0].numpy().astype(np.float32)
+            order = sorted(range(s.size), key=lambda i: (-float(s[i]), i))
+            assert np.array_equal(recs[l][key], np.sort(order[:k])), (l, key)
+    # chaining: layer l's input is layer l-1's output (h + MLP over its set)
+    for l in range(1, L):
+        r = recs[l - 1]
+        W = Ws[l - 1]
+        a = np.maximum(r["y2"] @ W["w1_t"][r["neuron_idx"]].astype(np.float64).T
+                       + W["b1"][r["neuron_idx"]].astype(np.float64), 0.0)
+        prev_out = r["h"] + a @ W["w2_t"][r["neuron_idx"]].astype(np.float64) + W["b2"].astype(np.float64)
+        assert np.allclose(recs[l]["x"], prev_out, rtol=0, atol=1e-12)
+    assert recs[-1]["x"].shape == out.shape
+
+
+def test_one_layer_stack_is_the_layer():
+    Ws, caches, x = _setup(9)
+    kA, kM = 3, 100
+    kv1 = [ref.KVState(caches[0][0].copy(), caches[0][1].copy())]
+    got, _ = ref.decode_stack_lookahead(x, Ws[:1], kv1, N0, k_heads=kA, k_neurons=kM, scale=0.25, hole_fill=False)
+    hi, ni, _, _ = ref.predict_sets(x, Ws[0], kA, kM)
+    kv2 = ref.KVState(caches[0][0].copy(), caches[0][1].copy())
+    want, _ = ref.decode_layer_lookahead(x, Ws[0], None, kv2, N0, head_idx=hi, neuron_idx=ni, k_heads=kA,
+                                         k_neurons=kM, scale=0.25, hole_fill=False)
+    assert np.array_equal(got, want)
