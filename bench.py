@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--layers", type=int, default=64)
     p.add_argument("--sweep", type=int, default=1, help="0 skips the keep sweep and the sequential schedule")
+    p.add_argument("--dense", type=int, default=1, help="0 skips the dense path (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time per oracle timing (two timings)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -226,7 +227,9 @@ def main():
     hb, tok_bytes = step_bytes(dv, head_cfg, L, n_att, rows)
 
     # dense path of the same library: every head and neuron, every fc2 row
-    dense_ms, _ = run.run(dense_cfg, W, K)
+    dense_ms, dense_bytes = float("nan"), float("nan")
+    if args.dense:
+        dense_ms, _ = run.run(dense_cfg, W, K)
     _, dense_bytes = step_bytes(dv, dense_cfg, L, n_att, dims.N)
 
     sweep, seq_ms = [], None

@@ -108,7 +108,7 @@ __device__ __forceinline__ void topk_classify(const uint32_t (&key)[4], int vali
 // keys.  Every load is issued at the start and the keys stay in registers,
 // so the role costs one memory round trip.  lds: kTopkThrWords.
 // 0 < k <= n <= kTopkRegN, n % 4 == 0, keys 16-byte aligned.
-constexpr int kTopkRegN = 20480;
+constexpr int kTopkRegN = 49152;                 // 48 keys per thread of 1024; d_ffn of OPT-175B
 constexpr int kTopkThrWords = 4096 + 256 + 2 * 20;
 template <int NT>
 __device__ __forceinline__ void topk_threshold(const uint32_t* __restrict__ keys, int n, int k,
@@ -191,34 +191,37 @@ __device__ __forceinline__ void topk_threshold(const uint32_t* __restrict__ keys
 
 // One workgroup per slice of 1024 keys: the slice's selected indices at
 // their place in the ascending set.  The selected and equal keys of the
-// slices before it are counted here too, every one of their loads issued
-// at once (each workgroup reads at most kTopkRegN - 1024 keys).  tot: 20
-// words.
+// slices before it are counted here too, EB slices' loads issued at once
+// (each workgroup reads at most kTopkRegN - 1024 keys, L2-resident).  tot:
+// 20 words.
 __device__ __forceinline__ void topk_emit_slice(const uint32_t* __restrict__ keys, int n, int k, int slice,
                                                 const TopkThreshold* __restrict__ thr, unsigned* tot,
                                                 int32_t* __restrict__ idx) {
-    constexpr int MAXB = kTopkRegN / kTopkSlice - 1;    // slices before the last
+    constexpr int EB = 12;                               // earlier slices per round of loads
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     const int n4 = n >> 2;
     const int own = slice * (kTopkSlice / 4) + tid;
     const uint4 mine = k4[own < n4 ? own : 0];
-    uint4 pre[MAXB];                                     // uint4 tid + 256 j of slice j < slice
-#pragma unroll
-    for (int j = 0; j < MAXB; ++j) pre[j] = j < slice ? k4[tid + (kTopkSlice / 4) * j] : uint4{0u, 0u, 0u, 0u};
     const TopkThreshold t = *thr;
     const bool done = t.done != 0u;
     unsigned pc = 0u;                                    // gt | eq << 16 over this thread's earlier keys
+    for (int j0 = 0; j0 < slice; j0 += EB) {             // uniform over the workgroup
+        uint4 pre[EB];                                   // uint4 tid + 256 j of slice j < slice
 #pragma unroll
-    for (int j = 0; j < MAXB; ++j) {
-        if (j < slice) {
-            const uint32_t kq[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+        for (int j = 0; j < EB; ++j)
+            pre[j] = j0 + j < slice ? k4[tid + (kTopkSlice / 4) * (j0 + j)] : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t mk = kq[e] & t.pmask;
-                pc += (mk > t.prefix || (done && mk == t.prefix)) ? 1u
-                      : (!done && kq[e] == t.prefix)             ? 0x10000u
-                                                                 : 0u;
+        for (int j = 0; j < EB; ++j) {
+            if (j0 + j < slice) {
+                const uint32_t kq[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t mk = kq[e] & t.pmask;
+                    pc += (mk > t.prefix || (done && mk == t.prefix)) ? 1u
+                          : (!done && kq[e] == t.prefix)             ? 0x10000u
+                                                                     : 0u;
+                }
             }
         }
     }
