@@ -115,6 +115,35 @@ static size_t splitk_ws(int B, int n_sel, int d_h, int max_positions, int num_sp
     return kCounterBytes + align_up((size_t)B * n_sel * num_splits * (d_h + 2) * 4, 256);
 }
 
+// The sparse MLP behind dv_sparse_mlp and its no-allocation variant: the
+// arguments checked, then fc1 and fc2 with scratch carved from ws.
+dv_status sparse_mlp_call(const char* who, const float* y, int B, int d, int N, const void* w1_t, const void* b1,
+                          const void* w2_t, const void* b2, int wdt, const int32_t* idx, int n_idx_max,
+                          const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
+                          int32_t* fc2_rows, unsigned flags, void* ws, size_t ws_bytes, hipStream_t s, bool run) {
+    REQ(y && w1_t && b1 && w2_t && b2 && out, DV_ERR_NULL, "%s: NULL pointer", who);
+    REQ(wdt_ok(wdt), DV_ERR_DTYPE, "%s: wdt %d", who, wdt);
+    REQ(B >= 1 && B <= 16 && d_ok(d) && N >= 1, DV_ERR_SHAPE, "%s: B=%d d=%d N=%d", who, B, d, N);
+    REQ(n_idx_max >= 0 && n_idx_max <= N, DV_ERR_RANGE, "%s: n_idx_max=%d N=%d", who, n_idx_max, N);
+    REQ(idx || n_idx_max == N, DV_ERR_SHAPE, "%s: idx NULL needs n_idx_max == N", who);
+    REQ((flags & ~(unsigned)DV_SKIP_NONPOS_FC2) == 0, DV_ERR_DTYPE, "%s: flags 0x%x", who, flags);
+    REQ((size_t)d * elt_bytes(wdt) % 16 == 0, DV_ERR_ALIGN, "%s: d=%d rows not 16-byte multiples", who, d);
+    REQ(a16(w1_t) && a16(w2_t) && a16(y), DV_ERR_ALIGN, "%s: pointers must be 16-byte aligned", who);
+    const size_t act_bytes = (size_t)B * d * 4;
+    REQ(!overlap(out, act_bytes, y, act_bytes) && !overlap(out, act_bytes, residual, act_bytes), DV_ERR_RANGE,
+        "%s: out overlaps y or residual", who);
+    const MlpWs w = mlp_ws(ws, B, d, n_idx_max, wdt, act_out == nullptr);
+    REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, w.bytes);
+    if (!run) return DV_OK;
+    float* a = act_out ? act_out : w.a;
+    TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
+    AxpyCall c{};
+    c.w = w2_t; c.wdt = wdt; c.d = d; c.w_rows = N; c.rows = n_idx_max; c.n_rows_dev = n_idx_dev; c.idx = idx; c.blk = 1;
+    c.coef = a; c.coef_stride = n_idx_max; c.skip_zero = (flags & DV_SKIP_NONPOS_FC2) != 0;
+    c.B = B; c.bias = b2; c.residual = residual; c.out = out; c.rows_read = fc2_rows; c.partial = w.partial;
+    return launch_axpy(c, s);
+}
+
 }  // namespace dvh
 
 using namespace dvh;
@@ -211,27 +240,8 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
                         const float* residual, float* out, float* act_out, int32_t* fc2_rows, unsigned flags,
                         void* ws, size_t ws_bytes, void* stream) {
     clear_error();
-    REQ(y && w1_t && b1 && w2_t && b2 && out, DV_ERR_NULL, "dv_sparse_mlp: NULL pointer");
-    REQ(wdt_ok(wdt), DV_ERR_DTYPE, "dv_sparse_mlp: wdt %d", wdt);
-    REQ(B >= 1 && B <= 16 && d_ok(d) && N >= 1, DV_ERR_SHAPE, "dv_sparse_mlp: B=%d d=%d N=%d", B, d, N);
-    REQ(n_idx_max >= 0 && n_idx_max <= N, DV_ERR_RANGE, "dv_sparse_mlp: n_idx_max=%d N=%d", n_idx_max, N);
-    REQ(idx || n_idx_max == N, DV_ERR_SHAPE, "dv_sparse_mlp: idx NULL needs n_idx_max == N");
-    REQ((flags & ~(unsigned)DV_SKIP_NONPOS_FC2) == 0, DV_ERR_DTYPE, "dv_sparse_mlp: flags 0x%x", flags);
-    REQ((size_t)d * elt_bytes(wdt) % 16 == 0, DV_ERR_ALIGN, "dv_sparse_mlp: d=%d rows not 16-byte multiples", d);
-    REQ(a16(w1_t) && a16(w2_t) && a16(y), DV_ERR_ALIGN, "dv_sparse_mlp: pointers must be 16-byte aligned");
-    const size_t act_bytes = (size_t)B * d * 4;
-    REQ(!overlap(out, act_bytes, y, act_bytes) && !overlap(out, act_bytes, residual, act_bytes), DV_ERR_RANGE,
-        "dv_sparse_mlp: out overlaps y or residual");
-    const MlpWs w = mlp_ws(ws, B, d, n_idx_max, wdt, act_out == nullptr);
-    REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "dv_sparse_mlp: workspace %zu < %zu", ws_bytes, w.bytes);
-    hipStream_t s = (hipStream_t)stream;
-    float* a = act_out ? act_out : w.a;
-    TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
-    AxpyCall c{};
-    c.w = w2_t; c.wdt = wdt; c.d = d; c.w_rows = N; c.rows = n_idx_max; c.n_rows_dev = n_idx_dev; c.idx = idx; c.blk = 1;
-    c.coef = a; c.coef_stride = n_idx_max; c.skip_zero = (flags & DV_SKIP_NONPOS_FC2) != 0;
-    c.B = B; c.bias = b2; c.residual = residual; c.out = out; c.rows_read = fc2_rows; c.partial = w.partial;
-    return launch_axpy(c, s);
+    return sparse_mlp_call("dv_sparse_mlp", y, B, d, N, w1_t, b1, w2_t, b2, wdt, idx, n_idx_max, n_idx_dev, residual,
+                           out, act_out, fc2_rows, flags, ws, ws_bytes, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- projections --

@@ -312,6 +312,11 @@ dv_status launch_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, c
                           float scale, int n_sink, int n_window, int width, float* scores,
                           float* raw, float* stats, hipStream_t s);
 size_t kv_score_stats_floats(int B, int h, int n, int n_obs);
+dv_status sparse_mlp_call(const char* who, const float* y, int B, int d, int N, const void* w1_t, const void* b1,
+                          const void* w2_t, const void* b2, int wdt, const int32_t* idx, int n_idx_max,
+                          const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
+                          int32_t* fc2_rows, unsigned flags, void* ws, size_t ws_bytes, hipStream_t s,
+                          bool run = true);
 dv_status launch_fill_normal(void* out, uint64_t n, int dtype, uint64_t seed, uint64_t stream, uint64_t offset,
                              float mean, float stdv, hipStream_t s);
 

@@ -98,6 +98,7 @@ _sig("dv_topk_workspace_bytes", sz, ci, ci, ci)
 _sig("dv_topk_select", ci, vp, ci, ci, ci, vp, vp, vp, vp, sz, vp)
 _sig("dv_sparse_mlp_workspace_bytes", sz, ci, ci, ci, ci)
 _sig("dv_sparse_mlp", ci, vp, ci, ci, ci, vp, vp, vp, vp, ci, vp, ci, vp, vp, vp, vp, vp, cu, vp, sz, vp)
+_sig("dv_sparse_mlp_noalloc", ci, vp, ci, ci, ci, vp, vp, vp, vp, ci, vp, ci, vp, vp, vp, vp, vp, cu, vp)
 _sig("dv_attn_proj_workspace_bytes", sz, ci, ci, ci, ci, ci, ci, ci)
 _sig("dv_sparse_attn_proj", ci, ci, ci, ci, ci, ci, vp, ci, vp, vp, ci, vp, vp, vp, C.POINTER(KVState), vp, sz, vp)
 _sig("dv_splitk_workspace_bytes", sz, ci, ci, ci, ci, ci)
@@ -118,7 +119,7 @@ EXPORTS = ("dv_api_version", "dv_status_str", "dv_last_error", "dv_layernorm", "
            "dv_sparse_mlp", "dv_attn_proj_workspace_bytes", "dv_sparse_attn_proj", "dv_splitk_workspace_bytes",
            "dv_splitk_attn", "dv_kv_score_workspace_bytes", "dv_kv_score", "dv_decode_workspace_bytes",
            "dv_decode_layer", "dv_stack_workspace_bytes", "dv_decode_stack", "dv_fill_normal", "dv_bytes_read",
-           "dv_time_launches", "dv_launch_events_used")
+           "dv_time_launches", "dv_launch_events_used", "dv_sparse_mlp_noalloc")
 
 
 class DVError(RuntimeError):
@@ -202,6 +203,19 @@ def dv_sparse_mlp(y, w1_t, b1, w2_t, b2, idx, n_idx_max, out, ws, *, n_idx_dev=N
     _check("dv_sparse_mlp", lib.dv_sparse_mlp(
         ptr(y), B, d, N, ptr(w1_t), ptr(b1), ptr(w2_t), ptr(b2), wdt_of(w1_t), ptr(idx), n_idx_max, ptr(n_idx_dev),
         ptr(residual), ptr(out), ptr(act_out), ptr(fc2_rows), flags, ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def dv_sparse_mlp_noalloc(y, w1_t, b1, w2_t, b2, idx, n_idx_max, out, *, n_idx_dev=None, residual=None,
+                          act_out=None, fc2_rows=None, flags=0, stream=None):
+    """dv_sparse_mlp with the library's built-in scratch instead of a workspace."""
+    B, d = y.shape
+    N = w1_t.shape[0]
+    _check("dv_sparse_mlp_noalloc", lib.dv_sparse_mlp_noalloc(
+        ptr(y), B, d, N, ptr(w1_t), ptr(b1), ptr(w2_t), ptr(b2), wdt_of(w1_t), ptr(idx), n_idx_max, ptr(n_idx_dev),
+        ptr(residual), ptr(out), ptr(act_out), ptr(fc2_rows), flags, stream_handle(stream)))
 
 
 def kv_state(K, V, pos, y_buf=None, valid_upto=None, pos_dev=None) -> KVState:

@@ -151,6 +151,24 @@ dv_status dv_sparse_mlp(const float* y, int B, int d, int N, const void* w1_t, c
                         size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * dv_sparse_mlp without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * dv_sparse_mlp; its scratch is a device array of DV_NOALLOC_SCRATCH_BYTES
+ * built into the library (each GPU the library runs on holds its own copy
+ * until the process ends).  A shape whose dv_sparse_mlp_workspace_bytes()
+ * exceeds that size gets DV_ERR_WORKSPACE.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Every call on one GPU
+ * uses that GPU's one array: calls that overlap in time on the same GPU
+ * (different streams, different host threads) race and must not be made.
+ */
+#define DV_NOALLOC_SCRATCH_BYTES (8u << 20)
+dv_status dv_sparse_mlp_noalloc(const float* y, int B, int d, int N, const void* w1_t, const void* b1,
+                                const void* w2_t, const void* b2, int wdt, const int32_t* idx, int n_idx_max,
+                                const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
+                                int32_t* fc2_rows, unsigned flags, void* stream);
+
+/* ------------------------------------------------------------------------
  * KV state of one layer, updated by dv_sparse_attn_proj(DV_PROJ_QKV).
  *   k_cache, v_cache  device fp16 [B][h][max_len][d_h]
  *   pos               slot written by this step, 0 <= pos < max_len

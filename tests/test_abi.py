@@ -238,3 +238,18 @@ def test_bytes_read_matches_the_oracle_account(dv):
                        wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.125, flags=0)
     with pytest.raises(dv.DVError):
         dv.dv_bytes_read(bad, 10, 10)
+
+
+def test_sparse_mlp_noalloc_validation(dv):
+    """Checked on the host before the built-in scratch is looked up; shapes
+    whose scratch would exceed it are refused with a clear error."""
+    L = dv.lib
+    assert L.dv_sparse_mlp_noalloc(0, 1, 64, 256, P, P, P, P, dv.DV_F16, P, 32, 0, 0, P + 4096, 0, 0, 0, 0) == 1
+    assert L.dv_sparse_mlp_noalloc(P, 1, 64, 256, P, P, P, P, 5, P, 32, 0, 0, P + 4096, 0, 0, 0, 0) == 3
+    assert L.dv_sparse_mlp_noalloc(P, 1, 64, 256, P, P, P, P, dv.DV_F16, P, 32, 0, 0, P, 0, 0, 0, 0) == 5
+    # d = 9216, 36864 rows, batch 16: far past 8 MiB of scratch
+    big = L.dv_sparse_mlp_noalloc(P, 16, 9216, 36864, P, P, P, P, dv.DV_F16, P, 36864, 0, 0, P + (1 << 24),
+                                  0, 0, 0, 0)
+    assert big == 6 and "scratch" in err(dv)
+    need = L.dv_sparse_mlp_workspace_bytes(16, 9216, 36864, dv.DV_F16)
+    assert need > dv.NOALLOC_SCRATCH_BYTES
