@@ -53,6 +53,11 @@ def parse():
     p.add_argument("--layers", type=int, default=64)
     p.add_argument("--sweep", type=int, default=1, help="0 skips the keep sweep and the sequential schedule")
     p.add_argument("--dense", type=int, default=1, help="0 skips the dense path (profiling runs)")
+    p.add_argument("--longctx", type=int, default=1,
+                   help="0 skips the long-context composition stack (32 layers, d=4096, 2K-128K context)")
+    p.add_argument("--batched", type=int, default=1,
+                   help="0 skips the batched OPT-175B-share stack (48 layers, d=12288, batch 1-16)")
+    p.add_argument("--extra-steps", type=int, default=12, help="timed tokens per point of the two extra stacks")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time per oracle timing (two timings)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -310,9 +315,166 @@ def main():
         "generate_s": round(gen_s, 2),
         "resident_weight_GB": round(resident / 1e9, 2),
     }
+    Xh = X[:16].cpu()
+    del run, stack, ws, head_sets, neuron_sets, X
+    torch.cuda.empty_cache()
+    if args.longctx:
+        result["longctx_composition"] = bench_longctx(torch, dv, synth, configs, args)
+    if args.batched:
+        result["batched_union"] = bench_batched(torch, dv, synth, configs, args)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dims, wl, L, X, head_cfg, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(dims, wl, L, Xh, head_cfg, args.cpu_seconds)
     print(json.dumps(result))
+
+
+def time_stack(torch, dv, stack, X, ws, cfg, warm, timed, head_sets=None, neuron_sets=None, neuron_counts=None):
+    """ms per step over `timed` graph-replayed steps after `warm`, from the
+    stack's seeded state; fc2 rows per layer per step; neuron counts read
+    back after the last step (per layer)."""
+    B, d = stack.B, stack.dims.d
+    x_cur = torch.empty(B, d, device="cuda")
+    x_out = torch.empty(B, d, device="cuda")
+    fc2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stack.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dv.dv_decode_stack(stack.layers_array(), cfg, x_cur, x_out, ws, head_sets=head_sets, neuron_sets=neuron_sets,
+                           neuron_counts=neuron_counts, fc2_rows=fc2)
+    for t in range(warm):
+        x_cur.copy_(X[t])
+        g.replay()
+    torch.cuda.synchronize()
+    fc2.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warm, warm + timed):
+        x_cur.copy_(X[t])
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / timed, int(fc2.item()) / (timed * stack.L)
+
+
+def bench_longctx(torch, dv, synth, configs, args):
+    """ByteCross's composition at long context (§3.3, §4.1-4.2): a 32-layer
+    stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 32K / 128K cached
+    tokens in four modes through the same kernels and the same split-K
+    attention: dense; projection-only (10% of MLP neurons, the sequential
+    form); KV-only (10% of cached positions per head chosen by the
+    attention-scored selection, plus the decoded tokens); composed.  The
+    selection's scoring pass runs once per context after the seeded prompt
+    and is timed on its own, outside tokens/s."""
+    from contextual_sparsity_decoding_amd.stack import Stack
+    wl = configs.LONGCTX_STACK
+    dims, L = wl.dims, wl.layers
+    W, K = 2, max(1, args.extra_steps)
+    T = W + K
+    scale = 1 / math.sqrt(dims.d_h)
+    kM = wl.k_neurons
+    stack = Stack(dims, L, 16, 32, SEED + 5, hole_fill=False)
+    X = torch.empty(T, 1, dims.d, device="cuda")
+    dv.dv_fill_normal(X, SEED + 5, synth.stream_id(0, "x"))
+    base = dv.DV_DENSE_ATTN | dv.DV_ADVANCE_POS
+    modes = {"dense": (base | dv.DV_DENSE_MLP, dims.N),
+             "proj": (base | dv.DV_SKIP_NONPOS_FC2, kM),
+             "kv": (base | dv.DV_DENSE_MLP | dv.DV_KV_SELECT, dims.N),
+             "composed": (base | dv.DV_SKIP_NONPOS_FC2 | dv.DV_KV_SELECT, kM)}
+    out = []
+    for n in wl.ctx_sweep:
+        b = int(math.floor(wl.kv_keep * n))
+        max_len = n + T + 8
+        stack.set_context(n, max_len)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        stack.select_kv(b)
+        e1.record()
+        torch.cuda.synchronize()
+        score_ms = e0.elapsed_time(e1)
+        ws = dv.workspace(max(dv.dv_stack_workspace_bytes(stack.cfg(dims.h, k, f, scale), max_len)
+                              for f, k in modes.values()))
+        row = {"n_ctx": n, "kv_budget": b, "scoring_ms_all_layers": round(score_ms, 3)}
+        res = {}
+        for name, (flags, k) in modes.items():
+            cfg = stack.cfg(dims.h, k, flags, scale)
+            ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K)
+            sel = bool(flags & dv.DV_KV_SELECT)
+            n_att = (b if sel else n) + W + (K - 1) / 2 + 1
+            by = L * dv.dv_bytes_read(cfg, n_att, rows if not (flags & dv.DV_DENSE_MLP) else dims.N, 0.0).total
+            res[name] = (ms, by)
+            row[name] = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1000 / ms, 2),
+                         "bytes_per_token": int(by), "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
+        for name in ("proj", "kv", "composed"):
+            row[name]["speedup"] = round(res["dense"][0] / res[name][0], 3)
+            row[name]["byte_bound_speedup"] = round(res["dense"][1] / res[name][1], 3)
+        out.append(row)
+        del ws
+    # the context where the two branches save the same time, measured and by bytes
+    def cross(key):
+        pts = [(r["n_ctx"], r["proj"][key] - r["kv"][key]) for r in out]
+        for (n0, a0), (n1, a1) in zip(pts, pts[1:]):
+            if a0 >= 0 > a1 or a0 > 0 >= a1:
+                f = a0 / (a0 - a1)
+                return round(math.exp(math.log(n0) + f * (math.log(n1) - math.log(n0))))
+        return None
+    del stack, X
+    torch.cuda.empty_cache()
+    return {"workload": "longctx-32L-d4096-h32-ffn16384-fp16: 32 layers, batch 1, neuron keep 10% (1638), "
+                        "KV keep 10% per head (attention-scored, 4 sinks + 64-token window forced), heads dense",
+            "points": out, "crossover_measured_n": cross("speedup"), "crossover_bytes_n": cross("byte_bound_speedup"),
+            "warmup": W, "steps": K}
+
+
+def bench_batched(torch, dv, synth, configs, args):
+    """DejaVu §5.2 / App. C.1: 48 OPT-175B-shaped layers (one GPU's share of
+    the stack; d = 12288, 96 heads dense, d_ffn = 49152) decoding batches of
+    1-16 independent sequences with 512 cached tokens each; each layer's MLP
+    reads the union of the sequences' top-10% neuron sets.  tokens/s =
+    B x steps/s; |U|/N is the union's share of the neurons."""
+    from contextual_sparsity_decoding_amd.stack import Stack
+    wl = configs.OPT175B_SHARE
+    dims, L = wl.dims, wl.layers
+    W, K = 2, max(1, args.extra_steps)
+    T = W + K
+    scale = 1 / math.sqrt(dims.d_h)
+    kM = wl.k_neurons
+    out = []
+    stack = None
+    for B in wl.batch:
+        if stack is None:
+            stack = Stack(dims, L, wl.n_ctx, wl.n_ctx + T + 8, SEED + 7, batch=max(wl.batch), hole_fill=False)
+        # one stack holds the largest batch's caches; a smaller batch uses the first B of them
+        sub = stack.batch_view(B)
+        X = torch.empty(T, B, dims.d, device="cuda")
+        dv.dv_fill_normal(X, SEED + 7, synth.stream_id(B, "x"))
+        flags = dv.DV_DENSE_ATTN | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
+        cfg = sub.cfg(dims.h, kM, flags, scale)
+        dcfg = sub.cfg(dims.h, dims.N, dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP | dv.DV_ADVANCE_POS, scale)
+        ws = dv.workspace(max(dv.dv_stack_workspace_bytes(c, sub.max_len) for c in (cfg, dcfg)))
+        nmax = min(dims.N, B * kM)
+        nsets = torch.zeros(L, nmax, dtype=torch.int32, device="cuda")
+        counts = torch.zeros(L, dtype=torch.int32, device="cuda")
+        ms, rows = time_stack(torch, dv, sub, X, ws, cfg, W, K, neuron_sets=nsets, neuron_counts=counts)
+        u = counts.float().mean().item()
+        dms, _ = time_stack(torch, dv, sub, X, ws, dcfg, W, K)
+        n_att = wl.n_ctx + W + (K - 1) / 2 + 1
+        ucfg = sub.cfg(dims.h, int(round(u)), flags, scale)
+        by = L * dv.dv_bytes_read(ucfg, n_att, rows, 0.0).total
+        dby = L * dv.dv_bytes_read(dcfg, n_att, dims.N, 0.0).total
+        out.append({"batch": B, "ms_per_step": round(ms, 4), "tokens_per_s": round(B * 1000 / ms, 2),
+                    "union_neurons": round(u, 1), "union_frac": round(u / dims.N, 4),
+                    "fc2_rows_per_layer": round(rows, 1), "bytes_per_step": int(by),
+                    "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                    "dense_ms_per_step": round(dms, 4), "speedup_vs_dense": round(dms / ms, 3),
+                    "byte_bound_speedup": round(dby / by, 3)})
+        del ws, X, nsets, counts
+    del stack, sub
+    torch.cuda.empty_cache()
+    return {"workload": "opt175b-48L-d12288-h96-ffn49152-fp16: 48 layers (one GPU's share), heads dense, 512 cached "
+                        "tokens per sequence, neuron keep 10% (4915) per sequence, union per layer",
+            "points": out, "warmup": W, "steps": K}
 
 
 def cpu_baseline(dims, wl, L, X, cfg, budget_s):
@@ -333,7 +495,7 @@ def cpu_baseline(dims, wl, L, X, cfg, budget_s):
     max_len = wl.n_ctx + 16
     K = synth.philox_tensor((1, dims.h, max_len, dims.d_h), SEED, 0, "K", 1.0, np.float16)
     V = synth.philox_tensor((1, dims.h, max_len, dims.d_h), SEED, 0, "V", 1.0, np.float16)
-    Xh = X[:16].cpu().numpy()
+    Xh = X.numpy()
     g = np.random.default_rng(SEED)
 
     def timing(threads):

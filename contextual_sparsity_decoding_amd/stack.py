@@ -13,6 +13,8 @@ the decode runs in libdv (dv_decode_stack).
 """
 from __future__ import annotations
 
+import copy
+import math
 from typing import List, Optional
 
 import torch
@@ -56,10 +58,65 @@ class Stack:
             self.y_buf.append(torch.zeros(batch, max_len, dims.d, device="cuda") if hole_fill else None)
             self.valid.append(torch.full((batch, dims.h), n_ctx - 1, dtype=torch.int32, device="cuda")
                               if hole_fill else None)
+        self.hole_fill = hole_fill
         self.pos_dev = torch.full((1,), n_ctx, dtype=torch.int32, device="cuda")
         self.wts = [dv.layer_weights(w) for w in self.W]
         self.sel = [None] * layers          # DV_KV_SELECT: (sel_idx, sel_len, sel_end) per layer
         self._arr = None
+
+    def set_context(self, n_ctx: int, max_len: int) -> None:
+        """New caches of max_len slots per layer with n_ctx positions filled
+        (the weights stay); clears any KV selection."""
+        d = self.dims
+        self.K, self.V, self._arr = [], [], None
+        self.sel = [None] * self.L
+        torch.cuda.empty_cache()
+        for l in range(self.L):
+            for name, lst in (("K", self.K), ("V", self.V)):
+                t = torch.empty(self.B, d.h, max_len, d.d_h, dtype=torch.float16, device="cuda")
+                dv.dv_fill_normal(t, self.seed, synth.stream_id(l, name))
+                lst.append(t)
+            if self.hole_fill:
+                self.y_buf[l] = torch.zeros(self.B, max_len, d.d, device="cuda")
+                self.valid[l] = torch.full((self.B, d.h), n_ctx - 1, dtype=torch.int32, device="cuda")
+        self.n_ctx, self.max_len = n_ctx, max_len
+        self.reset()
+
+    def select_kv(self, budget: int, n_obs: int = 64, n_sink: int = 4, width: int = 7) -> None:
+        """ByteCross §4.1 / App. A, once per layer after the seeded prompt: the
+        positions the last n_obs prompt queries (seeded N(0,1) fp16, one set
+        per layer) attend to most, smoothed, with the sinks and the
+        observation window forced in; the top `budget` per head are kept and
+        every position from n_ctx on (the decoded tokens) is always read."""
+        d, n = self.dims, self.n_ctx
+        scale = 1 / math.sqrt(d.d_h)
+        q = torch.empty(self.B, d.h, n_obs, d.d_h, dtype=torch.float16, device="cuda")
+        scores = torch.empty(self.B, d.h, n, device="cuda")
+        ws = dv.workspace(dv.dv_kv_score_workspace_bytes(self.B, d.h, n, n_obs))
+        for l in range(self.L):
+            dv.dv_fill_normal(q, self.seed, synth.stream_id(l, "q_obs"))
+            view = dv.kv_view(self.K[l], self.V[l], n)
+            dv.dv_kv_score(q, view, scale, n_sink, n_obs, width, scores, ws)
+            idx = torch.empty(self.B, d.h, budget, dtype=torch.int32, device="cuda")
+            dv.dv_topk_select(scores.view(self.B * d.h, n), budget, idx.view(self.B * d.h, budget))
+            lens = torch.full((self.B, d.h), budget, dtype=torch.int32, device="cuda")
+            self.sel[l] = (idx, lens, n)
+        self._arr = None
+
+    def batch_view(self, B: int) -> "Stack":
+        """The same layers with the first B sequences' caches (the stack's
+        batch is the caches' outermost dimension), sharing the decode position."""
+        if not 1 <= B <= self.B:
+            raise ValueError(f"batch {B} outside [1, {self.B}]")
+        v = copy.copy(self)
+        v.B = B
+        v.K = [k[:B] for k in self.K]
+        v.V = [t[:B] for t in self.V]
+        v.y_buf = [y[:B] if y is not None else None for y in self.y_buf]
+        v.valid = [t[:B] if t is not None else None for t in self.valid]
+        v.sel = [None] * self.L
+        v._arr = None
+        return v
 
     def reset(self) -> None:
         """Back to the seeded state: position n_ctx, every head valid up to n_ctx - 1
