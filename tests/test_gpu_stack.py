@@ -192,3 +192,135 @@ def test_stack_opt66b_sampled_layers(dvlib):
             ok_v, nv = f16_kv_ok(s["V_after"], kv.V)
             assert ok_k and ok_v, f"layer {l} token {t}: K off {nk}, V off {nv}"
             print(f"opt66b stack layer {l} token {t}: normwise {e:.2e}")
+
+
+def _union_follow(got_u, rec, k, what):
+    """The device's union of per-sequence neuron sets against the oracle's:
+    equal, or differing only in neurons that sit at some sequence's k-th
+    score within fp32 rounding.  Returns the union the oracle continues with."""
+    want = rec["neuron_idx"]
+    got_u = np.asarray(got_u, np.int64)
+    if np.array_equal(got_u, want):
+        return want
+    s = np.asarray(rec["neuron_scores"], np.float64)
+    kth = np.sort(s, axis=1)[:, ::-1][:, k - 1]
+    for j in set(got_u.tolist()) ^ set(want.tolist()):
+        assert np.any(np.abs(s[:, j] - kth) <= MARGIN * max(1.0, np.abs(s).max())), f"{what}: neuron {j}"
+    return got_u
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_stack_longctx_composed_sampled(dvlib):
+    """The 32-layer long-context stack (d = 4096, 32 heads, d_ffn = 16384) at
+    8192 cached tokens in the composed mode: 10% of each head's positions
+    chosen by the attention-scored selection (plus the decoded tokens), 10%
+    of neurons.  The selection of sampled heads against the oracle's; layers
+    {0, 15, 31} at tokens {0, 2} rerun by the oracle from the device's state."""
+    from contextual_sparsity_decoding_amd.stack import Stack
+    wl = configs.LONGCTX_STACK
+    dims, L, n, T, seed = wl.dims, wl.layers, 8192, 3, 515
+    b, kM = int(wl.kv_keep * n), wl.k_neurons
+    scale = 1 / math.sqrt(dims.d_h)
+    S = Stack(dims, L, n, n + T + 4, seed, hole_fill=False)
+    S.select_kv(b)
+    flags = dvlib.DV_DENSE_ATTN | dvlib.DV_KV_SELECT | dvlib.DV_SKIP_NONPOS_FC2 | dvlib.DV_ADVANCE_POS
+    cfg = S.cfg(dims.h, kM, flags, scale)
+    ws = dvlib.workspace(dvlib.dv_stack_workspace_bytes(cfg, S.max_len))
+    nsets = torch.full((L, kM), -1, dtype=torch.int32, device="cuda")
+    x_trace = torch.empty(L - 1, 1, dims.d, device="cuda")
+    x_out = torch.empty(1, dims.d, device="cuda")
+    X = torch.empty(T, 1, dims.d, device="cuda")
+    dvlib.dv_fill_normal(X, seed, synth.stream_id(0, "x"))
+    layers, tokens = (0, 15, 31), (0, 2)
+    # the selection itself, for two heads of layer 15, against the oracle's
+    Kh = synth.philox_tensor((1, dims.h, S.max_len, dims.d_h), seed, 15, "K", 1.0, np.float16)
+    assert np.array_equal(host(S.K[15]), Kh)
+    Q = synth.philox_tensor((1, dims.h, 64, dims.d_h), seed, 15, "q_obs", 1.0, np.float16)
+    sel15 = host(S.sel[15][0])
+    for i in (0, 19):
+        want_idx, sm = ref.kv_select(Q[0, i], Kh[0, i], n, scale, b, n_sink=4, n_window=64, width=7)
+        forced = sm.copy()
+        forced[:4] = np.inf
+        forced[n - 64:] = np.inf
+        assert_selection_close(sel15[0, i], want_idx, forced, b, 1e-5 * max(1.0, np.abs(sm).max()), f"head {i}")
+    snaps = {}
+    for t in range(T):
+        if t in tokens:
+            for l in layers:
+                snaps[(l, t)] = {"K": host(S.K[l]), "V": host(S.V[l])}
+        dvlib.dv_decode_stack(S.layers_array(), cfg, X[t], x_out, ws, neuron_sets=nsets, x_trace=x_trace)
+        if t in tokens:
+            tr, xo, ns = host(x_trace), host(x_out), host(nsets)
+            for l in layers:
+                snaps[(l, t)].update(x_in=host(X[t]) if l == 0 else tr[l - 1], x_out=tr[l] if l + 1 < L else xo,
+                                     neurons=ns[l], sel=host(S.sel[l][0]), sel_len=host(S.sel[l][1]))
+    torch.cuda.synchronize()
+    del S, ws
+    torch.cuda.empty_cache()
+    for l in layers:
+        W = synth.stack_layer_weights(dims, seed, l)
+        for t in tokens:
+            s = snaps[(l, t)]
+            kv = ref.KVState(s["K"].copy(), s["V"].copy())
+            want, rec = ref.decode_layer(s["x_in"], W, kv, n + t, k_heads=dims.h, k_neurons=kM, scale=scale,
+                                         dense_attn=True, skip_nonpos=True, hole_fill=False, sel_idx=s["sel"],
+                                         sel_len=s["sel_len"], sel_end=n)
+            used = _follow(s["neurons"], rec["neuron_idx"], rec["neuron_scores"][0], kM, f"layer {l} token {t}")
+            if used is not rec["neuron_idx"]:
+                want, _ = ref.sparse_mlp(rec["y2"], W["w1_t"], W["b1"], W["w2_t"], W["b2"], used, residual=rec["h"],
+                                         skip_nonpos=True)
+            e = check_close(s["x_out"], want, "f16", f"longctx layer {l} token {t}")
+            print(f"longctx stack layer {l} token {t}: normwise {e:.2e}")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_stack_opt175b_batch16_union_sampled(dvlib):
+    """Four layers at the OPT-175B share's width (d = 12288, 96 heads dense,
+    d_ffn = 49152) decoding 16 sequences with 512 cached tokens each; every
+    layer's MLP reads the union of the 16 top-10% neuron sets.  Layers {0, 3}
+    at tokens {0, 1} rerun by the oracle from the device's state."""
+    from contextual_sparsity_decoding_amd.stack import Stack
+    wl = configs.OPT175B_SHARE
+    dims, L, n, T, B, seed = wl.dims, 4, wl.n_ctx, 2, 16, 177
+    kM = wl.k_neurons
+    scale = 1 / math.sqrt(dims.d_h)
+    S = Stack(dims, L, n, n + T + 4, seed, batch=B, hole_fill=False)
+    flags = dvlib.DV_DENSE_ATTN | dvlib.DV_SKIP_NONPOS_FC2 | dvlib.DV_ADVANCE_POS
+    cfg = S.cfg(dims.h, kM, flags, scale)
+    ws = dvlib.workspace(dvlib.dv_stack_workspace_bytes(cfg, S.max_len))
+    nmax = min(dims.N, B * kM)
+    usets = torch.full((L, nmax), -1, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(L, dtype=torch.int32, device="cuda")
+    x_trace = torch.empty(L - 1, B, dims.d, device="cuda")
+    x_out = torch.empty(B, dims.d, device="cuda")
+    X = torch.empty(T, B, dims.d, device="cuda")
+    dvlib.dv_fill_normal(X, seed, synth.stream_id(B, "x"))
+    layers = (0, 3)
+    snaps = {}
+    for t in range(T):
+        for l in layers:
+            snaps[(l, t)] = {"K": host(S.K[l]), "V": host(S.V[l])}
+        dvlib.dv_decode_stack(S.layers_array(), cfg, X[t], x_out, ws, neuron_sets=usets, neuron_counts=counts,
+                              x_trace=x_trace)
+        tr, xo, us, uc = host(x_trace), host(x_out), host(usets), host(counts)
+        for l in layers:
+            snaps[(l, t)].update(x_in=host(X[t]) if l == 0 else tr[l - 1], x_out=tr[l] if l + 1 < L else xo,
+                                 union=us[l, :uc[l]])
+    torch.cuda.synchronize()
+    del S, ws
+    torch.cuda.empty_cache()
+    for l in layers:
+        W = synth.stack_layer_weights(dims, seed, l)
+        for t in range(T):
+            s = snaps[(l, t)]
+            kv = ref.KVState(s["K"].copy(), s["V"].copy())
+            want, rec = ref.decode_layer(s["x_in"], W, kv, n + t, k_heads=dims.h, k_neurons=kM, scale=scale,
+                                         dense_attn=True, skip_nonpos=True, hole_fill=False)
+            used = _union_follow(s["union"], rec, kM, f"layer {l} token {t}")
+            if used is not rec["neuron_idx"]:
+                want, _ = ref.sparse_mlp(rec["y2"], W["w1_t"], W["b1"], W["w2_t"], W["b2"], used, residual=rec["h"],
+                                         skip_nonpos=True)
+            e = check_close(s["x_out"], want, "f16", f"batched layer {l} token {t}")
+            print(f"batch-16 stack layer {l} token {t}: |U| = {len(s['union'])}, normwise {e:.2e}")
