@@ -15,7 +15,8 @@ namespace dv {
 // DejaVu §4.2: for the selected heads compute q, k, v; store k, v in the
 // cache; keep y for the heads not selected; recompute a selected head's
 // missing K/V from the stored inputs, reusing the weight rows already held
-// in registers.  Rows are ordered [which][s][e].
+// in registers.  Rows are ordered [which][s][e]; workgroups take the K and
+// V blocks before the Q blocks.
 struct QkvArgs {
     const float* y;
     int B, d, h, dh, n_sel;
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int r0 = qb * 4 * R;                         // 4*R divides dh: one head block per workgroup
-    const int which = r0 / (a.n_sel * dh);
+    // the K and V blocks (which may carry missing positions) are dispatched
+    // first and the Q blocks last, so cheap uniform blocks fill the tail
+    const int which = (r0 / (a.n_sel * dh) + 1) % 3;
     const int s = (r0 / dh) % a.n_sel;
     const int e0 = r0 % dh + wv * R;                   // this wave's first row in the block
     const int nchunk = d / E;
