@@ -83,6 +83,7 @@ static float* predict_part(void* ws) { return ws ? (float*)((char*)ws + kCounter
 struct MlpWs {
     float* a;
     float* partial;
+    float* mpart;             // the matrix-core fc1's partial sums (batches of 8-16), or NULL
     size_t bytes;
 };
 static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a) {
@@ -91,6 +92,7 @@ static MlpWs mlp_ws(void* ws, int B, int d, int n_idx_max, int wdt, bool need_a)
     w.a = need_a ? cv.take<float>((size_t)B * (n_idx_max > 0 ? n_idx_max : 1)) : nullptr;
     const AxpyPlan p = axpy_plan(d, n_idx_max, wdt);
     w.partial = cv.take<float>(axpy_ws_floats(p, B, d));
+    w.mpart = rowdot_mfma_ok(B, d, wdt) ? cv.take<float>(rowdot_mfma_part_floats(n_idx_max)) : nullptr;
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -136,7 +138,8 @@ dv_status sparse_mlp_call(const char* who, const float* y, int B, int d, int N, 
     REQ(ws && ws_bytes >= w.bytes, DV_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, w.bytes);
     if (!run) return DV_OK;
     float* a = act_out ? act_out : w.a;
-    TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
+    if (w.mpart) TRY(launch_fc1_mfma(y, B, d, w1_t, b1, idx, n_idx_max, n_idx_dev, N, a, w.mpart, s));
+    else TRY(launch_fc1(y, B, d, w1_t, b1, wdt, idx, n_idx_max, n_idx_dev, N, a, s));
     AxpyCall c{};
     c.w = w2_t; c.wdt = wdt; c.d = d; c.w_rows = N; c.rows = n_idx_max; c.n_rows_dev = n_idx_dev; c.idx = idx; c.blk = 1;
     c.coef = a; c.coef_stride = n_idx_max; c.skip_zero = (flags & DV_SKIP_NONPOS_FC2) != 0;
@@ -353,6 +356,7 @@ dv_status dv_kv_score(const void* q_obs, int B, int h, int d_h, int n_obs, const
 struct LayerWs {
     float *y, *hres, *y2, *hpart, *sA, *sM, *q, *o, *apart, *a, *xpart;
     float *ya, *hpartA, *hpartM, *sA2, *sM2;      // the look-ahead predictions' own scratch
+    float* mpart;                                 // matrix-core row-dot partial sums (batches of 8-16), or NULL
     unsigned* khist;                              // [4096] top-12-bit histogram of the next layer's neuron scores
     uint32_t* kkeys;                              // [N] their order keys
     void* kthr;                                   // their selection threshold
@@ -400,6 +404,8 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     w.khist = cv.take<unsigned>(4096);
     w.kkeys = cv.take<uint32_t>((size_t)c->N);
     w.kthr = cv.take<unsigned>(4);
+    const size_t mp = rowdot_mfma_part_floats(nmax > 3 * nsel * dh ? nmax : 3 * nsel * dh);
+    w.mpart = rowdot_mfma_ok(B, d, c->wdt) ? cv.take<float>(mp) : nullptr;
     w.bytes = align_up(cv.off, 256);
     return w;
 }
@@ -691,7 +697,10 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
     }
     const bool fill = kvs.y_buf && kvs.valid_upto;
     timed_begin(DV_KERNEL_QKV, s);
-    TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
+    if (L.mpart && !fill)
+        TRY(launch_qkv_mfma(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, L.q, &kvs, L.mpart, s));
+    else
+        TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
     timed_end(DV_KERNEL_QKV, s);
     // split-K partials go straight into the output projection, which merges them per row
     int splits = 0;
@@ -732,7 +741,8 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
         TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
     }
     timed_begin(DV_KERNEL_FC1, s);
-    TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
+    if (L.mpart) TRY(launch_fc1_mfma(L.y2, B, d, w->w1_t, w->b1, idx, n_max, n_dev, N, L.a, L.mpart, s));
+    else TRY(launch_fc1(L.y2, B, d, w->w1_t, w->b1, c->wdt, idx, n_max, n_dev, N, L.a, s));
     timed_end(DV_KERNEL_FC1, s);
     AxpyCall mc{};
     mc.w = w->w2_t; mc.wdt = c->wdt; mc.d = d; mc.w_rows = N; mc.rows = n_max; mc.n_rows_dev = n_dev; mc.idx = idx;

@@ -317,6 +317,15 @@ dv_status sparse_mlp_call(const char* who, const float* y, int B, int d, int N, 
                           const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
                           int32_t* fc2_rows, unsigned flags, void* ws, size_t ws_bytes, hipStream_t s,
                           bool run = true);
+// Batched row-dots on the matrix cores (k_rowdot_mfma.hip), B in [8, 16],
+// fp16 weights, d % 32 == 0; `part` holds rowdot_mfma_part_floats floats.
+bool rowdot_mfma_ok(int B, int d, int wdt);
+size_t rowdot_mfma_part_floats(int n_max);
+dv_status launch_fc1_mfma(const float* y, int B, int d, const void* w1_t, const void* b1, const int32_t* idx,
+                          int n_max, const int32_t* n_dev, int N, float* a_out, float* part, hipStream_t s);
+dv_status launch_qkv_mfma(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
+                          const void* w, const void* bias, float* q, const dv_kv_state* kv, float* part,
+                          hipStream_t s);
 dv_status launch_fill_normal(void* out, uint64_t n, int dtype, uint64_t seed, uint64_t stream, uint64_t offset,
                              float mean, float stdv, hipStream_t s);
 

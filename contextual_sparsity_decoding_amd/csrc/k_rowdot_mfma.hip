@@ -1,0 +1,231 @@
+// Batched row-dot products on the matrix cores: for a batch of 8-16 decode
+// rows every fp16 weight row meets 8-16 inputs, so sparse fc1 over the
+// batch's union of neurons (DejaVu §5.2 / App. C.1) and the Q/K/V
+// projections become a skinny dense contraction
+//     out[b][u] = sum_k y[b][k] * W[row(u)][k]        (b < B <= 16)
+// that the vector ALUs cannot keep up with at HBM speed (16 FMAs per weight
+// element; rocprof shows the VALU paths reading y again for every row).
+//
+// Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
+// Inference Time" (arXiv 2310.17157), §2.3 Eq. 1-2 (the products), §5.2
+// and App. C.1 (the batch runs over the union of its sets).
+//
+// v_mfma_f32_16x16x32_f16: A = 16 x 32 (batch x k), B = 32 x 16 (k x rows),
+// fp32 accumulate.  Lane l supplies A row l % 16 and B column l % 16, both
+// at k = 8 (l / 16) .. +7, so its B operand is 16 contiguous bytes of one
+// weight row: a wave's load covers 64 bytes of each of 16 rows.  The fp32
+// inputs are split into fp16 hi + lo (hi = fp16(y), lo = fp16(y - hi)) and
+// both go through the matrix core, so the inputs keep about 22 bits.
+//
+// A wave owns RT tiles of 16 rows over one of KS ranges of k; its partial
+// sums go to a [KS][16][n_max] buffer and a second launch adds the ranges in
+// order and applies the epilogue (fc1: bias and ReLU; Q/K/V: bias, q in
+// fp32 and K/V into the cache in fp16).
+#include "dv_internal.h"
+
+namespace dv {
+
+typedef _Float16 f16x8m __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaRT = 4;          // 16-row tiles per wave
+constexpr int kMfmaPF = 4;          // k-steps of weight loads in flight
+constexpr int kMfmaMaxKS = 8;
+
+struct MfmaArgs {
+    const float* y;           // [B][d]
+    int B, d;
+    const half_t* w;          // rows of d
+    int w_rows;
+    // fc1: row(u) = idx[u] (or u); Q/K/V: u = (which * n_sel + s) * dh + e,
+    // row = (which * h + head(s)) * dh + e
+    const int32_t* idx;
+    int qkv, n_sel, dh, h;
+    const int32_t* head_idx;
+    int n_max;
+    const int32_t* n_dev;
+    int ks, steps_per_split;  // k ranges and their length in 32-element steps
+    float* part;              // [ks][16][n_max]
+};
+
+__device__ __forceinline__ int mfma_row(const MfmaArgs& a, int u, int n) {
+    if (u >= n) return -1;
+    int j;
+    if (a.qkv) {
+        const int which = u / (a.n_sel * a.dh), s = (u / a.dh) % a.n_sel, e = u % a.dh;
+        const int head = a.head_idx ? a.head_idx[s] : s;
+        if ((unsigned)head >= (unsigned)a.h) return -1;
+        j = (which * a.h + head) * a.dh + e;
+    } else {
+        j = a.idx ? a.idx[u] : u;
+    }
+    return (unsigned)j < (unsigned)a.w_rows ? j : -1;
+}
+
+__global__ __launch_bounds__(kBlock) void k_rowdot_mfma(MfmaArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+    const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
+    const int tile = wid / a.ks, ksi = wid % a.ks;
+    const int u0 = tile * 16 * kMfmaRT;
+    if (u0 >= n) return;                                   // whole wave idle
+    const int nsteps = a.d / 32;
+    const int st0 = ksi * a.steps_per_split, st1 = min(nsteps, st0 + a.steps_per_split);
+    const int col = lane & 15, kq = lane >> 4;             // B column / A row, k block of 8
+    const half_t* rowp[kMfmaRT];
+    bool rv[kMfmaRT];
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) {
+        const int j = mfma_row(a, u0 + 16 * t + col, n);
+        rv[t] = j >= 0;
+        rowp[t] = a.w + (size_t)(j >= 0 ? j : 0) * a.d + 8 * kq;
+    }
+    const bool yrow = col < a.B;                           // A row = batch row
+    const float* yp = a.y + (size_t)(yrow ? col : 0) * a.d + 8 * kq;
+    f32x4 acc[kMfmaRT];
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 wr[kMfmaPF][kMfmaRT];
+    auto load_w = [&](int st, int slot) {
+#pragma unroll
+        for (int t = 0; t < kMfmaRT; ++t)
+            wr[slot][t] = (st < st1 && rv[t]) ? ld16_stream(rowp[t] + (size_t)st * 32) : u32x4{0u, 0u, 0u, 0u};
+    };
+#pragma unroll
+    for (int p = 0; p < kMfmaPF; ++p) load_w(st0 + p, p);
+    for (int st = st0; st < st1; st += kMfmaPF) {
+#pragma unroll
+        for (int p = 0; p < kMfmaPF; ++p) {
+            const int s = st + p;
+            if (s < st1) {                                 // uniform over the wave
+                f32x4 y0 = f32x4{0.f, 0.f, 0.f, 0.f}, y1 = y0;
+                if (yrow) {
+                    y0 = *reinterpret_cast<const f32x4*>(yp + (size_t)s * 32);
+                    y1 = *reinterpret_cast<const f32x4*>(yp + (size_t)s * 32 + 4);
+                }
+                f16x8m hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = (half_t)y0[e];
+                    hi[4 + e] = (half_t)y1[e];
+                    lo[e] = (half_t)(y0[e] - (float)hi[e]);
+                    lo[4 + e] = (half_t)(y1[e] - (float)hi[4 + e]);
+                }
+#pragma unroll
+                for (int t = 0; t < kMfmaRT; ++t) {
+                    const f16x8m wb = __builtin_bit_cast(f16x8m, wr[p][t]);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, wb, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, wb, acc[t], 0, 0, 0);
+                }
+                load_w(s + kMfmaPF, p);                    // the slot just consumed takes step s + PF
+            }
+        }
+    }
+    // D: lane l, register i = row (batch) 4 (l / 16) + i, column (tile row) l % 16
+    float* P = a.part + (size_t)ksi * 16 * a.n_max;
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) {
+        const int u = u0 + 16 * t + col;
+        if (u < a.n_max) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = 4 * kq + i;
+                if (b < a.B) P[(size_t)b * a.n_max + u] = acc[t][i];
+            }
+        }
+    }
+}
+
+struct MfmaEpi {
+    const float* part;
+    int ks, B, n_max;
+    const int32_t* n_dev;
+    const void* bias;
+    // fc1: out[b][n_max] = relu(sum + b1[row]); Q/K/V: q and the cache
+    float* out;
+    half_t* K;
+    half_t* V;
+    int max_len, pos;
+    const int32_t* pos_dev;
+};
+
+__global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi e) {
+    const int n = e.n_dev ? min(*e.n_dev, e.n_max) : e.n_max;
+    const int i = blockIdx.x * kBlock + threadIdx.x;       // (b, u)
+    if (i >= e.B * e.n_max) return;
+    const int b = i / e.n_max, u = i % e.n_max;
+    if (u >= n) return;
+    float v = 0.f;
+    for (int k = 0; k < e.ks; ++k) v += e.part[((size_t)k * 16 + b) * e.n_max + u];
+    const int j = mfma_row(a, u, n);
+    const half_t* bias = (const half_t*)e.bias;
+    if (!a.qkv) {
+        e.out[(size_t)b * e.n_max + u] = j >= 0 ? fmaxf(v + (float)bias[j], 0.f) : 0.f;
+        return;
+    }
+    if (j < 0) return;
+    v += (float)bias[j];
+    const int which = u / (a.n_sel * a.dh), s = (u / a.dh) % a.n_sel, el = u % a.dh;
+    if (which == 0) {
+        e.out[((size_t)b * a.n_sel + s) * a.dh + el] = v;
+        return;
+    }
+    const int pos = e.pos_dev ? *e.pos_dev : e.pos;
+    if (pos < 0 || pos >= e.max_len) return;
+    const int head = a.head_idx ? a.head_idx[s] : s;
+    (which == 1 ? e.K : e.V)[(((size_t)b * a.h + head) * e.max_len + pos) * a.dh + el] = (half_t)v;
+}
+
+}  // namespace dv
+
+namespace dvh {
+using namespace dv;
+
+bool rowdot_mfma_ok(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == DV_F16 && d % 32 == 0; }
+
+size_t rowdot_mfma_part_floats(int n_max) { return (size_t)kMfmaMaxKS * 16 * (n_max > 0 ? n_max : 1); }
+
+static void mfma_split(MfmaArgs& a) {
+    const int nsteps = a.d / 32;
+    const int tiles = cdiv(a.n_max > 0 ? a.n_max : 1, 16 * kMfmaRT);
+    int ks = cdiv(4096, tiles);                            // about 4096 waves in all
+    ks = ks < 1 ? 1 : ks > kMfmaMaxKS ? kMfmaMaxKS : ks;
+    if (ks > nsteps) ks = nsteps;
+    a.steps_per_split = cdiv(nsteps, ks);
+    a.ks = cdiv(nsteps, a.steps_per_split);
+}
+
+static dv_status mfma_go(MfmaArgs& a, MfmaEpi& e, hipStream_t s) {
+    if (a.n_max == 0) return DV_OK;
+    mfma_split(a);
+    e.part = a.part; e.ks = a.ks; e.B = a.B; e.n_max = a.n_max; e.n_dev = a.n_dev;
+    const int waves = cdiv(a.n_max, 16 * kMfmaRT) * a.ks;
+    hipLaunchKernelGGL(k_rowdot_mfma, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_rowdot_mfma_epi, dim3(cdiv((long)a.B * a.n_max, kBlock)), dim3(kBlock), 0, s, a, e);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return DV_OK;
+}
+
+dv_status launch_fc1_mfma(const float* y, int B, int d, const void* w1_t, const void* b1, const int32_t* idx,
+                          int n_max, const int32_t* n_dev, int N, float* a_out, float* part, hipStream_t s) {
+    MfmaArgs a{};
+    a.y = y; a.B = B; a.d = d; a.w = (const half_t*)w1_t; a.w_rows = N; a.idx = idx; a.qkv = 0;
+    a.n_max = n_max; a.n_dev = n_dev; a.part = part;
+    MfmaEpi e{};
+    e.bias = b1; e.out = a_out;
+    return mfma_go(a, e, s);
+}
+
+dv_status launch_qkv_mfma(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
+                          const void* w, const void* bias, float* q, const dv_kv_state* kv, float* part,
+                          hipStream_t s) {
+    MfmaArgs a{};
+    a.y = y; a.B = B; a.d = d; a.w = (const half_t*)w; a.w_rows = 3 * h * d_h; a.qkv = 1; a.n_sel = n_sel;
+    a.dh = d_h; a.h = h; a.head_idx = head_idx; a.n_max = 3 * n_sel * d_h; a.n_dev = nullptr; a.part = part;
+    MfmaEpi e{};
+    e.bias = bias; e.out = q; e.K = (half_t*)kv->k_cache; e.V = (half_t*)kv->v_cache; e.max_len = kv->max_len;
+    e.pos = kv->pos; e.pos_dev = kv->pos_dev;
+    return mfma_go(a, e, s);
+}
+
+}  // namespace dvh

@@ -161,6 +161,29 @@ def test_batch_union_decode(dvlib):
     assert rows == int(np.sum(np.any(rec["a"] > 0, axis=0)))
 
 
+@pytest.mark.parametrize("B", [8, 13, 16])
+def test_batch_union_decode_matrix_cores(dvlib, B):
+    """Batches of 8-16 with every head (no stored inputs): Q/K/V and fc1 run
+    on the matrix cores; every sequence's output, K/V entry and the union
+    against the oracle."""
+    from tests.test_gpu_stack import _union_follow
+    dims = LayerDims(d=1024, N=4096, h=8, d_h=128, r_attn=16, r_mlp=32, wdt="f16")
+    L = Layer(dvlib, dims, 30, 36, seed=40 + B, B=B)
+    x = synth.layer_inputs(dims.d, 1, B, seed=40 + B)[0]
+    flags = dvlib.DV_DENSE_ATTN | dvlib.DV_SKIP_NONPOS_FC2
+    out, _, ni, rows = L.step(x, 30, 8, 300, flags)
+    want, rec = L.oracle(x, 30, 8, 300, flags)
+    used = _union_follow(ni, rec, 300, f"batch {B}")
+    if used is not rec["neuron_idx"]:
+        want, _ = ref.sparse_mlp(rec["y2"], L.W["w1_t"], L.W["b1"], L.W["w2_t"], L.W["b2"], used,
+                                 residual=rec["h"], skip_nonpos=True)
+    e = check_close(out, want, "f16", f"batch {B}")
+    ok_k, nk = f16_kv_ok(host(L.K), L.okv.K)
+    ok_v, nv = f16_kv_ok(host(L.V), L.okv.V)
+    assert ok_k and ok_v, f"K entries off: {nk}, V entries off: {nv}"
+    print(f"batch {B}: |U| = {len(ni)}, normwise {e:.2e}")
+
+
 def test_kv_selected_decode(dvlib):
     dims = LayerDims(d=512, N=2048, h=8, d_h=128, r_attn=16, r_mlp=32, wdt="f16")
     n, budget = 400, 100
