@@ -361,8 +361,8 @@ def bench_longctx(torch, dv, synth, configs, args):
     """ByteCross's composition at long context (§3.3, §4.1-4.2): a 32-layer
     stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 32K / 128K cached
     tokens in four modes through the same kernels and the same split-K
-    attention: dense; projection-only (10% of MLP neurons, the sequential
-    form); KV-only (10% of cached positions per head chosen by the
+    attention: dense; projection-only (10% of MLP neurons, predicted one
+    layer ahead); KV-only (10% of cached positions per head chosen by the
     attention-scored selection, plus the decoded tokens); composed.  The
     selection's scoring pass runs once per context after the seeded prompt
     and is timed on its own, outside tokens/s."""
@@ -377,10 +377,12 @@ def bench_longctx(torch, dv, synth, configs, args):
     X = torch.empty(T, 1, dims.d, device="cuda")
     dv.dv_fill_normal(X, SEED + 5, synth.stream_id(0, "x"))
     base = dv.DV_DENSE_ATTN | dv.DV_ADVANCE_POS
+    ahead = dv.DV_SKIP_NONPOS_FC2 | dv.DV_LOOKAHEAD       # neuron sets predicted one layer ahead (DejaVu 4.3)
     modes = {"dense": (base | dv.DV_DENSE_MLP, dims.N),
-             "proj": (base | dv.DV_SKIP_NONPOS_FC2, kM),
+             "proj": (base | ahead, kM),
              "kv": (base | dv.DV_DENSE_MLP | dv.DV_KV_SELECT, dims.N),
-             "composed": (base | dv.DV_SKIP_NONPOS_FC2 | dv.DV_KV_SELECT, kM)}
+             "composed": (base | ahead | dv.DV_KV_SELECT, kM)}
+    nsets = torch.zeros(L, kM, dtype=torch.int32, device="cuda")
     out = []
     for n in wl.ctx_sweep:
         b = int(math.floor(wl.kv_keep * n))
@@ -399,7 +401,8 @@ def bench_longctx(torch, dv, synth, configs, args):
         res = {}
         for name, (flags, k) in modes.items():
             cfg = stack.cfg(dims.h, k, flags, scale)
-            ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K)
+            ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K,
+                                  neuron_sets=nsets if flags & dv.DV_LOOKAHEAD else None)
             sel = bool(flags & dv.DV_KV_SELECT)
             n_att = (b if sel else n) + W + (K - 1) / 2 + 1
             by = L * dv.dv_bytes_read(cfg, n_att, rows if not (flags & dv.DV_DENSE_MLP) else dims.N, 0.0).total
@@ -419,7 +422,7 @@ def bench_longctx(torch, dv, synth, configs, args):
                 f = a0 / (a0 - a1)
                 return round(math.exp(math.log(n0) + f * (math.log(n1) - math.log(n0))))
         return None
-    del stack, X
+    del stack, X, nsets
     torch.cuda.empty_cache()
     return {"workload": "longctx-32L-d4096-h32-ffn16384-fp16: 32 layers, batch 1, neuron keep 10% (1638), "
                         "KV keep 10% per head (attention-scored, 4 sinks + 64-token window forced), heads dense",

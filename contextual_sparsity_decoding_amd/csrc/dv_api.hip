@@ -525,16 +525,20 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     const bool dense_a = (c->flags & DV_DENSE_ATTN) != 0, dense_m = (c->flags & DV_DENSE_MLP) != 0;
     const bool predict = st->next_pa1_t || st->next_pm1_t;
     hipStream_t ps = st->aux_stream ? (hipStream_t)st->aux_stream : s;
-    const bool pair = st->next_pa1_t && st->next_pm1_t && c->k_heads > 0 && c->k_neurons > 0 &&
-                      row_ln_supported(d, c->wdt) && pred_topk_fusable(1, h, c->r_attn);
+    const bool pa = st->next_pa1_t && c->k_heads > 0;      // the next layer's head set is predicted
+    const bool pm = st->next_pm1_t && c->k_neurons > 0;    // the next layer's neuron set is predicted
     // Without a second stream the predictions ride in this layer's launches
-    // as extra workgroups: both first layers in the Q/K/V launch (same
-    // LN1(x)), both second layers in the attention launch, and the neuron
-    // selection split over later launches: a histogram of the scores beside
-    // the output projection, the threshold beside its finalize and the
-    // ordered emission beside fc2 (else a launch of its own after attention).
-    const bool ride = pair && !st->aux_stream && ln_fusable(1, d);
-    const bool ride_topk = ride && topk_split_supported(N, c->k_neurons);
+    // as extra workgroups: the predictors' first layers in the Q/K/V launch
+    // (same LN1(x)), their second layers (and the head selection) in the
+    // attention launch, and the neuron selection split over later launches:
+    // a histogram of the scores beside the output projection, the threshold
+    // beside its finalize and the ordered emission beside fc2 (else a
+    // launch of its own after attention).  Either predictor may be absent
+    // (every head, or every neuron, is used).
+    const bool ride = (pa || pm) && !st->aux_stream && ln_fusable(1, d) && row_ln_supported(d, c->wdt) &&
+                      (!pa || pred_topk_fusable(1, h, c->r_attn));
+    const bool ride_topk = ride && pm && topk_split_supported(N, c->k_neurons);
+    const int rA = pa ? c->r_attn : 0, rM = pm ? c->r_mlp : 0;
     if (predict && st->aux_stream) {
         HIP_TRY(hipEventRecord((hipEvent_t)st->ev_fork, s));
         HIP_TRY(hipStreamWaitEvent(ps, (hipEvent_t)st->ev_fork, 0));
@@ -555,9 +559,12 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     }
     const bool fill = kvs.y_buf && kvs.valid_upto;
     RowArgs p1{};
-    if (ride) {
-        p1.B = 1; p1.d = d; p1.w = st->next_pa1_t; p1.w2 = st->next_pm1_t; p1.split = c->r_attn;
-        p1.n_max = c->r_attn + c->r_mlp; p1.w_rows = p1.n_max; p1.out = L.hpartA;
+    if (ride) {   // hidden rows: the head predictor's rA, then the neuron predictor's rM
+        p1.B = 1; p1.d = d;
+        p1.w = pa ? st->next_pa1_t : st->next_pm1_t;
+        p1.w2 = pa && pm ? st->next_pm1_t : nullptr;
+        p1.split = pa && pm ? rA : rA + rM;
+        p1.n_max = rA + rM; p1.w_rows = p1.n_max; p1.out = L.hpartA;
     }
     if (ln_fusable(1, d)) {
         timed_begin(DV_KERNEL_QKV, s);
@@ -571,14 +578,15 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
         timed_end(DV_KERNEL_QKV, s);
     }
     int splits = 0;
-    Pred2Args p2 = pred2_args(L.hpartA, c->r_attn, st->next_pa2_t, h, L.sA2, c->k_heads, st->next_head_idx,
-                              L.hpartA + c->r_attn, c->r_mlp, st->next_pm2_t, N, L.sM2, c->pred_act, c->wdt);
+    Pred2Args p2 = pred2_args(L.hpartA, rA, pa ? st->next_pa2_t : nullptr, pa ? h : 0, L.sA2, pa ? c->k_heads : 0,
+                              st->next_head_idx, L.hpartA + rA, rM, pm ? st->next_pm2_t : nullptr, pm ? N : 0, L.sM2,
+                              c->pred_act, c->wdt);
     p2.zero = ride_topk ? L.khist : nullptr;
     timed_begin(DV_KERNEL_ATTN, s);
     TRY(launch_splitk(L.q, 1, dh, head_idx, n_sel, &view, st->kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
                       fill ? kvs.valid_upto : nullptr, st->kv.pos, st->kv.pos_dev, s, &splits, ride ? &p2 : nullptr));
     timed_end(DV_KERNEL_ATTN, s);
-    if (ride && !ride_topk) TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, s));
+    if (ride && pm && !ride_topk) TRY(launch_topk(L.sM2, 1, N, c->k_neurons, st->next_neuron_idx, s));
     const TopkSel tk{L.sM2, N, c->k_neurons, L.khist, L.kkeys, L.kthr, st->next_neuron_idx};
     {
         AxpyCall ac{};

@@ -265,7 +265,8 @@ __device__ __forceinline__ void pred2_pair_block(int blk, float* hid /* LDS [r_m
     if (blk == 0) {
         if (a.zero)
             for (int i = threadIdx.x; i < 4096; i += kBlock) a.zero[i] = 0u;
-        pred_topk_small_block<T>(a.hid_a, a.r_a, a.act, (const T*)a.p2_a, a.n_a, a.s_a, a.k_a, a.idx_a);
+        if (a.n_a > 0)                                  // the head predictor, when it rides
+            pred_topk_small_block<T>(a.hid_a, a.r_a, a.act, (const T*)a.p2_a, a.n_a, a.s_a, a.k_a, a.idx_a);
     }
     else
         pred_scores_block<T, 1>(blk - 1, hid, a.hid_m, 1, a.r_m, a.act, (const T*)a.p2_m, a.n_m, a.lpr,

@@ -228,3 +228,35 @@ def test_lookahead_graph(dvlib, aux):
             e = normwise(host(outs[p]), want[t0 + p])
             assert e < 1e-5, f"replay step {t0 + p}: normwise {e:.2e}"
     assert int(host(pos_dev)[0]) == n0 + 2 * replays
+
+
+@pytest.mark.parametrize("d,N,k_m", [(1024, 4096, 400), (4096, 16384, 1638)])
+def test_lookahead_neuron_predictor_alone(dvlib, d, N, k_m):
+    """Every head (no head predictor) and the neuron set predicted one layer
+    ahead: the neuron predictor alone rides in the layer's launches."""
+    dims = LayerDims(d=d, N=N, h=8, d_h=128, r_attn=32, r_mlp=64, wdt="f16")
+    n0, T = 30, 3
+    A = Ahead(dvlib, dims, n0, n0 + T + 2, seed=43, k_heads=dims.h, k_neurons=k_m)
+    X = synth.layer_inputs(dims.d, T, 1, seed=43)
+    flags = dvlib.DV_LOOKAHEAD | dvlib.DV_DENSE_ATTN | dvlib.DV_SKIP_NONPOS_FC2
+    cfg = A.cfg(flags)
+    ws = dvlib.workspace(dvlib.dv_decode_workspace_bytes(cfg, A.max_len))
+    g = np.random.default_rng(8)
+    ni = np.sort(g.choice(N, k_m, replace=False)).astype(np.int32)
+    dummy = torch.zeros(dims.h, dtype=torch.int32, device="cuda")
+    for t in range(T):
+        ni_d = dev(ni)
+        nn = torch.full((k_m,), -1, dtype=torch.int32, device="cuda")
+        out = torch.empty(1, dims.d, device="cuda")
+        st = A.state(n0 + t, dummy, ni_d, dummy, nn)
+        st.next_pa1_t = st.next_pa2_t = 0                      # no head predictor
+        dvlib.dv_decode_layer(A.wts, cfg, st, dev(X[t]), out, ws)
+        torch.cuda.synchronize()
+        want, rec = ref.decode_layer_lookahead(X[t], A.W, A.Wn, A.okv, n0 + t, head_idx=None, neuron_idx=ni,
+                                               k_heads=dims.h, k_neurons=k_m, scale=1 / math.sqrt(dims.d_h))
+        e = check_close(host(out), want, "f16", f"neuron-only look-ahead step {t}")
+        if selection_margin(rec["next_neuron_scores"][0], k_m) <= MARGIN:
+            break
+        assert np.array_equal(host(nn), rec["next_neuron_idx"]), f"step {t}: next neurons"
+        ni = rec["next_neuron_idx"].astype(np.int32)
+        print(f"neuron-only look-ahead step {t}: normwise {e:.2e}")
