@@ -357,15 +357,92 @@ def time_stack(torch, dv, stack, X, ws, cfg, warm, timed, head_sets=None, neuron
     return e0.elapsed_time(e1) / timed, int(fc2.item()) / (timed * stack.L)
 
 
+def attn_paths(torch, dv, stack, n, b, scale, reps=10):
+    """ByteCross §4.4 and App. D: one layer's attention (layer 0, 32 heads,
+    batch 1) at n cached positions, dense and through the KV window (4 sinks
+    plus the b - 4 most recent positions), on three attention paths:
+      splitk  the library's split-K kernel (splits chosen by the library);
+      fused   the same kernel with one 256-thread workgroup per head walking
+              all of that head's positions (num_splits = 4: a wave per quarter);
+      masked  PyTorch eager attention as transformer code writes it: the
+              score vector materialised by a batched product, an additive
+              mask, an fp32 softmax and a second product; the window reads a
+              compacted copy of its positions, built before timing.
+    The masked path is PyTorch's, not the library's: it is the baseline whose
+    speedups ByteCross shows to be inflated, timed here for that contrast only."""
+    dims = stack.dims
+    h, dh = dims.h, dims.d_h
+    K, V = stack.K[0], stack.V[0]
+    q = torch.empty(1, h, dh, device="cuda")
+    dv.dv_fill_normal(q, SEED + 9, 0)
+    heads = torch.arange(h, dtype=torch.int32, device="cuda")
+    o = torch.empty(1, h, dh, device="cuda")
+    win = (4, b - 4)
+    views = {"dense": dv.kv_view(K, V, n), "window": dv.kv_view(K, V, n, win_sink=win[0], win_len=win[1])}
+    npos = {"dense": n, "window": b}
+    ws = dv.workspace(dv.dv_splitk_workspace_bytes(1, h, dh, n, 0) + dv.dv_splitk_workspace_bytes(1, h, dh, n, 4))
+    q16 = q.half().unsqueeze(-1)                                   # [1][h][dh][1]
+    Kw = torch.cat([K[:, :, :win[0]], K[:, :, n - win[1]:n]], dim=2).contiguous()
+    Vw = torch.cat([V[:, :, :win[0]], V[:, :, n - win[1]:n]], dim=2).contiguous()
+    kv_of = {"dense": (K[:, :, :n], V[:, :, :n]), "window": (Kw, Vw)}
+    masks = {m: torch.zeros(1, 1, npos[m], device="cuda") for m in npos}
+
+    def masked(m):
+        Kn, Vn = kv_of[m]
+        s = torch.matmul(Kn, q16).squeeze(-1).float() * scale + masks[m]
+        p = torch.softmax(s, dim=-1).half().unsqueeze(-2)
+        return torch.matmul(p, Vn).squeeze(-2)
+
+    def run(path, m):
+        if path == "masked":
+            return masked(m)
+        dv.dv_splitk_attn(q, heads, h, views[m], scale, o, ws, num_splits=0 if path == "splitk" else 4)
+        return o
+
+    out = {}
+    for m in ("dense", "window"):
+        ref_o = run("splitk", m).clone()
+        for path in ("splitk", "fused", "masked"):
+            got = run(path, m).float()
+            err = float((got - ref_o).abs().max())
+            assert err < 2e-2, f"attention path {path}/{m} disagrees with split-K by {err}"
+            run(path, m)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run(path, m)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            by = 2.0 * h * npos[m] * dh * 2                         # K and V rows read once
+            out[(path, m)] = ms
+            out.setdefault(path, {})[m] = {"ms": round(ms, 4), "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                                           "frac_peak": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3),
+                                           "max_abs_vs_splitk": round(err, 6)}
+    for path in ("splitk", "fused", "masked"):
+        out[path]["window_speedup"] = round(out[(path, "dense")] / out[(path, "window")], 3)
+    del ws, Kw, Vw
+    return out
+
+
 def bench_longctx(torch, dv, synth, configs, args):
-    """ByteCross's composition at long context (§3.3, §4.1-4.2): a 32-layer
+    """ByteCross's composition at long context (§3.3, §4.1-4.4): a 32-layer
     stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 32K / 128K cached
-    tokens in four modes through the same kernels and the same split-K
+    tokens in five modes through the same kernels and the same split-K
     attention: dense; projection-only (10% of MLP neurons, predicted one
     layer ahead); KV-only (10% of cached positions per head chosen by the
-    attention-scored selection, plus the decoded tokens); composed.  The
-    selection's scoring pass runs once per context after the seeded prompt
-    and is timed on its own, outside tokens/s."""
+    attention-scored selection, plus the decoded tokens); the KV window
+    (4 sinks plus the most recent positions, the same 10% budget); composed.
+    The selection's scoring pass runs once per context after the seeded
+    prompt and is timed on its own, outside tokens/s.
+
+    §4.3's cost-aware crossing: a second sweep at 4K / 16K / 64K gives each
+    branch's cost beyond its byte-scaled dense time; with the dense time of
+    the first sweep interpolated log-log and the costs linearly, the branch
+    latencies are predicted and their crossing set beside the measured one
+    and the crossing of the bytes alone.  §4.4: at every context of the
+    first sweep, one layer's attention on three paths (attn_paths)."""
     from contextual_sparsity_decoding_amd.stack import Stack
     wl = configs.LONGCTX_STACK
     dims, L = wl.dims, wl.layers
@@ -381,52 +458,143 @@ def bench_longctx(torch, dv, synth, configs, args):
     modes = {"dense": (base | dv.DV_DENSE_MLP, dims.N),
              "proj": (base | ahead, kM),
              "kv": (base | dv.DV_DENSE_MLP | dv.DV_KV_SELECT, dims.N),
+             "window": (base | dv.DV_DENSE_MLP | dv.DV_KV_WINDOW, dims.N),
              "composed": (base | ahead | dv.DV_KV_SELECT, kM)}
     nsets = torch.zeros(L, kM, dtype=torch.int32, device="cuda")
-    out = []
-    for n in wl.ctx_sweep:
-        b = int(math.floor(wl.kv_keep * n))
-        max_len = n + T + 8
-        stack.set_context(n, max_len)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        stack.select_kv(b)
-        e1.record()
-        torch.cuda.synchronize()
-        score_ms = e0.elapsed_time(e1)
-        ws = dv.workspace(max(dv.dv_stack_workspace_bytes(stack.cfg(dims.h, k, f, scale), max_len)
-                              for f, k in modes.values()))
-        row = {"n_ctx": n, "kv_budget": b, "scoring_ms_all_layers": round(score_ms, 3)}
-        res = {}
-        for name, (flags, k) in modes.items():
-            cfg = stack.cfg(dims.h, k, flags, scale)
-            ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K,
-                                  neuron_sets=nsets if flags & dv.DV_LOOKAHEAD else None)
-            sel = bool(flags & dv.DV_KV_SELECT)
-            n_att = (b if sel else n) + W + (K - 1) / 2 + 1
-            by = L * dv.dv_bytes_read(cfg, n_att, rows if not (flags & dv.DV_DENSE_MLP) else dims.N, 0.0).total
-            res[name] = (ms, by)
-            row[name] = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1000 / ms, 2),
-                         "bytes_per_token": int(by), "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
-        for name in ("proj", "kv", "composed"):
-            row[name]["speedup"] = round(res["dense"][0] / res[name][0], 3)
-            row[name]["byte_bound_speedup"] = round(res["dense"][1] / res[name][1], 3)
-        out.append(row)
-        del ws
-    # the context where the two branches save the same time, measured and by bytes
-    def cross(key):
-        pts = [(r["n_ctx"], r["proj"][key] - r["kv"][key]) for r in out]
-        for (n0, a0), (n1, a1) in zip(pts, pts[1:]):
+
+    def mode_cfg(name, b):
+        flags, k = modes[name]
+        cfg = stack.cfg(dims.h, k, flags, scale)
+        if flags & dv.DV_KV_WINDOW:
+            cfg.win_sink, cfg.win_len = 4, b - 4
+        return cfg
+
+    def positions(name, n, b):
+        """Mean positions a head reads per timed token."""
+        flags = modes[name][0]
+        tail = W + (K - 1) / 2 + 1                          # decoded tokens: always read by the selection
+        if flags & dv.DV_KV_SELECT:
+            return b + tail
+        if flags & dv.DV_KV_WINDOW:
+            return float(b)
+        return n + tail
+
+    def step_bytes_of(name, n, b, rows):
+        cfg = mode_cfg(name, b)
+        dense_m = bool(modes[name][0] & dv.DV_DENSE_MLP)
+        return L * dv.dv_bytes_read(cfg, positions(name, n, b), dims.N if dense_m else rows, 0.0).total
+
+    def sweep(ctxs, names, paths):
+        pts = []
+        for n in ctxs:
+            b = int(math.floor(wl.kv_keep * n))
+            max_len = n + T + 8
+            stack.set_context(n, max_len)
+            torch.cuda.synchronize()
+            row = {"n_ctx": n, "kv_budget": b}
+            if "kv" in names or "composed" in names:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                stack.select_kv(b)
+                e1.record()
+                torch.cuda.synchronize()
+                row["scoring_ms_all_layers"] = round(e0.elapsed_time(e1), 3)
+            ws = dv.workspace(max(dv.dv_stack_workspace_bytes(mode_cfg(m, b), max_len) for m in names))
+            res = {}
+            for name in names:
+                cfg = mode_cfg(name, b)
+                ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K,
+                                      neuron_sets=nsets if modes[name][0] & dv.DV_LOOKAHEAD else None)
+                by = step_bytes_of(name, n, b, rows)
+                res[name] = (ms, by)
+                row[name] = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1000 / ms, 2),
+                             "bytes_per_token": int(by), "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
+                if name != "dense":
+                    row[name]["fc2_rows_per_layer"] = round(rows, 1)
+            for name in names:
+                if name != "dense":
+                    row[name]["speedup"] = round(res["dense"][0] / res[name][0], 3)
+                    row[name]["byte_bound_speedup"] = round(res["dense"][1] / res[name][1], 3)
+                    # ByteCross §4.3: the branch's cost beyond its byte-scaled dense time
+                    row[name]["cost_ms"] = round(res[name][0] - res["dense"][0] * res[name][1] / res["dense"][1], 4)
+            if paths:
+                row["attention_paths_one_layer"] = attn_paths(torch, dv, stack, n, b, scale)
+                ap = row["attention_paths_one_layer"]
+                # the step with its split-K attention time replaced by each path's (derived, not timed)
+                derived = {}
+                for path in ("splitk", "fused", "masked"):
+                    st = {m: res[m][0] + L * (ap[path][m]["ms"] - ap["splitk"][m]["ms"]) for m in ("dense", "window")}
+                    derived[path] = round(st["dense"] / st["window"], 3)
+                row["window_step_speedup_by_attention_path_derived"] = derived
+                row["window_byte_bound_speedup"] = row["window"]["byte_bound_speedup"]
+                row["attention_paths_one_layer"] = {k: v for k, v in ap.items() if isinstance(k, str)}
+            pts.append(row)
+            del ws
+        return pts
+
+    out = sweep(wl.ctx_sweep, list(modes), True)
+    cost_pts = sweep((4096, 16384, 65536), ["dense", "proj", "kv", "window"], False)
+
+    def cross_of(pts, key):
+        """log-linear crossing of proj and kv in `key` (speedup), or None."""
+        vals = [(r["n_ctx"], r["proj"][key] - r["kv"][key]) for r in pts]
+        for (n0, a0), (n1, a1) in zip(vals, vals[1:]):
             if a0 >= 0 > a1 or a0 > 0 >= a1:
                 f = a0 / (a0 - a1)
                 return round(math.exp(math.log(n0) + f * (math.log(n1) - math.log(n0))))
         return None
+
+    # the crossing of the bytes alone, from the byte account (fc2 rows of the proj branch at 32K)
+    rows_p = next(r for r in out if r["n_ctx"] == 32768)["proj"]["fc2_rows_per_layer"]
+
+    def byte_gap(n):
+        b = int(math.floor(wl.kv_keep * n))
+        return step_bytes_of("proj", n, b, rows_p) - step_bytes_of("kv", n, b, 0)
+
+    lo, hi = 1024.0, 1048576.0
+    bytes_cross = None
+    if byte_gap(lo) < 0 < byte_gap(hi):
+        for _ in range(60):
+            mid = math.sqrt(lo * hi)
+            lo, hi = (mid, hi) if byte_gap(mid) < 0 else (lo, mid)
+        bytes_cross = round(lo)
+
+    # cost-aware prediction: dense time log-log from the first sweep, costs
+    # linear in n from the second, byte ratios from the byte account
+    dn = [(math.log(r["n_ctx"]), math.log(r["dense"]["ms_per_token"])) for r in out]
+
+    def interp(xy, x):
+        xs = [p[0] for p in xy]
+        i = max(0, min(len(xy) - 2, sum(1 for v in xs if v <= x) - 1))
+        (x0, y0), (x1, y1) = xy[i], xy[i + 1]
+        return y0 + (y1 - y0) * (x - x0) / (x1 - x0)
+
+    costs = {m: [(r["n_ctx"], r[m]["cost_ms"]) for r in cost_pts] for m in ("proj", "kv", "window")}
+
+    def predict(m, n):
+        b = int(math.floor(wl.kv_keep * n))
+        td = math.exp(interp(dn, math.log(n)))
+        ratio = step_bytes_of(m, n, b, rows_p) / step_bytes_of("dense", n, b, 0)
+        return td * ratio + interp(costs[m], n)
+
+    pred_cross = None
+    grid = [2048 * 2 ** (i / 64) for i in range(64 * 6 + 1)]
+    for n0, n1 in zip(grid, grid[1:]):
+        a0, a1 = predict("proj", n0) - predict("kv", n0), predict("proj", n1) - predict("kv", n1)
+        if a0 <= 0 < a1 or a0 < 0 <= a1:
+            pred_cross = round(n0 + (n1 - n0) * (-a0) / (a1 - a0))
+            break
+    pred_at = [{"n_ctx": r["n_ctx"], **{m: {"predicted_ms": round(predict(m, r["n_ctx"]), 4),
+                                             "measured_ms": r[m]["ms_per_token"]} for m in ("proj", "kv", "window")}}
+               for r in out]
     del stack, X, nsets
     torch.cuda.empty_cache()
     return {"workload": "longctx-32L-d4096-h32-ffn16384-fp16: 32 layers, batch 1, neuron keep 10% (1638), "
-                        "KV keep 10% per head (attention-scored, 4 sinks + 64-token window forced), heads dense",
-            "points": out, "crossover_measured_n": cross("speedup"), "crossover_bytes_n": cross("byte_bound_speedup"),
+                        "KV keep 10% per head (attention-scored, 4 sinks + 64-token window forced; or the window "
+                        "of 4 sinks + the most recent positions), heads dense",
+            "points": out, "cost_sweep": cost_pts,
+            "crossover_measured_n": cross_of(out, "speedup"), "crossover_bytes_n": bytes_cross,
+            "crossover_cost_aware_predicted_n": pred_cross, "cost_model_check": pred_at,
             "warmup": W, "steps": K}
 
 

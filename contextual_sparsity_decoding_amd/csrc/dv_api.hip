@@ -306,6 +306,9 @@ static dv_status check_view(const dv_kv_view* kv, const char* who) {
         REQ(kv->sel_end >= 0 && kv->sel_end <= kv->n_ctx && kv->sel_cap >= 0 && kv->sel_cap <= kv->sel_end,
             DV_ERR_RANGE, "%s: sel_cap=%d sel_end=%d n_ctx=%d", who, kv->sel_cap, kv->sel_end, kv->n_ctx);
     }
+    REQ(kv->win_len >= 0 && kv->win_sink >= 0, DV_ERR_RANGE, "%s: win_sink=%d win_len=%d", who, kv->win_sink,
+        kv->win_len);
+    REQ(!(kv->sel_idx && kv->win_len > 0), DV_ERR_UNSUPPORTED, "%s: a KV window and retained positions together", who);
     return DV_OK;
 }
 
@@ -319,8 +322,7 @@ dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx
     REQ(isfinite(scale), DV_ERR_RANGE, "dv_splitk_attn: scale");
     REQ(num_splits >= 0 && num_splits <= 65536, DV_ERR_RANGE, "dv_splitk_attn: num_splits=%d", num_splits);
     REQ((long)B * n_sel * (num_splits > 0 ? num_splits : 1) <= (1L << 26), DV_ERR_RANGE, "dv_splitk_attn: too many splits");
-    const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
-    const size_t need = splitk_ws(B, n_sel, d_h, maxpos, num_splits);
+    const size_t need = splitk_ws(B, n_sel, d_h, view_positions(kv), num_splits);
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_splitk_attn: workspace %zu < %zu", ws_bytes, need);
     return launch_splitk(q, B, d_h, head_idx, n_sel, kv, kv->n_ctx_dev, 0, scale, num_splits, o,
                          (float*)((char*)ws + kCounterBytes), nullptr, 0, nullptr, (hipStream_t)stream);
@@ -415,7 +417,7 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(wdt_ok(c->wdt), DV_ERR_DTYPE, "dv_decode_layer: wdt %d", c->wdt);
     REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
     const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT | DV_ADVANCE_POS |
-                           DV_LOOKAHEAD;
+                           DV_LOOKAHEAD | DV_KV_WINDOW;
     REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
     REQ(c->B >= 1 && c->B <= 16 && d_ok(c->d) && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
         "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
@@ -434,6 +436,9 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
             c->k_neurons);
     }
     REQ(isfinite(c->scale) && c->eps >= 0.f && isfinite(c->eps), DV_ERR_RANGE, "dv_decode_layer: scale/eps");
+    REQ(!(c->flags & DV_KV_WINDOW) || (!(c->flags & DV_KV_SELECT) && c->win_len > 0 && c->win_sink >= 0),
+        DV_ERR_RANGE, "dv_decode_layer: DV_KV_WINDOW win_sink=%d win_len=%d (not with DV_KV_SELECT)", c->win_sink,
+        c->win_len);
     if (c->flags & DV_LOOKAHEAD) {
         REQ(c->B == 1, DV_ERR_UNSUPPORTED, "dv_decode_layer: DV_LOOKAHEAD with B=%d", c->B);
         REQ(c->r_attn >= 1 && c->r_attn <= 512 && (size_t)c->r_attn * eb % 16 == 0 && c->r_mlp >= 1 &&
@@ -665,6 +670,10 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
     view.k_cache = kv.k_cache; view.v_cache = kv.v_cache; view.h = c->h; view.max_len = kv.max_len;
     view.n_ctx = kv.pos + 1;
     view.sel_idx = nullptr; view.sel_len = nullptr; view.sel_cap = 0; view.sel_end = 0; view.n_ctx_dev = nullptr;
+    view.win_sink = 0; view.win_len = 0;
+    if (c->flags & DV_KV_WINDOW) {
+        view.win_sink = c->win_sink; view.win_len = c->win_len;
+    }
     if (c->flags & DV_KV_SELECT) {
         view.sel_idx = st->sel_idx; view.sel_len = st->sel_len; view.sel_cap = st->sel_cap; view.sel_end = st->sel_end;
         REQ(view.sel_idx, DV_ERR_NULL, "dv_decode_layer: DV_KV_SELECT without sel_idx");

@@ -302,6 +302,9 @@ dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hi
 dv_status launch_union(const int32_t* idx, int B, int k, int n, int32_t* union_idx,
                        int32_t* union_count, hipStream_t s);
 int splitk_auto(int max_positions, int rows);
+// Most positions one head of the view reads: the retained set plus the
+// appended tail, the sinks plus the recent window, or every position.
+int view_positions(const dv_kv_view* kv);
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
                         float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,

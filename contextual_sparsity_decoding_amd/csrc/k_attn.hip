@@ -36,6 +36,7 @@ struct AttnArgs {
     const int32_t* sel_idx;
     const int32_t* sel_len;
     int sel_cap, sel_end;
+    int win_sink, win_len;  // KV window: positions < win_sink and the last win_len (win_len > 0)
     float scale_log2;
     int num_splits, chunk;
     float* part;            // [B][n_sel][num_splits][DH + 2]
@@ -84,10 +85,17 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
     const int n_ctx = a.n_dev ? min(max(*a.n_dev + a.n_add, 0), a.n_ctx) : a.n_ctx;
     int cnt, sl = 0;
     const int32_t* sidx = nullptr;
+    // KV window (ByteCross §5.1, App. A): the sinks [0, w0) and the recent
+    // positions [wst, n_ctx), read in place
+    const bool win = a.win_len > 0;
+    const int w0 = win ? min(max(a.win_sink, 0), n_ctx) : 0;
+    const int wst = win ? max(w0, n_ctx - a.win_len) : 0;
     if (a.sel_idx) {
         sl = min(max(a.sel_len[b * a.h + head], 0), a.sel_cap);
         sidx = a.sel_idx + ((size_t)b * a.h + head) * a.sel_cap;
         cnt = sl + max(0, n_ctx - a.sel_end);
+    } else if (win) {
+        cnt = w0 + (n_ctx - wst);
     } else {
         cnt = n_ctx;
     }
@@ -111,7 +119,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
             valid[u] = j < j1;
             kw[u] = vw[u] = u32x4{0u, 0u, 0u, 0u};
             if (valid[u]) {
-                const int p = sidx ? (j < sl ? sidx[j] : a.sel_end + (j - sl)) : j;
+                const int p = sidx ? (j < sl ? sidx[j] : a.sel_end + (j - sl))
+                              : win ? (j < w0 ? j : wst + (j - w0)) : j;
                 valid[u] = (unsigned)p < (unsigned)n_ctx;         // a retained index past the cache reads nothing
                 if (valid[u]) {
                     kw[u] = ld16(Kh + (size_t)p * DH);
@@ -269,11 +278,18 @@ int splitk_auto(int max_positions, int rows) {
     return splits < 1 ? 1 : splits;
 }
 
+int view_positions(const dv_kv_view* kv) {
+    if (kv->sel_idx) return kv->sel_cap + (kv->n_ctx - kv->sel_end);
+    if (kv->win_len > 0) return min(kv->n_ctx, kv->win_sink + kv->win_len);
+    return kv->n_ctx;
+}
+
 dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx, int n_sel,
                         const dv_kv_view* kv, const int32_t* n_dev, int n_add, float scale, int num_splits, float* o,
                         float* part, int32_t* mark_valid, int mark_pos, const int32_t* mark_pos_dev, hipStream_t s,
                         int* splits_used, const Pred2Args* pred) {
-    const int maxpos = kv->sel_idx ? kv->sel_cap + (kv->n_ctx - kv->sel_end) : kv->n_ctx;
+    const bool win = kv->win_len > 0 && !kv->sel_idx;
+    const int maxpos = view_positions(kv);
     if (num_splits <= 0) num_splits = splitk_auto(maxpos, B * n_sel);
     if (splits_used) *splits_used = num_splits;
     if (n_sel == 0 && !pred) return DV_OK;
@@ -282,6 +298,7 @@ dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx,
     a.K = (const half_t*)kv->k_cache; a.V = (const half_t*)kv->v_cache;
     a.max_len = kv->max_len; a.n_ctx = kv->n_ctx; a.n_dev = n_dev; a.n_add = n_add;
     a.sel_idx = kv->sel_idx; a.sel_len = kv->sel_len; a.sel_cap = kv->sel_cap; a.sel_end = kv->sel_end;
+    a.win_sink = win ? kv->win_sink : 0; a.win_len = win ? kv->win_len : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.num_splits = num_splits;
     a.chunk = cdiv(maxpos < 1 ? 1 : maxpos, num_splits);

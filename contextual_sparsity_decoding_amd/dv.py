@@ -32,6 +32,7 @@ DV_HOLE_FILL = 0x8
 DV_KV_SELECT = 0x10
 DV_ADVANCE_POS = 0x20
 DV_LOOKAHEAD = 0x40
+DV_KV_WINDOW = 0x80
 DV_KERNEL_QKV, DV_KERNEL_ATTN, DV_KERNEL_OUT, DV_KERNEL_FC1, DV_KERNEL_FC2 = 1, 2, 3, 4, 5
 STATUS = ["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN", "DV_ERR_RANGE",
           "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]
@@ -46,13 +47,14 @@ class KVState(C.Structure):
 
 class KVView(C.Structure):
     _fields_ = [("k_cache", vp), ("v_cache", vp), ("h", ci), ("max_len", ci), ("n_ctx", ci),
-                ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci), ("sel_end", ci), ("n_ctx_dev", vp)]
+                ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci), ("sel_end", ci), ("n_ctx_dev", vp),
+                ("win_sink", ci), ("win_len", ci)]
 
 
 class DecodeCfg(C.Structure):
     _fields_ = [("B", ci), ("d", ci), ("h", ci), ("d_h", ci), ("N", ci), ("r_attn", ci), ("r_mlp", ci),
                 ("k_heads", ci), ("k_neurons", ci), ("wdt", ci), ("pred_act", ci), ("eps", cf),
-                ("scale", cf), ("flags", cu)]
+                ("scale", cf), ("flags", cu), ("win_sink", ci), ("win_len", ci)]
 
 
 class LayerWeights(C.Structure):
@@ -224,10 +226,11 @@ def kv_state(K, V, pos, y_buf=None, valid_upto=None, pos_dev=None) -> KVState:
     return s
 
 
-def kv_view(K, V, n_ctx, sel_idx=None, sel_len=None, sel_end=0, n_ctx_dev=None) -> KVView:
+def kv_view(K, V, n_ctx, sel_idx=None, sel_len=None, sel_end=0, n_ctx_dev=None, win_sink=0,
+            win_len=0) -> KVView:
     cap = sel_idx.shape[-1] if sel_idx is not None else 0
     v = KVView(ptr(K), ptr(V), K.shape[1], K.shape[2], n_ctx, ptr(sel_idx), ptr(sel_len), cap, sel_end,
-               ptr(n_ctx_dev))
+               ptr(n_ctx_dev), win_sink, win_len)
     v._keep = (K, V, sel_idx, sel_len, n_ctx_dev)
     return v
 

@@ -76,6 +76,7 @@ typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
 #define DV_KV_SELECT       0x10u /* attend to retained KV positions only (ByteCross §4.1) */
 #define DV_ADVANCE_POS     0x20u /* dv_decode_layer: add 1 to *kv.pos_dev when the step is done */
 #define DV_LOOKAHEAD       0x40u /* dv_decode_layer: DejaVu §4.3 parallel form (see dv_layer_state) */
+#define DV_KV_WINDOW       0x80u /* attend to the KV window of dv_decode_cfg.win_* (ByteCross §5.1) */
 
 int dv_api_version(void);
 const char* dv_status_str(int status);
@@ -226,6 +227,11 @@ dv_status dv_sparse_attn_proj(int mode, int B, int d, int h, int d_h, const int3
  *            receiving entries, ByteCross §3.2)
  *   n_ctx_dev device int32 [1] or NULL: when set, the count is read from
  *            here at run time (clamped to [0, n_ctx]) and n_ctx is its bound
+ *   win_sink, win_len  (win_len > 0, sel_idx NULL) the KV window policy
+ *            (ByteCross §5.1 and App. A): the positions < win_sink and the
+ *            last win_len positions before n_ctx, read in place; the window
+ *            slides as tokens are appended.  Both zero: every position.
+ *            win_len > 0 with sel_idx set is DV_ERR_UNSUPPORTED.
  */
 typedef struct {
     const void* k_cache;
@@ -238,6 +244,8 @@ typedef struct {
     int sel_cap;
     int sel_end;
     const int32_t* n_ctx_dev;
+    int win_sink;
+    int win_len;
 } dv_kv_view;
 
 /* ------------------------------------------------------------------------
@@ -291,6 +299,7 @@ typedef struct {
     float eps;                /* LayerNorm epsilon */
     float scale;              /* attention score scale */
     unsigned flags;           /* DV_* flags above */
+    int win_sink, win_len;    /* DV_KV_WINDOW: sink and recent positions, as in dv_kv_view */
 } dv_decode_cfg;
 
 typedef struct {

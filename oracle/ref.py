@@ -21,12 +21,14 @@ Readings taken where the pages are silent (each is listed in the design doc):
     selected later, every empty slot since its last selection is recomputed
     from the stored layer input (DejaVu §4.2);
   * for a batch, every sequence computes over the union of the per-sequence
-    sets (DejaVu §5.2 and App. C.1), for neurons and heads alike.
+    sets (DejaVu §5.2 and App. C.1), for neurons and heads alike;
+  * the KV window is the first n_sink positions plus the last win_len
+    positions of the cache, a position in both counted once.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -230,19 +232,32 @@ def retained_positions(n_ctx: int, sel: Optional[np.ndarray] = None,
     return np.concatenate([np.asarray(sel, dtype=np.int64), tail])
 
 
+def window_positions(n_ctx: int, n_sink: int, win_len: int) -> np.ndarray:
+    """The KV window (ByteCross §5.1 and App. A): the first ``n_sink``
+    positions (the sinks) and the last ``win_len`` positions before n_ctx,
+    each once, ascending.  The window moves on as the cache grows."""
+    sinks = np.arange(min(n_sink, n_ctx))
+    recent = np.arange(max(len(sinks), n_ctx - win_len), n_ctx)
+    return np.concatenate([sinks, recent])
+
+
 def attention(q, kv: KVState, head_idx, n_ctx: int, scale: float,
-              sel_idx=None, sel_len=None, sel_end: Optional[int] = None) -> np.ndarray:
+              sel_idx=None, sel_len=None, sel_end: Optional[int] = None,
+              window: Optional[Tuple[int, int]] = None) -> np.ndarray:
     """o [B][n_sel][d_h]: Eq. (2) for every selected head over its positions.
 
     ``sel_idx`` [B][h][cap] / ``sel_len`` [B][h] give retained positions per
-    head for the KV branch (ByteCross §4.1); None attends to all n_ctx.
+    head for the KV branch (ByteCross §4.1); ``window`` = (n_sink, win_len)
+    reads the KV window instead; neither attends to all n_ctx.
     """
     q = _f64(q)
     B, n_sel, d_h = q.shape
     o = np.zeros((B, n_sel, d_h), F64)
     for b in range(B):
         for s, i in enumerate(np.asarray(head_idx, dtype=np.int64)):
-            if sel_idx is None:
+            if window is not None:
+                P = window_positions(n_ctx, *window)
+            elif sel_idx is None:
                 P = retained_positions(n_ctx)
             else:
                 P = retained_positions(n_ctx, sel_idx[b, i, :int(sel_len[b, i])], sel_end)
@@ -361,7 +376,8 @@ def decode_layer(x, W: dict, kv: KVState, pos: int, *, k_heads: int, k_neurons: 
                  scale: float, eps: float = 1e-5, pred_act: str = "relu",
                  dense_attn: bool = False, dense_mlp: bool = False,
                  skip_nonpos: bool = True, hole_fill: bool = True,
-                 sel_idx=None, sel_len=None, sel_end: Optional[int] = None):
+                 sel_idx=None, sel_len=None, sel_end: Optional[int] = None,
+                 window: Optional[Tuple[int, int]] = None):
     """One decode step of one pre-LN OPT-style layer under contextual sparsity.
 
     DejaVu §4.3, the sequential form:  S_A <- SP_A(y);  y~ <- MHA_{S_A}(y);
@@ -369,7 +385,8 @@ def decode_layer(x, W: dict, kv: KVState, pos: int, *, k_heads: int, k_neurons: 
     LayerNorm before each block (App. B).  The predictors read the block's
     own normalised input.  The token sits at ``pos`` and attends to
     positions 0..pos (or, with ``sel_idx``, to the retained positions plus
-    [sel_end, pos]).  Scores are rounded to fp32 before selection.
+    [sel_end, pos]; with ``window`` = (n_sink, win_len), to the KV window of
+    pos + 1 positions).  Scores are rounded to fp32 before selection.
 
     x [B][d].  Returns (x_out [B][d], record dict).  Mutates ``kv``.
     """
@@ -387,7 +404,7 @@ def decode_layer(x, W: dict, kv: KVState, pos: int, *, k_heads: int, k_neurons: 
         head_idx = union_sorted(topk_rows(sA, k_heads))
     rec["head_idx"] = head_idx
     q = qkv_step(y, W["w_qkv_t"], W["b_qkv"], head_idx, kv, pos, hole_fill)
-    o = attention(q, kv, head_idx, pos + 1, scale, sel_idx, sel_len, sel_end)
+    o = attention(q, kv, head_idx, pos + 1, scale, sel_idx, sel_len, sel_end, window)
     hres = out_proj(o, W["w_o_t"], W["b_o"], head_idx, residual=x)
     y2 = layernorm(hres, W["ln2_g"], W["ln2_b"], eps)
     if dense_mlp:
@@ -406,7 +423,8 @@ def decode_layer(x, W: dict, kv: KVState, pos: int, *, k_heads: int, k_neurons: 
 def decode_layer_lookahead(x, W: dict, W_next: Optional[dict], kv: KVState, pos: int, *,
                            head_idx, neuron_idx, k_heads: int, k_neurons: int, scale: float,
                            eps: float = 1e-5, pred_act: str = "relu", skip_nonpos: bool = True,
-                           hole_fill: bool = True, sel_idx=None, sel_len=None, sel_end: Optional[int] = None):
+                           hole_fill: bool = True, sel_idx=None, sel_len=None, sel_end: Optional[int] = None,
+                           window: Optional[Tuple[int, int]] = None):
     """One decode step in DejaVu §4.3's parallel form (batch of one).
 
     This layer's sets S_A^l = ``head_idx`` and S_M^l = ``neuron_idx`` were
@@ -430,7 +448,7 @@ def decode_layer_lookahead(x, W: dict, W_next: Optional[dict], kv: KVState, pos:
     y = layernorm(x, W["ln1_g"], W["ln1_b"], eps)
     heads = np.arange(h) if head_idx is None else np.asarray(head_idx, dtype=np.int64)
     q = qkv_step(y, W["w_qkv_t"], W["b_qkv"], heads, kv, pos, hole_fill)
-    o = attention(q, kv, heads, pos + 1, scale, sel_idx, sel_len, sel_end)
+    o = attention(q, kv, heads, pos + 1, scale, sel_idx, sel_len, sel_end, window)
     hres = out_proj(o, W["w_o_t"], W["b_o"], heads, residual=x)
     y2 = layernorm(hres, W["ln2_g"], W["ln2_b"], eps)
     idx = np.arange(N) if neuron_idx is None else np.asarray(neuron_idx, dtype=np.int64)
@@ -464,7 +482,8 @@ def predict_sets(x, W: dict, k_heads: int, k_neurons: int, eps: float = 1e-5, pr
 
 def decode_stack_lookahead(x, Ws: Sequence[dict], kvs: Sequence[KVState], pos: int, *, k_heads: int,
                            k_neurons: int, scale: float, eps: float = 1e-5, pred_act: str = "relu",
-                           skip_nonpos: bool = True, hole_fill: bool = True):
+                           skip_nonpos: bool = True, hole_fill: bool = True,
+                           window: Optional[Tuple[int, int]] = None):
     """One token through a stack of layers in DejaVu §4.3's parallel form.
 
     The output of layer l is the input of layer l+1 (§3, the residual
@@ -483,7 +502,8 @@ def decode_stack_lookahead(x, Ws: Sequence[dict], kvs: Sequence[KVState], pos: i
         x_in = _f64(np.atleast_2d(x))
         x, rec = decode_layer_lookahead(x, W, W_next, kvs[l], pos, head_idx=heads, neuron_idx=neurons,
                                         k_heads=k_heads, k_neurons=k_neurons, scale=scale, eps=eps,
-                                        pred_act=pred_act, skip_nonpos=skip_nonpos, hole_fill=hole_fill)
+                                        pred_act=pred_act, skip_nonpos=skip_nonpos, hole_fill=hole_fill,
+                                        window=window)
         rec["x"] = x_in
         recs.append(rec)
         if W_next is not None:

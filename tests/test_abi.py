@@ -121,6 +121,14 @@ def test_splitk_and_score_validation(dv):
     assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 0, 0) == 6
     assert L.dv_kv_score(P, 1, 4, 64, 8, C.byref(v), 0.1, 4, 8, 6, P, P, 1 << 20, 0) == 5   # even width
     assert L.dv_kv_score(P, 1, 4, 64, 51, C.byref(v), 0.1, 4, 8, 7, P, P, 1 << 20, 0) == 5  # n_obs > n
+    v = dv.KVView(P, P, 4, 100, 50, 0, 0, 0, 0, 0, 4, -1)         # negative window
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 5
+    v = dv.KVView(P, P, 4, 100, 50, P, P, 20, 30, 0, 4, 8)         # window and retained set together
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, 1 << 20, 0) == 7
+    # the window sizes the workspace: 12 positions need fewer splits than 50
+    v = dv.KVView(P, P, 4, 100, 50, 0, 0, 0, 0, 0, 4, 8)
+    need = L.dv_splitk_workspace_bytes(1, 2, 64, 12, 0)
+    assert L.dv_splitk_attn(P, 1, 64, P, 2, C.byref(v), 0.1, 0, P, P, need - 1, 0) == 6
 
 
 def test_decode_layer_validation(dv):
@@ -142,6 +150,12 @@ def test_decode_layer_validation(dv):
     cfg.flags = 0
     cfg.k_neurons = 300
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+    cfg.k_neurons = 32
+    cfg.flags = dv.DV_KV_WINDOW                                        # win_len 0
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+    cfg.flags, cfg.win_sink, cfg.win_len = dv.DV_KV_WINDOW | dv.DV_KV_SELECT, 4, 8
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+    assert "DV_KV_WINDOW" in err(dv)
 
 
 def test_lookahead_sets_must_not_alias(dv):

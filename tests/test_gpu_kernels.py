@@ -330,6 +330,40 @@ def test_splitk_selected_positions(dvlib, splits):
     assert np.all(host(o) == 0)
 
 
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("n_ctx,n_sink,win_len", [(2049, 4, 200), (300, 4, 400), (77, 0, 10), (1000, 50, 3),
+                                                  (5000, 4, 496)])
+def test_splitk_window(dvlib, n_ctx, n_sink, win_len, splits):
+    """The KV window (sinks plus the recent positions), read in place."""
+    h, dh, B = 4, 128, 2
+    K, V = synth.kv_cache(h, dh, n_ctx, n_ctx + 5, seed=n_ctx + win_len, batch=B)
+    heads = np.array([3, 0, 1], np.int32)
+    q = synth.normal((B, 3, dh), 9, 0, "x")
+    view = dvlib.kv_view(dev(K), dev(V), n_ctx, win_sink=n_sink, win_len=win_len)
+    ws = dvlib.workspace(dvlib.dv_splitk_workspace_bytes(B, 3, dh, min(n_ctx, n_sink + win_len), splits))
+    o = torch.empty(B, 3, dh, device="cuda")
+    dvlib.dv_splitk_attn(dev(q), dev(heads), 3, view, 0.09, o, ws, num_splits=splits)
+    want = ref.attention(q, ref.KVState(K, V), heads, n_ctx, 0.09, window=(n_sink, win_len))
+    assert maxabs(host(o), want) < 1e-4
+
+
+def test_splitk_window_with_device_count(dvlib):
+    """The count read at run time moves the recent window with it."""
+    h, dh, B, bound, n_sink, win_len = 4, 128, 1, 3000, 4, 300
+    K, V = synth.kv_cache(h, dh, bound, bound, seed=33, batch=B)
+    heads = np.arange(h, dtype=np.int32)
+    q = synth.normal((B, h, dh), 10, 0, "x")
+    n_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    view = dvlib.kv_view(dev(K), dev(V), bound, n_ctx_dev=n_dev, win_sink=n_sink, win_len=win_len)
+    ws = dvlib.workspace(dvlib.dv_splitk_workspace_bytes(B, h, dh, n_sink + win_len, 0))
+    o = torch.empty(B, h, dh, device="cuda")
+    for n in (1, 200, 304, 2999, 3000):
+        n_dev.fill_(n)
+        dvlib.dv_splitk_attn(dev(q), dev(heads), h, view, 0.1, o, ws)
+        want = ref.attention(q, ref.KVState(K, V), heads, n, 0.1, window=(n_sink, win_len))
+        assert maxabs(host(o), want) < 1e-4, n
+
+
 def test_kv_score_and_selection(dvlib):
     h, dh, n, n_obs, B = 4, 128, 700, 64, 1
     K, V = synth.kv_cache(h, dh, n, n + 10, seed=21, batch=B)

@@ -62,12 +62,16 @@ def test_fill_normal_layout_of_a_tensor(dvlib):
 class DeviceStack:
     """A Stack plus the buffers a look-ahead decode carries."""
 
-    def __init__(self, dv, dims, L, n0, max_len, seed, k_heads, k_neurons):
+    def __init__(self, dv, dims, L, n0, max_len, seed, k_heads, k_neurons, window=None):
         from contextual_sparsity_decoding_amd.stack import Stack
         self.dv, self.dims, self.L, self.kA, self.kM = dv, dims, L, k_heads, k_neurons
         self.S = Stack(dims, L, n0, max_len, seed)
         flags = dv.DV_LOOKAHEAD | dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
+        if window is not None:
+            flags |= dv.DV_KV_WINDOW
         self.cfg = self.S.cfg(k_heads, k_neurons, flags, 1 / math.sqrt(dims.d_h))
+        if window is not None:
+            self.cfg.win_sink, self.cfg.win_len = window
         self.ws = dv.workspace(dv.dv_stack_workspace_bytes(self.cfg, max_len))
         self.head_sets = torch.full((L, k_heads), -1, dtype=torch.int32, device="cuda")
         self.neuron_sets = torch.full((L, k_neurons), -1, dtype=torch.int32, device="cuda")
@@ -91,13 +95,16 @@ def _follow(got, want, scores, k, what):
     return np.asarray(got, np.int64)
 
 
-def test_stack_chained_small(dvlib):
+@pytest.mark.parametrize("window", [None, (4, 16)])
+def test_stack_chained_small(dvlib, window):
     """3 layers x 4 tokens: every layer's sets, output, K/V and valid
     positions follow the oracle's chain (layer l's input is layer l-1's
-    output; its sets were predicted by layer l-1)."""
+    output; its sets were predicted by layer l-1).  With ``window`` every
+    layer reads its 4 sink and 16 most recent positions, a window that
+    slides one position per token."""
     dims = LayerDims(d=1024, N=4096, h=8, d_h=128, r_attn=32, r_mlp=64, wdt="f16")
-    L, n0, T, kA, kM, seed = 3, 40, 4, 3, 400, 17
-    D = DeviceStack(dvlib, dims, L, n0, n0 + T + 2, seed, kA, kM)
+    L, n0, T, kA, kM, seed = 3, 40, 4, 3, 400, 17 if window is None else 18
+    D = DeviceStack(dvlib, dims, L, n0, n0 + T + 2, seed, kA, kM, window)
     Ws = [synth.stack_layer_weights(dims, seed, l) for l in range(L)]
     kvs = []
     for l in range(L):
@@ -117,7 +124,7 @@ def test_stack_chained_small(dvlib):
         for l in range(L):
             Wn = Ws[l + 1] if l + 1 < L else None
             x, rec = ref.decode_layer_lookahead(x, Ws[l], Wn, kvs[l], n0 + t, head_idx=heads, neuron_idx=neurons,
-                                                k_heads=kA, k_neurons=kM, scale=scale)
+                                                k_heads=kA, k_neurons=kM, scale=scale, window=window)
             got = got_tr[l] if l + 1 < L else got_x
             errs.append(check_close(got, x, "f16", f"token {t} layer {l}"))
             if Wn is not None:

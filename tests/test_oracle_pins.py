@@ -304,6 +304,39 @@ def test_kv_selected_attention_with_full_budget_is_dense():
     np.testing.assert_allclose(a, b, atol=1e-12)
 
 
+@pytest.mark.parametrize("n,n_sink,win_len", [(40, 4, 10), (40, 0, 7), (40, 4, 36), (40, 4, 60), (40, 50, 3),
+                                            (1, 4, 1), (9, 4, 5), (9, 4, 6)])
+def test_window_attention_matches_sdpa_with_a_membership_mask(n, n_sink, win_len):
+    """The KV window read through its index set equals attention over the
+    whole cache with every position outside the window masked out (the mask
+    built by a membership test, not by the index construction)."""
+    dims = small_dims()
+    g = np.random.default_rng(16)
+    K, V = synth.kv_cache(dims.h, dims.d_h, n, 48, seed=16)
+    kv = ref.KVState(K, V)
+    q = g.standard_normal((1, dims.h, dims.d_h))
+    got = ref.attention(q, kv, np.arange(dims.h), n, 0.2, window=(n_sink, win_len))
+    keep = torch.tensor([p < n_sink or p >= n - win_len for p in range(n)])
+    want = F.scaled_dot_product_attention(t64(q)[0, :, None], t64(K[0, :, :n]), t64(V[0, :, :n]),
+                                          attn_mask=keep[None, None, :], scale=0.2)[:, 0].numpy()
+    np.testing.assert_allclose(got[0], want, atol=1e-12)
+
+
+def test_window_positions_brute_force_and_slide():
+    for n in range(0, 30):
+        for n_sink in (0, 1, 4, 40):
+            for win_len in (1, 3, 8, 50):
+                P = ref.window_positions(n, n_sink, win_len)
+                want = [p for p in range(n) if p < n_sink or p >= n - win_len]
+                assert P.tolist() == want
+                assert len(P) == min(n, n_sink + win_len)
+                if n >= 1:  # one more token: the newest enters, the oldest recent one leaves
+                    Q = ref.window_positions(n + 1, n_sink, win_len)
+                    assert n in Q.tolist()
+                    gone = set(P.tolist()) - set(Q.tolist())
+                    assert gone <= {n - win_len} and (gone or n - win_len < n_sink or n - win_len < 0)
+
+
 # ------------------------------------------------------- KV-position scores --
 
 def test_kv_scores_match_masked_softmax():
