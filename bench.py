@@ -255,13 +255,20 @@ def main():
                           "speedup_over_bound": round((dense_ms / ms) / (dense_bytes / b), 3)})
         seq_ms, _ = run.run(seq_cfg, W, K)
 
-    # the dominant kernel, timed on its own launches inside the headline step
+    # the dominant kernel, timed on its own launches inside the headline step.
+    # Riders: the next layer's predictor layer one (both predictors) rides in
+    # Q/K/V and layer two in the attention launch, in every layer but the
+    # last (so (L - 1) / L of them per launch on average).
+    ride = (L - 1) / L
+    p1_bytes = ride * 2 * (dims.r_attn + dims.r_mlp) * dims.d
+    p2_bytes = ride * 2 * (dims.r_attn * dims.h + dims.r_mlp * dims.N)
     kinds = {"k_qkv (Q/K/V + KV append + hole fill, LN1 and next-layer predictor rows folded in)":
-             (dv.DV_KERNEL_QKV, hb.qkv + 4 * dims.d + 2 * 2 * head_k * dims.d_h),
+             (dv.DV_KERNEL_QKV, hb.qkv + 4 * dims.d + 2 * 2 * head_k * dims.d_h + p1_bytes),
              "k_rowdot_ln (sparse fc1, LN2 folded in)": (dv.DV_KERNEL_FC1, hb.fc1 + 4 * dims.d),
              "k_axpy<ATTN> (W^O gather-AXPY, split-K merge)": (dv.DV_KERNEL_OUT, hb.out_proj),
              "k_axpy (fc2 gather-AXPY)": (dv.DV_KERNEL_FC2, hb.fc2),
-             "k_attn_split (split-K attention)": (dv.DV_KERNEL_ATTN, hb.kv_read)}
+             "k_attn_split (split-K attention, next-layer predictor layer two)": (dv.DV_KERNEL_ATTN,
+                                                                                  hb.kv_read + p2_bytes)}
     kernels = {}
     for name, (kind, nbytes) in kinds.items():
         d_ms = run.time_kernel(head_cfg, kind, tokens=2)
@@ -428,7 +435,7 @@ def attn_paths(torch, dv, stack, n, b, scale, reps=10):
 
 def bench_longctx(torch, dv, synth, configs, args):
     """ByteCross's composition at long context (§3.3, §4.1-4.4): a 32-layer
-    stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 32K / 128K cached
+    stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 16K / 32K / 128K cached
     tokens in five modes through the same kernels and the same split-K
     attention: dense; projection-only (10% of MLP neurons, predicted one
     layer ahead); KV-only (10% of cached positions per head chosen by the
@@ -437,7 +444,7 @@ def bench_longctx(torch, dv, synth, configs, args):
     The selection's scoring pass runs once per context after the seeded
     prompt and is timed on its own, outside tokens/s.
 
-    §4.3's cost-aware crossing: a second sweep at 4K / 16K / 64K gives each
+    §4.3's cost-aware crossing: a second sweep at 4K / 12K / 24K / 64K gives each
     branch's cost beyond its byte-scaled dense time; with the dense time of
     the first sweep interpolated log-log and the costs linearly, the branch
     latencies are predicted and their crossing set beside the measured one
@@ -533,7 +540,7 @@ def bench_longctx(torch, dv, synth, configs, args):
         return pts
 
     out = sweep(wl.ctx_sweep, list(modes), True)
-    cost_pts = sweep((4096, 16384, 65536), ["dense", "proj", "kv", "window"], False)
+    cost_pts = sweep((4096, 12288, 24576, 65536), ["dense", "proj", "kv", "window"], False)
 
     def cross_of(pts, key):
         """log-linear crossing of proj and kv in `key` (speedup), or None."""

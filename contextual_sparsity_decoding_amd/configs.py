@@ -87,7 +87,7 @@ LONGCTX_STACK = Workload(
     name="longctx-32L-d4096-h32-ffn16384-fp16",
     dims=LayerDims(d=4096, N=16384, h=32, d_h=128, r_attn=128, r_mlp=128, wdt="f16"),
     layers=32, k_heads=32, k_neurons=1638, kv_keep=0.10,
-    ctx_sweep=(2048, 8192, 32768, 131072),
+    ctx_sweep=(2048, 8192, 16384, 32768, 131072),
 )
 
 ALL = (MLP_BLOCK_FP32, OPT13B_LAYER, OPT66B_STACK, OPT175B_SHARE, LONGCTX_STACK)

@@ -17,6 +17,11 @@ namespace dv {
 // missing K/V from the stored inputs, reusing the weight rows already held
 // in registers.  Rows are ordered [which][s][e]; workgroups take the K and
 // V blocks before the Q blocks.
+#ifndef DV_QKV_FLIGHT_KB
+#define DV_QKV_FLIGHT_KB 8
+#endif
+constexpr int kQkvFlightKB = DV_QKV_FLIGHT_KB;   // weight bytes a wave keeps in flight (KB; 1 KB per row chunk)
+
 struct QkvArgs {
     const float* y;
     int B, d, h, dh, n_sel;
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     // product for after the last byte arrives.  A live workgroup issues all
     // R * CH loads (chunks past the row re-read chunk 0 and are never used:
     // the dot products stop at the row's end).
-    constexpr int PF = (8 / R) < CH ? 8 / R : CH;      // about 8 KB of rows in flight per wave
+    constexpr int PF = (kQkvFlightKB / R) < CH ? kQkvFlightKB / R : CH;   // kQkvFlightKB of rows in flight per wave
     u32x4 w[R][CH];
     auto load_chunk = [&](int i) {
 #pragma unroll
