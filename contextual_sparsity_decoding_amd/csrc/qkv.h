@@ -168,6 +168,10 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
 // reloads and computes half as much and twice as many run side by side.
 constexpr int qkv_hole_rows(int r) { return r >= 2 ? r / 2 : 1; }
 
+// Rows per wave of the predictor workgroups riding in the launch: one with
+// split rows, so that they need no more registers than the projection's.
+constexpr int qkv_pred_rows(int r, int split) { return split == 2 ? 1 : r; }
+
 // A workgroup owns 4*R consecutive rows of one (which, head) block; wave wv
 // holds rows wv*R .. wv*R+R-1 in registers (lane l: chunks l, l+64, ...), so
 // every input chunk read from LDS serves R rows.  The inputs are y (NB
@@ -180,16 +184,26 @@ constexpr int qkv_hole_rows(int r) { return r >= 2 ? r / 2 : 1; }
 // With LNF (batch of one) the input is the residual stream x and every
 // workgroup applies the block's LayerNorm in LDS while its weight rows are
 // still in flight.
-template <typename T, int NB, int CH, int R, int HB, bool YL, bool LNF>
+//
+// SPLIT = 2 (no LDS staging of stored inputs, HB = 0): a row's chunks are
+// shared by a pair of waves, each holding CH/2 of them for its R rows, so a
+// workgroup owns 2*R rows and a wave half the registers.  Each wave's dot
+// products cover its half; the pair adds the halves in a fixed order
+// (first + second) through LDS, on time and for recomputed positions alike.
+template <typename T, int NB, int CH, int R, int HB, bool YL, bool LNF, int SPLIT = 1>
 __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
+    static_assert(SPLIT == 1 || (SPLIT == 2 && HB == 0 && CH % 2 == 0), "split rows: even chunk count, no staged holes");
     constexpr int E = Vec<T>::E;
     constexpr int HV = HB > 0 ? HB : 1;
+    constexpr int CHW = CH / SPLIT;                    // chunks of a row held by one wave
+    constexpr int RG = 4 / SPLIT;                      // row groups (of R rows) per workgroup
     extern __shared__ float ys[];                      // y [NB][d], then [HB][d] stored inputs
+    __shared__ float pair_part[SPLIT == 2 ? RG * R * NB : 1];   // the second halves' sums
     int qb = blockIdx.x;                               // this workgroup among the projection's
     if constexpr (LNF) {
         if (qb < a.pred_blocks) {                      // look-ahead: the next layer's predictor rows, same LN1(x)
             const LnArgs ln{a.y, a.ln_g, a.ln_b, a.eps, nullptr};
-            rowdot_ln_block<T, CH, ROW_PLAIN, R>(qb, ys, a.pred, ln);
+            rowdot_ln_block<T, CH, ROW_PLAIN, qkv_pred_rows(R, SPLIT)>(qb, ys, a.pred, ln);
             return;
         }
         qb -= a.pred_blocks;
@@ -205,12 +219,15 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     const int d = a.d, dh = a.dh;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int r0 = qb * 4 * R;                         // 4*R divides dh: one head block per workgroup
+    const int grp = SPLIT == 2 ? wv >> 1 : wv;        // this wave's row group
+    const int half = SPLIT == 2 ? wv & 1 : 0;         // and its share of the chunks
+    const int cbase = half * CHW;                      // first chunk index of the share
+    const int r0 = qb * RG * R;                        // RG*R divides dh: one head block per workgroup
     // the K and V blocks (which may carry missing positions) are dispatched
     // first and the Q blocks last, so cheap uniform blocks fill the tail
     const int which = (r0 / (a.n_sel * dh) + 1) % 3;
     const int s = (r0 / dh) % a.n_sel;
-    const int e0 = r0 % dh + wv * R;                   // this wave's first row in the block
+    const int e0 = r0 % dh + grp * R;                  // this wave's first row in the block
     const int nchunk = d / E;
     const int head = a.head_idx ? a.head_idx[s] : s;
     const bool live = (unsigned)head < (unsigned)a.h;
@@ -232,12 +249,12 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     // product for after the last byte arrives.  A live workgroup issues all
     // R * CH loads (chunks past the row re-read chunk 0 and are never used:
     // the dot products stop at the row's end).
-    constexpr int PF = (kQkvFlightKB / R) < CH ? kQkvFlightKB / R : CH;   // kQkvFlightKB of rows in flight per wave
-    u32x4 w[R][CH];
+    constexpr int PF = (kQkvFlightKB / R) < CHW ? kQkvFlightKB / R : CHW;   // kQkvFlightKB of rows in flight per wave
+    u32x4 w[R][CHW];
     auto load_chunk = [&](int i) {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const int c = lane + i * kWave;
+            const int c = lane + (cbase + i) * kWave;
             w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
         }
     };
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
         for (int i = 0; i < PF; ++i) load_chunk(i);
     } else {
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
+        for (int i = 0; i < CHW; ++i)
 #pragma unroll
             for (int j = 0; j < R; ++j) w[j][i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -269,9 +286,34 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
         }
     }
 
-    // lane-partial dots of the R rows with NV inputs at `in` (stride d)
+    // lane-partial dots of the R rows with NV inputs at `in` (stride d),
+    // over this wave's share of the chunks
     auto dots = [&](const float* in, auto nv_tag, float (&acc)[R][decltype(nv_tag)::value]) {
-        qkv_dots<T, CH, R, decltype(nv_tag)::value>(w, in, d, nchunk, acc);
+        qkv_dots<T, CHW, R, decltype(nv_tag)::value>(w, in + (size_t)cbase * kWave * E, d, nchunk - cbase * kWave, acc);
+    };
+
+    // Whole-row sums of R * NV wave-reduced values: with split rows the
+    // second wave of each pair hands its sums to the first, which adds them
+    // after its own; the result is valid in the first wave of the pair.
+    auto pair_add = [&](auto nv_tag, float (&v)[R][decltype(nv_tag)::value]) {
+        constexpr int NV = decltype(nv_tag)::value;
+        if constexpr (SPLIT == 2) {
+            static_assert(NV <= NB, "pair buffer holds NB values per row");
+            if (half == 1 && lane == 0) {
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int u = 0; u < NV; ++u) pair_part[(grp * R + j) * NB + u] = v[j][u];
+            }
+            __syncthreads();
+            if (half == 0) {
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int u = 0; u < NV; ++u) v[j][u] = v[j][u] + pair_part[(grp * R + j) * NB + u];
+            }
+            __syncthreads();                           // read before the next round's writes
+        }
     };
 
     // The weight registers are marked as rewritten after each use, so the
@@ -281,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
-            for (int i = 0; i < CH; ++i) asm volatile("" : "+v"(w[j][i]));
+            for (int i = 0; i < CHW; ++i) asm volatile("" : "+v"(w[j][i]));
     };
 
     // ---- on-time q, k, v (same instructions per input as `dots`, so the
@@ -302,8 +344,8 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
         const float* yin = YL ? ys : a.y;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = lane + i * kWave;
+        for (int i = 0; i < CHW; ++i) {
+            const int c = lane + (cbase + i) * kWave;
             if (c < nchunk) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -344,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
                     }
                 }
             }
-            if (i + PF < CH) {
+            if (i + PF < CHW) {
                 issue_order_fence();                     // the next loads go out after this chunk's work
                 if (live) load_chunk(i + PF);
                 issue_order_fence();
@@ -353,8 +395,13 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[j][b] = wave_sum(acc[j][b]) + bv[j];
-        if (live && pos_ok && lane == 0) {
+            for (int b = 0; b < NB; ++b) acc[j][b] = wave_sum(acc[j][b]);
+        pair_add(std::integral_constant<int, NB>(), acc);
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[j][b] += bv[j];
+        if (live && pos_ok && lane == 0 && half == 0) {
 #pragma unroll
             for (int j = 0; j < R; ++j)
 #pragma unroll
@@ -410,9 +457,12 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             float hacc[R][1];
             dots(a.y_buf + (size_t)p * d, std::integral_constant<int, 1>(), hacc);
 #pragma unroll
+            for (int j = 0; j < R; ++j) hacc[j][0] = wave_sum(hacc[j][0]);
+            pair_add(std::integral_constant<int, 1>(), hacc);
+#pragma unroll
             for (int j = 0; j < R; ++j) {
-                const float hv = wave_sum(hacc[j][0]) + bv[j];
-                if (lane == 0) cache[((size_t)head * a.max_len + p) * dh + e0 + j] = (half_t)hv;
+                const float hv = hacc[j][0] + bv[j];
+                if (lane == 0 && half == 0) cache[((size_t)head * a.max_len + p) * dh + e0 + j] = (half_t)hv;
             }
             fence_w();
         }
@@ -424,9 +474,12 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             float hacc[R][1];
             dots(a.y_buf + ((size_t)b * a.max_len + p) * d, std::integral_constant<int, 1>(), hacc);
 #pragma unroll
+            for (int j = 0; j < R; ++j) hacc[j][0] = wave_sum(hacc[j][0]);
+            pair_add(std::integral_constant<int, 1>(), hacc);
+#pragma unroll
             for (int j = 0; j < R; ++j) {
-                const float hv = wave_sum(hacc[j][0]) + bv[j];
-                if (lane == 0) cache[(((size_t)b * a.h + head) * a.max_len + p) * dh + e0 + j] = (half_t)hv;
+                const float hv = hacc[j][0] + bv[j];
+                if (lane == 0 && half == 0) cache[(((size_t)b * a.h + head) * a.max_len + p) * dh + e0 + j] = (half_t)hv;
             }
             fence_w();
         }
@@ -453,32 +506,37 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     const int rows = 3 * a.n_sel * a.dh;
     const size_t row = (size_t)a.d * sizeof(float);
     const bool holes = a.y_buf && a.valid_upto;
-    if (a.dh % (4 * R)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
-    a.qkv_blocks = rows / (4 * R);
-    a.pred_blocks = a.pred.w ? cdiv(a.pred.n_max, 4 * R) : 0;
     const size_t yl = NB * row <= kQkvLdsMax ? NB * row : 0;   // y in LDS, else read from global memory
     // batch of one with inputs in LDS: one hole helper per K/V block of
     // 4 * qkv_hole_rows(R) rows (more items are taken in turn)
     const int hb = holes && yl + 2 * row <= kQkvLdsMax ? 2 : holes && yl + row <= kQkvLdsMax ? 1 : 0;
+    // without staged stored inputs, rows are split over wave pairs
+    constexpr bool kSplitOk = CH % 2 == 0;
+    const bool split = kSplitOk && hb == 0;
+    const int wg_rows = (split ? 2 : 4) * R;
+    if (a.dh % wg_rows) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
+    a.qkv_blocks = rows / wg_rows;
+    a.pred_blocks = a.pred.w ? cdiv(a.pred.n_max, 4 * qkv_pred_rows(R, split ? 2 : 1)) : 0;
     a.hole_blocks = NB == 1 && a.B == 1 && yl && hb > 0 && a.n_sel <= kWave ? 2 * a.n_sel * (a.dh / (4 * qkv_hole_rows(R))) : 0;
     const int grid = a.pred_blocks + a.qkv_blocks + a.hole_blocks;
     const bool lnf = a.ln_g != nullptr;
     if (lnf && (NB != 1 || !yl)) return fail(DV_ERR_UNSUPPORTED, "Q/K/V with LayerNorm: B=%d d=%d", a.B, a.d);
     if (a.pred.w && (!lnf || a.pred.d != a.d)) return fail(DV_ERR_UNSUPPORTED, "predictor rows need the LayerNorm-folded Q/K/V");
-#define DV_QKV(HB, LDS)                                                                                          \
-    do {                                                                                                         \
-        if constexpr (NB == 1) {                                                                                 \
-            if (lnf) {                                                                                           \
-                hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, true>), dim3(grid), dim3(kBlock), LDS, s, a);  \
-                break;                                                                                           \
-            }                                                                                                    \
-        }                                                                                                        \
-        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, false>), dim3(grid), dim3(kBlock), LDS, s, a); \
-        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false, false>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
+#define DV_QKV(HB, LDS, SP)                                                                                          \
+    do {                                                                                                             \
+        if constexpr (NB == 1) {                                                                                     \
+            if (lnf) {                                                                                               \
+                hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, true, SP>), dim3(grid), dim3(kBlock), LDS, s, a);  \
+                break;                                                                                               \
+            }                                                                                                        \
+        }                                                                                                            \
+        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, false, SP>), dim3(grid), dim3(kBlock), LDS, s, a); \
+        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false, false, SP>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
     } while (0)
-    if (hb == 2) DV_QKV(2, yl + 2 * row);
-    else if (hb == 1) DV_QKV(1, yl + row);
-    else DV_QKV(0, yl);
+    if (hb == 2) DV_QKV(2, yl + 2 * row, 1);
+    else if (hb == 1) DV_QKV(1, yl + row, 1);
+    else if constexpr (kSplitOk) DV_QKV(0, yl, 2);
+    else DV_QKV(0, yl, 1);
 #undef DV_QKV
     return DV_OK;
 }
