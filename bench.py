@@ -271,7 +271,7 @@ def main():
                                                                                   hb.kv_read + p2_bytes)}
     kernels = {}
     for name, (kind, nbytes) in kinds.items():
-        d_ms = run.time_kernel(head_cfg, kind, tokens=2)
+        d_ms = run.time_kernel(head_cfg, kind, tokens=2, warm=W)   # from the state the timed tokens start in
         avg = float(np.mean(d_ms)) if d_ms else float("nan")
         kernels[name] = {"avg_launch_ms": round(avg, 5), "launches": len(d_ms), "bytes_per_launch": int(nbytes),
                          "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),

@@ -436,6 +436,7 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
             c->k_neurons);
     }
     REQ(isfinite(c->scale) && c->eps >= 0.f && isfinite(c->eps), DV_ERR_RANGE, "dv_decode_layer: scale/eps");
+    REQ(c->n_dense_prefix >= 0, DV_ERR_RANGE, "dv_decode_layer: n_dense_prefix=%d", c->n_dense_prefix);
     REQ(!(c->flags & DV_KV_WINDOW) || (!(c->flags & DV_KV_SELECT) && c->win_len > 0 && c->win_sink >= 0),
         DV_ERR_RANGE, "dv_decode_layer: DV_KV_WINDOW win_sink=%d win_len=%d (not with DV_KV_SELECT)", c->win_sink,
         c->win_len);
@@ -771,9 +772,28 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
 }
 
 // ---------------------------------------------------------------- the stack --
+// The configuration of one layer of a stack: the first n_dense_prefix
+// layers compute every head and neuron (Explainer, "Handling the first
+// layer": the first layers run dense and prediction starts after them).
+static dv_decode_cfg stack_layer_cfg(const dv_decode_cfg* c, int l) {
+    dv_decode_cfg cl = *c;
+    if (l < c->n_dense_prefix) cl.flags |= DV_DENSE_ATTN | DV_DENSE_MLP;
+    return cl;
+}
+
+static size_t stack_layer_ws_bytes(const dv_decode_cfg* c, int max_len) {
+    size_t b = layer_ws(nullptr, c, max_len).bytes;
+    if (c->n_dense_prefix > 0) {
+        const dv_decode_cfg cd = stack_layer_cfg(c, 0);
+        const size_t bd = layer_ws(nullptr, &cd, max_len).bytes;
+        b = bd > b ? bd : b;
+    }
+    return b;
+}
+
 size_t dv_stack_workspace_bytes(const dv_decode_cfg* cfg, int max_len) {
     if (check_cfg(cfg) != DV_OK || max_len < 1) return 0;
-    return layer_ws(nullptr, cfg, max_len).bytes + align_up((size_t)2 * cfg->B * cfg->d * sizeof(float), 256);
+    return stack_layer_ws_bytes(cfg, max_len) + align_up((size_t)2 * cfg->B * cfg->d * sizeof(float), 256);
 }
 
 dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_decode_cfg* c, int32_t* head_sets,
@@ -793,7 +813,8 @@ dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_d
         DV_ERR_RANGE, "dv_decode_stack: x_trace overlaps x_in or x_out");
     int max_len = 1;
     for (int l = 0; l < n_layers; ++l) max_len = layers[l].kv.max_len > max_len ? layers[l].kv.max_len : max_len;
-    const size_t lw = layer_ws(nullptr, c, max_len).bytes;
+    const size_t lw = stack_layer_ws_bytes(c, max_len);
+    const int P = c->n_dense_prefix;
     const size_t need = lw + align_up(2 * act, 256);
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_decode_stack: workspace %zu < %zu", ws_bytes, need);
     float* xb[2] = {(float*)((char*)ws + lw), (float*)((char*)ws + lw) + (size_t)c->B * c->d};
@@ -812,28 +833,30 @@ dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_d
         st.kv = ly.kv;
         st.sel_idx = ly.sel_idx; st.sel_len = ly.sel_len; st.sel_cap = ly.sel_cap; st.sel_end = ly.sel_end;
         st.fc2_rows_out = fc2_rows;
-        cl = *c;
+        cl = stack_layer_cfg(c, l);
         // a decode position shared by several layers moves on in the last of them
         for (int m = l + 1; m < n_layers; ++m)
             if (layers[m].kv.pos_dev == ly.kv.pos_dev) cl.flags &= ~(unsigned)DV_ADVANCE_POS;
+        const bool la = dense_a || l < P, lm = dense_m || l < P;            // this layer computes every head / neuron
+        const bool na = dense_a || l + 1 < P, nm = dense_m || l + 1 < P;    // so does the next one
         if (ahead) {
-            if (!dense_a) st.head_idx_in = head_sets + (size_t)l * kA;
-            if (!dense_m) st.neuron_idx_in = neuron_sets + (size_t)l * nmax;
+            if (!la) st.head_idx_in = head_sets + (size_t)l * kA;
+            if (!lm) st.neuron_idx_in = neuron_sets + (size_t)l * nmax;
             if (l + 1 < n_layers) {
                 const dv_layer_weights& wn = layers[l + 1].w;
-                if (!dense_a && kA > 0) {
+                if (!na && kA > 0) {
                     st.next_pa1_t = wn.pa1_t; st.next_pa2_t = wn.pa2_t;
                     st.next_head_idx = head_sets + (size_t)(l + 1) * kA;
                 }
-                if (!dense_m && c->k_neurons > 0) {
+                if (!nm && c->k_neurons > 0) {
                     st.next_pm1_t = wn.pm1_t; st.next_pm2_t = wn.pm2_t;
                     st.next_neuron_idx = neuron_sets + (size_t)(l + 1) * nmax;
                 }
             }
         } else {
-            if (!dense_a && head_sets) st.head_idx_out = head_sets + (size_t)l * kA;
-            if (!dense_m && neuron_sets) st.neuron_idx_out = neuron_sets + (size_t)l * nmax;
-            if (!dense_m && neuron_counts) st.neuron_count_out = neuron_counts + l;
+            if (!la && head_sets) st.head_idx_out = head_sets + (size_t)l * kA;
+            if (!lm && neuron_sets) st.neuron_idx_out = neuron_sets + (size_t)l * nmax;
+            if (!lm && neuron_counts) st.neuron_count_out = neuron_counts + l;
         }
     };
     for (int l = 0; l < n_layers; ++l) {
@@ -848,10 +871,13 @@ dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_d
             snprintf(msg, sizeof msg, "%s", dv_last_error());
             return fail(r, "dv_decode_stack: layer %d: %s", l, msg);
         }
-        if (ahead && next_layer_predictors_missing(st, c, l + 1 < n_layers))
-            return fail(DV_ERR_NULL, "dv_decode_stack: layer %d: predictor of the next layer NULL", l + 1);
+        if (ahead && l + 1 < n_layers) {
+            const dv_decode_cfg cn = stack_layer_cfg(c, l + 1);
+            if (next_layer_predictors_missing(st, &cn, true))
+                return fail(DV_ERR_NULL, "dv_decode_stack: layer %d: predictor of the next layer NULL", l + 1);
+        }
     }
-    if (ahead) {   // the first layer's sets from its own predictors on LN1(x)
+    if (ahead && P == 0) {   // the first layer's sets from its own predictors on LN1(x)
         const dv_layer_weights& w0 = layers[0].w;
         REQ(dense_a || kA == 0 || (w0.pa1_t && w0.pa2_t), DV_ERR_NULL, "dv_decode_stack: layer 0 head predictor NULL");
         REQ(dense_m || c->k_neurons == 0 || (w0.pm1_t && w0.pm2_t), DV_ERR_NULL, "dv_decode_stack: layer 0 neuron predictor NULL");

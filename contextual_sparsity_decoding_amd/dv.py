@@ -54,7 +54,7 @@ class KVView(C.Structure):
 class DecodeCfg(C.Structure):
     _fields_ = [("B", ci), ("d", ci), ("h", ci), ("d_h", ci), ("N", ci), ("r_attn", ci), ("r_mlp", ci),
                 ("k_heads", ci), ("k_neurons", ci), ("wdt", ci), ("pred_act", ci), ("eps", cf),
-                ("scale", cf), ("flags", cu), ("win_sink", ci), ("win_len", ci)]
+                ("scale", cf), ("flags", cu), ("win_sink", ci), ("win_len", ci), ("n_dense_prefix", ci)]
 
 
 class LayerWeights(C.Structure):

@@ -300,6 +300,7 @@ typedef struct {
     float scale;              /* attention score scale */
     unsigned flags;           /* DV_* flags above */
     int win_sink, win_len;    /* DV_KV_WINDOW: sink and recent positions, as in dv_kv_view */
+    int n_dense_prefix;       /* dv_decode_stack: the first n layers run dense (>= 0; ignored by dv_decode_layer) */
 } dv_decode_cfg;
 
 typedef struct {
@@ -368,13 +369,19 @@ dv_status dv_decode_layer(const dv_layer_weights* w, const dv_decode_cfg* cfg,
  * last layer writes x_out.  Every layer uses `cfg` (with per-layer weights
  * and state from layers[l]).
  *
- * With DV_LOOKAHEAD (batch of one), layer 0's sets come from its own
- * predictors on LN1(x_in) (there is no layer before it), and layer l runs on
- * the sets layer l-1 predicted from its LN1 input, with layer l's
- * predictors, while computing its own block; the sets live in
+ * The first cfg->n_dense_prefix layers compute every head and neuron
+ * (Explainer, "Handling the first layer": the first one or two layers run
+ * dense and prediction starts after them); the layers after them use cfg.
+ *
+ * With DV_LOOKAHEAD (batch of one), layer l runs on the sets layer l-1
+ * predicted from its LN1 input, with layer l's predictors, while computing
+ * its own block.  The first sparse layer's sets come from the last dense
+ * layer, or, without a dense prefix, layer 0's from its own predictors on
+ * LN1(x_in) (there is no layer before it).  The sets live in
  *   head_sets    device int32 [n_layers][k_heads]   (required unless DV_DENSE_ATTN)
  *   neuron_sets  device int32 [n_layers][k_neurons] (required unless DV_DENSE_MLP)
- * and hold, after the call, the sets each layer ran on.  Without it each
+ * and hold, after the call, the sets each sparse layer ran on (the rows of
+ * the dense prefix are not written).  Without it each
  * layer predicts its own blocks' sets in the sequential form, and the
  * optional head_sets / neuron_sets (NULL to skip) receive them; with a
  * batch, row l of neuron_sets ([n_layers][min(N, B*k_neurons)]) holds the

@@ -483,22 +483,28 @@ def predict_sets(x, W: dict, k_heads: int, k_neurons: int, eps: float = 1e-5, pr
 def decode_stack_lookahead(x, Ws: Sequence[dict], kvs: Sequence[KVState], pos: int, *, k_heads: int,
                            k_neurons: int, scale: float, eps: float = 1e-5, pred_act: str = "relu",
                            skip_nonpos: bool = True, hole_fill: bool = True,
-                           window: Optional[Tuple[int, int]] = None):
+                           window: Optional[Tuple[int, int]] = None, n_dense_prefix: int = 0):
     """One token through a stack of layers in DejaVu §4.3's parallel form.
 
     The output of layer l is the input of layer l+1 (§3, the residual
-    stream).  Layer 0 runs on the sets its own predictors give for LN1(x)
-    (``predict_sets``); layer l > 0 runs on the sets layer l-1's
+    stream).  The first ``n_dense_prefix`` layers compute every head and
+    neuron (Explainer, "Handling the first layer").  The first sparse layer
+    runs on the sets the last dense layer predicted, or, with no dense
+    prefix, layer 0 on the sets its own predictors give for LN1(x)
+    (``predict_sets``); every later layer runs on the sets layer l-1's
     ``decode_layer_lookahead`` predicted from its normalised input with
     layer l's predictors.  Every layer's token sits at ``pos``.
 
     x [1][d].  Returns (x_out [1][d], list of per-layer records, each with
     the layer's input ``x`` and the sets it ran on).  Mutates ``kvs``.
     """
-    heads, neurons, _, _ = predict_sets(x, Ws[0], k_heads, k_neurons, eps, pred_act)
+    P = n_dense_prefix
+    heads = neurons = None
+    if P == 0:
+        heads, neurons, _, _ = predict_sets(x, Ws[0], k_heads, k_neurons, eps, pred_act)
     recs = []
     for l, W in enumerate(Ws):
-        W_next = Ws[l + 1] if l + 1 < len(Ws) else None
+        W_next = Ws[l + 1] if l + 1 < len(Ws) and l + 1 >= P else None
         x_in = _f64(np.atleast_2d(x))
         x, rec = decode_layer_lookahead(x, W, W_next, kvs[l], pos, head_idx=heads, neuron_idx=neurons,
                                         k_heads=k_heads, k_neurons=k_neurons, scale=scale, eps=eps,

@@ -156,6 +156,14 @@ def test_decode_layer_validation(dv):
     cfg.flags, cfg.win_sink, cfg.win_len = dv.DV_KV_WINDOW | dv.DV_KV_SELECT, 4, 8
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
     assert "DV_KV_WINDOW" in err(dv)
+    cfg.flags, cfg.win_sink, cfg.win_len, cfg.n_dense_prefix = 0, 0, 0, -1
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+    assert L.dv_stack_workspace_bytes(C.byref(cfg), 32) == 0
+    # a dense prefix needs room for the dense layers' workspace
+    cfg.n_dense_prefix = 0
+    sparse = L.dv_stack_workspace_bytes(C.byref(cfg), 32)
+    cfg.n_dense_prefix = 1
+    assert L.dv_stack_workspace_bytes(C.byref(cfg), 32) >= sparse
 
 
 def test_lookahead_sets_must_not_alias(dv):

@@ -62,7 +62,7 @@ def test_fill_normal_layout_of_a_tensor(dvlib):
 class DeviceStack:
     """A Stack plus the buffers a look-ahead decode carries."""
 
-    def __init__(self, dv, dims, L, n0, max_len, seed, k_heads, k_neurons, window=None):
+    def __init__(self, dv, dims, L, n0, max_len, seed, k_heads, k_neurons, window=None, n_dense_prefix=0):
         from contextual_sparsity_decoding_amd.stack import Stack
         self.dv, self.dims, self.L, self.kA, self.kM = dv, dims, L, k_heads, k_neurons
         self.S = Stack(dims, L, n0, max_len, seed)
@@ -72,6 +72,7 @@ class DeviceStack:
         self.cfg = self.S.cfg(k_heads, k_neurons, flags, 1 / math.sqrt(dims.d_h))
         if window is not None:
             self.cfg.win_sink, self.cfg.win_len = window
+        self.cfg.n_dense_prefix = n_dense_prefix
         self.ws = dv.workspace(dv.dv_stack_workspace_bytes(self.cfg, max_len))
         self.head_sets = torch.full((L, k_heads), -1, dtype=torch.int32, device="cuda")
         self.neuron_sets = torch.full((L, k_neurons), -1, dtype=torch.int32, device="cuda")
@@ -95,16 +96,18 @@ def _follow(got, want, scores, k, what):
     return np.asarray(got, np.int64)
 
 
-@pytest.mark.parametrize("window", [None, (4, 16)])
-def test_stack_chained_small(dvlib, window):
+@pytest.mark.parametrize("window,P", [(None, 0), ((4, 16), 0), (None, 1)])
+def test_stack_chained_small(dvlib, window, P):
     """3 layers x 4 tokens: every layer's sets, output, K/V and valid
     positions follow the oracle's chain (layer l's input is layer l-1's
     output; its sets were predicted by layer l-1).  With ``window`` every
     layer reads its 4 sink and 16 most recent positions, a window that
-    slides one position per token."""
+    slides one position per token; with P = 1 layer 0 runs dense and
+    predicts layer 1's sets."""
     dims = LayerDims(d=1024, N=4096, h=8, d_h=128, r_attn=32, r_mlp=64, wdt="f16")
-    L, n0, T, kA, kM, seed = 3, 40, 4, 3, 400, 17 if window is None else 18
-    D = DeviceStack(dvlib, dims, L, n0, n0 + T + 2, seed, kA, kM, window)
+    L, n0, T, kA, kM = 3, 40, 4, 3, 400
+    seed = 17 + (window is not None) + 2 * P
+    D = DeviceStack(dvlib, dims, L, n0, n0 + T + 2, seed, kA, kM, window, P)
     Ws = [synth.stack_layer_weights(dims, seed, l) for l in range(L)]
     kvs = []
     for l in range(L):
@@ -117,12 +120,14 @@ def test_stack_chained_small(dvlib, window):
     for t in range(T):
         D.token(dev(X[t]))
         got_h, got_n, got_x, got_tr = host(D.head_sets), host(D.neuron_sets), host(D.x_out), host(D.x_trace)
-        heads, neurons, sA, sM = ref.predict_sets(X[t], Ws[0], kA, kM)
-        heads = _follow(got_h[0], heads, sA[0], kA, f"token {t} layer 0 heads")
-        neurons = _follow(got_n[0], neurons, sM[0], kM, f"token {t} layer 0 neurons")
+        heads = neurons = None
+        if P == 0:
+            heads, neurons, sA, sM = ref.predict_sets(X[t], Ws[0], kA, kM)
+            heads = _follow(got_h[0], heads, sA[0], kA, f"token {t} layer 0 heads")
+            neurons = _follow(got_n[0], neurons, sM[0], kM, f"token {t} layer 0 neurons")
         x = X[t]
         for l in range(L):
-            Wn = Ws[l + 1] if l + 1 < L else None
+            Wn = Ws[l + 1] if l + 1 < L and l + 1 >= P else None
             x, rec = ref.decode_layer_lookahead(x, Ws[l], Wn, kvs[l], n0 + t, head_idx=heads, neuron_idx=neurons,
                                                 k_heads=kA, k_neurons=kM, scale=scale, window=window)
             got = got_tr[l] if l + 1 < L else got_x

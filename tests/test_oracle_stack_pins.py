@@ -99,3 +99,35 @@ def test_one_layer_stack_is_the_layer():
     want, _ = ref.decode_layer_lookahead(x, Ws[0], None, kv2, N0, head_idx=hi, neuron_idx=ni, k_heads=kA,
                                          k_neurons=kM, scale=0.25, hole_fill=False)
     assert np.array_equal(got, want)
+
+
+def test_dense_prefix_layers_are_plain_dense_layers():
+    """With n_dense_prefix = 2 of 3 layers: layers 0 and 1 are the plain
+    dense torch layer (every head and neuron), and layer 2 runs on the top-k
+    of its predictors applied to LN1 of layer 1's input."""
+    Ws, caches, x = _setup(7)
+    kA, kM = 2, 40
+    scale = 0.25
+    kvs = [ref.KVState(K.copy(), V.copy()) for K, V in caches]
+    out, recs = ref.decode_stack_lookahead(x, Ws, kvs, N0, k_heads=kA, k_neurons=kM, scale=scale,
+                                           skip_nonpos=False, hole_fill=False, n_dense_prefix=2)
+    want = np.atleast_2d(x).astype(np.float64)
+    for l in range(2):
+        K, V = caches[l][0].copy(), caches[l][1].copy()
+        want = torch_layer(want, Ws[l], K, V, N0, scale)
+        assert np.array_equal(recs[l]["head_idx"], np.arange(DIMS.h))
+        assert np.array_equal(recs[l]["neuron_idx"], np.arange(DIMS.N))
+    assert np.max(np.abs(recs[2]["x"] - want)) <= 1e-10 * np.max(np.abs(want))
+    y = F.layer_norm(_t(recs[1]["x"]), (DIMS.d,), _t(Ws[1]["ln1_g"]), _t(Ws[1]["ln1_b"]), 1e-5)
+    for p1, p2, k, key in (("pa1_t", "pa2_t", kA, "head_idx"), ("pm1_t", "pm2_t", kM, "neuron_idx")):
+        s = (torch.relu(y @ _t(Ws[2][p1]).T) @ _t(Ws[2][p2]).T)[0].numpy().astype(np.float32)
+        order = sorted(range(s.size), key=lambda i: (-float(s[i]), i))
+        assert np.array_equal(recs[2][key], np.sort(order[:k])), key
+    # a prefix covering the stack is the dense stack
+    kvs2 = [ref.KVState(K.copy(), V.copy()) for K, V in caches]
+    got, _ = ref.decode_stack_lookahead(x, Ws, kvs2, N0, k_heads=kA, k_neurons=kM, scale=scale, skip_nonpos=False,
+                                        hole_fill=False, n_dense_prefix=L)
+    kvs3 = [ref.KVState(K.copy(), V.copy()) for K, V in caches]
+    dense, _ = ref.decode_stack_lookahead(x, Ws, kvs3, N0, k_heads=DIMS.h, k_neurons=DIMS.N, scale=scale,
+                                          skip_nonpos=False, hole_fill=False)
+    assert np.array_equal(got, dense)
