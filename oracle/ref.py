@@ -462,6 +462,66 @@ def decode_layer_lookahead(x, W: dict, W_next: Optional[dict], kv: KVState, pos:
     return out, rec
 
 
+# ------------------------------------------------------ threshold sparsity --
+
+TEAL_INPUTS = ("qkv", "o", "fc1", "fc2")       # the input of each projection, in order
+
+
+def teal_mask(x, t: float) -> np.ndarray:
+    """x with every entry whose magnitude is not above t set to zero.
+
+    ByteCross §4.1 and App. A: the projection branch is TEAL activation
+    sparsity, a magnitude threshold on the input of each projection; a
+    projection then reads only the weights of the input channels kept
+    (§2: projection-side methods threshold active channels to cut weight
+    reads)."""
+    x = _f64(x)
+    return np.where(np.abs(x) > t, x, 0.0)
+
+
+def teal_layer(x, W: dict, kv: KVState, pos: int, *, thr: Sequence[float], scale: float, eps: float = 1e-5,
+               sel_idx=None, sel_len=None, sel_end: Optional[int] = None,
+               window: Optional[Tuple[int, int]] = None):
+    """One decode step of the pre-LN layer with threshold sparsity on the
+    input of every projection and every head and neuron computed.
+
+    thr = (t_qkv, t_o, t_fc1, t_fc2), the thresholds of the four projection
+    inputs y = LN1(x), o (the heads' attention outputs), y2 = LN2(h) and the
+    ReLU activations a.  K/V of the token are stored (fp16) for every head;
+    attention reads every position, or the retained set / window as in
+    ``attention`` (the composition with the KV branch, ByteCross §4.2).
+
+    x [B][d].  Returns (x_out [B][d], record with the inputs before the
+    threshold and ``kept``: per projection input, the channels some
+    sequence of the batch keeps, ascending).  Mutates ``kv``.
+    """
+    x = _f64(np.atleast_2d(x))
+    h = W["w_qkv_t"].shape[1]
+    heads = np.arange(h)
+    t_qkv, t_o, t_fc1, t_fc2 = (float(t) for t in thr)
+    y = layernorm(x, W["ln1_g"], W["ln1_b"], eps)
+    q = qkv_step(teal_mask(y, t_qkv), W["w_qkv_t"], W["b_qkv"], heads, kv, pos, hole_fill=False)
+    o = attention(q, kv, heads, pos + 1, scale, sel_idx, sel_len, sel_end, window)
+    hres = out_proj(teal_mask(o, t_o), W["w_o_t"], W["b_o"], heads, residual=x)
+    y2 = layernorm(hres, W["ln2_g"], W["ln2_b"], eps)
+    a = relu(teal_mask(y2, t_fc1) @ _f64(W["w1_t"]).T + _f64(W["b1"]))
+    out = hres + teal_mask(a, t_fc2) @ _f64(W["w2_t"]) + _f64(W["b2"])
+    B = x.shape[0]
+    inputs = {"qkv": y, "o": o.reshape(B, -1), "fc1": y2, "fc2": a}
+    kept = {k: np.flatnonzero(np.any(np.abs(v) > t, axis=0))
+            for (k, v), t in zip(inputs.items(), (t_qkv, t_o, t_fc1, t_fc2))}
+    return out, dict(inputs=inputs, kept=kept, q=q, h=hres)
+
+
+def teal_layer_bytes(d: int, h: int, d_h: int, N: int, kept: dict, wb: int = 2) -> float:
+    """Weight bytes one threshold-sparse step reads: the kept channels' rows
+    of the input-major projections (Q/K/V: 3 h d_h per input channel; W^O:
+    d; fc1: N; fc2: d), plus every bias."""
+    rows = (len(kept["qkv"]) * 3 * h * d_h + len(kept["o"]) * d + len(kept["fc1"]) * N
+            + len(kept["fc2"]) * d)
+    return wb * (rows + 3 * h * d_h + d + N + d)
+
+
 # ---------------------------------------------------------------- the stack --
 
 def predict_sets(x, W: dict, k_heads: int, k_neurons: int, eps: float = 1e-5, pred_act: str = "relu"):

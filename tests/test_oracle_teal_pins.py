@@ -1,0 +1,107 @@
+"""Pins of the oracle's threshold-sparse layer (ref.teal_layer, ByteCross
+§4.1 / App. A) to things other than itself: the dense layer (itself pinned
+to torch) when every channel is kept, a closed form when none is, weight
+perturbations that must or must not move the output, brute-force counts,
+and the byte account's dense total."""
+import math
+
+import numpy as np
+
+from contextual_sparsity_decoding_amd import synth
+from contextual_sparsity_decoding_amd.configs import LayerDims
+from oracle import bytes as obytes
+from oracle import ref
+
+DIMS = LayerDims(d=64, N=256, h=4, d_h=16, r_attn=8, r_mlp=8, wdt="f16")
+N0, MAXLEN = 9, 12
+SCALE = 1 / math.sqrt(DIMS.d_h)
+
+
+def _setup(seed, B=1):
+    W = synth.layer_weights(DIMS, seed)
+    K, V = synth.kv_cache(DIMS.h, DIMS.d_h, N0, MAXLEN, seed, batch=B)
+    x = synth.layer_inputs(DIMS.d, 1, B, seed)[0]
+    return W, K, V, x
+
+
+def _run(W, K, V, x, thr, **kw):
+    kv = ref.KVState(K.copy(), V.copy())
+    out, rec = ref.teal_layer(x, W, kv, N0, thr=thr, scale=SCALE, **kw)
+    return out, rec, kv
+
+
+def test_keeping_every_channel_is_the_dense_layer():
+    W, K, V, x = _setup(1)
+    got, _, kv1 = _run(W, K, V, x, (-1, -1, -1, -1))
+    kv2 = ref.KVState(K.copy(), V.copy())
+    want, _ = ref.decode_layer(x, W, kv2, N0, k_heads=DIMS.h, k_neurons=DIMS.N, scale=SCALE, dense_attn=True,
+                               dense_mlp=True, skip_nonpos=False, hole_fill=False)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert np.array_equal(kv1.K, kv2.K) and np.array_equal(kv1.V, kv2.V)
+
+
+def test_keeping_no_channel_leaves_the_biases():
+    W, K, V, x = _setup(2)
+    got, rec, kv = _run(W, K, V, x, (np.inf,) * 4)
+    want = np.atleast_2d(x).astype(np.float64) + W["b_o"].astype(np.float64) + W["b2"].astype(np.float64)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert np.array_equal(kv.K[0, :, N0], W["b_qkv"][1].astype(np.float16))
+    assert np.array_equal(kv.V[0, :, N0], W["b_qkv"][2].astype(np.float16))
+    assert all(len(v) == 0 for v in rec["kept"].values())
+
+
+def _perturbed(W, which, rows):
+    """A copy of W with the weights of input channels `rows` of projection
+    input `which` replaced by noise."""
+    W2 = {k: v.copy() for k, v in W.items()}
+    g = np.random.default_rng(5)
+    if which == "qkv":
+        W2["w_qkv_t"][..., rows] = g.standard_normal(W2["w_qkv_t"][..., rows].shape).astype(np.float16)
+    elif which == "o":
+        W2["w_o_t"][rows] = g.standard_normal(W2["w_o_t"][rows].shape).astype(np.float16)
+    elif which == "fc1":
+        W2["w1_t"][:, rows] = g.standard_normal(W2["w1_t"][:, rows].shape).astype(np.float16)
+    else:
+        W2["w2_t"][rows] = g.standard_normal(W2["w2_t"][rows].shape).astype(np.float16)
+    return W2
+
+
+def test_only_kept_channels_are_read():
+    """Noise in the weights of every dropped channel of a projection input
+    leaves the output as it is; noise in one kept channel moves it."""
+    W, K, V, x = _setup(3)
+    thr = (0.6, 0.05, 0.7, 0.02)
+    base, rec, _ = _run(W, K, V, x, thr)
+    widths = {"qkv": DIMS.d, "o": DIMS.h * DIMS.d_h, "fc1": DIMS.d, "fc2": DIMS.N}
+    for k in ref.TEAL_INPUTS:
+        kept = rec["kept"][k]
+        dropped = np.setdiff1d(np.arange(widths[k]), kept)
+        assert 0 < len(kept) < widths[k], k
+        out, rec2, _ = _run(_perturbed(W, k, dropped), K, V, x, thr)
+        assert np.array_equal(out, base), k
+        out, _, _ = _run(_perturbed(W, k, kept[:1]), K, V, x, thr)
+        assert not np.allclose(out, base, rtol=0, atol=1e-9), k
+
+
+def test_kept_channels_brute_force_and_batch_union():
+    W, K, V, x = _setup(4, B=2)
+    thr = (0.5, 0.04, 0.9, 0.01)
+    out, rec, _ = _run(W, K, V, x, thr)
+    for k, t in zip(ref.TEAL_INPUTS, thr):
+        v = rec["inputs"][k]
+        want = [i for i in range(v.shape[1]) if abs(v[0, i]) > t or abs(v[1, i]) > t]
+        assert rec["kept"][k].tolist() == want, k
+    # each sequence computes with its own thresholded inputs
+    for b in range(2):
+        ob, _, _ = _run(W, K[b:b + 1], V[b:b + 1], x[b:b + 1], thr)
+        assert np.allclose(out[b], ob[0], rtol=0, atol=1e-12)
+
+
+def test_byte_account_with_every_channel_is_the_dense_layer():
+    d = DIMS.d
+    kept = {"qkv": np.arange(d), "o": np.arange(d), "fc1": np.arange(d), "fc2": np.arange(DIMS.N)}
+    attn, mlp = obytes.opt_layer_params(d)
+    want = 2 * (attn + mlp) + 2 * (3 * d + d + DIMS.N + d)
+    assert ref.teal_layer_bytes(d, DIMS.h, DIMS.d_h, DIMS.N, kept) == want
+    half = {k: v[: len(v) // 2] for k, v in kept.items()}
+    assert ref.teal_layer_bytes(d, DIMS.h, DIMS.d_h, DIMS.N, half) == (attn + mlp) + 2 * (3 * d + d + DIMS.N + d)
