@@ -397,7 +397,14 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     const AxpyPlan po = axpy_plan(d, nsel * dh, c->wdt), pm = axpy_plan(d, nmax, c->wdt);
     const size_t xp = axpy_ws_floats(po, B, d) > axpy_ws_floats(pm, B, d) ? axpy_ws_floats(po, B, d)
                                                                            : axpy_ws_floats(pm, B, d);
-    w.xpart = cv.take<float>(xp);
+    size_t xpt = xp;
+    if (c->flags & DV_TEAL) {   // the input-major Q/K/V and fc1 sums are 3*h*d_h and N wide
+        const size_t a1 = axpy_ws_floats(axpy_plan(3 * h * dh, d, c->wdt), B, 3 * h * dh);
+        const size_t a2 = axpy_ws_floats(axpy_plan(c->N, d, c->wdt), B, c->N);
+        xpt = a1 > xpt ? a1 : xpt;
+        xpt = a2 > xpt ? a2 : xpt;
+    }
+    w.xpart = cv.take<float>(xpt);
     w.ya = cv.take<float>((size_t)d);
     w.hpartA = cv.take<float>((size_t)(c->r_attn > 0 ? c->r_attn : 1) + (c->r_mlp > 0 ? c->r_mlp : 1));   // [rA + rM]
     w.hpartM = cv.take<float>(pred_partials(1, d, c->r_mlp > 0 ? c->r_mlp : 1, c->wdt));
@@ -417,7 +424,7 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(wdt_ok(c->wdt), DV_ERR_DTYPE, "dv_decode_layer: wdt %d", c->wdt);
     REQ(c->pred_act == DV_ACT_NONE || c->pred_act == DV_ACT_RELU, DV_ERR_DTYPE, "dv_decode_layer: pred_act");
     const unsigned known = DV_SKIP_NONPOS_FC2 | DV_DENSE_ATTN | DV_DENSE_MLP | DV_HOLE_FILL | DV_KV_SELECT | DV_ADVANCE_POS |
-                           DV_LOOKAHEAD | DV_KV_WINDOW;
+                           DV_LOOKAHEAD | DV_KV_WINDOW | DV_TEAL;
     REQ((c->flags & ~known) == 0, DV_ERR_DTYPE, "dv_decode_layer: flags 0x%x", c->flags);
     REQ(c->B >= 1 && c->B <= 16 && d_ok(c->d) && c->h >= 1 && dh_ok(c->d_h) && c->N >= 1, DV_ERR_SHAPE,
         "dv_decode_layer: B=%d d=%d h=%d d_h=%d N=%d", c->B, c->d, c->h, c->d_h, c->N);
@@ -440,6 +447,10 @@ static dv_status check_cfg(const dv_decode_cfg* c) {
     REQ(!(c->flags & DV_KV_WINDOW) || (!(c->flags & DV_KV_SELECT) && c->win_len > 0 && c->win_sink >= 0),
         DV_ERR_RANGE, "dv_decode_layer: DV_KV_WINDOW win_sink=%d win_len=%d (not with DV_KV_SELECT)", c->win_sink,
         c->win_len);
+    REQ(!(c->flags & DV_TEAL) || ((c->flags & DV_DENSE_ATTN) && (c->flags & DV_DENSE_MLP) &&
+                                  !(c->flags & (DV_LOOKAHEAD | DV_HOLE_FILL))),
+        DV_ERR_UNSUPPORTED, "dv_decode_layer: DV_TEAL needs DV_DENSE_ATTN and DV_DENSE_MLP, without DV_LOOKAHEAD "
+        "or DV_HOLE_FILL (flags 0x%x)", c->flags);
     if (c->flags & DV_LOOKAHEAD) {
         REQ(c->B == 1, DV_ERR_UNSUPPORTED, "dv_decode_layer: DV_LOOKAHEAD with B=%d", c->B);
         REQ(c->r_attn >= 1 && c->r_attn <= 512 && (size_t)c->r_attn * eb % 16 == 0 && c->r_mlp >= 1 &&
@@ -628,6 +639,60 @@ static dv_status decode_lookahead(const dv_layer_weights* w, const dv_decode_cfg
     return DV_OK;
 }
 
+// ByteCross's projection branch (§4.1, App. A): every head and neuron, each
+// projection reading only the input-major rows of the input channels above
+// its threshold.  LN1, the Q/K/V gather-AXPY (its finalize scatters q and
+// the token's K/V), split-K attention with its combine, the output
+// projection, LN2, fc1 (finalize: bias and ReLU), fc2: each projection's
+// input is thresholded where its gather resolves its rows.
+static dv_status decode_teal(const dv_layer_weights* w, const dv_decode_cfg* c, const dv_layer_state* st,
+                             const dv_kv_view& view, const LayerWs& L, const float* x_in, float* x_out, hipStream_t s) {
+    const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N, hd = h * dh;
+    const dv_kv_state& kv = st->kv;
+    const int R = d > hd ? (d > N ? d : N) : (hd > N ? hd : N);
+    auto record = [&](int i, const float* src, int width) -> dv_status {   // the input before its threshold
+        if (!st->teal_rec) return DV_OK;
+        const hipError_t e = hipMemcpy2DAsync(st->teal_rec + (size_t)i * B * R, (size_t)R * 4, src, (size_t)width * 4,
+                                              (size_t)width * 4, B, hipMemcpyDeviceToDevice, s);
+        return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "teal_rec copy: %s", hipGetErrorString(e));
+    };
+    auto rows_out = [&](int i) { return st->teal_rows_out ? st->teal_rows_out + i : nullptr; };
+    auto gather = [&](const void* wt, int width, int rows, const float* coef, int i, const void* bias,
+                      const float* residual, float* out, int timed) {
+        AxpyCall ac{};
+        ac.w = wt; ac.wdt = c->wdt; ac.d = width; ac.w_rows = rows; ac.rows = rows; ac.blk = 1; ac.coef = coef;
+        ac.coef_stride = rows; ac.skip_zero = true; ac.thresh = true; ac.thr = st->teal_thr[i]; ac.B = B;
+        ac.bias = bias; ac.residual = residual; ac.out = out; ac.rows_read = rows_out(i); ac.partial = L.xpart;
+        ac.timed = timed;
+        return ac;
+    };
+    TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
+    TRY(record(0, L.y, d));
+    {
+        AxpyCall ac = gather(w->w_qkv_in, 3 * hd, d, L.y, 0, w->b_qkv, nullptr, nullptr, DV_KERNEL_QKV);
+        ac.epi.mode = FIN_QKV; ac.epi.q = L.q; ac.epi.k = (half_t*)kv.k_cache; ac.epi.v = (half_t*)kv.v_cache;
+        ac.epi.h = h; ac.epi.dh = dh; ac.epi.max_len = kv.max_len; ac.epi.pos = kv.pos; ac.epi.pos_dev = kv.pos_dev;
+        TRY(launch_axpy(ac, s));
+    }
+    timed_begin(DV_KERNEL_ATTN, s);
+    TRY(launch_splitk(L.q, B, dh, nullptr, h, &view, kv.pos_dev, 1, c->scale, 0, L.o, L.apart, nullptr, kv.pos,
+                      kv.pos_dev, s));
+    timed_end(DV_KERNEL_ATTN, s);
+    TRY(record(1, L.o, hd));
+    TRY(launch_axpy(gather(w->w_o_t, d, hd, L.o, 1, w->b_o, x_in, L.hres, DV_KERNEL_OUT), s));
+    TRY(launch_layernorm(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, s));
+    TRY(record(2, L.y2, d));
+    {
+        AxpyCall ac = gather(w->w1_in, N, d, L.y2, 2, w->b1, nullptr, L.a, DV_KERNEL_FC1);
+        ac.epi.mode = FIN_RELU;
+        TRY(launch_axpy(ac, s));
+    }
+    TRY(record(3, L.a, N));
+    AxpyCall mc = gather(w->w2_t, d, N, L.a, 3, w->b2, L.hres, x_out, DV_KERNEL_FC2);
+    mc.advance = (c->flags & DV_ADVANCE_POS) ? kv.pos_dev : nullptr;
+    return launch_axpy(mc, s);
+}
+
 size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len) {
     if (check_cfg(cfg) != DV_OK || max_len < 1) return 0;
     return layer_ws(nullptr, cfg, max_len).bytes;
@@ -683,9 +748,19 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
     const LayerWs L = layer_ws(ws, c, kv.max_len);
     REQ(ws && ws_bytes >= L.bytes, DV_ERR_WORKSPACE, "dv_decode_layer: workspace %zu < %zu", ws_bytes, L.bytes);
     if (ahead) TRY(check_lookahead(c, st));
+    const bool teal = (c->flags & DV_TEAL) != 0;
+    if (teal) {
+        REQ(w->w_qkv_in && w->w1_in, DV_ERR_NULL, "dv_decode_layer: DV_TEAL needs w_qkv_in and w1_in");
+        REQ(a16(w->w_qkv_in) && a16(w->w1_in), DV_ERR_ALIGN, "dv_decode_layer: input-major weight alignment");
+        REQ(((size_t)3 * c->h * c->d_h * elt_bytes(c->wdt)) % 16 == 0 && ((size_t)c->N * elt_bytes(c->wdt)) % 16 == 0,
+            DV_ERR_ALIGN, "dv_decode_layer: DV_TEAL rows of 3*h*d_h=%d or N=%d", 3 * c->h * c->d_h, c->N);
+        for (int i = 0; i < 4; ++i)
+            REQ(!isnan(st->teal_thr[i]), DV_ERR_RANGE, "dv_decode_layer: teal_thr[%d] is NaN", i);
+    }
     if (!run) return DV_OK;
 
     if (ahead) return decode_lookahead(w, c, st, view, L, x_in, x_out, ws, s);
+    if (teal) return decode_teal(w, c, st, view, L, x_in, x_out, s);
     const int B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N;
     // attention block: LN1 folded into the head predictor when heads are selected
     const int32_t* head_idx = nullptr;
@@ -833,6 +908,8 @@ dv_status dv_decode_stack(const dv_stack_layer* layers, int n_layers, const dv_d
         st.kv = ly.kv;
         st.sel_idx = ly.sel_idx; st.sel_len = ly.sel_len; st.sel_cap = ly.sel_cap; st.sel_end = ly.sel_end;
         st.fc2_rows_out = fc2_rows;
+        for (int i = 0; i < 4; ++i) st.teal_thr[i] = ly.teal_thr[i];
+        st.teal_rows_out = ly.teal_rows_out; st.teal_rec = ly.teal_rec;
         cl = stack_layer_cfg(c, l);
         // a decode position shared by several layers moves on in the last of them
         for (int m = l + 1; m < n_layers; ++m)

@@ -191,6 +191,19 @@ __device__ __forceinline__ void block_copy_f32(float* __restrict__ dst, const fl
 struct RowArgs;    // rowdot.h
 struct Pred2Args;  // pred.h
 
+// The finalize's epilogue (gather-AXPY): store the sums, store their ReLU,
+// or scatter a Q/K/V output row (columns [which][h][d_h]) into q (fp32
+// [B][h][d_h]) and the K/V caches' slot pos (*pos_dev when set).
+enum { FIN_STORE = 0, FIN_RELU = 1, FIN_QKV = 2 };
+struct FinEpi {
+    int mode;
+    float* q;
+    half_t* k;
+    half_t* v;
+    int h, dh, max_len, pos;
+    const int32_t* pos_dev;
+};
+
 }  // namespace dv
 
 // ---- host side --------------------------------------------------------------
@@ -261,6 +274,9 @@ struct AxpyCall {
     const float* coef;        // [B][coef_stride], or NULL with apart
     int coef_stride;
     bool skip_zero;
+    bool thresh;              // with skip_zero: coefficients of magnitude <= thr count as zero
+    float thr;
+    dv::FinEpi epi;           // the finalize's epilogue (FIN_STORE by default)
     const float* apart;       // split-K attention partials giving the coefficients, or NULL
     int num_splits;
     int B;

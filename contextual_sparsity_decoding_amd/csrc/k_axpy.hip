@@ -45,6 +45,8 @@ struct AxpyArgs {
     const float* coef;        // coef[b * coef_stride + u]
     int coef_stride;
     int skip_zero;
+    int thresh;               // coefficients of magnitude <= thr count as zero (threshold sparsity)
+    float thr;
     const float* apart;       // attention partials [B][rows / blk][num_splits][blk + 2], or NULL
     int num_splits;
     int B, n_groups;
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 cf[b] = b < a.B ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
+                if (a.thresh) cf[b] = fabsf(cf[b]) > a.thr ? cf[b] : 0.f;
                 any |= cf[b] != 0.f;
             }
             live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
@@ -319,11 +322,14 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 // covers 64 float4 columns of one batch row; its NT/64 waves each add a
 // contiguous share of the groups (all loads of a share in flight together),
 // then the shares are added in order.  One thread also advances a decode
-// position when asked (nothing here reads it).
+// position when asked (nothing here reads it).  The epilogue stores the sum
+// (FIN_STORE), its ReLU (FIN_RELU), or scatters a Q/K/V row (FIN_QKV): q in
+// fp32, K and V into the caches' slot pos in fp16.
 template <typename T, int NT = kBlock>
 __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ partial, int n_groups, int B, int d,
                                                     const void* bias, const float* __restrict__ residual,
-                                                    float* __restrict__ out, int32_t* advance) {
+                                                    float* __restrict__ out, int32_t* advance,
+                                                    const FinEpi& epi = FinEpi{}) {
     constexpr int NW = NT / kWave;
     constexpr int MAXQ = 16;                      // groups per share held in flight
     __shared__ f32x4 red[NW - 1][64];
@@ -363,7 +369,25 @@ __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ pa
         for (int w = 0; w < NW - 1; ++w) s = s + red[w][threadIdx.x];
         if (bias) s += bv;
         if (residual) s += rv;
-        reinterpret_cast<f32x4*>(out + (size_t)b * d)[c4] = s;
+        if (epi.mode == FIN_QKV) {
+            const int c = c4 * 4, hd = epi.h * epi.dh;     // 4 columns of one head (d_h % 4 == 0)
+            const int which = c / hd, head = (c % hd) / epi.dh, e = c % epi.dh;
+            if (which == 0) {
+                *reinterpret_cast<f32x4*>(epi.q + ((size_t)b * epi.h + head) * epi.dh + e) = s;
+            } else {
+                const int pos = epi.pos_dev ? *epi.pos_dev : epi.pos;
+                if (pos >= 0 && pos < epi.max_len) {
+                    half_t* dst = (which == 1 ? epi.k : epi.v) + (((size_t)b * epi.h + head) * epi.max_len + pos) * epi.dh + e;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[i] = (half_t)s[i];
+                }
+            }
+        } else {
+            if (epi.mode == FIN_RELU)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = fmaxf(s[i], 0.f);
+            reinterpret_cast<f32x4*>(out + (size_t)b * d)[c4] = s;
+        }
     }
     if (advance && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *advance += 1;
 }
@@ -371,8 +395,8 @@ __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ pa
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restrict__ partial, int n_groups, int B, int d,
                                                           const void* bias, const float* __restrict__ residual,
-                                                          float* __restrict__ out, int32_t* advance) {
-    axpy_finalize_block<T>(partial, n_groups, B, d, bias, residual, out, advance);
+                                                          float* __restrict__ out, int32_t* advance, FinEpi epi) {
+    axpy_finalize_block<T>(partial, n_groups, B, d, bias, residual, out, advance, epi);
 }
 
 // The finalize by 1024-thread workgroups, with one more workgroup (the last
@@ -434,6 +458,7 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     a.w = c.w; a.d = c.d; a.w_rows = c.w_rows; a.rows = c.rows; a.n_rows_dev = c.n_rows_dev; a.idx = c.idx;
     a.blk = c.blk; a.coef = c.coef; a.coef_stride = c.coef_stride; a.skip_zero = c.skip_zero ? 1 : 0;
     a.apart = c.apart; a.num_splits = c.num_splits;
+    a.thresh = c.thresh ? 1 : 0; a.thr = c.thr;
     a.B = c.B; a.n_groups = p.n_groups; a.partial = c.partial; a.rows_read = c.rows_read;
     a.tk_s = nullptr; a.tk_keys = nullptr; a.tk_n = a.tk_k = 0; a.tk_hist = nullptr; a.tk_thr = nullptr; a.tk_idx = nullptr;
     if (c.sel) {
@@ -468,10 +493,10 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
                                c.d, c.bias, c.residual, c.out, c.advance, f);
     } else if (c.wdt == DV_F16)
         hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
-                           c.residual, c.out, c.advance);
+                           c.residual, c.out, c.advance, c.epi);
     else
         hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
-                           c.residual, c.out, c.advance);
+                           c.residual, c.out, c.advance, c.epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DV_OK;

@@ -33,6 +33,7 @@ DV_KV_SELECT = 0x10
 DV_ADVANCE_POS = 0x20
 DV_LOOKAHEAD = 0x40
 DV_KV_WINDOW = 0x80
+DV_TEAL = 0x100
 DV_KERNEL_QKV, DV_KERNEL_ATTN, DV_KERNEL_OUT, DV_KERNEL_FC1, DV_KERNEL_FC2 = 1, 2, 3, 4, 5
 STATUS = ["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN", "DV_ERR_RANGE",
           "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]
@@ -59,7 +60,8 @@ class DecodeCfg(C.Structure):
 
 class LayerWeights(C.Structure):
     _fields_ = [(n, vp) for n in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "w_qkv_t", "b_qkv", "w_o_t", "b_o",
-                                  "w1_t", "b1", "w2_t", "b2", "pa1_t", "pa2_t", "pm1_t", "pm2_t")]
+                                  "w1_t", "b1", "w2_t", "b2", "pa1_t", "pa2_t", "pm1_t", "pm2_t",
+                                  "w_qkv_in", "w1_in")]
 
 
 class LayerState(C.Structure):
@@ -70,12 +72,14 @@ class LayerState(C.Structure):
                 ("head_idx_in", vp), ("neuron_idx_in", vp),
                 ("next_pa1_t", vp), ("next_pa2_t", vp), ("next_pm1_t", vp), ("next_pm2_t", vp),
                 ("next_head_idx", vp), ("next_neuron_idx", vp),
-                ("aux_stream", vp), ("ev_fork", vp), ("ev_join", vp)]
+                ("aux_stream", vp), ("ev_fork", vp), ("ev_join", vp),
+                # DV_TEAL
+                ("teal_thr", cf * 4), ("teal_rows_out", vp), ("teal_rec", vp)]
 
 
 class StackLayer(C.Structure):
     _fields_ = [("w", LayerWeights), ("kv", KVState), ("sel_idx", vp), ("sel_len", vp), ("sel_cap", ci),
-                ("sel_end", ci)]
+                ("sel_end", ci), ("teal_thr", cf * 4), ("teal_rows_out", vp), ("teal_rec", vp)]
 
 
 class Bytes(C.Structure):

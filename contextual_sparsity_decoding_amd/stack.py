@@ -32,7 +32,7 @@ class Stack:
     """
 
     def __init__(self, dims: LayerDims, layers: int, n_ctx: int, max_len: int, seed: int, batch: int = 1,
-                 hole_fill: bool = True):
+                 hole_fill: bool = True, teal: bool = False):
         self.dims, self.L, self.n_ctx, self.max_len, self.seed, self.B = dims, layers, n_ctx, max_len, seed, batch
         wdt = torch.float16 if dims.wdt == "f16" else torch.float32
         shapes = synth.stack_tensor_shapes(dims)
@@ -50,6 +50,9 @@ class Stack:
                 dv.dv_fill_normal(t, seed, synth.stream_id(l, name), std=synth.WEIGHT_STD)
                 w[name] = t
             w.update(ln1_g=one, ln1_b=zero, ln2_g=one, ln2_b=zero)
+            if teal:   # input-major copies for threshold sparsity (a layout change, no arithmetic)
+                w["w_qkv_in"] = w["w_qkv_t"].reshape(3 * dims.h * dims.d_h, dims.d).t().contiguous()
+                w["w1_in"] = w["w1_t"].t().contiguous()
             self.W.append(w)
             for name, lst in (("K", self.K), ("V", self.V)):
                 t = torch.empty(batch, dims.h, max_len, dims.d_h, dtype=torch.float16, device="cuda")
@@ -62,6 +65,9 @@ class Stack:
         self.pos_dev = torch.full((1,), n_ctx, dtype=torch.int32, device="cuda")
         self.wts = [dv.layer_weights(w) for w in self.W]
         self.sel = [None] * layers          # DV_KV_SELECT: (sel_idx, sel_len, sel_end) per layer
+        self.teal_thr = [(-1.0,) * 4] * layers   # DV_TEAL thresholds per layer (-1: every channel)
+        self.teal_rows = torch.zeros(4, dtype=torch.int32, device="cuda") if teal else None
+        self.teal_rec = None                # DV_TEAL: per-layer records of the projection inputs
         self._arr = None
 
     def set_context(self, n_ctx: int, max_len: int) -> None:
@@ -143,9 +149,45 @@ class Stack:
                     si, sn, se = self.sel[l]
                     sl.sel_idx, sl.sel_len, sl.sel_cap, sl.sel_end = si.data_ptr(), sn.data_ptr(), si.shape[-1], se
                     sl._keep_sel = (si, sn)
+                for i, t in enumerate(self.teal_thr[l]):
+                    sl.teal_thr[i] = t
+                if self.teal_rows is not None:
+                    sl.teal_rows_out = self.teal_rows.data_ptr()
+                if self.teal_rec is not None:
+                    sl.teal_rec = self.teal_rec[l].data_ptr()
                 items.append(sl)
             self._arr = dv.stack_layers(items)
         return self._arr
+
+    def calibrate_teal(self, keep: float, X: torch.Tensor, ws: torch.Tensor, cfg: dv.DecodeCfg) -> None:
+        """Threshold sparsity's thresholds from seeded activations: the stack
+        decodes the tokens X [T][B][d] with every channel kept (cfg carries
+        DV_TEAL; the decode state is reset before and after), recording each
+        layer's four projection inputs; each threshold is the (1 - keep)
+        quantile of that input's magnitudes over the tokens, so that a
+        fraction `keep` of the calibration entries exceeds it."""
+        d = self.dims
+        width = max(d.d, d.h * d.d_h, d.N)
+        T = X.shape[0]
+        rec = [torch.zeros(4, self.B, width, device="cuda") for _ in range(self.L)]
+        mags = [[[] for _ in range(4)] for _ in range(self.L)]
+        widths = (d.d, d.h * d.d_h, d.d, d.N)
+        self.teal_thr = [(-1.0,) * 4] * self.L
+        self.teal_rec, self._arr = rec, None
+        self.reset()
+        x_out = torch.empty(self.B, d.d, device="cuda")
+        x_trace = torch.empty(max(1, self.L - 1), self.B, d.d, device="cuda")
+        for t in range(T):
+            dv.dv_decode_stack(self.layers_array(), cfg, X[t], x_out, ws, x_trace=x_trace)
+            for l in range(self.L):
+                for i in range(4):
+                    mags[l][i].append(rec[l][i, :, :widths[i]].abs().flatten().clone())
+        torch.cuda.synchronize()
+        thr = []
+        for l in range(self.L):
+            thr.append(tuple(float(torch.quantile(torch.cat(mags[l][i]), 1.0 - keep)) for i in range(4)))
+        self.teal_thr, self.teal_rec, self._arr = thr, None, None
+        self.reset()
 
     def cfg(self, k_heads: int, k_neurons: int, flags: int, scale: float, eps: float = 1e-5,
             pred_act: int = dv.DV_ACT_RELU) -> dv.DecodeCfg:

@@ -43,7 +43,7 @@ _TENSOR_IDS = {
     "w1_t": 1, "b1": 2, "w2_t": 3, "b2": 4,
     "w_qkv_t": 5, "b_qkv": 6, "w_o_t": 7, "b_o": 8,
     "pa1_t": 9, "pa2_t": 10, "pm1_t": 11, "pm2_t": 12,
-    "K": 20, "V": 21, "x": 30, "q_obs": 31, "scores": 40,
+    "K": 20, "V": 21, "x": 30, "q_obs": 31, "x_cal": 32, "scores": 40,
 }
 WEIGHT_STD = 0.02
 

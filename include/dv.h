@@ -77,6 +77,7 @@ typedef enum { DV_PROJ_QKV = 0, DV_PROJ_OUT = 1 } dv_proj_mode;
 #define DV_ADVANCE_POS     0x20u /* dv_decode_layer: add 1 to *kv.pos_dev when the step is done */
 #define DV_LOOKAHEAD       0x40u /* dv_decode_layer: DejaVu §4.3 parallel form (see dv_layer_state) */
 #define DV_KV_WINDOW       0x80u /* attend to the KV window of dv_decode_cfg.win_* (ByteCross §5.1) */
+#define DV_TEAL            0x100u /* threshold sparsity on every projection input (ByteCross §4.1), see dv_layer_state */
 
 int dv_api_version(void);
 const char* dv_status_str(int status);
@@ -310,6 +311,12 @@ typedef struct {
     const void *w1_t, *b1, *w2_t, *b2;             /* [N][d], [N], [N][d], [d] */
     const void *pa1_t, *pa2_t;                     /* [r_attn][d], [h][r_attn] */
     const void *pm1_t, *pm2_t;                     /* [r_mlp][d], [N][r_mlp] */
+    /* DV_TEAL only: the projections stored input-major, so that an input
+     * channel's weights are one contiguous row (W^O and W2^T above already
+     * are): w_qkv_in[i][which][head][e] = w_qkv_t[which][head][e][i],
+     * w1_in[i][j] = w1_t[j][i]. */
+    const void *w_qkv_in;                          /* [d][3][h][d_h] */
+    const void *w1_in;                             /* [d][N] */
 } dv_layer_weights;
 
 typedef struct {
@@ -354,6 +361,21 @@ typedef struct {
     void* aux_stream;               /* hipStream_t, or NULL */
     void* ev_fork;                  /* hipEvent_t, required with aux_stream */
     void* ev_join;                  /* hipEvent_t, required with aux_stream */
+    /* DV_TEAL (with DV_DENSE_ATTN and DV_DENSE_MLP; not with DV_LOOKAHEAD or
+     * DV_HOLE_FILL): the projection branch of ByteCross (§4.1, App. A; TEAL
+     * activation sparsity).  Every head and neuron is computed; each
+     * projection reads only the input-major rows of the input channels whose
+     * magnitude exceeds its threshold (for a batch: in some sequence; each
+     * sequence zeroes its own entries at or below the threshold):
+     *   teal_thr = {t_qkv on y = LN1(x), t_o on the heads' attention
+     *   outputs, t_fc1 on y2 = LN2(h), t_fc2 on the ReLU activations}.
+     * teal_rows_out (device int32 [4] or NULL) is incremented by the rows
+     * each of the four projections read.  teal_rec (device fp32
+     * [4][B][max(d, h*d_h, N)] or NULL) receives the four inputs before the
+     * threshold (for calibrating thresholds). */
+    float teal_thr[4];
+    int32_t* teal_rows_out;
+    float* teal_rec;
 } dv_layer_state;
 
 size_t dv_decode_workspace_bytes(const dv_decode_cfg* cfg, int max_len);
@@ -402,6 +424,9 @@ typedef struct {
     const int32_t* sel_len;
     int sel_cap;
     int sel_end;
+    float teal_thr[4];          /* DV_TEAL: as in dv_layer_state */
+    int32_t* teal_rows_out;
+    float* teal_rec;
 } dv_stack_layer;
 
 size_t dv_stack_workspace_bytes(const dv_decode_cfg* cfg, int max_len);

@@ -481,7 +481,7 @@ def teal_mask(x, t: float) -> np.ndarray:
 
 def teal_layer(x, W: dict, kv: KVState, pos: int, *, thr: Sequence[float], scale: float, eps: float = 1e-5,
                sel_idx=None, sel_len=None, sel_end: Optional[int] = None,
-               window: Optional[Tuple[int, int]] = None):
+               window: Optional[Tuple[int, int]] = None, masks: Optional[dict] = None):
     """One decode step of the pre-LN layer with threshold sparsity on the
     input of every projection and every head and neuron computed.
 
@@ -491,26 +491,38 @@ def teal_layer(x, W: dict, kv: KVState, pos: int, *, thr: Sequence[float], scale
     attention reads every position, or the retained set / window as in
     ``attention`` (the composition with the KV branch, ByteCross §4.2).
 
+    ``masks`` (optional, per input name a bool array [B][width]) replaces
+    the threshold's decision for that input: a comparison with a device
+    that rounds the inputs differently follows its decisions where an
+    entry's magnitude lies within rounding of the threshold.
+
     x [B][d].  Returns (x_out [B][d], record with the inputs before the
-    threshold and ``kept``: per projection input, the channels some
-    sequence of the batch keeps, ascending).  Mutates ``kv``.
+    threshold, the decisions taken (``masks``) and ``kept``: per projection
+    input, the channels some sequence of the batch keeps, ascending).
+    Mutates ``kv``.
     """
     x = _f64(np.atleast_2d(x))
+    B = x.shape[0]
     h = W["w_qkv_t"].shape[1]
     heads = np.arange(h)
-    t_qkv, t_o, t_fc1, t_fc2 = (float(t) for t in thr)
+    ts = dict(zip(TEAL_INPUTS, (float(t) for t in thr)))
+    inputs, used = {}, {}
+
+    def cut(name, v):
+        inputs[name] = v.reshape(B, -1)
+        m = np.abs(inputs[name]) > ts[name] if masks is None or name not in masks else np.asarray(masks[name], bool)
+        used[name] = m
+        return np.where(m, inputs[name], 0.0).reshape(v.shape)
+
     y = layernorm(x, W["ln1_g"], W["ln1_b"], eps)
-    q = qkv_step(teal_mask(y, t_qkv), W["w_qkv_t"], W["b_qkv"], heads, kv, pos, hole_fill=False)
+    q = qkv_step(cut("qkv", y), W["w_qkv_t"], W["b_qkv"], heads, kv, pos, hole_fill=False)
     o = attention(q, kv, heads, pos + 1, scale, sel_idx, sel_len, sel_end, window)
-    hres = out_proj(teal_mask(o, t_o), W["w_o_t"], W["b_o"], heads, residual=x)
+    hres = out_proj(cut("o", o), W["w_o_t"], W["b_o"], heads, residual=x)
     y2 = layernorm(hres, W["ln2_g"], W["ln2_b"], eps)
-    a = relu(teal_mask(y2, t_fc1) @ _f64(W["w1_t"]).T + _f64(W["b1"]))
-    out = hres + teal_mask(a, t_fc2) @ _f64(W["w2_t"]) + _f64(W["b2"])
-    B = x.shape[0]
-    inputs = {"qkv": y, "o": o.reshape(B, -1), "fc1": y2, "fc2": a}
-    kept = {k: np.flatnonzero(np.any(np.abs(v) > t, axis=0))
-            for (k, v), t in zip(inputs.items(), (t_qkv, t_o, t_fc1, t_fc2))}
-    return out, dict(inputs=inputs, kept=kept, q=q, h=hres)
+    a = relu(cut("fc1", y2) @ _f64(W["w1_t"]).T + _f64(W["b1"]))
+    out = hres + cut("fc2", a) @ _f64(W["w2_t"]) + _f64(W["b2"])
+    kept = {k: np.flatnonzero(np.any(m, axis=0)) for k, m in used.items()}
+    return out, dict(inputs=inputs, masks=used, kept=kept, q=q, h=hres)
 
 
 def teal_layer_bytes(d: int, h: int, d_h: int, N: int, kept: dict, wb: int = 2) -> float:

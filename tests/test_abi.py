@@ -145,8 +145,19 @@ def test_decode_layer_validation(dv):
     assert L.dv_decode_workspace_bytes(C.byref(cfg), 32) > 0
     cfg.flags = 0x8
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 1  # hole state
-    cfg.flags = 0x100
+    cfg.flags = 0x200
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 3
+    cfg.flags = dv.DV_TEAL                                             # needs every head and neuron
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 7
+    cfg.flags = dv.DV_TEAL | dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP | dv.DV_HOLE_FILL
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 7
+    cfg.flags = dv.DV_TEAL | dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP          # input-major weights missing
+    assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 1
+    assert "w_qkv_in" in err(dv)
+    w2 = dv.LayerWeights(*([P] * 18))
+    st.teal_thr[2] = float("nan")
+    assert L.dv_decode_layer(C.byref(w2), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5
+    st.teal_thr[2] = 0.0
     cfg.flags = 0
     cfg.k_neurons = 300
     assert L.dv_decode_layer(C.byref(w), C.byref(cfg), C.byref(st), P, P + 8192, P, 1 << 30, 0) == 5

@@ -105,3 +105,15 @@ def test_byte_account_with_every_channel_is_the_dense_layer():
     assert ref.teal_layer_bytes(d, DIMS.h, DIMS.d_h, DIMS.N, kept) == want
     half = {k: v[: len(v) // 2] for k, v in kept.items()}
     assert ref.teal_layer_bytes(d, DIMS.h, DIMS.d_h, DIMS.N, half) == (attn + mlp) + 2 * (3 * d + d + DIMS.N + d)
+
+
+def test_given_decisions_equal_to_the_thresholds_change_nothing():
+    W, K, V, x = _setup(6)
+    thr = (0.6, 0.05, 0.7, 0.02)
+    base, rec, _ = _run(W, K, V, x, thr)
+    same, rec2, _ = _run(W, K, V, x, thr, masks=rec["masks"])
+    assert np.array_equal(same, base)
+    flip = {k: v.copy() for k, v in rec["masks"].items()}
+    flip["fc1"][0, int(rec["kept"]["fc1"][0])] = False          # one kept channel dropped by decision
+    moved, rec3, _ = _run(W, K, V, x, thr, masks=flip)
+    assert not np.array_equal(moved, base) and len(rec3["kept"]["fc1"]) == len(rec["kept"]["fc1"]) - 1
