@@ -336,8 +336,9 @@ def main():
 
 def time_stack(torch, dv, stack, X, ws, cfg, warm, timed, head_sets=None, neuron_sets=None, neuron_counts=None):
     """ms per step over `timed` graph-replayed steps after `warm`, from the
-    stack's seeded state; fc2 rows per layer per step; neuron counts read
-    back after the last step (per layer)."""
+    stack's seeded state; fc2 rows per layer per step; and, for a
+    threshold-sparse stack, the channels kept per layer per step by each of
+    its four projection inputs."""
     B, d = stack.B, stack.dims.d
     x_cur = torch.empty(B, d, device="cuda")
     x_out = torch.empty(B, d, device="cuda")
@@ -353,6 +354,8 @@ def time_stack(torch, dv, stack, X, ws, cfg, warm, timed, head_sets=None, neuron
         g.replay()
     torch.cuda.synchronize()
     fc2.zero_()
+    if stack.teal_rows is not None:
+        stack.teal_rows.zero_()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for t in range(warm, warm + timed):
@@ -361,7 +364,10 @@ def time_stack(torch, dv, stack, X, ws, cfg, warm, timed, head_sets=None, neuron
     e1.record()
     torch.cuda.synchronize()
     del g
-    return e0.elapsed_time(e1) / timed, int(fc2.item()) / (timed * stack.L)
+    kept = None
+    if stack.teal_rows is not None:
+        kept = [float(v) / (timed * stack.L) for v in stack.teal_rows.tolist()]
+    return e0.elapsed_time(e1) / timed, int(fc2.item()) / (timed * stack.L), kept
 
 
 def attn_paths(torch, dv, stack, n, b, scale, reps=10):
@@ -435,21 +441,30 @@ def attn_paths(torch, dv, stack, n, b, scale, reps=10):
 
 def bench_longctx(torch, dv, synth, configs, args):
     """ByteCross's composition at long context (§3.3, §4.1-4.4): a 32-layer
-    stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 16K / 32K / 128K cached
-    tokens in five modes through the same kernels and the same split-K
-    attention: dense; projection-only (10% of MLP neurons, predicted one
-    layer ahead); KV-only (10% of cached positions per head chosen by the
-    attention-scored selection, plus the decoded tokens); the KV window
-    (4 sinks plus the most recent positions, the same 10% budget); composed.
+    stack (d = 4096, 32 heads, d_ffn = 16384) at 2K / 8K / 16K / 32K / 128K
+    cached tokens, every mode through the same kernels and the same split-K
+    attention:
+      dense     every head and neuron;
+      proj      DejaVu's MLP sparsity: 10% of neurons, predicted one layer ahead;
+      teal      ByteCross's projection branch: threshold sparsity on the input
+                of every projection at 50% keep (thresholds calibrated per
+                context on 8 seeded tokens, as the pages' TEAL thresholds are
+                calibrated once per model);
+      kv        10% of cached positions per head chosen by the
+                attention-scored selection, plus the decoded tokens;
+      window    the KV window: 4 sinks plus the most recent positions, the
+                same 10% budget;
+      composed  proj + kv;   teal_kv  teal + kv (ByteCross's composition).
     The selection's scoring pass runs once per context after the seeded
     prompt and is timed on its own, outside tokens/s.
 
-    §4.3's cost-aware crossing: a second sweep at 4K / 12K / 24K / 64K gives each
-    branch's cost beyond its byte-scaled dense time; with the dense time of
-    the first sweep interpolated log-log and the costs linearly, the branch
-    latencies are predicted and their crossing set beside the measured one
-    and the crossing of the bytes alone.  §4.4: at every context of the
-    first sweep, one layer's attention on three paths (attn_paths)."""
+    §4.3's cost-aware crossing: a second sweep at 4K / 12K / 24K / 64K gives
+    each branch's cost beyond its byte-scaled dense time; with the dense time
+    of the first sweep interpolated log-log and the costs linearly, the branch
+    latencies are predicted and their crossing with the KV branch set beside
+    the measured one and the crossing of the bytes alone (for proj and teal).
+    §4.4: at every context of the first sweep, one layer's attention on three
+    paths (attn_paths)."""
     from contextual_sparsity_decoding_amd.stack import Stack
     wl = configs.LONGCTX_STACK
     dims, L = wl.dims, wl.layers
@@ -457,16 +472,22 @@ def bench_longctx(torch, dv, synth, configs, args):
     T = W + K
     scale = 1 / math.sqrt(dims.d_h)
     kM = wl.k_neurons
-    stack = Stack(dims, L, 16, 32, SEED + 5, hole_fill=False)
+    teal_keep = 0.5
+    stack = Stack(dims, L, 16, 32, SEED + 5, hole_fill=False, teal=True)
     X = torch.empty(T, 1, dims.d, device="cuda")
     dv.dv_fill_normal(X, SEED + 5, synth.stream_id(0, "x"))
+    Xcal = torch.empty(8, 1, dims.d, device="cuda")
+    dv.dv_fill_normal(Xcal, SEED + 5, synth.stream_id(0, "x_cal"))
     base = dv.DV_DENSE_ATTN | dv.DV_ADVANCE_POS
     ahead = dv.DV_SKIP_NONPOS_FC2 | dv.DV_LOOKAHEAD       # neuron sets predicted one layer ahead (DejaVu 4.3)
+    teal = dv.DV_DENSE_MLP | dv.DV_TEAL
     modes = {"dense": (base | dv.DV_DENSE_MLP, dims.N),
              "proj": (base | ahead, kM),
+             "teal": (base | teal, dims.N),
              "kv": (base | dv.DV_DENSE_MLP | dv.DV_KV_SELECT, dims.N),
              "window": (base | dv.DV_DENSE_MLP | dv.DV_KV_WINDOW, dims.N),
-             "composed": (base | ahead | dv.DV_KV_SELECT, kM)}
+             "composed": (base | ahead | dv.DV_KV_SELECT, kM),
+             "teal_kv": (base | teal | dv.DV_KV_SELECT, dims.N)}
     nsets = torch.zeros(L, kM, dtype=torch.int32, device="cuda")
 
     def mode_cfg(name, b):
@@ -486,8 +507,10 @@ def bench_longctx(torch, dv, synth, configs, args):
             return float(b)
         return n + tail
 
-    def step_bytes_of(name, n, b, rows):
+    def step_bytes_of(name, n, b, rows, kept=None):
         cfg = mode_cfg(name, b)
+        if modes[name][0] & dv.DV_TEAL:
+            return L * dv.dv_bytes_read_teal(cfg, positions(name, n, b), kept).total
         dense_m = bool(modes[name][0] & dv.DV_DENSE_MLP)
         return L * dv.dv_bytes_read(cfg, positions(name, n, b), dims.N if dense_m else rows, 0.0).total
 
@@ -499,7 +522,7 @@ def bench_longctx(torch, dv, synth, configs, args):
             stack.set_context(n, max_len)
             torch.cuda.synchronize()
             row = {"n_ctx": n, "kv_budget": b}
-            if "kv" in names or "composed" in names:
+            if any(modes[m][0] & dv.DV_KV_SELECT for m in names):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 stack.select_kv(b)
@@ -507,16 +530,27 @@ def bench_longctx(torch, dv, synth, configs, args):
                 torch.cuda.synchronize()
                 row["scoring_ms_all_layers"] = round(e0.elapsed_time(e1), 3)
             ws = dv.workspace(max(dv.dv_stack_workspace_bytes(mode_cfg(m, b), max_len) for m in names))
+            if any(modes[m][0] & dv.DV_TEAL for m in names):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                stack.calibrate_teal(teal_keep, Xcal, ws, mode_cfg("teal", b))
+                e1.record()
+                torch.cuda.synchronize()
+                row["teal_calibration_ms"] = round(e0.elapsed_time(e1), 3)
             res = {}
             for name in names:
                 cfg = mode_cfg(name, b)
-                ms, rows = time_stack(torch, dv, stack, X, ws, cfg, W, K,
-                                      neuron_sets=nsets if modes[name][0] & dv.DV_LOOKAHEAD else None)
-                by = step_bytes_of(name, n, b, rows)
+                ms, rows, kept = time_stack(torch, dv, stack, X, ws, cfg, W, K,
+                                            neuron_sets=nsets if modes[name][0] & dv.DV_LOOKAHEAD else None)
+                by = step_bytes_of(name, n, b, rows, kept)
                 res[name] = (ms, by)
                 row[name] = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1000 / ms, 2),
                              "bytes_per_token": int(by), "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
-                if name != "dense":
+                if modes[name][0] & dv.DV_TEAL:
+                    widths = (dims.d, dims.h * dims.d_h, dims.d, dims.N)
+                    row[name]["kept_fraction"] = [round(k / w_, 4) for k, w_ in zip(kept, widths)]
+                    row[name]["kept_channels"] = [round(k, 1) for k in kept]
+                elif name != "dense":
                     row[name]["fc2_rows_per_layer"] = round(rows, 1)
             for name in names:
                 if name != "dense":
@@ -525,46 +559,50 @@ def bench_longctx(torch, dv, synth, configs, args):
                     # ByteCross §4.3: the branch's cost beyond its byte-scaled dense time
                     row[name]["cost_ms"] = round(res[name][0] - res["dense"][0] * res[name][1] / res["dense"][1], 4)
             if paths:
-                row["attention_paths_one_layer"] = attn_paths(torch, dv, stack, n, b, scale)
-                ap = row["attention_paths_one_layer"]
+                ap = attn_paths(torch, dv, stack, n, b, scale)
                 # the step with its split-K attention time replaced by each path's (derived, not timed)
                 derived = {}
                 for path in ("splitk", "fused", "masked"):
                     st = {m: res[m][0] + L * (ap[path][m]["ms"] - ap["splitk"][m]["ms"]) for m in ("dense", "window")}
                     derived[path] = round(st["dense"] / st["window"], 3)
+                row["attention_paths_one_layer"] = {k: v for k, v in ap.items() if isinstance(k, str)}
                 row["window_step_speedup_by_attention_path_derived"] = derived
                 row["window_byte_bound_speedup"] = row["window"]["byte_bound_speedup"]
-                row["attention_paths_one_layer"] = {k: v for k, v in ap.items() if isinstance(k, str)}
             pts.append(row)
             del ws
         return pts
 
     out = sweep(wl.ctx_sweep, list(modes), True)
-    cost_pts = sweep((4096, 12288, 24576, 65536), ["dense", "proj", "kv", "window"], False)
+    cost_pts = sweep((4096, 12288, 24576, 65536), ["dense", "proj", "teal", "kv", "window"], False)
 
-    def cross_of(pts, key):
-        """log-linear crossing of proj and kv in `key` (speedup), or None."""
-        vals = [(r["n_ctx"], r["proj"][key] - r["kv"][key]) for r in pts]
+    def cross_of(pts, key, pb):
+        """log-linear crossing of branch pb and kv in `key` (speedup), or None."""
+        vals = [(r["n_ctx"], r[pb][key] - r["kv"][key]) for r in pts]
         for (n0, a0), (n1, a1) in zip(vals, vals[1:]):
             if a0 >= 0 > a1 or a0 > 0 >= a1:
                 f = a0 / (a0 - a1)
                 return round(math.exp(math.log(n0) + f * (math.log(n1) - math.log(n0))))
         return None
 
-    # the crossing of the bytes alone, from the byte account (fc2 rows of the proj branch at 32K)
-    rows_p = next(r for r in out if r["n_ctx"] == 32768)["proj"]["fc2_rows_per_layer"]
+    at32 = next(r for r in out if r["n_ctx"] == 32768)
+    rows_p = at32["proj"]["fc2_rows_per_layer"]
+    kept_t = at32["teal"]["kept_channels"]
 
-    def byte_gap(n):
+    def bytes_of(m, n):
         b = int(math.floor(wl.kv_keep * n))
-        return step_bytes_of("proj", n, b, rows_p) - step_bytes_of("kv", n, b, 0)
+        return step_bytes_of(m, n, b, rows_p, kept_t)
 
-    lo, hi = 1024.0, 1048576.0
-    bytes_cross = None
-    if byte_gap(lo) < 0 < byte_gap(hi):
+    def bytes_cross(pb):
+        """The context where branch pb and the KV branch read the same bytes
+        (fc2 survivors and kept channels as measured at 32K)."""
+        lo, hi = 1024.0, 1048576.0
+        gap = lambda n: bytes_of(pb, n) - bytes_of("kv", n)
+        if not gap(lo) < 0 < gap(hi):
+            return None
         for _ in range(60):
             mid = math.sqrt(lo * hi)
-            lo, hi = (mid, hi) if byte_gap(mid) < 0 else (lo, mid)
-        bytes_cross = round(lo)
+            lo, hi = (mid, hi) if gap(mid) < 0 else (lo, mid)
+        return round(lo)
 
     # cost-aware prediction: dense time log-log from the first sweep, costs
     # linear in n from the second, byte ratios from the byte account
@@ -576,33 +614,35 @@ def bench_longctx(torch, dv, synth, configs, args):
         (x0, y0), (x1, y1) = xy[i], xy[i + 1]
         return y0 + (y1 - y0) * (x - x0) / (x1 - x0)
 
-    costs = {m: [(r["n_ctx"], r[m]["cost_ms"]) for r in cost_pts] for m in ("proj", "kv", "window")}
+    costs = {m: [(r["n_ctx"], r[m]["cost_ms"]) for r in cost_pts] for m in ("proj", "teal", "kv", "window")}
 
     def predict(m, n):
-        b = int(math.floor(wl.kv_keep * n))
         td = math.exp(interp(dn, math.log(n)))
-        ratio = step_bytes_of(m, n, b, rows_p) / step_bytes_of("dense", n, b, 0)
-        return td * ratio + interp(costs[m], n)
+        return td * bytes_of(m, n) / bytes_of("dense", n) + interp(costs[m], n)
 
-    pred_cross = None
-    grid = [2048 * 2 ** (i / 64) for i in range(64 * 6 + 1)]
-    for n0, n1 in zip(grid, grid[1:]):
-        a0, a1 = predict("proj", n0) - predict("kv", n0), predict("proj", n1) - predict("kv", n1)
-        if a0 <= 0 < a1 or a0 < 0 <= a1:
-            pred_cross = round(n0 + (n1 - n0) * (-a0) / (a1 - a0))
-            break
+    def pred_cross(pb):
+        grid = [2048 * 2 ** (i / 64) for i in range(64 * 6 + 1)]
+        for n0, n1 in zip(grid, grid[1:]):
+            a0, a1 = predict(pb, n0) - predict("kv", n0), predict(pb, n1) - predict("kv", n1)
+            if a0 <= 0 < a1 or a0 < 0 <= a1:
+                return round(n0 + (n1 - n0) * (-a0) / (a1 - a0))
+        return None
+
+    crossings = {pb: {"measured_n": cross_of(out, "speedup", pb), "cost_aware_predicted_n": pred_cross(pb),
+                      "bytes_n": bytes_cross(pb)} for pb in ("proj", "teal")}
     pred_at = [{"n_ctx": r["n_ctx"], **{m: {"predicted_ms": round(predict(m, r["n_ctx"]), 4),
-                                             "measured_ms": r[m]["ms_per_token"]} for m in ("proj", "kv", "window")}}
-               for r in out]
-    del stack, X, nsets
+                                             "measured_ms": r[m]["ms_per_token"]}
+                                        for m in ("proj", "teal", "kv", "window")}} for r in out]
+    del stack, X, Xcal, nsets
     torch.cuda.empty_cache()
-    return {"workload": "longctx-32L-d4096-h32-ffn16384-fp16: 32 layers, batch 1, neuron keep 10% (1638), "
-                        "KV keep 10% per head (attention-scored, 4 sinks + 64-token window forced; or the window "
-                        "of 4 sinks + the most recent positions), heads dense",
-            "points": out, "cost_sweep": cost_pts,
-            "crossover_measured_n": cross_of(out, "speedup"), "crossover_bytes_n": bytes_cross,
-            "crossover_cost_aware_predicted_n": pred_cross, "cost_model_check": pred_at,
-            "warmup": W, "steps": K}
+    return {"workload": "longctx-32L-d4096-h32-ffn16384-fp16: 32 layers, batch 1, heads dense; projection branch "
+                        "10% of MLP neurons (DejaVu) or threshold sparsity at 50% keep on every projection input "
+                        "(ByteCross/TEAL); KV branch 10% of positions per head (attention-scored, 4 sinks + "
+                        "64-token window forced) or the window of 4 sinks + the most recent positions",
+            "points": out, "cost_sweep": cost_pts, "crossings_with_kv": crossings,
+            "crossover_measured_n": crossings["proj"]["measured_n"], "crossover_bytes_n": crossings["proj"]["bytes_n"],
+            "crossover_cost_aware_predicted_n": crossings["proj"]["cost_aware_predicted_n"],
+            "cost_model_check": pred_at, "warmup": W, "steps": K}
 
 
 def bench_batched(torch, dv, synth, configs, args):
@@ -634,9 +674,9 @@ def bench_batched(torch, dv, synth, configs, args):
         nmax = min(dims.N, B * kM)
         nsets = torch.zeros(L, nmax, dtype=torch.int32, device="cuda")
         counts = torch.zeros(L, dtype=torch.int32, device="cuda")
-        ms, rows = time_stack(torch, dv, sub, X, ws, cfg, W, K, neuron_sets=nsets, neuron_counts=counts)
+        ms, rows, _ = time_stack(torch, dv, sub, X, ws, cfg, W, K, neuron_sets=nsets, neuron_counts=counts)
         u = counts.float().mean().item()
-        dms, _ = time_stack(torch, dv, sub, X, ws, dcfg, W, K)
+        dms, _, _ = time_stack(torch, dv, sub, X, ws, dcfg, W, K)
         n_att = wl.n_ctx + W + (K - 1) / 2 + 1
         ucfg = sub.cfg(dims.h, int(round(u)), flags, scale)
         by = L * dv.dv_bytes_read(ucfg, n_att, rows, 0.0).total

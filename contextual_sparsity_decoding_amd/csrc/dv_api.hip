@@ -1028,4 +1028,31 @@ dv_status dv_bytes_read(const dv_decode_cfg* c, double n_att, double fc2_rows, d
     return DV_OK;
 }
 
+dv_status dv_bytes_read_teal(const dv_decode_cfg* c, double n_att, const double* kept, dv_bytes* out) {
+    clear_error();
+    TRY(check_cfg(c));
+    REQ(out && kept, DV_ERR_NULL, "dv_bytes_read_teal: NULL pointer");
+    REQ(c->flags & DV_TEAL, DV_ERR_RANGE, "dv_bytes_read_teal: cfg without DV_TEAL");
+    const double B = c->B, d = c->d, h = c->h, dh = c->d_h, N = c->N, wb = elt_bytes(c->wdt);
+    const double width[4] = {d, h * dh, d, N};
+    for (int i = 0; i < 4; ++i)
+        REQ(kept[i] >= 0 && kept[i] <= width[i], DV_ERR_RANGE, "dv_bytes_read_teal: kept[%d]=%g", i, kept[i]);
+    REQ(n_att >= 0, DV_ERR_RANGE, "dv_bytes_read_teal: n_att");
+    const double a = 4.0 * d * B;
+    dv_bytes r{};
+    r.qkv = (kept[0] * 3.0 * h * dh + 3.0 * h * dh) * wb;
+    r.out_proj = (kept[1] * d + d) * wb;
+    r.fc1 = (kept[2] * N + N) * wb;
+    r.fc2 = (kept[3] * d + d) * wb;
+    r.weights = r.qkv + r.out_proj + r.fc1 + r.fc2;
+    r.kv_read = 2.0 * 2.0 * h * n_att * dh * B;
+    r.kv_write = 2.0 * 2.0 * h * dh * B;
+    // layer input, LayerNorm vectors, the residual stream in and out of each
+    // block, and the four projection inputs read by their gathers
+    r.act = 2.0 * a + 4.0 * 4.0 * d + 4.0 * a + 4.0 * B * (d + h * dh + d + N);
+    r.total = r.weights + r.kv_read + r.kv_write + r.act;
+    *out = r;
+    return DV_OK;
+}
+
 }  // extern "C"

@@ -117,6 +117,7 @@ _sig("dv_stack_workspace_bytes", sz, C.POINTER(DecodeCfg), ci)
 _sig("dv_decode_stack", ci, C.POINTER(StackLayer), ci, C.POINTER(DecodeCfg), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp)
 _sig("dv_fill_normal", ci, vp, C.c_uint64, ci, C.c_uint64, C.c_uint64, C.c_uint64, cf, cf, vp)
 _sig("dv_bytes_read", ci, C.POINTER(DecodeCfg), C.c_double, C.c_double, C.c_double, C.POINTER(Bytes))
+_sig("dv_bytes_read_teal", ci, C.POINTER(DecodeCfg), C.c_double, C.POINTER(C.c_double), C.POINTER(Bytes))
 _sig("dv_time_launches", ci, ci, C.POINTER(vp), ci)
 _sig("dv_launch_events_used", ci)
 
@@ -125,7 +126,7 @@ EXPORTS = ("dv_api_version", "dv_status_str", "dv_last_error", "dv_layernorm", "
            "dv_sparse_mlp", "dv_attn_proj_workspace_bytes", "dv_sparse_attn_proj", "dv_splitk_workspace_bytes",
            "dv_splitk_attn", "dv_kv_score_workspace_bytes", "dv_kv_score", "dv_decode_workspace_bytes",
            "dv_decode_layer", "dv_stack_workspace_bytes", "dv_decode_stack", "dv_fill_normal", "dv_bytes_read",
-           "dv_time_launches", "dv_launch_events_used", "dv_sparse_mlp_noalloc")
+           "dv_bytes_read_teal", "dv_time_launches", "dv_launch_events_used", "dv_sparse_mlp_noalloc")
 
 
 class DVError(RuntimeError):
@@ -327,6 +328,13 @@ def dv_fill_normal(out, seed: int, stream_id: int, offset: int = 0, mean: float 
 def dv_bytes_read(cfg: DecodeCfg, n_att: float, fc2_rows: float, holes: float = 0.0) -> Bytes:
     b = Bytes()
     _check("dv_bytes_read", lib.dv_bytes_read(C.byref(cfg), n_att, fc2_rows, holes, C.byref(b)))
+    return b
+
+
+def dv_bytes_read_teal(cfg: DecodeCfg, n_att: float, kept) -> Bytes:
+    b = Bytes()
+    k = (C.c_double * 4)(*[float(v) for v in kept])
+    _check("dv_bytes_read_teal", lib.dv_bytes_read_teal(C.byref(cfg), n_att, k, C.byref(b)))
     return b
 
 

@@ -475,6 +475,15 @@ typedef struct {
 } dv_bytes;
 dv_status dv_bytes_read(const dv_decode_cfg* cfg, double n_att, double fc2_rows, double holes, dv_bytes* out);
 
+/* The same account for a DV_TEAL step (ByteCross §3.1 with §4.1's
+ * projection branch): each projection reads the input-major rows of its
+ * kept input channels plus its bias; every head attends to n_att
+ * positions.  kept[4] = channels kept per step for the Q/K/V, W^O, fc1 and
+ * fc2 inputs (the device counts of dv_layer_state.teal_rows_out per step),
+ * each within [0, width of that input].  cfg must carry DV_TEAL.  Host
+ * only. */
+dv_status dv_bytes_read_teal(const dv_decode_cfg* cfg, double n_att, const double* kept, dv_bytes* out);
+
 /* ------------------------------------------------------------------------
  * Launch timing, for measuring one kernel role inside the real decode step
  * (effective bandwidth of that kernel on the bytes it must read, ByteCross

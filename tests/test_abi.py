@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -271,6 +272,30 @@ def test_bytes_read_matches_the_oracle_account(dv):
                        wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.125, flags=0)
     with pytest.raises(dv.DVError):
         dv.dv_bytes_read(bad, 10, 10)
+
+
+def test_teal_bytes_match_the_oracle_account(dv):
+    """The threshold-sparse account's weight bytes against the oracle's
+    (ref.teal_layer_bytes); every channel kept is the dense layer's."""
+    from oracle import ref
+    d, h, dh, N = 4096, 32, 128, 16384
+    flags = dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP | dv.DV_TEAL
+    cfg = dv.DecodeCfg(B=1, d=d, h=h, d_h=dh, N=N, r_attn=128, r_mlp=128, k_heads=h, k_neurons=N,
+                       wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.088, flags=flags)
+    for kept in ((2048, 2100, 1990, 8000), (d, h * dh, d, N), (0, 0, 0, 0)):
+        b = dv.dv_bytes_read_teal(cfg, 8193, kept)
+        rows = {k: np.arange(int(v)) for k, v in zip(ref.TEAL_INPUTS, kept)}
+        assert b.weights == pytest.approx(ref.teal_layer_bytes(d, h, dh, N, rows), rel=1e-12)
+    full = dv.dv_bytes_read_teal(cfg, 8193, (d, h * dh, d, N))
+    dense = dv.dv_bytes_read(dv.DecodeCfg(B=1, d=d, h=h, d_h=dh, N=N, r_attn=128, r_mlp=128, k_heads=h, k_neurons=N,
+                                          wdt=dv.DV_F16, pred_act=1, eps=1e-5, scale=0.088,
+                                          flags=dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP), 8193, N)
+    assert full.weights == pytest.approx(dense.weights, rel=1e-12) and full.kv_read == dense.kv_read
+    with pytest.raises(dv.DVError):
+        dv.dv_bytes_read_teal(cfg, 10, (d + 1, 0, 0, 0))
+    cfg.flags = dv.DV_DENSE_ATTN | dv.DV_DENSE_MLP
+    with pytest.raises(dv.DVError):
+        dv.dv_bytes_read_teal(cfg, 10, (1, 1, 1, 1))
 
 
 def test_sparse_mlp_noalloc_validation(dv):
