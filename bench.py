@@ -45,6 +45,14 @@ SEED = 1234
 DECODE_TOKENS = 128
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg: str) -> None:
+    """One line per finished phase on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f}s] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -66,10 +74,15 @@ def parse():
     return p.parse_args()
 
 
+# The sources the dominant kernel (k_qkv at batch 1, fp16) is compiled from:
+# its traffic summary in profiles/ is used only while they are unchanged.
+QKV_SOURCES = ("qkv.h", "pred.h", "rowdot.h", "dv_internal.h", "k_qkv.hip", "k_qkv_f16_b1.hip")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "contextual_sparsity_decoding_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in QKV_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -200,6 +213,7 @@ def main():
     dv.dv_fill_normal(X, SEED, synth.stream_id(0, "x"))
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
+    progress(f"generated the {L}-layer stack in {gen_s:.1f} s")
     resident = sum(t.numel() * t.element_size() for w in stack.W for k, t in w.items() if k[:2] not in ("ln",))
 
     sparse_flags = dv.DV_HOLE_FILL | dv.DV_SKIP_NONPOS_FC2 | dv.DV_ADVANCE_POS
@@ -225,16 +239,19 @@ def main():
             dst_t.copy_(src_t)
         torch.cuda.synchronize()
         del src_t, dst_t
+        progress(f"copied {args.calibrate_copy_mib} MiB three times")
 
     # headline: 10% of neurons, look-ahead schedule
     head_cfg = ahead_cfg(k_of[0.10])
     ms_tok, rows = run.run(head_cfg, W, K)
     hb, tok_bytes = step_bytes(dv, head_cfg, L, n_att, rows)
+    progress(f"headline: {ms_tok:.3f} ms per token")
 
     # dense path of the same library: every head and neuron, every fc2 row
     dense_ms, dense_bytes = float("nan"), float("nan")
     if args.dense:
         dense_ms, _ = run.run(dense_cfg, W, K)
+        progress(f"dense path: {dense_ms:.3f} ms per token")
     _, dense_bytes = step_bytes(dv, dense_cfg, L, n_att, dims.N)
 
     sweep, seq_ms = [], None
@@ -244,6 +261,7 @@ def main():
                 ms, r = ms_tok, rows
             else:
                 ms, r = run.run(ahead_cfg(k_of[keep]), W, K)
+            progress(f"keep {keep:.2f}: {ms:.3f} ms per token")
             _, b = step_bytes(dv, ahead_cfg(k_of[keep]), L, n_att, r)
             sweep.append({"keep_neurons": keep, "k_neurons": k_of[keep], "ms_per_token": round(ms, 4),
                           "tokens_per_s": round(1000.0 / ms, 2),
@@ -254,6 +272,7 @@ def main():
                           "byte_bound_speedup": round(dense_bytes / b, 3),
                           "speedup_over_bound": round((dense_ms / ms) / (dense_bytes / b), 3)})
         seq_ms, _ = run.run(seq_cfg, W, K)
+        progress(f"sequential schedule: {seq_ms:.3f} ms per token")
 
     # the dominant kernel, timed on its own launches inside the headline step.
     # Riders: the next layer's predictor layer one (both predictors) rides in
@@ -272,6 +291,7 @@ def main():
     kernels = {}
     for name, (kind, nbytes) in kinds.items():
         d_ms = run.time_kernel(head_cfg, kind, tokens=2, warm=W)   # from the state the timed tokens start in
+        progress(f"timed the launches of {name.split(' ')[0]}")
         avg = float(np.mean(d_ms)) if d_ms else float("nan")
         kernels[name] = {"avg_launch_ms": round(avg, 5), "launches": len(d_ms), "bytes_per_launch": int(nbytes),
                          "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
@@ -517,6 +537,7 @@ def bench_longctx(torch, dv, synth, configs, args):
     def sweep(ctxs, names, paths):
         pts = []
         for n in ctxs:
+            progress(f"long context: {n} tokens, modes {', '.join(names)}")
             b = int(math.floor(wl.kv_keep * n))
             max_len = n + T + 8
             stack.set_context(n, max_len)
@@ -661,6 +682,7 @@ def bench_batched(torch, dv, synth, configs, args):
     out = []
     stack = None
     for B in wl.batch:
+        progress(f"batched stack: B = {B}")
         if stack is None:
             stack = Stack(dims, L, wl.n_ctx, wl.n_ctx + T + 8, SEED + 7, batch=max(wl.batch), hole_fill=False)
         # one stack holds the largest batch's caches; a smaller batch uses the first B of them
@@ -731,8 +753,11 @@ def cpu_baseline(dims, wl, L, X, cfg, budget_s):
         dt = time.perf_counter() - t0
         return steps, dt
 
+    progress("CPU baseline: layer 0 regenerated on the host")
     s1, t1 = timing(1)
+    progress(f"CPU baseline: {s1} steps with one thread in {t1:.1f} s")
     sa, ta = timing(blas)
+    progress(f"CPU baseline: {sa} steps with {blas} threads in {ta:.1f} s")
     per_layer_all = ta / sa
     return {"value": round(1.0 / (per_layer_all * L), 5), "unit": "tokens/s", "cores": blas, "kind": "oracle",
             "sample": f"{sa} decode steps of layer 0 of the stack (float64 NumPy oracle, look-ahead form, "

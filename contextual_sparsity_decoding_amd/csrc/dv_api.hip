@@ -31,18 +31,34 @@ struct LaunchTiming {
     int kind = 0;
     hipEvent_t* ev = nullptr;
     int n = 0, used = 0;
+    bool armed = false, taken = false;
 };
 static thread_local LaunchTiming g_timing;
 
+// The role's events: the start is recorded on the stream at once; the first
+// launch through DV_LAUNCH inside the role takes both, so that they mark that
+// kernel's own start and end; otherwise the end is recorded after the role.
 void timed_begin(int kind, hipStream_t s) {
-    if (kind != 0 && kind == g_timing.kind && g_timing.used + 2 <= g_timing.n)
+    if (kind != 0 && kind == g_timing.kind && g_timing.used + 2 <= g_timing.n) {
         (void)hipEventRecord(g_timing.ev[g_timing.used], s);
+        g_timing.armed = true;
+        g_timing.taken = false;
+    }
+}
+bool timed_take(hipEvent_t* ev) {
+    if (!g_timing.armed) return false;
+    g_timing.armed = false;
+    g_timing.taken = true;
+    ev[0] = g_timing.ev[g_timing.used];
+    ev[1] = g_timing.ev[g_timing.used + 1];
+    return true;
 }
 void timed_end(int kind, hipStream_t s) {
     if (kind != 0 && kind == g_timing.kind && g_timing.used + 2 <= g_timing.n) {
-        (void)hipEventRecord(g_timing.ev[g_timing.used + 1], s);
+        if (!g_timing.taken) (void)hipEventRecord(g_timing.ev[g_timing.used + 1], s);
         g_timing.used += 2;
     }
+    g_timing.armed = g_timing.taken = false;
 }
 
 int elt_bytes(int wdt) { return wdt == DV_F16 ? 2 : 4; }

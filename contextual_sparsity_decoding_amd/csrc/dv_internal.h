@@ -6,6 +6,7 @@
 // fixed-order (deterministic) reductions.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -215,6 +216,19 @@ void clear_error();
 // role being timed (no-ops otherwise).
 void timed_begin(int kind, hipStream_t s);
 void timed_end(int kind, hipStream_t s);
+bool timed_take(hipEvent_t* ev);   // the role's two events, for its first DV_LAUNCH
+
+// A kernel launch that, inside a timed role, carries the role's events on
+// the dispatch itself (hipExtLaunchKernelGGL): they then mark the kernel's
+// own start and end rather than the points around its launch.
+#define DV_LAUNCH(K, GRID, BLOCK, LDS, S, ...)                                                    \
+    do {                                                                                          \
+        hipEvent_t dv_ev_[2];                                                                     \
+        if (dvh::timed_take(dv_ev_))                                                              \
+            hipExtLaunchKernelGGL(K, GRID, BLOCK, LDS, S, dv_ev_[0], dv_ev_[1], 0, __VA_ARGS__);   \
+        else                                                                                      \
+            hipLaunchKernelGGL(K, GRID, BLOCK, LDS, S, __VA_ARGS__);                              \
+    } while (0)
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 int elt_bytes(int wdt);

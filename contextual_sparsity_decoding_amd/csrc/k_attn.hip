@@ -313,8 +313,8 @@ dv_status launch_splitk(const float* q, int B, int d_h, const int32_t* head_idx,
     const bool pf32 = pred && pred->wdt == DV_F32;
 #define DV_ATT(DH)                                                                                   \
     case DH:                                                                                         \
-        if (pf32) hipLaunchKernelGGL((k_attn_split<DH, float>), dim3(grid), dim3(kBlock), lds, s, a); \
-        else hipLaunchKernelGGL((k_attn_split<DH, half_t>), dim3(grid), dim3(kBlock), lds, s, a);    \
+        if (pf32) DV_LAUNCH((k_attn_split<DH, float>), dim3(grid), dim3(kBlock), lds, s, a);          \
+        else DV_LAUNCH((k_attn_split<DH, half_t>), dim3(grid), dim3(kBlock), lds, s, a);             \
         if (o && rows)                                                                               \
             hipLaunchKernelGGL((k_attn_combine<DH>), dim3(rows), dim3(kBlock), 0, s, part, rows,    \
                                num_splits, o);                                                       \

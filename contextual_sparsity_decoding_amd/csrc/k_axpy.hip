@@ -447,9 +447,9 @@ static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
     const int hs = a.tk_s ? cdiv(a.tk_n, kTopkSlice) : 0;
     const dim3 grid(n_slices + (hs ? 1 : 0), max(a.n_groups, hs));
     if (a.apart)
-        hipLaunchKernelGGL((k_axpy<T, NB, true>), grid, dim3(kBlock), 0, s, a);
+        DV_LAUNCH((k_axpy<T, NB, true>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((k_axpy<T, NB, false>), grid, dim3(kBlock), 0, s, a);
+        DV_LAUNCH((k_axpy<T, NB, false>), grid, dim3(kBlock), 0, s, a);
 }
 
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {

@@ -154,8 +154,8 @@ static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStr
     const size_t lds = (gb ? 3 : 1) * (size_t)a.d * sizeof(float);
 #define DV_RL(CH)                                                                                              \
     case CH:                                                                                                   \
-        if (gb) hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1, true>), dim3(grid), dim3(kBlock), lds, s, a, ln); \
-        else hipLaunchKernelGGL((k_rowdot_ln<T, CH, OP, 1, false>), dim3(grid), dim3(kBlock), lds, s, a, ln); \
+        if (gb) DV_LAUNCH((k_rowdot_ln<T, CH, OP, 1, true>), dim3(grid), dim3(kBlock), lds, s, a, ln);          \
+        else DV_LAUNCH((k_rowdot_ln<T, CH, OP, 1, false>), dim3(grid), dim3(kBlock), lds, s, a, ln);           \
         break;
     switch (ch) {
         DV_RL(4) DV_RL(8) DV_RL(10) DV_RL(12) DV_RL(16) DV_RL(18) DV_RL(24)

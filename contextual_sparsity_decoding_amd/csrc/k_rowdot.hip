@@ -106,19 +106,19 @@ static void rowdot_go(const RowArgs& a, int ch, hipStream_t s) {
     const size_t lds = (size_t)NB * a.d * sizeof(float);
     const bool fits = ch > 0 && lds <= kYLdsMax;
     if (!fits) {
-        hipLaunchKernelGGL((k_rowdot_long<T, NB, OP>), dim3(cdiv(a.n_max, 4)), dim3(kBlock), 0, s, a);
+        DV_LAUNCH((k_rowdot_long<T, NB, OP>), dim3(cdiv(a.n_max, 4)), dim3(kBlock), 0, s, a);
         return;
     }
     const int rpg = rows_per_group(a.n_max);
     const int grid = cdiv(a.n_max, rpg);
     switch (ch) {
-        case 4: hipLaunchKernelGGL((k_rowdot<T, NB, 4, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 8: hipLaunchKernelGGL((k_rowdot<T, NB, 8, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 10: hipLaunchKernelGGL((k_rowdot<T, NB, 10, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 12: hipLaunchKernelGGL((k_rowdot<T, NB, 12, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 16: hipLaunchKernelGGL((k_rowdot<T, NB, 16, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        case 18: hipLaunchKernelGGL((k_rowdot<T, NB, 18, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
-        default: hipLaunchKernelGGL((k_rowdot<T, NB, 24, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 4: DV_LAUNCH((k_rowdot<T, NB, 4, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 8: DV_LAUNCH((k_rowdot<T, NB, 8, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 10: DV_LAUNCH((k_rowdot<T, NB, 10, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 12: DV_LAUNCH((k_rowdot<T, NB, 12, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 16: DV_LAUNCH((k_rowdot<T, NB, 16, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        case 18: DV_LAUNCH((k_rowdot<T, NB, 18, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
+        default: DV_LAUNCH((k_rowdot<T, NB, 24, OP>), dim3(grid), dim3(kBlock), lds, s, a, rpg); break;
     }
 }
 

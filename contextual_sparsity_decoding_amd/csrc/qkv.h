@@ -526,12 +526,12 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     do {                                                                                                             \
         if constexpr (NB == 1) {                                                                                     \
             if (lnf) {                                                                                               \
-                hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, true, SP>), dim3(grid), dim3(kBlock), LDS, s, a);  \
+                DV_LAUNCH((k_qkv<T, NB, CH, R, HB, true, true, SP>), dim3(grid), dim3(kBlock), LDS, s, a);           \
                 break;                                                                                               \
             }                                                                                                        \
         }                                                                                                            \
-        if (yl) hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, true, false, SP>), dim3(grid), dim3(kBlock), LDS, s, a); \
-        else hipLaunchKernelGGL((k_qkv<T, NB, CH, R, HB, false, false, SP>), dim3(grid), dim3(kBlock), LDS - yl, s, a); \
+        if (yl) DV_LAUNCH((k_qkv<T, NB, CH, R, HB, true, false, SP>), dim3(grid), dim3(kBlock), LDS, s, a);          \
+        else DV_LAUNCH((k_qkv<T, NB, CH, R, HB, false, false, SP>), dim3(grid), dim3(kBlock), LDS - yl, s, a);     \
     } while (0)
     if (hb == 2) DV_QKV(2, yl + 2 * row, 1);
     else if (hb == 1) DV_QKV(1, yl + row, 1);

@@ -336,3 +336,30 @@ def test_stack_opt175b_batch16_union_sampled(dvlib):
                                          skip_nonpos=True)
             e = check_close(s["x_out"], want, "f16", f"batched layer {l} token {t}")
             print(f"batch-16 stack layer {l} token {t}: |U| = {len(s['union'])}, normwise {e:.2e}")
+
+
+def test_launch_timing_marks_each_kernel(dvlib):
+    """dv_time_launches: one event pair per launch of the role, each pair
+    inside the token's own span, and the decode's results unchanged by it."""
+    dims = LayerDims(d=1024, N=4096, h=8, d_h=128, r_attn=32, r_mlp=64, wdt="f16")
+    L, n0, kA, kM, seed = 3, 40, 3, 400, 23
+    D = DeviceStack(dvlib, dims, L, n0, n0 + 8, seed, kA, kM)
+    x = torch.empty(1, dims.d, device="cuda")
+    dvlib.dv_fill_normal(x, seed, synth.stream_id(0, "x"))
+    D.S.reset()
+    D.token(x)
+    plain = host(D.x_out)
+    for kind in (dvlib.DV_KERNEL_QKV, dvlib.DV_KERNEL_ATTN, dvlib.DV_KERNEL_OUT, dvlib.DV_KERNEL_FC1,
+                 dvlib.DV_KERNEL_FC2):
+        D.S.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        timer = dvlib.LaunchTimer(kind, L)
+        e0.record()
+        with timer:
+            D.token(x)
+        e1.record()
+        d_ms = timer.durations_ms()
+        span = e0.elapsed_time(e1)
+        assert len(d_ms) == L, (kind, len(d_ms))
+        assert all(0 < t < span for t in d_ms), (kind, d_ms, span)
+        assert np.array_equal(host(D.x_out), plain), kind
