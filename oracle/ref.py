@@ -534,6 +534,56 @@ def teal_layer_bytes(d: int, h: int, d_h: int, N: int, kept: dict, wb: int = 2) 
     return wb * (rows + 3 * h * d_h + d + N + d)
 
 
+# --------------------------------------------------------- 4-bit weights --
+
+W4_GROUP = 128
+
+
+def quantize_w4(w) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-wise symmetric int4 of a [rows][cols] matrix (cols a multiple of
+    128), the W4A16 weights DejaVu §5 combines with contextual sparsity
+    (Compatibility with Quantization, Table 7; the pages give no quantizer,
+    this one is a reading): per row, per group of 128 consecutive entries,
+    the scale s = fp16(max|w| / 7) (the division in fp32) and the codes
+    v = clamp(rint(w / s), -8, 7) (w / s in fp32, rint to nearest even; a
+    group of zeros has s = 0 and v = 0).  Integer decisions are taken in
+    fp32, the precision the device takes them in.
+    Returns (v int8 [rows][cols], s fp16 [rows][cols / 128])."""
+    w32 = np.asarray(w, dtype=np.float16).astype(np.float32)
+    rows, cols = w32.shape
+    g = w32.reshape(rows, cols // W4_GROUP, W4_GROUP)
+    m = np.abs(g).max(axis=2)
+    s16 = (m / np.float32(7.0)).astype(np.float16)
+    s32 = s16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s32 > 0, np.clip(np.rint(g / s32), -8, 7), 0.0)
+    return v.reshape(rows, cols).astype(np.int8), s16
+
+
+def pack_w4(v) -> np.ndarray:
+    """The stored codes: entry c of a row in byte c // 2, the low nibble for
+    even c, each nibble holding v + 8."""
+    u = (np.asarray(v, dtype=np.int16) + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def dequantize_w4(v, s) -> np.ndarray:
+    """The weights the codes stand for, v * s, in float64."""
+    v = np.asarray(v, dtype=np.float64)
+    rows, cols = v.shape
+    return (v.reshape(rows, cols // W4_GROUP, W4_GROUP) * _f64(s)[:, :, None]).reshape(rows, cols)
+
+
+def sparse_mlp_w4(y, v1, s1, b1, v2, s2, b2, idx, residual=None, skip_nonpos: bool = False):
+    """DejaVu Eq. (1) over the selected neurons with 4-bit weights: the
+    sparse MLP of ``sparse_mlp`` on the dequantized rows of W1^T and W2^T
+    (biases stay fp16).  v1, v2 int8 [N][d] codes; s1, s2 fp16 [N][d/128]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    W1 = dequantize_w4(np.asarray(v1)[idx], np.asarray(s1)[idx])
+    W2 = dequantize_w4(np.asarray(v2)[idx], np.asarray(s2)[idx])
+    return sparse_mlp(y, W1, _f64(b1)[idx], W2, b2, np.arange(len(idx)), residual, skip_nonpos)
+
+
 # ---------------------------------------------------------------- the stack --
 
 def predict_sets(x, W: dict, k_heads: int, k_neurons: int, eps: float = 1e-5, pred_act: str = "relu"):
