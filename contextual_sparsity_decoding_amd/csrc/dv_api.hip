@@ -11,6 +11,7 @@
 
 #include "pred.h"
 #include "topk_split.h"
+#include "w4.h"
 
 namespace dvh {
 
@@ -342,6 +343,62 @@ dv_status dv_splitk_attn(const float* q, int B, int d_h, const int32_t* head_idx
     REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_splitk_attn: workspace %zu < %zu", ws_bytes, need);
     return launch_splitk(q, B, d_h, head_idx, n_sel, kv, kv->n_ctx_dev, 0, scale, num_splits, o,
                          (float*)((char*)ws + kCounterBytes), nullptr, 0, nullptr, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- 4-bit weights --
+dv_status dv_quantize_w4(const void* w, int rows, int cols, uint8_t* q, void* scales, void* stream) {
+    clear_error();
+    REQ(w && q && scales, DV_ERR_NULL, "dv_quantize_w4: NULL pointer");
+    REQ(rows >= 1 && cols >= 128 && cols % 128 == 0, DV_ERR_SHAPE, "dv_quantize_w4: rows=%d cols=%d", rows, cols);
+    REQ(a16(w) && a16(q), DV_ERR_ALIGN, "dv_quantize_w4: pointers must be 16-byte aligned");
+    return launch_quant_w4(w, rows, cols, q, scales, (hipStream_t)stream);
+}
+
+static size_t w4_ws(int d, int n_idx_max, float** a, float** partial, void* ws) {
+    Carve cv(ws);
+    *a = cv.take<float>((size_t)(n_idx_max > 0 ? n_idx_max : 1));
+    *partial = cv.take<float>((size_t)w4_axpy_groups(n_idx_max) * d);
+    return align_up(cv.off, 256);
+}
+
+size_t dv_sparse_mlp_w4_workspace_bytes(int d, int n_idx_max) {
+    if (d < 128 || d % 128 || n_idx_max < 0) return 0;
+    float *a, *p;
+    return w4_ws(d, n_idx_max, &a, &p, nullptr);
+}
+
+dv_status dv_sparse_mlp_w4(const float* y, int d, int N, const uint8_t* q1, const void* s1, const void* b1,
+                           const uint8_t* q2, const void* s2, const void* b2, const int32_t* idx, int n_idx_max,
+                           const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
+                           int32_t* fc2_rows, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    REQ(y && q1 && s1 && b1 && q2 && s2 && b2 && out, DV_ERR_NULL, "dv_sparse_mlp_w4: NULL pointer");
+    REQ(d >= 128 && d % 128 == 0 && d <= 16384 && N >= 1, DV_ERR_SHAPE, "dv_sparse_mlp_w4: d=%d N=%d", d, N);
+    REQ(n_idx_max >= 0 && n_idx_max <= N, DV_ERR_RANGE, "dv_sparse_mlp_w4: n_idx_max=%d N=%d", n_idx_max, N);
+    REQ(idx || n_idx_max == N, DV_ERR_SHAPE, "dv_sparse_mlp_w4: idx NULL needs n_idx_max == N");
+    REQ((flags & ~(unsigned)DV_SKIP_NONPOS_FC2) == 0, DV_ERR_DTYPE, "dv_sparse_mlp_w4: flags 0x%x", flags);
+    REQ(a16(y) && a16(q1) && a16(q2), DV_ERR_ALIGN, "dv_sparse_mlp_w4: pointers must be 16-byte aligned");
+    const size_t act = (size_t)d * 4;
+    REQ(!overlap(out, act, y, act) && !overlap(out, act, residual, act), DV_ERR_RANGE,
+        "dv_sparse_mlp_w4: out overlaps y or residual");
+    float *wa, *part;
+    const size_t need = w4_ws(d, n_idx_max, &wa, &part, ws);
+    REQ(ws && ws_bytes >= need, DV_ERR_WORKSPACE, "dv_sparse_mlp_w4: workspace %zu < %zu", ws_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    float* a = act_out ? act_out : wa;
+    W4RowArgs r{};
+    r.y = y; r.d = d; r.q = q1; r.s = (const half_t*)s1; r.bias = (const half_t*)b1; r.idx = idx; r.n_max = n_idx_max;
+    r.n_dev = n_idx_dev; r.w_rows = N; r.out = a;
+    timed_begin(DV_KERNEL_FC1, s);
+    TRY(launch_rowdot_w4(r, s));
+    timed_end(DV_KERNEL_FC1, s);
+    W4AxpyArgs x{};
+    x.q = q2; x.s = (const half_t*)s2; x.d = d; x.w_rows = N; x.rows = n_idx_max; x.n_rows_dev = n_idx_dev; x.idx = idx;
+    x.coef = a; x.skip_zero = (flags & DV_SKIP_NONPOS_FC2) != 0; x.partial = part; x.rows_read = fc2_rows;
+    timed_begin(DV_KERNEL_FC2, s);
+    TRY(launch_axpy_w4(x, s));
+    timed_end(DV_KERNEL_FC2, s);
+    return launch_axpy_finalize(part, w4_axpy_groups(n_idx_max), 1, d, b2, DV_F16, residual, out, s);
 }
 
 // ---------------------------------------------------------------- KV scoring --

@@ -452,6 +452,19 @@ static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
         DV_LAUNCH((k_axpy<T, NB, false>), grid, dim3(kBlock), 0, s, a);
 }
 
+dv_status launch_axpy_finalize(const float* partial, int n_groups, int B, int d, const void* bias, int bias_wdt,
+                               const float* residual, float* out, hipStream_t s) {
+    const dim3 fg(cdiv(d / 4, 64), B);
+    if (bias_wdt == DV_F16)
+        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, partial, n_groups, B, d, bias, residual,
+                           out, nullptr, FinEpi{});
+    else
+        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, partial, n_groups, B, d, bias, residual,
+                           out, nullptr, FinEpi{});
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     const AxpyPlan p = axpy_plan(c.d, c.rows, c.wdt);
     AxpyArgs a;

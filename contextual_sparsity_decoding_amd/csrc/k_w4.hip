@@ -1,0 +1,266 @@
+// 4-bit weights (W4A16) in the sparse MLP: the group-wise int4 quantizer,
+// fc1 over selected rows and the fc2 gather-AXPY, dequantizing inside the
+// gather.  DejaVu §5 (Compatibility with Quantization, Table 7) combines
+// 4-bit weights with contextual sparsity; the pages do not give the
+// quantizer, so the format is defined in include/dv.h (dv_quantize_w4):
+// per row, groups of 128 entries, an fp16 scale s per group and codes
+// v in [-8, 7] stored as nibbles v + 8, entry c of a row in byte c / 2
+// (low nibble for even c).
+//
+// Pages: DejaVu = "Deja Vu: Contextual Sparsity for Efficient LLMs at
+// Inference Time" (arXiv 2310.17157).
+#include "rowdot.h"
+#include "w4.h"
+
+namespace dv {
+
+constexpr int kW4Group = 128;
+constexpr int kW4Chunk = 32;            // codes in one 16-byte chunk
+
+// Codes k*4 .. k*4+3 of a 16-byte chunk (sub-vector k of 8) as floats v.
+__device__ __forceinline__ void w4_sub(const u32x4& q, int k, float (&f)[4]) {
+    const unsigned dw = k < 4 ? (k < 2 ? q[0] : q[1]) : (k < 6 ? q[2] : q[3]);
+    const unsigned h = (k & 1) ? dw >> 16 : dw;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f[t] = (float)((int)((h >> (4 * t)) & 15u) - 8);
+}
+
+// One thread per group of 128: the largest magnitude, the scale, then the
+// codes (the group is read twice; the second read comes from the cache).
+__global__ __launch_bounds__(kBlock) void k_quant_w4(const half_t* __restrict__ w, int rows, int cols,
+                                                     uint8_t* __restrict__ q, half_t* __restrict__ s) {
+    const int gpr = cols / kW4Group;
+    const long g = (long)blockIdx.x * kBlock + threadIdx.x;
+    if (g >= (long)rows * gpr) return;
+    const long r = g / gpr;
+    const int gi = (int)(g % gpr);
+    const half_t* src = w + r * cols + (size_t)gi * kW4Group;
+    float m = 0.f;
+    for (int i = 0; i < kW4Group / 8; ++i) {
+        float f[8];
+        unpack(ld16(src + 8 * i), f, half_t());
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+    }
+    const half_t s16 = (half_t)__fdiv_rn(m, 7.f);
+    const float sf = (float)s16;
+    uint8_t* dst = q + r * (cols / 2) + (size_t)gi * (kW4Group / 2);
+    for (int i = 0; i < kW4Group / 32; ++i) {          // 32 codes -> 16 bytes
+        u32x4 out;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            float f[8];
+            unpack(ld16(src + 32 * i + 8 * wd), f, half_t());
+            unsigned word = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = sf > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(f[e], sf)), -8.f), 7.f) : 0.f;
+                word |= (unsigned)((int)v + 8) << (4 * e);
+            }
+            out[wd] = word;
+        }
+        *reinterpret_cast<u32x4*>(dst + 16 * i) = out;
+    }
+    s[r * gpr + gi] = s16;
+}
+
+// fc1 over the selected rows, batch of one: a[u] = max(0, y . w'[idx[u]] + b1).
+// Each wave takes R rows; lane l holds chunks l, l+64, ... (32 codes each,
+// one scale: 32 divides 128).  y is staged in LDS; a lane reads the 8
+// float4 of its chunk's inputs starting at sub-vector (l & 7), so that the 8
+// lanes of a group address 8 different 16-byte slots (no bank conflicts).
+// A chunk's sum over its 32 codes is taken first, then scaled.
+template <int CH, int R>
+__global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
+    extern __shared__ float ys[];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
+    const int u0 = (blockIdx.x * 4 + wv) * R;
+    stage_dma(ys, a.y, a.d);
+    const int nchunk = a.d / kW4Chunk, rb = a.d / 2, sb = a.d / kW4Group;
+    int j[R];
+    u32x4 w[R][CH];
+    float sc[R][CH];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int u = u0 + r;
+        int jj = -1;
+        if (u < n) {
+            jj = a.idx ? a.idx[u] : u;
+            jj = (unsigned)jj < (unsigned)a.w_rows ? jj : -1;
+        }
+        j[r] = __builtin_amdgcn_readfirstlane(jj);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = lane + i * kWave;
+            const bool ok = j[r] >= 0 && c < nchunk;
+            w[r][i] = ok ? ld16_stream(a.q + (size_t)j[r] * rb + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+            sc[r][i] = ok ? (float)a.s[(size_t)j[r] * sb + c / 4] : 0.f;
+        }
+    }
+    wait_dma_and_sync();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int u = u0 + r;
+        if (u >= n) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+                float p = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int k = (kk + lane) & 7;
+                    float f[4];
+                    w4_sub(w[r][i], k, f);
+                    const f32x4 y4 = reinterpret_cast<const f32x4*>(ys + (size_t)c * kW4Chunk)[k];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) p = fmaf(f[t], y4[t], p);
+                }
+                acc = fmaf(p, sc[r][i], acc);
+            }
+        }
+        float v = wave_sum(acc);
+        const float bj = j[r] >= 0 ? (float)a.bias[j[r]] : 0.f;
+        v = j[r] >= 0 ? fmaxf(v + bj, 0.f) : 0.f;
+        if (lane == 0) a.out[u] = v;
+    }
+}
+
+// fc2 gather-AXPY, batch of one: partial[g] = sum over the live rows of
+// group g (64 selected rows) of a[u] * w'[idx[u]] restricted to one slice
+// of 2048 columns (lane l: columns [32 l, 32 l + 32) of the slice, one
+// scale).  Rows whose coefficient is zero are skipped when asked (the
+// ReLU-sparsified second layer); the 4 waves' sums are added in order in
+// LDS and written as the group's partial, which k_axpy_finalize adds up.
+constexpr int kW4Rows = 64;
+__global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
+    __shared__ int s_row[kW4Rows];
+    __shared__ float s_cf[kW4Rows];
+    __shared__ unsigned s_n;
+    __shared__ float red[3][kWave * kW4Chunk];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slice = blockIdx.x, g = blockIdx.y;
+    const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
+    const int r0 = g * kW4Rows;
+    const int c = slice * kWave + lane;                // this lane's chunk of the row
+    const int nchunk = a.d / kW4Chunk, rb = a.d / 2, sb = a.d / kW4Group;
+    const bool colok = c < nchunk;
+    if (threadIdx.x < kWave) {
+        bool live = false;
+        int row = 0;
+        float cf = 0.f;
+        const int u = r0 + threadIdx.x;
+        if (u < rows) {
+            row = a.idx ? a.idx[u] : u;
+            cf = a.coef[u];
+            live = (unsigned)row < (unsigned)a.w_rows && (cf != 0.f || !a.skip_zero);
+        }
+        const unsigned lv = live ? 1u : 0u;
+        const unsigned incl = wave_incl_scan(lv);
+        if (live) {
+            s_row[incl - 1] = row;
+            s_cf[incl - 1] = cf;
+        }
+        if (threadIdx.x == 63) {
+            s_n = incl;
+            if (a.rows_read && slice == 0 && incl > 0) atomicAdd(a.rows_read, (int)incl);
+        }
+    }
+    __syncthreads();
+    const int nlive = (int)s_n;
+    constexpr int U = kW4Rows / 4;                     // rows per wave
+    u32x4 w[U];
+    float sc[U];
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+        const int k = wv + 4 * t;
+        const bool ok = k < nlive && colok;
+        const int rr = k < nlive ? s_row[k] : 0;
+        w[t] = ok ? ld16_stream(a.q + (size_t)rr * rb + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+        sc[t] = ok ? (float)a.s[(size_t)rr * sb + c / 4] : 0.f;
+    }
+    float acc[kW4Chunk];
+#pragma unroll
+    for (int e = 0; e < kW4Chunk; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+        const int k = wv + 4 * t;
+        if (k < nlive) {
+            const float cs = s_cf[k] * sc[t];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                float f[4];
+                w4_sub(w[t], kk, f);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) acc[4 * kk + tt] = fmaf(cs, f[tt], acc[4 * kk + tt]);
+            }
+        }
+    }
+    // waves 1..3 hand their sums to wave 0, which adds them in order; lane l's
+    // 32 columns sit at red[.][32 l ...], read back 16 bytes at a time from a
+    // rotated start so that 8 neighbouring lanes hit different banks
+    if (wv > 0) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = (kk + lane) & 7;
+            reinterpret_cast<f32x4*>(&red[wv - 1][lane * kW4Chunk])[k] =
+                f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
+        }
+    }
+    __syncthreads();
+    if (wv == 0 && colok) {
+        float* dst = a.partial + (size_t)g * a.d + (size_t)c * kW4Chunk;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = (kk + lane) & 7;
+            f32x4 o = f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
+#pragma unroll
+            for (int q = 0; q < 3; ++q) o += reinterpret_cast<const f32x4*>(&red[q][lane * kW4Chunk])[k];
+            reinterpret_cast<f32x4*>(dst)[k] = o;
+        }
+    }
+}
+
+}  // namespace dv
+
+namespace dvh {
+using namespace dv;
+
+dv_status launch_quant_w4(const void* w, int rows, int cols, uint8_t* q, void* s, hipStream_t st) {
+    const long groups = (long)rows * (cols / kW4Group);
+    if (groups == 0) return DV_OK;
+    hipLaunchKernelGGL(k_quant_w4, dim3((unsigned)((groups + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                       (const half_t*)w, rows, cols, q, (half_t*)s);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+int w4_chunks_per_lane(int d) { return cdiv(d / kW4Chunk, kWave); }
+
+dv_status launch_rowdot_w4(const W4RowArgs& a, hipStream_t s) {
+    constexpr int R = 2;
+    const int grid = cdiv(a.n_max < 1 ? 1 : a.n_max, 4 * R);
+    const size_t lds = (size_t)a.d * sizeof(float);
+    switch (w4_chunks_per_lane(a.d)) {
+#define DV_W4R(CH) case CH: DV_LAUNCH((k_rowdot_w4<CH, R>), dim3(grid), dim3(kBlock), lds, s, a); break;
+        DV_W4R(1) DV_W4R(2) DV_W4R(3) DV_W4R(4) DV_W4R(5) DV_W4R(6) DV_W4R(7) DV_W4R(8)
+#undef DV_W4R
+        default: return fail(DV_ERR_UNSUPPORTED, "4-bit fc1: d=%d", a.d);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+int w4_axpy_groups(int rows) { return cdiv(rows < 1 ? 1 : rows, kW4Rows); }
+
+dv_status launch_axpy_w4(const W4AxpyArgs& a, hipStream_t s) {
+    const dim3 grid(cdiv(a.d / kW4Chunk, kWave), w4_axpy_groups(a.rows));
+    DV_LAUNCH(k_axpy_w4, grid, dim3(kBlock), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+}  // namespace dvh

@@ -118,6 +118,9 @@ _sig("dv_decode_stack", ci, C.POINTER(StackLayer), ci, C.POINTER(DecodeCfg), vp,
 _sig("dv_fill_normal", ci, vp, C.c_uint64, ci, C.c_uint64, C.c_uint64, C.c_uint64, cf, cf, vp)
 _sig("dv_bytes_read", ci, C.POINTER(DecodeCfg), C.c_double, C.c_double, C.c_double, C.POINTER(Bytes))
 _sig("dv_bytes_read_teal", ci, C.POINTER(DecodeCfg), C.c_double, C.POINTER(C.c_double), C.POINTER(Bytes))
+_sig("dv_quantize_w4", ci, vp, ci, ci, vp, vp, vp)
+_sig("dv_sparse_mlp_w4_workspace_bytes", sz, ci, ci)
+_sig("dv_sparse_mlp_w4", ci, vp, ci, ci, vp, vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, vp, cu, vp, sz, vp)
 _sig("dv_time_launches", ci, ci, C.POINTER(vp), ci)
 _sig("dv_launch_events_used", ci)
 
@@ -126,7 +129,8 @@ EXPORTS = ("dv_api_version", "dv_status_str", "dv_last_error", "dv_layernorm", "
            "dv_sparse_mlp", "dv_attn_proj_workspace_bytes", "dv_sparse_attn_proj", "dv_splitk_workspace_bytes",
            "dv_splitk_attn", "dv_kv_score_workspace_bytes", "dv_kv_score", "dv_decode_workspace_bytes",
            "dv_decode_layer", "dv_stack_workspace_bytes", "dv_decode_stack", "dv_fill_normal", "dv_bytes_read",
-           "dv_bytes_read_teal", "dv_time_launches", "dv_launch_events_used", "dv_sparse_mlp_noalloc")
+           "dv_bytes_read_teal", "dv_quantize_w4", "dv_sparse_mlp_w4_workspace_bytes",
+           "dv_sparse_mlp_w4", "dv_time_launches", "dv_launch_events_used", "dv_sparse_mlp_noalloc")
 
 
 class DVError(RuntimeError):
@@ -336,6 +340,22 @@ def dv_bytes_read_teal(cfg: DecodeCfg, n_att: float, kept) -> Bytes:
     k = (C.c_double * 4)(*[float(v) for v in kept])
     _check("dv_bytes_read_teal", lib.dv_bytes_read_teal(C.byref(cfg), n_att, k, C.byref(b)))
     return b
+
+
+def dv_quantize_w4(w, q, scales, stream=None):
+    """w fp16 [rows][cols] -> q uint8 [rows][cols / 2], scales fp16 [rows][cols / 128]."""
+    rows, cols = w.shape
+    _check("dv_quantize_w4", lib.dv_quantize_w4(ptr(w), rows, cols, ptr(q), ptr(scales), stream_handle(stream)))
+
+
+def dv_sparse_mlp_w4(y, N, q1, s1, b1, q2, s2, b2, idx, out, ws, *, n_idx_max=None, n_idx_dev=None, residual=None,
+                     act_out=None, fc2_rows=None, flags=0, stream=None):
+    d = y.shape[-1]
+    n = n_idx_max if n_idx_max is not None else (idx.numel() if idx is not None else N)
+    _check("dv_sparse_mlp_w4", lib.dv_sparse_mlp_w4(ptr(y), d, N, ptr(q1), ptr(s1), ptr(b1), ptr(q2), ptr(s2), ptr(b2),
+                                                    ptr(idx), n, ptr(n_idx_dev), ptr(residual), ptr(out),
+                                                    ptr(act_out), ptr(fc2_rows), flags, ptr(ws), ws.numel(),
+                                                    stream_handle(stream)))
 
 
 class LaunchTimer:

@@ -171,6 +171,35 @@ dv_status dv_sparse_mlp_noalloc(const float* y, int B, int d, int N, const void*
                                 int32_t* fc2_rows, unsigned flags, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 4-bit weights (W4A16).  DejaVu §5 (Compatibility with Quantization,
+ * Table 7) applies 4-bit weight quantization together with contextual
+ * sparsity without naming the quantizer; this format is the library's:
+ * a matrix w [rows][cols] (fp16, cols a multiple of 128) is stored as
+ *   q       uint8 [rows][cols / 2]: entry c of a row in byte c / 2, the low
+ *           nibble for even c; a nibble holds v + 8, v in [-8, 7]
+ *   scales  fp16 [rows][cols / 128]: per row and group of 128 entries,
+ *           s = fp16(max |w| / 7) (fp32 division, round to nearest even)
+ * and stands for w' = v * s, with v = clamp(rint(w / s), -8, 7) (w / s in
+ * fp32, correctly rounded; rint to nearest even) and v = 0 where s = 0.
+ * w must be finite.  dv_quantize_w4 writes q and scales from w (device
+ * pointers, 16-byte aligned; rows >= 1; DV_ERR_SHAPE for cols not a
+ * multiple of 128).
+ */
+dv_status dv_quantize_w4(const void* w, int rows, int cols, uint8_t* q, void* scales, void* stream);
+
+/* dv_sparse_mlp (DejaVu §2.3 Eq. 1, the same a and out) with fc1 and fc2
+ * weights in the 4-bit format above, dequantized inside the gathers:
+ *   q1, s1   W1^T [N][d] as codes and scales; q2, s2 W2^T [N][d] likewise
+ *   b1 fp16 [N], b2 fp16 [d]
+ * Batch of one (B = 1); d a multiple of 128 and at most 16384; other
+ * arguments as in dv_sparse_mlp (flags: DV_SKIP_NONPOS_FC2). */
+size_t dv_sparse_mlp_w4_workspace_bytes(int d, int n_idx_max);
+dv_status dv_sparse_mlp_w4(const float* y, int d, int N, const uint8_t* q1, const void* s1, const void* b1,
+                           const uint8_t* q2, const void* s2, const void* b2, const int32_t* idx, int n_idx_max,
+                           const int32_t* n_idx_dev, const float* residual, float* out, float* act_out,
+                           int32_t* fc2_rows, unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * KV state of one layer, updated by dv_sparse_attn_proj(DV_PROJ_QKV).
  *   k_cache, v_cache  device fp16 [B][h][max_len][d_h]
  *   pos               slot written by this step, 0 <= pos < max_len
