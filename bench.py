@@ -65,6 +65,8 @@ def parse():
                    help="0 skips the long-context composition stack (32 layers, d=4096, 2K-128K context)")
     p.add_argument("--batched", type=int, default=1,
                    help="0 skips the batched OPT-175B-share stack (48 layers, d=12288, batch 1-16)")
+    p.add_argument("--w4", type=int, default=1,
+                   help="0 skips the 4-bit-weight sparse MLP (OPT-66B width, fp16 against 4-bit weights)")
     p.add_argument("--extra-steps", type=int, default=12, help="timed tokens per point of the two extra stacks")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time per oracle timing (two timings)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -349,6 +351,8 @@ def main():
         result["longctx_composition"] = bench_longctx(torch, dv, synth, configs, args)
     if args.batched:
         result["batched_union"] = bench_batched(torch, dv, synth, configs, args)
+    if args.w4:
+        result["w4_sparse_mlp"] = bench_w4(torch, dv, synth, configs, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dims, wl, L, Xh, head_cfg, args.cpu_seconds)
     print(json.dumps(result))
@@ -715,6 +719,86 @@ def bench_batched(torch, dv, synth, configs, args):
     return {"workload": "opt175b-48L-d12288-h96-ffn49152-fp16: 48 layers (one GPU's share), heads dense, 512 cached "
                         "tokens per sequence, neuron keep 10% (4915) per sequence, union per layer",
             "points": out, "warmup": W, "steps": K}
+
+
+def bench_w4(torch, dv, synth, configs, args):
+    """DejaVu §5 (Compatibility with Quantization): the sparse MLP block at
+    the OPT-66B width (d = 9216, d_ffn = 36864, batch 1, fc2 rows of zero
+    activations skipped) at 10% and 100% of neurons, with fp16 weights and
+    with the library's 4-bit weights (dv_quantize_w4), each over 8 layers'
+    weights in turn (so that no call finds its rows in the 256 MB
+    last-level cache), one HIP graph of the 8 calls replayed."""
+    wl = configs.OPT66B_STACK
+    d, N = wl.dims.d, wl.dims.N
+    L, reps = 8, max(2, args.extra_steps)
+    g = torch.Generator(device="cpu").manual_seed(SEED)
+    y = torch.empty(L, 1, d, device="cuda")
+    dv.dv_fill_normal(y, SEED + 11, synth.stream_id(0, "x"))
+    layers = []
+    for l in range(L):
+        w = {}
+        for name, shp in (("w1_t", (N, d)), ("b1", (N,)), ("w2_t", (N, d)), ("b2", (d,))):
+            t = torch.empty(shp, dtype=torch.float16, device="cuda")
+            dv.dv_fill_normal(t, SEED + 11, synth.stream_id(l, name), std=synth.WEIGHT_STD)
+            w[name] = t
+        for name in ("w1_t", "w2_t"):
+            q = torch.empty(N, d // 2, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(N, d // 128, dtype=torch.float16, device="cuda")
+            dv.dv_quantize_w4(w[name], q, sc)
+            w[name + "_q"], w[name + "_s"] = q, sc
+        layers.append(w)
+    out = torch.empty(1, d, device="cuda")
+    rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    result = {"workload": "sparse MLP block, d=9216, d_ffn=36864, batch 1, fc2 rows of zero activations skipped; "
+                          "fp16 weights vs 4-bit group-128 weights with fp16 scales; 8 layers' weights in turn"}
+    for keep in (0.10, 1.00):
+        k = int(math.floor(keep * N))
+        idx = [torch.sort(torch.randperm(N, generator=g)[:k]).values.to(torch.int32).cuda() for _ in range(L)]
+        ws16 = dv.workspace(dv.dv_sparse_mlp_workspace_bytes(1, d, k, dv.DV_F16))
+        ws4 = dv.workspace(dv.lib.dv_sparse_mlp_w4_workspace_bytes(d, k))
+
+        def call(fmt, l):
+            w = layers[l]
+            if fmt == "fp16":
+                dv.dv_sparse_mlp(y[l], w["w1_t"], w["b1"], w["w2_t"], w["b2"], idx[l], k, out, ws16, residual=y[l],
+                                 fc2_rows=rows, flags=dv.DV_SKIP_NONPOS_FC2)
+            else:
+                dv.dv_sparse_mlp_w4(y[l], N, w["w1_t_q"], w["w1_t_s"], w["b1"], w["w2_t_q"], w["w2_t_s"], w["b2"],
+                                    idx[l], out, ws4, n_idx_max=k, residual=y[l], fc2_rows=rows,
+                                    flags=dv.DV_SKIP_NONPOS_FC2)
+
+        res = {"k_neurons": k}
+        for fmt in ("fp16", "w4"):
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for l in range(L):
+                    call(fmt, l)
+            gr.replay()
+            torch.cuda.synchronize()
+            rows.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / (reps * L)
+            live = int(rows.item()) / (reps * L)
+            row_b = d * 2 if fmt == "fp16" else d // 2 + (d // 128) * 2
+            by = k * row_b + live * row_b + (k + d) * 2 + 3 * d * 4 + 8 * k
+            res[fmt] = {"ms_per_call": round(ms, 5), "fc2_rows": round(live, 1), "bytes_per_call": int(by),
+                        "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_8TBps": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3)}
+            del gr
+            progress(f"4-bit MLP, keep {keep:.2f}: {fmt} {ms * 1e3:.1f} us per call")
+        res["speedup_w4_over_fp16"] = round(res["fp16"]["ms_per_call"] / res["w4"]["ms_per_call"], 3)
+        res["byte_ratio"] = round(res["fp16"]["bytes_per_call"] / res["w4"]["bytes_per_call"], 3)
+        result[f"keep_{keep:.2f}"] = res
+        del ws16, ws4, idx
+    del layers, y
+    torch.cuda.empty_cache()
+    return result
 
 
 def cpu_baseline(dims, wl, L, X, cfg, budget_s):

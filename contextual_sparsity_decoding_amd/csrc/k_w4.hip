@@ -14,15 +14,23 @@
 
 namespace dv {
 
-constexpr int kW4Group = 128;
-constexpr int kW4Chunk = 32;            // codes in one 16-byte chunk
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Codes k*4 .. k*4+3 of a 16-byte chunk (sub-vector k of 8) as floats v.
-__device__ __forceinline__ void w4_sub(const u32x4& q, int k, float (&f)[4]) {
-    const unsigned dw = k < 4 ? (k < 2 ? q[0] : q[1]) : (k < 6 ? q[2] : q[3]);
-    const unsigned h = (k & 1) ? dw >> 16 : dw;
+constexpr int kW4Group = 128;
+constexpr int kW4Chunk = 32;            // codes in a 16-byte chunk (fc1)
+constexpr int kW4Half = 16;             // codes in an 8-byte chunk (fc2)
+
+// The 8 codes of a 32-bit word as the unsigned nibbles v + 8, in order:
+// byte j of `lo` holds code 2j, byte j of `hi` code 2j + 1.  Each is
+// turned into a float by one byte conversion; the offset 8 is taken out of
+// the sums once (sum of c * (n - 8) = sum of c * n - 8 * sum of c).
+__device__ __forceinline__ void w4_word(unsigned w, float (&f)[8]) {
+    const unsigned lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f[t] = (float)((int)((h >> (4 * t)) & 15u) - 8);
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = (float)((lo >> (8 * j)) & 0xFFu);
+        f[2 * j + 1] = (float)((hi >> (8 * j)) & 0xFFu);
+    }
 }
 
 // One thread per group of 128: the largest magnitude, the scale, then the
@@ -66,10 +74,10 @@ __global__ __launch_bounds__(kBlock) void k_quant_w4(const half_t* __restrict__ 
 
 // fc1 over the selected rows, batch of one: a[u] = max(0, y . w'[idx[u]] + b1).
 // Each wave takes R rows; lane l holds chunks l, l+64, ... (32 codes each,
-// one scale: 32 divides 128).  y is staged in LDS; a lane reads the 8
-// float4 of its chunk's inputs starting at sub-vector (l & 7), so that the 8
-// lanes of a group address 8 different 16-byte slots (no bank conflicts).
-// A chunk's sum over its 32 codes is taken first, then scaled.
+// one scale: 32 divides 128).  y sits in LDS transposed, float4 k of chunk
+// c at [k][c], so that for each k the lanes read consecutive 16 bytes.  A
+// chunk's sum over its codes is taken first, less 8 times its inputs' sum
+// (computed once per chunk for all the wave's rows), then scaled.
 template <int CH, int R>
 __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
     extern __shared__ float ys[];
@@ -77,7 +85,6 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
     const int u0 = (blockIdx.x * 4 + wv) * R;
-    stage_dma(ys, a.y, a.d);
     const int nchunk = a.d / kW4Chunk, rb = a.d / 2, sb = a.d / kW4Group;
     int j[R];
     u32x4 w[R][CH];
@@ -99,54 +106,81 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
             sc[r][i] = ok ? (float)a.s[(size_t)j[r] * sb + c / 4] : 0.f;
         }
     }
-    wait_dma_and_sync();
+    {   // y into LDS, transposed
+        const f32x4* y4 = reinterpret_cast<const f32x4*>(a.y);
+        f32x4* l4 = reinterpret_cast<f32x4*>(ys);
+        for (int i = threadIdx.x; i < a.d / 4; i += kBlock) l4[(i & 7) * nchunk + (i >> 3)] = y4[i];
+    }
+    __syncthreads();
+    const f32x4* l4 = reinterpret_cast<const f32x4*>(ys);
+    float ysum[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        float t = 0.f;
+        if (c < nchunk)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const f32x4 v = l4[k * nchunk + c];
+                t += (v[0] + v[1]) + (v[2] + v[3]);
+            }
+        ysum[i] = t;
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk) {
+            float p[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) p[r] = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 ya = l4[(2 * m) * nchunk + c], yb = l4[(2 * m + 1) * nchunk + c];
+                const float yv[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float f[8];
+                    w4_word(w[r][i][m], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p[r] = fmaf(f[e], yv[e], p[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(p[r] - 8.f * ysum[i], sc[r][i], acc[r]);
+        }
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int u = u0 + r;
-        if (u >= n) break;
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-                float p = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int k = (kk + lane) & 7;
-                    float f[4];
-                    w4_sub(w[r][i], k, f);
-                    const f32x4 y4 = reinterpret_cast<const f32x4*>(ys + (size_t)c * kW4Chunk)[k];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) p = fmaf(f[t], y4[t], p);
-                }
-                acc = fmaf(p, sc[r][i], acc);
-            }
-        }
-        float v = wave_sum(acc);
+        float v = wave_sum(acc[r]);
         const float bj = j[r] >= 0 ? (float)a.bias[j[r]] : 0.f;
         v = j[r] >= 0 ? fmaxf(v + bj, 0.f) : 0.f;
-        if (lane == 0) a.out[u] = v;
+        if (lane == 0 && u < n) a.out[u] = v;
     }
 }
 
 // fc2 gather-AXPY, batch of one: partial[g] = sum over the live rows of
 // group g (64 selected rows) of a[u] * w'[idx[u]] restricted to one slice
-// of 2048 columns (lane l: columns [32 l, 32 l + 32) of the slice, one
-// scale).  Rows whose coefficient is zero are skipped when asked (the
-// ReLU-sparsified second layer); the 4 waves' sums are added in order in
-// LDS and written as the group's partial, which k_axpy_finalize adds up.
+// of 1024 columns (lane l: columns [16 l, 16 l + 16) of the slice, 8 bytes
+// of codes per row, one scale).  Rows whose coefficient is zero are
+// skipped when asked (the ReLU-sparsified second layer); the 4 waves' sums
+// are added in order in LDS and written as the group's partial, which
+// k_axpy_finalize adds up.
 constexpr int kW4Rows = 64;
 __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
     __shared__ int s_row[kW4Rows];
     __shared__ float s_cf[kW4Rows];
     __shared__ unsigned s_n;
-    __shared__ float red[3][kWave * kW4Chunk];
+    __shared__ f32x4 red[3][4][kWave];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int slice = blockIdx.x, g = blockIdx.y;
     const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
     const int r0 = g * kW4Rows;
-    const int c = slice * kWave + lane;                // this lane's chunk of the row
-    const int nchunk = a.d / kW4Chunk, rb = a.d / 2, sb = a.d / kW4Group;
+    const int c = slice * kWave + lane;                // this lane's 8-byte chunk of the row
+    const int nchunk = a.d / kW4Half, rb = a.d / 2, sb = a.d / kW4Group;
     const bool colok = c < nchunk;
     if (threadIdx.x < kWave) {
         bool live = false;
@@ -172,54 +206,58 @@ __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
     __syncthreads();
     const int nlive = (int)s_n;
     constexpr int U = kW4Rows / 4;                     // rows per wave
-    u32x4 w[U];
+    unsigned w[U][2];
     float sc[U];
 #pragma unroll
     for (int t = 0; t < U; ++t) {
         const int k = wv + 4 * t;
         const bool ok = k < nlive && colok;
         const int rr = k < nlive ? s_row[k] : 0;
-        w[t] = ok ? ld16_stream(a.q + (size_t)rr * rb + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
-        sc[t] = ok ? (float)a.s[(size_t)rr * sb + c / 4] : 0.f;
+        if (ok) {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.q + (size_t)rr * rb + (size_t)c * 8));
+            w[t][0] = v[0];
+            w[t][1] = v[1];
+        } else {
+            w[t][0] = w[t][1] = 0x88888888u;             // codes of 0
+        }
+        sc[t] = ok ? (float)a.s[(size_t)rr * sb + c / 8] : 0.f;
     }
-    float acc[kW4Chunk];
+    float acc[kW4Half];
 #pragma unroll
-    for (int e = 0; e < kW4Chunk; ++e) acc[e] = 0.f;
+    for (int e = 0; e < kW4Half; ++e) acc[e] = 0.f;
+    float csum = 0.f;
 #pragma unroll
     for (int t = 0; t < U; ++t) {
         const int k = wv + 4 * t;
         if (k < nlive) {
             const float cs = s_cf[k] * sc[t];
+            csum += cs;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                float f[4];
-                w4_sub(w[t], kk, f);
+            for (int m = 0; m < 2; ++m) {
+                float f[8];
+                w4_word(w[t][m], f);
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) acc[4 * kk + tt] = fmaf(cs, f[tt], acc[4 * kk + tt]);
+                for (int e = 0; e < 8; ++e) acc[8 * m + e] = fmaf(cs, f[e], acc[8 * m + e]);
             }
         }
     }
-    // waves 1..3 hand their sums to wave 0, which adds them in order; lane l's
-    // 32 columns sit at red[.][32 l ...], read back 16 bytes at a time from a
-    // rotated start so that 8 neighbouring lanes hit different banks
+#pragma unroll
+    for (int e = 0; e < kW4Half; ++e) acc[e] = fmaf(-8.f, csum, acc[e]);
+    // waves 1..3 hand their sums to wave 0, which adds them in order
     if (wv > 0) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int k = (kk + lane) & 7;
-            reinterpret_cast<f32x4*>(&red[wv - 1][lane * kW4Chunk])[k] =
-                f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
-        }
+        for (int k = 0; k < 4; ++k)
+            red[wv - 1][k][lane] = f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
     }
     __syncthreads();
     if (wv == 0 && colok) {
-        float* dst = a.partial + (size_t)g * a.d + (size_t)c * kW4Chunk;
+        f32x4* dst = reinterpret_cast<f32x4*>(a.partial + (size_t)g * a.d + (size_t)c * kW4Half);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int k = (kk + lane) & 7;
+        for (int k = 0; k < 4; ++k) {
             f32x4 o = f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
 #pragma unroll
-            for (int q = 0; q < 3; ++q) o += reinterpret_cast<const f32x4*>(&red[q][lane * kW4Chunk])[k];
-            reinterpret_cast<f32x4*>(dst)[k] = o;
+            for (int q = 0; q < 3; ++q) o += red[q][k][lane];
+            dst[k] = o;
         }
     }
 }
@@ -257,7 +295,7 @@ dv_status launch_rowdot_w4(const W4RowArgs& a, hipStream_t s) {
 int w4_axpy_groups(int rows) { return cdiv(rows < 1 ? 1 : rows, kW4Rows); }
 
 dv_status launch_axpy_w4(const W4AxpyArgs& a, hipStream_t s) {
-    const dim3 grid(cdiv(a.d / kW4Chunk, kWave), w4_axpy_groups(a.rows));
+    const dim3 grid(cdiv(a.d / kW4Half, kWave), w4_axpy_groups(a.rows));
     DV_LAUNCH(k_axpy_w4, grid, dim3(kBlock), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
