@@ -510,8 +510,10 @@ static dv_status qkv_go3(const QkvArgs& a_in, hipStream_t s) {
     // batch of one with inputs in LDS: one hole helper per K/V block of
     // 4 * qkv_hole_rows(R) rows (more items are taken in turn)
     const int hb = holes && yl + 2 * row <= kQkvLdsMax ? 2 : holes && yl + row <= kQkvLdsMax ? 1 : 0;
-    // without staged stored inputs, rows are split over wave pairs
-    constexpr bool kSplitOk = CH % 2 == 0;
+    // without staged stored inputs, rows are split over wave pairs, where a
+    // wave holds at least two rows (with one, a workgroup would own two rows
+    // and stage all of y for them)
+    constexpr bool kSplitOk = CH % 2 == 0 && R >= 2;
     const bool split = kSplitOk && hb == 0;
     const int wg_rows = (split ? 2 : 4) * R;
     if (a.dh % wg_rows) return fail(DV_ERR_UNSUPPORTED, "Q/K/V projection: d_h=%d", a.dh);
