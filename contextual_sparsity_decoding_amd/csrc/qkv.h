@@ -240,6 +240,12 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     // inputs), then the weight rows, all in flight together
     if (YL) stage_dma(ys, a.y, a.B * d);
     if (HB > 0 && fill && pos > lo0) stage_dma(hin, a.y_buf + (size_t)lo0 * d, min(HB, pos - lo0) * d);
+    // LNF: the LayerNorm's gamma and beta into registers behind the inputs
+    // and ahead of the weight rows, so the LayerNorm waits for the inputs
+    // only (their registers are free again before most rows are loaded)
+    constexpr int GBN = LNF ? (CH * kWave * E / 4 + kBlock - 1) / kBlock : 1;
+    f32x4 gr[GBN], br[GBN];
+    if constexpr (LNF) ln_gamma_beta_regs<kBlock, GBN>(LnArgs{a.y, a.ln_g, a.ln_b, a.eps, nullptr}, d, gr, br);
     const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh + e0) * d;
     issue_order_fence();
     // Chunk-major, the order the dot products consume them in.  Only the
@@ -272,10 +278,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e0 + j]) : 0.f;
     if (live) sync_after_dma<R * PF>();              // the inputs have landed; the rows may still be in flight
     else sync_after_dma<0>();
-    if constexpr (LNF) {
-        const LnArgs ln{a.y, a.ln_g, a.ln_b, a.eps, nullptr};
-        layernorm_lds(ys, d, ln, false);
-    }
+    if constexpr (LNF) layernorm_lds_reg<kBlock, GBN>(ys, d, a.eps, gr, br);
     // this step's input joins the stored inputs: float4 c of [B][d] goes
     // with thread c of the grid (a handful of workgroups), from LDS when staged
     if (a.y_buf && pos_ok) {

@@ -66,10 +66,12 @@ struct LnArgs {
     float* y_out;
 };
 
-template <int NT = kBlock, bool GB = false>
-__device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
+// Mean and 1/sqrt(var + eps) of the row held in LDS (two passes, float4
+// reads, four independent partial sums per thread).
+template <int NT = kBlock>
+__device__ __forceinline__ void ln_stats_lds(const float* __restrict__ ys, int d, float eps, float* mean_out,
+                                             float* rstd_out) {
     __shared__ float red[NT / kWave];
-    // float4 LDS reads, four independent partial sums per thread
     const f32x4* x4 = reinterpret_cast<const f32x4*>(ys);
     f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -82,7 +84,14 @@ __device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) q4[e] = fmaf(t[e], t[e], q4[e]);
     }
-    const float rstd = 1.0f / sqrtf(block_sum_waves<NT / kWave>((q4[0] + q4[1]) + (q4[2] + q4[3]), red) / (float)d + ln.eps);
+    *rstd_out = 1.0f / sqrtf(block_sum_waves<NT / kWave>((q4[0] + q4[1]) + (q4[2] + q4[3]), red) / (float)d + eps);
+    *mean_out = mean;
+}
+
+template <int NT = kBlock, bool GB = false>
+__device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, const LnArgs& ln, bool write) {
+    float mean, rstd;
+    ln_stats_lds<NT>(ys, d, ln.eps, &mean, &rstd);
     // gamma and beta: staged in LDS after the row (GB), else from memory
     const f32x4* g4 = reinterpret_cast<const f32x4*>(GB ? ys + d : ln.g);
     const f32x4* b4 = reinterpret_cast<const f32x4*>(GB ? ys + 2 * d : ln.b);
@@ -95,6 +104,44 @@ __device__ __forceinline__ void layernorm_lds(float* __restrict__ ys, int d, con
         for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd * gg[e] + bb[e];
         y4[c] = v;
         if (write) reinterpret_cast<f32x4*>(ln.y_out)[c] = v;
+    }
+    lds_barrier();
+}
+
+// Gamma and beta for layernorm_lds_reg: float4 c = threadIdx.x + k * NT of
+// each, k < GBN, loaded into registers.  Issued before a kernel's weight
+// loads, they return ahead of them (vector loads retire in issue order), so
+// the LayerNorm does not wait for the weights in flight.
+template <int NT, int GBN>
+__device__ __forceinline__ void ln_gamma_beta_regs(const LnArgs& ln, int d, f32x4 (&gr)[GBN], f32x4 (&br)[GBN]) {
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(ln.g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(ln.b);
+#pragma unroll
+    for (int k = 0; k < GBN; ++k) {
+        const int c = threadIdx.x + k * NT;
+        gr[k] = c < d / 4 ? g4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        br[k] = c < d / 4 ? b4[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// layernorm_lds (without the y_out copy) with gamma and beta already in
+// registers; the same arithmetic per element.  d <= 4 * NT * GBN.
+template <int NT, int GBN>
+__device__ __forceinline__ void layernorm_lds_reg(float* __restrict__ ys, int d, float eps, const f32x4 (&gr)[GBN],
+                                                  const f32x4 (&br)[GBN]) {
+    float mean, rstd;
+    ln_stats_lds<NT>(ys, d, eps, &mean, &rstd);
+    f32x4* y4 = reinterpret_cast<f32x4*>(ys);
+#pragma unroll
+    for (int k = 0; k < GBN; ++k) {
+        const int c = threadIdx.x + k * NT;
+        if (c < d / 4) {
+            const f32x4 gg = gr[k], bb = br[k];
+            f32x4 v = y4[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (v[e] - mean) * rstd * gg[e] + bb[e];
+            y4[c] = v;
+        }
     }
     lds_barrier();
 }
