@@ -456,9 +456,19 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             round(ys, p0, cnt, std::integral_constant<int, HB2>());
         }
     } else {
-        for (int p = lo0; p < pos; ++p) {              // inputs too long for LDS: read from global memory
+        // one stored input at a time: with y in LDS (batch of one) it is
+        // staged there by DMA, y being consumed (one round trip, no
+        // registers), else read from global memory
+        for (int p = lo0; p < pos; ++p) {
+            const float* in = a.y_buf + (size_t)p * d;
+            if constexpr (YL && NB == 1) {
+                __syncthreads();                       // every wave has consumed y (or the previous input)
+                stage_dma(ys, in, d);
+                wait_dma_and_sync();
+                in = ys;
+            }
             float hacc[R][1];
-            dots(a.y_buf + (size_t)p * d, std::integral_constant<int, 1>(), hacc);
+            dots(in, std::integral_constant<int, 1>(), hacc);
 #pragma unroll
             for (int j = 0; j < R; ++j) hacc[j][0] = wave_sum(hacc[j][0]);
             pair_add(std::integral_constant<int, 1>(), hacc);

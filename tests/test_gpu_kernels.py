@@ -209,7 +209,8 @@ def _attn_setup(d, h, dh, max_len, n_filled, seed, wdt="f16", B=1):
 
 @pytest.mark.parametrize("B,h,dh,full,d", [(2, 8, 64, False, 512), (2, 8, 128, False, 512), (1, 8, 64, False, 512),
                                            (1, 8, 128, False, 512), (1, 80, 64, False, 512), (1, 8, 128, True, 512),
-                                           (1, 8, 128, False, 6144)])
+                                           (1, 8, 128, False, 6144), (1, 8, 128, False, 9216),
+                                           (2, 8, 128, False, 9216)])
 def test_qkv_with_holes_over_steps(dvlib, B, h, dh, full, d):
     """Missing K/V positions recomputed from the stored inputs (DejaVu §4.2):
     batch rows of two (each row its own holes), and a batch of one, where
@@ -218,7 +219,10 @@ def test_qkv_with_holes_over_steps(dvlib, B, h, dh, full, d):
     and then all 80, past the helpers' 64-head limit).  With `full` the
     cache holds exactly the positions the steps write (the last step writes
     slot max_len - 1).  At d = 6144 one stored input fits beside y in LDS:
-    the owner computes one missing position and helpers take one at a time."""
+    the owner computes one missing position and helpers take one at a time.
+    At d = 9216 none does: the owners (wave pairs splitting each row) take
+    every missing position, each staged in y's place once y is consumed
+    (batch of one) or read from global memory (two batch rows)."""
     n0, T = 10, 9
     L = n0 + T if full else 48
     W, K, V = _attn_setup(d, h, dh, L, n0, seed=dh + h + B, B=B)
