@@ -24,15 +24,8 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
     const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
     const int u0 = (blk * (NT / kWave) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) * RR;
     const int nchunk = a.d / E;
-    // x straight into LDS first (it depends on nothing), ahead of the row
-    // indices and the rows
-    stage_dma<NT>(ys, ln.x, a.d);
-    if constexpr (GB) {
-        // gamma and beta too: loads retire in issue order, so fetching them
-        // after the rows would hold the LayerNorm until the rows arrive
-        stage_dma<NT>(ys + a.d, ln.g, a.d);
-        stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
-    }
+    // The row indices first: the rows wait for them, and loads retire in
+    // issue order, so behind x's DMA they would make the rows wait for x.
     int j[RR];
     int jany = -1;                                   // a valid row of this wave, re-read in place of invalid ones
 #pragma unroll
@@ -46,9 +39,19 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         j[r] = __builtin_amdgcn_readfirstlane(jj);
         if (j[r] >= 0) jany = j[r];
     }
-    float bias[RR];                                  // fc1's bias now, ahead of the rows, not one more trip at the end
+    // x straight into LDS, ahead of the rows
+    stage_dma<NT>(ys, ln.x, a.d);
+    if constexpr (GB) {
+        // gamma and beta too: fetched after the rows they would hold the
+        // LayerNorm until the rows arrive
+        stage_dma<NT>(ys + a.d, ln.g, a.d);
+        stage_dma<NT>(ys + 2 * a.d, ln.b, a.d);
+    }
+    // fc1's bias as stored, also ahead of the rows; converted where it is
+    // added (a conversion next to its load would wait for x's DMA)
+    T braw[RR];
 #pragma unroll
-    for (int r = 0; r < RR; ++r) bias[r] = OP == ROW_FC1 && j[r] >= 0 ? to_f32(((const T*)a.bias)[j[r]]) : 0.f;
+    for (int r = 0; r < RR; ++r) braw[r] = OP == ROW_FC1 ? ((const T*)a.bias)[j[r] >= 0 ? j[r] : 0] : T(0);
     issue_order_fence();
     // With several rows per wave, the first PF chunks of every row now and
     // the rest one chunk ahead of the dot products (a wave's loads go out
@@ -111,7 +114,7 @@ __device__ __forceinline__ void rowdot_ln_block(int blk, float* ys, const RowArg
         const int u = u0 + r;
         if (u >= a.n_max) break;
         float v = wave_sum(j[r] >= 0 ? acc[r] : 0.f);
-        if (OP == ROW_FC1) v = j[r] >= 0 ? fmaxf(v + bias[r], 0.f) : 0.f;
+        if (OP == ROW_FC1) v = j[r] >= 0 ? fmaxf(v + to_f32(braw[r]), 0.f) : 0.f;
         if ((threadIdx.x & 63) == 0) a.out[u] = v;
     }
 }

@@ -138,6 +138,9 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
         const T* Wb = (const T*)a.w + ((size_t)(which * a.h + hd) * dh + e0) * d;
         __syncthreads();                               // the previous item's inputs are consumed
         stage_dma(ys, a.y_buf + (size_t)p0 * d, np * d);
+        T braw[R];                                     // the bias ahead of the rows (loads retire in issue order)
+#pragma unroll
+        for (int j = 0; j < R; ++j) braw[j] = ((const T*)a.bias)[(size_t)(which * a.h + hd) * dh + e0 + j];
         issue_order_fence();
         u32x4 w[R][CH];
 #pragma unroll
@@ -147,10 +150,10 @@ __device__ __forceinline__ void qkv_hole_items(const QkvArgs& a, int hid, float*
                 const int c = lane + i * kWave;
                 w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
             }
+        sync_after_dma<R * CH>();                      // the inputs have landed; the rows may still be in flight
         float bv[R];
 #pragma unroll
-        for (int j = 0; j < R; ++j) bv[j] = to_f32(((const T*)a.bias)[(size_t)(which * a.h + hd) * dh + e0 + j]);
-        sync_after_dma<R * CH>();                      // the inputs have landed; the rows may still be in flight
+        for (int j = 0; j < R; ++j) bv[j] = to_f32(braw[j]);
         float acc[R][NV];
         qkv_dots<T, CH, R, NV>(w, ys, d, nchunk, acc);
         half_t* cache = which == 1 ? a.K : a.V;
@@ -246,13 +249,19 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     constexpr int GBN = LNF ? (CH * kWave * E / 4 + kBlock - 1) / kBlock : 1;
     f32x4 gr[GBN], br[GBN];
     if constexpr (LNF) ln_gamma_beta_regs<kBlock, GBN>(LnArgs{a.y, a.ln_g, a.ln_b, a.eps, nullptr}, d, gr, br);
+    // the bias as stored, also ahead of the rows; converted where it is
+    // added (a conversion next to its load would wait for every load
+    // issued before it, the rows included)
+    T braw[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) braw[j] = ((const T*)a.bias)[(size_t)(which * a.h + (live ? head : 0)) * dh + e0 + j];
     const T* Wb = (const T*)a.w + ((size_t)(which * a.h + (live ? head : 0)) * dh + e0) * d;
     issue_order_fence();
     // Chunk-major, the order the dot products consume them in.  Only the
     // first PF chunks are issued here; the on-time dot products issue chunk
     // i + PF after consuming chunk i.  A wave cannot issue loads faster than
     // HBM drains them, so issuing all of them first would leave every dot
-    // product for after the last byte arrives.  A live workgroup issues all
+    // product for after the last byte arrives.  Every workgroup issues all
     // R * CH loads (chunks past the row re-read chunk 0 and are never used:
     // the dot products stop at the row's end).
     constexpr int PF = (kQkvFlightKB / R) < CHW ? kQkvFlightKB / R : CHW;   // kQkvFlightKB of rows in flight per wave
@@ -264,20 +273,16 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             w[j][i] = ld16_stream(Wb + (size_t)j * d + (size_t)(c < nchunk ? c : 0) * E);
         }
     };
-    if (live) {
+    // Every workgroup loads its rows, one whose head is outside W those of
+    // head 0 (it stores nothing): with a single path the compiler's wait
+    // for gamma, beta and the bias leaves these rows in flight (merged with
+    // a path without them it would wait for every load).
 #pragma unroll
-        for (int i = 0; i < PF; ++i) load_chunk(i);
-    } else {
+    for (int i = 0; i < PF; ++i) load_chunk(i);
+    sync_after_dma<R * PF>();                          // the inputs have landed; the rows may still be in flight
+    float bv[R];                                       // loaded before the rows: here they have landed
 #pragma unroll
-        for (int i = 0; i < CHW; ++i)
-#pragma unroll
-            for (int j = 0; j < R; ++j) w[j][i] = u32x4{0u, 0u, 0u, 0u};
-    }
-    float bv[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(((const T*)a.bias)[(size_t)(which * a.h + head) * dh + e0 + j]) : 0.f;
-    if (live) sync_after_dma<R * PF>();              // the inputs have landed; the rows may still be in flight
-    else sync_after_dma<0>();
+    for (int j = 0; j < R; ++j) bv[j] = live ? to_f32(braw[j]) : 0.f;
     if constexpr (LNF) layernorm_lds_reg<kBlock, GBN>(ys, d, a.eps, gr, br);
     // this step's input joins the stored inputs: float4 c of [B][d] goes
     // with thread c of the grid (a handful of workgroups), from LDS when staged
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
             }
             if (i + PF < CHW) {
                 issue_order_fence();                     // the next loads go out after this chunk's work
-                if (live) load_chunk(i + PF);
+                load_chunk(i + PF);
                 issue_order_fence();
             }
         }
