@@ -16,6 +16,12 @@ namespace dv {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// A scale held as its 16-bit pattern in a 32-bit register until it is used
+// (fp16 values held as such get packed two to a register, and the packing
+// waits for the load).
+__device__ __forceinline__ unsigned scale_bits(const half_t* p) { return *reinterpret_cast<const unsigned short*>(p); }
+__device__ __forceinline__ float scale_f32(unsigned b) { return (float)__builtin_bit_cast(half_t, (unsigned short)b); }
+
 constexpr int kW4Group = 128;
 constexpr int kW4Chunk = 32;            // codes in a 16-byte chunk (fc1)
 constexpr int kW4Half = 16;             // codes in an 8-byte chunk (fc2)
@@ -87,8 +93,6 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
     const int u0 = (blockIdx.x * 4 + wv) * R;
     const int nchunk = a.d / kW4Chunk, rb = a.d / 2, sb = a.d / kW4Group;
     int j[R];
-    u32x4 w[R][CH];
-    float sc[R][CH];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int u = u0 + r;
@@ -98,18 +102,42 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
             jj = (unsigned)jj < (unsigned)a.w_rows ? jj : -1;
         }
         j[r] = __builtin_amdgcn_readfirstlane(jj);
+    }
+    // Loads retire in issue order: y goes out first (into registers, on its
+    // way to LDS), then the codes and the scales, so that staging y waits
+    // for y only.  Every lane loads (one past the row, or of a row not
+    // selected, reads row 0 and its scale is masked to 0), and the scales
+    // are kept as stored and converted where they are used: a load under a
+    // lane mask, or a conversion next to its load, would make that wait
+    // cover every load before it.
+    constexpr int KY = CH * kW4Chunk / 4 * kWave / kBlock;   // float4 of y per thread (d <= CH * 2048)
+    f32x4 yr[KY];
+    {
+        const f32x4* y4 = reinterpret_cast<const f32x4*>(a.y);
+#pragma unroll
+        for (int k = 0; k < KY; ++k) {
+            const int i = threadIdx.x + k * kBlock;
+            yr[k] = i < a.d / 4 ? y4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    u32x4 w[R][CH];
+    unsigned scr[R][CH];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = lane + i * kWave;
-            const bool ok = j[r] >= 0 && c < nchunk;
-            w[r][i] = ok ? ld16_stream(a.q + (size_t)j[r] * rb + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
-            sc[r][i] = ok ? (float)a.s[(size_t)j[r] * sb + c / 4] : 0.f;
+            const size_t jr = (size_t)(j[r] >= 0 ? j[r] : 0), cc = (size_t)(c < nchunk ? c : 0);
+            w[r][i] = ld16_stream(a.q + jr * rb + cc * 16);
+            scr[r][i] = scale_bits(a.s + jr * sb + cc / 4);
         }
-    }
     {   // y into LDS, transposed
-        const f32x4* y4 = reinterpret_cast<const f32x4*>(a.y);
         f32x4* l4 = reinterpret_cast<f32x4*>(ys);
-        for (int i = threadIdx.x; i < a.d / 4; i += kBlock) l4[(i & 7) * nchunk + (i >> 3)] = y4[i];
+#pragma unroll
+        for (int k = 0; k < KY; ++k) {
+            const int i = threadIdx.x + k * kBlock;
+            if (i < a.d / 4) l4[(i & 7) * nchunk + (i >> 3)] = yr[k];
+        }
     }
     __syncthreads();
     const f32x4* l4 = reinterpret_cast<const f32x4*>(ys);
@@ -149,7 +177,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(p[r] - 8.f * ysum[i], sc[r][i], acc[r]);
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(p[r] - 8.f * ysum[i], j[r] >= 0 ? scale_f32(scr[r][i]) : 0.f, acc[r]);
         }
     }
 #pragma unroll
@@ -206,21 +234,25 @@ __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
     __syncthreads();
     const int nlive = (int)s_n;
     constexpr int U = kW4Rows / 4;                     // rows per wave
+    // Every lane of a live row loads (one past the row's end reads the row's
+    // first chunk; its scale is masked to 0), rows past the live ones are
+    // neither loaded nor read, and the scales are kept as stored and
+    // converted where they are used: a load under a lane mask, a value
+    // merged with a constant, or a conversion next to its load would each
+    // make a wait cover every load before it (one row at a time).
     unsigned w[U][2];
-    float sc[U];
+    unsigned scr[U];
 #pragma unroll
     for (int t = 0; t < U; ++t) {
         const int k = wv + 4 * t;
-        const bool ok = k < nlive && colok;
-        const int rr = k < nlive ? s_row[k] : 0;
-        if (ok) {
-            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.q + (size_t)rr * rb + (size_t)c * 8));
+        if (k < nlive) {                               // uniform over the wave
+            const int rr = s_row[k];
+            const size_t cc = (size_t)(colok ? c : 0);
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.q + (size_t)rr * rb + cc * 8));
             w[t][0] = v[0];
             w[t][1] = v[1];
-        } else {
-            w[t][0] = w[t][1] = 0x88888888u;             // codes of 0
+            scr[t] = scale_bits(a.s + (size_t)rr * sb + cc / 8);
         }
-        sc[t] = ok ? (float)a.s[(size_t)rr * sb + c / 8] : 0.f;
     }
     float acc[kW4Half];
 #pragma unroll
@@ -230,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
     for (int t = 0; t < U; ++t) {
         const int k = wv + 4 * t;
         if (k < nlive) {
-            const float cs = s_cf[k] * sc[t];
+            const float cs = s_cf[k] * (colok ? scale_f32(scr[t]) : 0.f);
             csum += cs;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
