@@ -54,6 +54,18 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[4], float) {
 template <typename T>
 __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 
+// An element held as its bits in a 32-bit register (fp16 zero-extended)
+// until it is used, converted then by bits_f32: an fp16 value converted
+// next to its load, or held as fp16 (packed two to a register), makes the
+// compiler wait for that load, and so for every load issued before it.
+__device__ __forceinline__ unsigned elt_bits(const half_t* p) { return *reinterpret_cast<const unsigned short*>(p); }
+__device__ __forceinline__ unsigned elt_bits(const float* p) { return *reinterpret_cast<const unsigned*>(p); }
+template <typename T> __device__ __forceinline__ float bits_f32(unsigned b);
+template <> __device__ __forceinline__ float bits_f32<half_t>(unsigned b) {
+    return (float)__builtin_bit_cast(half_t, (unsigned short)b);
+}
+template <> __device__ __forceinline__ float bits_f32<float>(unsigned b) { return __builtin_bit_cast(float, b); }
+
 // ---- cross-lane moves and reductions --------------------------------------
 // DPP (data-parallel primitives) move values between lanes inside the VALU
 // instruction itself, with no trip through the LDS crossbar.  gfx9 control

@@ -23,26 +23,36 @@ __global__ __launch_bounds__(kBlock) void k_rowdot(RowArgs a, int rpg) {
     const int u1 = min(n, u0 + rpg);
     const int nk = u1 - u0 > wv ? (u1 - u0 - wv + 3) / 4 : 0;   // rows of this wave
     const int nchunk = a.d / E;
-    // all of this wave's row indices in one load (lane k holds row k's)
+    // all of this wave's row indices in one load (lane k holds row k's),
+    // then fc1's biases the same way, kept as bits until used (read as
+    // converted values they would make the wave wait for every load before
+    // them, the next row's included)
     int my_j = -1;
     if ((threadIdx.x & 63) < nk) {
         const int u = u0 + wv + 4 * (threadIdx.x & 63);
         const int j = a.idx ? a.idx[u] : u;
         my_j = (unsigned)j < (unsigned)a.w_rows ? j : -1;   // an index outside W selects nothing
     }
+    const unsigned my_b = OP == ROW_FC1 ? elt_bits((const T*)a.bias + (my_j >= 0 ? my_j : 0)) : 0u;
     auto row_of = [&](int k) -> int { return __builtin_amdgcn_readlane(my_j, k); };   // k is wave-uniform
     stage_dma(ys, a.y, a.B * a.d);                        // y straight into LDS, ahead of the rows
     u32x4 wa[CH], wb[CH];
     int ja = nk > 0 ? row_of(0) : -1, jb = -1;
-    if (ja >= 0) load_row<T, CH, true>((const T*)a.w + (size_t)ja * a.d, nchunk, wa);
-    wait_dma_and_sync();
+    if (ja >= 0) {
+        // all CH loads go out (chunks past the row re-read chunk 0, never
+        // used), so that a wait for CH outstanding covers y's DMA
+        load_row_all<T, CH>((const T*)a.w + (size_t)ja * a.d, nchunk, wa);
+        sync_after_dma<CH>();                             // y has landed; the row may still be in flight
+    } else {
+        sync_after_dma<0>();
+    }
     auto emit = [&](int k, int j, const u32x4 (&w)[CH]) {
         const int u = u0 + wv + 4 * k;
         float acc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = 0.f;
         if (j >= 0) dot_row<T, CH, NB>(w, nchunk, ys, a.d, NB, acc);
-        const float bj = (OP == ROW_FC1 && j >= 0) ? to_f32(((const T*)a.bias)[j]) : 0.f;
+        const float bj = (OP == ROW_FC1 && j >= 0) ? bits_f32<T>(__builtin_amdgcn_readlane(my_b, k)) : 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float v = wave_sum(acc[b]);

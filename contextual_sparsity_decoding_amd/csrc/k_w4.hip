@@ -16,11 +16,6 @@ namespace dv {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// A scale held as its 16-bit pattern in a 32-bit register until it is used
-// (fp16 values held as such get packed two to a register, and the packing
-// waits for the load).
-__device__ __forceinline__ unsigned scale_bits(const half_t* p) { return *reinterpret_cast<const unsigned short*>(p); }
-__device__ __forceinline__ float scale_f32(unsigned b) { return (float)__builtin_bit_cast(half_t, (unsigned short)b); }
 
 constexpr int kW4Group = 128;
 constexpr int kW4Chunk = 32;            // codes in a 16-byte chunk (fc1)
@@ -129,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
             const int c = lane + i * kWave;
             const size_t jr = (size_t)(j[r] >= 0 ? j[r] : 0), cc = (size_t)(c < nchunk ? c : 0);
             w[r][i] = ld16_stream(a.q + jr * rb + cc * 16);
-            scr[r][i] = scale_bits(a.s + jr * sb + cc / 4);
+            scr[r][i] = elt_bits(a.s + jr * sb + cc / 4);
         }
     {   // y into LDS, transposed
         f32x4* l4 = reinterpret_cast<f32x4*>(ys);
@@ -177,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_w4(W4RowArgs a) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(p[r] - 8.f * ysum[i], j[r] >= 0 ? scale_f32(scr[r][i]) : 0.f, acc[r]);
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(p[r] - 8.f * ysum[i], j[r] >= 0 ? bits_f32<half_t>(scr[r][i]) : 0.f, acc[r]);
         }
     }
 #pragma unroll
@@ -251,7 +246,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
             const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.q + (size_t)rr * rb + cc * 8));
             w[t][0] = v[0];
             w[t][1] = v[1];
-            scr[t] = scale_bits(a.s + (size_t)rr * sb + cc / 8);
+            scr[t] = elt_bits(a.s + (size_t)rr * sb + cc / 8);
         }
     }
     float acc[kW4Half];
@@ -262,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy_w4(W4AxpyArgs a) {
     for (int t = 0; t < U; ++t) {
         const int k = wv + 4 * t;
         if (k < nlive) {
-            const float cs = s_cf[k] * (colok ? scale_f32(scr[t]) : 0.f);
+            const float cs = s_cf[k] * (colok ? bits_f32<half_t>(scr[t]) : 0.f);
             csum += cs;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
