@@ -21,7 +21,7 @@
 // sums go to a [KS][16][n_max] buffer and a second launch adds the ranges in
 // order and applies the epilogue (fc1: bias and ReLU; Q/K/V: bias, q in
 // fp32 and K/V into the cache in fp16).
-#include "dv_internal.h"
+#include "rowdot.h"
 
 namespace dv {
 
@@ -135,6 +135,122 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma(MfmaArgs a) {
     }
 }
 
+// The same contraction with each wave's k range a fixed SPS steps (the last
+// range of a row may be shorter), unrolled in full: with no loop the
+// compiler's waits count the loads of each slot exactly (in the loop above
+// its wait for the loop-carried slots falls back to every load).  Every
+// small load goes out before any is used, and the weight and input loads
+// are unmasked (a masked load, or a value merged with a default, makes the
+// next use wait for every load): a row not selected reads row 0 and a lane
+// past the batch row 0's inputs, both masked where used; a step past the
+// range reads this lane's inputs of the range's last step, never used.
+template <int SPS>
+__global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+    const int tile = wid / a.ks, ksi = wid % a.ks;
+    const int u0 = tile * 16 * kMfmaRT;
+    if (u0 >= a.n_max) return;                             // whole wave idle
+    const int nsteps = a.d / 32;
+    const int st0 = ksi * SPS, st1 = min(nsteps, st0 + SPS);
+    const int col = lane & 15, kq = lane >> 4;             // B column / A row, k block of 8
+    int key[kMfmaRT], raw[kMfmaRT];
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) {
+        const int u = u0 + 16 * t + col, uc = u < a.n_max ? u : a.n_max - 1;
+        key[t] = a.qkv ? (uc / a.dh) % a.n_sel : uc;
+    }
+    const int32_t* src = a.qkv ? a.head_idx : a.idx;
+    if (src) {
+#pragma unroll
+        for (int t = 0; t < kMfmaRT; ++t) raw[t] = src[key[t]];
+    } else {
+#pragma unroll
+        for (int t = 0; t < kMfmaRT; ++t) raw[t] = key[t];
+    }
+    const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
+    if (u0 >= n) return;
+    const half_t* rowp[kMfmaRT];
+    bool rv[kMfmaRT];
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) {
+        const int u = u0 + 16 * t + col;
+        int j = -1;
+        if (u < n) {
+            if (a.qkv) {
+                const int which = u / (a.n_sel * a.dh), e = u % a.dh, head = raw[t];
+                if ((unsigned)head < (unsigned)a.h) j = (which * a.h + head) * a.dh + e;
+            } else {
+                j = raw[t];
+            }
+            if ((unsigned)j >= (unsigned)a.w_rows) j = -1;   // an index outside W selects nothing
+        }
+        rv[t] = j >= 0;
+        rowp[t] = a.w + (size_t)(j >= 0 ? j : 0) * a.d + 8 * kq;
+    }
+    const bool yrow = col < a.B;                           // A row = batch row
+    const float* yp = a.y + (size_t)(yrow ? col : 0) * a.d + 8 * kq;
+    f32x4 acc[kMfmaRT];
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 wr[kMfmaPF][kMfmaRT];
+    f32x4 yr[kMfmaPF][2];
+    auto load_w = [&](int st, int slot) {
+        const bool in = st < st1;
+        const size_t sc = (size_t)(in ? st : st1 - 1) * 32;
+#pragma unroll
+        for (int t = 0; t < kMfmaRT; ++t)
+            wr[slot][t] = ld16_stream(in ? (const void*)(rowp[t] + sc) : (const void*)(yp + sc));
+        yr[slot][0] = *reinterpret_cast<const f32x4*>(yp + sc);
+        yr[slot][1] = *reinterpret_cast<const f32x4*>(yp + sc + 4);
+    };
+#pragma unroll
+    for (int p = 0; p < kMfmaPF; ++p) {                   // in slot order (the first slot's loads first)
+        load_w(st0 + p, p);
+        issue_order_fence();
+    }
+#pragma unroll
+    for (int i = 0; i < SPS; ++i) {
+        constexpr int PFc = kMfmaPF;
+        const int p = i % PFc;
+        if (st0 + i < st1) {                               // uniform over the wave
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 y0 = yrow ? yr[p][0] : zero, y1 = yrow ? yr[p][1] : zero;
+            f16x8m hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = (half_t)y0[e];
+                hi[4 + e] = (half_t)y1[e];
+                lo[e] = (half_t)(y0[e] - (float)hi[e]);
+                lo[4 + e] = (half_t)(y1[e] - (float)hi[4 + e]);
+            }
+#pragma unroll
+            for (int t = 0; t < kMfmaRT; ++t) {
+                const f16x8m wb = __builtin_bit_cast(f16x8m, rv[t] ? wr[p][t] : u32x4{0u, 0u, 0u, 0u});
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, wb, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, wb, acc[t], 0, 0, 0);
+            }
+        }
+        if (i + PFc < SPS) {                               // the slot just consumed takes step i + PF
+            issue_order_fence();
+            load_w(st0 + i + PFc, p);
+            issue_order_fence();
+        }
+    }
+    float* P = a.part + (size_t)ksi * 16 * a.n_max;
+#pragma unroll
+    for (int t = 0; t < kMfmaRT; ++t) {
+        const int u = u0 + 16 * t + col;
+        if (u < a.n_max) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = 4 * kq + i;
+                if (b < a.B) P[(size_t)b * a.n_max + u] = acc[t][i];
+            }
+        }
+    }
+}
+
 struct MfmaEpi {
     const float* part;
     int ks, B, n_max;
@@ -184,8 +300,17 @@ bool rowdot_mfma_ok(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == 
 
 size_t rowdot_mfma_part_floats(int n_max) { return (size_t)kMfmaMaxKS * 16 * (n_max > 0 ? n_max : 1); }
 
+constexpr int kMfmaSPS = 48;       // k steps per wave in the unrolled kernel (d <= 32 * 48 * kMfmaMaxKS)
+
+static bool mfma_unrolled(const MfmaArgs& a) { return a.d / 32 <= kMfmaSPS * kMfmaMaxKS; }
+
 static void mfma_split(MfmaArgs& a) {
     const int nsteps = a.d / 32;
+    if (mfma_unrolled(a)) {
+        a.steps_per_split = kMfmaSPS;
+        a.ks = cdiv(nsteps, kMfmaSPS);
+        return;
+    }
     const int tiles = cdiv(a.n_max > 0 ? a.n_max : 1, 16 * kMfmaRT);
     int ks = cdiv(4096, tiles);                            // about 4096 waves in all
     ks = ks < 1 ? 1 : ks > kMfmaMaxKS ? kMfmaMaxKS : ks;
@@ -199,7 +324,10 @@ static dv_status mfma_go(MfmaArgs& a, MfmaEpi& e, hipStream_t s) {
     mfma_split(a);
     e.part = a.part; e.ks = a.ks; e.B = a.B; e.n_max = a.n_max; e.n_dev = a.n_dev;
     const int waves = cdiv(a.n_max, 16 * kMfmaRT) * a.ks;
-    hipLaunchKernelGGL(k_rowdot_mfma, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
+    if (mfma_unrolled(a))
+        hipLaunchKernelGGL(k_rowdot_mfma_u<kMfmaSPS>, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_rowdot_mfma, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
     hipLaunchKernelGGL(k_rowdot_mfma_epi, dim3(cdiv((long)a.B * a.n_max, kBlock)), dim3(kBlock), 0, s, a, e);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
