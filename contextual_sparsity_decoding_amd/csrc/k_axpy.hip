@@ -67,14 +67,19 @@ struct AxpyArgs {
 // Coefficient of row u = s * dh + e for batch row b: the attention output
 // o[b][s][e] = sum_c 2^(m_c - M) acc_c[e] / sum_c 2^(m_c - M) l_c over the
 // splits c with l_c > 0 (log2-domain partials).  Wave q merges its quarter
-// of the splits with a running maximum; the quarters are merged in order.
+// of the splits with a running maximum per batch row; the quarters are
+// merged in order.  A round of loads takes CB splits of every batch row
+// (one round trip for all of them, not one per batch row).
 // after_loads() runs once per wave, right after the first round of partial
 // loads is issued (every lane loads; lanes past the live rows or batch rows
 // read row 0 and discard it), so loads issued there queue behind these.
 template <int NB, typename AfterLoads>
 __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, float* s_cf,
                                           float (*s_q)[kRowsPerGroup][NB][3], AfterLoads&& after_loads) {
-    constexpr int CB = 20;                         // splits in flight: up to 80 splits in one round of loads
+    // splits per batch row in one round: 20 for one batch row (up to 80
+    // splits a round), else about 12 of each kind of value per round (the
+    // round's values are all in registers at once)
+    constexpr int CB = NB == 1 ? 20 : (12 / NB > 0 ? 12 / NB : 1);
     const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
     const int dh = a.blk, ns = a.num_splits;
     const int n_sel = a.rows / dh;
@@ -83,48 +88,58 @@ __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, 
     const int s = u / dh, e = u % dh;
     const int per = (ns + 3) / 4;
     const int c0 = q * per, c1 = min(ns, c0 + per);
-    bool issued = false;
+    const size_t bstride = (size_t)n_sel * ns * (dh + 2);       // one batch row of partials
+    const float* P0 = a.apart + ((size_t)s * ns) * (dh + 2);
+    float m[NB], l[NB], num[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        float m = -INFINITY, l = 0.f, num = 0.f;
-        const bool act = b < a.B && ok;
-        {
-            const float* P = a.apart + ((size_t)((b < a.B ? b : 0) * n_sel + s) * ns) * (dh + 2);
-            for (int cb = c0; cb < c1; cb += CB) {     // uniform over the wave
-                float mc[CB], lc[CB], ac[CB];
+        m[b] = -INFINITY;
+        l[b] = 0.f;
+        num[b] = 0.f;
+    }
+    bool issued = false;
+    for (int cb = c0; cb < c1; cb += CB) {             // uniform over the wave
+        float mc[NB][CB], lc[NB][CB], ac[NB][CB];
 #pragma unroll
-                for (int i = 0; i < CB; ++i) {
-                    const bool in = cb + i < c1;
-                    const float* pc = P + (size_t)(in ? cb + i : c0) * (dh + 2);
-                    mc[i] = pc[dh];
-                    lc[i] = in ? pc[dh + 1] : 0.f;
-                    ac[i] = pc[e];
-                }
-                if (!issued) {
-                    issued = true;
-                    asm volatile("" ::: "memory");
-                    after_loads();
-                    asm volatile("" ::: "memory");
-                }
-                if (!act) continue;
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int i = 0; i < CB; ++i) {
-                    if (!(lc[i] > 0.f)) continue;
-                    const float M = fmaxf(m, mc[i]);
-                    const float sa = exp2f(m - M), sb = exp2f(mc[i] - M);
-                    num = num * sa + ac[i] * sb;
-                    l = l * sa + lc[i] * sb;
-                    m = M;
-                }
+            for (int i = 0; i < CB; ++i) {
+                const bool in = cb + i < c1;
+                const float* pc = P0 + (size_t)(b < a.B ? b : 0) * bstride + (size_t)(in ? cb + i : c0) * (dh + 2);
+                mc[b][i] = pc[dh];
+                lc[b][i] = in ? pc[dh + 1] : 0.f;
+                ac[b][i] = pc[e];
+            }
+        if (!issued) {
+            issued = true;
+            asm volatile("" ::: "memory");
+            after_loads();
+            asm volatile("" ::: "memory");
+        }
+        if (!ok) continue;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b >= a.B) continue;
+#pragma unroll
+            for (int i = 0; i < CB; ++i) {
+                if (!(lc[b][i] > 0.f)) continue;
+                const float M = fmaxf(m[b], mc[b][i]);
+                const float sa = exp2f(m[b] - M), sb = exp2f(mc[b][i] - M);
+                num[b] = num[b] * sa + ac[b][i] * sb;
+                l[b] = l[b] * sa + lc[b][i] * sb;
+                m[b] = M;
             }
         }
-        if (!issued) {                                 // a wave without splits
-            issued = true;
-            after_loads();
-        }
-        s_q[q][t][b][0] = m;
-        s_q[q][t][b][1] = l;
-        s_q[q][t][b][2] = num;
+    }
+    if (!issued) {                                     // a wave without splits
+        issued = true;
+        after_loads();
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        s_q[q][t][b][0] = m[b];
+        s_q[q][t][b][1] = l[b];
+        s_q[q][t][b][2] = num[b];
     }
     __syncthreads();
     if (threadIdx.x < kRowsPerGroup) {
