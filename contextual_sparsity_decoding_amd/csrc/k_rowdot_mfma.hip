@@ -1,5 +1,6 @@
 // Batched row-dot products on the matrix cores: for a batch of 8-16 decode
-// rows every fp16 weight row meets 8-16 inputs, so sparse fc1 over the
+// rows (or 4-7 whose inputs are too wide for LDS) every fp16 weight row meets
+// 4-16 inputs, so sparse fc1 over the
 // batch's union of neurons (DejaVu §5.2 / App. C.1) and the Q/K/V
 // projections become a skinny dense contraction
 //     out[b][u] = sum_k y[b][k] * W[row(u)][k]        (b < B <= 16)
@@ -296,7 +297,15 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi 
 namespace dvh {
 using namespace dv;
 
-bool rowdot_mfma_ok(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == DV_F16 && d % 32 == 0; }
+// Batches of 8-16, and batches of 4-7 whose inputs do not fit in LDS (the
+// vector paths would read them from global memory for every row; the
+// matrix cores take them as a padded 16-row operand).  At a batch of 2 the
+// vector paths measured faster over a union of neurons (OPT-175B width:
+// 91 against 84 tokens/s), at 4 slower (104 against 138).
+bool rowdot_mfma_ok(int B, int d, int wdt) {
+    const bool wide = B >= 4 && (size_t)B * d * sizeof(float) > kYLdsMax;
+    return (B >= 8 || wide) && B <= 16 && wdt == DV_F16 && d % 32 == 0;
+}
 
 size_t rowdot_mfma_part_floats(int n_max) { return (size_t)kMfmaMaxKS * 16 * (n_max > 0 ? n_max : 1); }
 

@@ -57,8 +57,8 @@ C4 = configs.OPT175B_SHARE
 B16 = 16
 
 
-def _c4_union(seed):
-    s = synth.tied_scores(B16, C4.dims.N, seed)
+def _c4_union(seed, B=B16):
+    s = synth.tied_scores(B, C4.dims.N, seed)
     return s, ref.union_sorted(ref.topk_rows(s, C4.k_neurons))
 
 
@@ -78,27 +78,29 @@ def test_opt175b_topk_and_union_b16(dvlib):
     print(f"union of 16 sets of {k}: {len(U)} of {C4.dims.N} neurons")
 
 
-def test_opt175b_mlp_over_union_b16(dvlib):
-    """fc1 over the union for 16 rows, fc2 skipping neurons that are zero in
-    every row, at d=12288, N=49152."""
+@pytest.mark.parametrize("B", [B16, 4])
+def test_opt175b_mlp_over_union(dvlib, B):
+    """fc1 over the union for B rows (on the matrix cores: 16 rows, or 4 rows
+    of 12288 inputs that do not fit in LDS), fc2 skipping neurons that are
+    zero in every row, at d=12288, N=49152."""
     d, N = C4.dims.d, C4.dims.N
-    _, U = _c4_union(175)
+    _, U = _c4_union(175, B)
     U = U.astype(np.int32)
     W = synth.mlp_weights(C4.dims, 175)
-    y = synth.layer_inputs(d, 1, B16, 175)[0]
-    res = synth.normal((B16, d), 176, 0, "x")
+    y = synth.layer_inputs(d, 1, B, 175)[0]
+    res = synth.normal((B, d), 176, 0, "x")
     Wd = {n: dev(v) for n, v in W.items() if n in ("w1_t", "b1", "w2_t", "b2")}
-    out = torch.empty(B16, d, device="cuda")
-    a = torch.empty(B16, len(U), device="cuda")
+    out = torch.empty(B, d, device="cuda")
+    a = torch.empty(B, len(U), device="cuda")
     rows = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws = dvlib.workspace(dvlib.dv_sparse_mlp_workspace_bytes(B16, d, len(U), dvlib.DV_F16))
+    ws = dvlib.workspace(dvlib.dv_sparse_mlp_workspace_bytes(B, d, len(U), dvlib.DV_F16))
     dvlib.dv_sparse_mlp(dev(y), Wd["w1_t"], Wd["b1"], Wd["w2_t"], Wd["b2"], dev(U), len(U), out, ws,
                         residual=dev(res), act_out=a, fc2_rows=rows, flags=dvlib.DV_SKIP_NONPOS_FC2)
     want, wa = ref.sparse_mlp(y, W["w1_t"], W["b1"], W["w2_t"], W["b2"], U, residual=res, skip_nonpos=True)
     check_close(host(a), wa, "f16", "fc1 over the union")
     e = check_close(host(out), want, "f16", "mlp out")
     assert int(host(rows)[0]) == int(np.sum(np.any(wa > 0, axis=0)))
-    print(f"opt175b-width union MLP, B=16: normwise {e:.2e}")
+    print(f"opt175b-width union MLP, B={B}: normwise {e:.2e}")
 
 
 def test_opt175b_attention_b16(dvlib):
