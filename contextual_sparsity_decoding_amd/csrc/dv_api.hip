@@ -868,16 +868,23 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
     else
         TRY(launch_qkv(L.y, B, d, h, dh, head_idx, n_sel, w->w_qkv_t, w->b_qkv, c->wdt, L.q, &kvs, false, s));
     timed_end(DV_KERNEL_QKV, s);
-    // split-K partials go straight into the output projection, which merges them per row
+    // split-K partials go straight into the output projection, which merges
+    // them per row; for the matrix cores they are merged into o first
+    const bool o_first = axpy_mfma_supported(B, d, c->wdt);
     int splits = 0;
     timed_begin(DV_KERNEL_ATTN, s);
-    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, nullptr, L.apart,
-                      fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s, &splits));
+    TRY(launch_splitk(L.q, B, dh, head_idx, n_sel, &view, kv.pos_dev, 1, c->scale, 0, o_first ? L.o : nullptr,
+                      L.apart, fill ? kvs.valid_upto : nullptr, kv.pos, kv.pos_dev, s, &splits));
     timed_end(DV_KERNEL_ATTN, s);
     {
         AxpyCall ac{};
         ac.w = w->w_o_t; ac.wdt = c->wdt; ac.d = d; ac.w_rows = h * dh; ac.rows = n_sel * dh; ac.idx = head_idx;
-        ac.blk = dh; ac.apart = L.apart; ac.num_splits = splits; ac.B = B; ac.bias = w->b_o; ac.residual = x_in;
+        ac.blk = dh; ac.B = B; ac.bias = w->b_o; ac.residual = x_in;
+        if (o_first) {
+            ac.coef = L.o; ac.coef_stride = n_sel * dh;
+        } else {
+            ac.apart = L.apart; ac.num_splits = splits;
+        }
         ac.out = L.hres; ac.partial = L.xpart; ac.timed = DV_KERNEL_OUT;
         TRY(launch_axpy(ac, s));
     }

@@ -317,6 +317,8 @@ struct AxpyCall {
     int timed;                // DV_KERNEL_* role of the main launch for dv_time_launches, or 0
 };
 dv_status launch_axpy(const AxpyCall& c, hipStream_t s);
+// batches whose gather-AXPY runs on the matrix cores when its coefficients are in memory
+bool axpy_mfma_supported(int B, int d, int wdt);
 bool qkv_supported(int B, int d, int wdt);
 dv_status launch_qkv(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,
                      const void* w, const void* bias, int wdt, float* q, const dv_kv_state* kv, bool mark_valid,

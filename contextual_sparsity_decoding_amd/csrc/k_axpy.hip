@@ -18,8 +18,15 @@
 // workgroup merges a head's splits (running max, rescaled sums) for its own
 // rows, so no separate combine pass runs.
 //
+// Batches of 8-16 run on the matrix cores instead (k_axpy_mfma): with 16
+// FMAs per weight element the vector ALUs fall far behind HBM, and a partial
+// of B x d floats per 64 rows would cost as many bytes as the weights, so a
+// workgroup there covers 256 rows.
+//
 // k_axpy_finalize then adds the partials in a fixed order, plus bias and
-// residual.  Results do not depend on scheduling.
+// residual, over the groups that hold live rows only (a device-side row count
+// may leave the last groups empty; they write nothing).  Results do not
+// depend on scheduling.
 //
 // In a look-ahead decode layer (DejaVu §4.3) these launches also carry the
 // next layer's neuron selection (topk_split.h): one more column of
@@ -161,44 +168,15 @@ __device__ __forceinline__ void attn_coef(const AxpyArgs& a, int r0, int nlive, 
     }
 }
 
-template <typename T, int NB, bool ATTN>
-__global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
-    constexpr int E = Vec<T>::E;
-    constexpr int SW = kWave * E;                  // columns per slice
-    constexpr int NBC = NB < 4 ? NB : 4;           // batch rows per LDS reduction round
-    constexpr int NQ = ATTN ? NB : 1;
-    constexpr int RED = 3 * NBC * SW, QF = ATTN ? 4 * kRowsPerGroup * NQ * 3 : 0;
-    __shared__ int s_row[kRowsPerGroup];
-    __shared__ float s_cf[kRowsPerGroup * NB];
-    __shared__ float shbuf[RED > QF ? RED : QF];   // split merging, then the wave reduction
-    __shared__ unsigned tot[20];
-    auto red = reinterpret_cast<float (*)[NBC][SW]>(shbuf);
-    auto s_q = reinterpret_cast<float (*)[kRowsPerGroup][NQ][3]>(shbuf);
-    const T* W = (const T*)a.w;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int slice = blockIdx.x, g = blockIdx.y;
-    if constexpr (NB == 1) {
-        static_assert(kBlock == 256, "a selection slice takes one 256-thread workgroup");
-        if (a.tk_s && slice == (int)gridDim.x - 1) {   // the extra column
-            if (g * kTopkSlice < a.tk_n) {
-                if constexpr (ATTN) {
-                    __shared__ unsigned tk_lds[4096];
-                    topk_hist_slice(a.tk_s, a.tk_n, g, tk_lds, a.tk_hist, a.tk_keys);
-                } else {
-                    topk_emit_slice(a.tk_keys, a.tk_n, a.tk_k, g, a.tk_thr, tot, a.tk_idx);
-                }
-            }
-            return;
-        }
-    }
-    if (g >= a.n_groups) return;                   // the extra column may be taller than the groups
-    const int col = slice * SW + lane * E;
-    const bool colok = col < a.d;
-    const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
-    const int r0 = g * kRowsPerGroup;
-
-    // ---- this group's rows (and coefficients read from memory), in order
-    int nlive;
+// This group's rows (and coefficients read from memory), in order, into
+// s_row / s_cf; returns the live rows.  The output projection uses every
+// selected row (an index outside W reads nothing: row -1); the second MLP
+// layer compacts the rows, dropping those whose coefficients are all zero
+// when asked.  Ends with a barrier.
+template <int NB, bool ATTN>
+__device__ __forceinline__ int axpy_group_rows(const AxpyArgs& a, int slice, int r0, int rows, int* s_row, float* s_cf,
+                                               unsigned* tot) {
+    int nlive = 0;
     if (ATTN) {
         // every selected row is used; an index outside W reads nothing
         nlive = max(0, min(kRowsPerGroup, rows - r0));
@@ -250,6 +228,48 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
     }
     __syncthreads();
     if (!ATTN) nlive = (int)tot[0];
+    return nlive;
+}
+
+template <typename T, int NB, bool ATTN>
+__global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
+    constexpr int E = Vec<T>::E;
+    constexpr int SW = kWave * E;                  // columns per slice
+    constexpr int NBC = NB < 4 ? NB : 4;           // batch rows per LDS reduction round
+    constexpr int NQ = ATTN ? NB : 1;
+    constexpr int RED = 3 * NBC * SW, QF = ATTN ? 4 * kRowsPerGroup * NQ * 3 : 0;
+    __shared__ int s_row[kRowsPerGroup];
+    __shared__ float s_cf[kRowsPerGroup * NB];
+    __shared__ float shbuf[RED > QF ? RED : QF];   // split merging, then the wave reduction
+    __shared__ unsigned tot[20];
+    auto red = reinterpret_cast<float (*)[NBC][SW]>(shbuf);
+    auto s_q = reinterpret_cast<float (*)[kRowsPerGroup][NQ][3]>(shbuf);
+    const T* W = (const T*)a.w;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slice = blockIdx.x, g = blockIdx.y;
+    if constexpr (NB == 1) {
+        static_assert(kBlock == 256, "a selection slice takes one 256-thread workgroup");
+        if (a.tk_s && slice == (int)gridDim.x - 1) {   // the extra column
+            if (g * kTopkSlice < a.tk_n) {
+                if constexpr (ATTN) {
+                    __shared__ unsigned tk_lds[4096];
+                    topk_hist_slice(a.tk_s, a.tk_n, g, tk_lds, a.tk_hist, a.tk_keys);
+                } else {
+                    topk_emit_slice(a.tk_keys, a.tk_n, a.tk_k, g, a.tk_thr, tot, a.tk_idx);
+                }
+            }
+            return;
+        }
+    }
+    if (g >= a.n_groups) return;                   // the extra column may be taller than the groups
+    const int col = slice * SW + lane * E;
+    const bool colok = col < a.d;
+    const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
+    const int r0 = g * kRowsPerGroup;
+    if (r0 >= rows) return;                        // past the live rows: the finalize stops before this group
+
+    // ---- this group's rows (and coefficients read from memory), in order
+    const int nlive = axpy_group_rows<NB, ATTN>(a, slice, r0, rows, s_row, s_cf, tot);
 
     // ---- this wave's rows wv, wv + 4, ...: for the output projection the
     // first PF go out right behind the split-K partials' loads (which are
@@ -333,6 +353,162 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 
 }
 
+// The gather-AXPY of a batch of 8-16 on the matrix cores (fp16 weights,
+// coefficients read from memory):
+//     partial[p][b][c] = sum over the part's rows u of coef[b][u] W[row(u)][c]
+// as D = A B with v_mfma_f32_16x16x32_f16, A = the coefficients (16 batch
+// rows x 32 rows of W, in fp16 hi + lo so that they keep about 22 bits) and
+// B = those 32 rows of W x 16 columns.  Lane l supplies A row l % 16 and B
+// column l % 16, both at rows 8 (l / 16) .. +7 of the step; D's register i
+// holds batch row 4 (l / 16) + i, column l % 16.
+//
+// A workgroup takes one 512-column slice of a part of kAxG groups of 64 rows.
+// Wave w first compacts group w's rows as the vector kernel does (dropping
+// rows whose coefficients are all zero when asked) and writes their
+// coefficients straight into the A operands.  Then each wave takes 128
+// columns over all of the part's rows, 32 a step, with the weight loads of
+// the next kAxPF steps in flight.  The B operand wants 8 rows of one column
+// per lane while a row of W is contiguous along columns, so a step's 32 x 128
+// tile goes through the wave's own LDS region: 16-byte loads (lane l: row
+// 4 i + l / 16, columns 8 (l % 16) .. +7), read back 2 bytes at a time.  Row
+// r sits at position (r % 8) * 4 + r / 8 with a 288-byte stride, so that
+// the 4 lane groups' reads (rows 8 apart) fall on disjoint banks.  One
+// partial per part, not per group, keeps the partial sums (B x d floats a
+// part, written and read back once) a quarter of what 64-row groups write.
+typedef _Float16 f16x8a __attribute__((ext_vector_type(8)));
+constexpr int kAxKS = 32;                      // rows per matrix-core step
+constexpr int kAxWC = 128;                     // columns per wave (8 tiles of 16)
+constexpr int kAxRS = 288;                     // LDS bytes per tile row (256 + 32)
+constexpr int kAxTile = kAxKS * kAxRS;         // one wave's tile
+constexpr int kAxSlice = 4 * kAxWC;            // columns per workgroup
+constexpr int kAxG = kBlock / kWave;           // 64-row groups per part (one per wave in the compaction)
+constexpr int kAxSteps = kAxG * kRowsPerGroup / kAxKS;
+constexpr int kAxPF = 2;                       // steps of weight loads in flight
+
+template <int NB>
+__global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
+    static_assert(NB >= 8 && NB <= 16 && kRowsPerGroup == kWave && kRowsPerGroup % kAxKS == 0, "batches of 8-16");
+    __shared__ int s_row[kAxG][kRowsPerGroup];
+    __shared__ int s_n[kAxG];
+    __shared__ __align__(16) half_t aop[kAxSteps][2][16][kAxKS];     // [step][hi, lo][batch row][row of the step]
+    __shared__ __align__(16) unsigned char tiles[kAxG * kAxTile];
+    const half_t* W = (const half_t*)a.w;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int slice = blockIdx.x, part = blockIdx.y;
+    const int rows = a.n_rows_dev ? min(*a.n_rows_dev, a.rows) : a.rows;
+    const int r0 = part * kAxG * kRowsPerGroup;
+    if (r0 >= rows) return;                        // past the live rows: the finalize stops before this part
+    {   // ---- wave wv compacts group wv's rows: live ones to slots 0 .. nl-1 in order
+        const int u = r0 + wv * kRowsPerGroup + lane;
+        bool live = false;
+        int row = 0;
+        float cf[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) cf[b] = 0.f;
+        if (u < rows) {
+            row = a.idx ? a.idx[u / a.blk] * a.blk + u % a.blk : u;
+            bool any = false;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                cf[b] = b < a.B ? a.coef[(size_t)b * a.coef_stride + u] : 0.f;
+                if (a.thresh) cf[b] = fabsf(cf[b]) > a.thr ? cf[b] : 0.f;
+                any |= cf[b] != 0.f;
+            }
+            live = (unsigned)row < (unsigned)a.w_rows && (any || !a.skip_zero);   // an index outside W selects nothing
+        }
+        const unsigned lv = live ? 1u : 0u;
+        const unsigned incl = wave_incl_scan(lv);
+        const int nl = __builtin_amdgcn_readlane((int)incl, 63);
+        // live lanes take slots 0 .. nl-1, the others the rest (zero coefficients)
+        const int slot = live ? (int)incl - 1 : nl + lane - (int)incl;
+        if (live) s_row[wv][slot] = row;
+        const int st = wv * (kRowsPerGroup / kAxKS) + slot / kAxKS, k = slot % kAxKS;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const float c = (live && b < NB) ? cf[b < NB ? b : 0] : 0.f;
+            const half_t hi = (half_t)c;
+            aop[st][0][b][k] = hi;
+            aop[st][1][b][k] = (half_t)(c - (float)hi);
+        }
+        if (lane == 0) {
+            s_n[wv] = nl;
+            if (a.rows_read && slice == 0 && nl > 0) atomicAdd(a.rows_read, nl);
+        }
+    }
+    __syncthreads();
+    // ---- this wave's 128 columns over the part's rows
+    const int c0 = slice * kAxSlice + wv * kAxWC;  // d % 512 == 0
+    int nlv[kAxG];
+#pragma unroll
+    for (int g = 0; g < kAxG; ++g) nlv[g] = __builtin_amdgcn_readfirstlane(s_n[g]);
+    // a step's loads are unmasked: rows past a group's live ones read its last
+    // live row (or row 0), their coefficients being zero
+    u32x4 w[kAxPF][8];
+    auto load_step = [&](int st, int slot) {
+        const int g = st / (kRowsPerGroup / kAxKS), kb = (st % (kRowsPerGroup / kAxKS)) * kAxKS;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = kb + 4 * i + (lane >> 4);
+            const int rr = nlv[g] > 0 ? s_row[g][k < nlv[g] ? k : nlv[g] - 1] : 0;
+            w[slot][i] = ld16_stream(W + (size_t)rr * a.d + c0 + 8 * (lane & 15));
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < kAxPF; ++p) {
+        load_step(p, p);
+        asm volatile("" ::: "memory");
+    }
+    unsigned char* tile = tiles + wv * kAxTile;
+    f32x4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < kAxSteps; ++st) {
+        const int slot = st % kAxPF;
+        const int g = st / (kRowsPerGroup / kAxKS), kb = (st % (kRowsPerGroup / kAxKS)) * kAxKS;
+        if (kb < nlv[g]) {                         // uniform: a step with a live row
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {          // row r = 4 i + l / 16 of the step
+                const int r = 4 * i + (lane >> 4);
+                *reinterpret_cast<u32x4*>(tile + ((r & 7) * 4 + (r >> 3)) * kAxRS + (lane & 15) * 16) = w[slot][i];
+            }
+            const f16x8a ahi = *reinterpret_cast<const f16x8a*>(&aop[st][0][lane & 15][8 * (lane >> 4)]);
+            const f16x8a alo = *reinterpret_cast<const f16x8a*>(&aop[st][1][lane & 15][8 * (lane >> 4)]);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                f16x8a bop;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)        // row 8 (l / 16) + j, column 16 nt + l % 16
+                    bop[j] = *reinterpret_cast<const half_t*>(tile + (j * 4 + (lane >> 4)) * kAxRS +
+                                                              (nt * 16 + (lane & 15)) * 2);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bop, acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bop, acc[nt], 0, 0, 0);
+            }
+        }
+        if (st + kAxPF < kAxSteps) {               // the slot just consumed takes step st + PF
+            asm volatile("" ::: "memory");
+            load_step(st + kAxPF, slot);
+            asm volatile("" ::: "memory");
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const int col = c0 + nt * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = 4 * (lane >> 4) + i;
+            if (b < a.B) a.partial[((size_t)part * a.B + b) * a.d + col] = acc[nt][i];
+        }
+    }
+}
+
+// The rows a gather-AXPY covered, when a device-side count cut them short:
+// its parts of rows_per_part rows past min(*n_rows_dev, rows) hold nothing.
+struct FinLive {
+    const int32_t* n_rows_dev = nullptr;
+    int rows = 0, rows_per_part = 1;
+};
+
 // out[b][c] = residual[b][c] + bias[c] + sum_g partial[g][b][c].  A block
 // covers 64 float4 columns of one batch row; its NT/64 waves each add a
 // contiguous share of the groups (all loads of a share in flight together),
@@ -344,10 +520,12 @@ template <typename T, int NT = kBlock>
 __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ partial, int n_groups, int B, int d,
                                                     const void* bias, const float* __restrict__ residual,
                                                     float* __restrict__ out, int32_t* advance,
-                                                    const FinEpi& epi = FinEpi{}) {
+                                                    const FinEpi& epi = FinEpi{}, const FinLive& lv = FinLive{}) {
     constexpr int NW = NT / kWave;
     constexpr int MAXQ = 16;                      // groups per share held in flight
     __shared__ f32x4 red[NW - 1][64];
+    if (lv.n_rows_dev)                            // parts past the live rows were never written
+        n_groups = min(n_groups, (max(0, min(*lv.n_rows_dev, lv.rows)) + lv.rows_per_part - 1) / lv.rows_per_part);
     const int b = blockIdx.y;
     const int c4 = blockIdx.x * 64 + (threadIdx.x & 63);
     const int q = threadIdx.x >> 6;
@@ -410,8 +588,9 @@ __device__ __forceinline__ void axpy_finalize_block(const float* __restrict__ pa
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_axpy_finalize(const float* __restrict__ partial, int n_groups, int B, int d,
                                                           const void* bias, const float* __restrict__ residual,
-                                                          float* __restrict__ out, int32_t* advance, FinEpi epi) {
-    axpy_finalize_block<T>(partial, n_groups, B, d, bias, residual, out, advance, epi);
+                                                          float* __restrict__ out, int32_t* advance, FinEpi epi,
+                                                          FinLive lv) {
+    axpy_finalize_block<T>(partial, n_groups, B, d, bias, residual, out, advance, epi, lv);
 }
 
 // The finalize by 1024-thread workgroups, with one more workgroup (the last
@@ -428,7 +607,8 @@ struct FinThr {
 template <typename T>
 __global__ __launch_bounds__(kFinThrThreads) void k_axpy_finalize_thr(const float* __restrict__ partial, int n_groups, int B,
                                                               int d, const void* bias, const float* __restrict__ residual,
-                                                              float* __restrict__ out, int32_t* advance, FinThr f) {
+                                                              float* __restrict__ out, int32_t* advance, FinThr f,
+                                                              FinLive lv) {
     if (blockIdx.x == gridDim.x - 1) {
         if (blockIdx.y == 0) {
             __shared__ unsigned lds[kTopkThrWords];
@@ -436,7 +616,7 @@ __global__ __launch_bounds__(kFinThrThreads) void k_axpy_finalize_thr(const floa
         }
         return;
     }
-    axpy_finalize_block<T, kFinThrThreads>(partial, n_groups, B, d, bias, residual, out, advance);
+    axpy_finalize_block<T, kFinThrThreads>(partial, n_groups, B, d, bias, residual, out, advance, FinEpi{}, lv);
 }
 
 }  // namespace dv
@@ -457,6 +637,18 @@ AxpyPlan axpy_plan(int d, int rows, int wdt) {
 
 size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_groups * B * d; }
 
+// Batches of 8-16 with fp16 weights, 512-column slices and coefficients in
+// memory take the matrix cores (an output projection first merges its
+// split-K partials into the attention output).
+bool axpy_mfma_supported(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == DV_F16 && d % kAxSlice == 0; }
+
+static bool axpy_mfma_ok(const AxpyCall& c) { return axpy_mfma_supported(c.B, c.d, c.wdt) && !c.apart && !c.sel; }
+
+template <int NB>
+static void axpy_mfma_go(const AxpyArgs& a, int n_parts, hipStream_t s) {
+    DV_LAUNCH((k_axpy_mfma<NB>), dim3(a.d / kAxSlice, n_parts), dim3(kBlock), 0, s, a);
+}
+
 template <typename T, int NB>
 static void axpy_go(const AxpyArgs& a, int n_slices, hipStream_t s) {
     const int hs = a.tk_s ? cdiv(a.tk_n, kTopkSlice) : 0;
@@ -472,10 +664,10 @@ dv_status launch_axpy_finalize(const float* partial, int n_groups, int B, int d,
     const dim3 fg(cdiv(d / 4, 64), B);
     if (bias_wdt == DV_F16)
         hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, partial, n_groups, B, d, bias, residual,
-                           out, nullptr, FinEpi{});
+                           out, nullptr, FinEpi{}, FinLive{});
     else
         hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, partial, n_groups, B, d, bias, residual,
-                           out, nullptr, FinEpi{});
+                           out, nullptr, FinEpi{}, FinLive{});
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DV_OK : fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
 }
@@ -503,9 +695,18 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
         if (c.wdt == DV_F16) axpy_go<half_t, NB>(a, p.n_slices, s);            \
         else axpy_go<float, NB>(a, p.n_slices, s);                             \
         break;
+    const bool mf = axpy_mfma_ok(c);
+    const int n_parts = mf ? cdiv(p.n_groups, kAxG) : p.n_groups;
+    FinLive lv;
+    lv.n_rows_dev = c.n_rows_dev; lv.rows = c.rows; lv.rows_per_part = mf ? kAxG * kRowsPerGroup : kRowsPerGroup;
     timed_begin(c.timed, s);
-    switch (nb) {
-        DV_AXPY(1) DV_AXPY(2) DV_AXPY(4) DV_AXPY(8) DV_AXPY(16)
+    if (mf) {
+        if (nb == 8) axpy_mfma_go<8>(a, n_parts, s);
+        else axpy_mfma_go<16>(a, n_parts, s);
+    } else {
+        switch (nb) {
+            DV_AXPY(1) DV_AXPY(2) DV_AXPY(4) DV_AXPY(8) DV_AXPY(16)
+        }
     }
 #undef DV_AXPY
     timed_end(c.timed, s);
@@ -514,17 +715,17 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
         const FinThr f{c.sel->keys, c.sel->n, c.sel->k, c.sel->hist, (TopkThreshold*)c.sel->thr};
         const dim3 fg2(fg.x + 1, fg.y);
         if (c.wdt == DV_F16)
-            hipLaunchKernelGGL(k_axpy_finalize_thr<half_t>, fg2, dim3(kFinThrThreads), 0, s, c.partial, p.n_groups, c.B,
-                               c.d, c.bias, c.residual, c.out, c.advance, f);
+            hipLaunchKernelGGL(k_axpy_finalize_thr<half_t>, fg2, dim3(kFinThrThreads), 0, s, c.partial, n_parts, c.B,
+                               c.d, c.bias, c.residual, c.out, c.advance, f, lv);
         else
-            hipLaunchKernelGGL(k_axpy_finalize_thr<float>, fg2, dim3(kFinThrThreads), 0, s, c.partial, p.n_groups, c.B,
-                               c.d, c.bias, c.residual, c.out, c.advance, f);
+            hipLaunchKernelGGL(k_axpy_finalize_thr<float>, fg2, dim3(kFinThrThreads), 0, s, c.partial, n_parts, c.B,
+                               c.d, c.bias, c.residual, c.out, c.advance, f, lv);
     } else if (c.wdt == DV_F16)
-        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
-                           c.residual, c.out, c.advance, c.epi);
+        hipLaunchKernelGGL(k_axpy_finalize<half_t>, fg, dim3(kBlock), 0, s, c.partial, n_parts, c.B, c.d, c.bias,
+                           c.residual, c.out, c.advance, c.epi, lv);
     else
-        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, c.partial, p.n_groups, c.B, c.d, c.bias,
-                           c.residual, c.out, c.advance, c.epi);
+        hipLaunchKernelGGL(k_axpy_finalize<float>, fg, dim3(kBlock), 0, s, c.partial, n_parts, c.B, c.d, c.bias,
+                           c.residual, c.out, c.advance, c.epi, lv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DV_OK;

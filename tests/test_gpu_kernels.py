@@ -277,7 +277,7 @@ def test_qkv_without_hole_fill(dvlib):
     assert np.all(host(Kd)[0, :, 5:8] == 0)          # skipped slots untouched
 
 
-@pytest.mark.parametrize("B,n_sel,wdt", [(1, 20, "f16"), (2, 3, "f16"), (1, 4, "f32")])
+@pytest.mark.parametrize("B,n_sel,wdt", [(1, 20, "f16"), (2, 3, "f16"), (1, 4, "f32"), (8, 20, "f16"), (13, 20, "f16")])
 def test_out_proj(dvlib, B, n_sel, wdt):
     d, h, dh = 5120 if n_sel == 20 else 320, 40 if n_sel == 20 else 6, 128
     W, _, _ = _attn_setup(d, h, dh, 4, 0, seed=n_sel, wdt=wdt)
