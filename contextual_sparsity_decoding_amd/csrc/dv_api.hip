@@ -486,7 +486,10 @@ static LayerWs layer_ws(void* ws, const dv_decode_cfg* c, int max_len) {
     w.khist = cv.take<unsigned>(4096);
     w.kkeys = cv.take<uint32_t>((size_t)c->N);
     w.kthr = cv.take<unsigned>(4);
-    const size_t mp = rowdot_mfma_part_floats(nmax > 3 * nsel * dh ? nmax : 3 * nsel * dh);
+    size_t mp = rowdot_mfma_part_floats(nmax > 3 * nsel * dh ? nmax : 3 * nsel * dh);
+    const size_t pp[4] = {rowdot_mfma_rows_part_floats(c->r_attn, d), rowdot_mfma_rows_part_floats(h, c->r_attn),
+                          rowdot_mfma_rows_part_floats(c->r_mlp, d), rowdot_mfma_rows_part_floats(c->N, c->r_mlp)};
+    for (size_t q : pp) mp = q > mp ? q : mp;      // the predictors' layers
     w.mpart = rowdot_mfma_ok(B, d, c->wdt) ? cv.take<float>(mp) : nullptr;
     w.bytes = align_up(cv.off, 256);
     return w;
@@ -848,7 +851,7 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
                 TRY(launch_layernorm(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, s));
         } else {
             TRY(launch_predict_ln(x_in, B, d, w->ln1_g, w->ln1_b, c->eps, L.y, w->pa1_t, c->r_attn, w->pa2_t, h,
-                                  c->wdt, c->pred_act, L.sA, L.hpart, s));
+                                  c->wdt, c->pred_act, L.sA, L.hpart, s, L.mpart));
             TRY(launch_topk(L.sA, B, h, c->k_heads, hi, s));
         }
         head_idx = hi;
@@ -894,7 +897,7 @@ static dv_status decode_one(const dv_layer_weights* w, const dv_decode_cfg* c, c
     int n_max = N;
     if (!(c->flags & DV_DENSE_MLP)) {
         TRY(launch_predict_ln(L.hres, B, d, w->ln2_g, w->ln2_b, c->eps, L.y2, w->pm1_t, c->r_mlp, w->pm2_t, N, c->wdt,
-                              c->pred_act, L.sM, L.hpart, s));
+                              c->pred_act, L.sM, L.hpart, s, L.mpart));
         if (B == 1) {
             int32_t* ni = st->neuron_idx_out ? st->neuron_idx_out : L.nidx;
             TRY(launch_topk(L.sM, 1, N, c->k_neurons, ni, s));

@@ -269,9 +269,11 @@ struct Carve {
 dv_status launch_layernorm(const float* x, int B, int d, const float* g, const float* b, float eps,
                            float* y, hipStream_t s);
 size_t pred_partials(int B, int d, int r, int wdt);
+// With mpart (rowdot_mfma_rows_part_floats of both layers) and a batch the
+// matrix cores take, both layers run there.
 dv_status launch_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t,
                          int n_out, int wdt, int act, float* scores, float* hid_part,
-                         hipStream_t s);
+                         hipStream_t s, float* mpart = nullptr);
 dv_status launch_fc1(const float* y, int B, int d, const void* w1_t, const void* b1, int wdt,
                      const int32_t* idx, int n_max, const int32_t* n_dev, int N, float* a, hipStream_t s);
 struct AxpyPlan {
@@ -330,7 +332,7 @@ dv_status launch_fc1_ln(const float* x, int d, const float* g, const float* b, f
 bool ln_fusable(int B, int d);
 dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
                             const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
-                            float* hid, hipStream_t s);
+                            float* hid, hipStream_t s, float* mpart = nullptr);
 bool pred_topk_fusable(int B, int n_out, int r);
 bool row_ln_supported(int d, int wdt);
 dv_status launch_predict_pair_ln(const float* x, int d, const float* g, const float* b, float eps, float* y_out,
@@ -368,6 +370,11 @@ dv_status sparse_mlp_call(const char* who, const float* y, int B, int d, int N, 
 // fp16 weights, d % 32 == 0; `part` holds rowdot_mfma_part_floats floats.
 bool rowdot_mfma_ok(int B, int d, int wdt);
 size_t rowdot_mfma_part_floats(int n_max);
+// out[b][j] = y[b] . W[j] (its ReLU when asked) for every row j < n_rows of W,
+// on the matrix cores; `part` holds rowdot_mfma_rows_part_floats(n_rows, d) floats
+size_t rowdot_mfma_rows_part_floats(int n_rows, int d);
+dv_status launch_rows_mfma(const float* y, int B, int d, const void* w, int n_rows, bool relu, float* out,
+                           float* part, hipStream_t s);
 dv_status launch_fc1_mfma(const float* y, int B, int d, const void* w1_t, const void* b1, const int32_t* idx,
                           int n_max, const int32_t* n_dev, int N, float* a_out, float* part, hipStream_t s);
 dv_status launch_qkv_mfma(const float* y, int B, int d, int h, int d_h, const int32_t* head_idx, int n_sel,

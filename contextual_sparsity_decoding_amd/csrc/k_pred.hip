@@ -125,7 +125,14 @@ static void scores_go(const float* hid, int B, int r, int act, const void* p2, i
 }
 
 dv_status launch_predict(const float* y, int B, int d, const void* p1_t, int r, const void* p2_t,
-                         int n_out, int wdt, int act, float* scores, float* hid, hipStream_t s) {
+                         int n_out, int wdt, int act, float* scores, float* hid, hipStream_t s, float* mpart) {
+    if (mpart && rowdot_mfma_ok(B, d, wdt) && rowdot_mfma_ok(B, r, wdt)) {
+        // both layers on the matrix cores; the activation is applied to the
+        // hidden layer as it is written
+        dv_status st = launch_rows_mfma(y, B, d, p1_t, r, act == DV_ACT_RELU, hid, mpart, s);
+        if (st != DV_OK) return st;
+        return launch_rows_mfma(hid, B, r, p2_t, n_out, false, scores, mpart, s);
+    }
     RowArgs a{};
     a.y = y; a.B = B; a.d = d; a.w = p1_t; a.bias = nullptr; a.idx = nullptr;
     a.n_max = r; a.n_dev = nullptr; a.w_rows = r; a.out = hid;
@@ -167,11 +174,11 @@ static dv_status predict_ln_t(const RowArgs& a, const LnArgs& ln, int ch, hipStr
 
 dv_status launch_predict_ln(const float* x, int B, int d, const float* g, const float* b, float eps, float* y_out,
                             const void* p1_t, int r, const void* p2_t, int n_out, int wdt, int act, float* scores,
-                            float* hid, hipStream_t s) {
+                            float* hid, hipStream_t s, float* mpart) {
     if (!ln_fusable(B, d) || ch_tier(d, wdt) == 0) {
         dv_status st = launch_layernorm(x, B, d, g, b, eps, y_out, s);
         if (st != DV_OK) return st;
-        return launch_predict(y_out, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, hid, s);
+        return launch_predict(y_out, B, d, p1_t, r, p2_t, n_out, wdt, act, scores, hid, s, mpart);
     }
     RowArgs a{};
     a.y = nullptr; a.B = 1; a.d = d; a.w = p1_t; a.n_max = r; a.w_rows = r; a.out = hid;

@@ -30,7 +30,7 @@ typedef _Float16 f16x8m __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaRT = 4;          // 16-row tiles per wave
 constexpr int kMfmaPF = 4;          // k-steps of weight loads in flight
-constexpr int kMfmaMaxKS = 8;
+constexpr int kMfmaMaxKS = 16;
 
 struct MfmaArgs {
     const float* y;           // [B][d]
@@ -136,22 +136,28 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma(MfmaArgs a) {
     }
 }
 
-// The same contraction with each wave's k range a fixed SPS steps (the last
-// range of a row may be shorter), unrolled in full: with no loop the
-// compiler's waits count the loads of each slot exactly (in the loop above
-// its wait for the loop-carried slots falls back to every load).  Every
-// small load goes out before any is used, and the weight and input loads
-// are unmasked (a masked load, or a value merged with a default, makes the
-// next use wait for every load): a row not selected reads row 0 and a lane
-// past the batch row 0's inputs, both masked where used; a step past the
-// range reads this lane's inputs of the range's last step, never used.
+// The same contraction by workgroups whose 4 waves share one k range of SPS
+// steps (the last range of a row may be shorter), each wave taking 4 tiles,
+// so that a workgroup covers 256 rows.  The range's inputs go into LDS once
+// per workgroup by DMA, ahead of the weight loads (at a batch of 16 the
+// per-wave input loads from L2 cost as much time as a third of the weight
+// loads); a row of them is padded by 16 bytes so that the 16 batch rows'
+// reads of one step fall on different banks.  The loop is unrolled in full:
+// with no loop the compiler's waits count the loads of each slot exactly.
+// The weight loads are unmasked and unconditional (a masked load, or a
+// value merged with a default, makes the next use wait for every load): a
+// row not selected reads row 0, masked where used; a step past the range
+// reads the range's last step again, never used.  They are plain loads:
+// with the streaming hint the two 64-byte halves of a line, read a few
+// instructions apart, were each fetched from HBM as a whole line (1.7x the
+// bytes).
 template <int SPS>
 __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
-    const int tile = wid / a.ks, ksi = wid % a.ks;
-    const int u0 = tile * 16 * kMfmaRT;
-    if (u0 >= a.n_max) return;                             // whole wave idle
+    constexpr int YS = SPS * 32 + 4;                      // floats per staged input row
+    __shared__ __align__(16) float yl[16 * YS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ksi = blockIdx.x % a.ks, rb = blockIdx.x / a.ks;
+    const int u0 = (rb * (kBlock / kWave) + wv) * 16 * kMfmaRT;
     const int nsteps = a.d / 32;
     const int st0 = ksi * SPS, st1 = min(nsteps, st0 + SPS);
     const int col = lane & 15, kq = lane >> 4;             // B column / A row, k block of 8
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
         for (int t = 0; t < kMfmaRT; ++t) raw[t] = key[t];
     }
     const int n = a.n_dev ? min(*a.n_dev, a.n_max) : a.n_max;
-    if (u0 >= n) return;
+    if (rb * (kBlock / kWave) * 16 * kMfmaRT >= n) return;   // the whole workgroup idle
     const half_t* rowp[kMfmaRT];
     bool rv[kMfmaRT];
 #pragma unroll
@@ -189,34 +195,50 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
         rv[t] = j >= 0;
         rowp[t] = a.w + (size_t)(j >= 0 ? j : 0) * a.d + 8 * kq;
     }
-    const bool yrow = col < a.B;                           // A row = batch row
-    const float* yp = a.y + (size_t)(yrow ? col : 0) * a.d + 8 * kq;
+    // the rows are resolved (their index loads waited for); then the inputs
+    // and the weights go out back to back
+    {   // the range's inputs, 1 KB a wave-instruction, a fixed count per wave
+        // and unconditional (a branch around one makes the compiler wait for
+        // every load): a row past the batch copies row 0 and k past a short
+        // range the range's last 4 inputs, neither ever used
+        constexpr int NKB = SPS * 32 / 256;
+        static_assert(SPS * 32 % 256 == 0 && 16 * NKB % (kBlock / kWave) == 0, "whole chunks per wave");
+        const int nk = (st1 - st0) * 32;
+        const int wu = __builtin_amdgcn_readfirstlane(wv);
+#pragma unroll
+        for (int r = 0; r < 16 * NKB / (kBlock / kWave); ++r) {
+            const int c = r * (kBlock / kWave) + wu, b = c / NKB, kc = c % NKB, e = min(kc * 256 + lane * 4, nk - 4);
+            __builtin_amdgcn_global_load_lds(a.y + (size_t)(b < a.B ? b : 0) * a.d + st0 * 32 + e,
+                                             (lds_void_t*)(yl + b * YS + kc * 256), 16, 0, 0);
+        }
+    }
+    asm volatile("" ::: "memory");
     f32x4 acc[kMfmaRT];
 #pragma unroll
     for (int t = 0; t < kMfmaRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 wr[kMfmaPF][kMfmaRT];
-    f32x4 yr[kMfmaPF][2];
     auto load_w = [&](int st, int slot) {
-        const bool in = st < st1;
-        const size_t sc = (size_t)(in ? st : st1 - 1) * 32;
+        const size_t sc = (size_t)(st < st1 ? st : st1 - 1) * 32;
 #pragma unroll
-        for (int t = 0; t < kMfmaRT; ++t)
-            wr[slot][t] = ld16_stream(in ? (const void*)(rowp[t] + sc) : (const void*)(yp + sc));
-        yr[slot][0] = *reinterpret_cast<const f32x4*>(yp + sc);
-        yr[slot][1] = *reinterpret_cast<const f32x4*>(yp + sc + 4);
+        for (int t = 0; t < kMfmaRT; ++t) wr[slot][t] = ld16(rowp[t] + sc);
     };
 #pragma unroll
     for (int p = 0; p < kMfmaPF; ++p) {                   // in slot order (the first slot's loads first)
         load_w(st0 + p, p);
-        issue_order_fence();
+        asm volatile("" ::: "memory");
     }
+    sync_after_dma<kMfmaPF * kMfmaRT>();                   // the inputs have landed; the weights may be in flight
+    if (u0 >= n) return;                                   // this wave idle (uniform)
+    const bool yrow = col < a.B;                           // A row = batch row
+    const float* yrw = yl + col * YS + 8 * kq;
 #pragma unroll
     for (int i = 0; i < SPS; ++i) {
         constexpr int PFc = kMfmaPF;
         const int p = i % PFc;
         if (st0 + i < st1) {                               // uniform over the wave
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 y0 = yrow ? yr[p][0] : zero, y1 = yrow ? yr[p][1] : zero;
+            const f32x4 y0 = yrow ? *reinterpret_cast<const f32x4*>(yrw + i * 32) : zero;
+            const f32x4 y1 = yrow ? *reinterpret_cast<const f32x4*>(yrw + i * 32 + 4) : zero;
             f16x8m hi, lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -233,9 +255,9 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
             }
         }
         if (i + PFc < SPS) {                               // the slot just consumed takes step i + PF
-            issue_order_fence();
+            asm volatile("" ::: "memory");
             load_w(st0 + i + PFc, p);
-            issue_order_fence();
+            asm volatile("" ::: "memory");
         }
     }
     float* P = a.part + (size_t)ksi * 16 * a.n_max;
@@ -256,8 +278,10 @@ struct MfmaEpi {
     const float* part;
     int ks, B, n_max;
     const int32_t* n_dev;
-    const void* bias;
-    // fc1: out[b][n_max] = relu(sum + b1[row]); Q/K/V: q and the cache
+    const void* bias;         // or NULL
+    int relu;
+    // fc1 and plain rows: out[b][n_max] = sum + bias[row], its ReLU when
+    // asked; Q/K/V: q and the cache
     float* out;
     half_t* K;
     half_t* V;
@@ -276,7 +300,8 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi 
     const int j = mfma_row(a, u, n);
     const half_t* bias = (const half_t*)e.bias;
     if (!a.qkv) {
-        e.out[(size_t)b * e.n_max + u] = j >= 0 ? fmaxf(v + (float)bias[j], 0.f) : 0.f;
+        if (j >= 0 && bias) v += (float)bias[j];
+        e.out[(size_t)b * e.n_max + u] = j < 0 ? 0.f : e.relu ? fmaxf(v, 0.f) : v;
         return;
     }
     if (j < 0) return;
@@ -309,15 +334,18 @@ bool rowdot_mfma_ok(int B, int d, int wdt) {
 
 size_t rowdot_mfma_part_floats(int n_max) { return (size_t)kMfmaMaxKS * 16 * (n_max > 0 ? n_max : 1); }
 
-constexpr int kMfmaSPS = 48;       // k steps per wave in the unrolled kernel (d <= 32 * 48 * kMfmaMaxKS)
+constexpr int kMfmaSPS = 24;       // k steps per workgroup in the unrolled kernel (d <= 32 * 24 * kMfmaMaxKS)
+
+constexpr int kMfmaSPSShort = 8;   // rows of at most 256 (a predictor's second layer)
 
 static bool mfma_unrolled(const MfmaArgs& a) { return a.d / 32 <= kMfmaSPS * kMfmaMaxKS; }
+static int mfma_sps(int d) { return d / 32 <= kMfmaSPSShort ? kMfmaSPSShort : kMfmaSPS; }
 
 static void mfma_split(MfmaArgs& a) {
     const int nsteps = a.d / 32;
     if (mfma_unrolled(a)) {
-        a.steps_per_split = kMfmaSPS;
-        a.ks = cdiv(nsteps, kMfmaSPS);
+        a.steps_per_split = mfma_sps(a.d);
+        a.ks = cdiv(nsteps, a.steps_per_split);
         return;
     }
     const int tiles = cdiv(a.n_max > 0 ? a.n_max : 1, 16 * kMfmaRT);
@@ -333,8 +361,11 @@ static dv_status mfma_go(MfmaArgs& a, MfmaEpi& e, hipStream_t s) {
     mfma_split(a);
     e.part = a.part; e.ks = a.ks; e.B = a.B; e.n_max = a.n_max; e.n_dev = a.n_dev;
     const int waves = cdiv(a.n_max, 16 * kMfmaRT) * a.ks;
-    if (mfma_unrolled(a))
-        hipLaunchKernelGGL(k_rowdot_mfma_u<kMfmaSPS>, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
+    const dim3 ug(cdiv(a.n_max, 16 * kMfmaRT * (kBlock / kWave)) * a.ks);   // 256 rows x one k range a workgroup
+    if (mfma_unrolled(a) && a.steps_per_split == kMfmaSPSShort)
+        hipLaunchKernelGGL(k_rowdot_mfma_u<kMfmaSPSShort>, ug, dim3(kBlock), 0, s, a);
+    else if (mfma_unrolled(a))
+        hipLaunchKernelGGL(k_rowdot_mfma_u<kMfmaSPS>, ug, dim3(kBlock), 0, s, a);
     else
         hipLaunchKernelGGL(k_rowdot_mfma, dim3(cdiv(waves, kBlock / kWave)), dim3(kBlock), 0, s, a);
     hipLaunchKernelGGL(k_rowdot_mfma_epi, dim3(cdiv((long)a.B * a.n_max, kBlock)), dim3(kBlock), 0, s, a, e);
@@ -349,7 +380,7 @@ dv_status launch_fc1_mfma(const float* y, int B, int d, const void* w1_t, const 
     a.y = y; a.B = B; a.d = d; a.w = (const half_t*)w1_t; a.w_rows = N; a.idx = idx; a.qkv = 0;
     a.n_max = n_max; a.n_dev = n_dev; a.part = part;
     MfmaEpi e{};
-    e.bias = b1; e.out = a_out;
+    e.bias = b1; e.relu = 1; e.out = a_out;
     return mfma_go(a, e, s);
 }
 
@@ -362,6 +393,22 @@ dv_status launch_qkv_mfma(const float* y, int B, int d, int h, int d_h, const in
     MfmaEpi e{};
     e.bias = bias; e.out = q; e.K = (half_t*)kv->k_cache; e.V = (half_t*)kv->v_cache; e.max_len = kv->max_len;
     e.pos = kv->pos; e.pos_dev = kv->pos_dev;
+    return mfma_go(a, e, s);
+}
+
+size_t rowdot_mfma_rows_part_floats(int n_rows, int d) {
+    MfmaArgs a{};
+    a.d = d; a.n_max = n_rows > 0 ? n_rows : 1;
+    mfma_split(a);
+    return (size_t)a.ks * 16 * a.n_max;
+}
+
+dv_status launch_rows_mfma(const float* y, int B, int d, const void* w, int n_rows, bool relu, float* out, float* part,
+                           hipStream_t s) {
+    MfmaArgs a{};
+    a.y = y; a.B = B; a.d = d; a.w = (const half_t*)w; a.w_rows = n_rows; a.qkv = 0; a.n_max = n_rows; a.part = part;
+    MfmaEpi e{};
+    e.relu = relu ? 1 : 0; e.out = out;
     return mfma_go(a, e, s);
 }
 
