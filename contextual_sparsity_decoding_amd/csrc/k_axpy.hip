@@ -57,7 +57,7 @@ struct AxpyArgs {
     const float* apart;       // attention partials [B][rows / blk][num_splits][blk + 2], or NULL
     int num_splits;
     int B, n_groups;
-    float* partial;           // [n_groups][B][d]
+    float* partial;           // [n_groups][B][d], or [parts][B][d]
     int32_t* rows_read;
     // NB == 1, tk_s set: the last column of workgroups runs a selection
     // role over scores tk_s[0, tk_n), 1024 per workgroup: ATTN stores their
@@ -367,14 +367,16 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 // rows whose coefficients are all zero when asked) and writes their
 // coefficients straight into the A operands.  Then each wave takes 128
 // columns over all of the part's rows, 32 a step, with the weight loads of
-// the next kAxPF steps in flight.  The B operand wants 8 rows of one column
+// the next kAxPF steps in flight (a step of no live row is not multiplied,
+// its loads re-read one row).  The B operand wants 8 rows of one column
 // per lane while a row of W is contiguous along columns, so a step's 32 x 128
 // tile goes through the wave's own LDS region: 16-byte loads (lane l: row
 // 4 i + l / 16, columns 8 (l % 16) .. +7), read back 2 bytes at a time.  Row
 // r sits at position (r % 8) * 4 + r / 8 with a 288-byte stride, so that
 // the 4 lane groups' reads (rows 8 apart) fall on disjoint banks.  One
 // partial per part, not per group, keeps the partial sums (B x d floats a
-// part, written and read back once) a quarter of what 64-row groups write.
+// part, written and read back once) a quarter of what 64-row groups write
+// (two groups a part, for twice the workgroups, measured slower).
 typedef _Float16 f16x8a __attribute__((ext_vector_type(8)));
 constexpr int kAxKS = 32;                      // rows per matrix-core step
 constexpr int kAxWC = 128;                     // columns per wave (8 tiles of 16)

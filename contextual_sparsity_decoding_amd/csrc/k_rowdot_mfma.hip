@@ -295,8 +295,12 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi 
     if (i >= e.B * e.n_max) return;
     const int b = i / e.n_max, u = i % e.n_max;
     if (u >= n) return;
+    float pv[kMfmaMaxKS];                                  // every range's load in flight, then the sum in order
+#pragma unroll
+    for (int k = 0; k < kMfmaMaxKS; ++k) pv[k] = k < e.ks ? e.part[((size_t)k * 16 + b) * e.n_max + u] : 0.f;
     float v = 0.f;
-    for (int k = 0; k < e.ks; ++k) v += e.part[((size_t)k * 16 + b) * e.n_max + u];
+#pragma unroll
+    for (int k = 0; k < kMfmaMaxKS; ++k) v += pv[k];
     const int j = mfma_row(a, u, n);
     const half_t* bias = (const half_t*)e.bias;
     if (!a.qkv) {

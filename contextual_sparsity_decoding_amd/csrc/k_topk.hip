@@ -13,6 +13,8 @@
 //           thread) writes the set in ascending index order.
 #include "dv_internal.h"
 
+#include <type_traits>
+
 namespace dv {
 
 // Digit search over a filled histogram of nb bins: the digit whose bin
@@ -188,10 +190,17 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores,
 // compare or two per element.  The first pass, where every key counts,
 // spreads each bin over 4 copies (lane & 3) so that equal digits within a
 // wave instruction rarely update the same LDS word.
+template <typename M>
+__device__ __forceinline__ unsigned popc_mask(M m) {
+    if constexpr (sizeof(M) == 8) return (unsigned)__popcll(m);
+    else return (unsigned)__popc(m);
+}
+
 template <int E>
 __global__ __launch_bounds__(1024) void k_topk_tile(const float* __restrict__ scores, int n, int k,
                                                     int32_t* __restrict__ idx) {
-    static_assert(E % 4 == 0 && E <= 32, "E in 4..32");
+    static_assert(E % 4 == 0 && E <= 64, "E in 4..64");
+    using M = typename std::conditional<(E > 32), unsigned long long, unsigned>::type;   // bit e = element i0 + e
     __shared__ unsigned hist[4096 * 4];
     __shared__ int32_t stage[kTopkStage];
     __shared__ unsigned tot[17];
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(1024) void k_topk_tile(const float* __restrict__ sc
     int32_t* out = idx + (size_t)blockIdx.x * k;
     const int i0 = tid * E;
     const int lim = max(0, min(E, n - i0));
-    const unsigned vmask = lim >= 32 ? 0xffffffffu : (1u << lim) - 1u;
+    const M vmask = lim >= (int)(8 * sizeof(M)) ? ~(M)0 : ((M)1 << lim) - (M)1;
     const bool vec = (n & 3) == 0 && ((uintptr_t)s & 15u) == 0;
     uint32_t key[E];
     load_keys<E>(s, n, i0, vec, key);
@@ -254,13 +263,13 @@ __global__ __launch_bounds__(1024) void k_topk_tile(const float* __restrict__ sc
         const int shift = ps == 1 ? 8 : 0;
         const int nb = ps == 1 ? 4096 : 256;
         const uint32_t dmask = (uint32_t)nb - 1u;
-        unsigned cm = 0u;
+        M cm = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) cm |= (unsigned)((key[e] & pmask) == prefix) << e;
+        for (int e = 0; e < E; ++e) cm |= (M)((key[e] & pmask) == prefix) << e;
         cm &= vmask;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            if (cm & (1u << e)) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+            if (cm & ((M)1 << e)) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
         __syncthreads();
         unsigned above, inbin;
         const unsigned d = find_digit(hist, nb, krem, tot, sh, &above, &inbin);
@@ -273,35 +282,35 @@ __global__ __launch_bounds__(1024) void k_topk_tile(const float* __restrict__ sc
     // ---- selection mask: keys above the threshold prefix (the whole last
     // bin after an early stop), then the first krem keys equal to the full
     // threshold in index order
-    unsigned sel = 0u, eqm = 0u;
+    M sel = 0, eqm = 0;
     if (done) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) sel |= (unsigned)((key[e] & pmask) >= prefix) << e;
+        for (int e = 0; e < E; ++e) sel |= (M)((key[e] & pmask) >= prefix) << e;
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            sel |= (unsigned)(key[e] > prefix) << e;
-            eqm |= (unsigned)(key[e] == prefix) << e;
+            sel |= (M)(key[e] > prefix) << e;
+            eqm |= (M)(key[e] == prefix) << e;
         }
     }
     sel &= vmask;
     eqm &= vmask;
     if (!done) {                                   // ties at the threshold: lowest indices first
         unsigned eq_tot;
-        const unsigned eq_before = block_excl_scan(__popc(eqm), tot, &eq_tot);
-        unsigned take = krem > eq_before ? min((unsigned)__popc(eqm), krem - eq_before) : 0u;
-        for (unsigned m = eqm; take > 0; --take) {
-            const unsigned low = m & (0u - m);
+        const unsigned eq_before = block_excl_scan(popc_mask(eqm), tot, &eq_tot);
+        unsigned take = krem > eq_before ? min(popc_mask(eqm), krem - eq_before) : 0u;
+        for (M m = eqm; take > 0; --take) {
+            const M low = m & ((M)0 - m);
             sel |= low;
             m ^= low;
         }
     }
     const bool staged = k <= kTopkStage;
     unsigned tsum;
-    unsigned pos = block_excl_scan(__popc(sel), tot, &tsum);
+    unsigned pos = block_excl_scan(popc_mask(sel), tot, &tsum);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        if (sel & (1u << e)) {
+        if (sel & ((M)1 << e)) {
             if (pos < (unsigned)k) {
                 if (staged) stage[pos] = i0 + e;
                 else out[pos] = i0 + e;
@@ -346,24 +355,73 @@ __global__ __launch_bounds__(1024) void k_union(const int32_t* __restrict__ idx,
     const int nw = (n + 31) >> 5;
     for (int i = threadIdx.x; i < nw; i += blockDim.x) bits[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < total_in; i += blockDim.x) {
-        const int j = idx[i];
-        if ((unsigned)j < (unsigned)n) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    // Coalesced loads of 4 consecutive entries a lane (a wave covers 256
+    // entries an instruction, 8 instructions in flight): a set is ascending,
+    // so a lane's 4 entries usually share one word and leave as one OR.
+    // (A lane reading 32 consecutive entries of its own sent each load
+    // instruction to 64 lines, which one compute unit serves a line a cycle.)
+    constexpr int U = 8;
+    const int nwv = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool vec = ((uintptr_t)idx & 15u) == 0;
+    for (int base = wv * U * kWave * 4; base < total_in; base += nwv * U * kWave * 4) {
+        int j[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e0 = base + (u * kWave + lane) * 4;
+            if (vec && e0 + 4 <= total_in) {
+                const int4 v = *reinterpret_cast<const int4*>(idx + e0);
+                j[u][0] = v.x; j[u][1] = v.y; j[u][2] = v.z; j[u][3] = v.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) j[u][e] = e0 + e < total_in ? idx[e0 + e] : -1;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int cw = -1;
+            unsigned acc = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = j[u][e];
+                if ((unsigned)q >= (unsigned)n) continue;   // past the entries, or outside [0, n)
+                if ((q >> 5) != cw) {
+                    if (acc) atomicOr(&bits[cw], acc);
+                    cw = q >> 5;
+                    acc = 0u;
+                }
+                acc |= 1u << (q & 31);
+            }
+            if (acc) atomicOr(&bits[cw], acc);
+        }
     }
     __syncthreads();
+    // The rank of each word's first bit, then every bit position q in turn:
+    // lane-consecutive positions write consecutive ranks, so the stores
+    // coalesce (a thread writing its own words' runs sent a wave's 64
+    // stores to 64 lines).  Ranks are kept in 16 bits (pre) beside the full
+    // rank of each 256-word block's first word (brank), which is less than
+    // 8192 below any rank in its block.
+    unsigned* brank = bits + nw;
+    unsigned short* pre = reinterpret_cast<unsigned short*>(brank + (nw + 255) / 256);
     const int W = (nw + blockDim.x - 1) / blockDim.x;
     const int w0 = threadIdx.x * W;
     unsigned cnt = 0;
     for (int w = w0; w < min(nw, w0 + W); ++w) cnt += __popc(bits[w]);
     unsigned total;
-    unsigned pos = block_excl_scan(cnt, tot, &total);
+    unsigned run = block_excl_scan(cnt, tot, &total);
     for (int w = w0; w < min(nw, w0 + W); ++w) {
-        unsigned m = bits[w];
-        while (m) {
-            const int b = __ffs(m) - 1;
-            if (pos < (unsigned)n) uidx[pos] = w * 32 + b;
-            ++pos;
-            m &= m - 1;
+        pre[w] = (unsigned short)(run & 0xffffu);
+        if ((w & 255) == 0) brank[w >> 8] = run;
+        run += __popc(bits[w]);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < n; q += blockDim.x) {
+        const int w = q >> 5;
+        const unsigned m = bits[w];
+        if ((m >> (q & 31)) & 1u) {
+            const unsigned b0 = brank[w >> 8];
+            const unsigned r = b0 + ((pre[w] - b0) & 0xffffu) + __popc(m & ((1u << (q & 31)) - 1u));
+            uidx[r] = q;
         }
     }
     if (threadIdx.x == 0 && ucount) *ucount = (int32_t)min(total, (unsigned)n);
@@ -398,6 +456,10 @@ dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hi
     else if (E <= 20) DV_TK(20);
     else if (E <= 24) DV_TK(24);
     else if (E <= 32) DV_TK(32);
+    else if (E <= 40) DV_TK(40);
+    else if (E <= 48) DV_TK(48);
+    else if (E <= 56) DV_TK(56);
+    else if (E <= 64) DV_TK(64);
     else hipLaunchKernelGGL((k_topk<16>), dim3(B), dim3(1024), 0, s, scores, n, k, idx);   // tiles of 16384
 #undef DV_TK
     hipError_t e = hipGetLastError();
@@ -407,7 +469,8 @@ dv_status launch_topk(const float* scores, int B, int n, int k, int32_t* idx, hi
 
 dv_status launch_union(const int32_t* idx, int B, int k, int n, int32_t* union_idx, int32_t* union_count,
                        hipStream_t s) {
-    const size_t lds = (size_t)((n + 31) / 32) * sizeof(unsigned);
+    const size_t nw = (size_t)(n + 31) / 32;
+    const size_t lds = nw * sizeof(unsigned) + (nw + 255) / 256 * sizeof(unsigned) + nw * sizeof(unsigned short);
     hipLaunchKernelGGL(k_union, dim3(1), dim3(1024), lds, s, idx, B * k, n, union_idx, union_count);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DV_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -77,7 +77,8 @@ def _scores(case, B, n, seed):
 TOPK_CASES = [(1, 40, 20), (1, 20480, 2048), (1, 49152, 4915), (1, 65536, 1000), (3, 1000, 77),
               (1, 7, 7), (2, 300, 1), (1, 36864, 1843), (1, 1, 1),
               (1, 257, 100), (1, 20481, 2048), (2, 32768, 3000),      # ragged and full single tiles
-              (1, 131072, 13107), (1, 70001, 5000)]                   # rows of several tiles
+              (1, 131072, 13107), (1, 70001, 5000),                   # rows of several tiles
+              (16, 49152, 4915), (5, 40001, 777)]                     # batches over one-tile rows of 40-48 per thread
 
 
 @pytest.mark.parametrize("case", ["normal", "ties", "specials"])
