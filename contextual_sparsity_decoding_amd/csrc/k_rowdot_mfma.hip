@@ -161,10 +161,15 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
     const int nsteps = a.d / 32;
     const int st0 = ksi * SPS, st1 = min(nsteps, st0 + SPS);
     const int col = lane & 15, kq = lane >> 4;             // B column / A row, k block of 8
+    // a tile's weights are loaded 4 lanes to a row (lane l: row l / 4, k
+    // block l % 4), so that consecutive lanes read consecutive bytes, and
+    // moved into the operand layout (row l % 16, k block l / 16) by a lane
+    // permute at use; loading in the operand layout measured 3% slower
+    const int lrow = lane >> 2, lkb = lane & 3;
     int key[kMfmaRT], raw[kMfmaRT];
 #pragma unroll
     for (int t = 0; t < kMfmaRT; ++t) {
-        const int u = u0 + 16 * t + col, uc = u < a.n_max ? u : a.n_max - 1;
+        const int u = u0 + 16 * t + lrow, uc = u < a.n_max ? u : a.n_max - 1;
         key[t] = a.qkv ? (uc / a.dh) % a.n_sel : uc;
     }
     const int32_t* src = a.qkv ? a.head_idx : a.idx;
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
     bool rv[kMfmaRT];
 #pragma unroll
     for (int t = 0; t < kMfmaRT; ++t) {
-        const int u = u0 + 16 * t + col;
+        const int u = u0 + 16 * t + lrow;
         int j = -1;
         if (u < n) {
             if (a.qkv) {
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
             if ((unsigned)j >= (unsigned)a.w_rows) j = -1;   // an index outside W selects nothing
         }
         rv[t] = j >= 0;
-        rowp[t] = a.w + (size_t)(j >= 0 ? j : 0) * a.d + 8 * kq;
+        rowp[t] = a.w + (size_t)(j >= 0 ? j : 0) * a.d + 8 * lkb;
     }
     // the rows are resolved (their index loads waited for); then the inputs
     // and the weights go out back to back
@@ -249,7 +254,10 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_u(MfmaArgs a) {
             }
 #pragma unroll
             for (int t = 0; t < kMfmaRT; ++t) {
-                const f16x8m wb = __builtin_bit_cast(f16x8m, rv[t] ? wr[p][t] : u32x4{0u, 0u, 0u, 0u});
+                u32x4 wq = rv[t] ? wr[p][t] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wq[e] = (unsigned)__builtin_amdgcn_ds_bpermute((4 * col + kq) * 4, (int)wq[e]);
+                const f16x8m wb = __builtin_bit_cast(f16x8m, wq);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, wb, acc[t], 0, 0, 0);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, wb, acc[t], 0, 0, 0);
             }
