@@ -65,6 +65,8 @@ def parse():
                    help="0 skips the long-context composition stack (32 layers, d=4096, 2K-128K context)")
     p.add_argument("--batched", type=int, default=1,
                    help="0 skips the batched OPT-175B-share stack (48 layers, d=12288, batch 1-16)")
+    p.add_argument("--batch-sizes", type=str, default="",
+                   help="comma-separated batch sizes of the batched stack (default: all of them)")
     p.add_argument("--w4", type=int, default=1,
                    help="0 skips the 4-bit-weight sparse MLP (OPT-66B width, fp16 against 4-bit weights)")
     p.add_argument("--extra-steps", type=int, default=12, help="timed tokens per point of the two extra stacks")
@@ -685,7 +687,10 @@ def bench_batched(torch, dv, synth, configs, args):
     kM = wl.k_neurons
     out = []
     stack = None
-    for B in wl.batch:
+    sizes = [int(b) for b in args.batch_sizes.split(",") if b] if args.batch_sizes else list(wl.batch)
+    for B in sizes:
+        if B not in wl.batch:
+            raise SystemExit(f"--batch-sizes: {B} is not one of {list(wl.batch)}")
         progress(f"batched stack: B = {B}")
         if stack is None:
             stack = Stack(dims, L, wl.n_ctx, wl.n_ctx + T + 8, SEED + 7, batch=max(wl.batch), hole_fill=False)
@@ -702,7 +707,7 @@ def bench_batched(torch, dv, synth, configs, args):
         counts = torch.zeros(L, dtype=torch.int32, device="cuda")
         ms, rows, _ = time_stack(torch, dv, sub, X, ws, cfg, W, K, neuron_sets=nsets, neuron_counts=counts)
         u = counts.float().mean().item()
-        dms, _, _ = time_stack(torch, dv, sub, X, ws, dcfg, W, K)
+        dms = time_stack(torch, dv, sub, X, ws, dcfg, W, K)[0] if args.dense else None
         n_att = wl.n_ctx + W + (K - 1) / 2 + 1
         ucfg = sub.cfg(dims.h, int(round(u)), flags, scale)
         by = L * dv.dv_bytes_read(ucfg, n_att, rows, 0.0).total
@@ -711,7 +716,8 @@ def bench_batched(torch, dv, synth, configs, args):
                     "union_neurons": round(u, 1), "union_frac": round(u / dims.N, 4),
                     "fc2_rows_per_layer": round(rows, 1), "bytes_per_step": int(by),
                     "effective_hbm_GBps": round(by / (ms * 1e-3) / 1e9, 1),
-                    "dense_ms_per_step": round(dms, 4), "speedup_vs_dense": round(dms / ms, 3),
+                    "dense_ms_per_step": round(dms, 4) if dms else None,
+                    "speedup_vs_dense": round(dms / ms, 3) if dms else None,
                     "byte_bound_speedup": round(dby / by, 3)})
         del ws, X, nsets, counts
     del stack, sub
