@@ -151,6 +151,35 @@ def test_sparse_mlp(dvlib, d, N, k, B, wdt, skip):
     assert 0 < live <= k and (B > 4 or live < k)
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_sparse_mlp_matrix_core_edges(dvlib, B):
+    """Batches on the matrix-core kernels with nothing to gather: every fc1
+    output non-positive (fc2 keeps no row, so out = residual + b2, and the
+    rows-read count is 0), and a device-side count of zero selected rows
+    (fc1 writes nothing, the finalize adds no group)."""
+    d, N, k = 1024, 4096, 333
+    W, y, idx = _mlp_inputs(d, N, k, B, "f16", seed=B + 71)
+    res = synth.normal((B, d), 72, 0, "x")
+    W = dict(W)
+    W["b1"] = np.full_like(W["b1"], -1e3)               # the ReLU closes every neuron
+    Wd = {n: dev(v) for n, v in W.items()}
+    out = torch.empty(B, d, device="cuda")
+    rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = dvlib.workspace(dvlib.dv_sparse_mlp_workspace_bytes(B, d, k, dvlib.DV_F16))
+    dvlib.dv_sparse_mlp(dev(y), Wd["w1_t"], Wd["b1"], Wd["w2_t"], Wd["b2"], dev(idx), k, out, ws, residual=dev(res),
+                        fc2_rows=rows, flags=dvlib.DV_SKIP_NONPOS_FC2)
+    want, wa = ref.sparse_mlp(y, W["w1_t"], W["b1"], W["w2_t"], W["b2"], idx, residual=res, skip_nonpos=True)
+    assert not np.any(wa > 0)
+    check_close(host(out), want, "f16", "all neurons closed")
+    assert int(host(rows)[0]) == 0
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out2 = torch.full((B, d), float("nan"), device="cuda")
+    dvlib.dv_sparse_mlp(dev(y), Wd["w1_t"], Wd["b1"], Wd["w2_t"], Wd["b2"], dev(idx), k, out2, ws, residual=dev(res),
+                        n_idx_dev=zero)
+    base = res.astype(np.float64) + W["b2"].astype(np.float64)[None, :]
+    check_close(host(out2), base, "f16", "no selected rows")
+
+
 def test_sparse_mlp_dense_and_union(dvlib):
     d, N, B = 512, 2048, 4
     W, y, _ = _mlp_inputs(d, N, 10, B, "f16", seed=5)
