@@ -45,6 +45,7 @@ struct MfmaArgs {
     int n_max;
     const int32_t* n_dev;
     int ks, steps_per_split;  // k ranges and their length in 32-element steps
+    int short_ranges;         // few rows: k ranges of kMfmaSPSShort steps (up to kMfmaMaxKSShort of them)
     float* part;              // [ks][16][n_max]
 };
 
@@ -303,12 +304,18 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi 
     if (i >= e.B * e.n_max) return;
     const int b = i / e.n_max, u = i % e.n_max;
     if (u >= n) return;
-    float pv[kMfmaMaxKS];                                  // every range's load in flight, then the sum in order
+    // up to 16 ranges' loads in flight, then their sum in order
+    auto add16 = [&](int k0, float v) {
+        float pv[16];
 #pragma unroll
-    for (int k = 0; k < kMfmaMaxKS; ++k) pv[k] = k < e.ks ? e.part[((size_t)k * 16 + b) * e.n_max + u] : 0.f;
-    float v = 0.f;
+        for (int k = 0; k < 16; ++k)
+            pv[k] = k0 + k < e.ks ? e.part[((size_t)(k0 + k) * 16 + b) * e.n_max + u] : 0.f;
 #pragma unroll
-    for (int k = 0; k < kMfmaMaxKS; ++k) v += pv[k];
+        for (int k = 0; k < 16; ++k) v += pv[k];
+        return v;
+    };
+    float v = add16(0, 0.f);
+    for (int k0 = 16; k0 < e.ks; k0 += 16) v = add16(k0, v);   // short ranges of few rows
     const int j = mfma_row(a, u, n);
     const half_t* bias = (const half_t*)e.bias;
     if (!a.qkv) {
@@ -348,16 +355,25 @@ size_t rowdot_mfma_part_floats(int n_max) { return (size_t)kMfmaMaxKS * 16 * (n_
 
 constexpr int kMfmaSPS = 24;       // k steps per workgroup in the unrolled kernel (d <= 32 * 24 * kMfmaMaxKS)
 
-constexpr int kMfmaSPSShort = 8;   // rows of at most 256 (a predictor's second layer)
+constexpr int kMfmaSPSShort = 8;   // rows of at most 256 (a predictor's second layer), or few rows
 
 static bool mfma_unrolled(const MfmaArgs& a) { return a.d / 32 <= kMfmaSPS * kMfmaMaxKS; }
 static int mfma_sps(int d) { return d / 32 <= kMfmaSPSShort ? kMfmaSPSShort : kMfmaSPS; }
+
+constexpr int kMfmaMaxKSShort = 64;
 
 static void mfma_split(MfmaArgs& a) {
     const int nsteps = a.d / 32;
     if (mfma_unrolled(a)) {
         a.steps_per_split = mfma_sps(a.d);
         a.ks = cdiv(nsteps, a.steps_per_split);
+        // a launch of fewer than 128 workgroups (a predictor's 128 rows) takes
+        // short k ranges instead: each wave's chain of loads is a third as long
+        const int wgs = cdiv(a.n_max > 0 ? a.n_max : 1, 16 * kMfmaRT * (kBlock / kWave)) * a.ks;
+        if (a.short_ranges && wgs < 128 && cdiv(nsteps, kMfmaSPSShort) <= kMfmaMaxKSShort) {
+            a.steps_per_split = kMfmaSPSShort;
+            a.ks = cdiv(nsteps, kMfmaSPSShort);
+        }
         return;
     }
     const int tiles = cdiv(a.n_max > 0 ? a.n_max : 1, 16 * kMfmaRT);
@@ -410,7 +426,7 @@ dv_status launch_qkv_mfma(const float* y, int B, int d, int h, int d_h, const in
 
 size_t rowdot_mfma_rows_part_floats(int n_rows, int d) {
     MfmaArgs a{};
-    a.d = d; a.n_max = n_rows > 0 ? n_rows : 1;
+    a.d = d; a.n_max = n_rows > 0 ? n_rows : 1; a.short_ranges = 1;
     mfma_split(a);
     return (size_t)a.ks * 16 * a.n_max;
 }
@@ -419,6 +435,7 @@ dv_status launch_rows_mfma(const float* y, int B, int d, const void* w, int n_ro
                            hipStream_t s) {
     MfmaArgs a{};
     a.y = y; a.B = B; a.d = d; a.w = (const half_t*)w; a.w_rows = n_rows; a.qkv = 0; a.n_max = n_rows; a.part = part;
+    a.short_ranges = 1;
     MfmaEpi e{};
     e.relu = relu ? 1 : 0; e.out = out;
     return mfma_go(a, e, s);
