@@ -362,30 +362,35 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 // column l % 16, both at rows 8 (l / 16) .. +7 of the step; D's register i
 // holds batch row 4 (l / 16) + i, column l % 16.
 //
-// A workgroup takes one 512-column slice of a part of kAxG groups of 64 rows.
+// A workgroup takes one 256-column slice of a part of kAxG groups of 64 rows.
 // Wave w first compacts group w's rows as the vector kernel does (dropping
 // rows whose coefficients are all zero when asked) and writes their
-// coefficients straight into the A operands.  Then each wave takes 128
+// coefficients straight into the A operands.  Then each wave takes 64
 // columns over all of the part's rows, 32 a step, with the weight loads of
 // the next kAxPF steps in flight (a step of no live row is not multiplied,
 // its loads re-read one row).  The B operand wants 8 rows of one column
-// per lane while a row of W is contiguous along columns, so a step's 32 x 128
+// per lane while a row of W is contiguous along columns, so a step's 32 x 64
 // tile goes through the wave's own LDS region: 16-byte loads (lane l: row
-// 4 i + l / 16, columns 8 (l % 16) .. +7), read back 2 bytes at a time.  Row
-// r sits at position (r % 8) * 4 + r / 8 with a 288-byte stride, so that
-// the 4 lane groups' reads (rows 8 apart) fall on disjoint banks.  One
+// 8 i + l / 8, columns 8 (l % 8) .. +7; 128 bytes, one line, of 8 rows a
+// load), read back 2 bytes at a time.  Row r sits at position
+// (r % 8) * 4 + r / 8 with a 160-byte stride, so that the 4 lane groups'
+// reads (rows 8 apart) fall on disjoint banks.  One
 // partial per part, not per group, keeps the partial sums (B x d floats a
 // part, written and read back once) a quarter of what 64-row groups write
 // (two groups a part, for twice the workgroups, measured slower).
 typedef _Float16 f16x8a __attribute__((ext_vector_type(8)));
 constexpr int kAxKS = 32;                      // rows per matrix-core step
-constexpr int kAxWC = 128;                     // columns per wave (8 tiles of 16)
-constexpr int kAxRS = 288;                     // LDS bytes per tile row (256 + 32)
+constexpr int kAxWC = 64;                      // columns per wave (4 tiles of 16; 128 measured 2-11% slower)
+constexpr int kAxLPR = kAxWC * 2 / 16;         // lanes per row in a load
+constexpr int kAxRPL = kWave / kAxLPR;         // rows per load
+constexpr int kAxNLD = kAxKS / kAxRPL;         // loads per step
+constexpr int kAxNT = kAxWC / 16;              // column tiles
+constexpr int kAxRS = kAxWC * 2 + 32;          // LDS bytes per tile row (the row + 32)
 constexpr int kAxTile = kAxKS * kAxRS;         // one wave's tile
 constexpr int kAxSlice = 4 * kAxWC;            // columns per workgroup
 constexpr int kAxG = kBlock / kWave;           // 64-row groups per part (one per wave in the compaction)
 constexpr int kAxSteps = kAxG * kRowsPerGroup / kAxKS;
-constexpr int kAxPF = 2;                       // steps of weight loads in flight
+constexpr int kAxPF = 4;                       // steps of weight loads in flight
 
 template <int NB>
 __global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
@@ -438,21 +443,22 @@ __global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
         }
     }
     __syncthreads();
-    // ---- this wave's 128 columns over the part's rows
-    const int c0 = slice * kAxSlice + wv * kAxWC;  // d % 512 == 0
+    // ---- this wave's 64 columns over the part's rows
+    const int c0 = slice * kAxSlice + wv * kAxWC;  // d % 256 == 0
     int nlv[kAxG];
 #pragma unroll
     for (int g = 0; g < kAxG; ++g) nlv[g] = __builtin_amdgcn_readfirstlane(s_n[g]);
     // a step's loads are unmasked: rows past a group's live ones read its last
     // live row (or row 0), their coefficients being zero
-    u32x4 w[kAxPF][8];
+    u32x4 w[kAxPF][kAxNLD];
     auto load_step = [&](int st, int slot) {
         const int g = st / (kRowsPerGroup / kAxKS), kb = (st % (kRowsPerGroup / kAxKS)) * kAxKS;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int k = kb + 4 * i + (lane >> 4);
+        for (int i = 0; i < kAxNLD; ++i) {
+            const int k = kb + kAxRPL * i + lane / kAxLPR;
             const int rr = nlv[g] > 0 ? s_row[g][k < nlv[g] ? k : nlv[g] - 1] : 0;
-            w[slot][i] = ld16_stream(W + (size_t)rr * a.d + c0 + 8 * (lane & 15));
+            const half_t* src = W + (size_t)rr * a.d + c0 + 8 * (lane % kAxLPR);
+            w[slot][i] = ld16_stream(src);         // whole lines: the streaming hint measured faster here
         }
     };
 #pragma unroll
@@ -461,23 +467,23 @@ __global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
         asm volatile("" ::: "memory");
     }
     unsigned char* tile = tiles + wv * kAxTile;
-    f32x4 acc[8];
+    f32x4 acc[kAxNT];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kAxNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < kAxSteps; ++st) {
         const int slot = st % kAxPF;
         const int g = st / (kRowsPerGroup / kAxKS), kb = (st % (kRowsPerGroup / kAxKS)) * kAxKS;
         if (kb < nlv[g]) {                         // uniform: a step with a live row
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {          // row r = 4 i + l / 16 of the step
-                const int r = 4 * i + (lane >> 4);
-                *reinterpret_cast<u32x4*>(tile + ((r & 7) * 4 + (r >> 3)) * kAxRS + (lane & 15) * 16) = w[slot][i];
+            for (int i = 0; i < kAxNLD; ++i) {     // row r of the step
+                const int r = kAxRPL * i + lane / kAxLPR;
+                *reinterpret_cast<u32x4*>(tile + ((r & 7) * 4 + (r >> 3)) * kAxRS + (lane % kAxLPR) * 16) = w[slot][i];
             }
             const f16x8a ahi = *reinterpret_cast<const f16x8a*>(&aop[st][0][lane & 15][8 * (lane >> 4)]);
             const f16x8a alo = *reinterpret_cast<const f16x8a*>(&aop[st][1][lane & 15][8 * (lane >> 4)]);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < kAxNT; ++nt) {
                 f16x8a bop;
 #pragma unroll
                 for (int j = 0; j < 8; ++j)        // row 8 (l / 16) + j, column 16 nt + l % 16
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
         }
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < kAxNT; ++nt) {
         const int col = c0 + nt * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -639,7 +645,7 @@ AxpyPlan axpy_plan(int d, int rows, int wdt) {
 
 size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_groups * B * d; }
 
-// Batches of 8-16 with fp16 weights, 512-column slices and coefficients in
+// Batches of 8-16 with fp16 weights, 256-column slices and coefficients in
 // memory take the matrix cores (an output projection first merges its
 // split-K partials into the attention output).
 bool axpy_mfma_supported(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == DV_F16 && d % kAxSlice == 0; }

@@ -126,6 +126,7 @@ MLP_CASES = [
     (1024, 4096, 333, 8, "f16"),      # ragged: 333 rows, not a multiple of the 64-row tiles
     (4096, 16384, 1638, 16, "f16"),
     (12288, 49152, 4915, 9, "f16"),   # OPT-175B width, odd batch
+    (1280, 5120, 512, 12, "f16"),     # five 256-column slices of the matrix-core gather-AXPY
 ]
 
 
