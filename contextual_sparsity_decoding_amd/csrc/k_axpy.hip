@@ -18,10 +18,11 @@
 // workgroup merges a head's splits (running max, rescaled sums) for its own
 // rows, so no separate combine pass runs.
 //
-// Batches of 8-16 run on the matrix cores instead (k_axpy_mfma): with 16
+// Batches of 2-16 run on the matrix cores instead (k_axpy_mfma): at 16
 // FMAs per weight element the vector ALUs fall far behind HBM, and a partial
 // of B x d floats per 64 rows would cost as many bytes as the weights, so a
-// workgroup there covers 256 rows.
+// workgroup there covers 256 rows (at a batch of 2-4 the partials alone
+// made the vector kernel slower).
 //
 // k_axpy_finalize then adds the partials in a fixed order, plus bias and
 // residual, over the groups that hold live rows only (a device-side row count
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(kBlock) void k_axpy(AxpyArgs a) {
 
 }
 
-// The gather-AXPY of a batch of 8-16 on the matrix cores (fp16 weights,
-// coefficients read from memory):
+// The gather-AXPY of a batch of 2-16 on the matrix cores (fp16 weights,
+// coefficients read from memory; batches of up to 8 in the 8-row bucket):
 //     partial[p][b][c] = sum over the part's rows u of coef[b][u] W[row(u)][c]
 // as D = A B with v_mfma_f32_16x16x32_f16, A = the coefficients (16 batch
 // rows x 32 rows of W, in fp16 hi + lo so that they keep about 22 bits) and
@@ -394,7 +395,7 @@ constexpr int kAxPF = 4;                       // steps of weight loads in fligh
 
 template <int NB>
 __global__ __launch_bounds__(kBlock) void k_axpy_mfma(AxpyArgs a) {
-    static_assert(NB >= 8 && NB <= 16 && kRowsPerGroup == kWave && kRowsPerGroup % kAxKS == 0, "batches of 8-16");
+    static_assert(NB >= 8 && NB <= 16 && kRowsPerGroup == kWave && kRowsPerGroup % kAxKS == 0, "batch buckets of 8 and 16");
     __shared__ int s_row[kAxG][kRowsPerGroup];
     __shared__ int s_n[kAxG];
     __shared__ __align__(16) half_t aop[kAxSteps][2][16][kAxKS];     // [step][hi, lo][batch row][row of the step]
@@ -645,10 +646,11 @@ AxpyPlan axpy_plan(int d, int rows, int wdt) {
 
 size_t axpy_ws_floats(const AxpyPlan& p, int B, int d) { return (size_t)p.n_groups * B * d; }
 
-// Batches of 8-16 with fp16 weights, 256-column slices and coefficients in
+// Batches of 2-16 with fp16 weights, 256-column slices and coefficients in
 // memory take the matrix cores (an output projection first merges its
-// split-K partials into the attention output).
-bool axpy_mfma_supported(int B, int d, int wdt) { return B >= 8 && B <= 16 && wdt == DV_F16 && d % kAxSlice == 0; }
+// split-K partials into the attention output); a batch of one keeps the
+// vector kernel, whose partials are a sixteenth of its weight bytes.
+bool axpy_mfma_supported(int B, int d, int wdt) { return B >= 2 && B <= 16 && wdt == DV_F16 && d % kAxSlice == 0; }
 
 static bool axpy_mfma_ok(const AxpyCall& c) { return axpy_mfma_supported(c.B, c.d, c.wdt) && !c.apart && !c.sel; }
 
@@ -709,7 +711,7 @@ dv_status launch_axpy(const AxpyCall& c, hipStream_t s) {
     lv.n_rows_dev = c.n_rows_dev; lv.rows = c.rows; lv.rows_per_part = mf ? kAxG * kRowsPerGroup : kRowsPerGroup;
     timed_begin(c.timed, s);
     if (mf) {
-        if (nb == 8) axpy_mfma_go<8>(a, n_parts, s);
+        if (nb <= 8) axpy_mfma_go<8>(a, n_parts, s);
         else axpy_mfma_go<16>(a, n_parts, s);
     } else {
         switch (nb) {

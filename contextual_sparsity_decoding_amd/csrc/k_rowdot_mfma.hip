@@ -341,13 +341,13 @@ __global__ __launch_bounds__(kBlock) void k_rowdot_mfma_epi(MfmaArgs a, MfmaEpi 
 namespace dvh {
 using namespace dv;
 
-// Batches of 8-16, and batches of 4-7 whose inputs do not fit in LDS (the
+// Batches of 8-16, and batches of 2-7 whose inputs do not fit in LDS (the
 // vector paths would read them from global memory for every row; the
-// matrix cores take them as a padded 16-row operand).  At a batch of 2 the
-// vector paths measured faster over a union of neurons (OPT-175B width:
-// 91 against 84 tokens/s), at 4 slower (104 against 138).
+// matrix cores take them as a padded 16-row operand).  OPT-175B width, 8
+// layers over a union of neurons: batch 2 3.66 -> 3.27 ms per step with
+// this and the matrix-core gather-AXPY, batch 4 4.25 -> 3.91.
 bool rowdot_mfma_ok(int B, int d, int wdt) {
-    const bool wide = B >= 4 && (size_t)B * d * sizeof(float) > kYLdsMax;
+    const bool wide = B >= 2 && (size_t)B * d * sizeof(float) > kYLdsMax;
     return (B >= 8 || wide) && B <= 16 && wdt == DV_F16 && d % 32 == 0;
 }
 

@@ -127,6 +127,8 @@ MLP_CASES = [
     (4096, 16384, 1638, 16, "f16"),
     (12288, 49152, 4915, 9, "f16"),   # OPT-175B width, odd batch
     (1280, 5120, 512, 12, "f16"),     # five 256-column slices of the matrix-core gather-AXPY
+    (1024, 4096, 400, 2, "f16"),      # a batch of 2 on the matrix-core gather-AXPY, fc1 on the vector path
+    (12288, 49152, 4915, 3, "f16"),   # a batch of 3 whose inputs do not fit in LDS: fc1 on the matrix cores
 ]
 
 
